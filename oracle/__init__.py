@@ -1,0 +1,5 @@
+"""CPU oracle of the LSA hot path: test infrastructure, never used by the product path."""
+from .lsa_oracle import *  # noqa: F401,F403
+from .lsa_oracle import (Index, IndexParams, SelectParams, attend, bf16_to_f64, build_index,
+                         bucket_keys, candidates, dense_select, eligible_keys, kmeans, pool,
+                         rhe_div, scores, select, sq_dist)

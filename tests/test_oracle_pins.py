@@ -1,0 +1,301 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+Each test ties one oracle function to an independent fact: exact rational
+rounding, hand-worked fixtures under tests/golden/, brute-force enumeration
+in plain Python, closed forms, and special cases that reduce to a library
+routine.  All CPU only.
+"""
+import json
+import os
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- rounding
+def test_rhe_div_exhaustive_against_fraction():
+    S = np.arange(-600, 601, dtype=np.int64)
+    for n in range(1, 70):
+        got = O.rhe_div(S, n)
+        want = np.array([round(Fraction(int(s), n)) for s in S])   # Python rounds halves to even
+        assert np.array_equal(got, want), n
+
+
+def test_pool_against_fraction_means():
+    rng = np.random.default_rng(1)
+    for p in (1, 2, 3, 4, 5, 8):
+        x = rng.integers(-128, 128, size=(p * 37 + (p - 1), 6))
+        got = O.pool(x, p)
+        assert got.shape == (37, 6)
+        for g in range(37):
+            for d in range(6):
+                s = int(x[g * p:(g + 1) * p, d].sum())
+                assert got[g, d] == round(Fraction(s, p))
+
+
+# ------------------------------------------------------------------ k-means
+def _brute_assign(X, mu):
+    """Plain-Python nearest centroid, lowest index on ties."""
+    out = []
+    for x in X.tolist():
+        best, bi = None, -1
+        for c, m in enumerate(mu.tolist()):
+            d = sum((a - b) * (a - b) for a, b in zip(x, m))
+            if best is None or d < best:
+                best, bi = d, c
+        out.append(bi)
+    return np.array(out)
+
+
+def _frac_mean(rows):
+    n = len(rows)
+    return [round(Fraction(int(sum(r[d] for r in rows)), n)) for d in range(len(rows[0]))]
+
+
+def test_kmeans_golden_tie():
+    g = _golden("hand_kmeans_tie.json")
+    mu, a = O.kmeans(np.array(g["X"]), g["C"], g["iters"])
+    assert a.tolist() == g["assign"]
+    assert mu.tolist() == g["centroids"]
+
+
+def test_kmeans_single_cluster_is_rounded_mean():
+    rng = np.random.default_rng(2)
+    X = rng.integers(-128, 128, size=(50, 8))
+    mu, a = O.kmeans(X, 1, 3)
+    assert (a == 0).all()
+    assert mu[0].tolist() == _frac_mean(X.tolist())
+
+
+def test_kmeans_one_cluster_per_vector_is_identity():
+    rng = np.random.default_rng(3)
+    X = rng.integers(-128, 128, size=(32, 8))
+    assert len({tuple(r) for r in X.tolist()}) == 32
+    mu, a = O.kmeans(X, 32, 4)
+    assert a.tolist() == list(range(32))
+    assert np.array_equal(mu, X)
+
+
+@pytest.mark.parametrize("iters", [1, 2, 3])
+def test_kmeans_steps_against_brute_force(iters):
+    rng = np.random.default_rng(10 + iters)
+    # coarse values make exact distance ties frequent
+    X = rng.integers(-3, 4, size=(48, 3)) * 2
+    C = 6
+    mu_prev, _ = O.kmeans(X, C, iters - 1) if iters > 1 else (X[np.arange(C) * (48 // C)], None)
+    mu, a = O.kmeans(X, C, iters)
+    assert a.tolist() == _brute_assign(X, mu_prev).tolist()
+    for c in range(C):
+        rows = X[a == c].tolist()
+        want = _frac_mean(rows) if rows else mu_prev[c].tolist()
+        assert mu[c].tolist() == want, c
+
+
+# ---------------------------------------------------------------- index
+def test_index_golden():
+    g = _golden("hand_index_select.json")
+    pr = g["params"]
+    latk = np.array(g["latk"])
+    idx = O.build_index(latk, len(latk), O.IndexParams(pr["pool"], pr["block"], pr["buckets"],
+                                                       pr["iters"]))
+    assert idx.pooled.tolist() == g["index"]["pooled"]
+    assert idx.centroids.tolist() == g["index"]["centroids"]
+    assert [m.tolist() for m in idx.members] == g["index"]["members"]
+
+
+def test_select_golden():
+    g = _golden("hand_index_select.json")
+    pr = g["params"]
+    latk = np.array(g["latk"])
+    idx = O.build_index(latk, len(latk), O.IndexParams(pr["pool"], pr["block"], pr["buckets"],
+                                                       pr["iters"]))
+    sp = O.SelectParams(**g["select_params"])
+    for case in g["queries"]:
+        got = O.select(idx, np.array(case["q"]), case["t"], sp)
+        assert got.tolist() == case["sel"], case["why"]
+
+
+def _random_index(seed, T, p, N, C, iters, dim=4, lo=-6, hi=7, tree=None):
+    rng = np.random.default_rng(seed)
+    latk = rng.integers(lo, hi, size=(T, dim))
+    params = O.IndexParams(p, N, C, iters, *(tree or (0, 0, 0)))
+    return latk, O.build_index(latk, T, params)
+
+
+def _brute_select(idx, latk, q, t, sp):
+    """Enumerate every (bucket, key) pair, order by (score desc, bucket asc,
+    key asc), keep the first `budget` eligible keys; add window and sinks."""
+    p = idx.params.pool
+    pairs = []
+    cands = O.candidates(idx, q, sp)
+    for beta in cands.tolist():
+        s = sum(int(a) * int(b) for a, b in zip(q, idx.centroids[beta]))
+        for g in idx.members[beta].tolist():
+            for r in range(p):
+                j = g * p + r
+                if sp.sinks <= j <= t - sp.window:
+                    pairs.append((-s, beta, j))
+    pairs.sort()
+    sel = {j for _, _, j in pairs[: sp.budget]}
+    sel |= set(range(max(0, t - sp.window + 1), t + 1))
+    sel |= set(range(0, min(sp.sinks, t + 1)))
+    return sorted(sel)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_against_enumeration(seed):
+    T = 64 + seed * 7
+    latk, idx = _random_index(seed, T, p=2, N=8, C=3, iters=2)
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(12):
+        sp = O.SelectParams(budget=int(rng.integers(1, 20)), window=int(rng.integers(2, 9)),
+                            sinks=int(rng.integers(0, 5)))
+        t = int(rng.integers(0, T))
+        q = rng.integers(-5, 6, size=latk.shape[1])
+        assert O.select(idx, q, t, sp).tolist() == _brute_select(idx, latk, q, t, sp)
+
+
+def test_select_count_window_sinks_causal_nesting():
+    T = 16384
+    latk, idx = _random_index(7, T, p=4, N=256, C=16, iters=3, dim=8, lo=-20, hi=21)
+    sp = O.SelectParams(budget=300, window=64, sinks=4)
+    rng = np.random.default_rng(8)
+    for t in [0, 1, 3, 4, 63, 64, 67, 68, 69, 200, 371, 372, 373, 1000, T - 1] + \
+            rng.integers(0, T, 10).tolist():
+        q = rng.integers(-30, 31, size=8)
+        sel = O.select(idx, q, t, sp)
+        assert len(sel) == min(t + 1, sp.budget + sp.window + sp.sinks)
+        assert sel.max() <= t and len(np.unique(sel)) == len(sel)
+        assert set(range(max(0, t - sp.window + 1), t + 1)) <= set(sel.tolist())
+        assert set(range(min(sp.sinks, t + 1))) <= set(sel.tolist())
+        bigger = O.select(idx, q, t, O.SelectParams(budget=500, window=64, sinks=4))
+        assert set(sel.tolist()) <= set(bigger.tolist())
+
+
+def test_singleton_buckets_equal_exact_topk():
+    """p = 1 and one bucket per vector: selection = exact top-k of per-key scores."""
+    T, N = 512, 64
+    rng = np.random.default_rng(9)
+    latk = rng.integers(-100, 101, size=(T, 8))
+    for b in range(T // N):
+        assert len({tuple(r) for r in latk[b * N:(b + 1) * N].tolist()}) == N
+    idx = O.build_index(latk, T, O.IndexParams(1, N, N, 2))
+    sp = O.SelectParams(budget=37, window=16, sinks=3)
+    for t in [100, 250, 511]:
+        q = rng.integers(-100, 101, size=8)
+        keys = np.arange(sp.sinks, t - sp.window + 1)
+        sc = latk[keys] @ q
+        top = keys[np.lexsort((keys, -sc))][: sp.budget]
+        want = set(top.tolist()) | set(range(t - sp.window + 1, t + 1)) | set(range(sp.sinks))
+        assert O.select(idx, q, t, sp).tolist() == sorted(want)
+        assert O.dense_select(latk, q, t, sp).tolist() == sorted(want)
+
+
+def test_tree_with_full_branching_equals_flat():
+    T = 4 * 16 * 6 + 50            # 6 full blocks of 16 pooled vectors + a tail; groups of 2 blocks
+    latk = np.random.default_rng(11).integers(-30, 31, size=(T, 6))
+    flat = O.build_index(latk, T, O.IndexParams(4, 16, 4, 2))
+    tree = O.build_index(latk, T, O.IndexParams(4, 16, 4, 2, 2, 3, 2))
+    assert tree.n_grp == 3 and tree.sup_centroids.shape[0] == 9
+    assert np.array_equal(flat.centroids, tree.centroids)
+    rng = np.random.default_rng(12)
+    for _ in range(10):
+        t = int(rng.integers(0, T))
+        q = rng.integers(-30, 31, size=6)
+        sp_f = O.SelectParams(budget=40, window=8, sinks=2)
+        sp_t = O.SelectParams(budget=40, window=8, sinks=2, tree_top=9)
+        assert np.array_equal(O.select(flat, q, t, sp_f), O.select(tree, q, t, sp_t))
+
+
+def test_tree_candidates_against_brute_force():
+    T = 4 * 16 * 6 + 50
+    latk = np.random.default_rng(13).integers(-30, 31, size=(T, 6))
+    tree = O.build_index(latk, T, O.IndexParams(4, 16, 4, 2, 2, 3, 2))
+    # every leaf of a complete group is in exactly one super cluster
+    cov = np.sort(np.concatenate(tree.sup_members))
+    assert cov.tolist() == list(range(tree.covered_leaves()))
+    rng = np.random.default_rng(14)
+    for R in (1, 2, 4):
+        q = rng.integers(-30, 31, size=6)
+        ss = [(-sum(int(a) * int(b) for a, b in zip(q, m)), i)
+              for i, m in enumerate(tree.sup_centroids)]
+        top = [i for _, i in sorted(ss)[:R]]
+        want = set()
+        for s in top:
+            want |= set(tree.sup_members[s].tolist())
+        want |= set(range(tree.covered_leaves(), tree.n_bkt))
+        got = O.candidates(tree, q, O.SelectParams(tree_top=R))
+        assert got.tolist() == sorted(want)
+        t = T - 1
+        sp = O.SelectParams(budget=30, window=8, sinks=2, tree_top=R)
+        assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
+
+
+def test_index_is_prefix_function():
+    """The index over keys [0, T') depends only on those keys (cache-consistent)."""
+    latk = np.random.default_rng(15).integers(-40, 41, size=(3000, 4))
+    params = O.IndexParams(4, 64, 8, 3)
+    cache = {}
+    for Tp in (0, 5, 255, 256, 257, 1024, 2999):
+        a = O.build_index(latk, Tp, params, cache)
+        b = O.build_index(latk[:Tp].copy(), Tp, params)
+        assert np.array_equal(a.centroids, b.centroids)
+        assert [m.tolist() for m in a.members] == [m.tolist() for m in b.members]
+        # every complete pooled group is in exactly one bucket
+        allm = np.sort(np.concatenate(a.members)) if a.members else np.zeros(0)
+        assert allm.tolist() == list(range(Tp // 4))
+
+
+# ---------------------------------------------------------------- attention
+def test_attention_golden():
+    g = _golden("hand_attention.json")
+    out = O.attend(np.array([g["q"]]), np.array(g["K"])[:, None, :], np.array(g["V"])[:, None, :], 1)
+    assert np.allclose(out[0], g["out"], rtol=0, atol=1e-12)
+
+
+def test_attention_full_selection_is_causal_sdpa():
+    """Selecting every key 0..t reduces to textbook causal attention."""
+    rng = np.random.default_rng(16)
+    T, Hq, Hkv, D = 40, 6, 2, 16
+    q = rng.standard_normal((T, Hq, D))
+    K = rng.standard_normal((T, Hkv, D))
+    V = rng.standard_normal((T, Hkv, D))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2),
+        torch.from_numpy(np.repeat(K, Hq // Hkv, axis=1)).permute(1, 0, 2),
+        torch.from_numpy(np.repeat(V, Hq // Hkv, axis=1)).permute(1, 0, 2),
+        is_causal=True).permute(1, 0, 2).numpy()
+    for t in range(T):
+        sel = np.arange(t + 1)
+        got = O.attend(q[t], K[sel], V[sel], Hkv)
+        assert np.allclose(got, ref[t], rtol=1e-12, atol=1e-12)
+
+
+def test_attention_single_key_returns_value():
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((8, 32))
+    K = rng.standard_normal((1, 4, 32))
+    V = rng.standard_normal((1, 4, 32))
+    out = O.attend(q, K, V, 4)
+    for h in range(8):
+        assert np.array_equal(out[h], V[0, h // 2])
+
+
+def test_bf16_decode_exact():
+    vals = np.array([1.0, -2.5, 0.0078125, 3.140625, -0.0], dtype=np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(O.bf16_to_f64(bits), vals.astype(np.float64))
+    t = torch.tensor(vals).to(torch.bfloat16)
+    assert np.array_equal(O.bf16_to_f64(t.view(torch.int16).numpy()), t.double().numpy())
