@@ -1,0 +1,493 @@
+// Host side of the C ABI declared in include/lsa.h: argument validation,
+// arena layout, index bookkeeping (all shape decisions are made on the host
+// from T, so no call ever waits on the device) and kernel launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "lsa_internal.h"
+
+using namespace lsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(LSA_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define LSA_HIP(call, where)                         \
+  do {                                               \
+    hipError_t e_ = (call);                          \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_index_params(const lsa_index_params* p) {
+  if (!p) return fail(LSA_E_ARG, "index params are NULL");
+  if (p->dim != kDim) return fail(LSA_E_UNSUPPORTED, "latent dim %d (only 64 is supported)", p->dim);
+  if (p->pool < 1 || p->pool > 64) return fail(LSA_E_ARG, "pool %d not in [1, 64]", p->pool);
+  if (p->block < 64 || p->block > 16384 || p->block % 64)
+    return fail(LSA_E_UNSUPPORTED, "block %d: need a multiple of 64 in [64, 16384]", p->block);
+  if (p->buckets < 16 || p->buckets > 256 || p->buckets % 16 || p->buckets > p->block)
+    return fail(LSA_E_UNSUPPORTED, "buckets %d: need a multiple of 16 in [16, min(256, block)]",
+                p->buckets);
+  if (p->iters < 1) return fail(LSA_E_ARG, "iters %d < 1", p->iters);
+  if (p->tree_group < 0) return fail(LSA_E_ARG, "tree_group %d < 0", p->tree_group);
+  if (p->tree_group > 0) {
+    const int64_t n = (int64_t)p->tree_group * p->buckets;
+    if (n > 16384 || n % 64)
+      return fail(LSA_E_UNSUPPORTED, "tree_group*buckets = %lld: need a multiple of 64 <= 16384",
+                  (long long)n);
+    if (p->tree_super < 16 || p->tree_super > 256 || p->tree_super % 16 || p->tree_super > n)
+      return fail(LSA_E_UNSUPPORTED, "tree_super %d: need a multiple of 16 in [16, 256]",
+                  p->tree_super);
+    if (p->tree_iters < 1) return fail(LSA_E_ARG, "tree_iters %d < 1", p->tree_iters);
+  }
+  if (p->max_tokens < 0 || p->max_tokens > INT32_MAX - 64)
+    return fail(LSA_E_ARG, "max_tokens %lld out of range", (long long)p->max_tokens);
+  return LSA_OK;
+}
+
+// Capacities and arena offsets.
+void layout(const lsa_index_params& p, Index* h) {
+  h->max_pool = p.max_tokens / p.pool;
+  h->max_full = h->max_pool / p.block;
+  h->max_bkt = h->max_full * p.buckets + p.block;
+  h->max_grp = p.tree_group > 0 ? h->max_full / p.tree_group : 0;
+  h->max_sup = h->max_grp * p.tree_super;
+  h->max_smem = h->max_grp * p.tree_group * p.buckets;
+  int64_t o = 0;
+  h->off_pooled = o; o = align_up(o + h->max_pool * kDim);
+  h->off_cent = o;   o = align_up(o + h->max_bkt * kDim);
+  h->off_bcnt = o;   o = align_up(o + h->max_bkt * 4);
+  h->off_boff = o;   o = align_up(o + h->max_bkt * 4);
+  h->off_bmem = o;   o = align_up(o + h->max_pool * 4);
+  h->off_bfirst = o; o = align_up(o + h->max_bkt * 4);
+  h->off_blast = o;  o = align_up(o + h->max_bkt * 4);
+  h->off_scent = o;  o = align_up(o + h->max_sup * kDim);
+  h->off_scnt = o;   o = align_up(o + h->max_sup * 4);
+  h->off_soff = o;   o = align_up(o + h->max_sup * 4);
+  h->off_smem = o;   o = align_up(o + h->max_smem * 4);
+  h->off_leafsup = o; o = align_up(o + (p.tree_group > 0 ? h->max_bkt * 4 : 0));
+  h->off_pend = o;   o = align_up(o + 2 * (int64_t)p.pool * kDim);
+  h->used_bytes = o;
+}
+
+Index* as_index(lsa_index* h) { return reinterpret_cast<Index*>(h); }
+const Index* as_index(const lsa_index* h) { return reinterpret_cast<const Index*>(h); }
+
+int check_index(const Index* h) {
+  if (!h) return fail(LSA_E_ARG, "index is NULL");
+  if (h->magic != kMagic) return fail(LSA_E_STATE, "index descriptor not initialised");
+  return LSA_OK;
+}
+
+int check_select_params(const lsa_select_params* sp, bool tree) {
+  if (!sp) return fail(LSA_E_ARG, "select params are NULL");
+  if (sp->budget < 0 || sp->budget > 4096)
+    return fail(LSA_E_UNSUPPORTED, "budget %d not in [0, 4096]", sp->budget);
+  if (sp->window < 1 || sp->window > (1 << 20)) return fail(LSA_E_ARG, "window %d not in [1, 2^20]", sp->window);
+  if (sp->sinks < 0 || sp->sinks > (1 << 20)) return fail(LSA_E_ARG, "sinks %d not in [0, 2^20]", sp->sinks);
+  if (tree && sp->tree_top < 1) return fail(LSA_E_ARG, "tree_top %d < 1", sp->tree_top);
+  return LSA_OK;
+}
+
+int check_attn_params(const lsa_attn_params* ap) {
+  if (!ap) return fail(LSA_E_ARG, "attention params are NULL");
+  if (ap->D != 64 && ap->D != 128) return fail(LSA_E_UNSUPPORTED, "head dim %d (64 or 128)", ap->D);
+  if (ap->Hkv < 1 || ap->Hq < 1 || ap->Hq % ap->Hkv)
+    return fail(LSA_E_UNSUPPORTED, "Hq %d must be a positive multiple of Hkv %d", ap->Hq, ap->Hkv);
+  if (ap->Hq / ap->Hkv > 16) return fail(LSA_E_UNSUPPORTED, "Hq/Hkv %d > 16", ap->Hq / ap->Hkv);
+  if (!(ap->scale >= 0.f) || isinf(ap->scale)) return fail(LSA_E_ARG, "bad scale");
+  return LSA_OK;
+}
+
+int32_t max_sel_of(const lsa_select_params* sp) { return sp->budget + sp->window + sp->sinks; }
+
+IdxView view_of(const Index* h) {
+  IdxView v;
+  memset(&v, 0, sizeof v);
+  v.cent = h->at<int8_t>(h->off_cent);
+  v.bcnt = h->at<int32_t>(h->off_bcnt);
+  v.boff = h->at<int32_t>(h->off_boff);
+  v.bmem = h->at<int32_t>(h->off_bmem);
+  v.bfirst = h->at<int32_t>(h->off_bfirst);
+  v.blast = h->at<int32_t>(h->off_blast);
+  v.n_bkt = (int32_t)h->n_bkt();
+  v.pool = h->prm.pool;
+  v.dense = 0;
+  if (h->prm.tree_group > 0 && h->n_grp > 0) {
+    v.leafsup = h->at<int32_t>(h->off_leafsup);
+    v.n_sup = (int32_t)(h->n_grp * h->prm.tree_super);
+    v.scent = h->at<int8_t>(h->off_scent);
+  }
+  return v;
+}
+
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+// Append n latent rows (device) to the index.  Shapes come from host counters.
+int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
+  const lsa_index_params& P = h->prm;
+  const int p = P.pool, N = P.block, C = P.buckets;
+  if (h->T + n > P.max_tokens)
+    return fail(LSA_E_CAPACITY, "T %lld + %lld exceeds capacity %lld", (long long)h->T,
+                (long long)n, (long long)P.max_tokens);
+  if (n == 0) return LSA_OK;
+  const int n_pend = (int)(h->T - h->n_pool * p);
+  int8_t* pend = h->at<int8_t>(h->off_pend) + (int64_t)h->pend_slot * p * kDim;
+  int8_t* pend2 = h->at<int8_t>(h->off_pend) + (int64_t)(h->pend_slot ^ 1) * p * kDim;
+  const int64_t total = n_pend + n;
+  const int64_t newg = total / p;
+  const int keep = (int)(total % p);
+  const int64_t g0 = h->n_pool;
+  int8_t* pooled = h->at<int8_t>(h->off_pooled);
+  LSA_HIP(launch_pool(pend, n_pend, src, n, p, pooled + g0 * kDim, newg, s), "pool");
+  LSA_HIP(launch_save_pending(pend, n_pend, src, n, keep, pend2, s), "pending");
+
+  const int64_t n_pool = g0 + newg;
+  const int64_t nf_old = h->n_full, nf_new = n_pool / N;
+  int8_t* cent = h->at<int8_t>(h->off_cent);
+  int32_t* bcnt = h->at<int32_t>(h->off_bcnt);
+  int32_t* boff = h->at<int32_t>(h->off_boff);
+  int32_t* bmem = h->at<int32_t>(h->off_bmem);
+  int32_t* bfirst = h->at<int32_t>(h->off_bfirst);
+  int32_t* blast = h->at<int32_t>(h->off_blast);
+  if (nf_new > nf_old) {
+    LSA_HIP(launch_kmeans(pooled + nf_old * N * kDim, N, C, P.iters, (int32_t)(nf_new - nf_old),
+                          nf_old * N, cent + nf_old * C * kDim, bcnt + nf_old * C,
+                          boff + nf_old * C, bmem + nf_old * N, bfirst + nf_old * C,
+                          blast + nf_old * C, nullptr, 0, s),
+            "kmeans");
+  }
+  const int64_t t0 = nf_new == nf_old ? g0 : nf_new * N;
+  LSA_HIP(launch_tail(pooled, t0, n_pool, nf_new, N, C, cent, bcnt, boff, bmem, bfirst, blast, s),
+          "tail");
+  int64_t ng_new = h->n_grp;
+  if (P.tree_group > 0) {
+    const int G = P.tree_group, S = P.tree_super;
+    ng_new = nf_new / G;
+    if (ng_new > h->n_grp) {
+      const int64_t g = h->n_grp;
+      const int64_t NL = (int64_t)G * C;
+      LSA_HIP(launch_kmeans(cent + g * NL * kDim, (int32_t)NL, S, P.tree_iters,
+                            (int32_t)(ng_new - g), g * NL, h->at<int8_t>(h->off_scent) + g * S * kDim,
+                            h->at<int32_t>(h->off_scnt) + g * S, h->at<int32_t>(h->off_soff) + g * S,
+                            h->at<int32_t>(h->off_smem) + g * NL, nullptr, nullptr,
+                            h->at<int32_t>(h->off_leafsup), (int32_t)(g * S), s),
+              "tree kmeans");
+    }
+  }
+  h->T += n;
+  h->n_pool = n_pool;
+  h->n_full = nf_new;
+  h->n_grp = ng_new;
+  h->pend_slot ^= 1;
+  return LSA_OK;
+}
+
+int select_impl(const Index* h, const int8_t* latq, const int32_t* qpos, int32_t qpos_base,
+                int32_t nq, const lsa_select_params* sp, int32_t* idx, int32_t* cnt,
+                hipStream_t s) {
+  IdxView v = view_of(h);
+  if (v.leafsup && v.n_sup > 2048)
+    return fail(LSA_E_UNSUPPORTED, "%d super clusters (at most 2048)", v.n_sup);
+  SelArgs a;
+  a.latq = latq; a.qpos = qpos; a.qpos_base = qpos_base; a.nq = nq;
+  a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
+  a.max_sel = max_sel_of(sp);
+  a.idx = idx; a.cnt = cnt;
+  LSA_HIP(launch_select(v, a, nullptr, s), "select");
+  return LSA_OK;
+}
+
+constexpr int kDecodeSplits = 32;
+
+}  // namespace
+
+extern "C" {
+
+const char* lsa_status_str(int status) {
+  switch (status) {
+    case LSA_OK: return "ok";
+    case LSA_E_ARG: return "invalid argument";
+    case LSA_E_UNSUPPORTED: return "unsupported shape or parameter";
+    case LSA_E_CAPACITY: return "capacity exceeded";
+    case LSA_E_STATE: return "bad index state";
+    case LSA_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* lsa_last_error(void) { return g_err.c_str(); }
+
+size_t lsa_index_sizeof(void) { return kIndexSizeof; }
+
+int lsa_index_bytes(const lsa_index_params* prm, size_t* bytes) {
+  if (int e = check_index_params(prm)) return e;
+  if (!bytes) return fail(LSA_E_ARG, "bytes is NULL");
+  Index tmp;
+  memset(&tmp, 0, sizeof tmp);
+  layout(*prm, &tmp);
+  *bytes = (size_t)tmp.used_bytes;
+  return LSA_OK;
+}
+
+int lsa_index_init(lsa_index* hh, const lsa_index_params* prm, void* d_arena, size_t arena_bytes) {
+  if (!hh) return fail(LSA_E_ARG, "index is NULL");
+  if (int e = check_index_params(prm)) return e;
+  if (!d_arena) return fail(LSA_E_ARG, "arena is NULL");
+  if (reinterpret_cast<uintptr_t>(d_arena) % kAlign) return fail(LSA_E_ARG, "arena not 256-byte aligned");
+  Index tmp;
+  memset(&tmp, 0, sizeof tmp);
+  layout(*prm, &tmp);
+  if ((int64_t)arena_bytes < tmp.used_bytes)
+    return fail(LSA_E_CAPACITY, "arena %zu bytes < %lld needed", arena_bytes, (long long)tmp.used_bytes);
+  tmp.magic = kMagic;
+  tmp.prm = *prm;
+  tmp.arena = static_cast<char*>(d_arena);
+  tmp.arena_bytes = arena_bytes;
+  memset(hh, 0, kIndexSizeof);
+  memcpy(hh, &tmp, sizeof tmp);
+  return LSA_OK;
+}
+
+int lsa_index_get_info(const lsa_index* hh, lsa_index_info* out) {
+  const Index* h = as_index(hh);
+  if (int e = check_index(h)) return e;
+  if (!out) return fail(LSA_E_ARG, "info is NULL");
+  out->T = h->T; out->n_pool = h->n_pool; out->n_full = h->n_full; out->n_bkt = h->n_bkt();
+  out->n_grp = h->n_grp; out->n_sup = h->n_grp * h->prm.tree_super;
+  out->off_pooled = h->off_pooled; out->off_cent = h->off_cent; out->off_bcnt = h->off_bcnt;
+  out->off_boff = h->off_boff; out->off_bmem = h->off_bmem; out->off_bfirst = h->off_bfirst;
+  out->off_blast = h->off_blast; out->off_scent = h->off_scent; out->off_scnt = h->off_scnt;
+  out->off_soff = h->off_soff; out->off_smem = h->off_smem;
+  out->arena_bytes = h->used_bytes;
+  return LSA_OK;
+}
+
+int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_params* sprm,
+                        const lsa_attn_params* aprm, int64_t n, size_t* bytes) {
+  if (!bytes) return fail(LSA_E_ARG, "bytes is NULL");
+  if (n < 0) return fail(LSA_E_ARG, "n < 0");
+  (void)iprm;
+  switch (op) {
+    case LSA_OP_BUILD: case LSA_OP_APPEND: case LSA_OP_SELECT: case LSA_OP_ATTN: case LSA_OP_DENSE:
+      *bytes = 0;
+      return LSA_OK;
+    case LSA_OP_PREFILL: {
+      if (int e = check_select_params(sprm, false)) return e;
+      *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4);
+      return LSA_OK;
+    }
+    case LSA_OP_DECODE: {
+      if (int e = check_select_params(sprm, false)) return e;
+      if (int e = check_attn_params(aprm)) return e;
+      *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4) +
+               (size_t)align_up((int64_t)attn_ws_bytes((int32_t)n, *aprm, kDecodeSplits));
+      return LSA_OK;
+    }
+    default:
+      return fail(LSA_E_ARG, "unknown op %d", op);
+  }
+}
+
+int lsa_build_index(lsa_index* hh, const int8_t* d_latk, int64_t T, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  (void)d_ws; (void)ws_bytes;
+  Index* h = as_index(hh);
+  if (int e = check_index(h)) return e;
+  if (T < 0) return fail(LSA_E_ARG, "T < 0");
+  if (T > 0 && !d_latk) return fail(LSA_E_ARG, "latents are NULL");
+  if (T > h->prm.max_tokens)
+    return fail(LSA_E_CAPACITY, "T %lld exceeds capacity %lld", (long long)T,
+                (long long)h->prm.max_tokens);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Index saved = *h;
+  h->T = 0; h->n_pool = 0; h->n_full = 0; h->n_grp = 0; h->pend_slot = 0;
+  if (h->prm.tree_group > 0) {
+    hipError_t e = fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s);
+    if (e != hipSuccess) { *h = saved; return hip_fail(e, "fill"); }
+  }
+  int rc = append_impl(h, d_latk, T, s);
+  if (rc != LSA_OK) *h = saved;
+  return rc;
+}
+
+int lsa_append_keys(lsa_index* hh, const int8_t* d_latk_new, int64_t n, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  (void)d_ws; (void)ws_bytes;
+  Index* h = as_index(hh);
+  if (int e = check_index(h)) return e;
+  if (n < 0) return fail(LSA_E_ARG, "n < 0");
+  if (n > 0 && !d_latk_new) return fail(LSA_E_ARG, "latents are NULL");
+  if (h->T == 0 && h->prm.tree_group > 0) {
+    hipError_t e = fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fill");
+  }
+  Index saved = *h;
+  int rc = append_impl(h, d_latk_new, n, static_cast<hipStream_t>(stream));
+  if (rc != LSA_OK) *h = saved;
+  return rc;
+}
+
+int lsa_select(const lsa_index* hh, const int8_t* d_latq, const int32_t* d_qpos, int32_t nq,
+               const lsa_select_params* sp, int32_t* d_idx, int32_t* d_cnt, void* d_ws,
+               size_t ws_bytes, void* stream) {
+  (void)d_ws; (void)ws_bytes;
+  const Index* h = as_index(hh);
+  if (int e = check_index(h)) return e;
+  if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
+  if (nq < 0) return fail(LSA_E_ARG, "nq < 0");
+  if (nq > 0 && (!d_latq || !d_qpos || !d_idx || !d_cnt)) return fail(LSA_E_ARG, "NULL buffer");
+  return select_impl(h, d_latq, d_qpos, 0, nq, sp, d_idx, d_cnt, static_cast<hipStream_t>(stream));
+}
+
+int lsa_sparse_attn(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v, int64_t kv_rows,
+                    const int32_t* d_idx, const int32_t* d_cnt, int32_t max_sel, int32_t nq,
+                    const lsa_attn_params* ap, void* d_out, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  (void)d_ws; (void)ws_bytes;
+  if (int e = check_attn_params(ap)) return e;
+  if (nq < 0 || max_sel < 1 || kv_rows < 1) return fail(LSA_E_ARG, "bad nq / max_sel / kv_rows");
+  if (nq > 0 && (!d_q || !d_k || !d_v || !d_idx || !d_cnt || !d_out)) return fail(LSA_E_ARG, "NULL buffer");
+  LSA_HIP(launch_attn(d_q, d_k, d_v, kv_rows, 0, nq > 0 ? nq : 1, d_idx, d_cnt, max_sel, nq, *ap,
+                      d_out, nullptr, 1, static_cast<hipStream_t>(stream)),
+          "attention");
+  return LSA_OK;
+}
+
+int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk,
+                      const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
+                      const uint16_t* d_v, int64_t kv_rows, const lsa_select_params* sp,
+                      const lsa_attn_params* ap, void* d_out, int32_t* d_idx_opt,
+                      int32_t* d_cnt_opt, void* d_ws, size_t ws_bytes, void* stream) {
+  Index* h = as_index(hh);
+  if (int e = check_index(h)) return e;
+  if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
+  if (int e = check_attn_params(ap)) return e;
+  if (n_chunk < 0 || n_chunk > INT32_MAX / 2) return fail(LSA_E_ARG, "bad n_chunk");
+  if (n_chunk == 0) return LSA_OK;
+  if (!d_latk_chunk || !d_latq || !d_q || !d_k || !d_v || !d_out) return fail(LSA_E_ARG, "NULL buffer");
+  if (kv_rows < h->T + n_chunk) return fail(LSA_E_ARG, "kv_rows %lld < T + n_chunk", (long long)kv_rows);
+  if (h->T + n_chunk > h->prm.max_tokens) return fail(LSA_E_CAPACITY, "chunk exceeds capacity");
+  const int32_t max_sel = max_sel_of(sp);
+  int32_t* idx = d_idx_opt;
+  int32_t* cnt = d_cnt_opt;
+  const size_t need = (size_t)align_up(n_chunk * max_sel * 4) + (size_t)align_up(n_chunk * 4);
+  if (!idx || !cnt) {
+    if (!d_ws || ws_bytes < need) return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+    idx = static_cast<int32_t*>(d_ws);
+    cnt = reinterpret_cast<int32_t*>(static_cast<char*>(d_ws) + align_up(n_chunk * max_sel * 4));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t t0 = h->T;
+  if (h->T == 0 && h->prm.tree_group > 0) {
+    LSA_HIP(fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s), "fill");
+  }
+  Index saved = *h;
+  int rc = append_impl(h, d_latk_chunk, n_chunk, s);
+  if (rc != LSA_OK) { *h = saved; return rc; }
+  rc = select_impl(h, d_latq, nullptr, (int32_t)t0, (int32_t)n_chunk, sp, idx, cnt, s);
+  if (rc != LSA_OK) return rc;
+  LSA_HIP(launch_attn(d_q, d_k, d_v, kv_rows, 0, (int32_t)n_chunk, idx, cnt, max_sel,
+                      (int32_t)n_chunk, *ap, d_out, nullptr, 1, s),
+          "attention");
+  return LSA_OK;
+}
+
+int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new,
+                    const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
+                    const uint16_t* d_v, int64_t seq_stride_rows, const lsa_select_params* sp,
+                    const lsa_attn_params* ap, void* d_out, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  if (!hs || nseq < 1 || nseq > 16) return fail(LSA_E_ARG, "nseq %d not in [1, 16]", nseq);
+  if (int e = check_attn_params(ap)) return e;
+  if (!d_latk_new || !d_latq || !d_q || !d_k || !d_v || !d_out) return fail(LSA_E_ARG, "NULL buffer");
+  for (int i = 0; i < nseq; ++i) {
+    const Index* h = as_index(hs[i]);
+    if (int e = check_index(h)) return e;
+    if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
+    if (h->T + 1 > h->prm.max_tokens) return fail(LSA_E_CAPACITY, "sequence %d is full", i);
+    if (seq_stride_rows < h->T + 1) return fail(LSA_E_ARG, "seq_stride_rows < T + 1 for sequence %d", i);
+    for (int j = 0; j < i; ++j)
+      if (hs[j] == hs[i]) return fail(LSA_E_ARG, "sequence %d repeats an index", i);
+  }
+  const int32_t max_sel = max_sel_of(sp);
+  const size_t a_idx = (size_t)align_up((int64_t)nseq * max_sel * 4);
+  const size_t a_cnt = (size_t)align_up((int64_t)nseq * 4);
+  const size_t a_att = (size_t)align_up((int64_t)attn_ws_bytes(nseq, *ap, kDecodeSplits));
+  if (!d_ws || ws_bytes < a_idx + a_cnt + a_att)
+    return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, a_idx + a_cnt + a_att);
+  char* ws = static_cast<char*>(d_ws);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + a_idx);
+  void* att = ws + a_idx + a_cnt;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < nseq; ++i) {
+    Index* h = as_index(hs[i]);
+    const int64_t t = h->T;
+    if (h->T == 0 && h->prm.tree_group > 0)
+      LSA_HIP(fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s), "fill");
+    Index saved = *h;
+    int rc = append_impl(h, d_latk_new + (int64_t)i * kDim, 1, s);
+    if (rc != LSA_OK) { *h = saved; return rc; }
+    rc = select_impl(h, d_latq + (int64_t)i * kDim, nullptr, (int32_t)t, 1, sp,
+                     idx + (int64_t)i * max_sel, cnt + i, s);
+    if (rc != LSA_OK) return rc;
+  }
+  LSA_HIP(launch_attn(d_q, d_k, d_v, seq_stride_rows, seq_stride_rows, 1, idx, cnt, max_sel,
+                      nseq, *ap, d_out, att, kDecodeSplits, s),
+          "decode attention");
+  return LSA_OK;
+}
+
+int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, const int32_t* d_qpos,
+                     int32_t nq, const lsa_select_params* sp, int32_t* d_idx, int32_t* d_cnt,
+                     void* d_ws, size_t ws_bytes, void* stream) {
+  (void)d_ws; (void)ws_bytes;
+  if (int e = check_select_params(sp, false)) return e;
+  if (T < 0 || T > INT32_MAX - 64 || nq < 0) return fail(LSA_E_ARG, "bad T / nq");
+  if (nq > 0 && (!d_latk || !d_latq || !d_qpos || !d_idx || !d_cnt)) return fail(LSA_E_ARG, "NULL buffer");
+  IdxView v;
+  memset(&v, 0, sizeof v);
+  v.cent = d_latk;
+  v.n_bkt = (int32_t)T;
+  v.pool = 1;
+  v.dense = 1;
+  SelArgs a;
+  a.latq = d_latq; a.qpos = d_qpos; a.qpos_base = 0; a.nq = nq;
+  a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = 0;
+  a.max_sel = max_sel_of(sp);
+  a.idx = d_idx; a.cnt = d_cnt;
+  LSA_HIP(launch_select(v, a, nullptr, static_cast<hipStream_t>(stream)), "dense select");
+  return LSA_OK;
+}
+
+}  // extern "C"

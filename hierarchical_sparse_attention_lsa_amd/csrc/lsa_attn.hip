@@ -1,0 +1,319 @@
+// Sparse GQA attention over the selected K/V rows.
+//
+// "Prefrontal's Latent Sparse Attention speeds up one attention layer 72x at
+// 10M tokens" (sysnote.net), section "What it changes": the attention itself
+// is unchanged and runs over a fixed number of keys whatever the context
+// length; LSA only decides which keys are read.  "Latent Sparse Attention:
+// un indice gerarchico per contesti lunghi" (mauroscia.it), search
+// paragraph: attention is computed on the selected keys and values; the KV
+// cache keeps the original representations.
+//
+// Design (gfx950): one wave owns one (query token, KV head) pair and walks
+// its selected rows 16 at a time.  K rows go straight from HBM into the A
+// operand of v_mfma_f32_16x16x32_bf16 (keys on M, head dim on K), with the
+// group's query heads as the B operand (N = 16 padded heads), so the output
+// tile is S^T [16 keys][16 heads] and each lane already holds the four
+// probabilities it must feed, as the A operand, to the 16x16x16 PV product.
+// V rows are staged through LDS (per-wave region, no workgroup barrier) and
+// read back key-major for the B operand.  Softmax runs online in fp32 with
+// exp2; P enters the PV product as bf16 hi + bf16 lo so that the probability
+// rounding stays far below the output tolerance.  The eight waves of a
+// workgroup take the eight KV heads of one query, so each 2 KiB K/V row is
+// fetched by one workgroup at once.  Workgroups are remapped so that each
+// XCD (own L2) walks a contiguous range of queries, whose recent windows
+// overlap.
+#include <climits>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+
+namespace {
+
+constexpr int AW = 8;            // waves per workgroup
+constexpr int AT = AW * 64;
+constexpr int KT = 16;           // keys per tile
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t kv_rows;           // rows per sequence (clamp bound of key ids)
+  int64_t seq_stride_rows;   // rows between sequences (decode)
+  int32_t qdiv;              // query -> sequence divisor
+  const int32_t* idx;
+  const int32_t* cnt;
+  int32_t max_sel;
+  int32_t nq;
+  int32_t Hq, Hkv, G;
+  int32_t splits;
+  float scale_log2;          // softmax scale * log2(e)
+  void* out;
+  float* part_o;             // [items][16][D] unnormalised partial outputs (split mode)
+  float* part_ml;            // [items][16][2] running max (log2 domain) and sum
+};
+
+__device__ __forceinline__ int xcd_remap(int b, int nwg) {
+  const int per = nwg >> 3, rem = nwg & 7, x = b & 7, k = b >> 3;
+  return x * per + min(x, rem) + k;
+}
+
+template <int D, bool OUT_F32, bool SPLIT>
+__global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
+  constexpr int NKK = D / 32;         // 32-deep slices of the head dim
+  constexpr int NB = D / 16;          // 16-wide output column blocks
+  constexpr int VROW = D * 2 + 16;    // padded LDS row (bytes)
+  constexpr int VCH = D / 8;          // 16-byte chunks per row
+  constexpr int VLD = KT * VCH / 64;  // 16-byte V loads per lane per tile
+  __shared__ __attribute__((aligned(16))) char vlds[AW][KT * VROW];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int nwg = gridDim.x;
+  const int item = xcd_remap(blockIdx.x, nwg) * AW + wave;
+  const int nitems = a.nq * a.Hkv * a.splits;
+  if (item >= nitems) return;
+  const int split = item % a.splits;
+  const int qg = item / a.splits;
+  const int q = qg / a.Hkv;
+  const int g = qg % a.Hkv;
+  const int G = a.G;
+  const int hl = lane & 15;           // head (S^T column) / key row for K loads
+  const int grp = lane >> 4;
+
+  const int cnt = min(a.cnt[q], a.max_sel);
+  int kbeg = 0, kend = cnt;
+  if (SPLIT) {
+    const int ch = ((cnt + a.splits - 1) / a.splits + KT - 1) / KT * KT;
+    kbeg = min(cnt, split * ch);
+    kend = min(cnt, kbeg + ch);
+  }
+  const int64_t rowbase = (int64_t)(q / a.qdiv) * a.seq_stride_rows;
+  const int64_t rowstride = (int64_t)a.Hkv * D;        // elements per K/V row
+  const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
+
+  // query heads of this group as the B operand (zero for padded heads)
+  v8bf qb[NKK];
+  {
+    const bool hv = hl < G;
+    const uint16_t* qp = a.q + ((int64_t)q * a.Hq + (int64_t)g * G + (hv ? hl : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      v4i raw = hv ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
+      qb[kk] = __builtin_bit_cast(v8bf, raw);
+    }
+  }
+
+  v4f o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;    // stats of head hl (replicated over grp)
+
+  char* vl = vlds[wave];
+  const uint16_t* kbase = a.k + (rowbase * a.Hkv + g) * D;
+  const uint16_t* vbase = a.v + (rowbase * a.Hkv + g) * D;
+  const int64_t rmax = a.kv_rows - 1;                 // rows of one sequence
+
+  for (int kb = kbeg; kb < kend; kb += KT) {
+    // selected rows of this tile: lane l holds key slot kb + (l % 16)
+    const int slot = kb + hl;
+    int r = slot < kend ? idxrow[slot] : 0;
+    r = (int)min((int64_t)max(r, 0), rmax);
+
+    // K rows -> A operand
+    v8bf ka[NKK];
+    {
+      const uint16_t* kp = kbase + (int64_t)r * rowstride + 8 * grp;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        ka[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * kk));
+    }
+    // V rows -> LDS (row key, 16-byte chunk c)
+    v4i vr[VLD];
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int c = i * 64 + lane;
+      const int key = c / VCH, ch = c % VCH;
+      const int rv = __shfl(r, key);
+      vr[i] = *reinterpret_cast<const v4i*>(vbase + (int64_t)rv * rowstride + ch * 8);
+    }
+
+    // S^T[key][head]
+    v4f s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_16x16x32(ka[kk], qb[kk], s);
+
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int c = i * 64 + lane;
+      const int key = c / VCH, ch = c % VCH;
+      *reinterpret_cast<v4i*>(vl + key * VROW + ch * 16) = vr[i];
+    }
+
+    // online softmax for head hl over keys 4*grp + v
+    float sv[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int key = kb + 4 * grp + v;
+      sv[v] = key < kend ? s[v] * a.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sv[v]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    float p[4], psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) { p[v] = exp2f(sv[v] - m_new); psum += p[v]; }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // P (A operand, rows = heads, k = keys 4*grp..+3) as bf16 hi + lo
+    v4s phi, plo;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t hb = f32_to_bf16_bits(p[v]);
+      const float rem = p[v] - bf16_bits_to_f32(hb);
+      phi[v] = (short)hb;
+      plo[v] = (short)f32_to_bf16_bits(rem);
+    }
+    // rescale the accumulators: o rows are heads 4*grp + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float av = __shfl(alpha, 4 * grp + v);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nb][v] *= av;
+    }
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // O += P V, V^T operand read key-major from LDS
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const char* vp = vl + (4 * grp) * VROW + (16 * nb + hl) * 2;
+      v4s vb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vb[e] = *reinterpret_cast<const short*>(vp + e * VROW);
+      o[nb] = mfma_bf16_16x16x16(phi, vb, o[nb]);
+      o[nb] = mfma_bf16_16x16x16(plo, vb, o[nb]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  if (SPLIT) {
+    float* po = a.part_o + (int64_t)item * 16 * D;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 4 * grp + v;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) po[h * D + 16 * nb + hl] = o[nb][v];
+    }
+    if (grp == 0) {
+      a.part_ml[(int64_t)item * 32 + 2 * hl] = m_run;
+      a.part_ml[(int64_t)item * 32 + 2 * hl + 1] = l_run;
+    }
+    return;
+  }
+
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int h = 4 * grp + v;
+    const float lh = __shfl(l_run, h);
+    if (h >= G) continue;
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const int64_t ob = ((int64_t)q * a.Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float val = o[nb][v] * inv;
+      if (OUT_F32) reinterpret_cast<float*>(a.out)[ob + 16 * nb + hl] = val;
+      else reinterpret_cast<uint16_t*>(a.out)[ob + 16 * nb + hl] = (uint16_t)f32_to_bf16_bits(val);
+    }
+  }
+}
+
+// Combine split partial results: out[q][head][d].
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(D) k_attn_merge(AttnArgs a) {
+  const int qh = blockIdx.x;            // q * Hq + head
+  const int d = threadIdx.x;
+  const int q = qh / a.Hq, head = qh % a.Hq;
+  const int g = head / a.G, h = head % a.G;
+  const int64_t it0 = ((int64_t)q * a.Hkv + g) * a.splits;
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(it0 + s) * 32 + 2 * h]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const float ms = a.part_ml[(it0 + s) * 32 + 2 * h];
+    const float ls = a.part_ml[(it0 + s) * 32 + 2 * h + 1];
+    if (ls <= 0.f) continue;
+    const float w = exp2f(ms - M);
+    num += w * a.part_o[(it0 + s) * 16 * D + h * D + d];
+    den += w * ls;
+  }
+  const float val = den > 0.f ? num / den : 0.f;
+  const int64_t ob = (int64_t)qh * D + d;
+  if (OUT_F32) reinterpret_cast<float*>(a.out)[ob] = val;
+  else reinterpret_cast<uint16_t*>(a.out)[ob] = (uint16_t)f32_to_bf16_bits(val);
+}
+
+}  // namespace
+
+size_t attn_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t splits) {
+  if (splits <= 1) return 0;
+  const size_t items = (size_t)nq * ap.Hkv * splits;
+  return items * 16 * ap.D * sizeof(float) + items * 32 * sizeof(float);
+}
+
+hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_rows,
+                       int64_t seq_stride_rows, int32_t qdiv, const int32_t* idx,
+                       const int32_t* cnt, int32_t max_sel, int32_t nq, const lsa_attn_params& ap,
+                       void* out, void* ws, int32_t splits, hipStream_t s) {
+  if (nq <= 0) return hipSuccess;
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.kv_rows = kv_rows; a.seq_stride_rows = seq_stride_rows;
+  a.qdiv = qdiv > 0 ? qdiv : 1;
+  a.idx = idx; a.cnt = cnt; a.max_sel = max_sel; a.nq = nq;
+  a.Hq = ap.Hq; a.Hkv = ap.Hkv; a.G = ap.Hq / ap.Hkv;
+  a.splits = splits > 1 ? splits : 1;
+  const float scale = ap.scale > 0.f ? ap.scale : 1.0f / sqrtf((float)ap.D);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  const size_t items = (size_t)nq * ap.Hkv * a.splits;
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_ml = a.part_o ? a.part_o + items * 16 * ap.D : nullptr;
+  const unsigned grid = (unsigned)((items + AW - 1) / AW);
+  const bool f32 = ap.out_f32 != 0;
+  if (a.splits > 1) {
+    if (ap.D == 128) hipLaunchKernelGGL((k_attn<128, false, true>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<64, false, true>), dim3(grid), dim3(AT), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned mg = (unsigned)(nq * ap.Hq);
+    if (ap.D == 128) {
+      if (f32) hipLaunchKernelGGL((k_attn_merge<128, true>), dim3(mg), dim3(128), 0, s, a);
+      else hipLaunchKernelGGL((k_attn_merge<128, false>), dim3(mg), dim3(128), 0, s, a);
+    } else {
+      if (f32) hipLaunchKernelGGL((k_attn_merge<64, true>), dim3(mg), dim3(64), 0, s, a);
+      else hipLaunchKernelGGL((k_attn_merge<64, false>), dim3(mg), dim3(64), 0, s, a);
+    }
+    return hipGetLastError();
+  }
+  if (ap.D == 128) {
+    if (f32) hipLaunchKernelGGL((k_attn<128, true, false>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<128, false, false>), dim3(grid), dim3(AT), 0, s, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((k_attn<64, true, false>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<64, false, false>), dim3(grid), dim3(AT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lsa

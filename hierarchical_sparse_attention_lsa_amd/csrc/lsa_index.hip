@@ -1,0 +1,317 @@
+// Index build kernels: pooling, per-block integer k-means with member lists,
+// tail singleton buckets.
+//
+// Follows "Latent Sparse Attention: un indice gerarchico per contesti lunghi"
+// (mauroscia.it), paragraph on the index: small groups of consecutive keys
+// are pooled, the pooled sequence is cut into blocks, the vectors of a block
+// are grouped by similarity into buckets, and each bucket keeps a centroid
+// and the indices of its original keys.  The same k-means kernel builds the
+// upper level of the hierarchy ("Prefrontal's Latent Sparse Attention speeds
+// up one attention layer 72x at 10M tokens", section "What it changes") by
+// clustering the leaf centroids of a group of blocks.
+#include <climits>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+
+// ---------------------------------------------------------------- pooling
+// Pooled vector g = round-half-even mean of rows g*p .. g*p+p-1 of the
+// virtual sequence (pend[0..n_pend) ++ src[0..n_src)).  One thread per
+// (pooled vector, 4 dims): 16 threads read a 64-byte row.
+__global__ void __launch_bounds__(256) k_pool(const int8_t* __restrict__ pend, int n_pend,
+                                              const int8_t* __restrict__ src, int p,
+                                              int8_t* __restrict__ out, int64_t n_groups) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t g = t >> 4;
+  const int c = (int)(t & 15) * 4;
+  if (g >= n_groups) return;
+  int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+  for (int r = 0; r < p; ++r) {
+    const int64_t row = g * p + r;
+    const int8_t* rp = row < n_pend ? pend + row * kDim : src + (row - n_pend) * kDim;
+    const char4 v = *reinterpret_cast<const char4*>(rp + c);
+    s0 += v.x; s1 += v.y; s2 += v.z; s3 += v.w;
+  }
+  char4 o;
+  o.x = (signed char)rhe_div(s0, p);
+  o.y = (signed char)rhe_div(s1, p);
+  o.z = (signed char)rhe_div(s2, p);
+  o.w = (signed char)rhe_div(s3, p);
+  *reinterpret_cast<char4*>(out + g * kDim + c) = o;
+}
+
+// Copy the last `keep` rows of (pend ++ src) into dst.
+__global__ void k_save_pending(const int8_t* __restrict__ pend, int n_pend,
+                               const int8_t* __restrict__ src, int64_t n_src, int keep,
+                               int8_t* __restrict__ dst) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= keep * kDim) return;
+  const int r = t / kDim, c = t % kDim;
+  const int64_t row = (int64_t)n_pend + n_src - keep + r;
+  dst[t] = row < n_pend ? pend[row * kDim + c] : src[(row - n_pend) * kDim + c];
+}
+
+// ---------------------------------------------------------------- tail
+// Pooled vectors g0 .. g1-1 of the partial tail block become singleton
+// buckets with id n_full*C + (g - n_full*N).
+__global__ void k_tail(const int8_t* __restrict__ pooled, int64_t g0, int64_t g1, int64_t n_full,
+                       int N, int C, int8_t* __restrict__ cent, int32_t* __restrict__ bcnt,
+                       int32_t* __restrict__ boff, int32_t* __restrict__ bmem,
+                       int32_t* __restrict__ bfirst, int32_t* __restrict__ blast) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t g = g0 + (t >> 2);
+  if (g >= g1) return;
+  const int part = (int)(t & 3);
+  const int64_t beta = n_full * C + (g - n_full * N);
+  reinterpret_cast<int4*>(cent + beta * kDim)[part] =
+      reinterpret_cast<const int4*>(pooled + g * kDim)[part];
+  if (part == 0) {
+    bcnt[beta] = 1;
+    boff[beta] = (int32_t)g;
+    bmem[g] = (int32_t)g;
+    bfirst[beta] = (int32_t)g;
+    blast[beta] = (int32_t)g;
+  }
+}
+
+// ---------------------------------------------------------------- k-means
+// One workgroup clusters one block of N vectors (int8 [N][64]) into C
+// centroids with `iters` Lloyd iterations:
+//   init     mu_c = X[c * (N / C)]
+//   assign   a_i = argmin_c |X_i - mu_c|^2 (lowest c on ties), evaluated as
+//            |mu_c|^2 - 2 X_i . mu_c with int8 MFMA (exact int32)
+//   update   mu_c = round-half-even(sum of members / count) when non-empty
+// then writes a stable member list (members of each cluster in ascending
+// row order), counts, offsets, first/last member and the centroids.
+constexpr int kKmWaves = 8;
+constexpr int kKmThreads = kKmWaves * 64;
+
+__host__ __device__ inline size_t kmeans_lds_bytes(int N, int C) {
+  size_t b = 0;
+  b += (size_t)C * kDim;                 // mu int8
+  b += (size_t)C * 4;                    // |mu|^2
+  b += (size_t)C * kDim * 4;             // sums (reused for first/last rows)
+  b += (size_t)C * 4;                    // counts
+  b += (size_t)C * 4;                    // exclusive offsets
+  b += (size_t)kKmWaves * C * 4;         // per-wave counts / cursors
+  b += ((size_t)N * 2 + 15) / 16 * 16;   // assignments (uint16)
+  return b;
+}
+
+__global__ void __launch_bounds__(kKmThreads)
+k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0,
+         int8_t* __restrict__ cent_all, int32_t* __restrict__ cnt_all,
+         int32_t* __restrict__ off_all, int32_t* __restrict__ mem_all,
+         int32_t* __restrict__ first_all, int32_t* __restrict__ last_all,
+         int32_t* __restrict__ map_all, int32_t map_base) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int8_t* mu = reinterpret_cast<int8_t*>(smem);
+  int32_t* musq = reinterpret_cast<int32_t*>(mu + (size_t)C * kDim);
+  int32_t* sums = musq + C;
+  int32_t* counts = sums + C * kDim;
+  int32_t* offs = counts + C;
+  int32_t* cw = offs + C;
+  uint16_t* assign = reinterpret_cast<uint16_t*>(cw + kKmWaves * C);
+
+  const int blk = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int8_t* X = X_all + (int64_t)blk * N * kDim;
+  const int stride = N / C;
+
+  // init at strided members
+  for (int e = tid; e < C * 4; e += kKmThreads) {
+    const int c = e >> 2, part = e & 3;
+    reinterpret_cast<int4*>(mu + c * kDim)[part] =
+        reinterpret_cast<const int4*>(X + (int64_t)c * stride * kDim)[part];
+  }
+  __syncthreads();
+
+  for (int it = 0; it < iters; ++it) {
+    for (int c = tid; c < C; c += kKmThreads) {
+      int s = 0;
+      for (int d = 0; d < kDim; ++d) { const int m = mu[c * kDim + d]; s += m * m; }
+      musq[c] = s;
+    }
+    __syncthreads();
+
+    // ---- assign: 16-row tiles, all C centroids per tile ----
+    const int ntile = N >> 4;
+    for (int rt = wave; rt < ntile; rt += kKmWaves) {
+      const v4i a = *reinterpret_cast<const v4i*>(X + (int64_t)(rt * 16 + (lane & 15)) * kDim +
+                                                  16 * (lane >> 4));
+      int best[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+      int bidx[4] = {0, 0, 0, 0};
+      for (int ct = 0; ct < (C >> 4); ++ct) {
+        const int c = ct * 16 + (lane & 15);
+        const v4i b = *reinterpret_cast<const v4i*>(mu + c * kDim + 16 * (lane >> 4));
+        const v4i z = {0, 0, 0, 0};
+        const v4i dot = mfma_i8_16x16x64(a, b, z);
+        const int msq = musq[c];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int d = msq - 2 * dot[v];
+          if (d < best[v]) { best[v] = d; bidx[v] = c; }
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ob = __shfl_xor(best[v], m);
+          const int oi = __shfl_xor(bidx[v], m);
+          if (ob < best[v] || (ob == best[v] && oi < bidx[v])) { best[v] = ob; bidx[v] = oi; }
+        }
+      }
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) assign[rt * 16 + 4 * (lane >> 4) + v] = (uint16_t)bidx[v];
+      }
+    }
+    for (int e = tid; e < C * kDim; e += kKmThreads) sums[e] = 0;
+    for (int e = tid; e < C; e += kKmThreads) counts[e] = 0;
+    __syncthreads();
+
+    // ---- update: per-cluster integer sums, rounded means ----
+    for (int i = wave; i < N; i += kKmWaves) {
+      const int c = assign[i];
+      atomicAdd(&sums[c * kDim + lane], (int)X[(int64_t)i * kDim + lane]);
+      if (lane == 0) atomicAdd(&counts[c], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < C * kDim; e += kKmThreads) {
+      const int c = e / kDim;
+      const int n = counts[c];
+      if (n > 0) mu[e] = (int8_t)rhe_div(sums[e], n);
+    }
+    __syncthreads();
+  }
+
+  // ---- stable member lists (counting sort by cluster, rows ascending) ----
+  // rows per wave: contiguous ranges so that wave order = row order
+  const int per_wave = (N + kKmWaves - 1) / kKmWaves;
+  const int r_begin = wave * per_wave;
+  const int r_end = min(N, r_begin + per_wave);
+  int32_t* firstrow = sums;
+  int32_t* lastrow = sums + C;
+  for (int e = tid; e < kKmWaves * C; e += kKmThreads) cw[e] = 0;
+  for (int e = tid; e < C; e += kKmThreads) { firstrow[e] = INT_MAX; lastrow[e] = -1; }
+  __syncthreads();
+  for (int r = r_begin + lane; r < r_end; r += 64) atomicAdd(&cw[wave * C + assign[r]], 1);
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      const int c = c0 + lane;
+      const int x = c < C ? counts[c] : 0;
+      int tot;
+      const int ex = wave_excl_scan(x, &tot);
+      if (c < C) offs[c] = carry + ex;
+      carry += tot;
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < C; c += kKmThreads) {
+    int run = offs[c];
+    for (int w = 0; w < kKmWaves; ++w) {
+      const int x = cw[w * C + c];
+      cw[w * C + c] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  const int64_t gbase = row0 + (int64_t)blk * N;
+  for (int r0 = r_begin; r0 < r_end; r0 += 64) {
+    const int r = r0 + lane;
+    const bool valid = r < r_end;
+    const int c = valid ? (int)assign[r] : 0;
+    unsigned long long mask = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (c >> bit) & 1;
+      const unsigned long long bb = __ballot(on);
+      mask &= on ? bb : ~bb;
+    }
+    if (valid) {
+      const unsigned long long below = mask & ((1ull << lane) - 1ull);
+      const int rank = __popcll(below);
+      const int pos = cw[wave * C + c] + rank;
+      mem_all[(int64_t)blk * N + pos] = (int32_t)(gbase + r);
+      if (map_all) map_all[gbase + r] = map_base + blk * C + c;
+      atomicMin(&firstrow[c], r);
+      atomicMax(&lastrow[c], r);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (mask & ((1ull << lane) - 1ull)) == 0ull) cw[wave * C + c] += __popcll(mask);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  for (int c = tid; c < C; c += kKmThreads) {
+    const int64_t b = (int64_t)blk * C + c;
+    cnt_all[b] = counts[c];
+    off_all[b] = (int32_t)(gbase + offs[c]);   // slot in the member array
+    if (first_all) {
+      first_all[b] = counts[c] > 0 ? (int32_t)(gbase + firstrow[c]) : INT_MAX;
+      last_all[b] = counts[c] > 0 ? (int32_t)(gbase + lastrow[c]) : -1;
+    }
+  }
+  for (int e = tid; e < C * 4; e += kKmThreads) {
+    const int c = e >> 2, part = e & 3;
+    reinterpret_cast<int4*>(cent_all + ((int64_t)blk * C + c) * kDim)[part] =
+        reinterpret_cast<const int4*>(mu + c * kDim)[part];
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_pool(const int8_t* pend, int32_t n_pend, const int8_t* src, int64_t n_src,
+                       int32_t p, int8_t* pooled_out, int64_t n_groups, hipStream_t s) {
+  (void)n_src;
+  if (n_groups <= 0) return hipSuccess;
+  const int64_t threads = n_groups * 16;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  hipLaunchKernelGGL(k_pool, dim3(grid), dim3(256), 0, s, pend, n_pend, src, p, pooled_out,
+                     n_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_save_pending(const int8_t* pend, int32_t n_pend, const int8_t* src,
+                               int64_t n_src, int32_t keep, int8_t* dst, hipStream_t s) {
+  if (keep <= 0) return hipSuccess;
+  const int threads = keep * kDim;
+  hipLaunchKernelGGL(k_save_pending, dim3((threads + 255) / 256), dim3(256), 0, s, pend, n_pend,
+                     src, n_src, keep, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail(const int8_t* pooled, int64_t g0, int64_t g1, int64_t n_full, int32_t N,
+                       int32_t C, int8_t* cent, int32_t* bcnt, int32_t* boff, int32_t* bmem,
+                       int32_t* bfirst, int32_t* blast, hipStream_t s) {
+  if (g1 <= g0) return hipSuccess;
+  const int64_t threads = (g1 - g0) * 4;
+  hipLaunchKernelGGL(k_tail, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, pooled,
+                     g0, g1, n_full, N, C, cent, bcnt, boff, bmem, bfirst, blast);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans(const int8_t* X, int32_t N, int32_t C, int32_t iters, int32_t nblk,
+                         int64_t row0, int8_t* cent_out, int32_t* cnt_out, int32_t* off_out,
+                         int32_t* mem_out, int32_t* first_out, int32_t* last_out,
+                         int32_t* map_out, int32_t map_base, hipStream_t s) {
+  if (nblk <= 0) return hipSuccess;
+  const size_t lds = kmeans_lds_bytes(N, C);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_kmeans,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_kmeans, dim3(nblk), dim3(kKmThreads), lds, s, X, N, C, iters, row0,
+                     cent_out, cnt_out, off_out, mem_out, first_out, last_out, map_out, map_base);
+  return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,88 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lsa.h"
+
+namespace lsa {
+
+constexpr int kDim = 64;          // latent dimension (bytes per latent row)
+constexpr uint64_t kMagic = 0x4c53414d49333535ull;
+
+// Host descriptor behind the opaque lsa_index.
+struct Index {
+  uint64_t magic;
+  lsa_index_params prm;
+  char* arena;
+  size_t arena_bytes;
+  int64_t T;        // keys covered
+  int64_t n_pool;   // complete pooled groups = T / pool
+  int64_t n_full;   // complete blocks
+  int64_t n_grp;    // complete Tree groups
+  int32_t pend_slot;  // which of the two pending-latent slots is live
+  // capacities
+  int64_t max_pool, max_full, max_bkt, max_grp, max_sup, max_smem;
+  // arena byte offsets
+  int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast;
+  int64_t off_scent, off_scnt, off_soff, off_smem, off_leafsup, off_pend;
+  int64_t used_bytes;
+
+  template <class T> T* at(int64_t off) const { return reinterpret_cast<T*>(arena + off); }
+  int64_t n_bkt() const { return n_full * prm.buckets + (n_pool - n_full * prm.block); }
+};
+static_assert(sizeof(Index) <= 512, "descriptor size");
+constexpr size_t kIndexSizeof = 512;
+
+// Device view of an index for the selection kernels.
+struct IdxView {
+  const int8_t* cent;     // [n_bkt][64]
+  const int32_t* bcnt;    // members per bucket
+  const int32_t* boff;    // first member slot
+  const int32_t* bmem;    // member pooled ids
+  const int32_t* bfirst;  // first member pooled id
+  const int32_t* blast;   // last member pooled id
+  const int32_t* leafsup; // leaf -> super id (Tree) or nullptr
+  int32_t n_bkt;
+  int32_t pool;
+  int32_t dense;          // 1: cent = raw latents, bucket j = key j (pool 1)
+  int32_t n_sup;
+  const int8_t* scent;    // [n_sup][64]
+};
+
+struct SelArgs {
+  const int8_t* latq;     // [nq][64]
+  const int32_t* qpos;    // [nq], or nullptr: position = qpos_base + query index
+  int32_t qpos_base;
+  int32_t nq;
+  int32_t budget, window, sinks, tree_top;
+  int32_t max_sel;
+  int32_t* idx;           // [nq][max_sel]
+  int32_t* cnt;           // [nq]
+};
+
+// ---- launchers (return hipError_t) ----
+hipError_t launch_pool(const int8_t* pend, int32_t n_pend, const int8_t* src, int64_t n_src,
+                       int32_t p, int8_t* pooled_out, int64_t n_groups, hipStream_t s);
+hipError_t launch_save_pending(const int8_t* pend, int32_t n_pend, const int8_t* src,
+                               int64_t n_src, int32_t keep, int8_t* dst, hipStream_t s);
+hipError_t launch_kmeans(const int8_t* X, int32_t N, int32_t C, int32_t iters, int32_t nblk,
+                         int64_t row0, int8_t* cent_out, int32_t* cnt_out, int32_t* off_out,
+                         int32_t* mem_out, int32_t* first_out, int32_t* last_out,
+                         int32_t* map_out, int32_t map_base, hipStream_t s);
+hipError_t launch_tail(const int8_t* pooled, int64_t g0, int64_t g1, int64_t n_full, int32_t N,
+                       int32_t C, int8_t* cent, int32_t* bcnt, int32_t* boff, int32_t* bmem,
+                       int32_t* bfirst, int32_t* blast, hipStream_t s);
+
+size_t select_ws_bytes(int32_t nq);
+hipError_t launch_select(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
+
+size_t attn_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t splits);
+hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_rows,
+                       int64_t seq_stride_rows, int32_t seq_of_query_div,
+                       const int32_t* idx, const int32_t* cnt, int32_t max_sel, int32_t nq,
+                       const lsa_attn_params& ap, void* out, void* ws, int32_t splits,
+                       hipStream_t s);
+
+}  // namespace lsa

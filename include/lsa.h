@@ -1,0 +1,209 @@
+/*
+ * lsa.h -- C ABI of the Latent Sparse Attention (LSA) hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations follow the pages about the preprint "Latent Sparse
+ * Attention: Towards Subquadratic Ultra-Long Context Attention" (arXiv
+ * 2610.42147):
+ *   - index build: "Latent Sparse Attention: un indice gerarchico per
+ *     contesti lunghi" (mauroscia.it), paragraph on the index -- consecutive
+ *     keys are pooled in small groups, the pooled sequence is split into
+ *     blocks, the vectors of each block are grouped by similarity into
+ *     buckets that keep a centroid and the indices of their original keys;
+ *   - search: same page, next paragraph -- the query is compared with the
+ *     centroids to pick the buckets whose keys are fetched, then attention
+ *     runs on the selected keys and values;
+ *   - budget: same page, D-LSA configuration paragraph -- 64-d index
+ *     representations, a fixed number of long-range keys (outside the recent
+ *     window), plus the most recent keys and a few sink keys at the start;
+ *   - hierarchy: "Prefrontal's Latent Sparse Attention speeds up one
+ *     attention layer 72x at 10M tokens" (sysnote.net), section "What it
+ *     changes" -- clusters grouped into a hierarchy that a query walks down,
+ *     with the attention kernel itself unchanged.
+ *
+ * Conventions
+ *   - Every device buffer is owned by the caller; the library never
+ *     allocates device memory.  Pointers prefixed d_ are device pointers.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
+ *     NULL = the null stream) except lsa_export_index, which synchronises it.
+ *   - Arguments are validated before anything is enqueued; on an error
+ *     nothing is enqueued and the index descriptor is unchanged.  A runtime
+ *     or launch failure returns LSA_E_HIP.  lsa_last_error() gives a
+ *     thread-local message for the last failing call.  No C++ exception
+ *     crosses the ABI.
+ *   - Calls on one index must be ordered on one stream; the API is not
+ *     thread-safe per index.
+ *   - Latents are int8, 64 per token, row-major [token][64].
+ *   - Q / K / V / O are bf16 bit patterns (uint16), token-major:
+ *     Q and O [nq][Hq][D], K and V [rows][Hkv][D].  Head h reads KV head
+ *     floor(h * Hkv / Hq).
+ *   - Selected key lists are int32 rows of `max_sel` = budget + window + sinks
+ *     entries: `cnt[i]` distinct key positions (a set; the order is
+ *     deterministic but unspecified) followed by -1 padding.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_API __attribute__((visibility("default")))
+
+enum {
+  LSA_OK = 0,
+  LSA_E_ARG = 1,          /* null pointer, bad size or parameter */
+  LSA_E_UNSUPPORTED = 2,  /* latent dim != 64, D not in {64,128}, Hq/Hkv not in 1..16, ... */
+  LSA_E_CAPACITY = 3,     /* T beyond the index capacity, workspace too small */
+  LSA_E_STATE = 4,        /* descriptor not initialised / corrupt */
+  LSA_E_HIP = 5           /* HIP runtime or launch failure */
+};
+
+/* workspace query ops */
+enum {
+  LSA_OP_BUILD = 0,    /* n = T */
+  LSA_OP_APPEND = 1,   /* n = new keys */
+  LSA_OP_SELECT = 2,   /* n = queries */
+  LSA_OP_ATTN = 3,     /* n = queries */
+  LSA_OP_PREFILL = 4,  /* n = chunk length */
+  LSA_OP_DECODE = 5,   /* n = sequences */
+  LSA_OP_DENSE = 6     /* n = queries */
+};
+
+/* Index shape.  dim must be 64.  pool >= 1.  block (pooled vectors per
+ * block) is a multiple of 64 in [64, 16384]; buckets (clusters per block)
+ * is a multiple of 16 in [16, 256] and <= block; iters >= 1.  Tree:
+ * tree_group blocks per super group (0 = Flat), tree_super clusters per
+ * group (multiple of 16, <= 256, tree_group*buckets <= 16384 and a multiple
+ * of 64), tree_iters >= 1.  max_tokens = capacity in keys. */
+typedef struct lsa_index_params {
+  int32_t dim, pool, block, buckets, iters;
+  int32_t tree_group, tree_super, tree_iters;
+  int64_t max_tokens;
+} lsa_index_params;
+
+/* Per-query selection: budget long-range keys (sinks <= j <= t - window),
+ * the window [t-window+1, t] and the sinks [0, sinks).  window >= pool.
+ * tree_top = super clusters a query walks into (Tree indexes only). */
+typedef struct lsa_select_params {
+  int32_t budget, window, sinks, tree_top;
+} lsa_select_params;
+
+/* Attention shape.  D in {64, 128}; 1 <= Hq/Hkv <= 16, Hq % Hkv == 0.
+ * scale = softmax scale (0 => 1/sqrt(D)).  out_f32 = 0: bf16 output;
+ * 1: float32 output (same arithmetic, no final rounding). */
+typedef struct lsa_attn_params {
+  int32_t Hq, Hkv, D, out_f32;
+  float scale;
+} lsa_attn_params;
+
+/* Opaque host descriptor; the caller provides lsa_index_sizeof() bytes. */
+typedef struct lsa_index lsa_index;
+
+/* Counts and arena byte offsets of the arrays of a built index.
+ *   pooled   int8  [n_pool][64]     pooled latent vectors
+ *   cent     int8  [n_bkt][64]      bucket centroids: block b owns ids b*C..b*C+C-1,
+ *                                   then one singleton bucket per tail pooled vector
+ *   bcnt     int32 [n_bkt]          members per bucket
+ *   boff     int32 [n_bkt]          first member's slot in bmem
+ *   bmem     int32 [n_pool]         pooled ids, grouped by bucket, ascending in each
+ *   bfirst   int32 [n_bkt]          smallest member pooled id (INT32_MAX if empty)
+ *   blast    int32 [n_bkt]          largest member pooled id (-1 if empty)
+ *   scent    int8  [n_sup][64]      super centroids (Tree)
+ *   scnt     int32 [n_sup]          leaves per super cluster
+ *   soff     int32 [n_sup]          first leaf's slot in smem
+ *   smem     int32 [n_grp*G*C]      leaf ids grouped by super cluster, ascending
+ * Key ids of pooled id g are g*pool .. g*pool+pool-1. */
+typedef struct lsa_index_info {
+  int64_t T, n_pool, n_full, n_bkt, n_grp, n_sup;
+  int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast;
+  int64_t off_scent, off_scnt, off_soff, off_smem;
+  int64_t arena_bytes;
+} lsa_index_info;
+
+LSA_API const char* lsa_status_str(int status);
+LSA_API const char* lsa_last_error(void);
+
+LSA_API size_t lsa_index_sizeof(void);
+/* Device arena bytes needed for an index with these params (LSA_E_ARG /
+ * LSA_E_UNSUPPORTED on invalid params). */
+LSA_API int lsa_index_bytes(const lsa_index_params* prm, size_t* bytes);
+/* Initialise the host descriptor `h` (lsa_index_sizeof() bytes) over the
+ * caller's device arena (256-byte aligned).  The index starts empty (T=0). */
+LSA_API int lsa_index_init(lsa_index* h, const lsa_index_params* prm, void* d_arena,
+                           size_t arena_bytes);
+LSA_API int lsa_index_get_info(const lsa_index* h, lsa_index_info* out);
+
+/* Workspace bytes for `op` with `n` as documented in the LSA_OP_* enum.
+ * Index params are needed for BUILD/APPEND/PREFILL/DECODE/SELECT, select
+ * params for SELECT/PREFILL/DECODE/DENSE, attention params for
+ * ATTN/PREFILL/DECODE; unused ones may be NULL. */
+LSA_API int lsa_workspace_bytes(int op, const lsa_index_params* iprm,
+                                const lsa_select_params* sprm, const lsa_attn_params* aprm,
+                                int64_t n, size_t* bytes);
+
+/* Build the index over keys [0, T) from scratch (pool, block k-means, tail
+ * singletons, Tree super level).  d_latk: int8 [T][64]. */
+LSA_API int lsa_build_index(lsa_index* h, const int8_t* d_latk, int64_t T, void* d_ws,
+                            size_t ws_bytes, void* stream);
+
+/* Append n keys (positions T .. T+n-1).  Complete pooled groups become tail
+ * singleton buckets; a tail block that fills is clustered; a Tree group that
+ * completes gets its super level.  The result equals lsa_build_index over
+ * all T+n keys. */
+LSA_API int lsa_append_keys(lsa_index* h, const int8_t* d_latk_new, int64_t n, void* d_ws,
+                            size_t ws_bytes, void* stream);
+
+/* Select keys for nq queries: d_latq int8 [nq][64], d_qpos int32 [nq] with
+ * 0 <= qpos < T (not checked on the device; out-of-range positions are
+ * clamped).  Writes d_idx int32 [nq][max_sel] and d_cnt int32 [nq]. */
+LSA_API int lsa_select(const lsa_index* h, const int8_t* d_latq, const int32_t* d_qpos,
+                       int32_t nq, const lsa_select_params* sp, int32_t* d_idx, int32_t* d_cnt,
+                       void* d_ws, size_t ws_bytes, void* stream);
+
+/* Attention of nq query tokens over their selected rows.  d_q [nq][Hq][D],
+ * d_k / d_v [kv_rows][Hkv][D] bf16; d_idx / d_cnt as written by lsa_select
+ * (row stride max_sel; key ids are clamped to [0, kv_rows)).  d_out
+ * [nq][Hq][D] bf16 (or float32 when out_f32). */
+LSA_API int lsa_sparse_attn(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                            int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                            int32_t max_sel, int32_t nq, const lsa_attn_params* ap, void* d_out,
+                            void* d_ws, size_t ws_bytes, void* stream);
+
+/* One prefill chunk: append the chunk's n_chunk latent keys, select for its
+ * n_chunk queries (positions T_old .. T_old+n_chunk-1, scored against the
+ * index that already holds the chunk's keys), attend.  The caller has
+ * written K/V rows up to T_old+n_chunk.  d_idx_opt / d_cnt_opt (nullable)
+ * receive the selection; otherwise it lives in the workspace. */
+LSA_API int lsa_prefill_chunk(lsa_index* h, const int8_t* d_latk_chunk, int64_t n_chunk,
+                              const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
+                              const uint16_t* d_v, int64_t kv_rows, const lsa_select_params* sp,
+                              const lsa_attn_params* ap, void* d_out, int32_t* d_idx_opt,
+                              int32_t* d_cnt_opt, void* d_ws, size_t ws_bytes, void* stream);
+
+/* One decode step for nseq (<= 16) independent sequences: append one key
+ * per sequence (d_latk_new int8 [nseq][64]), select for each sequence's
+ * new position with d_latq [nseq][64], attend with d_q [nseq][Hq][D].
+ * Sequence i's K/V rows start at d_k + i*seq_stride_rows*Hkv*D (the caller
+ * has written the new rows).  d_out [nseq][Hq][D]. */
+LSA_API int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new,
+                            const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
+                            const uint16_t* d_v, int64_t seq_stride_rows,
+                            const lsa_select_params* sp, const lsa_attn_params* ap, void* d_out,
+                            void* d_ws, size_t ws_bytes, void* stream);
+
+/* Quadratic comparator: every long-range key scored on its own latent
+ * (q . latk[j]), best `budget` by (score desc, position asc), plus window
+ * and sinks.  Same output format as lsa_select. */
+LSA_API int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq,
+                             const int32_t* d_qpos, int32_t nq, const lsa_select_params* sp,
+                             int32_t* d_idx, int32_t* d_cnt, void* d_ws, size_t ws_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H */

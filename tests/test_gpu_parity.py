@@ -1,0 +1,351 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Index arrays and selected key sets must match bit-exactly; attention must
+match the float64 oracle within 2e-3 normwise relative error
+(max |gpu - ref| / max |ref| over the compared tensor), measured on the
+kernel's float32 output, and the bf16 output must be the round-to-nearest-
+even of that float32 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lsa_synth as S
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _L():
+    import hierarchical_sparse_attention_lsa_amd as L
+    return L
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _iparams(wl, max_tokens=None):
+    L = _L()
+    return L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group,
+                         wl.tree_super, wl.tree_iters, max_tokens or wl.T)
+
+
+def _oparams(wl):
+    return O.IndexParams(wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
+                         wl.tree_iters)
+
+
+def check_index(gpu_arrays, ref: O.Index, blocks=None):
+    """Bit-exact comparison of the GPU index with the oracle's (optionally a subset of blocks)."""
+    a = {k: v.cpu().numpy() for k, v in gpu_arrays.items()}
+    assert a["cent"].shape[0] == ref.n_bkt
+    assert np.array_equal(a["pooled"], ref.pooled), "pooled vectors"
+    counts = np.array([len(m) for m in ref.members], dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(counts)[:-1]]) if len(counts) else counts
+    mem = np.concatenate(ref.members) if ref.members else np.zeros(0, np.int64)
+    if blocks is None:
+        assert np.array_equal(a["cent"], ref.centroids), "centroids"
+        assert np.array_equal(a["bcnt"], counts), "bucket counts"
+        assert np.array_equal(a["boff"], offs), "bucket offsets"
+        assert np.array_equal(a["bmem"], mem), "members"
+    else:
+        C, N = ref.params.buckets, ref.params.block
+        for b in blocks:
+            sl = slice(b * C, (b + 1) * C)
+            assert np.array_equal(a["cent"][sl], ref.centroids[sl]), f"centroids block {b}"
+            assert np.array_equal(a["bcnt"][sl], counts[sl]), f"counts block {b}"
+            assert np.array_equal(a["boff"][sl], offs[sl]), f"offsets block {b}"
+            assert np.array_equal(a["bmem"][b * N:(b + 1) * N], mem[b * N:(b + 1) * N])
+    nz = counts > 0
+    first = np.array([m[0] if len(m) else 2 ** 31 - 1 for m in ref.members])
+    last = np.array([m[-1] if len(m) else -1 for m in ref.members])
+    if blocks is None:
+        assert np.array_equal(a["bfirst"], first) and np.array_equal(a["blast"], last)
+    if ref.sup_centroids is not None and blocks is None:
+        assert np.array_equal(a["scent"], ref.sup_centroids), "super centroids"
+        sc = np.array([len(m) for m in ref.sup_members])
+        assert np.array_equal(a["scnt"], sc)
+        smem = np.concatenate(ref.sup_members) if ref.sup_members else np.zeros(0)
+        assert np.array_equal(a["smem"], smem)
+
+
+def check_selection(idx, cnt, refs, max_sel):
+    idx = idx.cpu().numpy()
+    cnt = cnt.cpu().numpy()
+    for i, ref in enumerate(refs):
+        n = int(cnt[i])
+        got = idx[i, :n]
+        assert np.array_equal(np.sort(got), ref), f"query {i}: {n} vs {len(ref)} keys"
+        assert (idx[i, n:] == -1).all()
+        assert n <= max_sel
+
+
+def oracle_attention(g: S.Synth, wl, positions, sels, scale=None):
+    out = []
+    for t, sel in zip(positions, sels):
+        rows = torch.from_numpy(np.asarray(sel, dtype=np.int64))
+        K = O.bf16_to_f64(g.k_rows(rows).view(torch.int16).numpy())
+        V = O.bf16_to_f64(g.v_rows(rows).view(torch.int16).numpy())
+        q = O.bf16_to_f64(g.q_rows(torch.tensor([t])).view(torch.int16).numpy())[0]
+        out.append(O.attend(q, K, V, wl.Hkv, scale))
+    return np.stack(out)
+
+
+def normwise(got, ref):
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+def rne_bf16_bits(x: np.ndarray) -> np.ndarray:
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tiny():
+    dev = _dev()
+    wl = S.WORKLOADS["tiny_flat"]
+    g = S.Synth(wl)
+    latk = g.latk(0, wl.T)
+    ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
+    return wl, g, latk, ref, dev
+
+
+def test_tiny_index_bit_exact(tiny):
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    torch.cuda.synchronize()
+    check_index(ix.arrays(), ref)
+
+
+def test_tiny_selection_bit_exact(tiny):
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    # the chunk's queries plus early positions (window-only, sinks overlap) and a ragged count
+    pos = list(range(wl.T - wl.chunk, wl.T)) + [0, 1, 3, 4, 100, 127, 128, 131, 132, 133, 5000]
+    lq = g.latq_rows(torch.tensor(pos))
+    idx, cnt = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
+    refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    check_selection(idx, cnt, refs, sp.max_sel)
+    # determinism: a second run is bitwise identical (order included)
+    idx2, cnt2 = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+
+
+def test_tiny_attention_within_tolerance(tiny):
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    pos = list(range(wl.T - wl.chunk, wl.T))
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    lq = g.latq_rows(torch.tensor(pos))
+    sels = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    max_sel = wl.max_sel
+    idx = torch.full((len(pos), max_sel), -1, dtype=torch.int32)
+    cnt = torch.zeros(len(pos), dtype=torch.int32)
+    for i, s in enumerate(sels):
+        idx[i, :len(s)] = torch.from_numpy(s[::-1].copy().astype(np.int32))   # any order
+        cnt[i] = len(s)
+    q = g.q_rows(torch.tensor(pos))
+    K = torch.empty((wl.T, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0)
+    g.fill_rows("v", V, 0)
+    args = [t.to(dev) for t in (q, K, V, idx, cnt)]
+    o32 = L.sparse_attn(*args, L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0))
+    o16 = L.sparse_attn(*args, L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0))
+    refo = oracle_attention(g, wl, pos, sels)
+    err = normwise(o32.cpu().numpy().astype(np.float64), refo)
+    print(f"tiny attention normwise error {err:.3e}")
+    assert err <= TOL
+    assert np.array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16),
+                          rne_bf16_bits(o32.cpu().numpy()))
+
+
+def test_tiny_prefill_chunk_fused(tiny):
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    ix = L.LsaIndex(_iparams(wl), dev)
+    t0 = wl.T - wl.chunk
+    ix.build(latk[:t0].to(dev))
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    K = torch.empty((wl.T, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0)
+    g.fill_rows("v", V, 0)
+    pos = list(range(t0, wl.T))
+    lq = g.latq_rows(torch.tensor(pos))
+    q = g.q_rows(torch.tensor(pos))
+    idx = torch.empty((wl.chunk, wl.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((wl.chunk,), dtype=torch.int32, device=dev)
+    out = ix.prefill_chunk(latk[t0:].to(dev), lq.to(dev), q.to(dev), K.to(dev), V.to(dev), sp, ap,
+                           idx=idx, cnt=cnt)
+    torch.cuda.synchronize()
+    check_index(ix.arrays(), ref)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    sels = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    check_selection(idx, cnt, sels, wl.max_sel)
+    err = normwise(out.cpu().numpy().astype(np.float64), oracle_attention(g, wl, pos, sels))
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_append_equals_build(seed):
+    """Chunked and per-token appends (crossing tail re-clusters) equal a one-shot build."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("app", 90 + seed, T=4 * 256 * 5 + 37, ncomp=64, block=256, buckets=32,
+                    iters=3, chunk=0, budget=200, window=64, sinks=4, Hq=4, Hkv=1, D=64)
+    g = S.Synth(wl, data_cfg=90 + seed)
+    latk = g.latk(0, wl.T)
+    ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
+    ix = L.LsaIndex(_iparams(wl), dev)
+    rng = np.random.default_rng(seed)
+    cuts = sorted(set(rng.integers(1, wl.T, 12).tolist() + [1, 2, 3, 1024, 1025, 2048]))
+    prev = 0
+    for c in cuts + [wl.T]:
+        ix.append(latk[prev:c].to(dev))
+        prev = c
+    torch.cuda.synchronize()
+    check_index(ix.arrays(), ref)
+    # one key at a time over a block boundary
+    ix2 = L.LsaIndex(_iparams(wl), dev)
+    ix2.build(latk[:1000].to(dev))
+    for t in range(1000, 1100):
+        ix2.append(latk[t:t + 1].to(dev))
+    torch.cuda.synchronize()
+    check_index(ix2.arrays(), O.build_index(latk.numpy(), 1100, _oparams(wl)))
+
+
+def test_edge_cases_small_contexts_ties_budget0():
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("edge", 80, T=4 * 64 * 3 + 2, ncomp=8, block=64, buckets=16, iters=2,
+                    chunk=0, budget=50, window=8, sinks=3, Hq=2, Hkv=2, D=64)
+    g = S.Synth(wl, data_cfg=80)
+    latk = g.latk(0, wl.T)
+    latk[100:300] = 5                                   # exact duplicates -> distance ties
+    ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    torch.cuda.synchronize()
+    check_index(ix.arrays(), ref)
+    pos = [0, 1, 2, 7, 8, 10, 11, 12, 60, 200, wl.T - 1, wl.T - 2, 333]
+    lq = g.latq_rows(torch.tensor(pos))
+    lq[3] = 0                                          # every score ties
+    for B in (0, 1, 7, 50, 400):
+        sp = L.SelectParams(B, wl.window, wl.sinks, 0)
+        osp = O.SelectParams(B, wl.window, wl.sinks)
+        idx, cnt = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
+        refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+        check_selection(idx, cnt, refs, sp.max_sel)
+    # empty query batch
+    idx, cnt = ix.select(lq[:0].to(dev), torch.zeros(0, dtype=torch.int32, device=dev),
+                         L.SelectParams(10, 8, 3, 0))
+    assert idx.shape == (0, 21)
+
+
+def test_dense_select_matches_oracle():
+    dev = _dev()
+    L = _L()
+    wl = S.WORKLOADS["tiny_flat"]
+    g = S.Synth(wl)
+    T = 6000
+    latk = g.latk(0, T)
+    pos = [5, 200, 1000, 2047, 4096, 5999, 3333, 4444, 5555, 130, 131]
+    lq = g.latq_rows(torch.tensor(pos))
+    sp = L.SelectParams(300, 128, 4, 0)
+    osp = O.SelectParams(300, 128, 4)
+    idx, cnt = L.dense_select(latk.to(dev), lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
+    refs = [O.dense_select(latk.numpy(), lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    check_selection(idx, cnt, refs, sp.max_sel)
+
+
+def test_tree_index_and_selection():
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("tree_small", 70, T=4 * 256 * 12 + 300, ncomp=128, block=256, buckets=32,
+                    iters=3, tree_group=4, tree_super=16, tree_iters=3, tree_top=5, chunk=0,
+                    budget=500, window=64, sinks=4, Hq=4, Hkv=1, D=64)
+    g = S.Synth(wl, data_cfg=70)
+    latk = g.latk(0, wl.T)
+    ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
+    assert ref.n_grp == 3
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    torch.cuda.synchronize()
+    check_index(ix.arrays(), ref)
+    pos = [wl.T - 1 - 37 * i for i in range(40)] + [70, 500, 4000]
+    lq = g.latq_rows(torch.tensor(pos))
+    for R in (1, 5, 48):
+        sp = L.SelectParams(wl.budget, wl.window, wl.sinks, R)
+        osp = O.SelectParams(wl.budget, wl.window, wl.sinks, R)
+        idx, cnt = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
+        refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+        check_selection(idx, cnt, refs, sp.max_sel)
+
+
+def test_decode_steps_match_oracle():
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("dec_small", 60, T=4 * 256 * 4 + 5, ncomp=64, block=256, buckets=32, iters=3,
+                    chunk=0, budget=300, window=64, sinks=4, Hq=8, Hkv=2, D=128, nseq=3, steps=9)
+    gens = [S.Synth(wl, seq=i, data_cfg=60) for i in range(wl.nseq)]
+    cap = wl.T + wl.steps
+    ixs, lat = [], []
+    K = torch.empty((wl.nseq, cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    for i, g in enumerate(gens):
+        lk = g.latk(0, cap)
+        lat.append(lk)
+        ix = L.LsaIndex(_iparams(wl, cap), dev)
+        ix.build(lk[:wl.T].to(dev))
+        ixs.append(ix)
+        g.fill_rows("k", K[i], 0)
+        g.fill_rows("v", V[i], 0)
+    Kd, Vd = K.to(dev), V.to(dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    errs = []
+    for step in range(wl.steps):
+        t = wl.T + step
+        lk_new = torch.stack([lat[i][t] for i in range(wl.nseq)])
+        lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i in range(wl.nseq)])
+        q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i in range(wl.nseq)])
+        out = L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kd, Vd, cap, sp, ap)
+        torch.cuda.synchronize()
+        for i in range(wl.nseq):
+            ref = O.build_index(lat[i].numpy(), t + 1, _oparams(wl))
+            sel = O.select(ref, lq[i].numpy(), t, osp)
+            ro = oracle_attention(gens[i], wl, [t], [sel])[0]
+            errs.append(normwise(out[i].cpu().numpy().astype(np.float64), ro))
+    check_index(ixs[0].arrays(), O.build_index(lat[0].numpy(), wl.T + wl.steps, _oparams(wl)))
+    print("decode max normwise error", max(errs))
+    assert max(errs) <= TOL
+
+
+def test_api_errors_leave_index_unchanged(tiny):
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    ix = L.LsaIndex(_iparams(wl, 4096), dev)
+    ix.build(latk[:4000].to(dev))
+    before = ix.snapshot()
+    with pytest.raises(L.LsaError, match="capacity"):
+        ix.append(latk[4000:4200].to(dev))
+    assert ix.snapshot() == before
+    with pytest.raises(L.LsaError):
+        ix.select(latk[:2].to(dev), torch.zeros(2, dtype=torch.int32, device=dev),
+                  L.SelectParams(5000, 8, 0, 0))
+    assert ix.info().T == 4000
