@@ -1,0 +1,398 @@
+#!/usr/bin/env python3
+"""Benchmark of the LSA hot path on one MI355X.
+
+A step is one prefill chunk of one attention layer at the headline shape:
+the last 32768 query tokens of a 10*2^20-token context (Flat index, 64-d int8
+latents, p=4, blocks of 4096 pooled vectors with 256 buckets, 4 k-means
+iterations; GQA 32 query / 8 KV heads, head dim 128, bf16 KV cache held on
+the GPU; 4096 long-range + 512 window + 4 sink keys per query).  The step
+appends the chunk's keys to the prebuilt index (pooling + clustering of the
+two blocks the chunk completes), selects keys for the 32768 queries and runs
+the sparse attention.  Inputs are synthetic (lsa_synth) and resident in HBM
+before the timed region.
+
+Prints one JSON line.  Extra fields: per-phase times, the attention kernel's
+roofline, decode tokens/s (8 sequences of 2^20 keys), full index-build
+keys/s, the on-GPU dense per-key scan (the quadratic comparison) and the CPU
+oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import hierarchical_sparse_attention_lsa_amd as L  # noqa: E402
+import lsa_synth as S  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "hierarchical_sparse_attention_lsa_amd", "csrc", "lsa_attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def gen_inputs(wl, dev, seq=0, T=None):
+    g = S.Synth(wl, seq=seq)
+    T = T or wl.T
+    latk = g.latk(0, T, device=dev, chunk=1 << 22)
+    K = torch.empty((T, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0, chunk=1 << 18)
+    g.fill_rows("v", V, 0, chunk=1 << 18)
+    return g, latk, K, V
+
+
+def iparams(wl, cap):
+    return L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group,
+                         wl.tree_super, wl.tree_iters, cap)
+
+
+def attn_algorithmic_bytes(wl, t0, n, cnt: np.ndarray) -> float:
+    """Algorithmic HBM bytes of one attention launch over the chunk.
+
+    Long-range rows are counted per query (their reuse is data dependent and
+    not credited); window and sink rows form one span for the whole chunk and
+    are counted once; plus the index lists, Q and O."""
+    row = wl.Hkv * wl.D * 2 * 2                     # K + V bytes per token
+    t = np.arange(t0, t0 + n)
+    wstart = np.maximum(0, t - wl.window + 1)
+    nw = t - wstart + 1
+    ns = np.maximum(0, np.minimum(wl.sinks, wstart))
+    lr = cnt.astype(np.int64) - nw - ns
+    span = (t0 + n - max(0, t0 - wl.window + 1)) + min(wl.sinks, max(0, t0 - wl.window + 1))
+    qo = n * wl.Hq * wl.D * 2 * 2
+    return float(lr.sum() * row + span * row + cnt.sum() * 4 + qo)
+
+
+def bench_prefill(args, dev):
+    wl = S.WORKLOADS[args.config]
+    n = wl.chunk
+    t0 = wl.T - n
+    log(f"[bench] generating {wl.name}: T={wl.T} keys, KV {2 * wl.T * wl.Hkv * wl.D * 2 / 2**30:.1f} GiB")
+    tg = time.time()
+    g, latk, K, V = gen_inputs(wl, dev)
+    pos = torch.arange(t0, wl.T, dtype=torch.int64)
+    latq = g.latq_rows(pos.to(dev), device=dev)
+    q = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    g.fill_rows("q", q, t0)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - tg:.1f}s")
+
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
+    ix = L.LsaIndex(iparams(wl, wl.T), dev)
+
+    # full index build over the whole context (reported as keys/s)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    build_ms = []
+    for _ in range(3):
+        ev[0].record()
+        ix.build(latk)
+        ev[1].record()
+        torch.cuda.synchronize()
+        build_ms.append(ev[0].elapsed_time(ev[1]))
+    # prebuilt index of the context before the chunk
+    ix.build(latk[:t0])
+    torch.cuda.synchronize()
+    snap = ix.snapshot()
+
+    idx = torch.empty((n, sp.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((n,), dtype=torch.int32, device=dev)
+    out = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    qpos = torch.arange(t0, wl.T, dtype=torch.int32, device=dev)
+    lk_chunk = latk[t0:]
+
+    def step(evs=None):
+        ix.restore(snap)
+        if evs: evs[0].record()
+        ix.append(lk_chunk)
+        if evs: evs[1].record()
+        ix.select(latq, qpos, sp, idx=idx, cnt=cnt)
+        if evs: evs[2].record()
+        L.sparse_attn(q, K, V, idx, cnt, ap, out=out)
+        if evs: evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                   for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+
+    # the fused entry point gives the same selection and output
+    ix.restore(snap)
+    idx2 = torch.empty_like(idx)
+    cnt2 = torch.empty_like(cnt)
+    out2 = ix.prefill_chunk(lk_chunk, latq, q, K, V, sp, ap, idx=idx2, cnt=cnt2)
+    torch.cuda.synchronize()
+    fused_same = bool(torch.equal(idx2, idx) and torch.equal(cnt2, cnt) and
+                      torch.equal(out2.view(torch.int16), out.view(torch.int16)))
+
+    cnt_h = cnt.cpu().numpy()
+    attn_ms = float(ph[:, 2].mean())
+    abytes = attn_algorithmic_bytes(wl, t0, n, cnt_h)
+    achieved = abytes / (attn_ms * 1e-3) / 1e9
+    res = {
+        "wl": wl, "t0": t0, "n": n, "ms_per_step": ms_per_step, "phase_ms": ph.mean(0).tolist(),
+        "attn_ms": attn_ms, "attn_bytes": abytes, "achieved_gbs": achieved,
+        "build_ms": float(np.median(build_ms)), "fused_same": fused_same,
+        "cnt_mean": float(cnt_h.mean()), "g": g, "latk": latk, "latq": latq, "idx": idx,
+        "cnt": cnt, "out": out, "K": K, "V": V, "q": q, "ix": ix, "snap": snap, "sp": sp,
+    }
+    return res
+
+
+def bench_dense(res, dev, nq=4096):
+    """Quadratic comparison: every long-range key scored on its own latent."""
+    wl, t0 = res["wl"], res["t0"]
+    sel = torch.linspace(0, res["n"] - 1, nq).round().to(torch.int64)
+    latq = res["latq"][sel.to(dev)].contiguous()
+    qpos = (sel + t0).to(torch.int32).to(dev)
+    sp = res["sp"]
+    L.dense_select(res["latk"], latq[:64].contiguous(), qpos[:64].contiguous(), sp)   # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    L.dense_select(res["latk"], latq, qpos, sp)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    return {"queries": nq, "ms": ms, "ms_per_chunk_scaled": ms * res["n"] / nq,
+            "note": "dense per-key int8 scan + exact top-B over all long-range keys, same "
+                    "selection rule (p=1 singleton buckets)"}
+
+
+def bench_decode(args, dev):
+    wl = S.WORKLOADS["decode_1m"]
+    cap = wl.T + wl.steps
+    log(f"[bench] decode: {wl.nseq} sequences x {wl.T} keys, {wl.steps} steps")
+    ixs, lat, gens = [], [], []
+    K = torch.empty((wl.nseq, cap, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    for i in range(wl.nseq):
+        g = S.Synth(wl, seq=i)
+        gens.append(g)
+        lk = g.latk(0, cap, device=dev, chunk=1 << 22)
+        lat.append(lk)
+        g.fill_rows("k", K[i], 0, chunk=1 << 18)
+        g.fill_rows("v", V[i], 0, chunk=1 << 18)
+        ix = L.LsaIndex(iparams(wl, cap), dev)
+        ix.build(lk[:wl.T])
+        ixs.append(ix)
+    steps = wl.steps
+    new_pos = torch.arange(wl.T, wl.T + steps, dtype=torch.int64, device=dev)
+    lk_new = torch.stack([lat[i][wl.T:wl.T + steps] for i in range(wl.nseq)], 1).contiguous()
+    lq = torch.stack([gens[i].latq_rows(new_pos, device=dev) for i in range(wl.nseq)], 1).contiguous()
+    qs = torch.stack([gens[i].q_rows(new_pos, device=dev) for i in range(wl.nseq)], 1).contiguous()
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
+    out = torch.empty((wl.nseq, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    wsb = L.workspace_bytes(L.binding.OP_DECODE, ixs[0].params, sp, ap, wl.nseq)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    snaps = [ix.snapshot() for ix in ixs]
+    torch.cuda.synchronize()
+
+    def run():
+        for s in range(steps):
+            L.decode_step(ixs, lk_new[s], lq[s], qs[s], K, V, cap, sp, ap, out=out, ws=ws)
+
+    run()                       # warm-up pass
+    torch.cuda.synchronize()
+    for ix, sn in zip(ixs, snaps):
+        ix.restore(sn)
+    t = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t
+    return {"sequences": wl.nseq, "context": wl.T, "steps": steps,
+            "ms_per_step": dt * 1e3 / steps, "tokens_per_s": wl.nseq * steps / dt}
+
+
+def cpu_baseline(res, workers_pool, n_sample=192):
+    """The oracle, timed on host cores on a bounded sample of the same workload."""
+    import oracle as O
+    from oracle.parallel_build import build_cache_parallel
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    wl, t0, n = res["wl"], res["t0"], res["n"]
+    g = S.Synth(wl)
+    tb = time.time()
+    cache0, latk_h = build_cache_parallel(wl.name, t0, workers_pool)   # untimed: prebuilt context
+    log(f"[bench] oracle prebuilt index ({t0} keys) in {time.time() - tb:.1f}s")
+    # timed: the chunk's index update (pool + cluster the two blocks it completes)
+    latk_chunk = g.latk(t0, wl.T).numpy()
+    latk_all = np.concatenate([latk_h, latk_chunk])
+    params = O.IndexParams(wl.pool, wl.block, wl.buckets, wl.iters)
+    ts = time.perf_counter()
+    P = O.pool(latk_all[t0 - (t0 % (wl.pool * wl.block)):], wl.pool)
+    b0 = t0 // (wl.pool * wl.block)
+    nb = wl.T // (wl.pool * wl.block) - b0
+    blk = []
+    for b in range(nb):
+        blk.append(O.kmeans(P[b * wl.block:(b + 1) * wl.block], wl.buckets, wl.iters))
+    t_update = time.perf_counter() - ts
+    cache = dict(cache0)
+    for b in range(nb):
+        cache[("blk", b0 + b)] = blk[b]
+    full = O.build_index(latk_all, wl.T, params, cache)
+    # timed: selection + attention for a sample of the chunk's queries
+    sel_i = np.unique(np.linspace(0, n - 1, n_sample).round().astype(np.int64))
+    positions = (t0 + sel_i).tolist()
+    lq = g.latq_rows(torch.tensor(positions)).numpy()
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    ts = time.perf_counter()
+    sels = [O.select(full, lq[i], t, osp) for i, t in enumerate(positions)]
+    t_sel = time.perf_counter() - ts
+    kv = []
+    for s in sels:
+        rows = torch.from_numpy(s)
+        kv.append((O.bf16_to_f64(g.k_rows(rows).view(torch.int16).numpy()),
+                   O.bf16_to_f64(g.v_rows(rows).view(torch.int16).numpy())))
+    qh = O.bf16_to_f64(g.q_rows(torch.tensor(positions)).view(torch.int16).numpy())
+    ts = time.perf_counter()
+    outs = [O.attend(qh[i], kv[i][0], kv[i][1], wl.Hkv) for i in range(len(positions))]
+    t_att = time.perf_counter() - ts
+    m = len(positions)
+    t_step = t_update + (t_sel + t_att) * n / m
+    # parity of the same sample against the GPU's timed step
+    idx, cnt = res["idx"].cpu().numpy(), res["cnt"].cpu().numpy()
+    same = sum(int(np.array_equal(np.sort(idx[i, :cnt[i]]), sels[j])) for j, i in enumerate(sel_i))
+    o = res["out"].float().cpu().numpy()[sel_i]
+    ref = np.stack(outs)
+    err = float(np.abs(o - ref).max() / np.abs(ref).max())
+    return {
+        "value": n / t_step, "unit": "queries/s", "cores": blas_threads, "kind": "oracle",
+        "sample": f"chunk index update (2 blocks) timed in full; select + attention timed on "
+                  f"{m} of {n} chunk queries and scaled to the chunk; prebuilt context index "
+                  f"built untimed",
+        "timed_s": t_update + t_sel + t_att,
+        "parity_sample": {"queries": m, "selections_bit_exact": same,
+                          "attn_bf16_normwise_err": err},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="flat_10m", choices=["flat_10m", "flat_1m", "tree_10m"])
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the LSA hot path here is built and timed on a "
+              "single MI355X (--gpus 1); multi-GPU sharding is a design note, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    workers_pool = None
+    if not args.no_cpu:
+        # forked before anything touches the GPU; the workers only run the CPU oracle
+        import multiprocessing as mp
+        workers_pool = mp.get_context("fork").Pool(min(16, os.cpu_count() or 1))
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    L.lib()
+
+    res = bench_prefill(args, dev)
+    wl = res["wl"]
+    log(f"[bench] prefill step {res['ms_per_step']:.2f} ms (append/select/attn "
+        f"{res['phase_ms'][0]:.3f}/{res['phase_ms'][1]:.3f}/{res['phase_ms'][2]:.3f} ms), "
+        f"attn {res['achieved_gbs']:.0f} GB/s")
+    dense = None if args.no_dense else bench_dense(res, dev)
+    if dense:
+        log(f"[bench] dense scan {dense['ms']:.1f} ms for {dense['queries']} queries")
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if os.path.exists(tf):
+        with open(tf) as f:
+            tj = json.load(f)
+        if tj.get("src_hash") == src_hash(ATTN_SRC) and tj.get("workload") == wl.name:
+            traffic = tj.get("bytes_per_launch")
+
+    decode = None
+    if not args.no_decode:
+        decode = bench_decode(args, dev)
+        log(f"[bench] decode {decode['tokens_per_s']:.0f} tok/s ({decode['ms_per_step']:.3f} ms/step)")
+
+    cpu = None
+    if not args.no_cpu:
+        try:
+            cpu = cpu_baseline(res, workers_pool)
+            log(f"[bench] cpu oracle {cpu['value']:.2f} queries/s, parity sample "
+                f"{cpu['parity_sample']}")
+        except Exception as e:  # report, never hide
+            log(f"[bench] cpu baseline failed: {e!r}")
+            cpu = {"value": None, "error": repr(e)}
+
+    if workers_pool is not None:
+        workers_pool.close()
+        workers_pool.join()
+    value = res["n"] / (res["ms_per_step"] / 1e3)
+    line = {
+        "metric": "LSA layer prefill queries/s at T=10M (32k chunk); decode tok/s; % roofline",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "context_tokens": wl.T, "chunk_queries": wl.chunk,
+                   "index": f"Flat p={wl.pool} blocks={wl.block} buckets={wl.buckets} iters={wl.iters}"
+                   + (f" tree G={wl.tree_group} S={wl.tree_super} R={wl.tree_top}" if wl.tree_group else ""),
+                   "select": f"{wl.budget}+{wl.window}+{wl.sinks}",
+                   "attention": f"GQA {wl.Hq}/{wl.Hkv} D={wl.D} bf16"},
+        "roofline": {"kernel": "k_attn (sparse GQA attention)", "bound": "hbm",
+                     "achieved": res["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": res["achieved_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": res["attn_bytes"],
+                     "avg_launch_ms": res["attn_ms"]},
+        "cpu_baseline": cpu,
+        "phases_ms": {"append": res["phase_ms"][0], "select": res["phase_ms"][1],
+                      "attention": res["phase_ms"][2]},
+        "fused_entry_point_identical": res["fused_same"],
+        "selected_keys_per_query": res["cnt_mean"],
+        "index_build_keys_per_s": wl.T / (res["build_ms"] * 1e-3),
+        "decode": decode,
+        "dense_scan": dense,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
