@@ -117,13 +117,15 @@ def bench_prefill(args, dev):
     out = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
     qpos = torch.arange(t0, wl.T, dtype=torch.int32, device=dev)
     lk_chunk = latk[t0:]
+    sel_ws = torch.empty(max(L.workspace_bytes(L.binding.OP_SELECT, ix.params, sp, None, n), 256),
+                         dtype=torch.uint8, device=dev)
 
     def step(evs=None):
         ix.restore(snap)
         if evs: evs[0].record()
         ix.append(lk_chunk)
         if evs: evs[1].record()
-        ix.select(latq, qpos, sp, idx=idx, cnt=cnt)
+        ix.select(latq, qpos, sp, idx=idx, cnt=cnt, ws=sel_ws)
         if evs: evs[2].record()
         L.sparse_attn(q, K, V, idx, cnt, ap, out=out)
         if evs: evs[3].record()

@@ -200,7 +200,10 @@ class LsaIndex:
 
     def select(self, latq: torch.Tensor, qpos: torch.Tensor, sp: SelectParams,
                idx: Optional[torch.Tensor] = None, cnt: Optional[torch.Tensor] = None,
-               stream=None):
+               ws: Optional[torch.Tensor] = None, use_workspace: bool = True, stream=None):
+        """Select keys for each query.  With a workspace (allocated here unless
+        given) large Flat batches take the single-scan list path; without one
+        (use_workspace=False) every query takes the exact refinement path."""
         nq = latq.shape[0]
         _need(latq, torch.int8, "latq", (nq, 64))
         _need(qpos, torch.int32, "qpos", (nq,))
@@ -210,8 +213,14 @@ class LsaIndex:
             cnt = torch.empty((nq,), dtype=torch.int32, device=latq.device)
         _need(idx, torch.int32, "idx", (nq, sp.max_sel))
         _need(cnt, torch.int32, "cnt", (nq,))
+        if use_workspace and ws is None:
+            ws = torch.empty(max(workspace_bytes(OP_SELECT, self.params, sp, None, nq), 256),
+                             dtype=torch.uint8, device=latq.device)
+        if not use_workspace:
+            ws = None
         _check(lib().lsa_select(self._desc, _ptr(latq), _ptr(qpos), nq, ctypes.byref(sp),
-                                _ptr(idx), _ptr(cnt), None, 0, _stream(stream)), "lsa_select")
+                                _ptr(idx), _ptr(cnt), _ptr(ws), ws.numel() if ws is not None else 0,
+                                _stream(stream)), "lsa_select")
         return idx, cnt
 
     def prefill_chunk(self, latk_chunk: torch.Tensor, latq: torch.Tensor, q: torch.Tensor,
@@ -231,17 +240,13 @@ class LsaIndex:
                               device=q.device)
         if (idx is None) != (cnt is None):
             raise LsaError("pass both idx and cnt or neither")
-        wsb = 0
-        if idx is None:
-            wsb = workspace_bytes(OP_PREFILL, self.params, sp, ap, n)
-            if ws is None or ws.numel() < wsb:
-                ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        wsb = workspace_bytes(OP_PREFILL, self.params, sp, ap, n)
+        if ws is None or ws.numel() < wsb:
+            ws = torch.empty(wsb, dtype=torch.uint8, device=q.device)
         _check(lib().lsa_prefill_chunk(self._desc, _ptr(latk_chunk), n, _ptr(latq), _ptr(q),
                                        _ptr(k), _ptr(v), k.shape[0], ctypes.byref(sp),
                                        ctypes.byref(ap), _ptr(out), _ptr(idx), _ptr(cnt),
-                                       _ptr(ws) if idx is None else None,
-                                       ws.numel() if (idx is None and ws is not None) else 0,
-                                       _stream(stream)), "lsa_prefill_chunk")
+                                       _ptr(ws), ws.numel(), _stream(stream)), "lsa_prefill_chunk")
         return out
 
 

@@ -37,6 +37,7 @@ int hip_fail(hipError_t e, const char* where) {
   } while (0)
 
 constexpr int64_t kAlign = 256;
+constexpr int kFastSelectMinQ = 64;
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int check_index_params(const lsa_index_params* p) {
@@ -214,7 +215,7 @@ int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
 
 int select_impl(const Index* h, const int8_t* latq, const int32_t* qpos, int32_t qpos_base,
                 int32_t nq, const lsa_select_params* sp, int32_t* idx, int32_t* cnt,
-                hipStream_t s) {
+                void* ws, size_t ws_bytes, hipStream_t s) {
   IdxView v = view_of(h);
   if (v.leafsup && v.n_sup > 2048)
     return fail(LSA_E_UNSUPPORTED, "%d super clusters (at most 2048)", v.n_sup);
@@ -222,8 +223,12 @@ int select_impl(const Index* h, const int8_t* latq, const int32_t* qpos, int32_t
   a.latq = latq; a.qpos = qpos; a.qpos_base = qpos_base; a.nq = nq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
   a.max_sel = max_sel_of(sp);
-  a.idx = idx; a.cnt = cnt;
-  LSA_HIP(launch_select(v, a, nullptr, s), "select");
+  a.idx = idx; a.cnt = cnt; a.only = nullptr;
+  if (!v.leafsup && nq >= kFastSelectMinQ && ws && ws_bytes >= select_fast_ws_bytes(nq)) {
+    LSA_HIP(launch_select_fast(v, a, ws, s), "select");
+  } else {
+    LSA_HIP(launch_select(v, a, nullptr, s), "select");
+  }
   return LSA_OK;
 }
 
@@ -298,12 +303,16 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
   if (n < 0) return fail(LSA_E_ARG, "n < 0");
   (void)iprm;
   switch (op) {
-    case LSA_OP_BUILD: case LSA_OP_APPEND: case LSA_OP_SELECT: case LSA_OP_ATTN: case LSA_OP_DENSE:
+    case LSA_OP_BUILD: case LSA_OP_APPEND: case LSA_OP_ATTN: case LSA_OP_DENSE:
       *bytes = 0;
+      return LSA_OK;
+    case LSA_OP_SELECT:
+      *bytes = select_fast_ws_bytes((int32_t)n);
       return LSA_OK;
     case LSA_OP_PREFILL: {
       if (int e = check_select_params(sprm, false)) return e;
-      *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4);
+      *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4) +
+               select_fast_ws_bytes((int32_t)n);
       return LSA_OK;
     }
     case LSA_OP_DECODE: {
@@ -360,13 +369,13 @@ int lsa_append_keys(lsa_index* hh, const int8_t* d_latk_new, int64_t n, void* d_
 int lsa_select(const lsa_index* hh, const int8_t* d_latq, const int32_t* d_qpos, int32_t nq,
                const lsa_select_params* sp, int32_t* d_idx, int32_t* d_cnt, void* d_ws,
                size_t ws_bytes, void* stream) {
-  (void)d_ws; (void)ws_bytes;
   const Index* h = as_index(hh);
   if (int e = check_index(h)) return e;
   if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
   if (nq < 0) return fail(LSA_E_ARG, "nq < 0");
   if (nq > 0 && (!d_latq || !d_qpos || !d_idx || !d_cnt)) return fail(LSA_E_ARG, "NULL buffer");
-  return select_impl(h, d_latq, d_qpos, 0, nq, sp, d_idx, d_cnt, static_cast<hipStream_t>(stream));
+  return select_impl(h, d_latq, d_qpos, 0, nq, sp, d_idx, d_cnt, d_ws, ws_bytes,
+                     static_cast<hipStream_t>(stream));
 }
 
 int lsa_sparse_attn(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v, int64_t kv_rows,
@@ -400,12 +409,14 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
   const int32_t max_sel = max_sel_of(sp);
   int32_t* idx = d_idx_opt;
   int32_t* cnt = d_cnt_opt;
-  const size_t need = (size_t)align_up(n_chunk * max_sel * 4) + (size_t)align_up(n_chunk * 4);
+  const size_t a_idx = (size_t)align_up(n_chunk * max_sel * 4) + (size_t)align_up(n_chunk * 4);
+  const size_t need = a_idx + select_fast_ws_bytes((int32_t)n_chunk);
+  if (!d_ws || ws_bytes < need) return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
   if (!idx || !cnt) {
-    if (!d_ws || ws_bytes < need) return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
     idx = static_cast<int32_t*>(d_ws);
     cnt = reinterpret_cast<int32_t*>(static_cast<char*>(d_ws) + align_up(n_chunk * max_sel * 4));
   }
+  void* sel_ws = static_cast<char*>(d_ws) + a_idx;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t t0 = h->T;
   if (h->T == 0 && h->prm.tree_group > 0) {
@@ -414,7 +425,8 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
   Index saved = *h;
   int rc = append_impl(h, d_latk_chunk, n_chunk, s);
   if (rc != LSA_OK) { *h = saved; return rc; }
-  rc = select_impl(h, d_latq, nullptr, (int32_t)t0, (int32_t)n_chunk, sp, idx, cnt, s);
+  rc = select_impl(h, d_latq, nullptr, (int32_t)t0, (int32_t)n_chunk, sp, idx, cnt, sel_ws,
+                   select_fast_ws_bytes((int32_t)n_chunk), s);
   if (rc != LSA_OK) return rc;
   LSA_HIP(launch_attn(d_q, d_k, d_v, kv_rows, 0, (int32_t)n_chunk, idx, cnt, max_sel,
                       (int32_t)n_chunk, *ap, d_out, nullptr, 1, s),
@@ -430,10 +442,14 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   if (!hs || nseq < 1 || nseq > 16) return fail(LSA_E_ARG, "nseq %d not in [1, 16]", nseq);
   if (int e = check_attn_params(ap)) return e;
   if (!d_latk_new || !d_latq || !d_q || !d_k || !d_v || !d_out) return fail(LSA_E_ARG, "NULL buffer");
+  const Index* h0 = as_index(hs[0]);
+  if (int e = check_index(h0)) return e;
   for (int i = 0; i < nseq; ++i) {
     const Index* h = as_index(hs[i]);
     if (int e = check_index(h)) return e;
     if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
+    if (memcmp(&h->prm, &h0->prm, sizeof h->prm) != 0)
+      return fail(LSA_E_ARG, "sequence %d has different index params", i);
     if (h->T + 1 > h->prm.max_tokens) return fail(LSA_E_CAPACITY, "sequence %d is full", i);
     if (seq_stride_rows < h->T + 1) return fail(LSA_E_ARG, "seq_stride_rows < T + 1 for sequence %d", i);
     for (int j = 0; j < i; ++j)
@@ -450,18 +466,62 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + a_idx);
   void* att = ws + a_idx + a_cnt;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int p = h0->prm.pool, N = h0->prm.block;
+
+  // 1. append one key per sequence: one batched launch; a sequence whose key
+  //    completes a block (a k-means is due) takes the general path
+  DecodeAppendArgs da;
+  memset(&da, 0, sizeof da);
+  da.off_pooled = h0->off_pooled; da.off_cent = h0->off_cent; da.off_bcnt = h0->off_bcnt;
+  da.off_boff = h0->off_boff; da.off_bmem = h0->off_bmem; da.off_bfirst = h0->off_bfirst;
+  da.off_blast = h0->off_blast; da.off_pend = h0->off_pend;
+  da.p = p; da.N = N; da.C = h0->prm.buckets;
+  int32_t qpos[16];
+  bool any_batched = false;
   for (int i = 0; i < nseq; ++i) {
     Index* h = as_index(hs[i]);
-    const int64_t t = h->T;
+    qpos[i] = (int32_t)h->T;
+    const int np = (int)(h->T - h->n_pool * p);
+    const bool completes_group = np + 1 == p;
+    const bool completes_block = completes_group && (h->n_pool + 1) % N == 0;
     if (h->T == 0 && h->prm.tree_group > 0)
       LSA_HIP(fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s), "fill");
-    Index saved = *h;
-    int rc = append_impl(h, d_latk_new + (int64_t)i * kDim, 1, s);
-    if (rc != LSA_OK) { *h = saved; return rc; }
-    rc = select_impl(h, d_latq + (int64_t)i * kDim, nullptr, (int32_t)t, 1, sp,
-                     idx + (int64_t)i * max_sel, cnt + i, s);
-    if (rc != LSA_OK) return rc;
+    if (completes_block) {
+      Index saved = *h;
+      int rc = append_impl(h, d_latk_new + (int64_t)i * kDim, 1, s);
+      if (rc != LSA_OK) { *h = saved; return rc; }
+      continue;
+    }
+    da.arena[i] = h->arena;
+    da.n_pool[i] = h->n_pool; da.n_full[i] = h->n_full;
+    da.n_pend[i] = np; da.pend_slot[i] = h->pend_slot;
+    da.batched[i] = 1;
+    any_batched = true;
   }
+  if (any_batched) LSA_HIP(launch_decode_append(da, d_latk_new, nseq, s), "decode append");
+  for (int i = 0; i < nseq; ++i) {
+    if (!da.batched[i]) continue;
+    Index* h = as_index(hs[i]);
+    const int np = (int)(h->T - h->n_pool * p);
+    h->T += 1;
+    if (np + 1 == p) h->n_pool += 1;
+  }
+
+  // 2. select: one workgroup per sequence, each on its own index
+  IdxView views[16];
+  for (int i = 0; i < nseq; ++i) {
+    views[i] = view_of(as_index(hs[i]));
+    if (views[i].leafsup && views[i].n_sup > 2048)
+      return fail(LSA_E_UNSUPPORTED, "%d super clusters (at most 2048)", views[i].n_sup);
+  }
+  SelArgs a;
+  memset(&a, 0, sizeof a);
+  a.latq = d_latq; a.qpos = nullptr; a.qpos_base = 0; a.nq = nseq;
+  a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
+  a.max_sel = max_sel; a.idx = idx; a.cnt = cnt; a.only = nullptr;
+  LSA_HIP(launch_select_multi(views, qpos, nseq, a, s), "decode select");
+
+  // 3. split-K attention over each sequence's own rows, then the merge
   LSA_HIP(launch_attn(d_q, d_k, d_v, seq_stride_rows, seq_stride_rows, 1, idx, cnt, max_sel,
                       nseq, *ap, d_out, att, kDecodeSplits, s),
           "decode attention");
@@ -485,7 +545,7 @@ int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, cons
   a.latq = d_latq; a.qpos = d_qpos; a.qpos_base = 0; a.nq = nq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = 0;
   a.max_sel = max_sel_of(sp);
-  a.idx = d_idx; a.cnt = d_cnt;
+  a.idx = d_idx; a.cnt = d_cnt; a.only = nullptr;
   LSA_HIP(launch_select(v, a, nullptr, static_cast<hipStream_t>(stream)), "dense select");
   return LSA_OK;
 }

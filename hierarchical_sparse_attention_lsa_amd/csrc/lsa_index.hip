@@ -265,6 +265,45 @@ k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0
   }
 }
 
+// ---------------------------------------------------------------- decode append
+// One new key per sequence (workgroup i = sequence i, thread = dimension).
+// The key joins its sequence's pending partial group; when the group
+// completes it is pooled into a new tail singleton bucket.  Sequences whose
+// append completes a block are handled by the general path instead.
+__global__ void __launch_bounds__(64) k_decode_append(DecodeAppendArgs a, const int8_t* __restrict__ src) {
+  const int i = blockIdx.x, d = threadIdx.x;
+  if (!a.batched[i]) return;
+  char* base = a.arena[i];
+  int8_t* pend = reinterpret_cast<int8_t*>(base + a.off_pend) + (int64_t)a.pend_slot[i] * a.p * kDim;
+  const int8_t val = src[(int64_t)i * kDim + d];
+  const int np = a.n_pend[i];
+  if (np + 1 < a.p) {
+    pend[np * kDim + d] = val;
+    return;
+  }
+  int sum = val;
+  for (int r = 0; r < np; ++r) sum += pend[r * kDim + d];
+  const int64_t g = a.n_pool[i];
+  const int8_t pv = (int8_t)rhe_div(sum, a.p);
+  reinterpret_cast<int8_t*>(base + a.off_pooled)[g * kDim + d] = pv;
+  const int64_t nf = a.n_full[i];
+  const int64_t beta = nf * a.C + (g - nf * a.N);
+  reinterpret_cast<int8_t*>(base + a.off_cent)[beta * kDim + d] = pv;
+  if (d == 0) {
+    reinterpret_cast<int32_t*>(base + a.off_bcnt)[beta] = 1;
+    reinterpret_cast<int32_t*>(base + a.off_boff)[beta] = (int32_t)g;
+    reinterpret_cast<int32_t*>(base + a.off_bmem)[g] = (int32_t)g;
+    reinterpret_cast<int32_t*>(base + a.off_bfirst)[beta] = (int32_t)g;
+    reinterpret_cast<int32_t*>(base + a.off_blast)[beta] = (int32_t)g;
+  }
+}
+
+hipError_t launch_decode_append(const DecodeAppendArgs& a, const int8_t* src, int nseq,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(k_decode_append, dim3(nseq), dim3(64), 0, s, a, src);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_pool(const int8_t* pend, int32_t n_pend, const int8_t* src, int64_t n_src,
                        int32_t p, int8_t* pooled_out, int64_t n_groups, hipStream_t s) {

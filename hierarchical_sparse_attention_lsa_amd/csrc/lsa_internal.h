@@ -60,9 +60,26 @@ struct SelArgs {
   int32_t max_sel;
   int32_t* idx;           // [nq][max_sel]
   int32_t* cnt;           // [nq]
+  const int32_t* only;    // nullable: serve only queries with only[q] != 0
+};
+
+// Batched one-key append for decode (all indexes share one layout).
+struct DecodeAppendArgs {
+  char* arena[16];
+  int64_t n_pool[16];
+  int64_t n_full[16];
+  int32_t n_pend[16];
+  int32_t pend_slot[16];
+  int32_t batched[16];
+  int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast, off_pend;
+  int32_t p, N, C;
 };
 
 // ---- launchers (return hipError_t) ----
+hipError_t launch_decode_append(const DecodeAppendArgs& a, const int8_t* src, int nseq,
+                                hipStream_t s);
+hipError_t launch_select_multi(const IdxView* views, const int32_t* qpos, int32_t nseq,
+                               const SelArgs& a, hipStream_t s);
 hipError_t launch_pool(const int8_t* pend, int32_t n_pend, const int8_t* src, int64_t n_src,
                        int32_t p, int8_t* pooled_out, int64_t n_groups, hipStream_t s);
 hipError_t launch_save_pending(const int8_t* pend, int32_t n_pend, const int8_t* src,
@@ -77,6 +94,9 @@ hipError_t launch_tail(const int8_t* pooled, int64_t g0, int64_t g1, int64_t n_f
 
 size_t select_ws_bytes(int32_t nq);
 hipError_t launch_select(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
+// large Flat batches: list-based single full pass (+ exact kernel for flagged queries)
+size_t select_fast_ws_bytes(int32_t nq);
+hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
 
 size_t attn_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t splits);
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_rows,

@@ -30,28 +30,24 @@
 //   4. emit: the taken buckets sorted by id, their eligible keys written in
 //      ascending position, then sinks and window.
 #include <climits>
+#include <cstring>
 
 #include "lsa_device.h"
 #include "lsa_internal.h"
+#include "lsa_select_common.h"
 
 namespace lsa {
 
 namespace {
+using namespace sel;
 
-constexpr int QT = 16;        // queries per workgroup (MFMA rows)
-constexpr int SW = 4;         // waves per workgroup
-constexpr int ST = SW * 64;
+constexpr int QT = 16;        // MFMA rows (query slots) per workgroup
 constexpr int NB = 256;       // histogram bins
 constexpr int CAP = 256;      // bracket buckets resolved by sorting
 constexpr int EMIT_MAX = 4096;  // taken buckets per query (budget <= 4096)
 constexpr int MAXSUPW = 64;   // Tree: up to 2048 super clusters (bitmask words)
 constexpr int SAMPLE_TILES = 1024;
-constexpr long long KOFF = 1ll << 21;
-constexpr long long KMINP = (-(1ll << 20) + KOFF) << 32;
-constexpr long long KMAXP = (((1ll << 20) + KOFF) << 32) | 0xffffffffll;
-
-enum { ST_REFINE = 1, ST_DONE = 2 };
-
+template <int SW, int NQ>
 struct __attribute__((aligned(16))) SelLds {
   long long lo[QT], hi[QT];
   long long ssum[QT];
@@ -66,102 +62,76 @@ struct __attribute__((aligned(16))) SelLds {
   int any_refine;
   unsigned supmask[QT][MAXSUPW];
   union {
-    struct { int hk[QT][NB]; int hb[QT][NB]; } h;
-    long long cand[QT][CAP];
-    int emit[SW][EMIT_MAX];
+    struct { int hk[NQ][NB]; int hb[NQ][NB]; } h;
+    long long cand[NQ][CAP];
+    int emit[(SW < NQ ? SW : NQ)][EMIT_MAX];
+    long long supkeys[(SW < NQ ? SW : NQ)][2048];
   } u;
 };
 
-__device__ __forceinline__ long long order_key(int s, int beta) {
-  return ((long long)(s + KOFF) << 32) | (long long)(0xffffffffu - (unsigned)beta);
-}
 
-// Number of keys of a bucket that are < x (members ascending, p keys each).
-__device__ __forceinline__ int keys_below(const int32_t* __restrict__ mem, int cnt, int p, int x) {
-  int lo = 0, hi = cnt;  // first member with m*p + p > x
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((long long)mem[mid] * p + p <= x) lo = mid + 1; else hi = mid;
-  }
-  int r = lo * p;
-  if (lo < cnt) r += min(p, max(0, x - mem[lo] * p));
-  return r;
-}
-
-struct BucketInfo {
-  int first, last, cnt, off;
+// Per-launch index views: one shared index (prefill, nviews == 1) or one
+// index per workgroup (decode: workgroup b serves sequence b, one query).
+struct IdxViews {
+  IdxView v[16];
+  int32_t qpos[16];
+  int32_t nviews;
 };
 
-// Eligible long-range keys of a bucket for the query at t: keys j with
-// sinks <= j <= t - window.  They form one run [klo, klo + e) of the
-// bucket's ascending key list.
-template <bool DENSE>
-__device__ __forceinline__ int eligible(const IdxView& V, int beta, const BucketInfo& b, int t,
-                                        int window, int sinks, int* klo) {
-  const int hiK = t - window;
-  *klo = 0;
-  if (DENSE) return (beta >= sinks && beta <= hiK) ? 1 : 0;
-  if (b.cnt <= 0) return 0;
-  const int p = V.pool;
-  const long long kf = (long long)b.first * p;
-  const long long kl = (long long)b.last * p + p - 1;
-  if (kf >= sinks && kl <= hiK) return b.cnt * p;
-  if (kl < sinks || kf > hiK || hiK < sinks) return 0;
-  const int32_t* m = V.bmem + b.off;
-  const int a = keys_below(m, b.cnt, p, sinks);
-  const int z = keys_below(m, b.cnt, p, hiK + 1);
-  *klo = a;
-  return z - a;
-}
-
-template <bool DENSE>
-__device__ __forceinline__ BucketInfo load_bucket(const IdxView& V, int beta) {
-  BucketInfo b;
-  if (DENSE || beta >= V.n_bkt) { b.first = beta; b.last = beta; b.cnt = beta < V.n_bkt; b.off = beta; return b; }
-  b.first = V.bfirst[beta];
-  b.last = V.blast[beta];
-  b.cnt = V.bcnt[beta];
-  b.off = V.boff[beta];
-  return b;
-}
-
-// Key at position k of a bucket's ascending key list.
-template <bool DENSE>
-__device__ __forceinline__ int bucket_key(const IdxView& V, int beta, const BucketInfo& b, int k) {
-  if (DENSE) return beta;
-  const int p = V.pool;
-  return V.bmem[b.off + k / p] * p + k % p;
-}
-
-// Bitonic sort (ascending) of n_pow2 int32 / int64 in LDS by one wave.
-template <class T>
-__device__ void wave_bitonic(T* a, int n) {
+// Runs f(bt, scores) for tiles first, first+step, ... < ntiles, with the
+// centroid operands of PU tiles in flight ahead of the MFMA (double-buffered
+// ring), so a wave never waits on one load at a time.
+template <int PU, class F>
+__device__ __forceinline__ void scan_tiles(const IdxView& V, const v4i& qa, int first, int step,
+                                           int ntiles, F&& f) {
   const int lane = lane_id();
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = lane; i < n; i += 64) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const T x = a[i], y = a[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) { a[i] = y; a[ixj] = x; }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int8_t* cbase = V.cent + 16 * (lane >> 4);
+  v4i cur[PU], nxt[PU];
+  auto load = [&](v4i* dst, int base) {
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int bt = base + u * step;
+      const int beta = bt * 16 + (lane & 15);
+      dst[u] = (bt < ntiles && beta < V.n_bkt)
+                   ? *reinterpret_cast<const v4i*>(cbase + (int64_t)beta * kDim)
+                   : v4i{0, 0, 0, 0};
     }
+  };
+  load(cur, first);
+  for (int base = first; base < ntiles; base += PU * step) {
+    const int nb = base + PU * step;
+    if (nb < ntiles) load(nxt, nb);
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int bt = base + u * step;
+      if (bt < ntiles) {
+        const v4i z = {0, 0, 0, 0};
+        f(bt, mfma_i8_16x16x64(qa, cur[u], z));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PU; ++u) cur[u] = nxt[u];
   }
 }
 
-template <bool DENSE, bool TREE>
-__global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
-  __shared__ SelLds S;
+template <bool DENSE, bool TREE, int SW, int NQ>
+__global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
+  constexpr int ST = SW * 64;
+  constexpr int PU = SW >= 16 ? 2 : 4;   // centroid tiles in flight per wave
+  __shared__ SelLds<SW, NQ> S;
+  // this workgroup's index view, read from the kernel-argument segment (VS is
+  // the first argument) so the runtime index does not copy VS to scratch
+  const IdxViews* vsp = (const IdxViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  const IdxView V = vsp->v[VS.nviews > 1 ? blockIdx.x : 0];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int q0 = blockIdx.x * QT;
-  const int nqt = min(QT, A.nq - q0);
+  const int q0 = blockIdx.x * NQ;
+  const int nqt = min(NQ, A.nq - q0);
   const int B = A.budget;
+  const int qrow = 4 * (lane >> 4);     // first query slot of this lane's score rows
+  // nothing to do for this workgroup (all its queries masked out)
+  if (!__syncthreads_or(tid < nqt && (!A.only || A.only[q0 + tid]))) return;
 
-  // ---- query operand (rows beyond nq are zero) ----
+  // ---- query operand (slots beyond the workgroup's queries are zero) ----
   v4i qa = {0, 0, 0, 0};
   {
     const int r = lane & 15;
@@ -169,24 +139,22 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
   }
   if (tid < QT) {
     const int qi = q0 + tid;
-    S.t[tid] = tid < nqt ? (A.qpos ? A.qpos[qi] : A.qpos_base + qi) : -1;
-    S.status[tid] = tid < nqt ? ST_REFINE : ST_DONE;
+    const bool val = tid < nqt && (!A.only || A.only[qi]);
+    S.t[tid] = val ? max(0, VS.nviews > 1 ? vsp->qpos[blockIdx.x] : (A.qpos ? A.qpos[qi] : A.qpos_base + qi)) : -1;
+    S.status[tid] = val ? ST_REFINE : ST_DONE;
     S.smax[tid] = INT_MIN; S.ssum[tid] = 0; S.sn[tid] = 0; S.above[tid] = 0;
     S.nfull[tid] = 0; S.ncand[tid] = 0; S.fullsum[tid] = 0; S.pbeta[tid] = -1; S.ptake[tid] = 0;
     S.lo[tid] = KMINP; S.hi[tid] = KMAXP;
-    if (tid < nqt && B <= 0) { S.status[tid] = ST_DONE; S.lo[tid] = KMAXP + 1; S.hi[tid] = KMAXP; }
+    if (val && B <= 0) { S.status[tid] = ST_DONE; S.lo[tid] = KMAXP + 1; S.hi[tid] = KMAXP; }
   }
-  if (TREE) {
-    // candidate super clusters: the tree_top best by (score desc, id asc)
+  if (TREE)
     for (int e = tid; e < QT * MAXSUPW; e += ST) (&S.supmask[0][0])[e] = 0u;
-  }
   __syncthreads();
   if (TREE) {
-    // one wave per query: score every super centroid, keep the top R
-    long long* keys = reinterpret_cast<long long*>(&S.u.emit[0][0]);   // [SW][2048]
+    // candidate super clusters: the tree_top best by (score desc, id asc); one wave per query
     const int nsp = 1 << (32 - __clz(max(V.n_sup, 2) - 1));
     for (int qi = wave; qi < nqt; qi += SW) {
-      long long* kk = keys + wave * 2048;
+      long long* kk = S.u.supkeys[wave];
       const int8_t* qv = A.latq + (int64_t)(q0 + qi) * kDim;
       for (int s = lane; s < nsp; s += 64) {
         long long key = LLONG_MAX;        // padding sorts last
@@ -212,8 +180,14 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
     }
     __syncthreads();
   }
+  auto is_cand = [&](int sup, int qi) -> bool {
+    return !TREE || sup < 0 || ((S.supmask[qi][sup >> 5] >> (sup & 31)) & 1u);
+  };
 
   const int ntiles = (V.n_bkt + 15) >> 4;
+  int tq[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) tq[v] = S.t[qrow + v];
 
   // ---- 1. sampled statistics ----
   {
@@ -222,30 +196,21 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
     long long ssum[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) { smax[v] = INT_MIN; sn[v] = 0; ssum[v] = 0; }
-    int tq[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) tq[v] = S.t[4 * (lane >> 4) + v];
-    for (int bt = wave * stride; bt < ntiles; bt += SW * stride) {
+    scan_tiles<PU>(V, qa, wave * stride, SW * stride, ntiles, [&](int bt, const v4i& sc) {
       const int beta = bt * 16 + (lane & 15);
-      v4i cb = {0, 0, 0, 0};
-      if (beta < V.n_bkt) cb = *reinterpret_cast<const v4i*>(V.cent + (int64_t)beta * kDim + 16 * (lane >> 4));
-      const v4i z = {0, 0, 0, 0};
-      const v4i sc = mfma_i8_16x16x64(qa, cb, z);
-      if (beta >= V.n_bkt) continue;
+      if (beta >= V.n_bkt) return;
       const BucketInfo bi = load_bucket<DENSE>(V, beta);
       const int sup = TREE ? V.leafsup[beta] : -1;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        if (tq[v] < 0) continue;
-        if (TREE && sup >= 0 && !((S.supmask[4 * (lane >> 4) + v][sup >> 5] >> (sup & 31)) & 1u)) continue;
+        if (tq[v] < 0 || !is_cand(sup, qrow + v)) continue;
         int klo;
-        const int e = eligible<DENSE>(V, beta, bi, tq[v], A.window, A.sinks, &klo);
-        if (e <= 0) continue;
+        if (eligible<DENSE>(V, beta, bi, tq[v], A.window, A.sinks, &klo) <= 0) continue;
         smax[v] = max(smax[v], sc[v]);
         ssum[v] += sc[v];
         sn[v] += 1;
       }
-    }
+    });
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
 #pragma unroll
@@ -254,22 +219,19 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
         sn[v] += __shfl_xor(sn[v], m);
         ssum[v] += shfl_xor_i64(ssum[v], m);
       }
-      if ((lane & 15) == 0) {
-        const int qi = 4 * (lane >> 4) + v;
-        atomicMax(&S.smax[qi], smax[v]);
-        atomicAdd(&S.sn[qi], sn[v]);
-        atomicAdd((unsigned long long*)&S.ssum[qi], (unsigned long long)ssum[v]);
+      if ((lane & 15) == 0 && qrow + v < NQ) {
+        atomicMax(&S.smax[qrow + v], smax[v]);
+        atomicAdd(&S.sn[qrow + v], sn[v]);
+        atomicAdd((unsigned long long*)&S.ssum[qrow + v], (unsigned long long)ssum[v]);
       }
     }
     __syncthreads();
-    if (tid < QT && S.status[tid] == ST_REFINE) {
-      if (S.sn[tid] > 0) {
-        const int mx = S.smax[tid];
-        const int mean = (int)(S.ssum[tid] / S.sn[tid]);
-        const int slo = mx - (mx - mean) / 2;
-        S.lo[tid] = (long long)(slo + KOFF) << 32;
-        S.hi[tid] = ((long long)(mx + KOFF) << 32) | 0xffffffffll;
-      }
+    if (tid < NQ && S.status[tid] == ST_REFINE && S.sn[tid] > 0) {
+      const int mx = S.smax[tid];
+      const int mean = (int)(S.ssum[tid] / S.sn[tid]);
+      const int slo = mx - (mx - mean) / 2;
+      S.lo[tid] = (long long)(slo + KOFF) << 32;
+      S.hi[tid] = ((long long)(mx + KOFF) << 32) | 0xffffffffll;
     }
     __syncthreads();
   }
@@ -278,11 +240,11 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
   for (int pass = 0; pass < 16; ++pass) {
     if (tid == 0) {
       int any = 0;
-      for (int i = 0; i < QT; ++i) any |= S.status[i] == ST_REFINE;
+      for (int i = 0; i < NQ; ++i) any |= S.status[i] == ST_REFINE;
       S.any_refine = any;
     }
-    for (int e = tid; e < QT * NB; e += ST) { (&S.u.h.hk[0][0])[e] = 0; (&S.u.h.hb[0][0])[e] = 0; }
-    if (tid < QT) {
+    for (int e = tid; e < NQ * NB; e += ST) { (&S.u.h.hk[0][0])[e] = 0; (&S.u.h.hb[0][0])[e] = 0; }
+    if (tid < NQ) {
       S.above[tid] = 0;
       const long long range = S.hi[tid] - S.lo[tid] + 1;
       int sh = 0;
@@ -293,35 +255,31 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
     if (!S.any_refine) break;
 
     long long lo[4], hi[4];
-    int slo[4], tq[4], sh[4], act[4], above[4];
+    int slo[4], sh[4], above[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int qi = 4 * (lane >> 4) + v;
-      act[v] = S.status[qi] == ST_REFINE;
-      lo[v] = S.lo[qi]; hi[v] = S.hi[qi];
-      slo[v] = (int)((lo[v] >> 32) - KOFF);
-      tq[v] = S.t[qi]; sh[v] = S.shift[qi]; above[v] = 0;
+      const int qi = qrow + v;
+      const bool act = qi < NQ && S.status[qi] == ST_REFINE;
+      lo[v] = act ? S.lo[qi] : 0; hi[v] = act ? S.hi[qi] : 0;
+      slo[v] = act ? (int)((lo[v] >> 32) - KOFF) : INT_MAX;
+      sh[v] = act ? S.shift[qi] : 0; above[v] = 0;
     }
-    for (int bt = wave; bt < ntiles; bt += SW) {
+    scan_tiles<PU>(V, qa, wave, SW, ntiles, [&](int bt, const v4i& sc) {
       const int beta = bt * 16 + (lane & 15);
-      v4i cb = {0, 0, 0, 0};
-      if (beta < V.n_bkt) cb = *reinterpret_cast<const v4i*>(V.cent + (int64_t)beta * kDim + 16 * (lane >> 4));
-      const v4i z = {0, 0, 0, 0};
-      const v4i sc = mfma_i8_16x16x64(qa, cb, z);
-      if (beta >= V.n_bkt) continue;
+      if (beta >= V.n_bkt) return;
       bool any = false;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) any |= act[v] && sc[v] >= slo[v];
-      if (!any) continue;
+      for (int v = 0; v < 4; ++v) any |= sc[v] >= slo[v];
+      if (!any) return;
       const BucketInfo bi = load_bucket<DENSE>(V, beta);
       const int sup = TREE ? V.leafsup[beta] : -1;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        if (!act[v] || sc[v] < slo[v]) continue;
+        if (sc[v] < slo[v]) continue;
         const long long K = order_key(sc[v], beta);
         if (K < lo[v]) continue;
-        const int qi = 4 * (lane >> 4) + v;
-        if (TREE && sup >= 0 && !((S.supmask[qi][sup >> 5] >> (sup & 31)) & 1u)) continue;
+        const int qi = qrow + v;
+        if (!is_cand(sup, qi)) continue;
         int klo;
         const int e = eligible<DENSE>(V, beta, bi, tq[v], A.window, A.sinks, &klo);
         if (e <= 0) continue;
@@ -330,24 +288,27 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
         atomicAdd(&S.u.h.hk[qi][bin], e);
         atomicAdd(&S.u.h.hb[qi][bin], 1);
       }
-    }
+    });
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
 #pragma unroll
       for (int m = 1; m < 16; m <<= 1) above[v] += __shfl_xor(above[v], m);
-      if ((lane & 15) == 0 && above[v]) atomicAdd(&S.above[4 * (lane >> 4) + v], above[v]);
+      if ((lane & 15) == 0 && above[v]) atomicAdd(&S.above[qrow + v], above[v]);
     }
     __syncthreads();
     // resolve: one wave per query
-    for (int qi = wave; qi < QT; qi += SW) {
+    for (int qi = wave; qi < NQ; qi += SW) {
       if (S.status[qi] != ST_REFINE) continue;
       const int A0 = S.above[qi];
       const long long lo_q = S.lo[qi], hi_q = S.hi[qi];
       const int shq = S.shift[qi];
-      // bins 4*lane .. 4*lane+3
-      int hk[4], hb[4], loc = 0;
+      int hk[NB / 64], hb[NB / 64], loc = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { hk[i] = S.u.h.hk[qi][4 * lane + i]; hb[i] = S.u.h.hb[qi][4 * lane + i]; loc += hk[i]; }
+      for (int i = 0; i < NB / 64; ++i) {
+        hk[i] = S.u.h.hk[qi][(NB / 64) * lane + i];
+        hb[i] = S.u.h.hb[qi][(NB / 64) * lane + i];
+        loc += hk[i];
+      }
       int tot;
       const int ex = wave_excl_scan(loc, &tot);
       if (lane == 0) {
@@ -361,8 +322,8 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
       if (A0 < B && A0 + tot >= B) {
         int cum = A0 + ex, found = -1, fb = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (found < 0 && cum + hk[i] >= B) { found = 4 * lane + i; fb = hb[i]; }
+        for (int i = 0; i < NB / 64; ++i) {
+          if (found < 0 && cum + hk[i] >= B) { found = (NB / 64) * lane + i; fb = hb[i]; }
           cum += hk[i];
         }
         const unsigned long long m = __ballot(found >= 0);
@@ -384,25 +345,21 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
   // ---- 3. collect: whole buckets above the bracket, sorted bracket ----
   {
     long long lo[4], hi[4];
-    int slo[4], tq[4];
+    int slo[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int qi = 4 * (lane >> 4) + v;
-      lo[v] = S.lo[qi]; hi[v] = S.hi[qi]; tq[v] = S.t[qi];
-      slo[v] = (int)((lo[v] >> 32) - KOFF);
-      if (tq[v] < 0 || lo[v] > KMAXP) slo[v] = INT_MAX;
+      const int qi = qrow + v;
+      const bool val = qi < NQ && tq[v] >= 0;
+      lo[v] = val ? S.lo[qi] : KMAXP + 1; hi[v] = val ? S.hi[qi] : KMAXP;
+      slo[v] = (!val || lo[v] > KMAXP) ? INT_MAX : (int)((lo[v] >> 32) - KOFF);
     }
-    for (int bt = wave; bt < ntiles; bt += SW) {
+    scan_tiles<PU>(V, qa, wave, SW, ntiles, [&](int bt, const v4i& sc) {
       const int beta = bt * 16 + (lane & 15);
-      v4i cb = {0, 0, 0, 0};
-      if (beta < V.n_bkt) cb = *reinterpret_cast<const v4i*>(V.cent + (int64_t)beta * kDim + 16 * (lane >> 4));
-      const v4i z = {0, 0, 0, 0};
-      const v4i sc = mfma_i8_16x16x64(qa, cb, z);
-      if (beta >= V.n_bkt) continue;
+      if (beta >= V.n_bkt) return;
       bool any = false;
 #pragma unroll
       for (int v = 0; v < 4; ++v) any |= sc[v] >= slo[v];
-      if (!any) continue;
+      if (!any) return;
       const BucketInfo bi = load_bucket<DENSE>(V, beta);
       const int sup = TREE ? V.leafsup[beta] : -1;
 #pragma unroll
@@ -410,8 +367,8 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
         if (sc[v] < slo[v]) continue;
         const long long K = order_key(sc[v], beta);
         if (K < lo[v]) continue;
-        const int qi = 4 * (lane >> 4) + v;
-        if (TREE && sup >= 0 && !((S.supmask[qi][sup >> 5] >> (sup & 31)) & 1u)) continue;
+        const int qi = qrow + v;
+        if (!is_cand(sup, qi)) continue;
         int klo;
         const int e = eligible<DENSE>(V, beta, bi, tq[v], A.window, A.sinks, &klo);
         if (e <= 0) continue;
@@ -424,7 +381,7 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
           if (c < CAP) S.u.cand[qi][c] = -K;      // ascending sort = K descending
         }
       }
-    }
+    });
     __syncthreads();
     // sort each query's bracket and take buckets until the budget is met
     for (int qi = wave; qi < nqt; qi += SW) {
@@ -467,52 +424,23 @@ __global__ void __launch_bounds__(ST) k_select(IdxView V, SelArgs A) {
 
   // ---- 4. emit keys ----
   for (int qi = wave; qi < nqt; qi += SW) {
+    if (S.t[qi] < 0) continue;
     int* em = S.u.emit[wave];
     const int64_t row = (int64_t)(q0 + qi) * A.max_sel;
     const int nfull = S.nfull[qi];
     const int pb = S.pbeta[qi];
     const int n = nfull + (pb >= 0 ? 1 : 0);
-    const int t = S.t[qi];
-    int np = 1;
-    while (np < n) np <<= 1;
-    for (int i = lane; i < np; i += 64) em[i] = i < nfull ? A.idx[row + i] : (i == nfull && pb >= 0 ? pb : INT_MAX);
+    for (int i = lane; i < n; i += 64) em[i] = i < nfull ? A.idx[row + i] : pb;
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (n > 1) wave_bitonic(em, np);
-    // take counts, exclusive offsets
-    int out = 0;
-    for (int base = 0; base < n; base += 64) {
-      const int i = base + lane;
-      int beta = -1, take = 0, klo = 0;
-      BucketInfo bi;
-      if (i < n) {
-        beta = em[i];
-        bi = load_bucket<DENSE>(V, beta);
-        const int e = eligible<DENSE>(V, beta, bi, t, A.window, A.sinks, &klo);
-        take = beta == pb ? S.ptake[qi] : e;
-      }
-      int tot;
-      const int off = out + wave_excl_scan(take, &tot);
-      // write this chunk's buckets one at a time, lanes over keys
-      for (int j = 0; j < 64 && base + j < n; ++j) {
-        const int bj = __shfl(beta, j), tj = __shfl(take, j), kj = __shfl(klo, j), oj = __shfl(off, j);
-        BucketInfo b;
-        b.first = __shfl(bi.first, j); b.last = __shfl(bi.last, j);
-        b.cnt = __shfl(bi.cnt, j); b.off = __shfl(bi.off, j);
-        for (int k = lane; k < tj; k += 64) A.idx[row + oj + k] = bucket_key<DENSE>(V, bj, b, kj + k);
-      }
-      out += tot;
-    }
-    // sinks not covered by the window, then the window
-    const int wstart = max(0, t - A.window + 1);
-    const int ns = max(0, min(A.sinks, wstart));
-    const int nw = t - wstart + 1;
-    for (int k = lane; k < ns; k += 64) A.idx[row + out + k] = k;
-    for (int k = lane; k < nw; k += 64) A.idx[row + out + ns + k] = wstart + k;
-    const int total = out + ns + nw;
-    for (int k = total + lane; k < A.max_sel; k += 64) A.idx[row + k] = -1;
-    if (lane == 0) A.cnt[q0 + qi] = total;
+    emit_row<DENSE>(V, em, n, pb, S.ptake[qi], S.t[qi], A.window, A.sinks, A.max_sel,
+                    A.idx + row, A.cnt + q0 + qi);
   }
+}
+
+template <bool DENSE, bool TREE, int SW, int NQ>
+hipError_t launch_k(const IdxViews& vs, const SelArgs& a, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_select<DENSE, TREE, SW, NQ>), dim3(grid), dim3(SW * 64), 0, s, vs, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -525,14 +453,33 @@ size_t select_ws_bytes(int32_t nq) {
 hipError_t launch_select(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s) {
   (void)ws;
   if (a.nq <= 0) return hipSuccess;
+  IdxViews vs;
+  memset(&vs, 0, sizeof vs);
+  vs.v[0] = v;
+  vs.nviews = 1;
   const unsigned grid = (unsigned)((a.nq + QT - 1) / QT);
-  if (v.dense)
-    hipLaunchKernelGGL((k_select<true, false>), dim3(grid), dim3(ST), 0, s, v, a);
-  else if (v.leafsup)
-    hipLaunchKernelGGL((k_select<false, true>), dim3(grid), dim3(ST), 0, s, v, a);
-  else
-    hipLaunchKernelGGL((k_select<false, false>), dim3(grid), dim3(ST), 0, s, v, a);
-  return hipGetLastError();
+  if (v.dense) return launch_k<true, false, 4, QT>(vs, a, grid, s);
+  if (v.leafsup) return launch_k<false, true, 4, QT>(vs, a, grid, s);
+  return launch_k<false, false, 4, QT>(vs, a, grid, s);
+}
+
+hipError_t launch_select_multi(const IdxView* views, const int32_t* qpos, int32_t nseq,
+                               const SelArgs& a, hipStream_t s) {
+  if (nseq <= 0) return hipSuccess;
+  IdxViews vs;
+  memset(&vs, 0, sizeof vs);
+  bool tree = false;
+  for (int i = 0; i < nseq; ++i) {
+    vs.v[i] = views[i];
+    vs.qpos[i] = qpos[i];
+    tree |= views[i].leafsup != nullptr;
+  }
+  vs.nviews = nseq;
+  SelArgs b = a;
+  b.nq = nseq;
+  // tree and flat sequences are served by the tree kernel (flat ones have no super level)
+  if (tree) return launch_k<false, true, 16, 1>(vs, b, (unsigned)nseq, s);
+  return launch_k<false, false, 16, 1>(vs, b, (unsigned)nseq, s);
 }
 
 }  // namespace lsa

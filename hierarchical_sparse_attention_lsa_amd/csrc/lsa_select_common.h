@@ -1,0 +1,150 @@
+// Helpers shared by the selection kernels: order keys, bucket eligibility,
+// key enumeration and a wave-level bitonic sort.
+#pragma once
+
+#include <climits>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+namespace sel {
+
+constexpr long long KOFF = 1ll << 21;
+constexpr long long KMINP = (-(1ll << 20) + KOFF) << 32;
+constexpr long long KMAXP = (((1ll << 20) + KOFF) << 32) | 0xffffffffll;
+
+enum { ST_REFINE = 1, ST_DONE = 2 };
+
+
+__device__ __forceinline__ long long order_key(int s, int beta) {
+  return ((long long)(s + KOFF) << 32) | (long long)(0xffffffffu - (unsigned)beta);
+}
+
+// Number of keys of a bucket that are < x (members ascending, p keys each).
+__device__ __forceinline__ int keys_below(const int32_t* __restrict__ mem, int cnt, int p, int x) {
+  int lo = 0, hi = cnt;  // first member with m*p + p > x
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((long long)mem[mid] * p + p <= x) lo = mid + 1; else hi = mid;
+  }
+  int r = lo * p;
+  if (lo < cnt) r += min(p, max(0, x - mem[lo] * p));
+  return r;
+}
+
+struct BucketInfo {
+  int first, last, cnt, off;
+};
+
+// Eligible long-range keys of a bucket for the query at t: keys j with
+// sinks <= j <= t - window.  They form one run [klo, klo + e) of the
+// bucket's ascending key list.
+template <bool DENSE>
+__device__ __forceinline__ int eligible(const IdxView& V, int beta, const BucketInfo& b, int t,
+                                        int window, int sinks, int* klo) {
+  const int hiK = t - window;
+  *klo = 0;
+  if (DENSE) return (beta >= sinks && beta <= hiK) ? 1 : 0;
+  if (b.cnt <= 0) return 0;
+  const int p = V.pool;
+  const long long kf = (long long)b.first * p;
+  const long long kl = (long long)b.last * p + p - 1;
+  if (kf >= sinks && kl <= hiK) return b.cnt * p;
+  if (kl < sinks || kf > hiK || hiK < sinks) return 0;
+  const int32_t* m = V.bmem + b.off;
+  const int a = keys_below(m, b.cnt, p, sinks);
+  const int z = keys_below(m, b.cnt, p, hiK + 1);
+  *klo = a;
+  return z - a;
+}
+
+template <bool DENSE>
+__device__ __forceinline__ BucketInfo load_bucket(const IdxView& V, int beta) {
+  BucketInfo b;
+  if (DENSE || beta >= V.n_bkt) { b.first = beta; b.last = beta; b.cnt = beta < V.n_bkt; b.off = beta; return b; }
+  b.first = V.bfirst[beta];
+  b.last = V.blast[beta];
+  b.cnt = V.bcnt[beta];
+  b.off = V.boff[beta];
+  return b;
+}
+
+// Key at position k of a bucket's ascending key list.
+template <bool DENSE>
+__device__ __forceinline__ int bucket_key(const IdxView& V, int beta, const BucketInfo& b, int k) {
+  if (DENSE) return beta;
+  const int p = V.pool;
+  return V.bmem[b.off + k / p] * p + k % p;
+}
+
+// Bitonic sort (ascending) of n_pow2 int32 / int64 in LDS by one wave.
+template <class T>
+__device__ void wave_bitonic(T* a, int n) {
+  const int lane = lane_id();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = lane; i < n; i += 64) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const T x = a[i], y = a[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) { a[i] = y; a[ixj] = x; }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+  }
+}
+
+
+// Writes one query's selection row: the taken buckets em[0..n) (bucket ids,
+// any order; `pb` is the one cut bucket, taking `ptake` keys, or -1) sorted
+// by id with their eligible keys in ascending position, then the sinks not
+// covered by the window, then the window, then -1 padding.  `em` must have
+// room for the next power of two >= n.  One wave.
+template <bool DENSE>
+__device__ void emit_row(const IdxView& V, int* em, int n, int pb, int ptake, int t, int window,
+                         int sinks, int max_sel, int32_t* __restrict__ row, int32_t* cnt_out) {
+  const int lane = lane_id();
+  int np = 1;
+  while (np < n) np <<= 1;
+  for (int i = n + lane; i < np; i += 64) em[i] = INT_MAX;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (n > 1) wave_bitonic(em, np);
+  int out = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    int beta = -1, take = 0, klo = 0;
+    BucketInfo bi = {0, 0, 0, 0};
+    if (i < n) {
+      beta = em[i];
+      bi = load_bucket<DENSE>(V, beta);
+      const int e = eligible<DENSE>(V, beta, bi, t, window, sinks, &klo);
+      take = beta == pb ? ptake : e;
+    }
+    int tot;
+    const int off = out + wave_excl_scan(take, &tot);
+    for (int j = 0; j < 64 && base + j < n; ++j) {
+      const int bj = __shfl(beta, j), tj = __shfl(take, j), kj = __shfl(klo, j), oj = __shfl(off, j);
+      BucketInfo b;
+      b.first = __shfl(bi.first, j); b.last = __shfl(bi.last, j);
+      b.cnt = __shfl(bi.cnt, j); b.off = __shfl(bi.off, j);
+      for (int k = lane; k < tj; k += 64) row[oj + k] = bucket_key<DENSE>(V, bj, b, kj + k);
+    }
+    out += tot;
+  }
+  const int wstart = max(0, t - window + 1);
+  const int ns = max(0, min(sinks, wstart));
+  const int nw = t - wstart + 1;
+  for (int k = lane; k < ns; k += 64) row[out + k] = k;
+  for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
+  const int total = out + ns + nw;
+  for (int k = total + lane; k < max_sel; k += 64) row[k] = -1;
+  if (lane == 0) *cnt_out = total;
+}
+
+}  // namespace sel
+}  // namespace lsa

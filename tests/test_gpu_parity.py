@@ -141,6 +141,10 @@ def test_tiny_selection_bit_exact(tiny):
     # determinism: a second run is bitwise identical (order included)
     idx2, cnt2 = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
     assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    # the exact refinement path alone (no workspace) gives the same rows
+    idx3, cnt3 = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp,
+                           use_workspace=False)
+    assert torch.equal(idx, idx3) and torch.equal(cnt, cnt3)
 
 
 def test_tiny_attention_within_tolerance(tiny):
