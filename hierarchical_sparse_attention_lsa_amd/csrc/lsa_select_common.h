@@ -127,12 +127,27 @@ __device__ void emit_row(const IdxView& V, int* em, int n, int pb, int ptake, in
     }
     int tot;
     const int off = out + wave_excl_scan(take, &tot);
-    for (int j = 0; j < 64 && base + j < n; ++j) {
-      const int bj = __shfl(beta, j), tj = __shfl(take, j), kj = __shfl(klo, j), oj = __shfl(off, j);
-      BucketInfo b;
-      b.first = __shfl(bi.first, j); b.last = __shfl(bi.last, j);
-      b.cnt = __shfl(bi.cnt, j); b.off = __shfl(bi.off, j);
-      for (int k = lane; k < tj; k += 64) row[oj + k] = bucket_key<DENSE>(V, bj, b, kj + k);
+    const int nround = min(64, n - base);
+    if (tot >= 16 * nround) {
+      // large buckets: one bucket at a time, lanes over its keys
+      for (int j = 0; j < nround; ++j) {
+        const int bj = __shfl(beta, j), tj = __shfl(take, j), kj = __shfl(klo, j), oj = __shfl(off, j);
+        BucketInfo b;
+        b.first = __shfl(bi.first, j); b.last = __shfl(bi.last, j);
+        b.cnt = __shfl(bi.cnt, j); b.off = __shfl(bi.off, j);
+        for (int k = lane; k < tj; k += 64) row[oj + k] = bucket_key<DENSE>(V, bj, b, kj + k);
+      }
+    } else {
+      // small buckets: each lane writes its own bucket, one member (p keys) per load
+      const int p = DENSE ? 1 : V.pool;
+      for (int k = 0; k < take;) {
+        const int kk = klo + k;
+        const int r0 = kk % p;
+        const int g = DENSE ? beta : V.bmem[bi.off + kk / p];
+        const int nh = min(p - r0, take - k);
+        for (int r = 0; r < nh; ++r) row[off + k + r] = g * p + r0 + r;
+        k += nh;
+      }
     }
     out += tot;
   }
