@@ -100,10 +100,11 @@ __device__ void wave_bitonic(T* a, int n) {
 
 
 // Writes one query's selection row: the taken buckets em[0..n) (bucket ids,
-// any order; `pb` is the one cut bucket, taking `ptake` keys, or -1) sorted
-// by id with their eligible keys in ascending position, then the sinks not
-// covered by the window, then the window, then -1 padding.  `em` must have
-// room for the next power of two >= n.  One wave.
+// any order; `pb` is the one cut bucket, taking `ptake` keys, or -1) in
+// ascending id order with their eligible keys in ascending position, then
+// the sinks not covered by the window, then the window, then -1 padding.
+// Every selection path writes rows in this order.  `em` must have room for
+// the next power of two >= n.  One wave.
 template <bool DENSE>
 __device__ void emit_row(const IdxView& V, int* em, int n, int pb, int ptake, int t, int window,
                          int sinks, int max_sel, int32_t* __restrict__ row, int32_t* cnt_out) {
