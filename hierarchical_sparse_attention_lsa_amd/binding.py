@@ -301,3 +301,12 @@ def decode_step(indexes: Sequence[LsaIndex], latk_new: torch.Tensor, latq: torch
                                  seq_stride_rows, ctypes.byref(sp), ctypes.byref(ap), _ptr(out),
                                  _ptr(ws), ws.numel(), _stream(stream)), "lsa_decode_step")
     return out
+
+
+def decode_selection(ws: torch.Tensor, nseq: int, sp: SelectParams):
+    """Views of the last decode step's selection at the head of its workspace."""
+    ms = sp.max_sel
+    a_idx = (nseq * ms * 4 + 255) // 256 * 256
+    idx = ws[: nseq * ms * 4].view(torch.int32).view(nseq, ms)
+    cnt = ws[a_idx: a_idx + nseq * 4].view(torch.int32)
+    return idx, cnt

@@ -158,8 +158,11 @@ LSA_API int lsa_append_keys(lsa_index* h, const int8_t* d_latk_new, int64_t n, v
                             size_t ws_bytes, void* stream);
 
 /* Select keys for nq queries: d_latq int8 [nq][64], d_qpos int32 [nq] with
- * 0 <= qpos < T (not checked on the device; out-of-range positions are
- * clamped).  Writes d_idx int32 [nq][max_sel] and d_cnt int32 [nq]. */
+ * 0 <= qpos < T (not checked on the device; a negative position is read as
+ * 0).  Writes d_idx int32 [nq][max_sel] and d_cnt int32 [nq].  With a
+ * workspace of lsa_workspace_bytes(LSA_OP_SELECT, .., nq) bytes, Flat
+ * batches of 64 or more queries take the single-scan list path; without one
+ * every query takes the exact refinement path (same rows, slower). */
 LSA_API int lsa_select(const lsa_index* h, const int8_t* d_latq, const int32_t* d_qpos,
                        int32_t nq, const lsa_select_params* sp, int32_t* d_idx, int32_t* d_cnt,
                        void* d_ws, size_t ws_bytes, void* stream);
@@ -188,7 +191,10 @@ LSA_API int lsa_prefill_chunk(lsa_index* h, const int8_t* d_latk_chunk, int64_t 
  * per sequence (d_latk_new int8 [nseq][64]), select for each sequence's
  * new position with d_latq [nseq][64], attend with d_q [nseq][Hq][D].
  * Sequence i's K/V rows start at d_k + i*seq_stride_rows*Hkv*D (the caller
- * has written the new rows).  d_out [nseq][Hq][D]. */
+ * has written the new rows).  d_out [nseq][Hq][D].  All sequences' indexes
+ * must share one lsa_index_params.  After the step the workspace begins
+ * with the step's selection: int32 idx [nseq][max_sel], then, at the next
+ * 256-byte boundary, int32 cnt [nseq]. */
 LSA_API int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new,
                             const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
                             const uint16_t* d_v, int64_t seq_stride_rows,

@@ -1,0 +1,200 @@
+"""GPU parity at the benchmarked sizes, in the benchmarked launch configuration.
+
+Each test runs the path the benchmark times (index prebuilt over the context
+before the chunk, then the fused prefill-chunk entry point; or 256 decode
+steps) and checks, against the CPU oracle built block by block in worker
+processes: every block's centroids and member lists bit-exactly, the
+selected key sets of a sample of queries bit-exactly, and the attention of a
+smaller sample within 2e-3 normwise (float32 output of the same kernel, with
+the bf16 output equal to its round-to-nearest-even).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lsa_synth as S
+import oracle as O
+from oracle.parallel_build import build_cache_parallel
+
+from test_gpu_parity import (TOL, check_index, normwise, oracle_attention, rne_bf16_bits)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _L():
+    import hierarchical_sparse_attention_lsa_amd as L
+    return L
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _oparams(wl):
+    return O.IndexParams(wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
+                         wl.tree_iters)
+
+
+def _sample_positions(wl, n_sel, seed):
+    n, t0 = wl.chunk, wl.T - wl.chunk
+    kpb = wl.pool * wl.block
+    fixed = [0, 1, n - 1, n - 2, kpb - 1, kpb, kpb + 1, n // 2]
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(n, n_sel - len(fixed), replace=False).tolist()
+    return sorted(set(i for i in fixed + rest if 0 <= i < n))
+
+
+def _gpu_prefill(wl, dev, out_f32_too=True):
+    """The benchmarked step: prebuilt index, then lsa_prefill_chunk (bf16 out)."""
+    L = _L()
+    g = S.Synth(wl)
+    n, t0 = wl.chunk, wl.T - wl.chunk
+    latk = g.latk(0, wl.T, device=dev, chunk=1 << 22)
+    K = torch.empty((wl.T, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0, chunk=1 << 18)
+    g.fill_rows("v", V, 0, chunk=1 << 18)
+    latq = g.latq_rows(torch.arange(t0, wl.T, device=dev), device=dev)
+    q = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    g.fill_rows("q", q, t0)
+    ix = L.LsaIndex(L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group,
+                                  wl.tree_super, wl.tree_iters, wl.T), dev)
+    ix.build(latk[:t0])
+    snap = ix.snapshot()
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    idx = torch.empty((n, sp.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((n,), dtype=torch.int32, device=dev)
+    o16 = ix.prefill_chunk(latk[t0:], latq, q, K, V, sp, L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0),
+                           idx=idx, cnt=cnt)
+    o32 = None
+    if out_f32_too:
+        ix.restore(snap)
+        o32 = ix.prefill_chunk(latk[t0:], latq, q, K, V, sp,
+                               L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0))
+    torch.cuda.synchronize()
+    res = dict(g=g, idx=idx.cpu().numpy(), cnt=cnt.cpu().numpy(), o16=o16, o32=o32,
+               arrays={k: v.cpu() for k, v in ix.arrays().items()})
+    del K, V, latk
+    torch.cuda.empty_cache()
+    return res
+
+
+def _check_prefill(wl, res, ref, n_sel, n_att, seed):
+    n, t0 = wl.chunk, wl.T - wl.chunk
+    check_index(res["arrays"], ref)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    pos = _sample_positions(wl, n_sel, seed)
+    latq = res["g"].latq_rows(torch.tensor([t0 + i for i in pos])).numpy()   # host-generated
+    sels = {}
+    for j, i in enumerate(pos):
+        ref_sel = O.select(ref, latq[j], t0 + i, osp)
+        got = np.sort(res["idx"][i, :res["cnt"][i]])
+        assert np.array_equal(got, ref_sel), f"query at position {t0 + i}"
+        assert (res["idx"][i, res["cnt"][i]:] == -1).all()
+        sels[i] = ref_sel
+    att = pos[:: max(1, len(pos) // n_att)][:n_att]
+    refo = oracle_attention(res["g"], wl, [t0 + i for i in att], [sels[i] for i in att])
+    o32 = res["o32"].cpu().numpy()[att].astype(np.float64)
+    err = normwise(o32, refo)
+    print(f"{wl.name}: {len(pos)} selections bit-exact, attention normwise error {err:.3e}")
+    assert err <= TOL
+    o16 = res["o16"].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(o16, rne_bf16_bits(res["o32"].cpu().numpy()))
+
+
+def test_flat_1m_prefill_chunk(oracle_pool):
+    dev = _dev()
+    wl = S.WORKLOADS["flat_1m"]
+    res = _gpu_prefill(wl, dev)
+    cache, latk = build_cache_parallel(wl.name, wl.T, oracle_pool)
+    ref = O.build_index(latk, wl.T, _oparams(wl), cache)
+    _check_prefill(wl, res, ref, n_sel=160, n_att=24, seed=1)
+
+
+@pytest.fixture(scope="module")
+def oracle_10m(oracle_pool):
+    wl = S.WORKLOADS["flat_10m"]
+    cache, latk = build_cache_parallel(wl.name, wl.T, oracle_pool)
+    return cache, latk
+
+
+def test_flat_10m_prefill_chunk(oracle_10m):
+    dev = _dev()
+    wl = S.WORKLOADS["flat_10m"]
+    res = _gpu_prefill(wl, dev)
+    cache, latk = oracle_10m
+    ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
+    _check_prefill(wl, res, ref, n_sel=128, n_att=16, seed=2)
+
+
+def test_tree_10m_prefill_chunk(oracle_10m):
+    dev = _dev()
+    wl = S.WORKLOADS["tree_10m"]
+    res = _gpu_prefill(wl, dev)
+    cache, latk = oracle_10m
+    ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
+    assert ref.n_grp == 10 and ref.sup_centroids.shape[0] == 640
+    _check_prefill(wl, res, ref, n_sel=96, n_att=12, seed=3)
+
+
+def test_decode_1m_256_steps(oracle_pool):
+    dev = _dev()
+    L = _L()
+    wl = S.WORKLOADS["decode_1m"]
+    cap = wl.T + wl.steps
+    gens = [S.Synth(wl, seq=i) for i in range(wl.nseq)]
+    K = torch.empty((wl.nseq, cap, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    ixs, lats = [], []
+    for i, g in enumerate(gens):
+        lk = g.latk(0, cap, device=dev, chunk=1 << 22)
+        lats.append(lk)
+        g.fill_rows("k", K[i], 0, chunk=1 << 18)
+        g.fill_rows("v", V[i], 0, chunk=1 << 18)
+        ix = L.LsaIndex(L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, cap), dev)
+        ix.build(lk[:wl.T])
+        ixs.append(ix)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    ap32 = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    wsb = L.workspace_bytes(L.binding.OP_DECODE, ixs[0].params, sp, ap32, wl.nseq)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    check_steps = {0, 1, 3, 4, wl.steps - 1}
+    got = {}
+    new_pos = torch.arange(wl.T, cap, device=dev)
+    lq_all = torch.stack([gens[i].latq_rows(new_pos, device=dev) for i in range(wl.nseq)], 1)
+    q_all = torch.stack([gens[i].q_rows(new_pos, device=dev) for i in range(wl.nseq)], 1)
+    for s in range(wl.steps):
+        t = wl.T + s
+        lk_new = torch.stack([lats[i][t] for i in range(wl.nseq)]).contiguous()
+        out = L.decode_step(ixs, lk_new, lq_all[s].contiguous(), q_all[s].contiguous(), K, V, cap,
+                            sp, ap32, ws=ws)
+        if s in check_steps:
+            idx, cnt = L.decode_selection(ws, wl.nseq, sp)
+            got[s] = (idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy())
+    torch.cuda.synchronize()
+    del K, V, lats
+    torch.cuda.empty_cache()
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    worst = 0.0
+    caches, lat_h = [], []
+    for i in range(wl.nseq):
+        cache, lat0 = build_cache_parallel(wl.name, wl.T, oracle_pool, seq=i)   # host-generated
+        caches.append(cache)
+        lat_h.append(np.concatenate([lat0, gens[i].latk(wl.T, cap).numpy()]))
+        for s in sorted(check_steps):
+            t = wl.T + s
+            ref = O.build_index(lat_h[i], t + 1, _oparams(wl), cache)
+            lq = gens[i].latq_rows(torch.tensor([t])).numpy()[0]
+            sel = O.select(ref, lq, t, osp)
+            idx, cnt, out = got[s]
+            assert np.array_equal(np.sort(idx[i, :cnt[i]]), sel), f"sequence {i} step {s}"
+            ro = oracle_attention(gens[i], wl, [t], [sel])[0]
+            worst = max(worst, normwise(out[i].astype(np.float64), ro))
+    print(f"decode: selections bit-exact at {len(check_steps)} steps x {wl.nseq} sequences, "
+          f"attention normwise error {worst:.3e}")
+    assert worst <= TOL
+    # the last step's index equals the oracle's over all keys
+    check_index({k: v.cpu() for k, v in ixs[0].arrays().items()},
+                O.build_index(lat_h[0], cap, _oparams(wl), caches[0]))
