@@ -299,6 +299,74 @@ def cpu_baseline(res, workers_pool, n_sample=192):
     }
 
 
+CALIB_BYTES = 2 << 30
+
+
+def profile_run(args, dev):
+    """One prefill step (the timed kernels) and a plain 2 GiB device copy whose
+    HBM bytes are known, for rocprofv3 counter runs."""
+    args.steps, args.warmup = 1, 0
+    res = bench_prefill(args, dev)
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[profile] prefill step {res['ms_per_step']:.2f} ms; calibration copy of {CALIB_BYTES} bytes done")
+
+
+def _pmc_last(path, key, counter):
+    """Counter value of the last dispatch whose kernel name contains `key`."""
+    import csv
+    best = None
+    for r in csv.DictReader(open(path)):
+        if key in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
+            d = int(r["Dispatch_Id"])
+            if best is None or d > best[0]:
+                best = (d, float(r["Counter_Value"]))
+    return None if best is None else best[1]
+
+
+def summarize(args):
+    """Turn rocprofv3 outputs into the committed text summaries.
+
+    --summarize STATS_CSV FETCH_CSV WRITE_CSV COMMAND"""
+    import csv
+    stats_csv, fetch_csv, write_csv, command = args.summarize
+    stats = list(csv.DictReader(open(stats_csv)))
+    lines = ["# rocprofv3 kernel statistics: LSA prefill chunk, Flat 10M (T=10*2^20, 32768 queries)", "",
+             f"Command: `{command}`", "",
+             "| kernel | calls | average ms | total ms |", "|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        if "lsa" not in r["Name"] and "copyBuffer" not in r["Name"]:
+            continue
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e6:.3f} | "
+                     f"{float(r['TotalDurationNs'])/1e6:.2f} |")
+    # the calibration copy is the run's last copy dispatch
+    cf = _pmc_last(fetch_csv, "copyBuffer", "FETCH_SIZE")
+    cw = _pmc_last(write_csv, "copyBuffer", "WRITE_SIZE")
+    af = _pmc_last(fetch_csv, "k_attn<128, false, false>", "FETCH_SIZE")
+    aw = _pmc_last(write_csv, "k_attn<128, false, false>", "WRITE_SIZE")
+    kf = CALIB_BYTES / (cf * 1024) if cf else None
+    kw = CALIB_BYTES / (cw * 1024) if cw else None
+    traffic = None
+    if af and aw and kf and kw:
+        traffic = af * 1024 * kf + aw * 1024 * kw
+    lines += ["", "## HBM traffic of the attention kernel (rocprofv3 --pmc, one dispatch)", "",
+              f"* calibration: a 2 GiB device copy reads FETCH_SIZE = {cf} KiB and writes WRITE_SIZE = {cw} KiB;"
+              f" scale factors {kf} (fetch) and {kw} (write)",
+              f"* k_attn: FETCH_SIZE = {af} KiB, WRITE_SIZE = {aw} KiB per dispatch",
+              f"* scaled traffic per launch = {traffic} bytes"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "attn_flat_10m_rocprof.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", "attn_traffic.json"), "w") as f:
+        json.dump({"workload": "flat_10m", "src_hash": src_hash(ATTN_SRC), "bytes_per_launch": traffic,
+                   "fetch_kib": af, "write_kib": aw, "calib_fetch_kib": cf, "calib_write_kib": cw,
+                   "command": command}, f, indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,14 +376,21 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="one prefill step plus a 2 GiB calibration copy (for rocprofv3 runs)")
+    ap.add_argument("--summarize", nargs=4, metavar=("STATS", "FETCH", "WRITE", "COMMAND"),
+                    help="write profiles/ summaries from rocprofv3 CSV outputs")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the LSA hot path here is built and timed on a "
               "single MI355X (--gpus 1); multi-GPU sharding is a design note, not built.",
               file=sys.stderr)
         sys.exit(2)
     workers_pool = None
-    if not args.no_cpu:
+    if not args.no_cpu and not args.profile:
         # forked before anything touches the GPU; the workers only run the CPU oracle
         import multiprocessing as mp
         workers_pool = mp.get_context("fork").Pool(min(16, os.cpu_count() or 1))
@@ -324,6 +399,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     L.lib()
+    if args.profile:
+        profile_run(args, dev)
+        return
 
     res = bench_prefill(args, dev)
     wl = res["wl"]

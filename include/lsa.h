@@ -25,7 +25,7 @@
  *   - Every device buffer is owned by the caller; the library never
  *     allocates device memory.  Pointers prefixed d_ are device pointers.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
- *     NULL = the null stream) except lsa_export_index, which synchronises it.
+ *     NULL = the null stream); none synchronises it.
  *   - Arguments are validated before anything is enqueued; on an error
  *     nothing is enqueued and the index descriptor is unchanged.  A runtime
  *     or launch failure returns LSA_E_HIP.  lsa_last_error() gives a
@@ -38,8 +38,10 @@
  *     Q and O [nq][Hq][D], K and V [rows][Hkv][D].  Head h reads KV head
  *     floor(h * Hkv / Hq).
  *   - Selected key lists are int32 rows of `max_sel` = budget + window + sinks
- *     entries: `cnt[i]` distinct key positions (a set; the order is
- *     deterministic but unspecified) followed by -1 padding.
+ *     entries: `cnt[i]` distinct key positions followed by -1 padding.  The
+ *     row is a set written in a fixed order: the taken buckets in ascending
+ *     id, each with its eligible keys in ascending position, then the sinks
+ *     not in the window, then the window.
  */
 #ifndef LSA_H
 #define LSA_H
