@@ -316,11 +316,15 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
       return LSA_OK;
     }
     case LSA_OP_DECODE: {
+      if (int e = check_index_params(iprm)) return e;
       if (int e = check_select_params(sprm, false)) return e;
       if (int e = check_attn_params(aprm)) return e;
+      Index tmp;
+      memset(&tmp, 0, sizeof tmp);
+      layout(*iprm, &tmp);
       *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4) +
                (size_t)align_up((int64_t)attn_ws_bytes((int32_t)n, *aprm, kDecodeSplits)) +
-               select_decode_ws_bytes((int32_t)n);
+               select_dec_ws_bytes((int32_t)n, tmp.max_bkt);
       return LSA_OK;
     }
     default:
@@ -460,7 +464,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   const size_t a_idx = (size_t)align_up((int64_t)nseq * max_sel * 4);
   const size_t a_cnt = (size_t)align_up((int64_t)nseq * 4);
   const size_t a_att = (size_t)align_up((int64_t)attn_ws_bytes(nseq, *ap, kDecodeSplits));
-  const size_t a_sel = select_decode_ws_bytes(nseq);
+  const size_t a_sel = select_dec_ws_bytes(nseq, h0->max_bkt);
   if (!d_ws || ws_bytes < a_idx + a_cnt + a_att + a_sel)
     return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, a_idx + a_cnt + a_att + a_sel);
   char* ws = static_cast<char*>(d_ws);
@@ -522,7 +526,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   a.latq = d_latq; a.qpos = nullptr; a.qpos_base = 0; a.nq = nseq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
   a.max_sel = max_sel; a.idx = idx; a.cnt = cnt; a.only = nullptr;
-  LSA_HIP(launch_select_decode(views, qpos, nseq, a, selws, s), "decode select");
+  LSA_HIP(launch_select_dec(views, qpos, nseq, h0->max_bkt, a, selws, s), "decode select");
 
   // 3. split-K attention over each sequence's own rows, then the merge
   LSA_HIP(launch_attn(d_q, d_k, d_v, seq_stride_rows, seq_stride_rows, 1, idx, cnt, max_sel,

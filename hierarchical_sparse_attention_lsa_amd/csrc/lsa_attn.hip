@@ -239,7 +239,8 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
   }
 }
 
-// Combine split partial results: out[q][head][d].
+// Combine split partial results: out[q][head][d] (one pass, online rescale;
+// the per-split loads are independent and unrolled so they overlap).
 template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(D) k_attn_merge(AttnArgs a) {
   const int qh = blockIdx.x;            // q * Hq + head
@@ -247,16 +248,18 @@ __global__ void __launch_bounds__(D) k_attn_merge(AttnArgs a) {
   const int q = qh / a.Hq, head = qh % a.Hq;
   const int g = head / a.G, h = head % a.G;
   const int64_t it0 = ((int64_t)q * a.Hkv + g) * a.splits;
-  float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(it0 + s) * 32 + 2 * h]);
-  float num = 0.f, den = 0.f;
+  float M = -INFINITY, num = 0.f, den = 0.f;
+#pragma unroll 8
   for (int s = 0; s < a.splits; ++s) {
     const float ms = a.part_ml[(it0 + s) * 32 + 2 * h];
     const float ls = a.part_ml[(it0 + s) * 32 + 2 * h + 1];
+    const float os = a.part_o[(it0 + s) * 16 * D + h * D + d];
     if (ls <= 0.f) continue;
-    const float w = exp2f(ms - M);
-    num += w * a.part_o[(it0 + s) * 16 * D + h * D + d];
-    den += w * ls;
+    const float nm = fmaxf(M, ms);
+    const float c0 = exp2f(M - nm), c1 = exp2f(ms - nm);
+    num = num * c0 + os * c1;
+    den = den * c0 + ls * c1;
+    M = nm;
   }
   const float val = den > 0.f ? num / den : 0.f;
   const int64_t ob = (int64_t)qh * D + d;

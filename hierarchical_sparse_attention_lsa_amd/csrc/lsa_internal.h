@@ -97,10 +97,10 @@ hipError_t launch_select(const IdxView& v, const SelArgs& a, void* ws, hipStream
 // large Flat batches: list-based single full pass (+ exact kernel for flagged queries)
 size_t select_fast_ws_bytes(int32_t nq);
 hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
-// decode: one query per sequence, each on its own index
-size_t select_decode_ws_bytes(int32_t nseq);
-hipError_t launch_select_decode(const IdxView* views, const int32_t* qpos, int32_t nseq,
-                                const SelArgs& a, void* ws, hipStream_t s);
+// decode: one query per sequence, each on its own index (max_bkt = bucket capacity)
+size_t select_dec_ws_bytes(int32_t nseq, int64_t max_bkt);
+hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t nseq,
+                             int64_t max_bkt, const SelArgs& a, void* ws, hipStream_t s);
 
 size_t attn_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t splits);
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_rows,

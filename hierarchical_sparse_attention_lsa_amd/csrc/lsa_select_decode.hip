@@ -1,0 +1,404 @@
+// Selection for decode steps: one query per sequence, each on its own index.
+//
+// The rule is the pages' ("Latent Sparse Attention: un indice gerarchico per
+// contesti lunghi", search and D-LSA configuration paragraphs): buckets in
+// (score desc, bucket asc) order, their eligible keys in ascending position
+// until the long-range budget is met, then the window and the sinks.
+//
+// A decode step has few queries and a small index per sequence, so the work
+// is spread differently from prefill:
+//   k_dec_score   one thread per (sequence, bucket) across many workgroups:
+//                 the int8 dot product (v_dot4), the bucket's eligible keys
+//                 for the new position and the order key go to the workspace;
+//   k_dec_select  one 1024-thread workgroup per sequence holds its buckets'
+//                 keys in registers, finds the exact cutoff by histogram
+//                 refinement (bins in LDS), sorts the <= 256 entries of the
+//                 final bracket, and writes the row: a block-wide prefix sum
+//                 over the threads (which own consecutive bucket ids) gives
+//                 every taken bucket its output offset in ascending id order.
+#include <climits>
+#include <cstring>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+#include "lsa_select_common.h"
+
+namespace lsa {
+
+namespace {
+using namespace sel;
+
+constexpr int DT = 1024;            // threads of the select workgroup
+constexpr int DW = DT / 64;
+constexpr int PERT = 24;            // buckets per thread (indexes of up to 24576 buckets)
+constexpr int RB = 256;
+constexpr int RCAP = 256;
+constexpr int kDecLds = PERT * DT * 4;
+
+struct DecViews {                   // first kernel argument (read through the kernarg pointer)
+  IdxView v[16];
+  int32_t qpos[16];
+  int32_t nseq;
+  int32_t cap;                      // workspace entries per sequence
+};
+
+struct DecWs {
+  int32_t* score;                   // [nseq][cap] int8 dot products
+  int32_t* elig;                    // [nseq][cap] eligible keys
+  int32_t* kstart;                  // [nseq][cap] first eligible key slot
+};
+
+__global__ void __launch_bounds__(256) k_dec_score(DecViews VS, SelArgs A, DecWs W) {
+  const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int seq = blockIdx.y;
+  const IdxView V = vsp->v[seq];
+  const int beta = blockIdx.x * 256 + threadIdx.x;
+  if (beta >= V.n_bkt) return;
+  const int t = vsp->qpos[seq];
+  const int* q4 = reinterpret_cast<const int*>(A.latq + (int64_t)seq * kDim);
+  const int4* c4 = reinterpret_cast<const int4*>(V.cent + (int64_t)beta * kDim);
+  int acc = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int4 c = c4[k];
+    acc = __builtin_amdgcn_sdot4(q4[4 * k + 0], c.x, acc, false);
+    acc = __builtin_amdgcn_sdot4(q4[4 * k + 1], c.y, acc, false);
+    acc = __builtin_amdgcn_sdot4(q4[4 * k + 2], c.z, acc, false);
+    acc = __builtin_amdgcn_sdot4(q4[4 * k + 3], c.w, acc, false);
+  }
+  const BucketInfo bi = load_bucket<false>(V, beta);
+  int klo;
+  const int e = eligible<false>(V, beta, bi, t, A.window, A.sinks, &klo);
+  const int64_t at = (int64_t)seq * VS.cap + beta;
+  W.score[at] = acc;
+  W.elig[at] = e;
+  W.kstart[at] = bi.off * V.pool + klo;
+}
+
+// Order key from a score and a bucket id, recomputed where it is used: the
+// empty asm keeps the compiler from hoisting all of a thread's keys out of the
+// refinement loop as 64-bit loop invariants (which would not fit in registers).
+__device__ __forceinline__ long long rebuilt_key(int s, int beta) {
+  asm volatile("" : "+v"(beta));
+  return order_key(s, beta);
+}
+
+// Block-wide reductions / scans over DT threads (LDS scratch of DW entries).
+__device__ __forceinline__ long long block_sum_ll(long long x, long long* red) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += shfl_xor_i64(x, m);
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  long long s = 0;
+  for (int w = 0; w < DW; ++w) s += red[w];
+  return s;
+}
+
+__device__ __forceinline__ long long block_min_ll(long long x, long long* red) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = min(x, shfl_xor_i64(x, m));
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  long long s = LLONG_MAX;
+  for (int w = 0; w < DW; ++w) s = min(s, red[w]);
+  return s;
+}
+
+__device__ __forceinline__ long long block_max_ll(long long x, long long* red) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = max(x, shfl_xor_i64(x, m));
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  long long s = LLONG_MIN;
+  for (int w = 0; w < DW; ++w) s = max(s, red[w]);
+  return s;
+}
+
+// Exclusive prefix sum over the block in thread order; *total = block sum.
+__device__ __forceinline__ int block_excl_scan(int x, int* red, int* total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int wt;
+  const int ex = wave_excl_scan(x, &wt);
+  __syncthreads();
+  if (lane == 0) red[wave] = wt;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < DW; ++w) {
+    const int v = red[w];
+    before += w < wave ? v : 0;
+    all += v;
+  }
+  *total = all;
+  return before + ex;
+}
+
+__global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs W,
+                                                   int32_t* __restrict__ flags) {
+  __shared__ int s_hk[RB], s_hb[RB];
+  __shared__ long long s_red[DW];
+  __shared__ int s_ired[DW];
+  __shared__ long long s_cq[RCAP];
+  __shared__ int s_ci[RCAP];
+  __shared__ int s_nc;
+  __shared__ int s_cut[2];
+  extern __shared__ int s_e[];         // [PERT][DT]: eligible keys, later the keys taken
+  const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int seq = blockIdx.x;
+  const IdxView V = vsp->v[seq];
+  const int t = vsp->qpos[seq];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int B = A.budget;
+  const int n = V.n_bkt;
+  const int p = V.pool;
+  const int64_t base = (int64_t)seq * VS.cap;
+  if (n > DT * PERT) {                 // too large for registers: the exact kernel serves it
+    if (tid == 0) flags[seq] = 1;
+    return;
+  }
+  // scores and eligible counts of buckets tid*PERT .. tid*PERT+PERT-1; the
+  // order key is rebuilt from the score and the (implicit) bucket id
+  int sc[PERT];
+#define KEY(u) rebuilt_key(sc[u], tid * PERT + (u))
+#define E(u) s_e[(u) * DT + tid]
+  long long lo = LLONG_MAX, hi = LLONG_MIN, tot = 0;
+#pragma unroll
+  for (int u = 0; u < PERT; ++u) {
+    const int j = tid * PERT + u;
+    sc[u] = j < n ? W.score[base + j] : 0;
+    E(u) = j < n ? W.elig[base + j] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < PERT; ++u) {   // branch-free: selects, no divergent blocks
+    const long long ku = KEY(u);
+    const int eu = E(u);
+    const bool ok = eu > 0;
+    lo = min(lo, ok ? ku : LLONG_MAX);
+    hi = max(hi, ok ? ku : LLONG_MIN);
+    tot += ok ? eu : 0;
+  }
+  tot = block_sum_ll(tot, s_red);
+  lo = block_min_ll(lo, s_red);
+  hi = block_max_ll(hi, s_red);
+  // keys above `hi` are taken whole; the bracket [lo, hi] holds the cutoff
+  if (B <= 0) {
+    hi = LLONG_MAX;                  // nothing is taken
+    lo = LLONG_MAX;
+  } else if (tot <= B) {
+    hi = LLONG_MIN;                  // every eligible bucket is taken whole
+    lo = LLONG_MIN + 1;
+  } else {
+    for (int pass = 0; pass < 8; ++pass) {
+      const long long range = hi - lo + 1;
+      int sh = 0;
+      while (sh < 62 && ((range + (1ll << sh) - 1) >> sh) > RB) ++sh;
+      for (int i = tid; i < RB; i += DT) { s_hk[i] = 0; s_hb[i] = 0; }
+      __syncthreads();
+      long long ab = 0;
+#pragma unroll
+      for (int u = 0; u < PERT; ++u) {
+        const long long ku = KEY(u);
+        const int eu = E(u);
+        ab += (eu > 0 && ku > hi) ? eu : 0;
+        if (eu <= 0 || ku > hi || ku < lo) continue;
+        const int bin = (int)((hi - ku) >> sh);
+        atomicAdd(&s_hk[bin], eu);
+        atomicAdd(&s_hb[bin], 1);
+      }
+      ab = block_sum_ll(ab, s_red);
+      if (wave == 0) {
+        int h[RB / 64], c[RB / 64], loc = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) { h[k] = s_hk[(RB / 64) * lane + k]; c[k] = s_hb[(RB / 64) * lane + k]; loc += h[k]; }
+        int wt;
+        const int ex = wave_excl_scan(loc, &wt);
+        long long cum = ab + ex;
+        int found = -1, fb = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) {
+          if (found < 0 && cum + h[k] >= B) { found = (RB / 64) * lane + k; fb = c[k]; }
+          cum += h[k];
+        }
+        const unsigned long long mk = __ballot(found >= 0);
+        const int src = mk ? __ffsll((long long)mk) - 1 : 0;
+        const int bsel = __shfl(found, src), nbsel = __shfl(fb, src);
+        if (lane == 0) {
+          s_cut[0] = mk ? bsel : -1;
+          s_cut[1] = mk ? nbsel : 0;
+        }
+      }
+      __syncthreads();
+      const int bin = s_cut[0], nb = s_cut[1];
+      if (bin < 0) break;              // cannot happen: the bracket holds the cutoff
+      const long long nhi = hi - ((long long)bin << sh);
+      long long nlo = hi - ((long long)(bin + 1) << sh) + 1;
+      if (nlo < lo) nlo = lo;
+      lo = nlo; hi = nhi;
+      __syncthreads();
+      if (nb <= RCAP) break;
+    }
+  }
+  // bracket entries: sorted by (score desc, id asc), taken in order, last one cut
+  if (tid == 0) s_nc = 0;
+  __syncthreads();
+  long long full = 0;
+#pragma unroll
+  for (int u = 0; u < PERT; ++u) {
+    const long long ku = KEY(u);
+    const int eu = E(u);
+    full += (eu > 0 && ku > hi) ? eu : 0;
+    if (eu <= 0 || ku > hi || ku < lo) continue;
+    const int c = atomicAdd(&s_nc, 1);
+    if (c < RCAP) { s_cq[c] = -ku; s_ci[c] = tid * PERT + u; }
+  }
+  full = block_sum_ll(full, s_red);
+  const int nc = min(s_nc, RCAP);
+  const bool overflow = s_nc > RCAP;
+  if (wave == 0 && nc > 0 && !overflow) {
+    int np = 1;
+    while (np < nc) np <<= 1;
+    for (int i = nc + lane; i < np; i += 64) { s_cq[i] = LLONG_MAX; s_ci[i] = -1; }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int k = 2; k <= np; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = lane; i < np; i += 64) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const long long x = s_cq[i], y = s_cq[ixj];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) { s_cq[i] = y; s_cq[ixj] = x; const int tmp = s_ci[i]; s_ci[i] = s_ci[ixj]; s_ci[ixj] = tmp; }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+    }
+    long long need = B - full;
+    for (int b0 = 0; b0 < nc; b0 += 64) {
+      const int i = b0 + lane;
+      int ee = 0, li = -1;
+      if (i < nc) { li = s_ci[i]; ee = s_e[(li % PERT) * DT + li / PERT]; }
+      int tot2;
+      const int before = wave_excl_scan(ee, &tot2);
+      const long long tk = max(0ll, min((long long)ee, need - before));
+      if (li >= 0) s_e[(li % PERT) * DT + li / PERT] = (int)tk;
+      need -= tot2;
+    }
+  }
+  __syncthreads();
+  // keys taken from this thread's buckets (ascending ids): whole above the
+  // bracket, as the walk set them inside it; then a prefix sum over the block
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < PERT; ++u) {
+    const long long ku = KEY(u);
+    const int eu = E(u);
+    const int tk = (eu > 0 && ku >= lo) ? eu : 0;
+    E(u) = tk;
+    mine += tk;
+  }
+  int out_total;
+  int off = block_excl_scan(mine, s_ired, &out_total);
+  int32_t* row = A.idx + (int64_t)seq * A.max_sel;
+  if (!overflow) {
+#pragma unroll
+    for (int u = 0; u < PERT; ++u) {
+      const int tk = E(u);
+      if (tk <= 0) continue;
+      const int ks = W.kstart[base + tid * PERT + u];
+      for (int k = 0; k < tk;) {
+        const int sl = ks + k;
+        const int r0 = sl % p;
+        const int g = V.bmem[sl / p];
+        const int nh = min(p - r0, tk - k);
+        for (int r = 0; r < nh; ++r) row[off + k + r] = g * p + r0 + r;
+        k += nh;
+      }
+      off += tk;
+    }
+  }
+  if (wave == 0 && !overflow) {
+    const int out = out_total;
+    const int wstart = max(0, t - A.window + 1);
+    const int ns = max(0, min(A.sinks, wstart));
+    const int nw = t - wstart + 1;
+    for (int k = lane; k < ns; k += 64) row[out + k] = k;
+    for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
+    const int totalk = out + ns + nw;
+    for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
+    if (lane == 0) A.cnt[seq] = totalk;
+  }
+  if (tid == 0) flags[seq] = overflow ? 1 : 0;
+#undef KEY
+#undef E
+}
+
+size_t dec_layout(int32_t nseq, int32_t cap, DecWs* W, int32_t** flags, void* ws) {
+  char* p = static_cast<char*>(ws);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { char* r = p ? p + o : nullptr; o += (bytes + 255) / 256 * 256; return r; };
+  DecWs w;
+  const size_t n = (size_t)nseq * cap;
+  w.score = reinterpret_cast<int32_t*>(take(n * sizeof(int32_t)));
+  w.elig = reinterpret_cast<int32_t*>(take(n * sizeof(int32_t)));
+  w.kstart = reinterpret_cast<int32_t*>(take(n * sizeof(int32_t)));
+  int32_t* f = reinterpret_cast<int32_t*>(take((size_t)nseq * sizeof(int32_t)));
+  if (W) *W = w;
+  if (flags) *flags = f;
+  return o;
+}
+
+}  // namespace
+
+size_t select_dec_ws_bytes(int32_t nseq, int64_t max_bkt) {
+  return dec_layout(nseq, (int32_t)max_bkt, nullptr, nullptr, nullptr);
+}
+
+hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t nseq,
+                             int64_t max_bkt, const SelArgs& a, void* ws, hipStream_t s) {
+  if (nseq <= 0) return hipSuccess;
+  DecViews vs;
+  memset(&vs, 0, sizeof vs);
+  bool tree = false;
+  int nmax = 0;
+  for (int i = 0; i < nseq; ++i) {
+    vs.v[i] = views[i];
+    vs.qpos[i] = qpos[i];
+    tree |= views[i].leafsup != nullptr;
+    nmax = nmax > views[i].n_bkt ? nmax : views[i].n_bkt;
+  }
+  vs.nseq = nseq;
+  vs.cap = (int32_t)max_bkt;
+  SelArgs b = a;
+  b.nq = nseq;
+  if (tree || nmax > DT * PERT) return launch_select_multi(views, qpos, nseq, b, s);
+  DecWs W;
+  int32_t* flags;
+  dec_layout(nseq, vs.cap, &W, &flags, ws);
+  if (nmax > 0) {
+    hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + 255) / 256), (unsigned)nseq), dim3(256), 0,
+                       s, vs, b, W);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_dec_select,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDecLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_dec_select, dim3((unsigned)nseq), dim3(DT), kDecLds, s, vs, b, W, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  b.only = flags;                   // bracket overflow (never seen): exact kernel
+  return launch_select_multi(views, qpos, nseq, b, s);
+}
+
+}  // namespace lsa

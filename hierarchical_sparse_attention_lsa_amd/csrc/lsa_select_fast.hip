@@ -1,6 +1,6 @@
-// Flat selection in one full scan of the centroids (prefill batches and
-// decode steps), as two kernels: a scan that collects candidate buckets and
-// a per-query resolve.
+// Flat selection for prefill batches in one full scan of the centroids, as
+// two kernels: a scan that collects candidate buckets and a per-query
+// resolve.
 //
 // Same result as the exact refinement kernel (lsa_select.hip) -- the pages'
 // rule: buckets in (score desc, bucket asc) order, their eligible keys in
@@ -8,7 +8,7 @@
 // Attention: un indice gerarchico per contesti lunghi", search and D-LSA
 // configuration paragraphs).
 //
-// k_scan (a workgroup per 64 queries for prefill, per sequence for decode):
+// k_scan (a workgroup per 64 queries):
 //   1. sampled pass: score max / mean of each query over the non-empty
 //      buckets of a strided subset of the centroids;
 //   2. sampled pass: histogram of the sampled buckets' key counts between
@@ -565,7 +565,6 @@ __global__ void __launch_bounds__(RW * 64) k_resolve(FastViews VS, SelArgs A, Li
 }
 
 constexpr int kPrefW = 4, kPrefQ = 64;     // prefill scan: 4 waves, 64 query slots
-constexpr int kDecW = 4, kDecQ = 16;       // decode scan: 4 waves splitting one 16-slot group
 
 size_t ws_layout(size_t slots, size_t nq, ListWs* W, void* base) {
   char* p = static_cast<char*>(base);
@@ -611,43 +610,6 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
   SelArgs b = a;
   b.only = W.flags;
   return launch_select(v, b, nullptr, s);
-}
-
-size_t select_decode_ws_bytes(int32_t nseq) {
-  return ws_layout((size_t)nseq * kDecQ, nseq, nullptr, nullptr);
-}
-
-hipError_t launch_select_decode(const IdxView* views, const int32_t* qpos, int32_t nseq,
-                                const SelArgs& a, void* ws, hipStream_t s) {
-  if (nseq <= 0) return hipSuccess;
-  FastViews vs;
-  memset(&vs, 0, sizeof vs);
-  bool tree = false;
-  for (int i = 0; i < nseq; ++i) {
-    vs.v[i] = views[i];
-    vs.qpos[i] = qpos[i];
-    tree |= views[i].leafsup != nullptr;
-  }
-  vs.nviews = nseq;
-  vs.slots_per_view = kDecQ;
-  SelArgs b = a;
-  b.nq = nseq;
-  if (tree || nseq < 2) {
-    // Tree indexes (candidate masks) and single sequences take the exact kernel
-    return launch_select_multi(views, qpos, nseq, b, s);
-  }
-  const size_t slots = (size_t)nseq * kDecQ;
-  ListWs W;
-  ws_layout(slots, nseq, &W, ws);
-  hipLaunchKernelGGL((k_scan<kDecW, kDecQ>), dim3((unsigned)nseq), dim3(kDecW * 64), 0, s, vs, b, W);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_resolve, dim3((unsigned)((slots + RW - 1) / RW)), dim3(RW * 64), 0, s, vs, b,
-                     W, (int32_t)slots);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  b.only = W.flags;
-  return launch_select_multi(views, qpos, nseq, b, s);
 }
 
 }  // namespace lsa
