@@ -367,6 +367,28 @@ def summarize(args):
     print("\n".join(lines))
 
 
+def summarize_decode(args):
+    """Decode kernel table from a rocprofv3 --stats CSV of `bench.py --profile-decode`."""
+    import csv
+    stats_csv, command = args.summarize_decode
+    wl = S.WORKLOADS["decode_1m"]
+    stats = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics: LSA decode, {wl.nseq} sequences x {wl.T} keys, "
+             f"{wl.steps} steps (run twice)", "", f"Command: `{command}`", "",
+             "Per-step kernels are called 2 x 256 = 512 times; the index build kernels run once "
+             "per sequence before the steps.", "",
+             "| kernel | calls | average us | total ms |", "|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        if "lsa" not in r["Name"]:
+            continue
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['TotalDurationNs'])/1e6:.3f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "decode_1m_rocprof.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,11 +400,18 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="one prefill step plus a 2 GiB calibration copy (for rocprofv3 runs)")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="only the decode benchmark (for rocprofv3 kernel traces)")
+    ap.add_argument("--summarize-decode", nargs=2, metavar=("STATS", "COMMAND"),
+                    help="write the decode kernel summary under profiles/ from a rocprofv3 stats CSV")
     ap.add_argument("--summarize", nargs=4, metavar=("STATS", "FETCH", "WRITE", "COMMAND"),
                     help="write profiles/ summaries from rocprofv3 CSV outputs")
     args = ap.parse_args()
     if args.summarize:
         summarize(args)
+        return
+    if args.summarize_decode:
+        summarize_decode(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the LSA hot path here is built and timed on a "
@@ -390,7 +419,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     workers_pool = None
-    if not args.no_cpu and not args.profile:
+    if not args.no_cpu and not args.profile and not args.profile_decode:
         # forked before anything touches the GPU; the workers only run the CPU oracle
         import multiprocessing as mp
         workers_pool = mp.get_context("fork").Pool(min(16, os.cpu_count() or 1))
@@ -401,6 +430,10 @@ def main():
     L.lib()
     if args.profile:
         profile_run(args, dev)
+        return
+    if args.profile_decode:
+        d = bench_decode(args, dev)
+        log(f"[profile] decode {d['tokens_per_s']:.0f} tok/s ({d['ms_per_step']:.3f} ms/step)")
         return
 
     res = bench_prefill(args, dev)

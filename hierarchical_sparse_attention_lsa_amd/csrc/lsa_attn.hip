@@ -209,10 +209,11 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
   }
 
   if (SPLIT) {
-    float* po = a.part_o + (int64_t)item * 16 * D;
+    float* po = a.part_o + (int64_t)item * G * D;     // [item][G][D]
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * grp + v;
+      if (h >= G) continue;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) po[h * D + 16 * nb + hl] = o[nb][v];
     }
@@ -239,8 +240,9 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
   }
 }
 
-// Combine split partial results: out[q][head][d] (one pass, online rescale;
-// the per-split loads are independent and unrolled so they overlap).
+// Combine split partial results: out[q][head][d]. The running maxima of the
+// splits are read first, then every split's weighted partial; the loads of
+// each loop are independent, so they are in flight together.
 template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(D) k_attn_merge(AttnArgs a) {
   const int qh = blockIdx.x;            // q * Hq + head
@@ -248,18 +250,22 @@ __global__ void __launch_bounds__(D) k_attn_merge(AttnArgs a) {
   const int q = qh / a.Hq, head = qh % a.Hq;
   const int g = head / a.G, h = head % a.G;
   const int64_t it0 = ((int64_t)q * a.Hkv + g) * a.splits;
-  float M = -INFINITY, num = 0.f, den = 0.f;
-#pragma unroll 8
+  const float* ml = a.part_ml + it0 * 32 + 2 * h;
+  float M = -INFINITY;
+#pragma unroll 16
   for (int s = 0; s < a.splits; ++s) {
-    const float ms = a.part_ml[(it0 + s) * 32 + 2 * h];
-    const float ls = a.part_ml[(it0 + s) * 32 + 2 * h + 1];
-    const float os = a.part_o[(it0 + s) * 16 * D + h * D + d];
-    if (ls <= 0.f) continue;
-    const float nm = fmaxf(M, ms);
-    const float c0 = exp2f(M - nm), c1 = exp2f(ms - nm);
-    num = num * c0 + os * c1;
-    den = den * c0 + ls * c1;
-    M = nm;
+    const float ms = ml[s * 32], ls = ml[s * 32 + 1];
+    M = ls > 0.f ? fmaxf(M, ms) : M;
+  }
+  const float* po = a.part_o + (it0 * a.G + h) * D + d;
+  float num = 0.f, den = 0.f;
+#pragma unroll 16
+  for (int s = 0; s < a.splits; ++s) {
+    const float ms = ml[s * 32], ls = ml[s * 32 + 1];
+    const float os = po[(int64_t)s * a.G * D];
+    const float w = ls > 0.f ? exp2f(ms - M) : 0.f;
+    num += os * w;
+    den += ls * w;
   }
   const float val = den > 0.f ? num / den : 0.f;
   const int64_t ob = (int64_t)qh * D + d;
