@@ -36,6 +36,7 @@ import lsa_synth as S  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "hierarchical_sparse_attention_lsa_amd", "csrc", "lsa_attn.hip")
+ATTN_KERNEL = "k_attn_win<128, false>"
 
 
 def log(*a):
@@ -68,7 +69,8 @@ def attn_algorithmic_bytes(wl, t0, n, cnt: np.ndarray) -> float:
 
     Long-range rows are counted per query (their reuse is data dependent and
     not credited); window and sink rows form one span for the whole chunk and
-    are counted once; plus the index lists, Q and O."""
+    are counted once; plus the index entries read (the long-range part of
+    each row and its count), Q and O."""
     row = wl.Hkv * wl.D * 2 * 2                     # K + V bytes per token
     t = np.arange(t0, t0 + n)
     wstart = np.maximum(0, t - wl.window + 1)
@@ -77,7 +79,7 @@ def attn_algorithmic_bytes(wl, t0, n, cnt: np.ndarray) -> float:
     lr = cnt.astype(np.int64) - nw - ns
     span = (t0 + n - max(0, t0 - wl.window + 1)) + min(wl.sinks, max(0, t0 - wl.window + 1))
     qo = n * wl.Hq * wl.D * 2 * 2
-    return float(lr.sum() * row + span * row + cnt.sum() * 4 + qo)
+    return float(lr.sum() * row + span * row + lr.sum() * 4 + n * 4 + qo)
 
 
 def bench_prefill(args, dev):
@@ -127,7 +129,7 @@ def bench_prefill(args, dev):
         if evs: evs[1].record()
         ix.select(latq, qpos, sp, idx=idx, cnt=cnt, ws=sel_ws)
         if evs: evs[2].record()
-        L.sparse_attn(q, K, V, idx, cnt, ap, out=out)
+        L.sparse_attn_window(q, K, V, idx, cnt, t0, sp, ap, out=out)
         if evs: evs[3].record()
 
     for _ in range(args.warmup):
@@ -345,8 +347,8 @@ def summarize(args):
     # the calibration copy is the run's last copy dispatch
     cf = _pmc_last(fetch_csv, "copyBuffer", "FETCH_SIZE")
     cw = _pmc_last(write_csv, "copyBuffer", "WRITE_SIZE")
-    af = _pmc_last(fetch_csv, "k_attn<128, false, false>", "FETCH_SIZE")
-    aw = _pmc_last(write_csv, "k_attn<128, false, false>", "WRITE_SIZE")
+    af = _pmc_last(fetch_csv, ATTN_KERNEL, "FETCH_SIZE")
+    aw = _pmc_last(write_csv, ATTN_KERNEL, "WRITE_SIZE")
     kf = CALIB_BYTES / (cf * 1024) if cf else None
     kw = CALIB_BYTES / (cw * 1024) if cw else None
     traffic = None
@@ -355,7 +357,7 @@ def summarize(args):
     lines += ["", "## HBM traffic of the attention kernel (rocprofv3 --pmc, one dispatch)", "",
               f"* calibration: a 2 GiB device copy reads FETCH_SIZE = {cf} KiB and writes WRITE_SIZE = {cw} KiB;"
               f" scale factors {kf} (fetch) and {kw} (write)",
-              f"* k_attn: FETCH_SIZE = {af} KiB, WRITE_SIZE = {aw} KiB per dispatch",
+              f"* {ATTN_KERNEL}: FETCH_SIZE = {af} KiB, WRITE_SIZE = {aw} KiB per dispatch",
               f"* scaled traffic per launch = {traffic} bytes"]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "attn_flat_10m_rocprof.md"), "w") as f:
@@ -490,7 +492,7 @@ def main():
                    + (f" tree G={wl.tree_group} S={wl.tree_super} R={wl.tree_top}" if wl.tree_group else ""),
                    "select": f"{wl.budget}+{wl.window}+{wl.sinks}",
                    "attention": f"GQA {wl.Hq}/{wl.Hkv} D={wl.D} bf16"},
-        "roofline": {"kernel": "k_attn (sparse GQA attention)", "bound": "hbm",
+        "roofline": {"kernel": f"{ATTN_KERNEL} (sparse GQA attention, shared windows)", "bound": "hbm",
                      "achieved": res["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": res["achieved_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": res["attn_bytes"],

@@ -61,6 +61,9 @@ EXPORTS = {
                            c_vp, c_sz, c_vp]),
     "lsa_sparse_attn": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32,
                                 ctypes.POINTER(AttnParams), c_vp, c_vp, c_sz, c_vp]),
+    "lsa_sparse_attn_window": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
+                                       ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                       c_vp, c_vp]),
     "lsa_prefill_chunk": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64,
                                   ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams), c_vp,
                                   c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -264,6 +267,25 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Te
     _check(lib().lsa_sparse_attn(_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt),
                                  idx.shape[1], nq, ctypes.byref(ap), _ptr(out), None, 0,
                                  _stream(stream)), "lsa_sparse_attn")
+    return out
+
+
+def sparse_attn_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                       cnt: torch.Tensor, qpos0: int, sp: SelectParams, ap: AttnParams,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention of queries at positions qpos0.. over rows written by select
+    with `sp`; the sinks and window are shared by consecutive queries."""
+    nq = q.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, torch.bfloat16, name)
+    _need(idx, torch.int32, "idx")
+    _need(cnt, torch.int32, "cnt", (nq,))
+    if out is None:
+        out = torch.empty((nq, ap.Hq, ap.D), dtype=torch.float32 if ap.out_f32 else torch.bfloat16,
+                          device=q.device)
+    _check(lib().lsa_sparse_attn_window(_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt),
+                                        idx.shape[1], nq, qpos0, ctypes.byref(sp), ctypes.byref(ap),
+                                        _ptr(out), _stream(stream)), "lsa_sparse_attn_window")
     return out
 
 

@@ -397,6 +397,26 @@ int lsa_sparse_attn(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_
   return LSA_OK;
 }
 
+int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                           int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                           int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
+                           const lsa_attn_params* ap, void* d_out, void* stream) {
+  if (int e = check_attn_params(ap)) return e;
+  if (!sp) return fail(LSA_E_ARG, "select params are NULL");
+  if (sp->window < 1 || sp->sinks < 0 || sp->budget < 0)
+    return fail(LSA_E_ARG, "bad select params (window %d, sinks %d, budget %d)", sp->window, sp->sinks,
+                sp->budget);
+  if (nq < 0 || kv_rows < 1 || qpos0 < 0) return fail(LSA_E_ARG, "bad nq / kv_rows / qpos0");
+  if (max_sel < max_sel_of(sp)) return fail(LSA_E_ARG, "max_sel %d < budget + window + sinks", max_sel);
+  if (qpos0 + nq > kv_rows) return fail(LSA_E_ARG, "query positions reach beyond kv_rows");
+  if (qpos0 + nq > INT32_MAX - 64) return fail(LSA_E_ARG, "query positions beyond int32");
+  if (nq > 0 && (!d_q || !d_k || !d_v || !d_idx || !d_cnt || !d_out)) return fail(LSA_E_ARG, "NULL buffer");
+  LSA_HIP(launch_attn_window(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp->window,
+                             sp->sinks, *ap, d_out, static_cast<hipStream_t>(stream)),
+          "attention");
+  return LSA_OK;
+}
+
 int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk,
                       const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
                       const uint16_t* d_v, int64_t kv_rows, const lsa_select_params* sp,
@@ -433,8 +453,8 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
   rc = select_impl(h, d_latq, nullptr, (int32_t)t0, (int32_t)n_chunk, sp, idx, cnt, sel_ws,
                    select_fast_ws_bytes((int32_t)n_chunk), s);
   if (rc != LSA_OK) return rc;
-  LSA_HIP(launch_attn(d_q, d_k, d_v, kv_rows, 0, (int32_t)n_chunk, idx, cnt, max_sel,
-                      (int32_t)n_chunk, *ap, d_out, nullptr, 1, s),
+  LSA_HIP(launch_attn_window(d_q, d_k, d_v, kv_rows, idx, cnt, max_sel, (int32_t)n_chunk, t0,
+                             sp->window, sp->sinks, *ap, d_out, s),
           "attention");
   return LSA_OK;
 }

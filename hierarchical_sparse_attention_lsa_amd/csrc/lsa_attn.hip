@@ -23,6 +23,7 @@
 // XCD (own L2) walks a contiguous range of queries, whose recent windows
 // overlap.
 #include <climits>
+#include <cstring>
 
 #include "lsa_device.h"
 #include "lsa_internal.h"
@@ -52,6 +53,11 @@ struct AttnArgs {
   void* out;
   float* part_o;             // [items][16][D] unnormalised partial outputs (split mode)
   float* part_ml;            // [items][16][2] running max (log2 domain) and sum
+  // window-sharing mode: queries are positions qpos0 .. qpos0+nq-1 and their
+  // rows end with the sinks and window of the select rule
+  int64_t qpos0;
+  int32_t window, sinks;
+  int32_t qpw;               // queries per wave (16 / G)
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int nwg) {
@@ -59,13 +65,115 @@ __device__ __forceinline__ int xcd_remap(int b, int nwg) {
   return x * per + min(x, rem) + k;
 }
 
+// One 16-key tile of the online-softmax attention of a wave.  Lane l loads
+// K row `r` for key slot l % 16 (every lane of that slot passes the same r);
+// bit v of `vmask` says whether S^T[4*(l/16)+v][l%16] (key 4*(l/16)+v of the
+// tile, column l%16) takes part.  o / m_run / l_run: the column's state.
+template <int D>
+__device__ __forceinline__ void attn_tile(const v8bf (&qb)[D / 32], const uint16_t* kbase,
+                                          const uint16_t* vbase, int64_t rowstride, int r,
+                                          unsigned vmask, float scale_log2, char* vl,
+                                          v4f (&o)[D / 16], float& m_run, float& l_run) {
+  constexpr int NKK = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int VROW = D * 2 + 16;
+  constexpr int VCH = D / 8;
+  constexpr int VLD = KT * VCH / 64;
+  const int lane = lane_id();
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+
+  // K rows -> A operand
+  v8bf ka[NKK];
+  {
+    const uint16_t* kp = kbase + (int64_t)r * rowstride + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      ka[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * kk));
+  }
+  // V rows -> LDS (row key, 16-byte chunk c)
+  v4i vr[VLD];
+#pragma unroll
+  for (int i = 0; i < VLD; ++i) {
+    const int c = i * 64 + lane;
+    const int key = c / VCH, ch = c % VCH;
+    const int rv = __shfl(r, key);
+    vr[i] = *reinterpret_cast<const v4i*>(vbase + (int64_t)rv * rowstride + ch * 8);
+  }
+
+  // S^T[key][column]
+  v4f s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_16x16x32(ka[kk], qb[kk], s);
+
+#pragma unroll
+  for (int i = 0; i < VLD; ++i) {
+    const int c = i * 64 + lane;
+    const int key = c / VCH, ch = c % VCH;
+    *reinterpret_cast<v4i*>(vl + key * VROW + ch * 16) = vr[i];
+  }
+
+  // online softmax for column hl over keys 4*grp + v
+  float sv[4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sv[v] = (vmask >> v) & 1u ? s[v] * scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, sv[v]);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(m_run, tmax);
+  const float alpha = exp2f(m_run - m_new);
+  float p[4], psum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) { p[v] = exp2f(sv[v] - m_new); psum += p[v]; }
+  psum += __shfl_xor(psum, 16);
+  psum += __shfl_xor(psum, 32);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+
+  // P (A operand, rows = columns, k = keys 4*grp..+3) as bf16 hi + lo
+  v4s phi, plo;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t hb = f32_to_bf16_bits(p[v]);
+    const float rem = p[v] - bf16_bits_to_f32(hb);
+    phi[v] = (short)hb;
+    plo[v] = (short)f32_to_bf16_bits(rem);
+  }
+  // rescale the accumulators: o rows are columns 4*grp + v
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float av = __shfl(alpha, 4 * grp + v);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb][v] *= av;
+  }
+
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // O += P V, V^T operand read key-major from LDS
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const char* vp = vl + (4 * grp) * VROW + (16 * nb + hl) * 2;
+    v4s vb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vb[e] = *reinterpret_cast<const short*>(vp + e * VROW);
+    o[nb] = mfma_bf16_16x16x16(phi, vb, o[nb]);
+    o[nb] = mfma_bf16_16x16x16(plo, vb, o[nb]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int D, bool OUT_F32, bool SPLIT>
 __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
   constexpr int NKK = D / 32;         // 32-deep slices of the head dim
   constexpr int NB = D / 16;          // 16-wide output column blocks
   constexpr int VROW = D * 2 + 16;    // padded LDS row (bytes)
-  constexpr int VCH = D / 8;          // 16-byte chunks per row
-  constexpr int VLD = KT * VCH / 64;  // 16-byte V loads per lane per tile
   __shared__ __attribute__((aligned(16))) char vlds[AW][KT * VROW];
 
   const int lane = lane_id();
@@ -120,92 +228,10 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
     const int slot = kb + hl;
     int r = slot < kend ? idxrow[slot] : 0;
     r = (int)min((int64_t)max(r, 0), rmax);
-
-    // K rows -> A operand
-    v8bf ka[NKK];
-    {
-      const uint16_t* kp = kbase + (int64_t)r * rowstride + 8 * grp;
+    unsigned vmask = 0;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        ka[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * kk));
-    }
-    // V rows -> LDS (row key, 16-byte chunk c)
-    v4i vr[VLD];
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int c = i * 64 + lane;
-      const int key = c / VCH, ch = c % VCH;
-      const int rv = __shfl(r, key);
-      vr[i] = *reinterpret_cast<const v4i*>(vbase + (int64_t)rv * rowstride + ch * 8);
-    }
-
-    // S^T[key][head]
-    v4f s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_16x16x32(ka[kk], qb[kk], s);
-
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int c = i * 64 + lane;
-      const int key = c / VCH, ch = c % VCH;
-      *reinterpret_cast<v4i*>(vl + key * VROW + ch * 16) = vr[i];
-    }
-
-    // online softmax for head hl over keys 4*grp + v
-    float sv[4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int key = kb + 4 * grp + v;
-      sv[v] = key < kend ? s[v] * a.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[v]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    float p[4], psum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) { p[v] = exp2f(sv[v] - m_new); psum += p[v]; }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // P (A operand, rows = heads, k = keys 4*grp..+3) as bf16 hi + lo
-    v4s phi, plo;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint32_t hb = f32_to_bf16_bits(p[v]);
-      const float rem = p[v] - bf16_bits_to_f32(hb);
-      phi[v] = (short)hb;
-      plo[v] = (short)f32_to_bf16_bits(rem);
-    }
-    // rescale the accumulators: o rows are heads 4*grp + v
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float av = __shfl(alpha, 4 * grp + v);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) o[nb][v] *= av;
-    }
-
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // O += P V, V^T operand read key-major from LDS
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const char* vp = vl + (4 * grp) * VROW + (16 * nb + hl) * 2;
-      v4s vb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vb[e] = *reinterpret_cast<const short*>(vp + e * VROW);
-      o[nb] = mfma_bf16_16x16x16(phi, vb, o[nb]);
-      o[nb] = mfma_bf16_16x16x16(plo, vb, o[nb]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int v = 0; v < 4; ++v) vmask |= (kb + 4 * grp + v < kend ? 1u : 0u) << v;
+    attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
   }
 
   if (SPLIT) {
@@ -231,6 +257,133 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
     if (h >= G) continue;
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     const int64_t ob = ((int64_t)q * a.Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float val = o[nb][v] * inv;
+      if (OUT_F32) reinterpret_cast<float*>(a.out)[ob + 16 * nb + hl] = val;
+      else reinterpret_cast<uint16_t*>(a.out)[ob + 16 * nb + hl] = (uint16_t)f32_to_bf16_bits(val);
+    }
+  }
+}
+
+// Window-sharing variant for consecutive query positions (prefill chunks).
+// The rows the select writes end with the sinks and the recent window, and
+// consecutive queries share almost all of their windows.  A wave here owns
+// QPW = 16 / G consecutive queries of one KV head: the 16 columns of S^T are
+// (query, head) pairs, so the MFMA tiles are full.  The wave first walks each
+// query's long-range keys (its own columns unmasked), then the union of the
+// group's sinks and windows once, as contiguous K/V rows, each column masked
+// to its own query's sinks and window.  Per query the result is the same
+// attention over the same key set; only the summation order differs.
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
+  constexpr int NKK = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int VROW = D * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char vlds[AW][KT * VROW];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int nwg = gridDim.x;
+  const int item = xcd_remap(blockIdx.x, nwg) * AW + wave;
+  const int QPW = a.qpw;
+  const int ngrp = (a.nq + QPW - 1) / QPW;
+  if (item >= ngrp * a.Hkv) return;
+  const int g = item % a.Hkv;
+  const int q0 = (item / a.Hkv) * QPW;
+  const int nqw = min(QPW, a.nq - q0);     // queries of this wave
+  const int G = a.G;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  // this lane's column: query jc of the group, head hc of the KV group
+  const int jc = hl / G, hc = hl % G;
+  const bool cval = jc < nqw;
+
+  const int64_t rowstride = (int64_t)a.Hkv * D;
+  const int64_t rmax = a.kv_rows - 1;
+
+  // query operand: column hl = (query q0 + jc, head g*G + hc)
+  v8bf qb[NKK];
+  {
+    const uint16_t* qp = a.q + ((int64_t)(q0 + (cval ? jc : 0)) * a.Hq + (int64_t)g * G + hc) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      v4i raw = cval ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
+      qb[kk] = __builtin_bit_cast(v8bf, raw);
+    }
+  }
+
+  v4f o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+
+  char* vl = vlds[wave];
+  const uint16_t* kbase = a.k + (int64_t)g * D;
+  const uint16_t* vbase = a.v + (int64_t)g * D;
+
+  // the select rule's sinks and window for query position t (positions fit
+  // in int32: an index holds fewer than 2^31 keys)
+  const int tq0 = (int)a.qpos0 + q0;
+  auto wstart_of = [&](int t) { return max(0, t - a.window + 1); };
+  auto nsink_of = [&](int ws) { return max(0, min(a.sinks, ws)); };
+
+  // 1. long-range keys of each query: the row's entries before its sinks and window
+  for (int j = 0; j < nqw; ++j) {
+    const int q = q0 + j;
+    const int t = tq0 + j;
+    const int ws = wstart_of(t);
+    const int nfix = nsink_of(ws) + (t - ws + 1);
+    const int nlr = max(0, min(a.cnt[q], a.max_sel) - nfix);
+    const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
+    const bool mine = cval && jc == j;
+    for (int kb = 0; kb < nlr; kb += KT) {
+      const int slot = kb + hl;
+      int r = slot < nlr ? idxrow[slot] : 0;
+      r = (int)min((int64_t)max(r, 0), rmax);
+      unsigned vmask = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) vmask |= (mine && kb + 4 * grp + v < nlr ? 1u : 0u) << v;
+      attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
+    }
+  }
+
+  // 2. the union of the group's sinks and windows, once: positions
+  //    [0, ns_last) then [max(ws_first, ns_last), t_last]
+  {
+    const int tl = tq0 + nqw - 1;
+    const int nsl = nsink_of(wstart_of(tl));
+    const int w0 = max(wstart_of(tq0), nsl);
+    const int nu = nsl + (tl - w0 + 1);
+    // this lane's column: its query's sinks [0, cns) and window [cws, ct]
+    const int ct = tq0 + jc;
+    const int cws = wstart_of(ct);
+    const int cns = nsink_of(cws);
+    const int shift = w0 - nsl;       // position of union slot u >= nsl is u + shift
+    for (int kb = 0; kb < nu; kb += KT) {
+      const int u = kb + hl;
+      const int pos = u < nsl ? u : u + shift;
+      const int r = (int)min((int64_t)pos, rmax);
+      unsigned vmask = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int uv = kb + 4 * grp + v;
+        const int pv = uv < nsl ? uv : uv + shift;
+        const bool in = cval && uv < nu && (pv < cns || (pv >= cws && pv <= ct));
+        vmask |= (in ? 1u : 0u) << v;
+      }
+      attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
+    }
+  }
+
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int col = 4 * grp + v;
+    const float lh = __shfl(l_run, col);
+    const int j = col / G, h = col % G;
+    if (j >= nqw) continue;
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const int64_t ob = ((int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float val = o[nb][v] * inv;
@@ -321,6 +474,35 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   } else {
     if (f32) hipLaunchKernelGGL((k_attn<64, true, false>), dim3(grid), dim3(AT), 0, s, a);
     else hipLaunchKernelGGL((k_attn<64, false, false>), dim3(grid), dim3(AT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
+                              int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
+                              int32_t sinks, const lsa_attn_params& ap, void* out, hipStream_t s) {
+  if (nq <= 0) return hipSuccess;
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q; a.k = k; a.v = v; a.kv_rows = kv_rows; a.seq_stride_rows = 0; a.qdiv = 1;
+  a.idx = idx; a.cnt = cnt; a.max_sel = max_sel; a.nq = nq;
+  a.Hq = ap.Hq; a.Hkv = ap.Hkv; a.G = ap.Hq / ap.Hkv;
+  a.splits = 1;
+  const float scale = ap.scale > 0.f ? ap.scale : 1.0f / sqrtf((float)ap.D);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.qpos0 = qpos0; a.window = window; a.sinks = sinks;
+  a.qpw = 16 / a.G;
+  const size_t items = (size_t)((nq + a.qpw - 1) / a.qpw) * ap.Hkv;
+  const unsigned grid = (unsigned)((items + AW - 1) / AW);
+  const bool f32 = ap.out_f32 != 0;
+  if (ap.D == 128) {
+    if (f32) hipLaunchKernelGGL((k_attn_win<128, true>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_win<128, false>), dim3(grid), dim3(AT), 0, s, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((k_attn_win<64, true>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_win<64, false>), dim3(grid), dim3(AT), 0, s, a);
   }
   return hipGetLastError();
 }

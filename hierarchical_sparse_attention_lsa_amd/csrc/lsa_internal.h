@@ -108,5 +108,10 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        const int32_t* idx, const int32_t* cnt, int32_t max_sel, int32_t nq,
                        const lsa_attn_params& ap, void* out, void* ws, int32_t splits,
                        hipStream_t s);
+// consecutive query positions qpos0.., rows ending with the select rule's sinks and window
+hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
+                              int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
+                              int32_t sinks, const lsa_attn_params& ap, void* out, hipStream_t s);
 
 }  // namespace lsa

@@ -178,11 +178,29 @@ LSA_API int lsa_sparse_attn(const uint16_t* d_q, const uint16_t* d_k, const uint
                             int32_t max_sel, int32_t nq, const lsa_attn_params* ap, void* d_out,
                             void* d_ws, size_t ws_bytes, void* stream);
 
+/* Attention of nq consecutive query tokens at positions qpos0 .. qpos0+nq-1
+ * over rows in the layout lsa_select writes with select params *sp: each row
+ * holds the long-range keys, then the sinks not in the window, then the
+ * window (the order documented above).  The sinks and the window are not
+ * read from the rows: they are the positions the select rule gives each
+ * query, and each group of 16/G consecutive queries (G = Hq/Hkv) reads the
+ * union of its sinks and windows once.  Requires max_sel >= budget + window +
+ * sinks and qpos0 + nq <= kv_rows.  Same attention over the same key set as
+ * lsa_sparse_attn on those rows; only the summation order differs.  (The
+ * selection paragraphs of the mauroscia.it page fix the sinks and window;
+ * sharing them between queries is this library's design.) */
+LSA_API int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                                   int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                                   int32_t max_sel, int32_t nq, int64_t qpos0,
+                                   const lsa_select_params* sp, const lsa_attn_params* ap,
+                                   void* d_out, void* stream);
+
 /* One prefill chunk: append the chunk's n_chunk latent keys, select for its
  * n_chunk queries (positions T_old .. T_old+n_chunk-1, scored against the
  * index that already holds the chunk's keys), attend.  The caller has
  * written K/V rows up to T_old+n_chunk.  d_idx_opt / d_cnt_opt (nullable)
- * receive the selection; otherwise it lives in the workspace. */
+ * receive the selection; otherwise it lives in the workspace.  Attention
+ * runs as lsa_sparse_attn_window. */
 LSA_API int lsa_prefill_chunk(lsa_index* h, const int8_t* d_latk_chunk, int64_t n_chunk,
                               const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
                               const uint16_t* d_v, int64_t kv_rows, const lsa_select_params* sp,

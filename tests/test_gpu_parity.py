@@ -204,6 +204,66 @@ def test_tiny_prefill_chunk_fused(tiny):
     assert err <= TOL
 
 
+WINDOW_CASES = [
+    # Hq, Hkv, D, qpos0, nq, budget, window, sinks
+    (4, 1, 64, 0, 37, 120, 40, 5),        # G=4: 4 queries a wave; windows cut at 0, no long-range keys
+    (8, 8, 128, 3000, 45, 200, 40, 5),    # G=1: 16 queries a wave, ragged group
+    (16, 2, 64, 2040, 33, 200, 64, 3),    # G=8: 2 queries a wave
+    (6, 2, 64, 100, 23, 80, 48, 7),       # G=3: 5 queries a wave, one column unused
+    (16, 1, 128, 4000, 20, 150, 40, 5),   # G=16: one query a wave
+    (4, 1, 64, 7, 50, 60, 4, 0),          # window = pool, no sinks
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES)
+def test_window_attention_matches_oracle(case):
+    """lsa_sparse_attn_window on rows laid out as the select writes them
+    (long-range keys in shuffled order, then sinks, then window), built on
+    the host from the oracle's selections."""
+    dev = _dev()
+    L = _L()
+    Hq, Hkv, D, qpos0, nq, budget, window, sinks = case
+    wl = S.Workload("win", 90, T=4096, ncomp=16, block=64, buckets=16, iters=2, chunk=0,
+                    budget=budget, window=window, sinks=sinks, Hq=Hq, Hkv=Hkv, D=D)
+    g = S.Synth(wl, data_cfg=90)
+    latk = g.latk(0, wl.T)
+    ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
+    pos = list(range(qpos0, qpos0 + nq))
+    lq = g.latq_rows(torch.tensor(pos))
+    osp = O.SelectParams(budget, window, sinks)
+    sels = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    rng = np.random.default_rng(qpos0 + nq)
+    idx = torch.full((nq, wl.max_sel), -1, dtype=torch.int32)
+    cnt = torch.zeros(nq, dtype=torch.int32)
+    for i, (t, sel) in enumerate(zip(pos, sels)):
+        ws = max(0, t - window + 1)
+        ns = max(0, min(sinks, ws))
+        fixed = list(range(ns)) + list(range(ws, t + 1))
+        assert set(fixed) <= set(sel.tolist())
+        lr = np.array(sorted(set(sel.tolist()) - set(fixed)), dtype=np.int64)
+        rng.shuffle(lr)
+        row = np.concatenate([lr, np.array(fixed, dtype=np.int64)]).astype(np.int32)
+        idx[i, :len(row)] = torch.from_numpy(row)
+        cnt[i] = len(row)
+    q = g.q_rows(torch.tensor(pos))
+    K = torch.empty((wl.T, Hkv, D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0)
+    g.fill_rows("v", V, 0)
+    qd, Kd, Vd, idd, cd = (t.to(dev) for t in (q, K, V, idx, cnt))
+    sp = L.SelectParams(budget, window, sinks, 0)
+    o32 = L.sparse_attn_window(qd, Kd, Vd, idd, cd, qpos0, sp, L.AttnParams(Hq, Hkv, D, 1, 0.0))
+    o16 = L.sparse_attn_window(qd, Kd, Vd, idd, cd, qpos0, sp, L.AttnParams(Hq, Hkv, D, 0, 0.0))
+    g32 = L.sparse_attn(qd, Kd, Vd, idd, cd, L.AttnParams(Hq, Hkv, D, 1, 0.0))
+    refo = oracle_attention(g, wl, pos, sels)
+    err = normwise(o32.cpu().numpy().astype(np.float64), refo)
+    err_generic = normwise(g32.cpu().numpy().astype(np.float64), refo)
+    print(f"window attention {case}: normwise error {err:.3e} (generic kernel {err_generic:.3e})")
+    assert err <= TOL and err_generic <= TOL
+    assert np.array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16),
+                          rne_bf16_bits(o32.cpu().numpy()))
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_append_equals_build(seed):
     """Chunked and per-token appends (crossing tail re-clusters) equal a one-shot build."""
