@@ -99,6 +99,66 @@ __device__ void wave_bitonic(T* a, int n) {
 }
 
 
+// Block-wide reductions and an exclusive scan over NT threads; `red` is LDS
+// scratch of NT/64 entries.  Every thread of the block must call them.
+template <int NT>
+__device__ __forceinline__ long long block_sum_ll(long long x, long long* red) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += shfl_xor_i64(x, m);
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  long long s = 0;
+  for (int w = 0; w < NT / 64; ++w) s += red[w];
+  return s;
+}
+
+template <int NT>
+__device__ __forceinline__ long long block_min_ll(long long x, long long* red) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = min(x, shfl_xor_i64(x, m));
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  long long s = LLONG_MAX;
+  for (int w = 0; w < NT / 64; ++w) s = min(s, red[w]);
+  return s;
+}
+
+template <int NT>
+__device__ __forceinline__ long long block_max_ll(long long x, long long* red) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = max(x, shfl_xor_i64(x, m));
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  long long s = LLONG_MIN;
+  for (int w = 0; w < NT / 64; ++w) s = max(s, red[w]);
+  return s;
+}
+
+// Exclusive prefix sum over the block in thread order; *total = block sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int x, int* red, int* total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int wt;
+  const int ex = wave_excl_scan(x, &wt);
+  __syncthreads();
+  if (lane == 0) red[wave] = wt;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < NT / 64; ++w) {
+    const int v = red[w];
+    before += w < wave ? v : 0;
+    all += v;
+  }
+  *total = all;
+  return before + ex;
+}
+
 // Writes one query's selection row: the taken buckets em[0..n) (bucket ids,
 // any order; `pb` is the one cut bucket, taking `ptake` keys, or -1) in
 // ascending id order with their eligible keys in ascending position, then

@@ -84,61 +84,6 @@ __device__ __forceinline__ long long rebuilt_key(int s, int beta) {
   return order_key(s, beta);
 }
 
-// Block-wide reductions / scans over DT threads (LDS scratch of DW entries).
-__device__ __forceinline__ long long block_sum_ll(long long x, long long* red) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += shfl_xor_i64(x, m);
-  __syncthreads();
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  long long s = 0;
-  for (int w = 0; w < DW; ++w) s += red[w];
-  return s;
-}
-
-__device__ __forceinline__ long long block_min_ll(long long x, long long* red) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = min(x, shfl_xor_i64(x, m));
-  __syncthreads();
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  long long s = LLONG_MAX;
-  for (int w = 0; w < DW; ++w) s = min(s, red[w]);
-  return s;
-}
-
-__device__ __forceinline__ long long block_max_ll(long long x, long long* red) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = max(x, shfl_xor_i64(x, m));
-  __syncthreads();
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  long long s = LLONG_MIN;
-  for (int w = 0; w < DW; ++w) s = max(s, red[w]);
-  return s;
-}
-
-// Exclusive prefix sum over the block in thread order; *total = block sum.
-__device__ __forceinline__ int block_excl_scan(int x, int* red, int* total) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int wt;
-  const int ex = wave_excl_scan(x, &wt);
-  __syncthreads();
-  if (lane == 0) red[wave] = wt;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < DW; ++w) {
-    const int v = red[w];
-    before += w < wave ? v : 0;
-    all += v;
-  }
-  *total = all;
-  return before + ex;
-}
-
 __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs W,
                                                    int32_t* __restrict__ flags) {
   __shared__ int s_hk[RB], s_hb[RB];
@@ -184,9 +129,9 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     hi = max(hi, ok ? ku : LLONG_MIN);
     tot += ok ? eu : 0;
   }
-  tot = block_sum_ll(tot, s_red);
-  lo = block_min_ll(lo, s_red);
-  hi = block_max_ll(hi, s_red);
+  tot = block_sum_ll<DT>(tot, s_red);
+  lo = block_min_ll<DT>(lo, s_red);
+  hi = block_max_ll<DT>(hi, s_red);
   // keys above `hi` are taken whole; the bracket [lo, hi] holds the cutoff
   if (B <= 0) {
     hi = LLONG_MAX;                  // nothing is taken
@@ -212,7 +157,7 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
         atomicAdd(&s_hk[bin], eu);
         atomicAdd(&s_hb[bin], 1);
       }
-      ab = block_sum_ll(ab, s_red);
+      ab = block_sum_ll<DT>(ab, s_red);
       if (wave == 0) {
         int h[RB / 64], c[RB / 64], loc = 0;
 #pragma unroll
@@ -258,7 +203,7 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     const int c = atomicAdd(&s_nc, 1);
     if (c < RCAP) { s_cq[c] = -ku; s_ci[c] = u * DT + tid; }
   }
-  full = block_sum_ll(full, s_red);
+  full = block_sum_ll<DT>(full, s_red);
   const int nc = min(s_nc, RCAP);
   const bool overflow = s_nc > RCAP;
   if (wave == 0 && nc > 0 && !overflow) {
@@ -313,8 +258,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     mcnt += tk[u] > 0 ? 1 : 0;
   }
   int out_total, nt;
-  int off = block_excl_scan(mine, s_ired, &out_total);
-  int rank = block_excl_scan(mcnt, s_ired, &nt);   // the scans' barriers end all reads of s_e
+  int off = block_excl_scan<DT>(mine, s_ired, &out_total);
+  int rank = block_excl_scan<DT>(mcnt, s_ired, &nt);   // the scans' barriers end all reads of s_e
   const bool ok = !overflow && nt <= kListCap;
   // list of taken buckets (output offset, first key slot), ascending ids, over s_e
   int* l_off = s_e;

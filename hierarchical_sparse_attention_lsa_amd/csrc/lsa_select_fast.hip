@@ -21,15 +21,17 @@
 //   The centroids and bucket sizes stream through LDS in double-buffered
 //   chunks (each centroid byte is read once per workgroup, all lanes keep
 //   loads in flight) and the full pass is MFMA + compare + rare store.
-// k_resolve (one wave per query; lane j owns sub-list j):
+// k_resolve (one 256-thread workgroup per query; the list's entries sit in
+// registers, 16 per thread):
 //   eligible key counts of the entries; if they reach the budget the cutoff
 //   is in the list: histogram refinement finds a bracket of <= 256 entries,
 //   entries above it are taken whole, the bracket is sorted and taken in
-//   order with the last bucket cut; the taken buckets are sorted by id and
-//   their keys written (ascending bucket ids keep each query's gather
-//   walking the KV cache once from start to end).  A query whose list
-//   overflowed or falls short of the budget is flagged and the exact
-//   refinement kernel recomputes it.
+//   order with the last bucket cut; the taken buckets are sorted by id
+//   (bitonic, in registers) and their keys written, every thread on its own
+//   output slots (ascending bucket ids keep each query's gather walking the
+//   KV cache once from start to end).  A query whose list overflowed or
+//   falls short of the budget is flagged and the exact refinement kernel
+//   recomputes it.
 #include <climits>
 #include <cstring>
 
@@ -85,6 +87,7 @@ struct __attribute__((aligned(16))) ScanLds {
   int slo[QS];
   long long ssum[QS];
   int hist[QS][NB2];
+  int nl[QS][NSUB];                 // sub-list sizes
   v4i cent[2][CHT * 64];
   int cnt[2][CHT * 16];
 };
@@ -157,6 +160,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     W.meta[2 * (lbase + i) + 1] = t;
   }
   for (int e = tid; e < QS * NB2; e += C::FT) (&S.hist[0][0])[e] = 0;
+  for (int e = tid; e < QS * NSUB; e += C::FT) (&S.nl[0][0])[e] = 0;
   __syncthreads();
 
   v4i qa = {0, 0, 0, 0};
@@ -250,318 +254,377 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   }
 
   // ---- 3. full pass: buckets at or above the threshold join the lists ----
+  // The MFMA starts from -threshold, so a (query, bucket) pair is a hit when
+  // its result is >= 0.  Per group of four tiles a lane folds the sign bits
+  // of its 16 results into a mask (one alignbit each); only lanes with hits
+  // loop over them (about one pair in a hundred), picking the result with a
+  // select tree and taking a slot of the sub-list (bucket id mod 64) from an
+  // LDS counter.
   {
-    // prefill: a lane sees tiles of every residue mod 4 (4 sub-lists per
-    // query); decode: each wave's tiles share one residue (1 sub-list)
-    constexpr int NSL = C::PH == 1 ? 4 : 1;
-    int slo[4], nl[NSL][4];
-    long long* lp[4];
+    static_assert(C::PH == 1, "the full pass gives each wave its own query group");
+    int slo[4];
+    v4i bias;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      slo[v] = act[v] ? S.slo[qrow + v] : INT_MAX;
-      lp[v] = W.key + (lbase + qrow + v) * LC + col;
-#pragma unroll
-      for (int u = 0; u < NSL; ++u) nl[u][v] = 0;
+      slo[v] = act[v] ? S.slo[qrow + v] : (1 << 30);    // 1<<30: no score reaches it
+      bias[v] = -slo[v];
     }
     stream_chunks(V, S, 0, 1, nchunks, [&](int c, int buf) {
-      constexpr int TPW = CHT / C::PH;              // tiles of this wave per chunk
 #pragma unroll
-      for (int g = 0; g < TPW; g += 4) {
-        v4i sc[4];
+      for (int g = 0; g < CHT; g += 4) {
+        int d[16];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const v4i z = {0, 0, 0, 0};
-          sc[u] = mfma_i8_16x16x64(qa, S.cent[buf][(phase + (g + u) * C::PH) * 64 + lane], z);
+          const v4i r = mfma_i8_16x16x64(qa, S.cent[buf][(g + u) * 64 + lane], bias);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) d[4 * u + v] = r[v];
         }
+        unsigned miss = 0;                // bit k: pair k = 4u + v below the threshold
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int tile = c * CHT + phase + (g + u) * C::PH;
-          const int beta = tile * 16 + col;
-          const int su = NSL == 4 ? u : 0;
-          const int sub = (tile & 3) * 16 + col;      // = beta mod 64
+        for (int k = 15; k >= 0; --k) miss = __builtin_amdgcn_alignbit(miss, (unsigned)d[k], 31);
+        unsigned hits = ~miss & 0xffffu;
+        const int tb = c * CHT + g;       // first tile of the group
+        if ((tb + 4) * 16 > V.n_bkt) {    // last group: no buckets past the end
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            if (sc[u][v] >= slo[v] && beta < V.n_bkt) {
-              if (nl[su][v] < SUBCAP)
-                lp[v][(int64_t)nl[su][v] * NSUB + (sub - col)] = order_key(sc[u][v], beta);
-              ++nl[su][v];
-            }
-          }
+          for (int u = 0; u < 4; ++u)
+            if ((tb + u) * 16 + col >= V.n_bkt) hits &= ~(0xfu << (4 * u));
+        }
+        while (hits) {
+          const int k = __builtin_ctz(hits);
+          hits &= hits - 1;
+          // d[k] as a tree of bit selects (a plain d[k] would put d in memory)
+          const unsigned m0 = 0u - (k & 1), m1 = 0u - ((k >> 1) & 1);
+          const unsigned m2 = 0u - ((k >> 2) & 1), m3 = 0u - ((k >> 3) & 1);
+          unsigned x[8], y[4], z[2];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = ((unsigned)d[2 * i + 1] & m0) | ((unsigned)d[2 * i] & ~m0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = (x[2 * i + 1] & m1) | (x[2 * i] & ~m1);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) z[i] = (y[2 * i + 1] & m2) | (y[2 * i] & ~m2);
+          const int dk = (int)((z[1] & m3) | (z[0] & ~m3));
+          const int v = k & 3, u = k >> 2;
+          const int sv = (v & 2) ? ((v & 1) ? slo[3] : slo[2]) : ((v & 1) ? slo[1] : slo[0]);
+          const int beta = (tb + u) * 16 + col;
+          const int jl = beta & (NSUB - 1);
+          const int qs = qrow + v;
+          const int pos = atomicAdd(&S.nl[qs][jl], 1);
+          if (pos < SUBCAP) W.key[(lbase + qs) * LC + (int64_t)pos * NSUB + jl] = order_key(dk + sv, beta);
         }
       }
     });
+    for (int e = tid; e < QS * NSUB; e += C::FT)
+      W.nsub[(lbase + e / NSUB) * NSUB + e % NSUB] = (&S.nl[0][0])[e];
+  }
+}
+
+// One 256-thread workgroup per query slot.  The list's entries, numbered
+// sub-list by sub-list, are dealt to the threads: thread tid holds entries
+// tid + RT*u (u < TPQ) in registers.
+constexpr int RT = 256;
+constexpr int TPQ = 16;             // entries per thread
+constexpr int KCAP = TPQ * RT;      // entries per query (else the exact kernel)
+constexpr int ECAP2 = 1024;         // taken buckets per query (else the exact kernel)
+constexpr int EPT = ECAP2 / RT;     // sorted taken buckets per thread
+
+// Ascending bitonic sort of the block's ECAP2 values, EPT consecutive ones per
+// thread (element tid*EPT + i in v[i]): partners in the same thread swap in
+// registers, in the same wave through shuffles, across waves through `tmp`.
+__device__ __forceinline__ void block_bitonic(long long (&v)[EPT], long long* tmp) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= ECAP2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      long long pv[EPT];
+      if (j < EPT) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (!act[v]) continue;
+        for (int i = 0; i < EPT; ++i) pv[i] = v[i ^ j];
+      } else if (j < EPT * 64) {
 #pragma unroll
-      for (int u = 0; u < NSL; ++u) {
-        const int sub = (NSL == 4 ? u : phase) * 16 + col;
-        W.nsub[(lbase + qrow + v) * NSUB + sub] = nl[u][v];
+        for (int i = 0; i < EPT; ++i) pv[i] = shfl_xor_i64(v[i], j / EPT);
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) tmp[tid * EPT + i] = v[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) pv[i] = tmp[(tid * EPT + i) ^ j];
+      }
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        const bool up = (e & k) == 0, lower = (e & j) == 0;
+        const long long mn = min(v[i], pv[i]), mx = max(v[i], pv[i]);
+        v[i] = (up == lower) ? mn : mx;
       }
     }
   }
 }
 
-// One wave per query slot.
-constexpr int RW = 4;               // waves per resolve workgroup
-
-__global__ void __launch_bounds__(RW * 64) k_resolve(FastViews VS, SelArgs A, ListWs W,
-                                                     int32_t nslots) {
-  __shared__ int s_hk[RW][RB];
-  __shared__ int s_hb[RW][RB];
-  __shared__ long long s_cq[RW][RCAP];
-  __shared__ int s_ci[RW][RCAP];
-  __shared__ long long s_em[RW][ECAP];
+__global__ void __launch_bounds__(RT) k_resolve(FastViews VS, SelArgs A, ListWs W) {
+  __shared__ int s_hk[RB], s_hb[RB];
+  __shared__ long long s_red[RT / 64];
+  __shared__ int s_ired[RT / 64];
+  __shared__ long long s_cq[RCAP];   // bracket: -order key, then sorted
+  __shared__ int s_ci[RCAP];         // bracket: collection index (payload of the sort)
+  __shared__ int s_ce[RCAP], s_cks[RCAP];
+  __shared__ long long s_key[ECAP2]; // taken: (bucket id << 32 | entry); sort scratch; (offset << 32 | first key slot)
+  __shared__ int s_tk[ECAP2], s_ks[ECAP2];
+  __shared__ int s_nc, s_nt, s_cut[2];
+  __shared__ int s_pre[NSUB + 1];    // entries before sub-list j
   const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int64_t slot = (int64_t)blockIdx.x * RW + wave;
-  if (slot >= nslots) return;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int64_t slot = blockIdx.x;
   const int q = W.meta[2 * slot];
-  if (q < 0) return;
+  if (q < 0) return;                 // uniform over the workgroup
   const int t = W.meta[2 * slot + 1];
   const IdxView V = vsp->v[VS.nviews > 1 ? (int)(slot / VS.slots_per_view) : 0];
   const int B = A.budget;
   const int p = V.pool;
-  int* hk = s_hk[wave];
-  int* hb = s_hb[wave];
-  long long* cq = s_cq[wave];
-  int* ci = s_ci[wave];
-  long long* em = s_em[wave];
-  long long* lk = W.key + slot * LC;
-  int32_t* le = W.elig + slot * LC;
-  int32_t* ls = W.kstart + slot * LC;
-
-  // lane j owns sub-list j: entries k*64 + j, k < len
-  const int len = W.nsub[slot * NSUB + lane];
-  bool ok = B > 0 && __ballot(len > SUBCAP) == 0ull;
-  int kmax = min(len, SUBCAP);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) kmax = max(kmax, __shfl_xor(kmax, m));
-  const int mylen = min(len, SUBCAP);
-
-  // eligible keys of each entry and where its first key sits
-  long long lo = LLONG_MAX, hi = LLONG_MIN;
-  int total = 0;
-  if (ok) {
-    for (int k0 = 0; k0 < kmax; k0 += 8) {
-      long long K[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) K[u] = k0 + u < mylen ? lk[(k0 + u) * NSUB + lane] : LLONG_MIN;
-      BucketInfo bi[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int beta = (int)(0xffffffffu - (unsigned)(K[u] & 0xffffffffll));
-        bi[u] = K[u] != LLONG_MIN ? load_bucket<false>(V, beta) : BucketInfo{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (K[u] == LLONG_MIN) continue;
-        int klo;
-        const int e = eligible<false>(V, 0, bi[u], t, A.window, A.sinks, &klo);
-        le[(k0 + u) * NSUB + lane] = e;
-        ls[(k0 + u) * NSUB + lane] = bi[u].off * p + klo;
-        total += e;
-        if (e > 0) { lo = min(lo, K[u]); hi = max(hi, K[u]); }
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      lo = min(lo, shfl_xor_i64(lo, m));
-      hi = max(hi, shfl_xor_i64(hi, m));
-      total += __shfl_xor(total, m);
-    }
-    ok = total >= B;
+  const long long* lk = W.key + slot * LC;
+  int len = 0;
+  if (wave == 0) {
+    len = W.nsub[slot * NSUB + lane];
+    int all;
+    const int ex = wave_excl_scan(min(len, SUBCAP), &all);
+    s_pre[lane] = ex;
+    if (lane == 63) s_pre[NSUB] = all;
   }
-  __threadfence_block();
+  if (tid == 0) { s_nc = 0; s_nt = 0; }
+  // a sub-list that overflowed, or more entries than the registers hold: exact kernel
+  bool ok = __syncthreads_or(len > SUBCAP) == 0;
+  const int ntot = s_pre[NSUB];
+  ok = ok && B > 0 && ntot <= KCAP;
 
-  // histogram refinement over the list until the cutoff bracket is small
-  bool done = false;
-  for (int pass = 0; ok && pass < 8 && !done; ++pass) {
-    const long long range = hi - lo + 1;
-    int sh = 0;
-    while (sh < 62 && ((range + (1ll << sh) - 1) >> sh) > RB) ++sh;
-    for (int i = lane; i < RB; i += 64) { hk[i] = 0; hb[i] = 0; }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    int ab = 0;
-    for (int k0 = 0; k0 < kmax; k0 += 4) {
-      long long K[4];
-      int e[4];
+  // entries, their eligible keys and first key slots (all loads of a thread in flight together)
+  // (the first key slot of entry f goes to kstart[f])
+  long long K[TPQ];
+  int e[TPQ];
+  long long lo = LLONG_MAX, hi = LLONG_MIN, tot = 0;
+  if (ok) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool in = k0 + u < mylen;
-        K[u] = in ? lk[(k0 + u) * NSUB + lane] : 0;
-        e[u] = in ? le[(k0 + u) * NSUB + lane] : 0;
+    for (int u = 0; u < TPQ; ++u) {
+      const int f = tid + RT * u;    // entry number -> (sub-list a, position f - s_pre[a])
+      K[u] = LLONG_MIN;
+      if (f < ntot) {
+        int a = 0, b = NSUB - 1;     // last sub-list starting at or before f
+        while (a < b) {
+          const int m = (a + b + 1) >> 1;
+          if (s_pre[m] <= f) a = m; else b = m - 1;
+        }
+        K[u] = lk[(f - s_pre[a]) * NSUB + a];
       }
+    }
+    BucketInfo bi[TPQ];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (e[u] <= 0) continue;
-        if (K[u] > hi) { ab += e[u]; continue; }
-        if (K[u] < lo) continue;
+    for (int u = 0; u < TPQ; ++u) {
+      const int beta = (int)(0xffffffffu - (unsigned)(K[u] & 0xffffffffll));
+      bi[u] = K[u] != LLONG_MIN ? load_bucket<false>(V, beta) : BucketInfo{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < TPQ; ++u) {
+      e[u] = 0;
+      if (K[u] == LLONG_MIN) continue;
+      int klo;
+      e[u] = eligible<false>(V, 0, bi[u], t, A.window, A.sinks, &klo);
+      W.kstart[slot * LC + tid + RT * u] = bi[u].off * p + klo;
+    }
+#pragma unroll
+    for (int u = 0; u < TPQ; ++u) {
+      const bool in = e[u] > 0;
+      lo = min(lo, in ? K[u] : LLONG_MAX);
+      hi = max(hi, in ? K[u] : LLONG_MIN);
+      tot += in ? e[u] : 0;
+    }
+  }
+  tot = block_sum_ll<RT>(tot, s_red);
+  lo = block_min_ll<RT>(lo, s_red);
+  hi = block_max_ll<RT>(hi, s_red);
+  ok = ok && tot >= B;               // the list must hold the cutoff
+
+  // histogram refinement: keys above `hi` are taken whole, the cutoff is in [lo, hi]
+  if (ok) {
+    for (int pass = 0; pass < 8; ++pass) {
+      const long long range = hi - lo + 1;
+      int sh = 0;
+      while (sh < 62 && ((range + (1ll << sh) - 1) >> sh) > RB) ++sh;
+      for (int i = tid; i < RB; i += RT) { s_hk[i] = 0; s_hb[i] = 0; }
+      __syncthreads();
+      long long ab = 0;
+#pragma unroll
+      for (int u = 0; u < TPQ; ++u) {
+        ab += (e[u] > 0 && K[u] > hi) ? e[u] : 0;
+        if (e[u] <= 0 || K[u] > hi || K[u] < lo) continue;
         const int bin = (int)((hi - K[u]) >> sh);
-        atomicAdd(&hk[bin], e[u]);
-        atomicAdd(&hb[bin], 1);
+        atomicAdd(&s_hk[bin], e[u]);
+        atomicAdd(&s_hb[bin], 1);
+      }
+      ab = block_sum_ll<RT>(ab, s_red);
+      if (wave == 0) {
+        int h[RB / 64], c[RB / 64], loc = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) { h[k] = s_hk[(RB / 64) * lane + k]; c[k] = s_hb[(RB / 64) * lane + k]; loc += h[k]; }
+        int wt;
+        const int ex = wave_excl_scan(loc, &wt);
+        long long cum = ab + ex;
+        int found = -1, fb = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) {
+          if (found < 0 && cum + h[k] >= B) { found = (RB / 64) * lane + k; fb = c[k]; }
+          cum += h[k];
+        }
+        const unsigned long long mk = __ballot(found >= 0);
+        const int src = mk ? __ffsll((long long)mk) - 1 : 0;
+        const int bsel = __shfl(found, src), nbsel = __shfl(fb, src);
+        if (lane == 0) { s_cut[0] = mk ? bsel : -1; s_cut[1] = mk ? nbsel : 0; }
+      }
+      __syncthreads();
+      const int bin = s_cut[0], nb = s_cut[1];
+      if (bin < 0) { ok = false; break; }   // not reached: the bracket holds the cutoff
+      const long long nhi = hi - ((long long)bin << sh);
+      long long nlo = hi - ((long long)(bin + 1) << sh) + 1;
+      if (nlo < lo) nlo = lo;
+      lo = nlo; hi = nhi;
+      __syncthreads();
+      if (nb <= RCAP) break;
+    }
+  }
+
+  // taken entries: above the bracket whole (straight into the taken list);
+  // bracket entries collected for the ordered walk
+  const int64_t lbase = slot * LC;
+  if (ok) {
+#pragma unroll
+    for (int u = 0; u < TPQ; ++u) {
+      if (e[u] <= 0 || K[u] < lo) continue;
+      const int i = tid + RT * u;
+      const int beta = (int)(0xffffffffu - (unsigned)(K[u] & 0xffffffffll));
+      if (K[u] > hi) {
+        const int r = atomicAdd(&s_nt, 1);
+        if (r < ECAP2) {
+          s_key[r] = ((long long)beta << 32) | (unsigned)r;
+          s_tk[r] = e[u];
+          s_ks[r] = W.kstart[lbase + i];
+        }
+      } else {
+        const int c = atomicAdd(&s_nc, 1);
+        if (c < RCAP) { s_cq[c] = -K[u]; s_ci[c] = c; s_ce[c] = e[u]; s_cks[c] = W.kstart[lbase + i]; }
       }
     }
-    int abt;
-    wave_excl_scan(ab, &abt);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    int h[RB / 64], c[RB / 64], loc = 0;
-#pragma unroll
-    for (int k = 0; k < RB / 64; ++k) { h[k] = hk[(RB / 64) * lane + k]; c[k] = hb[(RB / 64) * lane + k]; loc += h[k]; }
-    int tot;
-    const int ex = wave_excl_scan(loc, &tot);
-    int cum = abt + ex, found = -1, fb = 0;
-#pragma unroll
-    for (int k = 0; k < RB / 64; ++k) {
-      if (found < 0 && cum + h[k] >= B) { found = (RB / 64) * lane + k; fb = c[k]; }
-      cum += h[k];
-    }
-    const unsigned long long mk = __ballot(found >= 0);
-    if (!mk) { ok = false; break; }
-    const int src = __ffsll((long long)mk) - 1;
-    const int bin = __shfl(found, src);
-    const int nb = __shfl(fb, src);
-    const long long nhi = hi - ((long long)bin << sh);
-    long long nlo = hi - ((long long)(bin + 1) << sh) + 1;
-    if (nlo < lo) nlo = lo;
-    lo = nlo; hi = nhi;
-    done = nb <= RCAP;
   }
-  ok = ok && done;
-
-  if (ok) {
-    // takes: entries above the bracket whole, below nothing; the bracket's
-    // entries collected for the ordered walk
-    int nc = 0, full = 0;
-    for (int k0 = 0; k0 < kmax; ++k0) {
-      const bool in = k0 < mylen;
-      const int i = k0 * NSUB + lane;
-      const long long K = in ? lk[i] : 0;
-      const int e = in ? le[i] : 0;
-      const bool tk = e > 0 && K > hi;
-      const bool cd = e > 0 && K >= lo && K <= hi;
-      const unsigned long long mc = __ballot(cd);
-      const int r = nc + __popcll(mc & ((1ull << lane) - 1ull));
-      if (cd) { cq[r] = -K; ci[r] = i; }
-      nc += __popcll(mc);
-      if (in) le[i] = tk ? e : 0;
-      full += tk ? e : 0;
-    }
+  long long full = 0;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) full += __shfl_xor(full, m);
-    // bracket in (score desc, id asc) order; payload = list index
+  for (int u = 0; u < TPQ; ++u) full += (ok && e[u] > 0 && K[u] > hi) ? e[u] : 0;
+  full = block_sum_ll<RT>(full, s_red);
+  const int nc = s_nc;
+  ok = ok && nc <= RCAP;
+  if (ok && wave == 0 && nc > 0) {
     int np = 1;
     while (np < nc) np <<= 1;
-    for (int i = nc + lane; i < np; i += 64) { cq[i] = LLONG_MAX; ci[i] = -1; }
+    for (int i = nc + lane; i < np; i += 64) { s_cq[i] = LLONG_MAX; s_ci[i] = -1; }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     for (int k = 2; k <= np; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
         for (int i = lane; i < np; i += 64) {
-          const int ixj = i ^ j;
+          const int ixj = i ^ jj;
           if (ixj > i) {
-            const long long x = cq[i], y = cq[ixj];
+            const long long x = s_cq[i], y = s_cq[ixj];
             const bool up = (i & k) == 0;
-            if ((x > y) == up) { cq[i] = y; cq[ixj] = x; const int tmp = ci[i]; ci[i] = ci[ixj]; ci[ixj] = tmp; }
+            if ((x > y) == up) { s_cq[i] = y; s_cq[ixj] = x; const int tmp = s_ci[i]; s_ci[i] = s_ci[ixj]; s_ci[ixj] = tmp; }
           }
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       }
     }
-    __threadfence_block();
-    int need = B - full;
-    for (int base = 0; base < nc; base += 64) {
-      const int i = base + lane;
-      int e = 0, li = -1;
-      if (i < nc) {
-        li = ci[i];
-        const long long K = -cq[i];
-        const int beta = (int)(0xffffffffu - (unsigned)(K & 0xffffffffll));
-        const BucketInfo bi = load_bucket<false>(V, beta);
-        int klo;
-        e = eligible<false>(V, 0, bi, t, A.window, A.sinks, &klo);
+    // walk in (score desc, id asc) order; the last bucket taken is cut
+    long long need = B - full;
+    for (int b0 = 0; b0 < nc; b0 += 64) {
+      const int i = b0 + lane;
+      int ee = 0, c = -1;
+      if (i < nc) { c = s_ci[i]; ee = s_ce[c]; }
+      int tot2;
+      const int before = wave_excl_scan(ee, &tot2);
+      const int tk = (int)max(0ll, min((long long)ee, need - before));
+      if (tk > 0) {
+        const int r = atomicAdd(&s_nt, 1);
+        if (r < ECAP2) {
+          const long long Kc = -s_cq[i];
+          const int beta = (int)(0xffffffffu - (unsigned)(Kc & 0xffffffffll));
+          s_key[r] = ((long long)beta << 32) | (unsigned)r;
+          s_tk[r] = tk;
+          s_ks[r] = s_cks[c];
+        }
       }
-      int tot;
-      const int before = wave_excl_scan(e, &tot);
-      const int take = min(e, max(0, need - before));
-      if (li >= 0) le[li] = take;
-      need -= tot;
+      need -= tot2;
     }
-    __threadfence_block();
+  }
+  __syncthreads();
+  const int nt = s_nt;
+  ok = ok && nt <= ECAP2;
 
-    // taken buckets sorted by id (key: id << 32 | list index), keys written in order
-    int ntake = 0;
-    for (int k0 = 0; k0 < kmax; ++k0) {
-      const int i = k0 * NSUB + lane;
-      const int take = k0 < mylen ? le[i] : 0;
-      const unsigned long long mt = __ballot(take > 0);
-      if (take > 0) {
-        const int r = ntake + __popcll(mt & ((1ull << lane) - 1ull));
-        if (r < ECAP) {
-          const long long K = lk[i];
-          em[r] = ((long long)(0xffffffffu - (unsigned)(K & 0xffffffffll)) << 32) | (long long)i;
-        }
-      }
-      ntake += __popcll(mt);
-    }
-    ok = ntake <= ECAP;
-  }
+  int32_t* row = A.idx + (int64_t)q * A.max_sel;
   if (ok) {
-    int ntake = 0;
-    for (int k0 = 0; k0 < kmax; ++k0) ntake += __popcll(__ballot(k0 < mylen && le[k0 * NSUB + lane] > 0));
-    int np = 1;
-    while (np < ntake) np <<= 1;
-    for (int i = ntake + lane; i < np; i += 64) em[i] = LLONG_MAX;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (ntake > 1) wave_bitonic(em, np);
-    int32_t* row = A.idx + (int64_t)q * A.max_sel;
-    int out_total = 0;
-    for (int base = 0; base < ntake; base += 64) {
-      const int j = base + lane;
-      int take = 0, ks = 0;
-      if (j < ntake) {
-        const int i = (int)(em[j] & 0xffffffffll);
-        take = le[i];
-        ks = ls[i];
-      }
-      int tot;
-      const int off = out_total + wave_excl_scan(take, &tot);
-      const int nround = min(64, ntake - base);
-      if (tot >= 16 * nround) {
-        for (int jj = 0; jj < nround; ++jj) {
-          const int tj = __shfl(take, jj), kj = __shfl(ks, jj), oj = __shfl(off, jj);
-          for (int k = lane; k < tj; k += 64) {
-            const int sl = kj + k;
-            row[oj + k] = V.bmem[sl / p] * p + sl % p;
-          }
-        }
-      } else {
-        for (int k = 0; k < take;) {
-          const int sl = ks + k;
-          const int r0 = sl % p;
-          const int g = V.bmem[sl / p];
-          const int nh = min(p - r0, take - k);
-          for (int r = 0; r < nh; ++r) row[off + k + r] = g * p + r0 + r;
-          k += nh;
-        }
-      }
-      out_total += tot;
+    // taken buckets in ascending id order (padding sorts last)
+    long long v[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = tid * EPT + i < nt ? s_key[tid * EPT + i] : LLONG_MAX;
+    block_bitonic(v, s_key);
+    // output offsets: a block scan over the sorted order
+    int tk[EPT], ks[EPT], mine = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const bool in = tid * EPT + i < nt;
+      const int src = in ? (int)(v[i] & 0xffffffffll) : 0;
+      tk[i] = in ? s_tk[src] : 0;
+      ks[i] = in ? s_ks[src] : 0;
+      mine += tk[i];
     }
-    const int out = out_total;
-    const int wstart = max(0, t - A.window + 1);
-    const int ns = max(0, min(A.sinks, wstart));
-    const int nw = t - wstart + 1;
-    for (int k = lane; k < ns; k += 64) row[out + k] = k;
-    for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
-    const int totalk = out + ns + nw;
-    for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
-    if (lane == 0) A.cnt[q] = totalk;
+    int out_total;
+    int off = block_excl_scan<RT>(mine, s_ired, &out_total);   // barriers: the sort's reads of s_key are done
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (tid * EPT + i < nt) s_key[tid * EPT + i] = ((long long)off << 32) | (unsigned)ks[i];
+      off += tk[i];
+    }
+    __syncthreads();
+    // keys: one output slot per thread and round, all rounds' loads in flight
+    constexpr int NR = 16;
+    for (int o0 = tid; o0 < out_total; o0 += NR * RT) {
+      int sl[NR], g[NR];
+#pragma unroll
+      for (int jv = 0; jv < NR; ++jv) {
+        const int o = o0 + jv * RT;
+        sl[jv] = 0;
+        if (o < out_total) {
+          int a = 0, b = nt - 1;       // last taken bucket with offset <= o
+          while (a < b) {
+            const int m = (a + b + 1) >> 1;
+            if ((int)(s_key[m] >> 32) <= o) a = m; else b = m - 1;
+          }
+          const long long ev = s_key[a];
+          sl[jv] = (int)(ev & 0xffffffffll) + (o - (int)(ev >> 32));
+        }
+      }
+#pragma unroll
+      for (int jv = 0; jv < NR; ++jv) g[jv] = o0 + jv * RT < out_total ? V.bmem[sl[jv] / p] : 0;
+#pragma unroll
+      for (int jv = 0; jv < NR; ++jv)
+        if (o0 + jv * RT < out_total) row[o0 + jv * RT] = g[jv] * p + sl[jv] % p;
+    }
+    if (wave == 0) {
+      const int out = out_total;
+      const int wstart = max(0, t - A.window + 1);
+      const int ns = max(0, min(A.sinks, wstart));
+      const int nw = t - wstart + 1;
+      for (int k = lane; k < ns; k += 64) row[out + k] = k;
+      for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
+      const int totalk = out + ns + nw;
+      for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
+      if (lane == 0) A.cnt[q] = totalk;
+    }
   }
-  if (lane == 0) W.flags[q] = ok ? 0 : 1;
+  if (tid == 0) W.flags[q] = ok ? 0 : 1;
 }
 
 constexpr int kPrefW = 4, kPrefQ = 64;     // prefill scan: 4 waves, 64 query slots
@@ -602,8 +665,7 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
                      0, s, vs, a, W);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_resolve, dim3((unsigned)((slots + RW - 1) / RW)), dim3(RW * 64), 0, s, vs, a,
-                     W, (int32_t)slots);
+  hipLaunchKernelGGL(k_resolve, dim3((unsigned)slots), dim3(RT), 0, s, vs, a, W);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // exact refinement for the (rare) flagged queries; other workgroups exit at once
