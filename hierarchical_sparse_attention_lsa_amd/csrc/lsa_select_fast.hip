@@ -330,17 +330,21 @@ constexpr int EPT = ECAP2 / RT;     // sorted taken buckets per thread
 // Ascending bitonic sort of the block's ECAP2 values, EPT consecutive ones per
 // thread (element tid*EPT + i in v[i]): partners in the same thread swap in
 // registers, in the same wave through shuffles, across waves through `tmp`.
-__device__ __forceinline__ void block_bitonic(long long (&v)[EPT], long long* tmp) {
+__device__ __forceinline__ int shfl_xor_t(int v, int m) { return __shfl_xor(v, m); }
+__device__ __forceinline__ long long shfl_xor_t(long long v, int m) { return shfl_xor_i64(v, m); }
+
+template <class T>
+__device__ __forceinline__ void block_bitonic(T (&v)[EPT], T* tmp) {
   const int tid = threadIdx.x;
   for (int k = 2; k <= ECAP2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      long long pv[EPT];
+      T pv[EPT];
       if (j < EPT) {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) pv[i] = v[i ^ j];
       } else if (j < EPT * 64) {
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) pv[i] = shfl_xor_i64(v[i], j / EPT);
+        for (int i = 0; i < EPT; ++i) pv[i] = shfl_xor_t(v[i], j / EPT);
       } else {
         __syncthreads();
 #pragma unroll
@@ -353,7 +357,7 @@ __device__ __forceinline__ void block_bitonic(long long (&v)[EPT], long long* tm
       for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
         const bool up = (e & k) == 0, lower = (e & j) == 0;
-        const long long mn = min(v[i], pv[i]), mx = max(v[i], pv[i]);
+        const T mn = min(v[i], pv[i]), mx = max(v[i], pv[i]);
         v[i] = (up == lower) ? mn : mx;
       }
     }
@@ -565,19 +569,34 @@ __global__ void __launch_bounds__(RT) k_resolve(FastViews VS, SelArgs A, ListWs 
 
   int32_t* row = A.idx + (int64_t)q * A.max_sel;
   if (ok) {
-    // taken buckets in ascending id order (padding sorts last)
-    long long v[EPT];
+    // taken buckets in ascending id order (padding sorts last); entry r of
+    // s_key is (id << 32 | r).  Ids below 2^21 sort as 32-bit (id << 10 | r).
+    int src[EPT];
+    if (V.n_bkt < (1 << 21)) {
+      int v[EPT];
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) v[i] = tid * EPT + i < nt ? s_key[tid * EPT + i] : LLONG_MAX;
-    block_bitonic(v, s_key);
+      for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        v[i] = e < nt ? (int)(((s_key[e] >> 32) << 10) | (s_key[e] & (ECAP2 - 1))) : INT_MAX;
+      }
+      block_bitonic(v, reinterpret_cast<int*>(s_key));
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) src[i] = v[i] & (ECAP2 - 1);
+    } else {
+      long long v[EPT];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) v[i] = tid * EPT + i < nt ? s_key[tid * EPT + i] : LLONG_MAX;
+      block_bitonic(v, s_key);
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) src[i] = (int)(v[i] & 0xffffffffll);
+    }
     // output offsets: a block scan over the sorted order
     int tk[EPT], ks[EPT], mine = 0;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const bool in = tid * EPT + i < nt;
-      const int src = in ? (int)(v[i] & 0xffffffffll) : 0;
-      tk[i] = in ? s_tk[src] : 0;
-      ks[i] = in ? s_ks[src] : 0;
+      tk[i] = in ? s_tk[src[i]] : 0;
+      ks[i] = in ? s_ks[src[i]] : 0;
       mine += tk[i];
     }
     int out_total;
@@ -588,29 +607,53 @@ __global__ void __launch_bounds__(RT) k_resolve(FastViews VS, SelArgs A, ListWs 
       off += tk[i];
     }
     __syncthreads();
-    // keys: one output slot per thread and round, all rounds' loads in flight
-    constexpr int NR = 16;
-    for (int o0 = tid; o0 < out_total; o0 += NR * RT) {
-      int sl[NR], g[NR];
+    // keys: thread tid writes output slots [tid*PO, tid*PO + PO), walking the
+    // taken buckets from one binary search; all its member loads in flight
+    constexpr int MAXPO = 16;          // budget <= 4096 = MAXPO * RT
+    const int PO = (((out_total + RT - 1) / RT) + 3) & ~3;
+    const int o0 = tid * PO;
+    if (o0 < out_total) {
+      int a = 0, b = nt - 1;           // last taken bucket with offset <= o0
+      while (a < b) {
+        const int m = (a + b + 1) >> 1;
+        if ((int)(s_key[m] >> 32) <= o0) a = m; else b = m - 1;
+      }
+      long long ev = s_key[a];
+      int nextoff = a + 1 < nt ? (int)(s_key[a + 1] >> 32) : INT_MAX;
+      int sl[MAXPO], g[MAXPO];
 #pragma unroll
-      for (int jv = 0; jv < NR; ++jv) {
-        const int o = o0 + jv * RT;
-        sl[jv] = 0;
-        if (o < out_total) {
-          int a = 0, b = nt - 1;       // last taken bucket with offset <= o
-          while (a < b) {
-            const int m = (a + b + 1) >> 1;
-            if ((int)(s_key[m] >> 32) <= o) a = m; else b = m - 1;
+      for (int jv = 0; jv < MAXPO; ++jv) {
+        const int o = o0 + jv;
+        sl[jv] = -1;
+        if (jv < PO && o < out_total) {
+          while (o >= nextoff) {
+            ++a;
+            ev = s_key[a];
+            nextoff = a + 1 < nt ? (int)(s_key[a + 1] >> 32) : INT_MAX;
           }
-          const long long ev = s_key[a];
           sl[jv] = (int)(ev & 0xffffffffll) + (o - (int)(ev >> 32));
         }
       }
 #pragma unroll
-      for (int jv = 0; jv < NR; ++jv) g[jv] = o0 + jv * RT < out_total ? V.bmem[sl[jv] / p] : 0;
+      for (int jv = 0; jv < MAXPO; ++jv) g[jv] = sl[jv] >= 0 ? V.bmem[sl[jv] / p] : 0;
 #pragma unroll
-      for (int jv = 0; jv < NR; ++jv)
-        if (o0 + jv * RT < out_total) row[o0 + jv * RT] = g[jv] * p + sl[jv] % p;
+      for (int jv = 0; jv < MAXPO; jv += 4) {
+        if (sl[jv] < 0) continue;
+        int4 w;
+        w.x = g[jv] * p + sl[jv] % p;
+        w.y = g[jv + 1] * p + sl[jv + 1] % p;
+        w.z = g[jv + 2] * p + sl[jv + 2] % p;
+        w.w = g[jv + 3] * p + sl[jv + 3] % p;
+        int32_t* dst = row + o0 + jv;
+        if (sl[jv + 3] >= 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          *reinterpret_cast<int4*>(dst) = w;
+        } else {
+          dst[0] = w.x;
+          if (sl[jv + 1] >= 0) dst[1] = w.y;
+          if (sl[jv + 2] >= 0) dst[2] = w.z;
+          if (sl[jv + 3] >= 0) dst[3] = w.w;
+        }
+      }
     }
     if (wave == 0) {
       const int out = out_total;
