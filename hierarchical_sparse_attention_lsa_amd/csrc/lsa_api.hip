@@ -138,6 +138,10 @@ IdxView view_of(const Index* h) {
     v.leafsup = h->at<int32_t>(h->off_leafsup);
     v.n_sup = (int32_t)(h->n_grp * h->prm.tree_super);
     v.scent = h->at<int8_t>(h->off_scent);
+    v.scnt = h->at<int32_t>(h->off_scnt);
+    v.soff = h->at<int32_t>(h->off_soff);
+    v.smem = h->at<int32_t>(h->off_smem);
+    v.covered = (int32_t)(h->n_grp * h->prm.tree_group * h->prm.buckets);
   }
   return v;
 }
@@ -226,6 +230,8 @@ int select_impl(const Index* h, const int8_t* latq, const int32_t* qpos, int32_t
   a.idx = idx; a.cnt = cnt; a.only = nullptr;
   if (!v.leafsup && nq >= kFastSelectMinQ && ws && ws_bytes >= select_fast_ws_bytes(nq)) {
     LSA_HIP(launch_select_fast(v, a, ws, s), "select");
+  } else if (v.leafsup && ws && ws_bytes >= select_tree_ws_bytes(nq)) {
+    LSA_HIP(launch_select_tree(v, a, ws, s), "select");
   } else {
     LSA_HIP(launch_select(v, a, nullptr, s), "select");
   }

@@ -49,6 +49,10 @@ struct IdxView {
   int32_t dense;          // 1: cent = raw latents, bucket j = key j (pool 1)
   int32_t n_sup;
   const int8_t* scent;    // [n_sup][64]
+  const int32_t* scnt;    // leaves per super cluster (Tree)
+  const int32_t* soff;    // first leaf slot in smem
+  const int32_t* smem;    // leaf ids grouped by super cluster
+  int32_t covered;        // leaves inside complete groups (n_grp * group * buckets)
 };
 
 struct SelArgs {
@@ -97,6 +101,9 @@ hipError_t launch_select(const IdxView& v, const SelArgs& a, void* ws, hipStream
 // large Flat batches: list-based single full pass (+ exact kernel for flagged queries)
 size_t select_fast_ws_bytes(int32_t nq);
 hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
+// Tree selection, one workgroup per query; workspace: select_tree_ws_bytes(nq)
+size_t select_tree_ws_bytes(int32_t nq);
+hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
 // decode: one query per sequence, each on its own index (max_bkt = bucket capacity)
 size_t select_dec_ws_bytes(int32_t nseq, int64_t max_bkt);
 hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t nseq,

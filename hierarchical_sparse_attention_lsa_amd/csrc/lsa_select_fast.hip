@@ -333,29 +333,30 @@ constexpr int EPT = ECAP2 / RT;     // sorted taken buckets per thread
 __device__ __forceinline__ int shfl_xor_t(int v, int m) { return __shfl_xor(v, m); }
 __device__ __forceinline__ long long shfl_xor_t(long long v, int m) { return shfl_xor_i64(v, m); }
 
-template <class T>
-__device__ __forceinline__ void block_bitonic(T (&v)[EPT], T* tmp) {
+template <int N, class T>
+__device__ __forceinline__ void block_bitonic(T (&v)[N / RT], T* tmp) {
+  constexpr int PT = N / RT;
   const int tid = threadIdx.x;
-  for (int k = 2; k <= ECAP2; k <<= 1) {
+  for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      T pv[EPT];
-      if (j < EPT) {
+      T pv[PT];
+      if (j < PT) {
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) pv[i] = v[i ^ j];
-      } else if (j < EPT * 64) {
+        for (int i = 0; i < PT; ++i) pv[i] = v[i ^ j];
+      } else if (j < PT * 64) {
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) pv[i] = shfl_xor_t(v[i], j / EPT);
+        for (int i = 0; i < PT; ++i) pv[i] = shfl_xor_t(v[i], j / PT);
       } else {
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) tmp[tid * EPT + i] = v[i];
+        for (int i = 0; i < PT; ++i) tmp[tid * PT + i] = v[i];
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) pv[i] = tmp[(tid * EPT + i) ^ j];
+        for (int i = 0; i < PT; ++i) pv[i] = tmp[(tid * PT + i) ^ j];
       }
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const int e = tid * EPT + i;
+      for (int i = 0; i < PT; ++i) {
+        const int e = tid * PT + i;
         const bool up = (e & k) == 0, lower = (e & j) == 0;
         const T mn = min(v[i], pv[i]), mx = max(v[i], pv[i]);
         v[i] = (up == lower) ? mn : mx;
@@ -364,16 +365,272 @@ __device__ __forceinline__ void block_bitonic(T (&v)[EPT], T* tmp) {
   }
 }
 
-__global__ void __launch_bounds__(RT) k_resolve(FastViews VS, SelArgs A, ListWs W) {
-  __shared__ int s_hk[RB], s_hb[RB];
-  __shared__ long long s_red[RT / 64];
-  __shared__ int s_ired[RT / 64];
-  __shared__ long long s_cq[RCAP];   // bracket: -order key, then sorted
-  __shared__ int s_ci[RCAP];         // bracket: collection index (payload of the sort)
-  __shared__ int s_ce[RCAP], s_cks[RCAP];
-  __shared__ long long s_key[ECAP2]; // taken: (bucket id << 32 | entry); sort scratch; (offset << 32 | first key slot)
-  __shared__ int s_tk[ECAP2], s_ks[ECAP2];
-  __shared__ int s_nc, s_nt, s_cut[2];
+// Shared tail of the list resolve and the Tree select: exact selection over
+// the entries a workgroup of RT threads holds in registers (order keys K,
+// eligible key counts e; entries with e <= 0 take no part), then the row.
+// Keys above `hi` are taken whole and the cutoff lies in [lo, hi] (the
+// block-wide min / max of the keys with e > 0); `tot` is this thread's sum of
+// e.  ksof(u) gives the first key slot of the thread's entry u.  `complete`:
+// the entries are all of the query's candidates, so fewer eligible keys than
+// the budget means every one is taken; otherwise the list must reach the
+// budget.  Returns false (nothing written) when the query must go to the
+// exact kernel.
+struct ResolveLds {
+  int hk[RB], hb[RB];
+  long long red[RT / 64];
+  int ired[RT / 64];
+  long long cq[RCAP];   // bracket: -order key, then sorted
+  int ci[RCAP];         // bracket: collection index (payload of the sort)
+  int ce[RCAP], cks[RCAP];
+  long long key[ECAP2]; // taken: (bucket id << 32 | entry); sort scratch; (offset << 32 | first key slot)
+  int tk[ECAP2], ks[ECAP2];
+  int nc, nt, cut[2];
+};
+
+template <int TPQ, class KsOf>
+__device__ __forceinline__ bool select_and_emit(ResolveLds& L, const IdxView& V, const SelArgs& A,
+                                                int q, int t, bool ok, const long long (&K)[TPQ],
+                                                const int (&e)[TPQ], long long lo, long long hi,
+                                                long long tot, bool complete, KsOf ksof) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int B = A.budget;
+  const int p = V.pool;
+  tot = block_sum_ll<RT>(tot, L.red);
+  lo = block_min_ll<RT>(lo, L.red);
+  hi = block_max_ll<RT>(hi, L.red);
+  bool all = false;
+  if (complete && tot <= B) {         // every eligible candidate is taken whole
+    all = true;
+    hi = LLONG_MIN;
+    lo = LLONG_MIN + 1;
+  }
+  ok = ok && (all || tot >= B);       // a list must hold the cutoff
+
+  // histogram refinement: keys above `hi` are taken whole, the cutoff is in [lo, hi]
+  if (ok && !all) {
+    for (int pass = 0; pass < 8; ++pass) {
+      const long long range = hi - lo + 1;
+      int sh = 0;
+      while (sh < 62 && ((range + (1ll << sh) - 1) >> sh) > RB) ++sh;
+      for (int i = tid; i < RB; i += RT) { L.hk[i] = 0; L.hb[i] = 0; }
+      __syncthreads();
+      long long ab = 0;
+#pragma unroll
+      for (int u = 0; u < TPQ; ++u) {
+        ab += (e[u] > 0 && K[u] > hi) ? e[u] : 0;
+        if (e[u] <= 0 || K[u] > hi || K[u] < lo) continue;
+        const int bin = (int)((hi - K[u]) >> sh);
+        atomicAdd(&L.hk[bin], e[u]);
+        atomicAdd(&L.hb[bin], 1);
+      }
+      ab = block_sum_ll<RT>(ab, L.red);
+      if (wave == 0) {
+        int h[RB / 64], c[RB / 64], loc = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) { h[k] = L.hk[(RB / 64) * lane + k]; c[k] = L.hb[(RB / 64) * lane + k]; loc += h[k]; }
+        int wt;
+        const int ex = wave_excl_scan(loc, &wt);
+        long long cum = ab + ex;
+        int found = -1, fb = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) {
+          if (found < 0 && cum + h[k] >= B) { found = (RB / 64) * lane + k; fb = c[k]; }
+          cum += h[k];
+        }
+        const unsigned long long mk = __ballot(found >= 0);
+        const int src = mk ? __ffsll((long long)mk) - 1 : 0;
+        const int bsel = __shfl(found, src), nbsel = __shfl(fb, src);
+        if (lane == 0) { L.cut[0] = mk ? bsel : -1; L.cut[1] = mk ? nbsel : 0; }
+      }
+      __syncthreads();
+      const int bin = L.cut[0], nb = L.cut[1];
+      if (bin < 0) { ok = false; break; }   // not reached: the bracket holds the cutoff
+      const long long nhi = hi - ((long long)bin << sh);
+      long long nlo = hi - ((long long)(bin + 1) << sh) + 1;
+      if (nlo < lo) nlo = lo;
+      lo = nlo; hi = nhi;
+      __syncthreads();
+      if (nb <= RCAP) break;
+    }
+  }
+
+  // taken entries: above the bracket whole (straight into the taken list);
+  // bracket entries collected for the ordered walk
+    if (ok) {
+#pragma unroll
+    for (int u = 0; u < TPQ; ++u) {
+      if (e[u] <= 0 || K[u] < lo) continue;
+      const int beta = (int)(0xffffffffu - (unsigned)(K[u] & 0xffffffffll));
+      if (K[u] > hi) {
+        const int r = atomicAdd(&L.nt, 1);
+        if (r < ECAP2) {
+          L.key[r] = ((long long)beta << 32) | (unsigned)r;
+          L.tk[r] = e[u];
+          L.ks[r] = ksof(u);
+        }
+      } else {
+        const int c = atomicAdd(&L.nc, 1);
+        if (c < RCAP) { L.cq[c] = -K[u]; L.ci[c] = c; L.ce[c] = e[u]; L.cks[c] = ksof(u); }
+      }
+    }
+  }
+  long long full = 0;
+#pragma unroll
+  for (int u = 0; u < TPQ; ++u) full += (ok && e[u] > 0 && K[u] > hi) ? e[u] : 0;
+  full = block_sum_ll<RT>(full, L.red);
+  const int nc = L.nc;
+  ok = ok && nc <= RCAP;
+  if (ok && wave == 0 && nc > 0) {
+    int np = 1;
+    while (np < nc) np <<= 1;
+    for (int i = nc + lane; i < np; i += 64) { L.cq[i] = LLONG_MAX; L.ci[i] = -1; }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int k = 2; k <= np; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = lane; i < np; i += 64) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const long long x = L.cq[i], y = L.cq[ixj];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) { L.cq[i] = y; L.cq[ixj] = x; const int tmp = L.ci[i]; L.ci[i] = L.ci[ixj]; L.ci[ixj] = tmp; }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+    }
+    // walk in (score desc, id asc) order; the last bucket taken is cut
+    long long need = B - full;
+    for (int b0 = 0; b0 < nc; b0 += 64) {
+      const int i = b0 + lane;
+      int ee = 0, c = -1;
+      if (i < nc) { c = L.ci[i]; ee = L.ce[c]; }
+      int tot2;
+      const int before = wave_excl_scan(ee, &tot2);
+      const int tk = (int)max(0ll, min((long long)ee, need - before));
+      if (tk > 0) {
+        const int r = atomicAdd(&L.nt, 1);
+        if (r < ECAP2) {
+          const long long Kc = -L.cq[i];
+          const int beta = (int)(0xffffffffu - (unsigned)(Kc & 0xffffffffll));
+          L.key[r] = ((long long)beta << 32) | (unsigned)r;
+          L.tk[r] = tk;
+          L.ks[r] = L.cks[c];
+        }
+      }
+      need -= tot2;
+    }
+  }
+  __syncthreads();
+  const int nt = L.nt;
+  ok = ok && nt <= ECAP2;
+
+  int32_t* row = A.idx + (int64_t)q * A.max_sel;
+  if (ok) {
+    // taken buckets in ascending id order (padding sorts last); entry r of
+    // L.key is (id << 32 | r).  Ids below 2^21 sort as 32-bit (id << 10 | r).
+    int src[EPT];
+    if (V.n_bkt < (1 << 21)) {
+      int v[EPT];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        v[i] = e < nt ? (int)(((L.key[e] >> 32) << 10) | (L.key[e] & (ECAP2 - 1))) : INT_MAX;
+      }
+      block_bitonic<ECAP2>(v, reinterpret_cast<int*>(L.key));
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) src[i] = v[i] & (ECAP2 - 1);
+    } else {
+      long long v[EPT];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) v[i] = tid * EPT + i < nt ? L.key[tid * EPT + i] : LLONG_MAX;
+      block_bitonic<ECAP2>(v, L.key);
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) src[i] = (int)(v[i] & 0xffffffffll);
+    }
+    // output offsets: a block scan over the sorted order
+    int tk[EPT], ks[EPT], mine = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const bool in = tid * EPT + i < nt;
+      tk[i] = in ? L.tk[src[i]] : 0;
+      ks[i] = in ? L.ks[src[i]] : 0;
+      mine += tk[i];
+    }
+    int out_total;
+    int off = block_excl_scan<RT>(mine, L.ired, &out_total);   // barriers: the sort's reads of L.key are done
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (tid * EPT + i < nt) L.key[tid * EPT + i] = ((long long)off << 32) | (unsigned)ks[i];
+      off += tk[i];
+    }
+    __syncthreads();
+    // keys: thread tid writes output slots [tid*PO, tid*PO + PO), walking the
+    // taken buckets from one binary search; all its member loads in flight
+    constexpr int MAXPO = 16;          // budget <= 4096 = MAXPO * RT
+    const int PO = (((out_total + RT - 1) / RT) + 3) & ~3;
+    const int o0 = tid * PO;
+    if (o0 < out_total) {
+      int a = 0, b = nt - 1;           // last taken bucket with offset <= o0
+      while (a < b) {
+        const int m = (a + b + 1) >> 1;
+        if ((int)(L.key[m] >> 32) <= o0) a = m; else b = m - 1;
+      }
+      long long ev = L.key[a];
+      int nextoff = a + 1 < nt ? (int)(L.key[a + 1] >> 32) : INT_MAX;
+      int sl[MAXPO], g[MAXPO];
+#pragma unroll
+      for (int jv = 0; jv < MAXPO; ++jv) {
+        const int o = o0 + jv;
+        sl[jv] = -1;
+        if (jv < PO && o < out_total) {
+          while (o >= nextoff) {
+            ++a;
+            ev = L.key[a];
+            nextoff = a + 1 < nt ? (int)(L.key[a + 1] >> 32) : INT_MAX;
+          }
+          sl[jv] = (int)(ev & 0xffffffffll) + (o - (int)(ev >> 32));
+        }
+      }
+#pragma unroll
+      for (int jv = 0; jv < MAXPO; ++jv) g[jv] = sl[jv] >= 0 ? V.bmem[sl[jv] / p] : 0;
+#pragma unroll
+      for (int jv = 0; jv < MAXPO; jv += 4) {
+        if (sl[jv] < 0) continue;
+        int4 w;
+        w.x = g[jv] * p + sl[jv] % p;
+        w.y = g[jv + 1] * p + sl[jv + 1] % p;
+        w.z = g[jv + 2] * p + sl[jv + 2] % p;
+        w.w = g[jv + 3] * p + sl[jv + 3] % p;
+        int32_t* dst = row + o0 + jv;
+        if (sl[jv + 3] >= 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          *reinterpret_cast<int4*>(dst) = w;
+        } else {
+          dst[0] = w.x;
+          if (sl[jv + 1] >= 0) dst[1] = w.y;
+          if (sl[jv + 2] >= 0) dst[2] = w.z;
+          if (sl[jv + 3] >= 0) dst[3] = w.w;
+        }
+      }
+    }
+    if (wave == 0) {
+      const int out = out_total;
+      const int wstart = max(0, t - A.window + 1);
+      const int ns = max(0, min(A.sinks, wstart));
+      const int nw = t - wstart + 1;
+      for (int k = lane; k < ns; k += 64) row[out + k] = k;
+      for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
+      const int totalk = out + ns + nw;
+      for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
+      if (lane == 0) A.cnt[q] = totalk;
+    }
+  }
+  return ok;
+}
+
+__global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, ListWs W) {
+  __shared__ ResolveLds L;
   __shared__ int s_pre[NSUB + 1];    // entries before sub-list j
   const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -393,7 +650,7 @@ __global__ void __launch_bounds__(RT) k_resolve(FastViews VS, SelArgs A, ListWs 
     s_pre[lane] = ex;
     if (lane == 63) s_pre[NSUB] = all;
   }
-  if (tid == 0) { s_nc = 0; s_nt = 0; }
+  if (tid == 0) { L.nc = 0; L.nt = 0; }
   // a sub-list that overflowed, or more entries than the registers hold: exact kernel
   bool ok = __syncthreads_or(len > SUBCAP) == 0;
   const int ntot = s_pre[NSUB];
@@ -440,234 +697,150 @@ __global__ void __launch_bounds__(RT) k_resolve(FastViews VS, SelArgs A, ListWs 
       tot += in ? e[u] : 0;
     }
   }
-  tot = block_sum_ll<RT>(tot, s_red);
-  lo = block_min_ll<RT>(lo, s_red);
-  hi = block_max_ll<RT>(hi, s_red);
-  ok = ok && tot >= B;               // the list must hold the cutoff
+  ok = select_and_emit<TPQ>(L, V, A, q, t, ok, K, e, lo, hi, tot, false,
+                           [&](int u) { return W.kstart[slot * LC + tid + RT * u]; });
+  if (tid == 0) W.flags[q] = ok ? 0 : 1;
+}
 
-  // histogram refinement: keys above `hi` are taken whole, the cutoff is in [lo, hi]
-  if (ok) {
-    for (int pass = 0; pass < 8; ++pass) {
-      const long long range = hi - lo + 1;
-      int sh = 0;
-      while (sh < 62 && ((range + (1ll << sh) - 1) >> sh) > RB) ++sh;
-      for (int i = tid; i < RB; i += RT) { s_hk[i] = 0; s_hb[i] = 0; }
-      __syncthreads();
-      long long ab = 0;
+// Tree selection ("Prefrontal's Latent Sparse Attention speeds up one
+// attention layer 72x at 10M tokens", section "What it changes": clusters
+// grouped into a hierarchy that a query walks down).  One 256-thread
+// workgroup per query: score every super cluster (v_dot4), keep the
+// tree_top best by (score desc, id asc) with a bitonic sort, enumerate their
+// leaves plus the leaves outside complete groups, score those, and finish
+// with the same exact selection and row emission as the list resolve.  A
+// query with more supers or candidates than the registers hold is flagged
+// for the exact kernel.
+constexpr int SUPN = 2048;          // supers sorted per query (n_sup <= SUPN)
+constexpr int CPT = 8;              // candidate leaves per thread
+constexpr int TOPCAP = 256;         // tree_top served here
+
+__device__ __forceinline__ int dot64(const int (&qv)[16], const int8_t* c) {
+  const int4* c4 = reinterpret_cast<const int4*>(c);
+  int acc = 0;
 #pragma unroll
-      for (int u = 0; u < TPQ; ++u) {
-        ab += (e[u] > 0 && K[u] > hi) ? e[u] : 0;
-        if (e[u] <= 0 || K[u] > hi || K[u] < lo) continue;
-        const int bin = (int)((hi - K[u]) >> sh);
-        atomicAdd(&s_hk[bin], e[u]);
-        atomicAdd(&s_hb[bin], 1);
-      }
-      ab = block_sum_ll<RT>(ab, s_red);
-      if (wave == 0) {
-        int h[RB / 64], c[RB / 64], loc = 0;
+  for (int k = 0; k < 4; ++k) {
+    const int4 x = c4[k];
+    acc = __builtin_amdgcn_sdot4(qv[4 * k + 0], x.x, acc, false);
+    acc = __builtin_amdgcn_sdot4(qv[4 * k + 1], x.y, acc, false);
+    acc = __builtin_amdgcn_sdot4(qv[4 * k + 2], x.z, acc, false);
+    acc = __builtin_amdgcn_sdot4(qv[4 * k + 3], x.w, acc, false);
+  }
+  return acc;
+}
+
+template <int NS>
+__device__ __forceinline__ void top_supers(const IdxView& V, const int (&qv)[16], int R,
+                                           long long* tmp, int* s_sup) {
+  constexpr int PT = NS / RT;
+  const int tid = threadIdx.x;
+  // ascending sort of -order key = (score desc, id asc)
+  long long v[PT];
 #pragma unroll
-        for (int k = 0; k < RB / 64; ++k) { h[k] = s_hk[(RB / 64) * lane + k]; c[k] = s_hb[(RB / 64) * lane + k]; loc += h[k]; }
-        int wt;
-        const int ex = wave_excl_scan(loc, &wt);
-        long long cum = ab + ex;
-        int found = -1, fb = 0;
+  for (int i = 0; i < PT; ++i) {
+    const int s = tid * PT + i;
+    v[i] = s < V.n_sup ? -order_key(dot64(qv, V.scent + (int64_t)s * kDim), s) : LLONG_MAX;
+  }
+  block_bitonic<NS>(v, tmp);
 #pragma unroll
-        for (int k = 0; k < RB / 64; ++k) {
-          if (found < 0 && cum + h[k] >= B) { found = (RB / 64) * lane + k; fb = c[k]; }
-          cum += h[k];
-        }
-        const unsigned long long mk = __ballot(found >= 0);
-        const int src = mk ? __ffsll((long long)mk) - 1 : 0;
-        const int bsel = __shfl(found, src), nbsel = __shfl(fb, src);
-        if (lane == 0) { s_cut[0] = mk ? bsel : -1; s_cut[1] = mk ? nbsel : 0; }
-      }
-      __syncthreads();
-      const int bin = s_cut[0], nb = s_cut[1];
-      if (bin < 0) { ok = false; break; }   // not reached: the bracket holds the cutoff
-      const long long nhi = hi - ((long long)bin << sh);
-      long long nlo = hi - ((long long)(bin + 1) << sh) + 1;
-      if (nlo < lo) nlo = lo;
-      lo = nlo; hi = nhi;
-      __syncthreads();
-      if (nb <= RCAP) break;
+  for (int i = 0; i < PT; ++i) {
+    const int r = tid * PT + i;
+    if (r < R) s_sup[r] = (int)(0xffffffffu - (unsigned)((-v[i]) & 0xffffffffll));
+  }
+}
+
+__global__ void __launch_bounds__(RT, 4) k_tree_select(IdxView V, SelArgs A, int32_t* flags) {
+  __shared__ ResolveLds L;
+  __shared__ long long s_tmp[SUPN];
+  __shared__ int s_sup[TOPCAP];       // selected supers
+  __shared__ int s_pre[TOPCAP + 1];   // candidates before selected super j
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int q = blockIdx.x;
+  const int t = max(0, A.qpos ? A.qpos[q] : A.qpos_base + q);
+  const int R = min(A.tree_top, V.n_sup);
+  const int n_unc = V.n_bkt - V.covered;
+  bool ok = A.budget > 0 && R >= 1 && R <= TOPCAP && V.n_sup <= SUPN;
+  if (tid == 0) { L.nc = 0; L.nt = 0; }
+  int qv[16];
+  {
+    const int4* q4 = reinterpret_cast<const int4*>(A.latq + (int64_t)q * kDim);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int4 x = q4[k];
+      qv[4 * k] = x.x; qv[4 * k + 1] = x.y; qv[4 * k + 2] = x.z; qv[4 * k + 3] = x.w;
     }
   }
-
-  // taken entries: above the bracket whole (straight into the taken list);
-  // bracket entries collected for the ordered walk
-  const int64_t lbase = slot * LC;
   if (ok) {
+    if (V.n_sup <= 1024) top_supers<1024>(V, qv, R, s_tmp, s_sup);
+    else top_supers<SUPN>(V, qv, R, s_tmp, s_sup);
+    __syncthreads();
+    if (wave == 0) {                  // leaves of the selected supers, prefix over them
+      int c[TOPCAP / 64], loc = 0;
 #pragma unroll
-    for (int u = 0; u < TPQ; ++u) {
-      if (e[u] <= 0 || K[u] < lo) continue;
-      const int i = tid + RT * u;
-      const int beta = (int)(0xffffffffu - (unsigned)(K[u] & 0xffffffffll));
-      if (K[u] > hi) {
-        const int r = atomicAdd(&s_nt, 1);
-        if (r < ECAP2) {
-          s_key[r] = ((long long)beta << 32) | (unsigned)r;
-          s_tk[r] = e[u];
-          s_ks[r] = W.kstart[lbase + i];
-        }
-      } else {
-        const int c = atomicAdd(&s_nc, 1);
-        if (c < RCAP) { s_cq[c] = -K[u]; s_ci[c] = c; s_ce[c] = e[u]; s_cks[c] = W.kstart[lbase + i]; }
+      for (int k = 0; k < TOPCAP / 64; ++k) {
+        const int j = (TOPCAP / 64) * lane + k;
+        c[k] = j < R ? V.scnt[s_sup[j]] : 0;
+        loc += c[k];
       }
-    }
-  }
-  long long full = 0;
+      int all;
+      int ex = wave_excl_scan(loc, &all);
 #pragma unroll
-  for (int u = 0; u < TPQ; ++u) full += (ok && e[u] > 0 && K[u] > hi) ? e[u] : 0;
-  full = block_sum_ll<RT>(full, s_red);
-  const int nc = s_nc;
-  ok = ok && nc <= RCAP;
-  if (ok && wave == 0 && nc > 0) {
-    int np = 1;
-    while (np < nc) np <<= 1;
-    for (int i = nc + lane; i < np; i += 64) { s_cq[i] = LLONG_MAX; s_ci[i] = -1; }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    for (int k = 2; k <= np; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = lane; i < np; i += 64) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const long long x = s_cq[i], y = s_cq[ixj];
-            const bool up = (i & k) == 0;
-            if ((x > y) == up) { s_cq[i] = y; s_cq[ixj] = x; const int tmp = s_ci[i]; s_ci[i] = s_ci[ixj]; s_ci[ixj] = tmp; }
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      for (int k = 0; k < TOPCAP / 64; ++k) {
+        s_pre[(TOPCAP / 64) * lane + k] = ex;
+        ex += c[k];
       }
-    }
-    // walk in (score desc, id asc) order; the last bucket taken is cut
-    long long need = B - full;
-    for (int b0 = 0; b0 < nc; b0 += 64) {
-      const int i = b0 + lane;
-      int ee = 0, c = -1;
-      if (i < nc) { c = s_ci[i]; ee = s_ce[c]; }
-      int tot2;
-      const int before = wave_excl_scan(ee, &tot2);
-      const int tk = (int)max(0ll, min((long long)ee, need - before));
-      if (tk > 0) {
-        const int r = atomicAdd(&s_nt, 1);
-        if (r < ECAP2) {
-          const long long Kc = -s_cq[i];
-          const int beta = (int)(0xffffffffu - (unsigned)(Kc & 0xffffffffll));
-          s_key[r] = ((long long)beta << 32) | (unsigned)r;
-          s_tk[r] = tk;
-          s_ks[r] = s_cks[c];
-        }
-      }
-      need -= tot2;
-    }
-  }
-  __syncthreads();
-  const int nt = s_nt;
-  ok = ok && nt <= ECAP2;
-
-  int32_t* row = A.idx + (int64_t)q * A.max_sel;
-  if (ok) {
-    // taken buckets in ascending id order (padding sorts last); entry r of
-    // s_key is (id << 32 | r).  Ids below 2^21 sort as 32-bit (id << 10 | r).
-    int src[EPT];
-    if (V.n_bkt < (1 << 21)) {
-      int v[EPT];
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        const int e = tid * EPT + i;
-        v[i] = e < nt ? (int)(((s_key[e] >> 32) << 10) | (s_key[e] & (ECAP2 - 1))) : INT_MAX;
-      }
-      block_bitonic(v, reinterpret_cast<int*>(s_key));
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) src[i] = v[i] & (ECAP2 - 1);
-    } else {
-      long long v[EPT];
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) v[i] = tid * EPT + i < nt ? s_key[tid * EPT + i] : LLONG_MAX;
-      block_bitonic(v, s_key);
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) src[i] = (int)(v[i] & 0xffffffffll);
-    }
-    // output offsets: a block scan over the sorted order
-    int tk[EPT], ks[EPT], mine = 0;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      const bool in = tid * EPT + i < nt;
-      tk[i] = in ? s_tk[src[i]] : 0;
-      ks[i] = in ? s_ks[src[i]] : 0;
-      mine += tk[i];
-    }
-    int out_total;
-    int off = block_excl_scan<RT>(mine, s_ired, &out_total);   // barriers: the sort's reads of s_key are done
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      if (tid * EPT + i < nt) s_key[tid * EPT + i] = ((long long)off << 32) | (unsigned)ks[i];
-      off += tk[i];
+      if (lane == 0) s_pre[TOPCAP] = all;
     }
     __syncthreads();
-    // keys: thread tid writes output slots [tid*PO, tid*PO + PO), walking the
-    // taken buckets from one binary search; all its member loads in flight
-    constexpr int MAXPO = 16;          // budget <= 4096 = MAXPO * RT
-    const int PO = (((out_total + RT - 1) / RT) + 3) & ~3;
-    const int o0 = tid * PO;
-    if (o0 < out_total) {
-      int a = 0, b = nt - 1;           // last taken bucket with offset <= o0
-      while (a < b) {
-        const int m = (a + b + 1) >> 1;
-        if ((int)(s_key[m] >> 32) <= o0) a = m; else b = m - 1;
-      }
-      long long ev = s_key[a];
-      int nextoff = a + 1 < nt ? (int)(s_key[a + 1] >> 32) : INT_MAX;
-      int sl[MAXPO], g[MAXPO];
+  }
+  const int nsel = ok ? s_pre[TOPCAP] : 0;
+  const int ncand = nsel + n_unc;
+  ok = ok && ncand <= CPT * RT;
+
+  long long K[CPT];
+  int e[CPT], ks[CPT];
+  long long lo = LLONG_MAX, hi = LLONG_MIN, tot = 0;
 #pragma unroll
-      for (int jv = 0; jv < MAXPO; ++jv) {
-        const int o = o0 + jv;
-        sl[jv] = -1;
-        if (jv < PO && o < out_total) {
-          while (o >= nextoff) {
-            ++a;
-            ev = s_key[a];
-            nextoff = a + 1 < nt ? (int)(s_key[a + 1] >> 32) : INT_MAX;
-          }
-          sl[jv] = (int)(ev & 0xffffffffll) + (o - (int)(ev >> 32));
+  for (int u = 0; u < CPT; ++u) { K[u] = LLONG_MIN; e[u] = 0; ks[u] = 0; }
+  if (ok) {
+    int leaf[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int f = tid + RT * u;
+      leaf[u] = -1;
+      if (f < nsel) {
+        int a = 0, b = R - 1;         // last selected super starting at or before f
+        while (a < b) {
+          const int m = (a + b + 1) >> 1;
+          if (s_pre[m] <= f) a = m; else b = m - 1;
         }
-      }
-#pragma unroll
-      for (int jv = 0; jv < MAXPO; ++jv) g[jv] = sl[jv] >= 0 ? V.bmem[sl[jv] / p] : 0;
-#pragma unroll
-      for (int jv = 0; jv < MAXPO; jv += 4) {
-        if (sl[jv] < 0) continue;
-        int4 w;
-        w.x = g[jv] * p + sl[jv] % p;
-        w.y = g[jv + 1] * p + sl[jv + 1] % p;
-        w.z = g[jv + 2] * p + sl[jv + 2] % p;
-        w.w = g[jv + 3] * p + sl[jv + 3] % p;
-        int32_t* dst = row + o0 + jv;
-        if (sl[jv + 3] >= 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-          *reinterpret_cast<int4*>(dst) = w;
-        } else {
-          dst[0] = w.x;
-          if (sl[jv + 1] >= 0) dst[1] = w.y;
-          if (sl[jv + 2] >= 0) dst[2] = w.z;
-          if (sl[jv + 3] >= 0) dst[3] = w.w;
-        }
+        leaf[u] = V.smem[V.soff[s_sup[a]] + (f - s_pre[a])];
+      } else if (f < ncand) {
+        leaf[u] = V.covered + (f - nsel);
       }
     }
-    if (wave == 0) {
-      const int out = out_total;
-      const int wstart = max(0, t - A.window + 1);
-      const int ns = max(0, min(A.sinks, wstart));
-      const int nw = t - wstart + 1;
-      for (int k = lane; k < ns; k += 64) row[out + k] = k;
-      for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
-      const int totalk = out + ns + nw;
-      for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
-      if (lane == 0) A.cnt[q] = totalk;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      if (leaf[u] >= 0) K[u] = order_key(dot64(qv, V.cent + (int64_t)leaf[u] * kDim), leaf[u]);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      if (leaf[u] < 0) continue;
+      const BucketInfo bi = load_bucket<false>(V, leaf[u]);
+      int klo;
+      e[u] = eligible<false>(V, leaf[u], bi, t, A.window, A.sinks, &klo);
+      ks[u] = bi.off * V.pool + klo;
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const bool in = e[u] > 0;
+      lo = min(lo, in ? K[u] : LLONG_MAX);
+      hi = max(hi, in ? K[u] : LLONG_MIN);
+      tot += in ? e[u] : 0;
     }
   }
-  if (tid == 0) W.flags[q] = ok ? 0 : 1;
+  ok = select_and_emit<CPT>(L, V, A, q, t, ok, K, e, lo, hi, tot, true,
+                            [&](int u) { return ks[u]; });
+  if (tid == 0) flags[q] = ok ? 0 : 1;
 }
 
 constexpr int kPrefW = 4, kPrefQ = 64;     // prefill scan: 4 waves, 64 query slots
@@ -714,6 +887,20 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
   // exact refinement for the (rare) flagged queries; other workgroups exit at once
   SelArgs b = a;
   b.only = W.flags;
+  return launch_select(v, b, nullptr, s);
+}
+
+size_t select_tree_ws_bytes(int32_t nq) { return ((size_t)nq * sizeof(int32_t) + 255) / 256 * 256; }
+
+hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  int32_t* flags = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)a.nq), dim3(RT), 0, s, v, a, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // exact refinement for the flagged queries; other workgroups exit at once
+  SelArgs b = a;
+  b.only = flags;
   return launch_select(v, b, nullptr, s);
 }
 
