@@ -235,7 +235,7 @@ def bench_decode(args, dev):
             "ms_per_step": dt * 1e3 / steps, "tokens_per_s": wl.nseq * steps / dt}
 
 
-def cpu_baseline(res, workers_pool, n_sample=192):
+def cpu_baseline(res, workers_pool, n_sample=512):
     """The oracle, timed on host cores on a bounded sample of the same workload."""
     import oracle as O
     from oracle.parallel_build import build_cache_parallel
