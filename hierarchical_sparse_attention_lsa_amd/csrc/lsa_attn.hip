@@ -51,7 +51,7 @@ struct AttnArgs {
   int32_t splits;
   float scale_log2;          // softmax scale * log2(e)
   void* out;
-  float* part_o;             // [items][16][D] unnormalised partial outputs (split mode)
+  float* part_o;             // [items][G][D] unnormalised partial outputs (split mode)
   float* part_ml;            // [items][16][2] running max (log2 domain) and sum
   // window-sharing mode: queries are positions qpos0 .. qpos0+nq-1 and their
   // rows end with the sinks and window of the select rule
@@ -65,15 +65,44 @@ __device__ __forceinline__ int xcd_remap(int b, int nwg) {
   return x * per + min(x, rem) + k;
 }
 
-// One 16-key tile of the online-softmax attention of a wave.  Lane l loads
-// K row `r` for key slot l % 16 (every lane of that slot passes the same r);
-// bit v of `vmask` says whether S^T[4*(l/16)+v][l%16] (key 4*(l/16)+v of the
-// tile, column l%16) takes part.  o / m_run / l_run: the column's state.
+// One 16-key tile of the online-softmax attention of a wave, in two halves so
+// that a caller can keep the next tile's loads in flight: tile_load fetches
+// K rows into the A operand and V rows into registers; tile_compute does the
+// QK^T MFMAs, the online softmax and the PV MFMAs.  Lane l loads K row `r`
+// for key slot l % 16 (every lane of that slot passes the same r); bit v of
+// `vmask` says whether S^T[4*(l/16)+v][l%16] (key 4*(l/16)+v of the tile,
+// column l%16) takes part.  o / m_run / l_run: the column's state.
 template <int D>
-__device__ __forceinline__ void attn_tile(const v8bf (&qb)[D / 32], const uint16_t* kbase,
-                                          const uint16_t* vbase, int64_t rowstride, int r,
-                                          unsigned vmask, float scale_log2, char* vl,
-                                          v4f (&o)[D / 16], float& m_run, float& l_run) {
+struct TileRegs {
+  v8bf ka[D / 32];
+  v4i vr[KT * (D / 8) / 64];
+};
+
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D>& T, const uint16_t* kbase, const uint16_t* vbase,
+                                          int64_t rowstride, int r) {
+  constexpr int NKK = D / 32;
+  constexpr int VCH = D / 8;
+  constexpr int VLD = KT * VCH / 64;
+  const int lane = lane_id();
+  const int grp = lane >> 4;
+  const uint16_t* kp = kbase + (int64_t)r * rowstride + 8 * grp;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    T.ka[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * kk));
+#pragma unroll
+  for (int i = 0; i < VLD; ++i) {
+    const int c = i * 64 + lane;
+    const int key = c / VCH, ch = c % VCH;
+    const int rv = __shfl(r, key);
+    T.vr[i] = *reinterpret_cast<const v4i*>(vbase + (int64_t)rv * rowstride + ch * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_compute(const v8bf (&qb)[D / 32], const TileRegs<D>& T,
+                                             unsigned vmask, float scale_log2, char* vl,
+                                             v4f (&o)[D / 16], float& m_run, float& l_run) {
   constexpr int NKK = D / 32;
   constexpr int NB = D / 16;
   constexpr int VROW = D * 2 + 16;
@@ -83,34 +112,16 @@ __device__ __forceinline__ void attn_tile(const v8bf (&qb)[D / 32], const uint16
   const int hl = lane & 15;
   const int grp = lane >> 4;
 
-  // K rows -> A operand
-  v8bf ka[NKK];
-  {
-    const uint16_t* kp = kbase + (int64_t)r * rowstride + 8 * grp;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      ka[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kp + 32 * kk));
-  }
-  // V rows -> LDS (row key, 16-byte chunk c)
-  v4i vr[VLD];
-#pragma unroll
-  for (int i = 0; i < VLD; ++i) {
-    const int c = i * 64 + lane;
-    const int key = c / VCH, ch = c % VCH;
-    const int rv = __shfl(r, key);
-    vr[i] = *reinterpret_cast<const v4i*>(vbase + (int64_t)rv * rowstride + ch * 8);
-  }
-
   // S^T[key][column]
   v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_16x16x32(ka[kk], qb[kk], s);
+  for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_16x16x32(T.ka[kk], qb[kk], s);
 
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
     const int c = i * 64 + lane;
     const int key = c / VCH, ch = c % VCH;
-    *reinterpret_cast<v4i*>(vl + key * VROW + ch * 16) = vr[i];
+    *reinterpret_cast<v4i*>(vl + key * VROW + ch * 16) = T.vr[i];
   }
 
   // online softmax for column hl over keys 4*grp + v
@@ -169,7 +180,17 @@ __device__ __forceinline__ void attn_tile(const v8bf (&qb)[D / 32], const uint16
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, bool OUT_F32, bool SPLIT>
+template <int D>
+__device__ __forceinline__ void attn_tile(const v8bf (&qb)[D / 32], const uint16_t* kbase,
+                                          const uint16_t* vbase, int64_t rowstride, int r,
+                                          unsigned vmask, float scale_log2, char* vl,
+                                          v4f (&o)[D / 16], float& m_run, float& l_run) {
+  TileRegs<D> T;
+  tile_load<D>(T, kbase, vbase, rowstride, r);
+  tile_compute<D>(qb, T, vmask, scale_log2, vl, o, m_run, l_run);
+}
+
+template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
   constexpr int NKK = D / 32;         // 32-deep slices of the head dim
   constexpr int NB = D / 16;          // 16-wide output column blocks
@@ -180,23 +201,15 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
   const int wave = threadIdx.x >> 6;
   const int nwg = gridDim.x;
   const int item = xcd_remap(blockIdx.x, nwg) * AW + wave;
-  const int nitems = a.nq * a.Hkv * a.splits;
-  if (item >= nitems) return;
-  const int split = item % a.splits;
-  const int qg = item / a.splits;
-  const int q = qg / a.Hkv;
-  const int g = qg % a.Hkv;
+  if (item >= a.nq * a.Hkv) return;
+  const int q = item / a.Hkv;
+  const int g = item % a.Hkv;
   const int G = a.G;
   const int hl = lane & 15;           // head (S^T column) / key row for K loads
   const int grp = lane >> 4;
 
   const int cnt = min(a.cnt[q], a.max_sel);
-  int kbeg = 0, kend = cnt;
-  if (SPLIT) {
-    const int ch = ((cnt + a.splits - 1) / a.splits + KT - 1) / KT * KT;
-    kbeg = min(cnt, split * ch);
-    kend = min(cnt, kbeg + ch);
-  }
+  const int kbeg = 0, kend = cnt;
   const int64_t rowbase = (int64_t)(q / a.qdiv) * a.seq_stride_rows;
   const int64_t rowstride = (int64_t)a.Hkv * D;        // elements per K/V row
   const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
@@ -232,22 +245,6 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) vmask |= (kb + 4 * grp + v < kend ? 1u : 0u) << v;
     attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
-  }
-
-  if (SPLIT) {
-    float* po = a.part_o + (int64_t)item * G * D;     // [item][G][D]
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int h = 4 * grp + v;
-      if (h >= G) continue;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) po[h * D + 16 * nb + hl] = o[nb][v];
-    }
-    if (grp == 0) {
-      a.part_ml[(int64_t)item * 32 + 2 * hl] = m_run;
-      a.part_ml[(int64_t)item * 32 + 2 * hl + 1] = l_run;
-    }
-    return;
   }
 
 #pragma unroll
@@ -393,37 +390,165 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   }
 }
 
-// Combine split partial results: out[q][head][d]. The running maxima of the
-// splits are read first, then every split's weighted partial; the loads of
-// each loop are independent, so they are in flight together.
+// Decode: split-K attention.  A wave owns one split of one (sequence, KV
+// head), the workgroup's waves the KV heads of one (sequence, split); its row ids for up to MAXT tiles are fetched at once (entry e in
+// lane e % 64 of register e / 64) and the next tile's K/V loads are issued
+// before the current tile's MFMAs, so a split costs about one memory round
+// trip plus its tiles' compute.  The split's unnormalised result and its
+// (max, sum) per head go to the workspace for k_attn_merge.
+constexpr int MAXT = 16;
+constexpr bool kDecPipe = true;     // next tile's loads in flight during the current tile
+
+template <int D, bool PIPE>
+__global__ void __launch_bounds__(AT) k_attn_dec(AttnArgs a) {
+  constexpr int NKK = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int VROW = D * 2 + 16;
+  constexpr int NRID = MAXT * KT / 64;
+  __shared__ __attribute__((aligned(16))) char vlds[AW][KT * VROW];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int item = xcd_remap(blockIdx.x, gridDim.x) * AW + wave;
+  if (item >= a.nq * a.Hkv * a.splits) return;
+  // the 8 waves of a workgroup take the KV heads of one (query, split), so
+  // every 2 KiB K/V row is fetched by one workgroup at once
+  const int g = item % a.Hkv;
+  const int split = (item / a.Hkv) % a.splits;
+  const int q = item / (a.Hkv * a.splits);
+  const int64_t pitem = ((int64_t)q * a.Hkv + g) * a.splits + split;   // partial-result slot
+  const int G = a.G;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+
+  const int cnt = min(a.cnt[q], a.max_sel);
+  const int ch = ((cnt + a.splits - 1) / a.splits + KT - 1) / KT * KT;
+  const int kbeg = min(cnt, split * ch);
+  const int kend = min(cnt, kbeg + ch);
+  const int64_t rowbase = (int64_t)(q / a.qdiv) * a.seq_stride_rows;
+  const int64_t rowstride = (int64_t)a.Hkv * D;
+  const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
+  const int64_t rmax = a.kv_rows - 1;
+
+  int rid[NRID];
+#pragma unroll
+  for (int j = 0; j < NRID; ++j) {
+    const int slot = kbeg + lane + 64 * j;
+    const int r = slot < kend ? idxrow[slot] : 0;
+    rid[j] = (int)min((int64_t)max(r, 0), rmax);
+  }
+  auto row_of = [&](int i) -> int {   // this lane's key row of tile i
+    if (i < MAXT) {
+      const int j = i >> 2;
+      const int v = j == 0 ? rid[0] : j == 1 ? rid[1] : j == 2 ? rid[2] : rid[3];
+      return __shfl(v, (i & 3) * 16 + hl);
+    }
+    const int slot = kbeg + i * KT + hl;
+    const int r = slot < kend ? idxrow[slot] : 0;
+    return (int)min((int64_t)max(r, 0), rmax);
+  };
+  auto mask_of = [&](int i) -> unsigned {
+    unsigned m = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) m |= (kbeg + i * KT + 4 * grp + v < kend ? 1u : 0u) << v;
+    return m;
+  };
+
+  v8bf qb[NKK];
+  {
+    const bool hv = hl < G;
+    const uint16_t* qp = a.q + ((int64_t)q * a.Hq + (int64_t)g * G + (hv ? hl : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      v4i raw = hv ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
+      qb[kk] = __builtin_bit_cast(v8bf, raw);
+    }
+  }
+  v4f o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+  char* vl = vlds[wave];
+  const uint16_t* kbase = a.k + (rowbase * a.Hkv + g) * D;
+  const uint16_t* vbase = a.v + (rowbase * a.Hkv + g) * D;
+
+  const int ntl = (kend - kbeg + KT - 1) / KT;
+  if (PIPE) {
+    TileRegs<D> T0, T1;
+    if (ntl > 0) tile_load<D>(T0, kbase, vbase, rowstride, row_of(0));
+    int i = 0;
+    for (; i + 1 < ntl; i += 2) {
+      tile_load<D>(T1, kbase, vbase, rowstride, row_of(i + 1));
+      tile_compute<D>(qb, T0, mask_of(i), a.scale_log2, vl, o, m_run, l_run);
+      if (i + 2 < ntl) tile_load<D>(T0, kbase, vbase, rowstride, row_of(i + 2));
+      tile_compute<D>(qb, T1, mask_of(i + 1), a.scale_log2, vl, o, m_run, l_run);
+    }
+    if (i < ntl) tile_compute<D>(qb, T0, mask_of(i), a.scale_log2, vl, o, m_run, l_run);
+  } else {
+    for (int i = 0; i < ntl; ++i) {
+      TileRegs<D> T0;
+      tile_load<D>(T0, kbase, vbase, rowstride, row_of(i));
+      tile_compute<D>(qb, T0, mask_of(i), a.scale_log2, vl, o, m_run, l_run);
+    }
+  }
+
+  // this split's partial result: [slot][G][D] and (max, sum) per head
+  float* po = a.part_o + pitem * G * D;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int h = 4 * grp + v;
+    if (h >= G) continue;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) po[h * D + 16 * nb + hl] = o[nb][v];
+  }
+  if (grp == 0) {
+    a.part_ml[pitem * 32 + 2 * hl] = m_run;
+    a.part_ml[pitem * 32 + 2 * hl + 1] = l_run;
+  }
+}
+
+// Combine the splits of each (query, head): one wave per head row.  Lane s
+// holds split s's (max, sum), the wave reduces the common max and the
+// denominator, then every lane sums its D/64 output dims over the splits
+// with the weights broadcast from their lanes (loads in flight together).
 template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(D) k_attn_merge(AttnArgs a) {
-  const int qh = blockIdx.x;            // q * Hq + head
-  const int d = threadIdx.x;
-  const int q = qh / a.Hq, head = qh % a.Hq;
+__global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
+  const int lane = lane_id();
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // q * Hq + head
+  if (row >= a.nq * a.Hq) return;
+  const int q = row / a.Hq, head = row % a.Hq;
   const int g = head / a.G, h = head % a.G;
   const int64_t it0 = ((int64_t)q * a.Hkv + g) * a.splits;
-  const float* ml = a.part_ml + it0 * 32 + 2 * h;
-  float M = -INFINITY;
-#pragma unroll 16
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = ml[s * 32], ls = ml[s * 32 + 1];
-    M = ls > 0.f ? fmaxf(M, ms) : M;
+  const int S = a.splits;                                  // <= 64
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < S) {
+    ms = a.part_ml[(it0 + lane) * 32 + 2 * h];
+    ls = a.part_ml[(it0 + lane) * 32 + 2 * h + 1];
   }
-  const float* po = a.part_o + (it0 * a.G + h) * D + d;
-  float num = 0.f, den = 0.f;
+  float M = ls > 0.f ? ms : -INFINITY;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+  const float w = (ls > 0.f) ? exp2f(ms - M) : 0.f;
+  float den = ls * w;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+  const float* po = a.part_o + (it0 * a.G + h) * D + lane;
+  float num[D / 64];
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) num[c] = 0.f;
 #pragma unroll 16
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = ml[s * 32], ls = ml[s * 32 + 1];
-    const float os = po[(int64_t)s * a.G * D];
-    const float w = ls > 0.f ? exp2f(ms - M) : 0.f;
-    num += os * w;
-    den += ls * w;
+  for (int s2 = 0; s2 < S; ++s2) {
+    const float ws = __shfl(w, s2);
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) num[c] += po[(int64_t)s2 * a.G * D + 64 * c] * ws;
   }
-  const float val = den > 0.f ? num / den : 0.f;
-  const int64_t ob = (int64_t)qh * D + d;
-  if (OUT_F32) reinterpret_cast<float*>(a.out)[ob] = val;
-  else reinterpret_cast<uint16_t*>(a.out)[ob] = (uint16_t)f32_to_bf16_bits(val);
+  const int64_t ob = (int64_t)row * D + lane;
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) {
+    const float val = den > 0.f ? num[c] / den : 0.f;
+    if (OUT_F32) reinterpret_cast<float*>(a.out)[ob + 64 * c] = val;
+    else reinterpret_cast<uint16_t*>(a.out)[ob + 64 * c] = (uint16_t)f32_to_bf16_bits(val);
+  }
 }
 
 }  // namespace
@@ -440,6 +565,7 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        void* out, void* ws, int32_t splits, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   AttnArgs a;
+  memset(&a, 0, sizeof a);
   a.q = q; a.k = k; a.v = v; a.kv_rows = kv_rows; a.seq_stride_rows = seq_stride_rows;
   a.qdiv = qdiv > 0 ? qdiv : 1;
   a.idx = idx; a.cnt = cnt; a.max_sel = max_sel; a.nq = nq;
@@ -454,26 +580,27 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   const unsigned grid = (unsigned)((items + AW - 1) / AW);
   const bool f32 = ap.out_f32 != 0;
   if (a.splits > 1) {
-    if (ap.D == 128) hipLaunchKernelGGL((k_attn<128, false, true>), dim3(grid), dim3(AT), 0, s, a);
-    else hipLaunchKernelGGL((k_attn<64, false, true>), dim3(grid), dim3(AT), 0, s, a);
+    if (a.splits > 64) return hipErrorInvalidValue;
+    if (ap.D == 128) hipLaunchKernelGGL((k_attn_dec<128, kDecPipe>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_dec<64, kDecPipe>), dim3(grid), dim3(AT), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned mg = (unsigned)(nq * ap.Hq);
+    const unsigned mg = (unsigned)((nq * ap.Hq + 3) / 4);
     if (ap.D == 128) {
-      if (f32) hipLaunchKernelGGL((k_attn_merge<128, true>), dim3(mg), dim3(128), 0, s, a);
-      else hipLaunchKernelGGL((k_attn_merge<128, false>), dim3(mg), dim3(128), 0, s, a);
+      if (f32) hipLaunchKernelGGL((k_attn_merge<128, true>), dim3(mg), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_attn_merge<128, false>), dim3(mg), dim3(256), 0, s, a);
     } else {
-      if (f32) hipLaunchKernelGGL((k_attn_merge<64, true>), dim3(mg), dim3(64), 0, s, a);
-      else hipLaunchKernelGGL((k_attn_merge<64, false>), dim3(mg), dim3(64), 0, s, a);
+      if (f32) hipLaunchKernelGGL((k_attn_merge<64, true>), dim3(mg), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_attn_merge<64, false>), dim3(mg), dim3(256), 0, s, a);
     }
     return hipGetLastError();
   }
   if (ap.D == 128) {
-    if (f32) hipLaunchKernelGGL((k_attn<128, true, false>), dim3(grid), dim3(AT), 0, s, a);
-    else hipLaunchKernelGGL((k_attn<128, false, false>), dim3(grid), dim3(AT), 0, s, a);
+    if (f32) hipLaunchKernelGGL((k_attn<128, true>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<128, false>), dim3(grid), dim3(AT), 0, s, a);
   } else {
-    if (f32) hipLaunchKernelGGL((k_attn<64, true, false>), dim3(grid), dim3(AT), 0, s, a);
-    else hipLaunchKernelGGL((k_attn<64, false, false>), dim3(grid), dim3(AT), 0, s, a);
+    if (f32) hipLaunchKernelGGL((k_attn<64, true>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<64, false>), dim3(grid), dim3(AT), 0, s, a);
   }
   return hipGetLastError();
 }
