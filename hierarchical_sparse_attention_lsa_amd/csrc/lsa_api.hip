@@ -88,6 +88,15 @@ void layout(const lsa_index_params& p, Index* h) {
   h->off_smem = o;   o = align_up(o + h->max_smem * 4);
   h->off_leafsup = o; o = align_up(o + (p.tree_group > 0 ? h->max_bkt * 4 : 0));
   h->off_pend = o;   o = align_up(o + 2 * (int64_t)p.pool * kDim);
+  {
+    size_t km = kmeans_scratch_bytes(p.block, p.buckets);
+    if (p.tree_group > 0) {
+      const size_t kt = kmeans_scratch_bytes(p.tree_group * p.buckets, p.tree_super);
+      km = km > kt ? km : kt;
+    }
+    h->kmws_bytes = (int64_t)km;
+  }
+  h->off_kmws = o;   o = align_up(o + h->kmws_bytes);
   h->used_bytes = o;
 }
 
@@ -188,7 +197,8 @@ int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
     LSA_HIP(launch_kmeans(pooled + nf_old * N * kDim, N, C, P.iters, (int32_t)(nf_new - nf_old),
                           nf_old * N, cent + nf_old * C * kDim, bcnt + nf_old * C,
                           boff + nf_old * C, bmem + nf_old * N, bfirst + nf_old * C,
-                          blast + nf_old * C, nullptr, 0, s),
+                          blast + nf_old * C, nullptr, 0, h->at<char>(h->off_kmws),
+                          (size_t)h->kmws_bytes, s),
             "kmeans");
   }
   const int64_t t0 = nf_new == nf_old ? g0 : nf_new * N;
@@ -205,7 +215,8 @@ int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
                             (int32_t)(ng_new - g), g * NL, h->at<int8_t>(h->off_scent) + g * S * kDim,
                             h->at<int32_t>(h->off_scnt) + g * S, h->at<int32_t>(h->off_soff) + g * S,
                             h->at<int32_t>(h->off_smem) + g * NL, nullptr, nullptr,
-                            h->at<int32_t>(h->off_leafsup), (int32_t)(g * S), s),
+                            h->at<int32_t>(h->off_leafsup), (int32_t)(g * S),
+                            h->at<char>(h->off_kmws), (size_t)h->kmws_bytes, s),
               "tree kmeans");
     }
   }

@@ -100,12 +100,16 @@ __host__ __device__ inline size_t kmeans_lds_bytes(int N, int C) {
   return b;
 }
 
+// mu_in / asg_in (members mode, iters = 0): the final centroids and
+// assignments come from the multi-workgroup iterations; only the member lists
+// and bucket records are built here.
 __global__ void __launch_bounds__(kKmThreads)
 k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0,
          int8_t* __restrict__ cent_all, int32_t* __restrict__ cnt_all,
          int32_t* __restrict__ off_all, int32_t* __restrict__ mem_all,
          int32_t* __restrict__ first_all, int32_t* __restrict__ last_all,
-         int32_t* __restrict__ map_all, int32_t map_base) {
+         int32_t* __restrict__ map_all, int32_t map_base, const int8_t* __restrict__ mu_in,
+         const uint16_t* __restrict__ asg_in) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int8_t* mu = reinterpret_cast<int8_t*>(smem);
   int32_t* musq = reinterpret_cast<int32_t*>(mu + (size_t)C * kDim);
@@ -122,11 +126,20 @@ k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0
   const int8_t* X = X_all + (int64_t)blk * N * kDim;
   const int stride = N / C;
 
-  // init at strided members
+  // init at strided members (members mode: the final centroids and assignments)
   for (int e = tid; e < C * 4; e += kKmThreads) {
     const int c = e >> 2, part = e & 3;
-    reinterpret_cast<int4*>(mu + c * kDim)[part] =
-        reinterpret_cast<const int4*>(X + (int64_t)c * stride * kDim)[part];
+    const int8_t* src = mu_in ? mu_in + ((int64_t)blk * C + c) * kDim : X + (int64_t)c * stride * kDim;
+    reinterpret_cast<int4*>(mu + c * kDim)[part] = reinterpret_cast<const int4*>(src)[part];
+  }
+  if (asg_in) {
+    for (int e = tid; e < C; e += kKmThreads) counts[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < N; i += kKmThreads) {
+      const uint16_t c = asg_in[(int64_t)blk * N + i];
+      assign[i] = c;
+      atomicAdd(&counts[c], 1);
+    }
   }
   __syncthreads();
 
@@ -265,6 +278,136 @@ k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0
   }
 }
 
+// ---------------------------------------------------------------- few-block k-means
+// When only a few blocks complete (a prefill chunk, a decode step, a Tree
+// group), one workgroup per block would leave the GPU idle, so each block's
+// points are split over W workgroups.  Per iteration: k_km_assign (centroids
+// of the iteration, MFMA distances, argmin with lowest-index ties, per-
+// workgroup integer sums and counts of its points) then k_km_reduce (sums
+// over the W parts, round-half-even means, empty clusters keep their
+// centroid); the member lists come from k_kmeans in members mode.  Integer
+// sums are order-free, so the result equals the one-workgroup kernel's.
+constexpr int kKmW = 16;            // most workgroups per block
+constexpr int kKmAT = 256;          // threads of k_km_assign
+
+struct KmScratch {
+  int32_t* part;                    // [nblk][W][C][65]: 64 dim sums + count
+  int8_t* cent;                     // [nblk][C][64]: centroids of the last reduce
+  uint16_t* asg;                    // [nblk][N]: last assignment
+};
+
+size_t km_layout(int N, int C, int nblk, KmScratch* S, void* base) {
+  char* p = static_cast<char*>(base);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { char* r = p ? p + o : nullptr; o += (bytes + 255) / 256 * 256; return r; };
+  KmScratch k;
+  k.part = reinterpret_cast<int32_t*>(take((size_t)nblk * kKmW * C * 65 * 4));
+  k.cent = reinterpret_cast<int8_t*>(take((size_t)nblk * C * kDim));
+  k.asg = reinterpret_cast<uint16_t*>(take((size_t)nblk * N * 2));
+  if (S) *S = k;
+  return o;
+}
+
+int km_parts(int N) {               // W: N must split into 16-row tiles
+  int w = kKmW;
+  while (w > 1 && N % (16 * w)) w >>= 1;
+  return w;
+}
+
+__global__ void __launch_bounds__(kKmAT) k_km_assign(const int8_t* __restrict__ X_all, int N, int C,
+                                                     int W, int it, KmScratch S) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int8_t* mu = reinterpret_cast<int8_t*>(smem);
+  int32_t* musq = reinterpret_cast<int32_t*>(mu + (size_t)C * kDim);
+  int32_t* sums = musq + C;
+  int32_t* cnts = sums + C * kDim;
+  const int b = blockIdx.x / W, w = blockIdx.x % W;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int8_t* X = X_all + (int64_t)b * N * kDim;
+  const int stride = N / C;
+  for (int e = tid; e < C * 4; e += kKmAT) {
+    const int c = e >> 2, part = e & 3;
+    const int8_t* src = it == 0 ? X + (int64_t)c * stride * kDim : S.cent + ((int64_t)b * C + c) * kDim;
+    reinterpret_cast<int4*>(mu + c * kDim)[part] = reinterpret_cast<const int4*>(src)[part];
+  }
+  for (int e = tid; e < C * kDim; e += kKmAT) sums[e] = 0;
+  for (int e = tid; e < C; e += kKmAT) cnts[e] = 0;
+  __syncthreads();
+  for (int c = tid; c < C; c += kKmAT) {
+    int sq = 0;
+    for (int d = 0; d < kDim; ++d) { const int m = mu[c * kDim + d]; sq += m * m; }
+    musq[c] = sq;
+  }
+  __syncthreads();
+  const int rows = N / W;
+  const int r0 = w * rows;
+  for (int rt = wave; rt < rows / 16; rt += kKmAT / 64) {
+    const int row = r0 + rt * 16;
+    const v4i a = *reinterpret_cast<const v4i*>(X + (int64_t)(row + (lane & 15)) * kDim + 16 * (lane >> 4));
+    int best[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+    int bidx[4] = {0, 0, 0, 0};
+    for (int ct = 0; ct < (C >> 4); ++ct) {
+      const int c = ct * 16 + (lane & 15);
+      const v4i bv = *reinterpret_cast<const v4i*>(mu + c * kDim + 16 * (lane >> 4));
+      const v4i z = {0, 0, 0, 0};
+      const v4i dot = mfma_i8_16x16x64(a, bv, z);
+      const int msq = musq[c];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int d = msq - 2 * dot[v];
+        if (d < best[v]) { best[v] = d; bidx[v] = c; }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ob = __shfl_xor(best[v], m);
+        const int oi = __shfl_xor(bidx[v], m);
+        if (ob < best[v] || (ob == best[v] && oi < bidx[v])) { best[v] = ob; bidx[v] = oi; }
+      }
+    }
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) S.asg[(int64_t)b * N + row + 4 * (lane >> 4) + v] = (uint16_t)bidx[v];
+    }
+    // the tile's 16 rows join their clusters' sums (lane = dimension)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = __shfl(bidx[r & 3], (r >> 2) * 16);
+      atomicAdd(&sums[c * kDim + lane], (int)X[(int64_t)(row + r) * kDim + lane]);
+      if (lane == 0) atomicAdd(&cnts[c], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* part = S.part + ((int64_t)b * W + w) * C * 65;
+  for (int e = tid; e < C * 65; e += kKmAT) {
+    const int c = e / 65, d = e % 65;
+    part[e] = d < kDim ? sums[c * kDim + d] : cnts[c];
+  }
+}
+
+// One thread per (block, cluster, dimension).
+__global__ void __launch_bounds__(256) k_km_reduce(const int8_t* __restrict__ X_all, int N, int C,
+                                                   int W, int it, int nblk, KmScratch S) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)nblk * C * kDim) return;
+  const int b = (int)(e / (C * kDim));
+  const int c = (int)((e / kDim) % C);
+  const int d = (int)(e % kDim);
+  const int32_t* part = S.part + (int64_t)b * W * C * 65 + c * 65;
+  int sum = 0, n = 0;
+  for (int w = 0; w < W; ++w) {
+    sum += part[(int64_t)w * C * 65 + d];
+    n += part[(int64_t)w * C * 65 + kDim];
+  }
+  int8_t* dst = S.cent + ((int64_t)b * C + c) * kDim + d;
+  const int8_t prev = it == 0 ? X_all[((int64_t)b * N + (int64_t)c * (N / C)) * kDim + d] : *dst;
+  *dst = n > 0 ? (int8_t)rhe_div(sum, n) : prev;
+}
+
+size_t kmeans_mw_lds(int C) { return (size_t)C * kDim + (size_t)C * 4 + (size_t)C * kDim * 4 + (size_t)C * 4; }
+
 // ---------------------------------------------------------------- decode append
 // One new key per sequence (workgroup i = sequence i, thread = dimension).
 // The key joins its sequence's pending partial group; when the group
@@ -335,21 +478,52 @@ hipError_t launch_tail(const int8_t* pooled, int64_t g0, int64_t g1, int64_t n_f
   return hipGetLastError();
 }
 
+size_t kmeans_scratch_bytes(int32_t N, int32_t C) {
+  return km_layout(N, C, kKmMaxBlk, nullptr, nullptr);
+}
+
 hipError_t launch_kmeans(const int8_t* X, int32_t N, int32_t C, int32_t iters, int32_t nblk,
                          int64_t row0, int8_t* cent_out, int32_t* cnt_out, int32_t* off_out,
                          int32_t* mem_out, int32_t* first_out, int32_t* last_out,
-                         int32_t* map_out, int32_t map_base, hipStream_t s) {
+                         int32_t* map_out, int32_t map_base, void* scratch,
+                         size_t scratch_bytes, hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
-  const size_t lds = kmeans_lds_bytes(N, C);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_kmeans,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)k_km_assign, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
+  const size_t lds = kmeans_lds_bytes(N, C);
+  const int W = km_parts(N);
+  // few blocks: W workgroups per block, one launch pair per iteration
+  if (scratch && nblk <= kKmMaxBlk && W > 1 && nblk * W <= 256 && iters > 0 &&
+      scratch_bytes >= km_layout(N, C, nblk, nullptr, nullptr)) {
+    KmScratch S;
+    km_layout(N, C, nblk, &S, scratch);
+    const size_t alds = kmeans_mw_lds(C);
+    const unsigned rgrid = (unsigned)(((int64_t)nblk * C * kDim + 255) / 256);
+    for (int it = 0; it < iters; ++it) {
+      hipLaunchKernelGGL(k_km_assign, dim3((unsigned)(nblk * W)), dim3(kKmAT), alds, s, X, N, C, W,
+                         it, S);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_km_reduce, dim3(rgrid), dim3(256), 0, s, X, N, C, W, it, nblk, S);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_kmeans, dim3(nblk), dim3(kKmThreads), lds, s, X, N, C, 0, row0, cent_out,
+                       cnt_out, off_out, mem_out, first_out, last_out, map_out, map_base,
+                       (const int8_t*)S.cent, (const uint16_t*)S.asg);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_kmeans, dim3(nblk), dim3(kKmThreads), lds, s, X, N, C, iters, row0,
-                     cent_out, cnt_out, off_out, mem_out, first_out, last_out, map_out, map_base);
+                     cent_out, cnt_out, off_out, mem_out, first_out, last_out, map_out, map_base,
+                     (const int8_t*)nullptr, (const uint16_t*)nullptr);
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct Index {
   // arena byte offsets
   int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast;
   int64_t off_scent, off_scnt, off_soff, off_smem, off_leafsup, off_pend;
+  int64_t off_kmws, kmws_bytes;   // k-means scratch (few-block clustering)
   int64_t used_bytes;
 
   template <class T> T* at(int64_t off) const { return reinterpret_cast<T*>(arena + off); }
@@ -88,10 +89,15 @@ hipError_t launch_pool(const int8_t* pend, int32_t n_pend, const int8_t* src, in
                        int32_t p, int8_t* pooled_out, int64_t n_groups, hipStream_t s);
 hipError_t launch_save_pending(const int8_t* pend, int32_t n_pend, const int8_t* src,
                                int64_t n_src, int32_t keep, int8_t* dst, hipStream_t s);
+// Scratch for clustering up to kKmMaxBlk blocks of N points into C clusters
+// with several workgroups per block (0: that path is not used).
+constexpr int kKmMaxBlk = 8;
+size_t kmeans_scratch_bytes(int32_t N, int32_t C);
 hipError_t launch_kmeans(const int8_t* X, int32_t N, int32_t C, int32_t iters, int32_t nblk,
                          int64_t row0, int8_t* cent_out, int32_t* cnt_out, int32_t* off_out,
                          int32_t* mem_out, int32_t* first_out, int32_t* last_out,
-                         int32_t* map_out, int32_t map_base, hipStream_t s);
+                         int32_t* map_out, int32_t map_base, void* scratch,
+                         size_t scratch_bytes, hipStream_t s);
 hipError_t launch_tail(const int8_t* pooled, int64_t g0, int64_t g1, int64_t n_full, int32_t N,
                        int32_t C, int8_t* cent, int32_t* bcnt, int32_t* boff, int32_t* bmem,
                        int32_t* bfirst, int32_t* blast, hipStream_t s);
