@@ -75,7 +75,7 @@ struct Cfg {
   static constexpr int FT = FW * 64;
   static constexpr int NQW = QS / 16;        // query groups (16 MFMA rows each)
   static constexpr int PH = FW / NQW;        // waves sharing a query group (tile phases)
-  static_assert(FW % NQW == 0 && (PH == 1 || PH == 4), "unsupported scan shape");
+  static_assert(FW % NQW == 0 && (PH == 1 || PH == 2 || PH == 4), "unsupported scan shape");
 };
 
 template <int FW, int QS>
@@ -261,7 +261,8 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   // select tree and taking a slot of the sub-list (bucket id mod 64) from an
   // LDS counter.
   {
-    static_assert(C::PH == 1, "the full pass gives each wave its own query group");
+    constexpr int TPW = CHT / C::PH;    // this wave's tiles per chunk: phase, phase + PH, ...
+    static_assert(TPW % 4 == 0, "the full pass takes groups of four of a wave's tiles");
     int slo[4];
     v4i bias;
 #pragma unroll
@@ -271,11 +272,11 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     }
     stream_chunks(V, S, 0, 1, nchunks, [&](int c, int buf) {
 #pragma unroll
-      for (int g = 0; g < CHT; g += 4) {
+      for (int g = 0; g < TPW; g += 4) {
         int d[16];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const v4i r = mfma_i8_16x16x64(qa, S.cent[buf][(g + u) * 64 + lane], bias);
+          const v4i r = mfma_i8_16x16x64(qa, S.cent[buf][(phase + C::PH * (g + u)) * 64 + lane], bias);
 #pragma unroll
           for (int v = 0; v < 4; ++v) d[4 * u + v] = r[v];
         }
@@ -283,11 +284,11 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
 #pragma unroll
         for (int k = 15; k >= 0; --k) miss = __builtin_amdgcn_alignbit(miss, (unsigned)d[k], 31);
         unsigned hits = ~miss & 0xffffu;
-        const int tb = c * CHT + g;       // first tile of the group
-        if ((tb + 4) * 16 > V.n_bkt) {    // last group: no buckets past the end
+        const int tb = c * CHT + phase + C::PH * g;   // tile of u: tb + PH * u
+        if ((c + 1) * CHT * 16 > V.n_bkt) {           // last chunk: no buckets past the end
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            if ((tb + u) * 16 + col >= V.n_bkt) hits &= ~(0xfu << (4 * u));
+            if ((tb + C::PH * u) * 16 + col >= V.n_bkt) hits &= ~(0xfu << (4 * u));
         }
         while (hits) {
           const int k = __builtin_ctz(hits);
@@ -305,7 +306,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           const int dk = (int)((z[1] & m3) | (z[0] & ~m3));
           const int v = k & 3, u = k >> 2;
           const int sv = (v & 2) ? ((v & 1) ? slo[3] : slo[2]) : ((v & 1) ? slo[1] : slo[0]);
-          const int beta = (tb + u) * 16 + col;
+          const int beta = (tb + C::PH * u) * 16 + col;
           const int jl = beta & (NSUB - 1);
           const int qs = qrow + v;
           const int pos = atomicAdd(&S.nl[qs][jl], 1);
@@ -843,7 +844,7 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(IdxView V, SelArgs A, int
   if (tid == 0) flags[q] = ok ? 0 : 1;
 }
 
-constexpr int kPrefW = 4, kPrefQ = 64;     // prefill scan: 4 waves, 64 query slots
+constexpr int kPrefW = 8, kPrefQ = 64;     // prefill scan: 8 waves (two per query group), 64 query slots
 
 size_t ws_layout(size_t slots, size_t nq, ListWs* W, void* base) {
   char* p = static_cast<char*>(base);
