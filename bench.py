@@ -35,6 +35,7 @@ import hierarchical_sparse_attention_lsa_amd as L  # noqa: E402
 import lsa_synth as S  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_OPS = 5.0e15          # dense int8 MFMA, ops/s
 ATTN_SRC = os.path.join(ROOT, "hierarchical_sparse_attention_lsa_amd", "csrc", "lsa_attn.hip")
 ATTN_KERNEL = "k_attn_win<128, false>"
 
@@ -169,6 +170,34 @@ def bench_prefill(args, dev):
     return res
 
 
+def measured_copy_gbs(dev, nbytes=2 << 30):
+    """Read + write bandwidth of a plain device copy (torch), for context."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(3):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (min(ts) * 1e-3) / 1e9
+
+
+def layer_roof_ms(wl, res):
+    """Roofline time of the whole chunk step: attention bytes at the HBM peak plus
+    the query x centroid scoring at the int8 MFMA peak (append and the rest of
+    the selection are latency terms with no bandwidth floor of note)."""
+    n_bkt = (wl.T // wl.pool // wl.block) * wl.buckets
+    score_ops = 2.0 * res["n"] * n_bkt * 64
+    return res["attn_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3 + score_ops / INT8_PEAK_OPS * 1e3
+
+
 def bench_dense(res, dev, nq=4096):
     """Quadratic comparison: every long-range key scored on its own latent."""
     wl, t0 = res["wl"], res["t0"]
@@ -187,6 +216,44 @@ def bench_dense(res, dev, nq=4096):
     return {"queries": nq, "ms": ms, "ms_per_chunk_scaled": ms * res["n"] / nq,
             "note": "dense per-key int8 scan + exact top-B over all long-range keys, same "
                     "selection rule (p=1 singleton buckets)"}
+
+
+def bench_full_prefill(args, dev):
+    """Every chunk of the context through lsa_prefill_chunk, the index grown
+    chunk by chunk from empty: the whole prefill of one layer (a per-layer
+    time-to-first-token analogue).  Only the fused calls are timed; the next
+    chunk's Q and latent queries are generated outside the timed regions."""
+    wl = S.WORKLOADS[args.config]
+    n = wl.chunk
+    nchunks = wl.T // n
+    log(f"[full] {wl.name}: {nchunks} chunks of {n} queries")
+    g, latk, K, V = gen_inputs(wl, dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
+    ix = L.LsaIndex(iparams(wl, wl.T), dev)
+    q = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_PREFILL, ix.params, sp, ap, n), dtype=torch.uint8,
+                     device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for c in range(nchunks):
+        t0 = c * n
+        latq = g.latq_rows(torch.arange(t0, t0 + n, device=dev), device=dev)
+        g.fill_rows("q", q, t0)
+        torch.cuda.synchronize()
+        e0.record()
+        ix.prefill_chunk(latk[t0:t0 + n], latq, q, K, V, sp, ap, out=out, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        if c % 32 == 0 or c == nchunks - 1:
+            log(f"[full] chunk {c}: {times[-1]:.2f} ms")
+    t = np.array(times)
+    return {"workload": wl.name, "context_tokens": wl.T, "chunks": nchunks, "chunk_queries": n,
+            "total_s": float(t.sum() / 1e3), "queries_per_s": float(wl.T / (t.sum() / 1e3)),
+            "chunk_ms": {"first": float(t[0]), "median": float(np.median(t)), "last": float(t[-1]),
+                         "max": float(t.max())}}
 
 
 def bench_decode(args, dev):
@@ -402,6 +469,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="one prefill step plus a 2 GiB calibration copy (for rocprofv3 runs)")
+    ap.add_argument("--full-prefill", action="store_true",
+                    help="the whole context chunk by chunk (index grown from empty); prints its own line")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only the decode benchmark (for rocprofv3 kernel traces)")
     ap.add_argument("--summarize-decode", nargs=2, metavar=("STATS", "COMMAND"),
@@ -421,7 +490,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     workers_pool = None
-    if not args.no_cpu and not args.profile and not args.profile_decode:
+    if not args.no_cpu and not args.profile and not args.profile_decode and not args.full_prefill:
         # forked before anything touches the GPU; the workers only run the CPU oracle
         import multiprocessing as mp
         workers_pool = mp.get_context("fork").Pool(min(16, os.cpu_count() or 1))
@@ -432,6 +501,12 @@ def main():
     L.lib()
     if args.profile:
         profile_run(args, dev)
+        return
+    if args.full_prefill:
+        fp = bench_full_prefill(args, dev)
+        print(json.dumps({"metric": "LSA layer whole-prefill time (all chunks, index grown chunk by chunk)",
+                          "value": fp["total_s"], "unit": "s", "higher_is_better": False,
+                          "n_gpus": 1, "data": "synthetic", "config": fp}), flush=True)
         return
     if args.profile_decode:
         d = bench_decode(args, dev)
@@ -455,6 +530,9 @@ def main():
         if tj.get("src_hash") == src_hash(ATTN_SRC) and tj.get("workload") == wl.name:
             traffic = tj.get("bytes_per_launch")
 
+    copy_gbs = measured_copy_gbs(dev)
+    log(f"[bench] plain device copy {copy_gbs:.0f} GB/s (read + write)")
+
     decode = None
     if not args.no_decode:
         decode = bench_decode(args, dev)
@@ -474,6 +552,7 @@ def main():
         workers_pool.close()
         workers_pool.join()
     value = res["n"] / (res["ms_per_step"] / 1e3)
+    roof_ms = layer_roof_ms(wl, res)
     line = {
         "metric": "LSA layer prefill queries/s at T=10M (32k chunk); decode tok/s; % roofline",
         "value": value,
@@ -496,7 +575,10 @@ def main():
                      "achieved": res["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": res["achieved_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": res["attn_bytes"],
-                     "avg_launch_ms": res["attn_ms"]},
+                     "avg_launch_ms": res["attn_ms"],
+                     "measured_copy_gbs": copy_gbs,
+                     "layer": {"roof_ms": roof_ms, "measured_ms": res["ms_per_step"],
+                               "frac": roof_ms / res["ms_per_step"]}},
         "cpu_baseline": cpu,
         "phases_ms": {"append": res["phase_ms"][0], "select": res["phase_ms"][1],
                       "attention": res["phase_ms"][2]},

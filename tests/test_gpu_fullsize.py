@@ -198,3 +198,58 @@ def test_decode_1m_256_steps(oracle_pool):
     # the last step's index equals the oracle's over all keys
     check_index({k: v.cpu() for k, v in ixs[0].arrays().items()},
                 O.build_index(lat_h[0], cap, _oparams(wl), caches[0]))
+
+
+def test_flat_1m_chunked_prefill_from_empty(oracle_pool):
+    """The whole 1M context through lsa_prefill_chunk, 32 chunks from an empty
+    index: the final index equals the oracle's build, and sampled queries of
+    several chunks select the oracle's key sets and attend within tolerance."""
+    dev = _dev()
+    L = _L()
+    wl = S.WORKLOADS["flat_1m"]
+    n = wl.chunk
+    nchunks = wl.T // n
+    g = S.Synth(wl)
+    latk = g.latk(0, wl.T, device=dev, chunk=1 << 22)
+    K = torch.empty((wl.T, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0, chunk=1 << 18)
+    g.fill_rows("v", V, 0, chunk=1 << 18)
+    ix = L.LsaIndex(L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, wl.T), dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    q = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((n, sp.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((n,), dtype=torch.int32, device=dev)
+    checked = {0: [0, 1, 511, 512, 4095, 20000, n - 1], 1: [0, 7, 30000],
+               15: [0, 12345, n - 1], nchunks - 1: [0, 9999, n - 2, n - 1]}
+    got = {}
+    for c in range(nchunks):
+        t0 = c * n
+        latq = g.latq_rows(torch.arange(t0, t0 + n, device=dev), device=dev)
+        g.fill_rows("q", q, t0)
+        out = ix.prefill_chunk(latk[t0:t0 + n], latq, q, K, V, sp, ap, idx=idx, cnt=cnt)
+        if c in checked:
+            rows = checked[c]
+            got[c] = (idx[rows].cpu().numpy(), cnt[rows].cpu().numpy(), out[rows].cpu().numpy())
+    torch.cuda.synchronize()
+    arrays = {k: v.cpu() for k, v in ix.arrays().items()}
+    del K, V
+    torch.cuda.empty_cache()
+    cache, latk_h = build_cache_parallel(wl.name, wl.T, oracle_pool)    # host-generated
+    check_index(arrays, O.build_index(latk_h, wl.T, _oparams(wl), dict(cache)))
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    worst = 0.0
+    for c, rows in checked.items():
+        ref = O.build_index(latk_h, (c + 1) * n, _oparams(wl), dict(cache))
+        pos = [c * n + r for r in rows]
+        lq = g.latq_rows(torch.tensor(pos)).numpy()
+        sels = [O.select(ref, lq[j], t, osp) for j, t in enumerate(pos)]
+        gi, gc, go = got[c]
+        for j, t in enumerate(pos):
+            assert np.array_equal(np.sort(gi[j, :gc[j]]), sels[j]), f"chunk {c} position {t}"
+        refo = oracle_attention(g, wl, pos, sels)
+        worst = max(worst, normwise(go.astype(np.float64), refo))
+    print(f"chunked prefill from empty: {sum(len(r) for r in checked.values())} selections bit-exact, "
+          f"attention normwise error {worst:.3e}")
+    assert worst <= TOL
