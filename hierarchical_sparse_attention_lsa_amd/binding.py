@@ -28,7 +28,8 @@ class IndexParams(ctypes.Structure):
 
 
 class SelectParams(ctypes.Structure):
-    _fields_ = [("budget", c_i32), ("window", c_i32), ("sinks", c_i32), ("tree_top", c_i32)]
+    _fields_ = [("budget", c_i32), ("window", c_i32), ("sinks", c_i32), ("tree_top", c_i32),
+                ("early_budget", c_i32), ("early_until", c_i32)]
 
     @property
     def max_sel(self) -> int:

@@ -116,6 +116,9 @@ int check_select_params(const lsa_select_params* sp, bool tree) {
   if (sp->window < 1 || sp->window > (1 << 20)) return fail(LSA_E_ARG, "window %d not in [1, 2^20]", sp->window);
   if (sp->sinks < 0 || sp->sinks > (1 << 20)) return fail(LSA_E_ARG, "sinks %d not in [0, 2^20]", sp->sinks);
   if (tree && sp->tree_top < 1) return fail(LSA_E_ARG, "tree_top %d < 1", sp->tree_top);
+  if (sp->early_until < 0) return fail(LSA_E_ARG, "early_until %d < 0", sp->early_until);
+  if (sp->early_until > 0 && (sp->early_budget < 0 || sp->early_budget > sp->budget))
+    return fail(LSA_E_ARG, "early_budget %d not in [0, budget]", sp->early_budget);
   return LSA_OK;
 }
 
@@ -237,6 +240,7 @@ int select_impl(const Index* h, const int8_t* latq, const int32_t* qpos, int32_t
   SelArgs a;
   a.latq = latq; a.qpos = qpos; a.qpos_base = qpos_base; a.nq = nq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
+  a.early_budget = sp->early_budget; a.early_until = sp->early_until;
   a.max_sel = max_sel_of(sp);
   a.idx = idx; a.cnt = cnt; a.only = nullptr;
   if (!v.leafsup && nq >= kFastSelectMinQ && ws && ws_bytes >= select_fast_ws_bytes(nq)) {
@@ -562,6 +566,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   memset(&a, 0, sizeof a);
   a.latq = d_latq; a.qpos = nullptr; a.qpos_base = 0; a.nq = nseq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
+  a.early_budget = sp->early_budget; a.early_until = sp->early_until;
   a.max_sel = max_sel; a.idx = idx; a.cnt = cnt; a.only = nullptr;
   LSA_HIP(launch_select_dec(views, qpos, nseq, h0->max_bkt, a, selws, s), "decode select");
 
@@ -588,6 +593,7 @@ int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, cons
   SelArgs a;
   a.latq = d_latq; a.qpos = d_qpos; a.qpos_base = 0; a.nq = nq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = 0;
+  a.early_budget = sp->early_budget; a.early_until = sp->early_until;
   a.max_sel = max_sel_of(sp);
   a.idx = d_idx; a.cnt = d_cnt; a.only = nullptr;
   LSA_HIP(launch_select(v, a, nullptr, static_cast<hipStream_t>(stream)), "dense select");

@@ -62,11 +62,17 @@ struct SelArgs {
   int32_t qpos_base;
   int32_t nq;
   int32_t budget, window, sinks, tree_top;
+  int32_t early_budget, early_until;   // queries at t < early_until take early_budget
   int32_t max_sel;
   int32_t* idx;           // [nq][max_sel]
   int32_t* cnt;           // [nq]
   const int32_t* only;    // nullable: serve only queries with only[q] != 0
 };
+
+// Long-range key budget of the query at position t.
+__host__ __device__ inline int budget_at(const SelArgs& a, int t) {
+  return t < a.early_until ? a.early_budget : a.budget;
+}
 
 // Batched one-key append for decode (all indexes share one layout).
 struct DecodeAppendArgs {

@@ -126,7 +126,6 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int q0 = blockIdx.x * NQ;
   const int nqt = min(NQ, A.nq - q0);
-  const int B = A.budget;
   const int qrow = 4 * (lane >> 4);     // first query slot of this lane's score rows
   // nothing to do for this workgroup (all its queries masked out)
   if (!__syncthreads_or(tid < nqt && (!A.only || A.only[q0 + tid]))) return;
@@ -145,7 +144,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
     S.smax[tid] = INT_MIN; S.ssum[tid] = 0; S.sn[tid] = 0; S.above[tid] = 0;
     S.nfull[tid] = 0; S.ncand[tid] = 0; S.fullsum[tid] = 0; S.pbeta[tid] = -1; S.ptake[tid] = 0;
     S.lo[tid] = KMINP; S.hi[tid] = KMAXP;
-    if (val && B <= 0) { S.status[tid] = ST_DONE; S.lo[tid] = KMAXP + 1; S.hi[tid] = KMAXP; }
+    if (val && budget_at(A, S.t[tid]) <= 0) { S.status[tid] = ST_DONE; S.lo[tid] = KMAXP + 1; S.hi[tid] = KMAXP; }
   }
   if (TREE)
     for (int e = tid; e < QT * MAXSUPW; e += ST) (&S.supmask[0][0])[e] = 0u;
@@ -300,6 +299,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
     for (int qi = wave; qi < NQ; qi += SW) {
       if (S.status[qi] != ST_REFINE) continue;
       const int A0 = S.above[qi];
+      const int B = budget_at(A, S.t[qi]);   // this query's long-range budget
       const long long lo_q = S.lo[qi], hi_q = S.hi[qi];
       const int shq = S.shift[qi];
       int hk[NB / 64], hb[NB / 64], loc = 0;
@@ -394,8 +394,8 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       wave_bitonic(cq, np);
-      int need = B - S.fullsum[qi];
       const int t = S.t[qi];
+      int need = budget_at(A, t) - S.fullsum[qi];
       for (int base = 0; base < nc && need > 0; base += 64) {
         const int i = base + lane;
         int e = 0, beta = -1, klo;

@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   const IdxView V = vsp->v[seq];
   const int t = vsp->qpos[seq];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int B = A.budget;
+  const int B = budget_at(A, t);
   const int n = V.n_bkt;
   const int p = V.pool;
   const int64_t base = (int64_t)seq * VS.cap;

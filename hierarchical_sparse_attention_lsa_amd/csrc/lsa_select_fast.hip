@@ -147,7 +147,6 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   const int phase = wave / C::NQW;
   const int qrow = qgrp * 16 + 4 * (lane >> 4);    // slot of score row v = 0
   const int col = lane & 15;
-  const int B = A.budget;
   const int p = V.pool;
 
   for (int i = tid; i < QS; i += C::FT) {
@@ -239,7 +238,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           int s = 0;
           while (s < 30 && (((mx - mn + 1) + (1 << s) - 1) >> s) > NB2) ++s;
           const int sampled = (nchunks + sstep - 1) / sstep;
-          const long long target = (2ll * B * sampled + nchunks - 1) / nchunks;
+          const long long target = (2ll * budget_at(A, S.t[qs]) * sampled + nchunks - 1) / nchunks;
           long long cum = 0;
           slo = mn;
           for (int b = 0; b < NB2; ++b) {
@@ -394,7 +393,7 @@ __device__ __forceinline__ bool select_and_emit(ResolveLds& L, const IdxView& V,
                                                 const int (&e)[TPQ], long long lo, long long hi,
                                                 long long tot, bool complete, KsOf ksof) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int B = A.budget;
+  const int B = budget_at(A, t);
   const int p = V.pool;
   tot = block_sum_ll<RT>(tot, L.red);
   lo = block_min_ll<RT>(lo, L.red);
@@ -640,7 +639,7 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
   if (q < 0) return;                 // uniform over the workgroup
   const int t = W.meta[2 * slot + 1];
   const IdxView V = vsp->v[VS.nviews > 1 ? (int)(slot / VS.slots_per_view) : 0];
-  const int B = A.budget;
+  const int B = budget_at(A, t);
   const int p = V.pool;
   const long long* lk = W.key + slot * LC;
   int len = 0;
@@ -760,7 +759,7 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(IdxView V, SelArgs A, int
   const int t = max(0, A.qpos ? A.qpos[q] : A.qpos_base + q);
   const int R = min(A.tree_top, V.n_sup);
   const int n_unc = V.n_bkt - V.covered;
-  bool ok = A.budget > 0 && R >= 1 && R <= TOPCAP && V.n_sup <= SUPN;
+  bool ok = budget_at(A, t) > 0 && R >= 1 && R <= TOPCAP && V.n_sup <= SUPN;
   if (tid == 0) { L.nc = 0; L.nt = 0; }
   int qv[16];
   {

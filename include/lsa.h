@@ -89,9 +89,15 @@ typedef struct lsa_index_params {
 
 /* Per-query selection: budget long-range keys (sinks <= j <= t - window),
  * the window [t-window+1, t] and the sinks [0, sinks).  window >= pool.
- * tree_top = super clusters a query walks into (Tree indexes only). */
+ * tree_top = super clusters a query walks into (Tree indexes only).
+ * Position-dependent budget (mauroscia.it, D-LSA paragraph: on GLM, Flat
+ * takes 2048 long-range keys for queries before position 1M): a query at
+ * t < early_until takes early_budget long-range keys instead of budget;
+ * 0 <= early_budget <= budget.  early_until = 0 turns it off.  Rows keep the
+ * stride budget + window + sinks. */
 typedef struct lsa_select_params {
   int32_t budget, window, sinks, tree_top;
+  int32_t early_budget, early_until;
 } lsa_select_params;
 
 /* Attention shape.  D in {64, 128}; 1 <= Hq/Hkv <= 16, Hq % Hkv == 0.

@@ -223,6 +223,14 @@ class SelectParams:
     window: int = 512
     sinks: int = 4
     tree_top: int = 0
+    # position-dependent budget (mauroscia.it D-LSA paragraph: on GLM, Flat
+    # takes 2048 long-range keys for queries before position 1M):
+    # queries at t < early_until take early_budget long-range keys
+    early_budget: int = 0
+    early_until: int = 0
+
+    def budget_at(self, t: int) -> int:
+        return self.early_budget if t < self.early_until else self.budget
 
 
 def bucket_keys(idx: Index, beta: int) -> np.ndarray:
@@ -263,16 +271,16 @@ def select(idx: Index, q: np.ndarray, t: int, sp: SelectParams) -> np.ndarray:
     """Sorted key ids attended by the query at position t (t < idx.T).
 
     Candidate buckets are visited in (score desc, bucket id asc) order; each
-    contributes its eligible keys in ascending position until ``budget``
-    long-range keys are held (the last bucket is cut at its lowest
-    positions).  The window [t-w+1, t] and the sinks [0, sinks) are added;
+    contributes its eligible keys in ascending position until the budget
+    (``sp.budget_at(t)``) of long-range keys is held (the last bucket is cut
+    at its lowest positions).  The window [t-w+1, t] and the sinks [0, sinks) are added;
     every key is <= t.
     """
     cand = candidates(idx, q, sp)
     s = scores(idx.centroids[cand], q)
     order = cand[np.lexsort((cand, -s))]
     picked: List[np.ndarray] = []
-    need = sp.budget
+    need = sp.budget_at(t)
     for beta in order:
         if need <= 0:
             break
@@ -290,11 +298,12 @@ def select(idx: Index, q: np.ndarray, t: int, sp: SelectParams) -> np.ndarray:
 
 def dense_select(latk: np.ndarray, q: np.ndarray, t: int, sp: SelectParams) -> np.ndarray:
     """Quadratic comparator: score every long-range key itself, keep the best
-    ``budget`` by (score desc, position asc), add the window and the sinks."""
+    ``sp.budget_at(t)`` by (score desc, position asc), add the window and
+    the sinks."""
     lo, hi = sp.sinks, t - sp.window
     keys = np.arange(lo, hi + 1, dtype=np.int64) if hi >= lo else np.zeros(0, np.int64)
     sc = scores(latk[keys], q) if keys.size else np.zeros(0, np.int64)
-    best = keys[np.lexsort((keys, -sc))][: sp.budget]
+    best = keys[np.lexsort((keys, -sc))][: sp.budget_at(t)]
     window = np.arange(max(0, t - sp.window + 1), t + 1, dtype=np.int64)
     sinks = np.arange(0, min(sp.sinks, t + 1), dtype=np.int64)
     return np.unique(np.concatenate([best, window, sinks]))

@@ -40,13 +40,13 @@ def _oparams(wl):
 def _sample_positions(wl, n_sel, seed):
     n, t0 = wl.chunk, wl.T - wl.chunk
     kpb = wl.pool * wl.block
-    fixed = [0, 1, n - 1, n - 2, kpb - 1, kpb, kpb + 1, n // 2]
+    fixed = [0, 1, n - 1, n - 2, kpb - 1, kpb, kpb + 1, n // 2 - 1, n // 2]
     rng = np.random.default_rng(seed)
     rest = rng.choice(n, n_sel - len(fixed), replace=False).tolist()
     return sorted(set(i for i in fixed + rest if 0 <= i < n))
 
 
-def _gpu_prefill(wl, dev, out_f32_too=True):
+def _gpu_prefill(wl, dev, out_f32_too=True, early=(0, 0)):
     """The benchmarked step: prebuilt index, then lsa_prefill_chunk (bf16 out)."""
     L = _L()
     g = S.Synth(wl)
@@ -63,7 +63,7 @@ def _gpu_prefill(wl, dev, out_f32_too=True):
                                   wl.tree_super, wl.tree_iters, wl.T), dev)
     ix.build(latk[:t0])
     snap = ix.snapshot()
-    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, *early)
     idx = torch.empty((n, sp.max_sel), dtype=torch.int32, device=dev)
     cnt = torch.empty((n,), dtype=torch.int32, device=dev)
     o16 = ix.prefill_chunk(latk[t0:], latq, q, K, V, sp, L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0),
@@ -81,10 +81,10 @@ def _gpu_prefill(wl, dev, out_f32_too=True):
     return res
 
 
-def _check_prefill(wl, res, ref, n_sel, n_att, seed):
+def _check_prefill(wl, res, ref, n_sel, n_att, seed, early=(0, 0)):
     n, t0 = wl.chunk, wl.T - wl.chunk
     check_index(res["arrays"], ref)
-    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, *early)
     pos = _sample_positions(wl, n_sel, seed)
     latq = res["g"].latq_rows(torch.tensor([t0 + i for i in pos])).numpy()   # host-generated
     sels = {}
@@ -104,13 +104,23 @@ def _check_prefill(wl, res, ref, n_sel, n_att, seed):
     assert np.array_equal(o16, rne_bf16_bits(res["o32"].cpu().numpy()))
 
 
-def test_flat_1m_prefill_chunk(oracle_pool):
+@pytest.fixture(scope="module")
+def oracle_1m(oracle_pool):
+    wl = S.WORKLOADS["flat_1m"]
+    cache, latk = build_cache_parallel(wl.name, wl.T, oracle_pool)
+    return cache, latk
+
+
+# (early_budget, early_until): the second keeps 2048 long-range keys for the
+# first half of the chunk and the full budget from the middle on
+@pytest.mark.parametrize("early", [(0, 0), (2048, (1 << 20) - (1 << 14))])
+def test_flat_1m_prefill_chunk(oracle_1m, early):
     dev = _dev()
     wl = S.WORKLOADS["flat_1m"]
-    res = _gpu_prefill(wl, dev)
-    cache, latk = build_cache_parallel(wl.name, wl.T, oracle_pool)
-    ref = O.build_index(latk, wl.T, _oparams(wl), cache)
-    _check_prefill(wl, res, ref, n_sel=160, n_att=24, seed=1)
+    res = _gpu_prefill(wl, dev, early=early)
+    cache, latk = oracle_1m
+    ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
+    _check_prefill(wl, res, ref, n_sel=160, n_att=24, seed=1 + early[0], early=early)
 
 
 @pytest.fixture(scope="module")
@@ -200,7 +210,7 @@ def test_decode_1m_256_steps(oracle_pool):
                 O.build_index(lat_h[0], cap, _oparams(wl), caches[0]))
 
 
-def test_flat_1m_chunked_prefill_from_empty(oracle_pool):
+def test_flat_1m_chunked_prefill_from_empty(oracle_1m):
     """The whole 1M context through lsa_prefill_chunk, 32 chunks from an empty
     index: the final index equals the oracle's build, and sampled queries of
     several chunks select the oracle's key sets and attend within tolerance."""
@@ -236,7 +246,7 @@ def test_flat_1m_chunked_prefill_from_empty(oracle_pool):
     arrays = {k: v.cpu() for k, v in ix.arrays().items()}
     del K, V
     torch.cuda.empty_cache()
-    cache, latk_h = build_cache_parallel(wl.name, wl.T, oracle_pool)    # host-generated
+    cache, latk_h = oracle_1m                                            # host-generated
     check_index(arrays, O.build_index(latk_h, wl.T, _oparams(wl), dict(cache)))
     osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
     worst = 0.0

@@ -204,6 +204,60 @@ def test_tiny_prefill_chunk_fused(tiny):
     assert err <= TOL
 
 
+def test_position_dependent_budget(tiny):
+    """Queries before early_until take early_budget long-range keys, later ones
+    the full budget; the switch falls inside one launch.  Checked on the
+    scan + resolve path, the exact path, the fused prefill chunk and the
+    dense (every-key) selection."""
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    t0 = wl.T - wl.chunk
+    pos = list(range(t0, wl.T)) + [0, 3, 131, 132, 5000, 9000]
+    lq = g.latq_rows(torch.tensor(pos))
+    pos_d = torch.tensor(pos, dtype=torch.int32, device=dev)
+    for eb, eu in ((300, t0 + 37), (0, t0 + 64), (wl.budget, wl.T), (17, 6000), (200, 0)):
+        sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0, eb, eu)
+        osp = O.SelectParams(wl.budget, wl.window, wl.sinks, 0, eb, eu)
+        refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+        idx, cnt = ix.select(lq.to(dev), pos_d, sp)
+        check_selection(idx, cnt, refs, sp.max_sel)
+        idx2, cnt2 = ix.select(lq.to(dev), pos_d, sp, use_workspace=False)
+        assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    # fused prefill chunk with the switch in the middle of the chunk
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0, 400, t0 + 50)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, 0, 400, t0 + 50)
+    ix2 = L.LsaIndex(_iparams(wl), dev)
+    ix2.build(latk[:t0].to(dev))
+    K = torch.empty((wl.T, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0)
+    g.fill_rows("v", V, 0)
+    cpos = list(range(t0, wl.T))
+    clq = g.latq_rows(torch.tensor(cpos))
+    q = g.q_rows(torch.tensor(cpos))
+    idx = torch.empty((wl.chunk, wl.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((wl.chunk,), dtype=torch.int32, device=dev)
+    out = ix2.prefill_chunk(latk[t0:].to(dev), clq.to(dev), q.to(dev), K.to(dev), V.to(dev), sp,
+                            L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0), idx=idx, cnt=cnt)
+    torch.cuda.synchronize()
+    sels = [O.select(ref, clq[i].numpy(), t, osp) for i, t in enumerate(cpos)]
+    check_selection(idx, cnt, sels, wl.max_sel)
+    assert len(sels[0]) < len(sels[-1])
+    err = normwise(out.cpu().numpy().astype(np.float64), oracle_attention(g, wl, cpos, sels))
+    assert err <= TOL
+    # dense selection
+    dpos = [5, 200, 1000, 2047, 4096, 5999, 3333]
+    dlq = g.latq_rows(torch.tensor(dpos))
+    sp = L.SelectParams(300, 128, 4, 0, 90, 3000)
+    osp = O.SelectParams(300, 128, 4, 0, 90, 3000)
+    idx, cnt = L.dense_select(latk[:6000].to(dev), dlq.to(dev),
+                              torch.tensor(dpos, dtype=torch.int32, device=dev), sp)
+    refs = [O.dense_select(latk[:6000].numpy(), dlq[i].numpy(), t, osp) for i, t in enumerate(dpos)]
+    check_selection(idx, cnt, refs, sp.max_sel)
+
+
 WINDOW_CASES = [
     # Hq, Hkv, D, qpos0, nq, budget, window, sinks
     (4, 1, 64, 0, 37, 120, 40, 5),        # G=4: 4 queries a wave; windows cut at 0, no long-range keys
@@ -352,15 +406,16 @@ def test_tree_index_and_selection():
     check_index(ix.arrays(), ref)
     pos = [wl.T - 1 - 37 * i for i in range(40)] + [70, 500, 4000]
     lq = g.latq_rows(torch.tensor(pos))
-    for R in (1, 5, 48):
-        sp = L.SelectParams(wl.budget, wl.window, wl.sinks, R)
-        osp = O.SelectParams(wl.budget, wl.window, wl.sinks, R)
+    for R, eb, eu in ((1, 0, 0), (5, 0, 0), (48, 0, 0), (5, 120, 9000)):
+        sp = L.SelectParams(wl.budget, wl.window, wl.sinks, R, eb, eu)
+        osp = O.SelectParams(wl.budget, wl.window, wl.sinks, R, eb, eu)
         idx, cnt = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
         refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
         check_selection(idx, cnt, refs, sp.max_sel)
 
 
-def test_decode_steps_match_oracle():
+@pytest.mark.parametrize("early", [(0, 0), (100, 4 * 256 * 4 + 5 + 4)])
+def test_decode_steps_match_oracle(early):
     dev = _dev()
     L = _L()
     wl = S.Workload("dec_small", 60, T=4 * 256 * 4 + 5, ncomp=64, block=256, buckets=32, iters=3,
@@ -379,8 +434,8 @@ def test_decode_steps_match_oracle():
         g.fill_rows("k", K[i], 0)
         g.fill_rows("v", V[i], 0)
     Kd, Vd = K.to(dev), V.to(dev)
-    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
-    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0, *early)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, 0, *early)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
     errs = []
     for step in range(wl.steps):

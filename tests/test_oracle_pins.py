@@ -167,6 +167,22 @@ def test_select_against_enumeration(seed):
         assert O.select(idx, q, t, sp).tolist() == _brute_select(idx, latk, q, t, sp)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_position_dependent_budget_against_enumeration(seed):
+    """Before early_until the query keeps early_budget long-range keys, from
+    there on budget: each side against the plain enumeration with that budget."""
+    T = 72 + seed * 5
+    latk, idx = _random_index(20 + seed, T, p=2, N=8, C=3, iters=2)
+    rng = np.random.default_rng(200 + seed)
+    switch = T // 2
+    sp = O.SelectParams(budget=14, window=4, sinks=2, early_budget=5, early_until=switch)
+    for t in [0, 3, switch - 2, switch - 1, switch, switch + 1, T - 1]:
+        q = rng.integers(-5, 6, size=latk.shape[1])
+        b = 5 if t < switch else 14
+        assert O.select(idx, q, t, sp).tolist() == \
+            _brute_select(idx, latk, q, t, O.SelectParams(budget=b, window=4, sinks=2))
+
+
 def test_select_count_window_sinks_causal_nesting():
     T = 16384
     latk, idx = _random_index(7, T, p=4, N=256, C=16, iters=3, dim=8, lo=-20, hi=21)
@@ -192,15 +208,17 @@ def test_singleton_buckets_equal_exact_topk():
     for b in range(T // N):
         assert len({tuple(r) for r in latk[b * N:(b + 1) * N].tolist()}) == N
     idx = O.build_index(latk, T, O.IndexParams(1, N, N, 2))
-    sp = O.SelectParams(budget=37, window=16, sinks=3)
-    for t in [100, 250, 511]:
-        q = rng.integers(-100, 101, size=8)
-        keys = np.arange(sp.sinks, t - sp.window + 1)
-        sc = latk[keys] @ q
-        top = keys[np.lexsort((keys, -sc))][: sp.budget]
-        want = set(top.tolist()) | set(range(t - sp.window + 1, t + 1)) | set(range(sp.sinks))
-        assert O.select(idx, q, t, sp).tolist() == sorted(want)
-        assert O.dense_select(latk, q, t, sp).tolist() == sorted(want)
+    # the second setting keeps 9 long-range keys for queries before position 251
+    for sp, early in ((O.SelectParams(budget=37, window=16, sinks=3), {}),
+                      (O.SelectParams(37, 16, 3, 0, 9, 251), {100: 9, 250: 9})):
+        for t in [100, 250, 511]:
+            q = rng.integers(-100, 101, size=8)
+            keys = np.arange(sp.sinks, t - sp.window + 1)
+            sc = latk[keys] @ q
+            top = keys[np.lexsort((keys, -sc))][: early.get(t, 37)]
+            want = set(top.tolist()) | set(range(t - sp.window + 1, t + 1)) | set(range(sp.sinks))
+            assert O.select(idx, q, t, sp).tolist() == sorted(want)
+            assert O.dense_select(latk, q, t, sp).tolist() == sorted(want)
 
 
 def test_tree_with_full_branching_equals_flat():
