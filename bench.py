@@ -363,8 +363,11 @@ def cpu_baseline(res, workers_pool, n_sample=512):
                   f"{m} of {n} chunk queries and scaled to the chunk; prebuilt context index "
                   f"built untimed",
         "timed_s": t_update + t_sel + t_att,
+        # the timed step stores bf16, whose rounding alone may reach the unit
+        # roundoff 2^-8 of the largest output; the float32 output of the same
+        # kernel is held to 2e-3 by the parity tests
         "parity_sample": {"queries": m, "selections_bit_exact": same,
-                          "attn_bf16_normwise_err": err},
+                          "attn_bf16_normwise_err": err, "bf16_unit_roundoff": 2.0 ** -8},
     }
 
 
