@@ -337,3 +337,81 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, Hkv: int,
         w /= w.sum()
         out[h] = w @ V[:, g, :]
     return out
+
+
+def attend_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray, Hkv: int,
+               scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """attend() and, per head, the natural log of the softmax denominator
+    (log-sum-exp of the scaled logits over the selected rows): float64 [Hq]."""
+    Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    lse = np.zeros(Hq, dtype=np.float64)
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        logits = (K[:, g, :] @ q[h]) * scale
+        m = logits.max()
+        lse[h] = m + np.log(np.exp(logits - m).sum())
+    return attend(q, K, V, Hkv, scale), lse
+
+
+# --------------------------------------------------------------------------
+# backward of the sparse attention over stored selections ("Latent Sparse
+# Attention: un indice gerarchico per contesti lunghi", mauroscia.it, N-LSA
+# paragraph: training keeps the indices of the selected keys for the backward
+# pass).  The selection is discrete and fixed; gradients flow to Q, K and V
+# through the softmax attention only.  Per head h (KV head g), with
+# s_j = scale * k_j . q_h, p = softmax(s), o_h = sum_j p_j v_j and the
+# upstream gradient do_h:
+#   dv_j += p_j do_h
+#   dp_j  = do_h . v_j
+#   ds_j  = p_j (dp_j - sum_k p_k dp_k)
+#   dq_h  = scale * sum_j ds_j k_j
+#   dk_j += scale * ds_j q_h
+# --------------------------------------------------------------------------
+def attend_backward(q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, Hkv: int,
+                    scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of sum(dO * attend(q, K, V)) for one token.
+
+    q, dO: float64 [Hq][D]; K, V: float64 [n_sel][Hkv][D].  Returns
+    (dq [Hq][D], dK [n_sel][Hkv][D], dV [n_sel][Hkv][D]); a row listed twice
+    would get the sum of both entries' gradients.
+    """
+    Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dq = np.zeros_like(q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        logits = (K[:, g, :] @ q[h]) * scale
+        p = np.exp(logits - logits.max())
+        p /= p.sum()
+        dV[:, g, :] += np.outer(p, dO[h])
+        dp = V[:, g, :] @ dO[h]
+        ds = p * (dp - (p * dp).sum())
+        dq[h] = scale * (ds @ K[:, g, :])
+        dK[:, g, :] += scale * np.outer(ds, q[h])
+    return dq, dK, dV
+
+
+def sparse_attention_backward(Q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, dO: np.ndarray,
+                              rows: Sequence[np.ndarray], Hkv: int, scale: Optional[float] = None
+                              ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients for a batch of tokens: token i attends over cache rows rows[i].
+
+    Q, dO: float64 [n][Hq][D]; Kc, Vc: float64 [T][Hkv][D].  Returns
+    dQ [n][Hq][D] and dK, dV [T][Hkv][D], where a cache row's gradient is the
+    sum over every token that selected it (zero if none did).
+    """
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(Kc)
+    dV = np.zeros_like(Vc)
+    for i, r in enumerate(rows):
+        r = np.asarray(r, dtype=np.int64)
+        dq, dk, dv = attend_backward(Q[i], Kc[r], Vc[r], dO[i], Hkv, scale)
+        dQ[i] = dq
+        np.add.at(dK, r, dk)
+        np.add.at(dV, r, dv)
+    return dQ, dK, dV
