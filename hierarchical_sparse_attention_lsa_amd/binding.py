@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblsa_hip.so")
 
 c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
-OP_BUILD, OP_APPEND, OP_SELECT, OP_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE = range(7)
+OP_BUILD, OP_APPEND, OP_SELECT, OP_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE, OP_ATTN_BWD = range(8)
 
 
 class IndexParams(ctypes.Structure):
@@ -65,6 +65,12 @@ EXPORTS = {
     "lsa_sparse_attn_window": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                        ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                        c_vp, c_vp]),
+    "lsa_sparse_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
+                                    ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                    c_vp, c_vp, c_vp]),
+    "lsa_sparse_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
+                                    ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                    c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lsa_prefill_chunk": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64,
                                   ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams), c_vp,
                                   c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -288,6 +294,61 @@ def sparse_attn_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: t
                                         idx.shape[1], nq, qpos0, ctypes.byref(sp), ctypes.byref(ap),
                                         _ptr(out), _stream(stream)), "lsa_sparse_attn_window")
     return out
+
+
+def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                    cnt: torch.Tensor, qpos0: int, sp: SelectParams, ap: AttnParams,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Training forward: sparse_attn_window plus the log-sum-exp float32 [nq][Hq]."""
+    nq = q.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, torch.bfloat16, name)
+    _need(idx, torch.int32, "idx")
+    _need(cnt, torch.int32, "cnt", (nq,))
+    if out is None:
+        out = torch.empty((nq, ap.Hq, ap.D), dtype=torch.float32 if ap.out_f32 else torch.bfloat16,
+                          device=q.device)
+    if lse is None:
+        lse = torch.empty((nq, ap.Hq), dtype=torch.float32, device=q.device)
+    _need(lse, torch.float32, "lse", (nq, ap.Hq))
+    _check(lib().lsa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt),
+                                     idx.shape[1], nq, qpos0, ctypes.byref(sp), ctypes.byref(ap),
+                                     _ptr(out), _ptr(lse), _stream(stream)), "lsa_sparse_attn_fwd")
+    return out, lse
+
+
+def sparse_attn_bwd(index: "LsaIndex", q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    idx: torch.Tensor, cnt: torch.Tensor, qpos0: int, sp: SelectParams,
+                    ap: AttnParams, out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                    dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                    dv: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Gradients (float32) of the sparse attention for queries at positions
+    qpos0.. over rows that `index` selected with `sp`; returns (dq, dk, dv)."""
+    nq = q.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need(t, torch.bfloat16, name)
+    _need(idx, torch.int32, "idx")
+    _need(cnt, torch.int32, "cnt", (nq,))
+    _need(out, torch.float32 if ap.out_f32 else torch.bfloat16, "out", (nq, ap.Hq, ap.D))
+    _need(lse, torch.float32, "lse", (nq, ap.Hq))
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((nq, ap.Hq, ap.D), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((k.shape[0], ap.Hkv, ap.D), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((k.shape[0], ap.Hkv, ap.D), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(workspace_bytes(OP_ATTN_BWD, index.params, sp, ap, nq), 256),
+                         dtype=torch.uint8, device=dev)
+    _check(lib().lsa_sparse_attn_bwd(index.handle, _ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx),
+                                     _ptr(cnt), idx.shape[1], nq, qpos0, ctypes.byref(sp),
+                                     ctypes.byref(ap), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)),
+           "lsa_sparse_attn_bwd")
+    return dq, dk, dv
 
 
 def dense_select(latk: torch.Tensor, latq: torch.Tensor, qpos: torch.Tensor, sp: SelectParams,

@@ -257,6 +257,21 @@ constexpr int kDecodeSplits = 32;
 
 }  // namespace
 
+// Arguments shared by the window-sharing attention entry points.
+static int check_window_attn(int64_t kv_rows, int32_t max_sel, int32_t nq, int64_t qpos0,
+                      const lsa_select_params* sp, const lsa_attn_params* ap) {
+  if (int e = check_attn_params(ap)) return e;
+  if (!sp) return fail(LSA_E_ARG, "select params are NULL");
+  if (sp->window < 1 || sp->sinks < 0 || sp->budget < 0)
+    return fail(LSA_E_ARG, "bad select params (window %d, sinks %d, budget %d)", sp->window, sp->sinks,
+                sp->budget);
+  if (nq < 0 || kv_rows < 1 || qpos0 < 0) return fail(LSA_E_ARG, "bad nq / kv_rows / qpos0");
+  if (max_sel < max_sel_of(sp)) return fail(LSA_E_ARG, "max_sel %d < budget + window + sinks", max_sel);
+  if (qpos0 + nq > kv_rows) return fail(LSA_E_ARG, "query positions reach beyond kv_rows");
+  if (kv_rows > INT32_MAX - 64) return fail(LSA_E_ARG, "kv_rows beyond int32");
+  return LSA_OK;
+}
+
 extern "C" {
 
 const char* lsa_status_str(int status) {
@@ -348,6 +363,17 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
                select_dec_ws_bytes((int32_t)n, tmp.max_bkt);
       return LSA_OK;
     }
+    case LSA_OP_ATTN_BWD: {
+      if (int e = check_index_params(iprm)) return e;
+      if (int e = check_select_params(sprm, false)) return e;
+      if (int e = check_attn_params(aprm)) return e;
+      if (n > INT32_MAX) return fail(LSA_E_ARG, "n > INT32_MAX");
+      Index tmp;
+      memset(&tmp, 0, sizeof tmp);
+      layout(*iprm, &tmp);
+      *bytes = attn_bwd_ws_bytes((int32_t)n, *aprm, tmp.max_pool, tmp.max_bkt, sprm->budget);
+      return LSA_OK;
+    }
     default:
       return fail(LSA_E_ARG, "unknown op %d", op);
   }
@@ -422,19 +448,58 @@ int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, const uint1
                            int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
                            int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
                            const lsa_attn_params* ap, void* d_out, void* stream) {
-  if (int e = check_attn_params(ap)) return e;
-  if (!sp) return fail(LSA_E_ARG, "select params are NULL");
-  if (sp->window < 1 || sp->sinks < 0 || sp->budget < 0)
-    return fail(LSA_E_ARG, "bad select params (window %d, sinks %d, budget %d)", sp->window, sp->sinks,
-                sp->budget);
-  if (nq < 0 || kv_rows < 1 || qpos0 < 0) return fail(LSA_E_ARG, "bad nq / kv_rows / qpos0");
-  if (max_sel < max_sel_of(sp)) return fail(LSA_E_ARG, "max_sel %d < budget + window + sinks", max_sel);
-  if (qpos0 + nq > kv_rows) return fail(LSA_E_ARG, "query positions reach beyond kv_rows");
-  if (qpos0 + nq > INT32_MAX - 64) return fail(LSA_E_ARG, "query positions beyond int32");
+  if (int e = check_window_attn(kv_rows, max_sel, nq, qpos0, sp, ap)) return e;
   if (nq > 0 && (!d_q || !d_k || !d_v || !d_idx || !d_cnt || !d_out)) return fail(LSA_E_ARG, "NULL buffer");
   LSA_HIP(launch_attn_window(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp->window,
-                             sp->sinks, *ap, d_out, static_cast<hipStream_t>(stream)),
+                             sp->sinks, *ap, d_out, nullptr, static_cast<hipStream_t>(stream)),
           "attention");
+  return LSA_OK;
+}
+
+int lsa_sparse_attn_fwd(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                        int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                        int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
+                        const lsa_attn_params* ap, void* d_out, float* d_lse, void* stream) {
+  if (int e = check_window_attn(kv_rows, max_sel, nq, qpos0, sp, ap)) return e;
+  if (nq > 0 && (!d_q || !d_k || !d_v || !d_idx || !d_cnt || !d_out || !d_lse))
+    return fail(LSA_E_ARG, "NULL buffer");
+  LSA_HIP(launch_attn_window(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp->window,
+                             sp->sinks, *ap, d_out, d_lse, static_cast<hipStream_t>(stream)),
+          "attention");
+  return LSA_OK;
+}
+
+int lsa_sparse_attn_bwd(const lsa_index* hh, const uint16_t* d_q, const uint16_t* d_k,
+                        const uint16_t* d_v, int64_t kv_rows, const int32_t* d_idx,
+                        const int32_t* d_cnt, int32_t max_sel, int32_t nq, int64_t qpos0,
+                        const lsa_select_params* sp, const lsa_attn_params* ap, const void* d_out,
+                        const float* d_lse, const uint16_t* d_dout, float* d_dq, float* d_dk,
+                        float* d_dv, void* d_ws, size_t ws_bytes, void* stream) {
+  const Index* h = as_index(hh);
+  if (int e = check_index(h)) return e;
+  if (int e = check_select_params(sp, false)) return e;
+  if (int e = check_window_attn(kv_rows, max_sel, nq, qpos0, sp, ap)) return e;
+  if (sp->sinks > 64) return fail(LSA_E_UNSUPPORTED, "sinks %d > 64 in the backward", sp->sinks);
+  if (qpos0 + nq > h->T) return fail(LSA_E_ARG, "query positions reach beyond the index (T %lld)",
+                                     (long long)h->T);
+  if (nq == 0) return LSA_OK;
+  if (!d_q || !d_k || !d_v || !d_idx || !d_cnt || !d_out || !d_lse || !d_dout || !d_dq || !d_dk ||
+      !d_dv)
+    return fail(LSA_E_ARG, "NULL buffer");
+  const size_t need = attn_bwd_ws_bytes(nq, *ap, h->max_pool, h->max_bkt, sp->budget);
+  if (!d_ws || ws_bytes < need) return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+  const IdxView v = view_of(h);
+  BwdInputs in;
+  memset(&in, 0, sizeof in);
+  in.q = d_q; in.k = d_k; in.v = d_v; in.o = d_out; in.dout = d_dout; in.lse = d_lse;
+  in.kv_rows = kv_rows; in.idx = d_idx; in.cnt = d_cnt; in.max_sel = max_sel; in.nq = nq;
+  in.qpos0 = qpos0; in.window = sp->window; in.sinks = sp->sinks; in.budget = sp->budget;
+  in.dq = d_dq; in.dk = d_dk; in.dv = d_dv;
+  in.bcnt = v.bcnt; in.boff = v.boff; in.bmem = v.bmem;
+  in.n_bkt = v.n_bkt; in.pool = v.pool; in.n_pool = (int32_t)h->n_pool;
+  in.max_pool = h->max_pool; in.max_bkt = h->max_bkt;
+  in.ws = d_ws;
+  LSA_HIP(launch_attn_bwd(in, *ap, static_cast<hipStream_t>(stream)), "attention backward");
   return LSA_OK;
 }
 
@@ -475,7 +540,7 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
                    select_fast_ws_bytes((int32_t)n_chunk), s);
   if (rc != LSA_OK) return rc;
   LSA_HIP(launch_attn_window(d_q, d_k, d_v, kv_rows, idx, cnt, max_sel, (int32_t)n_chunk, t0,
-                             sp->window, sp->sinks, *ap, d_out, s),
+                             sp->window, sp->sinks, *ap, d_out, nullptr, s),
           "attention");
   return LSA_OK;
 }

@@ -58,6 +58,7 @@ struct AttnArgs {
   int64_t qpos0;
   int32_t window, sinks;
   int32_t qpw;               // queries per wave (16 / G)
+  float* lse;                // nullable [nq][Hq]: natural log-sum-exp of the scaled logits
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int nwg) {
@@ -377,10 +378,14 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   for (int v = 0; v < 4; ++v) {
     const int col = 4 * grp + v;
     const float lh = __shfl(l_run, col);
+    const float mh = __shfl(m_run, col);
     const int j = col / G, h = col % G;
     if (j >= nqw) continue;
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     const int64_t ob = ((int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h) * D;
+    // log-sum-exp: m_run and l_run are in the log2 domain of the scaled logits
+    if (a.lse && hl == 0) a.lse[(int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h] =
+        (mh + __log2f(lh)) * 0.6931471805599453f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float val = o[nb][v] * inv;
@@ -608,7 +613,8 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                               int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
-                              int32_t sinks, const lsa_attn_params& ap, void* out, hipStream_t s) {
+                              int32_t sinks, const lsa_attn_params& ap, void* out, float* lse,
+                              hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   AttnArgs a;
   memset(&a, 0, sizeof a);
@@ -621,6 +627,7 @@ hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16
   a.out = out;
   a.qpos0 = qpos0; a.window = window; a.sinks = sinks;
   a.qpw = 16 / a.G;
+  a.lse = lse;
   const size_t items = (size_t)((nq + a.qpw - 1) / a.qpw) * ap.Hkv;
   const unsigned grid = (unsigned)((items + AW - 1) / AW);
   const bool f32 = ap.out_f32 != 0;

@@ -131,6 +131,36 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                               int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
-                              int32_t sinks, const lsa_attn_params& ap, void* out, hipStream_t s);
+                              int32_t sinks, const lsa_attn_params& ap, void* out, float* lse,
+                              hipStream_t s);
+
+// Backward of the sparse attention (dQ, dK, dV) over rows the select wrote
+// for consecutive query positions qpos0.., with the index they came from.
+struct BwdInputs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* o;            // forward output, bf16 or float32 (attention params out_f32)
+  const uint16_t* dout;
+  const float* lse;         // [nq][Hq] natural log-sum-exp from the forward
+  int64_t kv_rows;
+  const int32_t* idx;
+  const int32_t* cnt;
+  int32_t max_sel, nq;
+  int64_t qpos0;
+  int32_t window, sinks, budget;
+  float* dq;                // [nq][Hq][D]
+  float* dk;                // [kv_rows][Hkv][D]
+  float* dv;
+  const int32_t* bcnt;
+  const int32_t* boff;
+  const int32_t* bmem;
+  int32_t n_bkt, pool, n_pool;
+  int64_t max_pool, max_bkt;  // index capacities (workspace layout)
+  void* ws;
+};
+size_t attn_bwd_ws_bytes(int32_t nq, const lsa_attn_params& ap, int64_t max_pool, int64_t max_bkt,
+                         int32_t budget);
+hipError_t launch_attn_bwd(const BwdInputs& in, const lsa_attn_params& ap, hipStream_t s);
 
 }  // namespace lsa

@@ -72,7 +72,8 @@ enum {
   LSA_OP_ATTN = 3,     /* n = queries */
   LSA_OP_PREFILL = 4,  /* n = chunk length */
   LSA_OP_DECODE = 5,   /* n = sequences */
-  LSA_OP_DENSE = 6     /* n = queries */
+  LSA_OP_DENSE = 6,    /* n = queries */
+  LSA_OP_ATTN_BWD = 7  /* n = queries; index, select and attention params */
 };
 
 /* Index shape.  dim must be 64.  pool >= 1.  block (pooled vectors per
@@ -200,6 +201,39 @@ LSA_API int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, con
                                    int32_t max_sel, int32_t nq, int64_t qpos0,
                                    const lsa_select_params* sp, const lsa_attn_params* ap,
                                    void* d_out, void* stream);
+
+/* Training forward: lsa_sparse_attn_window that also stores, per (query,
+ * head), the natural log of the softmax denominator over the query's
+ * selected keys, lse = log sum_j exp(scale * q . k_j): d_lse float32
+ * [nq][Hq].  The backward takes it to rebuild the probabilities. */
+LSA_API int lsa_sparse_attn_fwd(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                                int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                                int32_t max_sel, int32_t nq, int64_t qpos0,
+                                const lsa_select_params* sp, const lsa_attn_params* ap,
+                                void* d_out, float* d_lse, void* stream);
+
+/* Backward of the sparse attention over stored selections (the N-LSA
+ * paragraph of the mauroscia.it page: training keeps the selected key
+ * indices for the backward pass).  The selection is fixed; gradients flow
+ * through the softmax attention only.  Inputs are those of
+ * lsa_sparse_attn_fwd plus its outputs d_out (bf16, or float32 when
+ * ap->out_f32) and d_lse, and the upstream gradient d_dout bf16
+ * [nq][Hq][D].  The rows must be the ones lsa_select / lsa_prefill_chunk
+ * wrote for queries at positions qpos0 .. qpos0+nq-1 with index `h` in its
+ * current state and select params *sp (the backward finds each taken bucket
+ * in them: a run of long-range entries in one bucket, ending at the largest
+ * key taken).  Requires qpos0 + nq <= T of the index <= kv_rows and sinks <=
+ * 64.  Writes float32 d_dq [nq][Hq][D] and d_dk, d_dv [kv_rows][Hkv][D]
+ * (every row; zero for keys no query selected).  Workspace:
+ * lsa_workspace_bytes(LSA_OP_ATTN_BWD, .., nq).  Deterministic: every
+ * gradient is summed in a fixed order. */
+LSA_API int lsa_sparse_attn_bwd(const lsa_index* h, const uint16_t* d_q, const uint16_t* d_k,
+                                const uint16_t* d_v, int64_t kv_rows, const int32_t* d_idx,
+                                const int32_t* d_cnt, int32_t max_sel, int32_t nq, int64_t qpos0,
+                                const lsa_select_params* sp, const lsa_attn_params* ap,
+                                const void* d_out, const float* d_lse, const uint16_t* d_dout,
+                                float* d_dq, float* d_dk, float* d_dv, void* d_ws,
+                                size_t ws_bytes, void* stream);
 
 /* One prefill chunk: append the chunk's n_chunk latent keys, select for its
  * n_chunk queries (positions T_old .. T_old+n_chunk-1, scored against the

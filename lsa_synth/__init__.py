@@ -180,7 +180,7 @@ WORKLOADS = {
 }
 
 # stream ids
-S_MEANS, S_KCOMP, S_KNOISE, S_QCOMP, S_QNOISE, S_Q, S_K, S_V = range(8)
+S_MEANS, S_KCOMP, S_KNOISE, S_QCOMP, S_QNOISE, S_Q, S_K, S_V, S_DO = range(9)
 
 
 class Synth:
@@ -192,7 +192,7 @@ class Synth:
         # the Tree workload shares the Flat 10M data
         cfg = data_cfg if data_cfg is not None else (3 if wl.cfg_id == 5 else wl.cfg_id)
         self.cfg = cfg
-        self._keys = {s: _key_scalar(2026, cfg, s, seq) for s in range(8)}
+        self._keys = {s: _key_scalar(2026, cfg, s, seq) for s in range(9)}
         self._means = {}
 
     def key(self, stream: int) -> int:
@@ -257,9 +257,13 @@ class Synth:
     def v_rows(self, rows, device="cpu"):
         return self._bf16_rows(S_V, rows, self.wl.Hkv, self.wl.D, device)
 
+    def do_rows(self, rows, device="cpu"):
+        """Upstream gradient of the attention output (training), [len(rows)][Hq][D]."""
+        return self._bf16_rows(S_DO, rows, self.wl.Hq, self.wl.D, device)
+
     def fill_rows(self, which: str, out: torch.Tensor, t0: int, chunk: int = 1 << 16) -> None:
-        """Fill ``out`` ([n][H][D] bf16, any device) with rows t0.. of Q, K or V."""
-        stream = {"q": S_Q, "k": S_K, "v": S_V}[which]
+        """Fill ``out`` ([n][H][D] bf16, any device) with rows t0.. of Q, K, V or dO."""
+        stream = {"q": S_Q, "k": S_K, "v": S_V, "do": S_DO}[which]
         n, H, D = out.shape
         dev = out.device
         for a in range(0, n, chunk):

@@ -319,6 +319,19 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """x rounded to bfloat16 (round to nearest, ties to even), as float64:
+    the value a bf16 store of x holds.  Rounds x itself, not an intermediate
+    float32."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    m, e = np.frexp(x[nz])                  # x = m * 2^e, 0.5 <= |m| < 1
+    # 8 significant bits: scale m to [128, 256), round half to even
+    out[nz] = np.ldexp(np.round(m * 256.0), e - 8)
+    return out
+
+
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, Hkv: int,
            scale: Optional[float] = None) -> np.ndarray:
     """Softmax attention of one token over the selected rows.
@@ -370,12 +383,15 @@ def attend_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray, Hkv: int,
 #   dk_j += scale * ds_j q_h
 # --------------------------------------------------------------------------
 def attend_backward(q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, Hkv: int,
-                    scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                    scale: Optional[float] = None, o: Optional[np.ndarray] = None
+                    ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients of sum(dO * attend(q, K, V)) for one token.
 
     q, dO: float64 [Hq][D]; K, V: float64 [n_sel][Hkv][D].  Returns
     (dq [Hq][D], dK [n_sel][Hkv][D], dV [n_sel][Hkv][D]); a row listed twice
-    would get the sum of both entries' gradients.
+    would get the sum of both entries' gradients.  sum_k p_k dp_k equals
+    do_h . o_h; given ``o`` (the forward output as a caller stored it, e.g.
+    rounded to bf16) that dot product is taken from it instead.
     """
     Hq, D = q.shape
     if scale is None:
@@ -390,27 +406,31 @@ def attend_backward(q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray,
         p /= p.sum()
         dV[:, g, :] += np.outer(p, dO[h])
         dp = V[:, g, :] @ dO[h]
-        ds = p * (dp - (p * dp).sum())
+        dsum = (p * dp).sum() if o is None else float(dO[h] @ o[h])
+        ds = p * (dp - dsum)
         dq[h] = scale * (ds @ K[:, g, :])
         dK[:, g, :] += scale * np.outer(ds, q[h])
     return dq, dK, dV
 
 
 def sparse_attention_backward(Q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, dO: np.ndarray,
-                              rows: Sequence[np.ndarray], Hkv: int, scale: Optional[float] = None
+                              rows: Sequence[np.ndarray], Hkv: int, scale: Optional[float] = None,
+                              O: Optional[np.ndarray] = None
                               ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients for a batch of tokens: token i attends over cache rows rows[i].
 
     Q, dO: float64 [n][Hq][D]; Kc, Vc: float64 [T][Hkv][D].  Returns
     dQ [n][Hq][D] and dK, dV [T][Hkv][D], where a cache row's gradient is the
-    sum over every token that selected it (zero if none did).
+    sum over every token that selected it (zero if none did).  ``O``: the
+    stored forward outputs (see attend_backward's ``o``), or None.
     """
     dQ = np.zeros_like(Q)
     dK = np.zeros_like(Kc)
     dV = np.zeros_like(Vc)
     for i, r in enumerate(rows):
         r = np.asarray(r, dtype=np.int64)
-        dq, dk, dv = attend_backward(Q[i], Kc[r], Vc[r], dO[i], Hkv, scale)
+        dq, dk, dv = attend_backward(Q[i], Kc[r], Vc[r], dO[i], Hkv, scale,
+                                     None if O is None else O[i])
         dQ[i] = dq
         np.add.at(dK, r, dk)
         np.add.at(dV, r, dv)

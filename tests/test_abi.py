@@ -44,6 +44,10 @@ def test_host_validation_without_device():
     sp = L.SelectParams(4096, 512, 4, 0)
     ap = L.AttnParams(32, 8, 128, 0, 0.0)
     assert L.workspace_bytes(L.binding.OP_PREFILL, p, sp, ap, 32768) >= 32768 * 4612 * 4
+    # backward at a 128k training step: the (bucket -> queries) list alone
+    # needs a slot for every (query, taken bucket)
+    p128 = L.IndexParams(64, 4, 4096, 256, 4, 0, 0, 0, 2 ** 17)
+    assert L.workspace_bytes(L.binding.OP_ATTN_BWD, p128, sp, ap, 2 ** 17) >= 2 ** 17 * 2048 * 8
     bad = L.AttnParams(32, 8, 96, 0, 0.0)
     with pytest.raises(L.LsaError):
         L.workspace_bytes(L.binding.OP_DECODE, p, sp, bad, 8)

@@ -113,3 +113,26 @@ def test_lse_against_scipy():
         assert abs(lse[h] - logsumexp(0.4 * (K[:, g, :] @ q[h]))) <= 1e-12
     _, lse1 = O.attend_lse(q, K[:1], V[:1], 3, 0.4)
     assert np.allclose(lse1, [0.4 * K[0, h * 3 // 6] @ q[h] for h in range(6)], atol=1e-14)
+
+
+def test_stored_output_variant_equals_exact_when_given_the_exact_output():
+    q, K, V, dO = _rand(13, n_sel=20, Hq=4, Hkv=2, D=16)
+    o = O.attend(q, K, V, 2)
+    a = O.attend_backward(q, K, V, dO, 2)
+    b = O.attend_backward(q, K, V, dO, 2, o=o)
+    for x, y in zip(a, b):
+        assert np.abs(x - y).max() <= 1e-12 * max(1.0, np.abs(x).max())
+    # a perturbed stored output moves dq and dK, never dV
+    c = O.attend_backward(q, K, V, dO, 2, o=o + 1e-3)
+    assert np.abs(c[0] - a[0]).max() > 1e-6 and np.abs(c[1] - a[1]).max() > 1e-6
+    assert np.array_equal(c[2], a[2])
+
+
+def test_round_bf16_against_torch_on_float32_values():
+    rng = np.random.default_rng(17)
+    x = (rng.normal(size=200000) * 10.0 ** rng.uniform(-20, 20, 200000)).astype(np.float32)
+    x[:4] = [0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)]   # exact ties
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x.astype(np.float64)), want)
+    assert O.round_bf16(np.array([1.0 + 2 ** -8]))[0] == 1.0            # tie to even
+    assert O.round_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
