@@ -256,6 +256,75 @@ def bench_full_prefill(args, dev):
                          "max": float(t.max())}}
 
 
+def bench_train(args, dev, steps=3, warmup=1):
+    """One attention layer's training step at 128k context, every position a
+    query: index build over all keys, selection, forward with log-sum-exp,
+    backward (dQ, dK, dV) from a synthetic upstream gradient.  Phases are
+    timed with events on the stream the kernels run on."""
+    wl = S.WORKLOADS["train_128k"]
+    T = wl.T
+    log(f"[train] generating {wl.name}: T={T}, every position a query")
+    g, latk, K, V = gen_inputs(wl, dev)
+    pos = torch.arange(0, T, device=dev)
+    latq = g.latq_rows(pos, device=dev)
+    q = torch.empty((T, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    do = torch.empty_like(q)
+    g.fill_rows("q", q, 0)
+    g.fill_rows("do", do, 0)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
+    ix = L.LsaIndex(iparams(wl, T), dev)
+    qpos = pos.to(torch.int32)
+    idx = torch.empty((T, sp.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((T,), dtype=torch.int32, device=dev)
+    out = torch.empty((T, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, wl.Hq), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+    dk = torch.empty((T, wl.Hkv, wl.D), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    sel_ws = torch.empty(L.workspace_bytes(L.binding.OP_SELECT, ix.params, sp, None, T),
+                         dtype=torch.uint8, device=dev)
+    bwd_ws = torch.empty(L.workspace_bytes(L.binding.OP_ATTN_BWD, ix.params, sp, ap, T),
+                         dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def step():
+        ev[0].record()
+        ix.build(latk)
+        ev[1].record()
+        ix.select(latq, qpos, sp, idx=idx, cnt=cnt, ws=sel_ws)
+        ev[2].record()
+        L.sparse_attn_fwd(q, K, V, idx, cnt, 0, sp, ap, out=out, lse=lse)
+        ev[3].record()
+        L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do, dq=dq, dk=dk, dv=dv,
+                          ws=bwd_ws)
+        ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ph = np.zeros(4)
+    for _ in range(steps):
+        step()
+        torch.cuda.synchronize()
+        ph += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    ph /= steps
+    cnt_h = cnt.cpu().numpy()
+    fwd_bytes = attn_algorithmic_bytes(wl, 0, T, cnt_h)
+    total = float(ph.sum())
+    res = {"workload": wl.name, "context_tokens": T, "queries": T,
+           "ms_per_step": total, "tokens_per_s": T / (total * 1e-3),
+           "phases_ms": {"index_build": float(ph[0]), "select": float(ph[1]),
+                         "forward": float(ph[2]), "backward": float(ph[3])},
+           "forward_algorithmic_gbs": fwd_bytes / (ph[2] * 1e-3) / 1e9,
+           "forward_algorithmic_bytes": fwd_bytes,
+           "selected_keys_per_query": float(cnt_h.mean())}
+    log(f"[train] step {total:.1f} ms: build {ph[0]:.2f}, select {ph[1]:.2f}, forward {ph[2]:.2f}, "
+        f"backward {ph[3]:.2f} ms; forward {res['forward_algorithmic_gbs']:.0f} GB/s algorithmic")
+    return res
+
+
 def bench_decode(args, dev):
     wl = S.WORKLOADS["decode_1m"]
     cap = wl.T + wl.steps
@@ -474,6 +543,8 @@ def main():
                     help="one prefill step plus a 2 GiB calibration copy (for rocprofv3 runs)")
     ap.add_argument("--full-prefill", action="store_true",
                     help="the whole context chunk by chunk (index grown from empty); prints its own line")
+    ap.add_argument("--train", action="store_true",
+                    help="only the 128k training step (forward + backward of one layer)")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only the decode benchmark (for rocprofv3 kernel traces)")
     ap.add_argument("--summarize-decode", nargs=2, metavar=("STATS", "COMMAND"),
@@ -493,7 +564,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     workers_pool = None
-    if not args.no_cpu and not args.profile and not args.profile_decode and not args.full_prefill:
+    if not (args.no_cpu or args.profile or args.profile_decode or args.full_prefill or args.train):
         # forked before anything touches the GPU; the workers only run the CPU oracle
         import multiprocessing as mp
         workers_pool = mp.get_context("fork").Pool(min(16, os.cpu_count() or 1))
@@ -510,6 +581,12 @@ def main():
         print(json.dumps({"metric": "LSA layer whole-prefill time (all chunks, index grown chunk by chunk)",
                           "value": fp["total_s"], "unit": "s", "higher_is_better": False,
                           "n_gpus": 1, "data": "synthetic", "config": fp}), flush=True)
+        return
+    if args.train:
+        tr = bench_train(args, dev)
+        print(json.dumps({"metric": "LSA layer training step (fwd + bwd) tokens/s at 128k",
+                          "value": tr["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                          "data": "synthetic", "config": tr}), flush=True)
         return
     if args.profile_decode:
         d = bench_decode(args, dev)

@@ -73,6 +73,16 @@ __device__ __forceinline__ int xcd_remap(int b, int nwg) {
 // for key slot l % 16 (every lane of that slot passes the same r); bit v of
 // `vmask` says whether S^T[4*(l/16)+v][l%16] (key 4*(l/16)+v of the tile,
 // column l%16) takes part.  o / m_run / l_run: the column's state.
+constexpr float kLazy = 8.f;     // log2 headroom before the reference max moves
+
+// Sum of a column's partial softmax denominators over the four lanes that
+// hold it (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float finish_l(float l) {
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  return l;
+}
+
 template <int D>
 struct TileRegs {
   v8bf ka[D / 32];
@@ -125,7 +135,11 @@ __device__ __forceinline__ void tile_compute(const v8bf (&qb)[D / 32], const Til
     *reinterpret_cast<v4i*>(vl + key * VROW + ch * 16) = T.vr[i];
   }
 
-  // online softmax for column hl over keys 4*grp + v
+  // online softmax for column hl over keys 4*grp + v.  The reference max
+  // m_run moves only when a logit exceeds it by more than kLazy (log2
+  // units), so most tiles skip the cross-lane max and the rescale of the
+  // accumulators; probabilities stay below 2^kLazy.  l_run is this lane's
+  // partial sum (keys 4*grp + v); finish_l adds the four partials.
   float sv[4];
   float tmax = -INFINITY;
 #pragma unroll
@@ -133,17 +147,27 @@ __device__ __forceinline__ void tile_compute(const v8bf (&qb)[D / 32], const Til
     sv[v] = (vmask >> v) & 1u ? s[v] * scale_log2 : -INFINITY;
     tmax = fmaxf(tmax, sv[v]);
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float m_new = fmaxf(m_run, tmax);
-  const float alpha = exp2f(m_run - m_new);
-  float p[4], psum = 0.f;
+  if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazy) != 0) {      // wave-uniform
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+    // rescale the accumulators: o rows are columns 4*grp + v
 #pragma unroll
-  for (int v = 0; v < 4; ++v) { p[v] = exp2f(sv[v] - m_new); psum += p[v]; }
-  psum += __shfl_xor(psum, 16);
-  psum += __shfl_xor(psum, 32);
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
+    for (int v = 0; v < 4; ++v) {
+      const float av = __shfl(alpha, 4 * grp + v);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nb][v] *= av;
+    }
+  }
+  float p[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    p[v] = exp2f(sv[v] - m_run);
+    l_run += p[v];
+  }
 
   // P (A operand, rows = columns, k = keys 4*grp..+3) as bf16 hi + lo
   v4s phi, plo;
@@ -154,14 +178,6 @@ __device__ __forceinline__ void tile_compute(const v8bf (&qb)[D / 32], const Til
     phi[v] = (short)hb;
     plo[v] = (short)f32_to_bf16_bits(rem);
   }
-  // rescale the accumulators: o rows are columns 4*grp + v
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float av = __shfl(alpha, 4 * grp + v);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o[nb][v] *= av;
-  }
-
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -248,6 +264,7 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
     attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
   }
 
+  l_run = finish_l(l_run);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int h = 4 * grp + v;
@@ -374,6 +391,7 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
     }
   }
 
+  l_run = finish_l(l_run);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int col = 4 * grp + v;
@@ -506,6 +524,7 @@ __global__ void __launch_bounds__(AT) k_attn_dec(AttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) po[h * D + 16 * nb + hl] = o[nb][v];
   }
+  l_run = finish_l(l_run);
   if (grp == 0) {
     a.part_ml[pitem * 32 + 2 * hl] = m_run;
     a.part_ml[pitem * 32 + 2 * hl + 1] = l_run;

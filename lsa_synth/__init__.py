@@ -177,6 +177,8 @@ WORKLOADS = {
     "decode_1m": Workload("decode_1m", 4, T=M, ncomp=4096, chunk=0, nseq=8, steps=256),
     "tree_10m": Workload("tree_10m", 5, T=10 * M, ncomp=16384, tree_group=64,
                          tree_super=64, tree_iters=4, tree_top=32),
+    # one attention layer's training step at 128k context: every position is a query
+    "train_128k": Workload("train_128k", 6, T=M // 8, ncomp=1024, chunk=M // 8),
 }
 
 # stream ids
