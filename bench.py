@@ -530,6 +530,30 @@ def summarize_decode(args):
     print("\n".join(lines))
 
 
+def summarize_train(args):
+    """Training-step kernel table from a rocprofv3 --stats CSV of `bench.py --train`."""
+    import csv
+    stats_csv, command = args.summarize_train
+    wl = S.WORKLOADS["train_128k"]
+    stats = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics: LSA training step of one layer, T={wl.T}, every "
+             f"position a query (Hq={wl.Hq}, Hkv={wl.Hkv}, D={wl.D}, select "
+             f"{wl.budget}+{wl.window}+{wl.sinks})", "", f"Command: `{command}`", "",
+             "Each step: index build, select, forward with log-sum-exp (k_attn_win), backward "
+             "(k_bwd_dq, then k_bwd_dkv band / long range / sinks and the list kernels); "
+             "4 steps (1 warmup + 3 timed).", "",
+             "| kernel | calls | average ms | total ms |", "|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        if "lsa" not in r["Name"]:
+            continue
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e6:.3f} | "
+                     f"{float(r['TotalDurationNs'])/1e6:.2f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "train_128k_rocprof.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -549,6 +573,8 @@ def main():
                     help="only the decode benchmark (for rocprofv3 kernel traces)")
     ap.add_argument("--summarize-decode", nargs=2, metavar=("STATS", "COMMAND"),
                     help="write the decode kernel summary under profiles/ from a rocprofv3 stats CSV")
+    ap.add_argument("--summarize-train", nargs=2, metavar=("STATS", "COMMAND"),
+                    help="write the training-step kernel summary under profiles/ from a rocprofv3 stats CSV")
     ap.add_argument("--summarize", nargs=4, metavar=("STATS", "FETCH", "WRITE", "COMMAND"),
                     help="write profiles/ summaries from rocprofv3 CSV outputs")
     args = ap.parse_args()
@@ -557,6 +583,9 @@ def main():
         return
     if args.summarize_decode:
         summarize_decode(args)
+        return
+    if args.summarize_train:
+        summarize_train(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the LSA hot path here is built and timed on a "

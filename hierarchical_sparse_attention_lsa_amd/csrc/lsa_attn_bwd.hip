@@ -504,13 +504,18 @@ __global__ void __launch_bounds__(KW * 64, 2) k_bwd_dkv(BwdArgs a) {
     return c;
   };
 
-  // staged loads of one group: Q and dO chunks held in registers
-  v4i ld[NLD];
-  auto fetch = [&](int cg) {
+  // one group's loads, held in registers until the group is staged in LDS:
+  // Q and dO chunks, and (threads 0..15) the column's lse, dsum and key range
+  struct Grp {
+    v4i ld[NLD];
+    float l2, ds;
+    int lo, hi;
+  };
+  auto fetch = [&](Grp& R, int cg) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int c = tid + i * KW * 64;
-      ld[i] = v4i{0, 0, 0, 0};
+      R.ld[i] = v4i{0, 0, 0, 0};
       if (c < 2 * 16 * CH) {
         const int tsel = c / (16 * CH);
         const int rem = c % (16 * CH);
@@ -520,12 +525,28 @@ __global__ void __launch_bounds__(KW * 64, 2) k_bwd_dkv(BwdArgs a) {
           int jm;
           const int qi = query_of(cpos, jm);
           const int64_t e = ((int64_t)qi * a.Hq + (int64_t)g * G + col % G) * D + ch * 8;
-          ld[i] = *reinterpret_cast<const v4i*>((tsel ? a.dout : a.q) + e);
+          R.ld[i] = *reinterpret_cast<const v4i*>((tsel ? a.dout : a.q) + e);
         }
       }
     }
+    R.l2 = 0.f; R.ds = 0.f; R.lo = 1; R.hi = 0;      // empty key range
+    if (tid < 16) {
+      const int col = tid;
+      const int cpos = cg + col / G;
+      if (col / G < QPW && cpos < c1) {
+        int jm;
+        const int qi = query_of(cpos, jm);
+        const int64_t qh = (int64_t)qi * a.Hq + (int64_t)g * G + col % G;
+        R.l2 = a.lse[qh] * kLog2e;
+        R.ds = a.dsum[qh];
+        const int t = a.qpos0 + qi;
+        if (MODE == M_BAND) { R.lo = t - a.window + 1; R.hi = t; }
+        else if (MODE == M_SINK) { R.lo = 0; R.hi = min(a.sinks - 1, t - a.window); }
+        else { R.lo = a.sinks; R.hi = jm; }
+      }
+    }
   };
-  auto stash = [&](int cg) {
+  auto stash = [&](const Grp& R) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int c = tid + i * KW * 64;
@@ -533,38 +554,27 @@ __global__ void __launch_bounds__(KW * 64, 2) k_bwd_dkv(BwdArgs a) {
         const int tsel = c / (16 * CH);
         const int rem = c % (16 * CH);
         const int col = rem / CH, ch = rem % CH;
-        *reinterpret_cast<v4i*>((tsel ? s_d : s_q) + col * KROW + ch * 16) = ld[i];
+        *reinterpret_cast<v4i*>((tsel ? s_d : s_q) + col * KROW + ch * 16) = R.ld[i];
       }
     }
     if (tid < 16) {
-      const int col = tid;
-      const int cpos = cg + col / G;
-      float l2 = 0.f, ds = 0.f;
-      int lo = 1, hi = 0;             // empty mask
-      if (col / G < QPW && cpos < c1) {
-        int jm;
-        const int qi = query_of(cpos, jm);
-        const int64_t qh = (int64_t)qi * a.Hq + (int64_t)g * G + col % G;
-        l2 = a.lse[qh] * kLog2e;
-        ds = a.dsum[qh];
-        const int t = a.qpos0 + qi;
-        if (MODE == M_BAND) { lo = t - a.window + 1; hi = t; }
-        else if (MODE == M_SINK) { lo = 0; hi = min(a.sinks - 1, t - a.window); }
-        else { lo = a.sinks; hi = jm; }
-      }
-      s_lse[col] = l2;
-      s_dsum[col] = ds;
-      s_lo[col] = lo;
-      s_hi[col] = hi;
+      s_lse[tid] = R.l2;
+      s_dsum[tid] = R.ds;
+      s_lo[tid] = R.lo;
+      s_hi[tid] = R.hi;
     }
   };
 
-  if (c0 < c1) fetch(c0);
+  // two groups in flight ahead of the one being computed
+  Grp ra, rb;
+  if (c0 < c1) fetch(ra, c0);
+  if (c0 + QPW < c1) fetch(rb, c0 + QPW);
   for (int cg = c0; cg < c1; cg += QPW) {
     __syncthreads();                 // previous group's LDS reads are done
-    stash(cg);
+    stash(ra);
     __syncthreads();
-    if (cg + QPW < c1) fetch(cg + QPW);
+    ra = rb;
+    if (cg + 2 * QPW < c1) fetch(rb, cg + 2 * QPW);
 
     v8bf qa[NKK], da[NKK];
 #pragma unroll
