@@ -116,6 +116,10 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
 // Tree selection, one workgroup per query; workspace: select_tree_ws_bytes(nq)
 size_t select_tree_ws_bytes(int32_t nq);
 hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
+// Tree decode: query i is sequence i's new position on its own index (<= 16);
+// flags: nseq ints of workspace
+hipError_t launch_select_tree_multi(const IdxView* views, const int32_t* qpos, int32_t nseq,
+                                   const SelArgs& a, int32_t* flags, hipStream_t s);
 // decode: one query per sequence, each on its own index (max_bkt = bucket capacity)
 size_t select_dec_ws_bytes(int32_t nseq, int64_t max_bkt);
 hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t nseq,

@@ -354,10 +354,11 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   vs.cap = (int32_t)max_bkt;
   SelArgs b = a;
   b.nq = nseq;
-  if (tree || nmax > DT * PERT) return launch_select_multi(views, qpos, nseq, b, s);
   DecWs W;
   int32_t* flags;
   dec_layout(nseq, vs.cap, &W, &flags, ws);
+  if (tree) return launch_select_tree_multi(views, qpos, nseq, b, flags, s);
+  if (nmax > DT * PERT) return launch_select_multi(views, qpos, nseq, b, s);
   if (nmax > 0) {
     hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + 255) / 256), (unsigned)nseq), dim3(256), 0,
                        s, vs, b, W);

@@ -59,6 +59,7 @@ struct FastViews {                  // first kernel argument (read through the k
   int32_t qpos[16];
   int32_t nviews;
   int32_t slots_per_view;           // decode: query slots per sequence
+  int32_t view_per_query;           // Tree: query q uses view q at position qpos[q]
 };
 
 struct ListWs {
@@ -749,17 +750,24 @@ __device__ __forceinline__ void top_supers(const IdxView& V, const int (&qv)[16]
   }
 }
 
-__global__ void __launch_bounds__(RT, 4) k_tree_select(IdxView V, SelArgs A, int32_t* flags) {
+__global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, int32_t* flags) {
   __shared__ ResolveLds L;
   __shared__ long long s_tmp[SUPN];
   __shared__ int s_sup[TOPCAP];       // selected supers
   __shared__ int s_pre[TOPCAP + 1];   // candidates before selected super j
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int q = blockIdx.x;
-  const int t = max(0, A.qpos ? A.qpos[q] : A.qpos_base + q);
+  // one index for every query (prefill), or one per query (decode: each
+  // sequence's index and new position)
+  const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  const bool per_q = VS.view_per_query != 0;
+  const IdxView V = vsp->v[per_q ? q : 0];
+  const int t = max(0, per_q ? vsp->qpos[q] : (A.qpos ? A.qpos[q] : A.qpos_base + q));
   const int R = min(A.tree_top, V.n_sup);
   const int n_unc = V.n_bkt - V.covered;
-  bool ok = budget_at(A, t) > 0 && R >= 1 && R <= TOPCAP && V.n_sup <= SUPN;
+  // no super level yet (no complete group): every leaf is a candidate
+  const bool sup = V.n_sup > 0;
+  bool ok = budget_at(A, t) > 0 && (!sup || (R >= 1 && R <= TOPCAP)) && V.n_sup <= SUPN;
   if (tid == 0) { L.nc = 0; L.nt = 0; }
   int qv[16];
   {
@@ -770,7 +778,7 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(IdxView V, SelArgs A, int
       qv[4 * k] = x.x; qv[4 * k + 1] = x.y; qv[4 * k + 2] = x.z; qv[4 * k + 3] = x.w;
     }
   }
-  if (ok) {
+  if (ok && sup) {
     if (V.n_sup <= 1024) top_supers<1024>(V, qv, R, s_tmp, s_sup);
     else top_supers<SUPN>(V, qv, R, s_tmp, s_sup);
     __syncthreads();
@@ -793,7 +801,7 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(IdxView V, SelArgs A, int
     }
     __syncthreads();
   }
-  const int nsel = ok ? s_pre[TOPCAP] : 0;
+  const int nsel = ok && sup ? s_pre[TOPCAP] : 0;
   const int ncand = nsel + n_unc;
   ok = ok && ncand <= CPT * RT;
 
@@ -892,10 +900,36 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
 
 size_t select_tree_ws_bytes(int32_t nq) { return ((size_t)nq * sizeof(int32_t) + 255) / 256 * 256; }
 
+hipError_t launch_select_tree_multi(const IdxView* views, const int32_t* qpos, int32_t nseq,
+                                   const SelArgs& a, int32_t* flags, hipStream_t s) {
+  if (nseq <= 0) return hipSuccess;
+  if (nseq > 16) return hipErrorInvalidValue;
+  FastViews vs;
+  memset(&vs, 0, sizeof vs);
+  for (int i = 0; i < nseq; ++i) {
+    vs.v[i] = views[i];
+    vs.qpos[i] = qpos[i];
+  }
+  vs.nviews = nseq;
+  vs.view_per_query = 1;
+  SelArgs b = a;
+  b.nq = nseq;
+  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)nseq), dim3(RT), 0, s, vs, b, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // exact refinement for the flagged sequences; other workgroups exit at once
+  b.only = flags;
+  return launch_select_multi(views, qpos, nseq, b, s);
+}
+
 hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
   int32_t* flags = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)a.nq), dim3(RT), 0, s, v, a, flags);
+  FastViews vs;
+  memset(&vs, 0, sizeof vs);
+  vs.v[0] = v;
+  vs.nviews = 1;
+  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)a.nq), dim3(RT), 0, s, vs, a, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // exact refinement for the flagged queries; other workgroups exit at once
