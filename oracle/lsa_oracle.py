@@ -124,6 +124,13 @@ class IndexParams:
     tree_group: int = 0
     tree_super: int = 0
     tree_iters: int = 0
+    # third level (sysnote.net "What it changes": clusters are grouped into a
+    # hierarchy and a query walks it level by level): the super clusters of
+    # each complete run of ``tree2_group`` groups are clustered into
+    # ``tree2_super`` top nodes
+    tree2_group: int = 0
+    tree2_super: int = 0
+    tree2_iters: int = 0
 
 
 @dataclasses.dataclass
@@ -147,6 +154,9 @@ class Index:
     n_grp: int = 0
     sup_centroids: Optional[np.ndarray] = None   # int64 [n_sup][dim]
     sup_members: Optional[List[np.ndarray]] = None  # per super: ascending leaf ids
+    n_grp2: int = 0
+    top_centroids: Optional[np.ndarray] = None   # int64 [n_top][dim] (third level)
+    top_members: Optional[List[np.ndarray]] = None  # per top node: ascending super ids
 
     @property
     def n_bkt(self) -> int:
@@ -155,6 +165,10 @@ class Index:
     def covered_leaves(self) -> int:
         """Leaves with id < this value belong to a super cluster."""
         return self.n_grp * self.params.tree_group * self.params.buckets
+
+    def covered_supers(self) -> int:
+        """Super clusters with id < this value belong to a top node."""
+        return self.n_grp2 * self.params.tree2_group * self.params.tree_super
 
 
 def build_index(latk: np.ndarray, T: int, params: IndexParams,
@@ -211,6 +225,24 @@ def build_index(latk: np.ndarray, T: int, params: IndexParams,
                 sm.append(g * G * C + np.nonzero(a == c)[0].astype(np.int64))
         idx.sup_centroids = np.concatenate(sc, axis=0) if sc else np.zeros((0, dim), np.int64)
         idx.sup_members = sm
+        if params.tree2_group > 0:
+            G2, S2 = params.tree2_group, params.tree2_super
+            idx.n_grp2 = idx.n_grp // G2
+            tc, tm = [], []
+            for g2 in range(idx.n_grp2):
+                key = ("grp2", g2)
+                sups = idx.sup_centroids[g2 * G2 * S:(g2 + 1) * G2 * S]
+                if cache is not None and key in cache:
+                    mu, a = cache[key]
+                else:
+                    mu, a = kmeans(sups, S2, params.tree2_iters)
+                    if cache is not None:
+                        cache[key] = (mu, a)
+                tc.append(mu)
+                for c in range(S2):
+                    tm.append(g2 * G2 * S + np.nonzero(a == c)[0].astype(np.int64))
+            idx.top_centroids = np.concatenate(tc, axis=0) if tc else np.zeros((0, dim), np.int64)
+            idx.top_members = tm
     return idx
 
 
@@ -228,6 +260,7 @@ class SelectParams:
     # queries at t < early_until take early_budget long-range keys
     early_budget: int = 0
     early_until: int = 0
+    tree2_top: int = 0     # top nodes taken per query (third tree level)
 
     def budget_at(self, t: int) -> int:
         return self.early_budget if t < self.early_until else self.budget
@@ -255,12 +288,21 @@ def candidates(idx: Index, q: np.ndarray, sp: SelectParams) -> np.ndarray:
 
     Tree: the ``tree_top`` best super clusters by (score desc, id asc), the
     union of their leaf members, plus every leaf not covered by a super
-    cluster (blocks outside complete groups and the tail).
+    cluster (blocks outside complete groups and the tail).  With a third
+    level the super clusters ranked are only those under the ``tree2_top``
+    best top nodes, plus every super cluster not under a top node.
     """
     if idx.params.tree_group <= 0:
         return np.arange(idx.n_bkt, dtype=np.int64)
-    ss = scores(idx.sup_centroids, q)
-    order = np.lexsort((np.arange(len(ss)), -ss))
+    sup_ids = np.arange(idx.sup_centroids.shape[0], dtype=np.int64)
+    if idx.params.tree2_group > 0:
+        ts = scores(idx.top_centroids, q)
+        top2 = np.lexsort((np.arange(len(ts)), -ts))[: sp.tree2_top]
+        sparts = [idx.top_members[n] for n in top2]
+        sparts.append(np.arange(idx.covered_supers(), len(sup_ids), dtype=np.int64))
+        sup_ids = np.sort(np.concatenate(sparts))
+    ss = scores(idx.sup_centroids[sup_ids], q)
+    order = sup_ids[np.lexsort((sup_ids, -ss))]
     top = order[: sp.tree_top]
     parts = [idx.sup_members[s] for s in top]
     parts.append(np.arange(idx.covered_leaves(), idx.n_bkt, dtype=np.int64))

@@ -261,6 +261,68 @@ def test_tree_candidates_against_brute_force():
         assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
 
 
+def _tree3(seed):
+    # 10 full blocks of 16 pooled vectors + a tail; groups of 2 blocks (3 supers
+    # each), top groups of 2 groups (2 top nodes each): 2 complete top groups,
+    # group 4 outside them
+    T = 4 * 16 * 10 + 37
+    latk = np.random.default_rng(seed).integers(-30, 31, size=(T, 6))
+    prm = O.IndexParams(4, 16, 4, 2, 2, 3, 2, 2, 2, 3)
+    return T, latk, O.build_index(latk, T, prm)
+
+
+def test_tree3_top_level_partitions_and_means():
+    T, latk, tree = _tree3(21)
+    assert tree.n_grp == 5 and tree.n_grp2 == 2 and tree.top_centroids.shape[0] == 4
+    assert tree.covered_supers() == 12
+    cov = np.sort(np.concatenate(tree.top_members))
+    assert cov.tolist() == list(range(12))
+    # after the last update every non-empty node's centroid is the rounded
+    # (half-even) mean of the super centroids assigned to it
+    for n, m in enumerate(tree.top_members):
+        if len(m):
+            assert tree.top_centroids[n].tolist() == _frac_mean(tree.sup_centroids[m].tolist())
+
+
+def test_tree3_full_top_branching_equals_two_levels():
+    T, latk, tree3 = _tree3(22)
+    tree2 = O.build_index(latk, T, O.IndexParams(4, 16, 4, 2, 2, 3, 2))
+    assert np.array_equal(tree2.sup_centroids, tree3.sup_centroids)
+    rng = np.random.default_rng(23)
+    for R in (1, 3, 7):
+        for _ in range(4):
+            q = rng.integers(-30, 31, size=6)
+            t = int(rng.integers(0, T))
+            sp2 = O.SelectParams(budget=40, window=8, sinks=2, tree_top=R)
+            sp3 = O.SelectParams(budget=40, window=8, sinks=2, tree_top=R, tree2_top=4)
+            assert np.array_equal(O.select(tree2, q, t, sp2), O.select(tree3, q, t, sp3))
+
+
+def test_tree3_candidates_against_brute_force():
+    T, latk, tree = _tree3(24)
+    rng = np.random.default_rng(25)
+
+    def dot(a, b):
+        return sum(int(x) * int(y) for x, y in zip(a, b))
+
+    for R2, R in ((1, 1), (1, 3), (2, 2), (3, 5)):
+        q = rng.integers(-30, 31, size=6)
+        tops = sorted((-dot(q, m), i) for i, m in enumerate(tree.top_centroids))[:R2]
+        sups = set()
+        for _, n in tops:
+            sups |= set(tree.top_members[n].tolist())
+        sups |= set(range(tree.covered_supers(), len(tree.sup_centroids)))
+        best = sorted((-dot(q, tree.sup_centroids[s]), s) for s in sups)[:R]
+        want = set()
+        for _, s in best:
+            want |= set(tree.sup_members[s].tolist())
+        want |= set(range(tree.covered_leaves(), tree.n_bkt))
+        sp = O.SelectParams(budget=30, window=8, sinks=2, tree_top=R, tree2_top=R2)
+        assert O.candidates(tree, q, sp).tolist() == sorted(want)
+        t = T - 1 - int(rng.integers(0, 100))
+        assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
+
+
 def test_index_is_prefix_function():
     """The index over keys [0, T') depends only on those keys (cache-consistent)."""
     latk = np.random.default_rng(15).integers(-40, 41, size=(3000, 4))
