@@ -62,7 +62,8 @@ def gen_inputs(wl, dev, seq=0, T=None):
 
 def iparams(wl, cap):
     return L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group,
-                         wl.tree_super, wl.tree_iters, cap)
+                         wl.tree_super, wl.tree_iters, cap, wl.tree2_group, wl.tree2_super,
+                         wl.tree2_iters)
 
 
 def attn_algorithmic_bytes(wl, t0, n, cnt: np.ndarray) -> float:
@@ -97,7 +98,7 @@ def bench_prefill(args, dev):
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - tg:.1f}s")
 
-    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, 0, 0, wl.tree2_top)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
     ix = L.LsaIndex(iparams(wl, wl.T), dev)
 
@@ -559,7 +560,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="flat_10m", choices=["flat_10m", "flat_1m", "tree_10m"])
+    ap.add_argument("--config", default="flat_10m", choices=["flat_10m", "flat_1m", "tree_10m", "tree3_10m"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -677,7 +678,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "context_tokens": wl.T, "chunk_queries": wl.chunk,
                    "index": f"Flat p={wl.pool} blocks={wl.block} buckets={wl.buckets} iters={wl.iters}"
-                   + (f" tree G={wl.tree_group} S={wl.tree_super} R={wl.tree_top}" if wl.tree_group else ""),
+                   + (f" tree G={wl.tree_group} S={wl.tree_super} R={wl.tree_top}" if wl.tree_group else "")
+                   + (f" top G2={wl.tree2_group} S2={wl.tree2_super} R2={wl.tree2_top}"
+                      if wl.tree2_group else ""),
                    "select": f"{wl.budget}+{wl.window}+{wl.sinks}",
                    "attention": f"GQA {wl.Hq}/{wl.Hkv} D={wl.D} bf16"},
         "roofline": {"kernel": f"{ATTN_KERNEL} (sparse GQA attention, shared windows)", "bound": "hbm",

@@ -24,12 +24,13 @@ OP_BUILD, OP_APPEND, OP_SELECT, OP_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE, OP_ATT
 class IndexParams(ctypes.Structure):
     _fields_ = [("dim", c_i32), ("pool", c_i32), ("block", c_i32), ("buckets", c_i32),
                 ("iters", c_i32), ("tree_group", c_i32), ("tree_super", c_i32),
-                ("tree_iters", c_i32), ("max_tokens", c_i64)]
+                ("tree_iters", c_i32), ("max_tokens", c_i64), ("tree2_group", c_i32),
+                ("tree2_super", c_i32), ("tree2_iters", c_i32)]
 
 
 class SelectParams(ctypes.Structure):
     _fields_ = [("budget", c_i32), ("window", c_i32), ("sinks", c_i32), ("tree_top", c_i32),
-                ("early_budget", c_i32), ("early_until", c_i32)]
+                ("early_budget", c_i32), ("early_until", c_i32), ("tree2_top", c_i32)]
 
     @property
     def max_sel(self) -> int:
@@ -44,7 +45,8 @@ class IndexInfo(ctypes.Structure):
     _fields_ = [(n, c_i64) for n in (
         "T", "n_pool", "n_full", "n_bkt", "n_grp", "n_sup",
         "off_pooled", "off_cent", "off_bcnt", "off_boff", "off_bmem", "off_bfirst", "off_blast",
-        "off_scent", "off_scnt", "off_soff", "off_smem", "arena_bytes")]
+        "off_scent", "off_scnt", "off_soff", "off_smem", "arena_bytes",
+        "n_grp2", "n_top", "off_tcent", "off_tcnt", "off_toff", "off_tmem")]
 
 
 EXPORTS = {
@@ -206,6 +208,11 @@ class LsaIndex:
             "scnt": view(i.off_scnt, i.n_sup, torch.int32),
             "soff": view(i.off_soff, i.n_sup, torch.int32),
             "smem": view(i.off_smem, nsm, torch.int32),
+            "tcent": view(i.off_tcent, i.n_top, torch.int8, 64),
+            "tcnt": view(i.off_tcnt, i.n_top, torch.int32),
+            "toff": view(i.off_toff, i.n_top, torch.int32),
+            "tmem": view(i.off_tmem, i.n_grp2 * self.params.tree2_group * self.params.tree_super,
+                         torch.int32),
         }
 
     def select(self, latq: torch.Tensor, qpos: torch.Tensor, sp: SelectParams,

@@ -61,6 +61,18 @@ int check_index_params(const lsa_index_params* p) {
                   p->tree_super);
     if (p->tree_iters < 1) return fail(LSA_E_ARG, "tree_iters %d < 1", p->tree_iters);
   }
+  if (p->tree2_group < 0) return fail(LSA_E_ARG, "tree2_group %d < 0", p->tree2_group);
+  if (p->tree2_group > 0) {
+    if (p->tree_group <= 0) return fail(LSA_E_ARG, "a third Tree level needs tree_group > 0");
+    const int64_t n = (int64_t)p->tree2_group * p->tree_super;
+    if (n > 16384 || n % 64)
+      return fail(LSA_E_UNSUPPORTED, "tree2_group*tree_super = %lld: need a multiple of 64 <= 16384",
+                  (long long)n);
+    if (p->tree2_super < 16 || p->tree2_super > 256 || p->tree2_super % 16 || p->tree2_super > n)
+      return fail(LSA_E_UNSUPPORTED, "tree2_super %d: need a multiple of 16 in [16, 256]",
+                  p->tree2_super);
+    if (p->tree2_iters < 1) return fail(LSA_E_ARG, "tree2_iters %d < 1", p->tree2_iters);
+  }
   if (p->max_tokens < 0 || p->max_tokens > INT32_MAX - 64)
     return fail(LSA_E_ARG, "max_tokens %lld out of range", (long long)p->max_tokens);
   return LSA_OK;
@@ -74,6 +86,8 @@ void layout(const lsa_index_params& p, Index* h) {
   h->max_grp = p.tree_group > 0 ? h->max_full / p.tree_group : 0;
   h->max_sup = h->max_grp * p.tree_super;
   h->max_smem = h->max_grp * p.tree_group * p.buckets;
+  h->max_grp2 = p.tree2_group > 0 ? h->max_grp / p.tree2_group : 0;
+  h->max_top = h->max_grp2 * p.tree2_super;
   int64_t o = 0;
   h->off_pooled = o; o = align_up(o + h->max_pool * kDim);
   h->off_cent = o;   o = align_up(o + h->max_bkt * kDim);
@@ -88,11 +102,20 @@ void layout(const lsa_index_params& p, Index* h) {
   h->off_smem = o;   o = align_up(o + h->max_smem * 4);
   h->off_leafsup = o; o = align_up(o + (p.tree_group > 0 ? h->max_bkt * 4 : 0));
   h->off_pend = o;   o = align_up(o + 2 * (int64_t)p.pool * kDim);
+  h->off_tcent = o;  o = align_up(o + h->max_top * kDim);
+  h->off_tcnt = o;   o = align_up(o + h->max_top * 4);
+  h->off_toff = o;   o = align_up(o + h->max_top * 4);
+  h->off_tmem = o;   o = align_up(o + h->max_grp2 * p.tree2_group * p.tree_super * 4);
+  h->off_suptop = o; o = align_up(o + (p.tree2_group > 0 ? h->max_sup * 4 : 0));
   {
     size_t km = kmeans_scratch_bytes(p.block, p.buckets);
     if (p.tree_group > 0) {
       const size_t kt = kmeans_scratch_bytes(p.tree_group * p.buckets, p.tree_super);
       km = km > kt ? km : kt;
+    }
+    if (p.tree2_group > 0) {
+      const size_t k2 = kmeans_scratch_bytes(p.tree2_group * p.tree_super, p.tree2_super);
+      km = km > k2 ? km : k2;
     }
     h->kmws_bytes = (int64_t)km;
   }
@@ -109,8 +132,9 @@ int check_index(const Index* h) {
   return LSA_OK;
 }
 
-int check_select_params(const lsa_select_params* sp, bool tree) {
+int check_select_params(const lsa_select_params* sp, bool tree, bool tree3 = false) {
   if (!sp) return fail(LSA_E_ARG, "select params are NULL");
+  if (tree3 && sp->tree2_top < 1) return fail(LSA_E_ARG, "tree2_top %d < 1", sp->tree2_top);
   if (sp->budget < 0 || sp->budget > 4096)
     return fail(LSA_E_UNSUPPORTED, "budget %d not in [0, 4096]", sp->budget);
   if (sp->window < 1 || sp->window > (1 << 20)) return fail(LSA_E_ARG, "window %d not in [1, 2^20]", sp->window);
@@ -154,6 +178,15 @@ IdxView view_of(const Index* h) {
     v.soff = h->at<int32_t>(h->off_soff);
     v.smem = h->at<int32_t>(h->off_smem);
     v.covered = (int32_t)(h->n_grp * h->prm.tree_group * h->prm.buckets);
+    if (h->prm.tree2_group > 0 && h->n_grp2 > 0) {
+      v.n_top = (int32_t)(h->n_grp2 * h->prm.tree2_super);
+      v.covered_sup = (int32_t)(h->n_grp2 * h->prm.tree2_group * h->prm.tree_super);
+      v.tcent = h->at<int8_t>(h->off_tcent);
+      v.tcnt = h->at<int32_t>(h->off_tcnt);
+      v.toff = h->at<int32_t>(h->off_toff);
+      v.tmem = h->at<int32_t>(h->off_tmem);
+      v.suptop = h->at<int32_t>(h->off_suptop);
+    }
   }
   return v;
 }
@@ -167,6 +200,15 @@ hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
+}
+
+// Leaf -> super and super -> top-node maps start at -1 ("not covered"):
+// entries are written when their group (top group) is clustered.
+hipError_t reset_tree_maps(Index* h, hipStream_t s) {
+  hipError_t e = fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s);
+  if (e == hipSuccess && h->prm.tree2_group > 0)
+    e = fill_i32(h->at<int32_t>(h->off_suptop), h->max_sup, -1, s);
+  return e;
 }
 
 // Append n latent rows (device) to the index.  Shapes come from host counters.
@@ -223,10 +265,28 @@ int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
               "tree kmeans");
     }
   }
+  int64_t ng2_new = h->n_grp2;
+  if (P.tree2_group > 0) {
+    const int G2 = P.tree2_group, S = P.tree_super, S2 = P.tree2_super;
+    ng2_new = ng_new / G2;
+    if (ng2_new > h->n_grp2) {
+      const int64_t g2 = h->n_grp2;
+      const int64_t NS = (int64_t)G2 * S;
+      LSA_HIP(launch_kmeans(h->at<int8_t>(h->off_scent) + g2 * NS * kDim, (int32_t)NS, S2,
+                            P.tree2_iters, (int32_t)(ng2_new - g2), g2 * NS,
+                            h->at<int8_t>(h->off_tcent) + g2 * S2 * kDim,
+                            h->at<int32_t>(h->off_tcnt) + g2 * S2, h->at<int32_t>(h->off_toff) + g2 * S2,
+                            h->at<int32_t>(h->off_tmem) + g2 * NS, nullptr, nullptr,
+                            h->at<int32_t>(h->off_suptop), (int32_t)(g2 * S2),
+                            h->at<char>(h->off_kmws), (size_t)h->kmws_bytes, s),
+              "top-level kmeans");
+    }
+  }
   h->T += n;
   h->n_pool = n_pool;
   h->n_full = nf_new;
   h->n_grp = ng_new;
+  h->n_grp2 = ng2_new;
   h->pend_slot ^= 1;
   return LSA_OK;
 }
@@ -240,7 +300,7 @@ int select_impl(const Index* h, const int8_t* latq, const int32_t* qpos, int32_t
   SelArgs a;
   a.latq = latq; a.qpos = qpos; a.qpos_base = qpos_base; a.nq = nq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
-  a.early_budget = sp->early_budget; a.early_until = sp->early_until;
+  a.early_budget = sp->early_budget; a.early_until = sp->early_until; a.tree2_top = sp->tree2_top;
   a.max_sel = max_sel_of(sp);
   a.idx = idx; a.cnt = cnt; a.only = nullptr;
   if (!v.leafsup && nq >= kFastSelectMinQ && ws && ws_bytes >= select_fast_ws_bytes(nq)) {
@@ -330,6 +390,9 @@ int lsa_index_get_info(const lsa_index* hh, lsa_index_info* out) {
   out->off_blast = h->off_blast; out->off_scent = h->off_scent; out->off_scnt = h->off_scnt;
   out->off_soff = h->off_soff; out->off_smem = h->off_smem;
   out->arena_bytes = h->used_bytes;
+  out->n_grp2 = h->n_grp2; out->n_top = h->n_grp2 * h->prm.tree2_super;
+  out->off_tcent = h->off_tcent; out->off_tcnt = h->off_tcnt; out->off_toff = h->off_toff;
+  out->off_tmem = h->off_tmem;
   return LSA_OK;
 }
 
@@ -391,9 +454,9 @@ int lsa_build_index(lsa_index* hh, const int8_t* d_latk, int64_t T, void* d_ws, 
                 (long long)h->prm.max_tokens);
   hipStream_t s = static_cast<hipStream_t>(stream);
   Index saved = *h;
-  h->T = 0; h->n_pool = 0; h->n_full = 0; h->n_grp = 0; h->pend_slot = 0;
+  h->T = 0; h->n_pool = 0; h->n_full = 0; h->n_grp = 0; h->n_grp2 = 0; h->pend_slot = 0;
   if (h->prm.tree_group > 0) {
-    hipError_t e = fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s);
+    hipError_t e = reset_tree_maps(h, s);
     if (e != hipSuccess) { *h = saved; return hip_fail(e, "fill"); }
   }
   int rc = append_impl(h, d_latk, T, s);
@@ -409,7 +472,7 @@ int lsa_append_keys(lsa_index* hh, const int8_t* d_latk_new, int64_t n, void* d_
   if (n < 0) return fail(LSA_E_ARG, "n < 0");
   if (n > 0 && !d_latk_new) return fail(LSA_E_ARG, "latents are NULL");
   if (h->T == 0 && h->prm.tree_group > 0) {
-    hipError_t e = fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, static_cast<hipStream_t>(stream));
+    hipError_t e = reset_tree_maps(h, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fill");
   }
   Index saved = *h;
@@ -423,7 +486,7 @@ int lsa_select(const lsa_index* hh, const int8_t* d_latq, const int32_t* d_qpos,
                size_t ws_bytes, void* stream) {
   const Index* h = as_index(hh);
   if (int e = check_index(h)) return e;
-  if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
+  if (int e = check_select_params(sp, h->prm.tree_group > 0, h->prm.tree2_group > 0)) return e;
   if (nq < 0) return fail(LSA_E_ARG, "nq < 0");
   if (nq > 0 && (!d_latq || !d_qpos || !d_idx || !d_cnt)) return fail(LSA_E_ARG, "NULL buffer");
   return select_impl(h, d_latq, d_qpos, 0, nq, sp, d_idx, d_cnt, d_ws, ws_bytes,
@@ -510,7 +573,7 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
                       int32_t* d_cnt_opt, void* d_ws, size_t ws_bytes, void* stream) {
   Index* h = as_index(hh);
   if (int e = check_index(h)) return e;
-  if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
+  if (int e = check_select_params(sp, h->prm.tree_group > 0, h->prm.tree2_group > 0)) return e;
   if (int e = check_attn_params(ap)) return e;
   if (n_chunk < 0 || n_chunk > INT32_MAX / 2) return fail(LSA_E_ARG, "bad n_chunk");
   if (n_chunk == 0) return LSA_OK;
@@ -531,7 +594,7 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t t0 = h->T;
   if (h->T == 0 && h->prm.tree_group > 0) {
-    LSA_HIP(fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s), "fill");
+    LSA_HIP(reset_tree_maps(h, s), "fill");
   }
   Index saved = *h;
   int rc = append_impl(h, d_latk_chunk, n_chunk, s);
@@ -558,7 +621,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   for (int i = 0; i < nseq; ++i) {
     const Index* h = as_index(hs[i]);
     if (int e = check_index(h)) return e;
-    if (int e = check_select_params(sp, h->prm.tree_group > 0)) return e;
+    if (int e = check_select_params(sp, h->prm.tree_group > 0, h->prm.tree2_group > 0)) return e;
     if (memcmp(&h->prm, &h0->prm, sizeof h->prm) != 0)
       return fail(LSA_E_ARG, "sequence %d has different index params", i);
     if (h->T + 1 > h->prm.max_tokens) return fail(LSA_E_CAPACITY, "sequence %d is full", i);
@@ -598,7 +661,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
     const bool completes_group = np + 1 == p;
     const bool completes_block = completes_group && (h->n_pool + 1) % N == 0;
     if (h->T == 0 && h->prm.tree_group > 0)
-      LSA_HIP(fill_i32(h->at<int32_t>(h->off_leafsup), h->max_bkt, -1, s), "fill");
+      LSA_HIP(reset_tree_maps(h, s), "fill");
     if (completes_block) {
       Index saved = *h;
       int rc = append_impl(h, d_latk_new + (int64_t)i * kDim, 1, s);
@@ -631,7 +694,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   memset(&a, 0, sizeof a);
   a.latq = d_latq; a.qpos = nullptr; a.qpos_base = 0; a.nq = nseq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
-  a.early_budget = sp->early_budget; a.early_until = sp->early_until;
+  a.early_budget = sp->early_budget; a.early_until = sp->early_until; a.tree2_top = sp->tree2_top;
   a.max_sel = max_sel; a.idx = idx; a.cnt = cnt; a.only = nullptr;
   LSA_HIP(launch_select_dec(views, qpos, nseq, h0->max_bkt, a, selws, s), "decode select");
 
@@ -658,7 +721,7 @@ int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, cons
   SelArgs a;
   a.latq = d_latq; a.qpos = d_qpos; a.qpos_base = 0; a.nq = nq;
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = 0;
-  a.early_budget = sp->early_budget; a.early_until = sp->early_until;
+  a.early_budget = sp->early_budget; a.early_until = sp->early_until; a.tree2_top = sp->tree2_top;
   a.max_sel = max_sel_of(sp);
   a.idx = d_idx; a.cnt = d_cnt; a.only = nullptr;
   LSA_HIP(launch_select(v, a, nullptr, static_cast<hipStream_t>(stream)), "dense select");

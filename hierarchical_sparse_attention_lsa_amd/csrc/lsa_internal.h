@@ -21,12 +21,14 @@ struct Index {
   int64_t n_pool;   // complete pooled groups = T / pool
   int64_t n_full;   // complete blocks
   int64_t n_grp;    // complete Tree groups
+  int64_t n_grp2;   // complete runs of tree2_group groups (third level)
   int32_t pend_slot;  // which of the two pending-latent slots is live
   // capacities
-  int64_t max_pool, max_full, max_bkt, max_grp, max_sup, max_smem;
+  int64_t max_pool, max_full, max_bkt, max_grp, max_sup, max_smem, max_grp2, max_top;
   // arena byte offsets
   int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast;
   int64_t off_scent, off_scnt, off_soff, off_smem, off_leafsup, off_pend;
+  int64_t off_tcent, off_tcnt, off_toff, off_tmem, off_suptop;
   int64_t off_kmws, kmws_bytes;   // k-means scratch (few-block clustering)
   int64_t used_bytes;
 
@@ -54,6 +56,14 @@ struct IdxView {
   const int32_t* soff;    // first leaf slot in smem
   const int32_t* smem;    // leaf ids grouped by super cluster
   int32_t covered;        // leaves inside complete groups (n_grp * group * buckets)
+  // third level (n_top = 0: none)
+  int32_t n_top;
+  int32_t covered_sup;    // supers inside complete top groups (n_grp2 * group2 * tree_super)
+  const int8_t* tcent;    // [n_top][64]
+  const int32_t* tcnt;    // supers per top node
+  const int32_t* toff;    // first super slot in tmem
+  const int32_t* tmem;    // super ids grouped by top node
+  const int32_t* suptop;  // super -> top node id, or -1
 };
 
 struct SelArgs {
@@ -63,6 +73,7 @@ struct SelArgs {
   int32_t nq;
   int32_t budget, window, sinks, tree_top;
   int32_t early_budget, early_until;   // queries at t < early_until take early_budget
+  int32_t tree2_top;                   // top nodes walked into (third Tree level)
   int32_t max_sel;
   int32_t* idx;           // [nq][max_sel]
   int32_t* cnt;           // [nq]

@@ -150,14 +150,47 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
     for (int e = tid; e < QT * MAXSUPW; e += ST) (&S.supmask[0][0])[e] = 0u;
   __syncthreads();
   if (TREE) {
-    // candidate super clusters: the tree_top best by (score desc, id asc); one wave per query
+    // candidate super clusters: the tree_top best by (score desc, id asc); one wave per query.
+    // With a third level only the supers under the tree2_top best top nodes, and
+    // those under no top node, are ranked (the top-node bits sit in the same
+    // mask words first).
     const int nsp = 1 << (32 - __clz(max(V.n_sup, 2) - 1));
+    const int ntp = 1 << (32 - __clz(max(V.n_top, 2) - 1));
     for (int qi = wave; qi < nqt; qi += SW) {
       long long* kk = S.u.supkeys[wave];
       const int8_t* qv = A.latq + (int64_t)(q0 + qi) * kDim;
+      if (V.n_top > 0) {
+        for (int s = lane; s < ntp; s += 64) {
+          long long key = LLONG_MAX;
+          if (s < V.n_top) {
+            int acc = 0;
+            const int* c4 = reinterpret_cast<const int*>(V.tcent + (int64_t)s * kDim);
+            const int* q4 = reinterpret_cast<const int*>(qv);
+#pragma unroll
+            for (int d = 0; d < 16; ++d) acc = __builtin_amdgcn_sdot4(q4[d], c4[d], acc, false);
+            key = -order_key(acc, s);
+          }
+          kk[s] = key;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        wave_bitonic(kk, ntp);
+        const int R2 = min(A.tree2_top, V.n_top);
+        for (int i = lane; i < R2; i += 64) {
+          const int s = (int)(0xffffffffu - (unsigned)((-kk[i]) & 0xffffffffll));
+          atomicOr(&S.supmask[qi][s >> 5], 1u << (s & 31));
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
       for (int s = lane; s < nsp; s += 64) {
+        bool live = s < V.n_sup;
+        if (live && V.n_top > 0) {
+          const int tp = V.suptop[s];
+          live = tp < 0 || ((S.supmask[qi][tp >> 5] >> (tp & 31)) & 1u);
+        }
         long long key = LLONG_MAX;        // padding sorts last
-        if (s < V.n_sup) {
+        if (live) {
           int acc = 0;
           const int* c4 = reinterpret_cast<const int*>(V.scent + (int64_t)s * kDim);
           const int* q4 = reinterpret_cast<const int*>(qv);
@@ -169,9 +202,15 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (V.n_top > 0) {                 // the top-node bits are read: clear them
+        for (int w = lane; w < MAXSUPW; w += 64) S.supmask[qi][w] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
       wave_bitonic(kk, nsp);
       const int R = min(A.tree_top, V.n_sup);
       for (int i = lane; i < R; i += 64) {
+        if (kk[i] == LLONG_MAX) continue;  // fewer live supers than tree_top
         const long long key = -kk[i];
         const int s = (int)(0xffffffffu - (unsigned)(key & 0xffffffffll));
         atomicOr(&S.supmask[qi][s >> 5], 1u << (s & 31));

@@ -713,7 +713,7 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
 // query with more supers or candidates than the registers hold is flagged
 // for the exact kernel.
 constexpr int SUPN = 2048;          // supers sorted per query (n_sup <= SUPN)
-constexpr int CPT = 8;              // candidate leaves per thread
+constexpr int CPT = 16;             // candidate leaves per thread
 constexpr int TOPCAP = 256;         // tree_top served here
 
 __device__ __forceinline__ int dot64(const int (&qv)[16], const int8_t* c) {
@@ -730,24 +730,72 @@ __device__ __forceinline__ int dot64(const int (&qv)[16], const int8_t* c) {
   return acc;
 }
 
-template <int NS>
-__device__ __forceinline__ void top_supers(const IdxView& V, const int (&qv)[16], int R,
-                                           long long* tmp, int* s_sup) {
+// The R best of n nodes by (score desc, id asc): candidate c is node id_of(c)
+// with centroid cent[id]; out[r] = id of rank r (R <= n).  Every thread
+// reads its candidates before the sort's first barrier and writes after it.
+template <int NS, class IdOf>
+__device__ __forceinline__ void top_nodes(const int8_t* cent, int n, IdOf id_of,
+                                          const int (&qv)[16], int R, long long* tmp, int* out) {
   constexpr int PT = NS / RT;
   const int tid = threadIdx.x;
   // ascending sort of -order key = (score desc, id asc)
   long long v[PT];
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
-    const int s = tid * PT + i;
-    v[i] = s < V.n_sup ? -order_key(dot64(qv, V.scent + (int64_t)s * kDim), s) : LLONG_MAX;
+    const int c = tid * PT + i;
+    long long key = LLONG_MAX;
+    if (c < n) {
+      const int id = id_of(c);
+      key = -order_key(dot64(qv, cent + (int64_t)id * kDim), id);
+    }
+    v[i] = key;
   }
   block_bitonic<NS>(v, tmp);
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int r = tid * PT + i;
-    if (r < R) s_sup[r] = (int)(0xffffffffu - (unsigned)((-v[i]) & 0xffffffffll));
+    if (r < R) out[r] = (int)(0xffffffffu - (unsigned)((-v[i]) & 0xffffffffll));
   }
+}
+
+template <class IdOf>
+__device__ __forceinline__ void top_nodes_any(const int8_t* cent, int n, IdOf id_of,
+                                              const int (&qv)[16], int R, long long* tmp, int* out) {
+  if (n <= 1024) top_nodes<1024>(cent, n, id_of, qv, R, tmp, out);
+  else top_nodes<SUPN>(cent, n, id_of, qv, R, tmp, out);
+}
+
+// Prefix sums over the counts of the R nodes out[0..R) (wave 0): pre[j] =
+// members of nodes before j, pre[TOPCAP] = all.
+__device__ __forceinline__ void node_prefix(const int32_t* cnt, const int* nodes, int R, int* pre) {
+  const int lane = lane_id();
+  int c[TOPCAP / 64], loc = 0;
+#pragma unroll
+  for (int k = 0; k < TOPCAP / 64; ++k) {
+    const int j = (TOPCAP / 64) * lane + k;
+    c[k] = j < R ? cnt[nodes[j]] : 0;
+    loc += c[k];
+  }
+  int all;
+  int ex = wave_excl_scan(loc, &all);
+#pragma unroll
+  for (int k = 0; k < TOPCAP / 64; ++k) {
+    pre[(TOPCAP / 64) * lane + k] = ex;
+    ex += c[k];
+  }
+  if (lane == 0) pre[TOPCAP] = all;
+}
+
+// member f of the nodes listed in `nodes` (prefix `pre`): last node starting
+// at or before f, then its slot in the member array
+__device__ __forceinline__ int nth_member(const int32_t* off, const int32_t* mem, const int* nodes,
+                                          const int* pre, int R, int f) {
+  int a = 0, b = R - 1;
+  while (a < b) {
+    const int m = (a + b + 1) >> 1;
+    if (pre[m] <= f) a = m; else b = m - 1;
+  }
+  return mem[off[nodes[a]] + (f - pre[a])];
 }
 
 __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, int32_t* flags) {
@@ -778,27 +826,34 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, 
       qv[4 * k] = x.x; qv[4 * k + 1] = x.y; qv[4 * k + 2] = x.z; qv[4 * k + 3] = x.w;
     }
   }
-  if (ok && sup) {
-    if (V.n_sup <= 1024) top_supers<1024>(V, qv, R, s_tmp, s_sup);
-    else top_supers<SUPN>(V, qv, R, s_tmp, s_sup);
-    __syncthreads();
-    if (wave == 0) {                  // leaves of the selected supers, prefix over them
-      int c[TOPCAP / 64], loc = 0;
-#pragma unroll
-      for (int k = 0; k < TOPCAP / 64; ++k) {
-        const int j = (TOPCAP / 64) * lane + k;
-        c[k] = j < R ? V.scnt[s_sup[j]] : 0;
-        loc += c[k];
+  int Rs = R;                          // supers taken (third level: at most R)
+  if (ok && sup && V.n_top > 0) {
+    // third level: the tree2_top best top nodes; candidate supers are their
+    // members and the supers under no top node
+    const int R2 = min(A.tree2_top, V.n_top);
+    ok = R2 >= 1 && R2 <= TOPCAP;
+    if (ok) {
+      top_nodes_any(V.tcent, V.n_top, [](int c) { return c; }, qv, R2, s_tmp, s_sup);
+      __syncthreads();
+      if (wave == 0) node_prefix(V.tcnt, s_sup, R2, s_pre);
+      __syncthreads();
+      const int nsel2 = s_pre[TOPCAP];
+      const int ncs = nsel2 + (V.n_sup - V.covered_sup);
+      ok = ncs <= SUPN;
+      if (ok) {
+        Rs = min(R, ncs);
+        top_nodes_any(V.scent, ncs, [&](int c) {
+          return c < nsel2 ? nth_member(V.toff, V.tmem, s_sup, s_pre, R2, c)
+                           : V.covered_sup + (c - nsel2);
+        }, qv, Rs, s_tmp, s_sup);
       }
-      int all;
-      int ex = wave_excl_scan(loc, &all);
-#pragma unroll
-      for (int k = 0; k < TOPCAP / 64; ++k) {
-        s_pre[(TOPCAP / 64) * lane + k] = ex;
-        ex += c[k];
-      }
-      if (lane == 0) s_pre[TOPCAP] = all;
     }
+  } else if (ok && sup) {
+    top_nodes_any(V.scent, V.n_sup, [](int c) { return c; }, qv, R, s_tmp, s_sup);
+  }
+  if (ok && sup) {
+    __syncthreads();
+    if (wave == 0) node_prefix(V.scnt, s_sup, Rs, s_pre);   // leaves of the taken supers
     __syncthreads();
   }
   const int nsel = ok && sup ? s_pre[TOPCAP] : 0;
@@ -817,12 +872,7 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, 
       const int f = tid + RT * u;
       leaf[u] = -1;
       if (f < nsel) {
-        int a = 0, b = R - 1;         // last selected super starting at or before f
-        while (a < b) {
-          const int m = (a + b + 1) >> 1;
-          if (s_pre[m] <= f) a = m; else b = m - 1;
-        }
-        leaf[u] = V.smem[V.soff[s_sup[a]] + (f - s_pre[a])];
+        leaf[u] = nth_member(V.soff, V.smem, s_sup, s_pre, Rs, f);
       } else if (f < ncand) {
         leaf[u] = V.covered + (f - nsel);
       }

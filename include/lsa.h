@@ -81,11 +81,17 @@ enum {
  * is a multiple of 16 in [16, 256] and <= block; iters >= 1.  Tree:
  * tree_group blocks per super group (0 = Flat), tree_super clusters per
  * group (multiple of 16, <= 256, tree_group*buckets <= 16384 and a multiple
- * of 64), tree_iters >= 1.  max_tokens = capacity in keys. */
+ * of 64), tree_iters >= 1.  max_tokens = capacity in keys.  Third Tree
+ * level (the hierarchy of the sysnote.net page, "What it changes", one
+ * level deeper): the super clusters of each complete run of tree2_group
+ * groups are clustered into tree2_super top nodes (tree2_group = 0: two
+ * levels; else tree_group > 0, tree2_super a multiple of 16 in [16, 256],
+ * tree2_group*tree_super <= 16384 and a multiple of 64, tree2_iters >= 1). */
 typedef struct lsa_index_params {
   int32_t dim, pool, block, buckets, iters;
   int32_t tree_group, tree_super, tree_iters;
   int64_t max_tokens;
+  int32_t tree2_group, tree2_super, tree2_iters;
 } lsa_index_params;
 
 /* Per-query selection: budget long-range keys (sinks <= j <= t - window),
@@ -95,10 +101,14 @@ typedef struct lsa_index_params {
  * takes 2048 long-range keys for queries before position 1M): a query at
  * t < early_until takes early_budget long-range keys instead of budget;
  * 0 <= early_budget <= budget.  early_until = 0 turns it off.  Rows keep the
- * stride budget + window + sinks. */
+ * stride budget + window + sinks.  tree2_top = top nodes a query walks into
+ * on an index with a third level (>= 1 there); the tree_top super clusters
+ * are then the best among those under the chosen top nodes and those not
+ * under any top node yet. */
 typedef struct lsa_select_params {
   int32_t budget, window, sinks, tree_top;
   int32_t early_budget, early_until;
+  int32_t tree2_top;
 } lsa_select_params;
 
 /* Attention shape.  D in {64, 128}; 1 <= Hq/Hkv <= 16, Hq % Hkv == 0.
@@ -125,12 +135,17 @@ typedef struct lsa_index lsa_index;
  *   scnt     int32 [n_sup]          leaves per super cluster
  *   soff     int32 [n_sup]          first leaf's slot in smem
  *   smem     int32 [n_grp*G*C]      leaf ids grouped by super cluster, ascending
+ *   tcent    int8  [n_top][64]      top-node centroids (third level)
+ *   tcnt     int32 [n_top]          super clusters per top node
+ *   toff     int32 [n_top]          first super's slot in tmem
+ *   tmem     int32 [n_grp2*G2*S]    super ids grouped by top node, ascending
  * Key ids of pooled id g are g*pool .. g*pool+pool-1. */
 typedef struct lsa_index_info {
   int64_t T, n_pool, n_full, n_bkt, n_grp, n_sup;
   int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast;
   int64_t off_scent, off_scnt, off_soff, off_smem;
   int64_t arena_bytes;
+  int64_t n_grp2, n_top, off_tcent, off_tcnt, off_toff, off_tmem;
 } lsa_index_info;
 
 LSA_API const char* lsa_status_str(int status);

@@ -149,6 +149,10 @@ class Workload:
     tree_super: int = 0    # super clusters per group
     tree_iters: int = 0
     tree_top: int = 0      # super clusters taken per query
+    tree2_group: int = 0   # third level: groups per top group
+    tree2_super: int = 0   # top nodes per top group
+    tree2_iters: int = 0
+    tree2_top: int = 0     # top nodes taken per query
     chunk: int = 32768     # queries = the last ``chunk`` positions
     budget: int = 4096
     window: int = 512
@@ -177,6 +181,10 @@ WORKLOADS = {
     "decode_1m": Workload("decode_1m", 4, T=M, ncomp=4096, chunk=0, nseq=8, steps=256),
     "tree_10m": Workload("tree_10m", 5, T=10 * M, ncomp=16384, tree_group=64,
                          tree_super=64, tree_iters=4, tree_top=32),
+    # three levels: top nodes over the supers of each run of 5 groups
+    "tree3_10m": Workload("tree3_10m", 5, T=10 * M, ncomp=16384, tree_group=64,
+                          tree_super=64, tree_iters=4, tree_top=32, tree2_group=5,
+                          tree2_super=32, tree2_iters=4, tree2_top=16),
     # one attention layer's training step at 128k context: every position is a query
     "train_128k": Workload("train_128k", 6, T=M // 8, ncomp=1024, chunk=M // 8),
 }

@@ -44,6 +44,12 @@ def test_host_validation_without_device():
     sp = L.SelectParams(4096, 512, 4, 0)
     ap = L.AttnParams(32, 8, 128, 0, 0.0)
     assert L.workspace_bytes(L.binding.OP_PREFILL, p, sp, ap, 32768) >= 32768 * 4612 * 4
+    # a third Tree level needs the second one and MFMA-sized point counts
+    for t2, code in (((2, 16, 2), 0), ((3, 16, 2), 2), ((2, 8, 2), 2), ((2, 16, 0), 1)):
+        q = L.IndexParams(64, 4, 4096, 256, 4, 64, 32, 2, 1 << 20, *t2)
+        assert lib.lsa_index_bytes(ctypes.byref(q), ctypes.byref(n)) == code, t2
+    q = L.IndexParams(64, 4, 4096, 256, 4, 0, 0, 0, 1 << 20, 2, 16, 2)
+    assert lib.lsa_index_bytes(ctypes.byref(q), ctypes.byref(n)) == 1
     # backward at a 128k training step: the (bucket -> queries) list alone
     # needs a slot for every (query, taken bucket)
     p128 = L.IndexParams(64, 4, 4096, 256, 4, 0, 0, 0, 2 ** 17)

@@ -34,7 +34,7 @@ def _dev():
 
 def _oparams(wl):
     return O.IndexParams(wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
-                         wl.tree_iters)
+                         wl.tree_iters, wl.tree2_group, wl.tree2_super, wl.tree2_iters)
 
 
 def _sample_positions(wl, n_sel, seed):
@@ -60,10 +60,11 @@ def _gpu_prefill(wl, dev, out_f32_too=True, early=(0, 0)):
     q = torch.empty((n, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
     g.fill_rows("q", q, t0)
     ix = L.LsaIndex(L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group,
-                                  wl.tree_super, wl.tree_iters, wl.T), dev)
+                                  wl.tree_super, wl.tree_iters, wl.T, wl.tree2_group,
+                                  wl.tree2_super, wl.tree2_iters), dev)
     ix.build(latk[:t0])
     snap = ix.snapshot()
-    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, *early)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, *early, wl.tree2_top)
     idx = torch.empty((n, sp.max_sel), dtype=torch.int32, device=dev)
     cnt = torch.empty((n,), dtype=torch.int32, device=dev)
     o16 = ix.prefill_chunk(latk[t0:], latq, q, K, V, sp, L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0),
@@ -84,7 +85,7 @@ def _gpu_prefill(wl, dev, out_f32_too=True, early=(0, 0)):
 def _check_prefill(wl, res, ref, n_sel, n_att, seed, early=(0, 0)):
     n, t0 = wl.chunk, wl.T - wl.chunk
     check_index(res["arrays"], ref)
-    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, *early)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, *early, wl.tree2_top)
     pos = _sample_positions(wl, n_sel, seed)
     latq = res["g"].latq_rows(torch.tensor([t0 + i for i in pos])).numpy()   # host-generated
     sels = {}
@@ -147,6 +148,16 @@ def test_tree_10m_prefill_chunk(oracle_10m):
     ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
     assert ref.n_grp == 10 and ref.sup_centroids.shape[0] == 640
     _check_prefill(wl, res, ref, n_sel=96, n_att=12, seed=3)
+
+
+def test_tree3_10m_prefill_chunk(oracle_10m):
+    dev = _dev()
+    wl = S.WORKLOADS["tree3_10m"]
+    res = _gpu_prefill(wl, dev)
+    cache, latk = oracle_10m
+    ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
+    assert ref.n_grp2 == 2 and ref.top_centroids.shape[0] == 64
+    _check_prefill(wl, res, ref, n_sel=96, n_att=12, seed=4)
 
 
 def test_decode_1m_256_steps(oracle_pool):

@@ -32,12 +32,13 @@ def _dev():
 def _iparams(wl, max_tokens=None):
     L = _L()
     return L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group,
-                         wl.tree_super, wl.tree_iters, max_tokens or wl.T)
+                         wl.tree_super, wl.tree_iters, max_tokens or wl.T, wl.tree2_group,
+                         wl.tree2_super, wl.tree2_iters)
 
 
 def _oparams(wl):
     return O.IndexParams(wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
-                         wl.tree_iters)
+                         wl.tree_iters, wl.tree2_group, wl.tree2_super, wl.tree2_iters)
 
 
 def check_index(gpu_arrays, ref: O.Index, blocks=None):
@@ -72,6 +73,14 @@ def check_index(gpu_arrays, ref: O.Index, blocks=None):
         assert np.array_equal(a["scnt"], sc)
         smem = np.concatenate(ref.sup_members) if ref.sup_members else np.zeros(0)
         assert np.array_equal(a["smem"], smem)
+    if ref.top_centroids is not None and blocks is None:
+        assert np.array_equal(a["tcent"], ref.top_centroids), "top-node centroids"
+        tcn = np.array([len(m) for m in ref.top_members])
+        assert np.array_equal(a["tcnt"], tcn)
+        toff = np.concatenate([[0], np.cumsum(tcn)[:-1]]) if len(tcn) else tcn
+        assert np.array_equal(a["toff"], toff)
+        tmem = np.concatenate(ref.top_members) if ref.top_members else np.zeros(0)
+        assert np.array_equal(a["tmem"], tmem)
 
 
 def check_selection(idx, cnt, refs, max_sel):
@@ -412,6 +421,90 @@ def test_tree_index_and_selection():
         idx, cnt = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp)
         refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
         check_selection(idx, cnt, refs, sp.max_sel)
+
+
+TREE3 = S.Workload("tree3_small", 71, T=4 * 64 * 2 * 10 + 300, ncomp=96, block=64, buckets=32,
+                   iters=3, tree_group=2, tree_super=16, tree_iters=3, tree_top=6, tree2_group=4,
+                   tree2_super=16, tree2_iters=3, tree2_top=3, chunk=0, budget=300, window=64,
+                   sinks=4, Hq=4, Hkv=1, D=64)
+
+
+def test_tree3_index_and_selection():
+    """Three-level Tree: 10 groups of 2 blocks, top groups of 4 groups (2
+    complete, 2 groups and a partial block outside them).  Index bit-exact,
+    selections of the fast Tree kernel and of the exact kernel bit-exact."""
+    dev = _dev()
+    L = _L()
+    wl = TREE3
+    g = S.Synth(wl, data_cfg=71)
+    latk = g.latk(0, wl.T)
+    ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
+    assert ref.n_grp == 10 and ref.n_grp2 == 2 and ref.top_centroids.shape[0] == 32
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    torch.cuda.synchronize()
+    check_index(ix.arrays(), ref)
+    pos = [wl.T - 1 - 41 * i for i in range(48)] + [70, 700, 3000, 6000]
+    lq = g.latq_rows(torch.tensor(pos))
+    qd = torch.tensor(pos, dtype=torch.int32, device=dev)
+    for R, R2 in ((1, 1), (6, 3), (6, 8), (40, 2)):
+        sp = L.SelectParams(wl.budget, wl.window, wl.sinks, R, 0, 0, R2)
+        osp = O.SelectParams(wl.budget, wl.window, wl.sinks, R, tree2_top=R2)
+        refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+        idx, cnt = ix.select(lq.to(dev), qd, sp)
+        check_selection(idx, cnt, refs, sp.max_sel)
+        idx2, cnt2 = ix.select(lq.to(dev), qd, sp, use_workspace=False)
+        assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    with pytest.raises(L.LsaError, match="tree2_top"):
+        ix.select(lq.to(dev), qd, L.SelectParams(wl.budget, wl.window, wl.sinks, 6))
+
+
+def test_tree3_append_equals_build_and_decode():
+    """Appending key by key across a top-group completion gives the built
+    index; decode steps on two sequences select the oracle's keys."""
+    dev = _dev()
+    L = _L()
+    wl = TREE3
+    kpt = wl.pool * wl.block * wl.tree_group * wl.tree2_group     # keys per top group
+    Ts = [kpt - 2, 2 * kpt + 77]
+    steps = 5
+    cap = max(Ts) + steps
+    gens = [S.Synth(wl, seq=i, data_cfg=72) for i in range(2)]
+    ip = _iparams(wl, cap)
+    op = _oparams(wl)
+    K = torch.empty((2, cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    ixs, lat = [], []
+    for i, gg in enumerate(gens):
+        lk = gg.latk(0, cap)
+        lat.append(lk)
+        ix = L.LsaIndex(ip, dev)
+        ix.build(lk[:Ts[i]].to(dev))
+        ixs.append(ix)
+        gg.fill_rows("k", K[i], 0)
+        gg.fill_rows("v", V[i], 0)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, 0, 0, wl.tree2_top)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, tree2_top=wl.tree2_top)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, 2), dtype=torch.uint8,
+                     device=dev)
+    Kd, Vd = K.to(dev), V.to(dev)
+    for step in range(steps):
+        ts = [T + step for T in Ts]
+        lk_new = torch.stack([lat[i][t] for i, t in enumerate(ts)])
+        lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kd, Vd, cap, sp, ap, ws=ws)
+        idx, cnt = L.decode_selection(ws, 2, sp)
+        torch.cuda.synchronize()
+        for i, t in enumerate(ts):
+            sel = O.select(O.build_index(lat[i].numpy(), t + 1, op), lq[i].numpy(), t, osp)
+            n = int(cnt[i])
+            assert np.array_equal(np.sort(idx[i, :n].cpu().numpy()), sel), f"seq {i} step {step}"
+    for i in range(2):
+        full = O.build_index(lat[i].numpy(), Ts[i] + steps, op)
+        check_index(ixs[i].arrays(), full)
+    assert full.n_grp2 == 2
 
 
 @pytest.mark.parametrize("early", [(0, 0), (100, 4 * 256 * 4 + 5 + 4)])
