@@ -44,9 +44,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The measured kernel (the window-sharing attention and the tile code it
+# uses) is the part of its source before the decode kernels; counters taken
+# on it stay valid while only the code after this marker changes.
+ATTN_SRC_END = b"// Decode: split-K attention."
+
+
 def src_hash(path: str) -> str:
     with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        data = f.read()
+    cut = data.find(ATTN_SRC_END)
+    return hashlib.sha256(data if cut < 0 else data[:cut]).hexdigest()[:16]
 
 
 def gen_inputs(wl, dev, seq=0, T=None):

@@ -560,11 +560,20 @@ __global__ void __launch_bounds__(256) k_attn_merge(AttnArgs a) {
   float num[D / 64];
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) num[c] = 0.f;
-#pragma unroll 16
-  for (int s2 = 0; s2 < S; ++s2) {
-    const float ws = __shfl(w, s2);
+  // 16 splits' partial rows in flight at once, then their weighted sum
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float pv[16][D / 64];
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) num[c] += po[(int64_t)s2 * a.G * D + 64 * c] * ws;
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c)
+        pv[j][c] = s0 + j < S ? po[(int64_t)(s0 + j) * a.G * D + 64 * c] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float ws = __shfl(w, s0 + j);
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) num[c] += pv[j][c] * ws;
+    }
   }
   const int64_t ob = (int64_t)row * D + lane;
 #pragma unroll

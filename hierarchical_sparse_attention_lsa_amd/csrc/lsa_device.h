@@ -60,16 +60,42 @@ __device__ __forceinline__ long long shfl_xor_i64(long long v, int m) {
   return ((long long)hi << 32) | (unsigned int)lo;
 }
 
+// Wave-wide inclusive scans on DPP lane moves (VALU, no LDS crossbar):
+// shifts by 1, 2, 4, 8 inside each 16-lane row, then row 1 and 3 take the
+// last lane of the row before (row_bcast:15) and rows 2 and 3 lane 31
+// (row_bcast:31).  Lanes whose source is outside the row, or whose row is
+// masked off, receive `id`.  Every lane of the wave must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int id, int x) {
+  return __builtin_amdgcn_update_dpp(id, x, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ long long dpp_move(long long id, long long x) {
+  const int lo = dpp_move<CTRL, ROWS>((int)(id & 0xffffffffll), (int)(x & 0xffffffffll));
+  const int hi = dpp_move<CTRL, ROWS>((int)(id >> 32), (int)(x >> 32));
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+template <class T, class Op>
+__device__ __forceinline__ T wave_incl_scan(T x, T id, Op op) {
+  x = op(x, dpp_move<0x111, 0xf>(id, x));
+  x = op(x, dpp_move<0x112, 0xf>(id, x));
+  x = op(x, dpp_move<0x114, 0xf>(id, x));
+  x = op(x, dpp_move<0x118, 0xf>(id, x));
+  x = op(x, dpp_move<0x142, 0xa>(id, x));
+  x = op(x, dpp_move<0x143, 0xc>(id, x));
+  return x;
+}
+__device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
+__device__ __forceinline__ long long lane63(long long x) {
+  const int lo = __builtin_amdgcn_readlane((int)(x & 0xffffffffll), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), 63);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
 // Exclusive prefix sum over a wave; returns the wave total in *total.
 __device__ __forceinline__ int wave_excl_scan(int x, int* total) {
-  const int l = lane_id();
-  int s = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(s, d);
-    if (l >= d) s += y;
-  }
-  *total = __shfl(s, 63);
+  const int s = wave_incl_scan(x, 0, [](int a, int b) { return a + b; });
+  *total = lane63(s);
   return s - x;
 }
 

@@ -104,8 +104,7 @@ __device__ void wave_bitonic(T* a, int n) {
 template <int NT>
 __device__ __forceinline__ long long block_sum_ll(long long x, long long* red) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += shfl_xor_i64(x, m);
+  x = lane63(wave_incl_scan(x, 0ll, [](long long a, long long b) { return a + b; }));
   __syncthreads();
   if (lane == 0) red[wave] = x;
   __syncthreads();
@@ -117,8 +116,7 @@ __device__ __forceinline__ long long block_sum_ll(long long x, long long* red) {
 template <int NT>
 __device__ __forceinline__ long long block_min_ll(long long x, long long* red) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = min(x, shfl_xor_i64(x, m));
+  x = lane63(wave_incl_scan(x, LLONG_MAX, [](long long a, long long b) { return min(a, b); }));
   __syncthreads();
   if (lane == 0) red[wave] = x;
   __syncthreads();
@@ -130,8 +128,7 @@ __device__ __forceinline__ long long block_min_ll(long long x, long long* red) {
 template <int NT>
 __device__ __forceinline__ long long block_max_ll(long long x, long long* red) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = max(x, shfl_xor_i64(x, m));
+  x = lane63(wave_incl_scan(x, LLONG_MIN, [](long long a, long long b) { return max(a, b); }));
   __syncthreads();
   if (lane == 0) red[wave] = x;
   __syncthreads();

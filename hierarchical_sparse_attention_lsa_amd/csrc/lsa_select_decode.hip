@@ -30,11 +30,11 @@ using namespace sel;
 
 constexpr int DT = 1024;            // threads of the select workgroup
 constexpr int DW = DT / 64;
-constexpr int PERT = 24;            // buckets per thread (indexes of up to 24576 buckets)
+constexpr int PERT_MAX = 24;        // buckets per thread (indexes of up to 24576 buckets)
 constexpr int RB = 256;
 constexpr int RCAP = 256;
-constexpr int kDecLds = PERT * DT * 4;
-constexpr int kListCap = PERT * DT / 2;   // taken buckets the emission list can hold
+constexpr int dec_lds(int pert) { return pert * DT * 4; }
+constexpr int list_cap(int pert) { return pert * DT / 2; }   // taken buckets the emission list holds
 
 struct DecViews {                   // first kernel argument (read through the kernarg pointer)
   IdxView v[16];
@@ -84,8 +84,12 @@ __device__ __forceinline__ long long rebuilt_key(int s, int beta) {
   return order_key(s, beta);
 }
 
+// PERT buckets per thread: the smallest instance that holds the index is
+// launched, since every pass costs VALU time per slot, used or not.
+template <int PERT>
 __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs W,
                                                    int32_t* __restrict__ flags) {
+  constexpr int kListCap = list_cap(PERT);
   __shared__ int s_hk[RB], s_hb[RB];
   __shared__ long long s_red[DW];
   __shared__ int s_ired[DW];
@@ -93,6 +97,7 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   __shared__ int s_ci[RCAP];
   __shared__ int s_nc;
   __shared__ int s_cut[2];
+  __shared__ long long s_r3[DW][3];
   extern __shared__ int s_e[];         // [bucket id]: eligible keys, later the keys taken
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int seq = blockIdx.x;
@@ -113,25 +118,50 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   int sc[PERT];
 #define KEY(u) rebuilt_key(sc[u], (u) * DT + tid)
 #define E(u) s_e[(u) * DT + tid]
+  // f(u, E(u)) for every bucket of the thread; the LDS reads of each batch of
+  // four are issued together instead of one round trip per bucket
+  auto each = [&](auto&& f) {
+#pragma unroll
+    for (int u0 = 0; u0 < PERT; u0 += 4) {
+      int eb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) eb[j] = E(u0 + j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f(u0 + j, eb[j]);
+    }
+  };
   long long lo = LLONG_MAX, hi = LLONG_MIN, tot = 0;
+  {
+    int ev[PERT];                      // all loads in flight before the first use
 #pragma unroll
-  for (int u = 0; u < PERT; ++u) {
-    const int j = u * DT + tid;
-    sc[u] = j < n ? W.score[base + j] : 0;
-    E(u) = j < n ? W.elig[base + j] : 0;
-  }
+    for (int u = 0; u < PERT; ++u) {
+      const int j = u * DT + tid;
+      sc[u] = j < n ? W.score[base + j] : 0;
+      ev[u] = j < n ? W.elig[base + j] : 0;
+    }
 #pragma unroll
-  for (int u = 0; u < PERT; ++u) {   // branch-free: selects, no divergent blocks
-    const long long ku = KEY(u);
-    const int eu = E(u);
-    const bool ok = eu > 0;
-    lo = min(lo, ok ? ku : LLONG_MAX);
-    hi = max(hi, ok ? ku : LLONG_MIN);
-    tot += ok ? eu : 0;
+    for (int u = 0; u < PERT; ++u) {   // branch-free: selects, no divergent blocks
+      E(u) = ev[u];
+      const long long ku = KEY(u);
+      const bool ok = ev[u] > 0;
+      lo = min(lo, ok ? ku : LLONG_MAX);
+      hi = max(hi, ok ? ku : LLONG_MIN);
+      tot += ok ? ev[u] : 0;
+    }
   }
-  tot = block_sum_ll<DT>(tot, s_red);
-  lo = block_min_ll<DT>(lo, s_red);
-  hi = block_max_ll<DT>(hi, s_red);
+  // one block reduction for (sum, min, max)
+  tot = lane63(wave_incl_scan(tot, 0ll, [](long long a, long long b) { return a + b; }));
+  lo = lane63(wave_incl_scan(lo, LLONG_MAX, [](long long a, long long b) { return min(a, b); }));
+  hi = lane63(wave_incl_scan(hi, LLONG_MIN, [](long long a, long long b) { return max(a, b); }));
+  if (lane == 0) { s_r3[wave][0] = tot; s_r3[wave][1] = lo; s_r3[wave][2] = hi; }
+  __syncthreads();
+  tot = 0; lo = LLONG_MAX; hi = LLONG_MIN;
+#pragma unroll
+  for (int w = 0; w < DW; ++w) {
+    tot += s_r3[w][0];
+    lo = min(lo, s_r3[w][1]);
+    hi = max(hi, s_r3[w][2]);
+  }
   // keys above `hi` are taken whole; the bracket [lo, hi] holds the cutoff
   if (B <= 0) {
     hi = LLONG_MAX;                  // nothing is taken
@@ -147,16 +177,14 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       for (int i = tid; i < RB; i += DT) { s_hk[i] = 0; s_hb[i] = 0; }
       __syncthreads();
       long long ab = 0;
-#pragma unroll
-      for (int u = 0; u < PERT; ++u) {
+      each([&](int u, int eu) {
         const long long ku = KEY(u);
-        const int eu = E(u);
         ab += (eu > 0 && ku > hi) ? eu : 0;
-        if (eu <= 0 || ku > hi || ku < lo) continue;
+        if (eu <= 0 || ku > hi || ku < lo) return;
         const int bin = (int)((hi - ku) >> sh);
         atomicAdd(&s_hk[bin], eu);
         atomicAdd(&s_hb[bin], 1);
-      }
+      });
       ab = block_sum_ll<DT>(ab, s_red);
       if (wave == 0) {
         int h[RB / 64], c[RB / 64], loc = 0;
@@ -194,15 +222,13 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   if (tid == 0) s_nc = 0;
   __syncthreads();
   long long full = 0;
-#pragma unroll
-  for (int u = 0; u < PERT; ++u) {
+  each([&](int u, int eu) {
     const long long ku = KEY(u);
-    const int eu = E(u);
     full += (eu > 0 && ku > hi) ? eu : 0;
-    if (eu <= 0 || ku > hi || ku < lo) continue;
+    if (eu <= 0 || ku > hi || ku < lo) return;
     const int c = atomicAdd(&s_nc, 1);
     if (c < RCAP) { s_cq[c] = -ku; s_ci[c] = u * DT + tid; }
-  }
+  });
   full = block_sum_ll<DT>(full, s_red);
   const int nc = min(s_nc, RCAP);
   const bool overflow = s_nc > RCAP;
@@ -240,12 +266,10 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   }
   __syncthreads();
   // keys taken per bucket: whole above the bracket, as the walk set them inside it
-#pragma unroll
-  for (int u = 0; u < PERT; ++u) {
+  each([&](int u, int eu) {
     const long long ku = KEY(u);
-    const int eu = E(u);
     E(u) = (eu > 0 && ku >= lo) ? eu : 0;
-  }
+  });
   __syncthreads();
   // output offsets in ascending bucket id: thread tid sums ids
   // [tid*PERT, tid*PERT + PERT), block scans join the chunks
@@ -257,9 +281,13 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     mine += tk[u];
     mcnt += tk[u] > 0 ? 1 : 0;
   }
-  int out_total, nt;
-  int off = block_excl_scan<DT>(mine, s_ired, &out_total);
-  int rank = block_excl_scan<DT>(mcnt, s_ired, &nt);   // the scans' barriers end all reads of s_e
+  // one scan of (keys << 16 | buckets): key totals stay <= budget <= 4096 and
+  // bucket totals <= 24576, so neither half carries into the other
+  int packed_total;
+  // (an overflowed bracket leaves more keys here; that result is discarded)
+  const int packed = block_excl_scan<DT>((min(mine, 4096) << 16) | mcnt, s_ired, &packed_total);
+  int off = packed >> 16, rank = packed & 0xffff;     // the scan's barriers end all reads of s_e
+  const int out_total = packed_total >> 16, nt = packed_total & 0xffff;
   const bool ok = !overflow && nt <= kListCap;
   // list of taken buckets (output offset, first key slot), ascending ids, over s_e
   int* l_off = s_e;
@@ -358,7 +386,8 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   int32_t* flags;
   dec_layout(nseq, vs.cap, &W, &flags, ws);
   if (tree) return launch_select_tree_multi(views, qpos, nseq, b, flags, s);
-  if (nmax > DT * PERT) return launch_select_multi(views, qpos, nseq, b, s);
+  if (nmax > DT * PERT_MAX) return launch_select_multi(views, qpos, nseq, b, s);
+  const bool small = nmax <= DT * 20;
   if (nmax > 0) {
     hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + 255) / 256), (unsigned)nseq), dim3(256), 0,
                        s, vs, b, W);
@@ -367,12 +396,19 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   }
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_dec_select,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDecLds);
+    hipError_t e = hipFuncSetAttribute((const void*)k_dec_select<20>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(20));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)k_dec_select<PERT_MAX>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(PERT_MAX));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_dec_select, dim3((unsigned)nseq), dim3(DT), kDecLds, s, vs, b, W, flags);
+  if (small)
+    hipLaunchKernelGGL(k_dec_select<20>, dim3((unsigned)nseq), dim3(DT), dec_lds(20), s, vs, b, W, flags);
+  else
+    hipLaunchKernelGGL(k_dec_select<PERT_MAX>, dim3((unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s, vs, b,
+                       W, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // The bracket always fits: every refinement pass narrows the key range by
@@ -380,7 +416,7 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   // passes. The emission list can only overflow when more than kListCap
   // buckets are taken, which needs a budget above kListCap; only then can a
   // sequence be flagged, and the exact kernel serves the flagged ones.
-  if (a.budget <= kListCap) return hipSuccess;
+  if (a.budget <= list_cap(small ? 20 : PERT_MAX)) return hipSuccess;
   b.only = flags;
   return launch_select_multi(views, qpos, nseq, b, s);
 }
