@@ -572,6 +572,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="one prefill step plus a 2 GiB calibration copy (for rocprofv3 runs)")
     ap.add_argument("--full-prefill", action="store_true",
@@ -656,6 +657,11 @@ def main():
         decode = bench_decode(args, dev)
         log(f"[bench] decode {decode['tokens_per_s']:.0f} tok/s ({decode['ms_per_step']:.3f} ms/step)")
 
+    train = None
+    if not args.no_train:
+        torch.cuda.empty_cache()
+        train = bench_train(args, dev)
+
     cpu = None
     if not args.no_cpu:
         try:
@@ -707,6 +713,7 @@ def main():
         "index_build_keys_per_s": wl.T / (res["build_ms"] * 1e-3),
         "decode": decode,
         "dense_scan": dense,
+        "train_step_128k": train,
     }
     print(json.dumps(line), flush=True)
 
