@@ -274,3 +274,83 @@ def test_flat_1m_chunked_prefill_from_empty(oracle_1m):
     print(f"chunked prefill from empty: {sum(len(r) for r in checked.values())} selections bit-exact, "
           f"attention normwise error {worst:.3e}")
     assert worst <= TOL
+
+
+def test_train_128k_backward(oracle_pool):
+    """The benchmarked training step at 128k (every position a query, bf16
+    forward output): dQ of sampled queries and dK / dV of the last keys
+    (reached only through windows) against the oracle over its own
+    selections, and the zero-sum / value-sum properties over all keys."""
+    dev = _dev()
+    L = _L()
+    wl = S.WORKLOADS["train_128k"]
+    T = wl.T
+    g = S.Synth(wl)
+    latk = g.latk(0, T, device=dev)
+    K = torch.empty((T, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    q = torch.empty((T, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    do = torch.empty_like(q)
+    for name, tt in (("k", K), ("v", V), ("q", q), ("do", do)):
+        g.fill_rows(name, tt, 0)
+    ix = L.LsaIndex(L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, T), dev)
+    ix.build(latk)
+    pos = torch.arange(T, device=dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
+    idx, cnt = ix.select(g.latq_rows(pos, device=dev), pos.to(torch.int32), sp)
+    # properties over all keys, with a float32 forward output (exact row sums):
+    # the softmax gradients sum to zero over the keys; the value gradients sum
+    # to the upstream gradients of each KV head's query heads
+    ap32 = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    out32, lse32 = L.sparse_attn_fwd(q, K, V, idx, cnt, 0, sp, ap32)
+    _, dk32, dv32 = L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap32, out32, lse32, do)
+    G = wl.Hq // wl.Hkv
+    dks = dk32.double().sum(0)
+    assert float(dks.abs().max()) <= 1e-4 * float(dk32.double().abs().sum(0).max())
+    want = do.double().view(T, wl.Hkv, G, wl.D).sum((0, 2))
+    assert float((dv32.double().sum(0) - want).abs().max()) <= 1e-4 * float(want.abs().max())
+    del out32, lse32, dk32, dv32
+    # the benchmarked configuration: bf16 forward output
+    out, lse = L.sparse_attn_fwd(q, K, V, idx, cnt, 0, sp, ap)
+    dq, dk, dv = L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do)
+    torch.cuda.synchronize()
+    # oracle over its own selections
+    cache, latk_h = build_cache_parallel(wl.name, T, oracle_pool)
+    ref = O.build_index(latk_h, T, _oparams(wl), cache)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+
+    def f64(t):
+        return O.bf16_to_f64(t.view(torch.int16).numpy())
+
+    def grads(t):
+        sel = O.select(ref, g.latq_rows(torch.tensor([t])).numpy()[0], t, osp)
+        rows = torch.from_numpy(sel)
+        Kr, Vr = f64(g.k_rows(rows)), f64(g.v_rows(rows))
+        qt = f64(g.q_rows(torch.tensor([t])))[0]
+        dot = f64(g.do_rows(torch.tensor([t])))[0]
+        o = O.round_bf16(O.attend(qt, Kr, Vr, wl.Hkv))        # the stored bf16 output
+        return sel, O.attend_backward(qt, Kr, Vr, dot, wl.Hkv, o=o)
+
+    qs = [0, 1, 511, 512, 513, 4100, 20000, 77777, T - 300, T - 1]
+    got = dq[qs].cpu().numpy().astype(np.float64)
+    refq = np.stack([grads(t)[1][0] for t in qs])
+    eq = normwise(got, refq)
+    # keys after T - window reach no long-range row: their gradients come from the
+    # windows of the queries t = j .. T-1
+    keys = [T - 1, T - 2, T - 57, T - 200]
+    j0 = min(keys)
+    dK = {j: np.zeros((wl.Hkv, wl.D)) for j in keys}
+    dV = {j: np.zeros((wl.Hkv, wl.D)) for j in keys}
+    for t in range(j0, T):
+        sel, (_, gk, gv) = grads(t)
+        for j in keys:
+            if j <= t:
+                r = int(np.searchsorted(sel, j))
+                assert sel[r] == j
+                dK[j] += gk[r]
+                dV[j] += gv[r]
+    ek = normwise(dk[keys].cpu().numpy().astype(np.float64), np.stack([dK[j] for j in keys]))
+    ev = normwise(dv[keys].cpu().numpy().astype(np.float64), np.stack([dV[j] for j in keys]))
+    print(f"train 128k: dQ ({len(qs)} queries) {eq:.2e}, dK {ek:.2e}, dV {ev:.2e} normwise")
+    assert max(eq, ek, ev) <= TOL
