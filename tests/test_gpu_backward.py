@@ -82,6 +82,13 @@ CASES = [
     ("d64_g3_early", S.Workload("bwd_c", 92, T=2 * 64 * 6 + 5, ncomp=8, block=64, buckets=16,
                                 iters=2, chunk=0, budget=80, window=16, sinks=2, Hq=3, Hkv=1, D=64),
      (20, 400)),
+    # G = 1 (16 queries per column group) and G = 16 (one), window = pool
+    ("d128_g1", S.Workload("bwd_d", 93, T=4 * 64 * 3 + 70, ncomp=10, block=64, buckets=16,
+                           iters=2, chunk=0, budget=64, window=4, sinks=1, Hq=4, Hkv=4, D=128),
+     (0, 0)),
+    ("d64_g16", S.Workload("bwd_e", 94, T=4 * 64 * 3 + 9, ncomp=10, block=64, buckets=16,
+                           iters=2, chunk=0, budget=90, window=24, sinks=3, Hq=16, Hkv=1, D=64),
+     (0, 0)),
 ]
 
 
@@ -145,6 +152,23 @@ def test_backward_of_a_suffix_and_unselected_keys():
     never = np.setdiff1d(np.arange(wl.T), np.concatenate(sels))
     assert len(never) > 0
     assert (dk[never] == 0).all() and (dv[never] == 0).all()
+
+
+def test_empty_batches():
+    dev = _dev()
+    L = _L()
+    wl = CASES[0][1]
+    r = _setup(wl, dev)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    K, V = r["K"].to(dev), r["V"].to(dev)
+    z = lambda *sh, dt=torch.bfloat16: torch.zeros(sh, dtype=dt, device=dev)
+    idx0 = z(0, r["sp"].max_sel, dt=torch.int32)
+    cnt0 = z(0, dt=torch.int32)
+    out, lse = L.sparse_attn_fwd(z(0, wl.Hq, wl.D), K, V, idx0, cnt0, 5, r["sp"], ap)
+    assert out.shape == (0, wl.Hq, wl.D) and lse.shape == (0, wl.Hq)
+    dq, dk, dv = L.sparse_attn_bwd(r["ix"], z(0, wl.Hq, wl.D), K, V, idx0, cnt0, 5, r["sp"], ap,
+                                   out, lse, z(0, wl.Hq, wl.D))
+    assert dq.shape == (0, wl.Hq, wl.D)
 
 
 def test_backward_rejects_bad_arguments():

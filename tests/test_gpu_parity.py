@@ -548,6 +548,58 @@ def test_decode_steps_match_oracle(early):
     assert max(errs) <= TOL
 
 
+def test_decode_sixteen_sequences():
+    """The largest decode batch: 16 sequences of different lengths."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("dec16", 62, T=0, ncomp=32, block=64, buckets=16, iters=2, chunk=0,
+                    budget=120, window=32, sinks=2, Hq=4, Hkv=2, D=64)
+    Ts = [300 + 157 * i for i in range(16)]
+    steps = 3
+    cap = max(Ts) + steps
+    gens = [S.Synth(wl, seq=i, data_cfg=62) for i in range(16)]
+    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, cap)
+    op = _oparams(wl)
+    K = torch.empty((16, cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    ixs, lat = [], []
+    for i, g in enumerate(gens):
+        lk = g.latk(0, cap)
+        lat.append(lk)
+        ix = L.LsaIndex(ip, dev)
+        ix.build(lk[:Ts[i]].to(dev))
+        ixs.append(ix)
+        g.fill_rows("k", K[i], 0)
+        g.fill_rows("v", V[i], 0)
+    Kd, Vd = K.to(dev), V.to(dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, 16), dtype=torch.uint8,
+                     device=dev)
+    errs = []
+    for step in range(steps):
+        ts = [T + step for T in Ts]
+        lk_new = torch.stack([lat[i][t] for i, t in enumerate(ts)])
+        lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        out = L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kd, Vd, cap, sp, ap, ws=ws)
+        idx, cnt = L.decode_selection(ws, 16, sp)
+        torch.cuda.synchronize()
+        for i, t in enumerate(ts):
+            sel = O.select(O.build_index(lat[i].numpy(), t + 1, op), lq[i].numpy(), t, osp)
+            n = int(cnt[i])
+            assert np.array_equal(np.sort(idx[i, :n].cpu().numpy()), sel), f"seq {i} step {step}"
+            errs.append(normwise(out[i].cpu().numpy().astype(np.float64),
+                                 oracle_attention(gens[i], wl, [t], [sel])[0]))
+    assert max(errs) <= TOL
+    with pytest.raises(L.LsaError, match="nseq"):
+        L.decode_step(ixs + ixs[:1], torch.zeros((17, 64), dtype=torch.int8, device=dev),
+                      torch.zeros((17, 64), dtype=torch.int8, device=dev),
+                      torch.zeros((17, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev), Kd, Vd, cap,
+                      sp, ap, ws=ws)
+
+
 def test_tree_decode_steps_match_oracle():
     """Decode on Tree indexes: sequences of different lengths, one without a
     complete group until its third step (its super level is built during
