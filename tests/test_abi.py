@@ -63,3 +63,46 @@ def test_host_validation_without_device():
     info = L.IndexInfo()
     assert lib.lsa_index_get_info(desc, ctypes.byref(info)) == 4
     assert lib.lsa_select(desc, None, None, 0, ctypes.byref(sp), None, None, None, 0, None) == 4
+
+
+def _fake_index(lib, p):
+    """A descriptor over an aligned address that is never dereferenced: the
+    calls below fail validation before anything is enqueued."""
+    desc = ctypes.create_string_buffer(lib.lsa_index_sizeof())
+    n = ctypes.c_size_t(0)
+    assert lib.lsa_index_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert lib.lsa_index_init(desc, ctypes.byref(p), ctypes.c_void_p(1 << 40), n.value) == 0
+    return desc
+
+
+def test_training_and_tree_argument_validation_without_device():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("library not built")
+    lib = L.lib()
+    fake = ctypes.c_void_p(1 << 40)
+    p3 = L.IndexParams(64, 4, 256, 32, 2, 2, 16, 2, 1 << 16, 4, 16, 2)
+    desc = _fake_index(lib, p3)
+    # a three-level index needs tree2_top; a two-level one does not
+    sp = L.SelectParams(100, 32, 4, 5)
+    assert lib.lsa_select(desc, fake, fake, 1, ctypes.byref(sp), fake, fake, None, 0, None) == 1
+    assert b"tree2_top" in lib.lsa_last_error()
+    ap = L.AttnParams(8, 2, 128, 0, 0.0)
+    args = lambda spp, nq, qpos0, kv: (desc, fake, fake, fake, kv, fake, fake, spp.max_sel, nq,
+                                       qpos0, ctypes.byref(spp), ctypes.byref(ap), fake, fake,
+                                       fake, fake, fake, fake, fake, 1 << 30, None)
+    sp1 = L.SelectParams(100, 32, 65, 0)
+    assert lib.lsa_sparse_attn_bwd(*args(sp1, 4, 0, 1000)) == 2          # sinks > 64
+    sp2 = L.SelectParams(100, 32, 4, 0)
+    assert lib.lsa_sparse_attn_bwd(*args(sp2, 4, 0, 1000)) == 1          # beyond the index's T = 0
+    assert b"beyond" in lib.lsa_last_error()
+    assert lib.lsa_sparse_attn_bwd(*args(sp2, 4, 999, 1000)) == 1        # beyond kv_rows
+    assert lib.lsa_sparse_attn_bwd(*args(sp2, 0, 0, 1000)) == 0          # empty batch: nothing to do
+    bad_ap = L.AttnParams(8, 3, 128, 0, 0.0)
+    assert lib.lsa_sparse_attn_fwd(fake, fake, fake, 1000, fake, fake, sp2.max_sel, 4, 0,
+                                   ctypes.byref(sp2), ctypes.byref(bad_ap), fake, fake, None) == 2
+    assert lib.lsa_sparse_attn_fwd(fake, fake, fake, 1000, fake, fake, sp2.max_sel, 4, 0,
+                                   ctypes.byref(sp2), ctypes.byref(ap), fake, None, None) == 1
+    # early budget beyond the budget
+    sp3 = L.SelectParams(100, 32, 4, 5, 200, 10, 2)
+    assert lib.lsa_select(desc, fake, fake, 1, ctypes.byref(sp3), fake, fake, None, 0, None) == 1
+    assert b"early_budget" in lib.lsa_last_error()
