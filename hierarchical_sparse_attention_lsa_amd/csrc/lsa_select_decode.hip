@@ -11,11 +11,16 @@
 //                 the int8 dot product (v_dot4), the bucket's eligible keys
 //                 for the new position and the order key go to the workspace;
 //   k_dec_select  one 1024-thread workgroup per sequence holds its buckets'
-//                 keys in registers, finds the exact cutoff by histogram
-//                 refinement (bins in LDS), sorts the <= 256 entries of the
-//                 final bracket, and writes the row: a block-wide prefix sum
-//                 over the threads (which own consecutive bucket ids) gives
-//                 every taken bucket its output offset in ascending id order.
+//                 scores in registers and bins them in an LDS histogram on a
+//                 log scale of the score; the bin where the eligible keys
+//                 reach the budget is the cutoff bin: buckets above it are
+//                 taken whole, its own (few) buckets are ranked by order key
+//                 and taken in turn.  The taken buckets are put in ascending
+//                 id order through a bitmap, and a prefix sum gives each its
+//                 output offset.  A cutoff bin with more than BCAP buckets
+//                 (many equal scores) takes the general path: histogram
+//                 refinement of the order-key range until the bracket holding
+//                 the cutoff has at most 256 entries, which are sorted.
 #include <climits>
 #include <cstring>
 
@@ -33,7 +38,28 @@ constexpr int DW = DT / 64;
 constexpr int PERT_MAX = 24;        // buckets per thread (indexes of up to 24576 buckets)
 constexpr int RB = 256;
 constexpr int RCAP = 256;
-constexpr int dec_lds(int pert) { return pert * DT * 4; }
+// Score bins of the decode histogram, monotone in the score: magnitudes below
+// 64 get a bin each, larger ones 64 bins per power of two (relative width
+// 1/64), negative scores mirrored below zero.  |q . mu| <= 64 * 128 * 128 =
+// 2^20, so a magnitude code stays below 1024 and a bin below NBIN.
+constexpr int NBIN = 2048;
+__device__ __forceinline__ int mag_code(int u) {
+  if (u < 64) return u;
+  const int e = 31 - __clz(u);
+  return 64 + ((e - 6) << 6) + ((u >> (e - 6)) & 63);
+}
+__device__ __forceinline__ int score_bin(int s) { return s >= 0 ? 1024 + mag_code(s) : 1023 - mag_code(-s); }
+// Every taken bucket gives at least one key and the budget is at most 4096
+// keys, so at most 4096 buckets are taken.
+constexpr int TCAP = 4096;
+constexpr int BCAP = 256;           // buckets of the cutoff bin the fast path ranks
+static_assert(BCAP <= RCAP && BCAP <= DT, "the cutoff bin uses the bracket arrays, one thread per entry");
+static_assert(TCAP % DT == 0 && DT * PERT_MAX / 32 <= DT, "list and bitmap shapes");
+
+// dynamic LDS: the general path's per-bucket array, or the fast path's
+// histogram and lists
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int dec_lds(int pert) { return cmax(pert * DT, cmax(2 * NBIN, 5 * TCAP + 2 * (DT * pert / 32))) * 4; }
 constexpr int list_cap(int pert) { return pert * DT / 2; }   // taken buckets the emission list holds
 
 struct DecViews {                   // first kernel argument (read through the kernarg pointer)
@@ -49,13 +75,10 @@ struct DecWs {
   int32_t* kstart;                  // [nseq][cap] first eligible key slot
 };
 
-__global__ void __launch_bounds__(256) k_dec_score(DecViews VS, SelArgs A, DecWs W) {
-  const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
-  const int seq = blockIdx.y;
-  const IdxView V = vsp->v[seq];
-  const int beta = blockIdx.x * 256 + threadIdx.x;
-  if (beta >= V.n_bkt) return;
-  const int t = vsp->qpos[seq];
+
+
+__device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, const DecWs& W, int t,
+                                          int seq, int cap, int beta) {
   const int* q4 = reinterpret_cast<const int*>(A.latq + (int64_t)seq * kDim);
   const int4* c4 = reinterpret_cast<const int4*>(V.cent + (int64_t)beta * kDim);
   int acc = 0;
@@ -70,11 +93,20 @@ __global__ void __launch_bounds__(256) k_dec_score(DecViews VS, SelArgs A, DecWs
   const BucketInfo bi = load_bucket<false>(V, beta);
   int klo;
   const int e = eligible<false>(V, beta, bi, t, A.window, A.sinks, &klo);
-  const int64_t at = (int64_t)seq * VS.cap + beta;
+  const int64_t at = (int64_t)seq * cap + beta;
   W.score[at] = acc;
   W.elig[at] = e;
   W.kstart[at] = bi.off * V.pool + klo;
 }
+
+__global__ void __launch_bounds__(256) k_dec_score(DecViews VS, SelArgs A, DecWs W) {
+  const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int seq = blockIdx.y;
+  const IdxView V = vsp->v[seq];
+  const int beta = blockIdx.x * 256 + threadIdx.x;
+  if (beta < V.n_bkt) score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta);
+}
+
 
 // Order key from a score and a bucket id, recomputed where it is used: the
 // empty asm keeps the compiler from hoisting all of a thread's keys out of the
@@ -111,6 +143,180 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   if (n > DT * PERT) {                 // too large for registers: the exact kernel serves it
     if (tid == 0) flags[seq] = 1;
     return;
+  }
+  int32_t* row = A.idx + (int64_t)seq * A.max_sel;
+  // the window and the sinks after `out` taken keys, -1 padding, the count
+  auto finish_row = [&](int out) {
+    if (wave == 0) {
+      const int wstart = max(0, t - A.window + 1);
+      const int ns = max(0, min(A.sinks, wstart));
+      const int nw = t - wstart + 1;
+      for (int k = lane; k < ns; k += 64) row[out + k] = k;
+      for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
+      const int totalk = out + ns + nw;
+      for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
+      if (lane == 0) A.cnt[seq] = totalk;
+    }
+  };
+  // out_total keys of the nt taken buckets listed in ascending id: bucket r
+  // starts at output offset l_off[r] and first key slot l_ks[r]; one output
+  // key per thread and round, four rounds in flight
+  auto emit_keys = [&](const int* l_off, const int* l_ks, int nt, int out_total) {
+    for (int o0 = tid; o0 < out_total; o0 += 4 * DT) {
+      int sl[4], g[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = o0 + j * DT;
+        sl[j] = 0;
+        if (o < out_total) {
+          int a = 0, b = nt - 1;       // last entry with l_off <= o
+          while (a < b) {
+            const int m = (a + b + 1) >> 1;
+            if (l_off[m] <= o) a = m; else b = m - 1;
+          }
+          sl[j] = l_ks[a] + (o - l_off[a]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[j] = o0 + j * DT < out_total ? V.bmem[sl[j] / p] : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (o0 + j * DT < out_total) row[o0 + j * DT] = g[j] * p + sl[j] % p;
+    }
+  };
+
+  // ---- fast path: the cutoff located in a score histogram ----
+  // Buckets whose score bin lies above the bin where the eligible keys reach
+  // the budget are taken whole; the buckets of that bin are ranked by order
+  // key and taken in turn, the last one cut.  A cutoff bin of more than BCAP
+  // buckets (many equal or near-equal scores) leaves it to the general path.
+  {
+    __shared__ int s_fc[3];            // cut bin, keys above it, buckets in it
+    __shared__ int s_nt, s_nb;
+    __shared__ int s_ce[BCAP], s_ck[BCAP], s_re[BCAP], s_rs[BCAP];
+    unsigned long long* hist = reinterpret_cast<unsigned long long*>(s_e);   // [NBIN] keys << 32 | buckets
+    int scv[PERT], ev[PERT], ksv[PERT];
+#pragma unroll
+    for (int u = 0; u < PERT; ++u) {
+      const int j = u * DT + tid;
+      scv[u] = j < n ? W.score[base + j] : 0;
+      ev[u] = j < n ? W.elig[base + j] : 0;
+      ksv[u] = j < n ? W.kstart[base + j] : 0;
+    }
+    for (int b = tid; b < NBIN; b += DT) hist[b] = 0ull;
+    if (tid == 0) { s_fc[0] = NBIN; s_fc[1] = 0; s_fc[2] = 0; s_nt = 0; s_nb = 0; }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PERT; ++u)
+      if (ev[u] > 0) atomicAdd(&hist[score_bin(scv[u])], ((unsigned long long)ev[u] << 32) | 1ull);
+    __syncthreads();
+    // bins from the top score down: thread tid takes bins NBIN-1-2tid, NBIN-2-2tid
+    int he[2], hc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const unsigned long long h = hist[NBIN - 1 - (2 * tid + j)];
+      he[j] = (int)(h >> 32);
+      hc[j] = (int)(h & 0xffffffffull);
+    }
+    // a thread's sum saturates at B + 1: every prefix below the budget stays exact
+    int te;
+    const int pe = block_excl_scan<DT>(min(he[0] + he[1], B + 1), s_ired, &te);
+    if (B > 0 && te <= B) {            // every eligible bucket is taken whole
+      if (tid == 0) { s_fc[0] = -1; s_fc[1] = te; }
+    } else if (B > 0) {                // the bin where the keys above reach the budget
+      int ce = pe;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (ce < B && he[j] >= B - ce) { s_fc[0] = NBIN - 1 - (2 * tid + j); s_fc[1] = ce; s_fc[2] = hc[j]; }
+        ce = he[j] >= B - ce ? B : ce + he[j];
+      }
+    }
+    __syncthreads();
+    const int cut = s_fc[0], above = s_fc[1], ncut = s_fc[2];
+    if (ncut <= BCAP) {                // uniform; else the general path below
+      constexpr int NBW = DT * PERT / 32;
+      int* ids = s_e;                  // [TCAP] taken bucket ids, any order; later output offsets
+      int* tks = s_e + TCAP;           // [TCAP] keys taken from them
+      int* kss = s_e + 2 * TCAP;       // [TCAP] their first key slots
+      int* stk = s_e + 3 * TCAP;       // [TCAP] keys taken, ascending bucket id
+      int* sks = s_e + 4 * TCAP;       // [TCAP] first key slots, ascending bucket id
+      unsigned* bm = reinterpret_cast<unsigned*>(s_e + 5 * TCAP);   // taken-id bitmap
+      int* wp = s_e + 5 * TCAP + NBW;                               // taken ids before each word
+      for (int w = tid; w < NBW; w += DT) bm[w] = 0u;
+      // one pass over the registers: above the cut bin taken whole, the cut bin collected
+#pragma unroll
+      for (int u = 0; u < PERT; ++u) {
+        if (ev[u] <= 0) continue;
+        const int j = u * DT + tid;
+        const int b = score_bin(scv[u]);
+        if (b > cut) {
+          const int pos = atomicAdd(&s_nt, 1);
+          if (pos < TCAP) { ids[pos] = j; tks[pos] = ev[u]; kss[pos] = ksv[u]; }
+        } else if (b == cut) {
+          const int pos = atomicAdd(&s_nb, 1);
+          if (pos < BCAP) { s_cq[pos] = order_key(scv[u], j); s_ci[pos] = j; s_ce[pos] = ev[u]; s_ck[pos] = ksv[u]; }
+        }
+      }
+      __syncthreads();
+      const int nb = min(s_nb, BCAP);
+      if (nb > 0) {                    // uniform
+        // rank in the cut bin (order keys are distinct): larger keys first
+        if (tid < nb) {
+          const long long k = s_cq[tid];
+          int r = 0;
+          for (int i = 0; i < nb; ++i) r += s_cq[i] > k ? 1 : 0;
+          s_re[r] = s_ce[tid];
+          s_rs[r] = tid;
+        }
+        __syncthreads();
+        int tot;
+        const int x = tid < nb ? s_re[tid] : 0;
+        const int before = block_excl_scan<DT>(x, s_ired, &tot);
+        const int tk = max(0, min(x, B - above - before));
+        if (tk > 0) {
+          const int sl = s_rs[tid];
+          const int pos = atomicAdd(&s_nt, 1);
+          if (pos < TCAP) { ids[pos] = s_ci[sl]; tks[pos] = tk; kss[pos] = s_ck[sl]; }
+        }
+      }
+      __syncthreads();
+      const int nt = min(s_nt, TCAP);
+      // ascending ids: an entry's rank is the number of taken ids below it
+      for (int i = tid; i < nt; i += DT) atomicOr(&bm[ids[i] >> 5], 1u << (ids[i] & 31));
+      __syncthreads();
+      int totw;
+      const int wpre = block_excl_scan<DT>(tid < NBW ? __popc(bm[tid]) : 0, s_ired, &totw);
+      if (tid < NBW) wp[tid] = wpre;
+      __syncthreads();
+      for (int i = tid; i < nt; i += DT) {
+        const int id = ids[i], w = id >> 5;
+        const int r = wp[w] + __popc(bm[w] & ((1u << (id & 31)) - 1u));
+        stk[r] = tks[i];
+        sks[r] = kss[i];
+      }
+      __syncthreads();
+      // output offsets: thread tid sums entries [tid*ENT, tid*ENT + ENT)
+      constexpr int ENT = TCAP / DT;
+      int loc = 0;
+#pragma unroll
+      for (int k = 0; k < ENT; ++k) {
+        const int r = tid * ENT + k;
+        loc += r < nt ? stk[r] : 0;
+      }
+      int out_total;
+      int off = block_excl_scan<DT>(loc, s_ired, &out_total);   // its barriers end the reads of ids
+      int* soff = ids;
+#pragma unroll
+      for (int k = 0; k < ENT; ++k) {
+        const int r = tid * ENT + k;
+        if (r < nt) { soff[r] = off; off += stk[r]; }
+      }
+      __syncthreads();
+      emit_keys(soff, sks, nt, out_total);
+      finish_row(out_total);
+      if (tid == 0) flags[seq] = 0;
+      return;
+    }
   }
   // thread tid holds the scores of buckets u*DT + tid (coalesced loads; the
   // order key is rebuilt from the score and the implicit bucket id); the
@@ -303,41 +509,9 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     }
   }
   __syncthreads();
-  int32_t* row = A.idx + (int64_t)seq * A.max_sel;
   if (ok) {
-    // one output key per thread and round, four rounds in flight
-    for (int o0 = tid; o0 < out_total; o0 += 4 * DT) {
-      int sl[4], g[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = o0 + j * DT;
-        sl[j] = 0;
-        if (o < out_total) {
-          int a = 0, b = nt - 1;       // last entry with l_off <= o
-          while (a < b) {
-            const int m = (a + b + 1) >> 1;
-            if (l_off[m] <= o) a = m; else b = m - 1;
-          }
-          sl[j] = l_ks[a] + (o - l_off[a]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) g[j] = o0 + j * DT < out_total ? V.bmem[sl[j] / p] : 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (o0 + j * DT < out_total) row[o0 + j * DT] = g[j] * p + sl[j] % p;
-    }
-  }
-  if (wave == 0 && ok) {
-    const int out = out_total;
-    const int wstart = max(0, t - A.window + 1);
-    const int ns = max(0, min(A.sinks, wstart));
-    const int nw = t - wstart + 1;
-    for (int k = lane; k < ns; k += 64) row[out + k] = k;
-    for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
-    const int totalk = out + ns + nw;
-    for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
-    if (lane == 0) A.cnt[seq] = totalk;
+    emit_keys(l_off, l_ks, nt, out_total);
+    finish_row(out_total);
   }
   if (tid == 0) flags[seq] = ok ? 0 : 1;
 #undef KEY

@@ -600,6 +600,50 @@ def test_decode_sixteen_sequences():
                       sp, ap, ws=ws)
 
 
+def test_decode_tied_scores_and_small_budgets():
+    """Decode with every score tied (a zero latent query: one score bin holds
+    all 322 buckets, more than the cutoff bin a direct ranking takes), budgets
+    of 0, 7, 150 and one above every eligible key, next to an ordinary query."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("dec_ties", 63, T=4 * 64 * 20 + 11, ncomp=16, block=64, buckets=16, iters=2,
+                    chunk=0, budget=150, window=16, sinks=2, Hq=4, Hkv=2, D=64)
+    gens = [S.Synth(wl, seq=i, data_cfg=63) for i in range(2)]
+    cap = wl.T + 1
+    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, cap)
+    op = _oparams(wl)
+    K = torch.empty((2, cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    lat = [g.latk(0, cap) for g in gens]
+    for i, g in enumerate(gens):
+        g.fill_rows("k", K[i], 0)
+        g.fill_rows("v", V[i], 0)
+    Kd, Vd = K.to(dev), V.to(dev)
+    t = wl.T
+    lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i in range(2)])
+    lq[0] = 0
+    q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i in range(2)])
+    lk_new = torch.stack([lat[i][t] for i in range(2)])
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    for budget in (0, 7, 150, 4096):
+        ixs = []
+        for i in range(2):
+            ix = L.LsaIndex(ip, dev)
+            ix.build(lat[i][:t].to(dev))
+            ixs.append(ix)
+        sp = L.SelectParams(budget, wl.window, wl.sinks, 0)
+        osp = O.SelectParams(budget, wl.window, wl.sinks)
+        ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, 2), dtype=torch.uint8,
+                         device=dev)
+        L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kd, Vd, cap, sp, ap, ws=ws)
+        idx, cnt = L.decode_selection(ws, 2, sp)
+        torch.cuda.synchronize()
+        for i in range(2):
+            sel = O.select(O.build_index(lat[i].numpy(), t + 1, op), lq[i].numpy(), t, osp)
+            n = int(cnt[i])
+            assert np.array_equal(np.sort(idx[i, :n].cpu().numpy()), sel), f"seq {i} budget {budget}"
+
+
 def test_tree_decode_steps_match_oracle():
     """Decode on Tree indexes: sequences of different lengths, one without a
     complete group until its third step (its super level is built during
