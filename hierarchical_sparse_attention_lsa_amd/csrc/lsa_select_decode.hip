@@ -7,20 +7,21 @@
 //
 // A decode step has few queries and a small index per sequence, so the work
 // is spread differently from prefill:
-//   k_dec_score   one thread per (sequence, bucket) across many workgroups:
+//   k_dec_score   one thread per (sequence, bucket), 1024-bucket workgroups:
 //                 the int8 dot product (v_dot4), the bucket's eligible keys
-//                 for the new position and the order key go to the workspace;
-//   k_dec_select  one 1024-thread workgroup per sequence holds its buckets'
-//                 scores in registers and bins them in an LDS histogram on a
-//                 log scale of the score; the bin where the eligible keys
-//                 reach the budget is the cutoff bin: buckets above it are
-//                 taken whole, its own (few) buckets are ranked by order key
-//                 and taken in turn.  The taken buckets are put in ascending
-//                 id order through a bitmap, and a prefix sum gives each its
-//                 output offset.  A cutoff bin with more than BCAP buckets
-//                 (many equal scores) takes the general path: histogram
-//                 refinement of the order-key range until the bracket holding
-//                 the cutoff has at most 256 entries, which are sorted.
+//                 for the new position and its first key slot go to the
+//                 workspace, and each workgroup writes its histogram of
+//                 eligible keys over score bins (a log scale of the score);
+//   k_dec_select  one 1024-thread workgroup per sequence sums the partial
+//                 histograms; the bin where the eligible keys reach the
+//                 budget is the cutoff bin: buckets above it are taken whole,
+//                 its own (few) buckets are ranked by order key and taken in
+//                 turn.  The taken buckets are put in ascending id order
+//                 through a bitmap, and a prefix sum gives each its output
+//                 offset.  A cutoff bin with more than BCAP buckets (many
+//                 equal scores) takes the general path: histogram refinement
+//                 of the order-key range until the bracket holding the cutoff
+//                 has at most 256 entries, which are sorted.
 #include <climits>
 #include <cstring>
 
@@ -49,6 +50,19 @@ __device__ __forceinline__ int mag_code(int u) {
   return 64 + ((e - 6) << 6) + ((u >> (e - 6)) & 63);
 }
 __device__ __forceinline__ int score_bin(int s) { return s >= 0 ? 1024 + mag_code(s) : 1023 - mag_code(-s); }
+// the magnitudes [lo, hi] with code c
+__device__ __forceinline__ void code_range(int c, int* lo, int* hi) {
+  if (c < 64) { *lo = *hi = c; return; }
+  const int e = 6 + ((c - 64) >> 6), m = (c - 64) & 63;
+  *lo = (64 + m) << (e - 6);
+  *hi = ((65 + m) << (e - 6)) - 1;
+}
+// the scores [lo, hi] of bin b
+__device__ __forceinline__ void bin_range(int b, int* lo, int* hi) {
+  int a, z;
+  if (b >= 1024) { code_range(b - 1024, &a, &z); *lo = a; *hi = z; }
+  else { code_range(1023 - b, &a, &z); *lo = -z; *hi = -a; }
+}
 // Every taken bucket gives at least one key and the budget is at most 4096
 // keys, so at most 4096 buckets are taken.
 constexpr int TCAP = 4096;
@@ -56,10 +70,9 @@ constexpr int BCAP = 256;           // buckets of the cutoff bin the fast path r
 static_assert(BCAP <= RCAP && BCAP <= DT, "the cutoff bin uses the bracket arrays, one thread per entry");
 static_assert(TCAP % DT == 0 && DT * PERT_MAX / 32 <= DT, "list and bitmap shapes");
 
-// dynamic LDS: the general path's per-bucket array, or the fast path's
-// histogram and lists
+// dynamic LDS: the general path's per-bucket array, or the fast path's lists
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int dec_lds(int pert) { return cmax(pert * DT, cmax(2 * NBIN, 5 * TCAP + 2 * (DT * pert / 32))) * 4; }
+constexpr int dec_lds(int pert) { return cmax(pert * DT, 4 * TCAP + 2 * (DT * pert / 32)) * 4; }
 constexpr int list_cap(int pert) { return pert * DT / 2; }   // taken buckets the emission list holds
 
 struct DecViews {                   // first kernel argument (read through the kernarg pointer)
@@ -73,12 +86,15 @@ struct DecWs {
   int32_t* score;                   // [nseq][cap] int8 dot products
   int32_t* elig;                    // [nseq][cap] eligible keys
   int32_t* kstart;                  // [nseq][cap] first eligible key slot
+  int32_t* hpart;                   // [nseq][cap / DT rounded up][NBIN] eligible keys per score bin,
+                                    // one histogram per score workgroup
+  int32_t n_part;                   // histograms per sequence
 };
 
 
 
 __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, const DecWs& W, int t,
-                                          int seq, int cap, int beta) {
+                                          int seq, int cap, int beta, int* hist) {
   const int* q4 = reinterpret_cast<const int*>(A.latq + (int64_t)seq * kDim);
   const int4* c4 = reinterpret_cast<const int4*>(V.cent + (int64_t)beta * kDim);
   int acc = 0;
@@ -97,14 +113,23 @@ __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, co
   W.score[at] = acc;
   W.elig[at] = e;
   W.kstart[at] = bi.off * V.pool + klo;
+  if (e > 0) atomicAdd(&hist[score_bin(acc)], e);
 }
 
-__global__ void __launch_bounds__(256) k_dec_score(DecViews VS, SelArgs A, DecWs W) {
+__global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs W) {
+  __shared__ int hist[NBIN];
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int seq = blockIdx.y;
   const IdxView V = vsp->v[seq];
-  const int beta = blockIdx.x * 256 + threadIdx.x;
-  if (beta < V.n_bkt) score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta);
+  if ((int)blockIdx.x * DT >= V.n_bkt) return;      // uniform: past this sequence's index
+  for (int b = threadIdx.x; b < NBIN; b += DT) hist[b] = 0;
+  __syncthreads();
+  const int beta = blockIdx.x * DT + threadIdx.x;
+  if (beta < V.n_bkt) score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta, hist);
+  __syncthreads();
+  // the whole histogram, zeros included: nothing has to be cleared beforehand
+  int2* out = reinterpret_cast<int2*>(W.hpart + ((int64_t)seq * W.n_part + blockIdx.x) * NBIN);
+  for (int b = threadIdx.x; b < NBIN / 2; b += DT) out[b] = make_int2(hist[2 * b], hist[2 * b + 1]);
 }
 
 
@@ -185,80 +210,104 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     }
   };
 
-  // ---- fast path: the cutoff located in a score histogram ----
+  // ---- fast path: the cutoff located in the score histogram ----
   // Buckets whose score bin lies above the bin where the eligible keys reach
   // the budget are taken whole; the buckets of that bin are ranked by order
   // key and taken in turn, the last one cut.  A cutoff bin of more than BCAP
   // buckets (many equal or near-equal scores) leaves it to the general path.
   {
-    __shared__ int s_fc[3];            // cut bin, keys above it, buckets in it
+    __shared__ int s_fc[4];            // cut bin, keys above it, its scores [lo, hi]
     __shared__ int s_nt, s_nb;
-    __shared__ int s_ce[BCAP], s_ck[BCAP], s_re[BCAP], s_rs[BCAP];
-    unsigned long long* hist = reinterpret_cast<unsigned long long*>(s_e);   // [NBIN] keys << 32 | buckets
-    int scv[PERT], ev[PERT], ksv[PERT];
+    __shared__ int s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
+    int scv[PERT], ev[PERT];
 #pragma unroll
     for (int u = 0; u < PERT; ++u) {
       const int j = u * DT + tid;
       scv[u] = j < n ? W.score[base + j] : 0;
       ev[u] = j < n ? W.elig[base + j] : 0;
-      ksv[u] = j < n ? W.kstart[base + j] : 0;
     }
-    for (int b = tid; b < NBIN; b += DT) hist[b] = 0ull;
-    if (tid == 0) { s_fc[0] = NBIN; s_fc[1] = 0; s_fc[2] = 0; s_nt = 0; s_nb = 0; }
-    __syncthreads();
+    // bins from the top score down: thread tid takes bins NBIN-1-2tid (he[0])
+    // and NBIN-2-2tid (he[1]), summed over the score workgroups
+    int he[2] = {0, 0};
+    {
+      const int nwg = (n + DT - 1) / DT;
+      const int2* hp = reinterpret_cast<const int2*>(W.hpart + (int64_t)seq * W.n_part * NBIN) + (NBIN / 2 - 1 - tid);
+      int w = 0;
+      for (; w + 4 <= nwg; w += 4) {
+        int2 x[4];
 #pragma unroll
-    for (int u = 0; u < PERT; ++u)
-      if (ev[u] > 0) atomicAdd(&hist[score_bin(scv[u])], ((unsigned long long)ev[u] << 32) | 1ull);
-    __syncthreads();
-    // bins from the top score down: thread tid takes bins NBIN-1-2tid, NBIN-2-2tid
-    int he[2], hc[2];
+        for (int k = 0; k < 4; ++k) x[k] = hp[(int64_t)(w + k) * (NBIN / 2)];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const unsigned long long h = hist[NBIN - 1 - (2 * tid + j)];
-      he[j] = (int)(h >> 32);
-      hc[j] = (int)(h & 0xffffffffull);
+        for (int k = 0; k < 4; ++k) { he[0] += x[k].y; he[1] += x[k].x; }
+      }
+      for (; w < nwg; ++w) {
+        const int2 x = hp[(int64_t)w * (NBIN / 2)];
+        he[0] += x.y;
+        he[1] += x.x;
+      }
     }
+    if (tid == 0) { s_fc[0] = NBIN; s_fc[1] = 0; s_fc[2] = INT_MAX; s_fc[3] = INT_MAX; s_nt = 0; s_nb = 0; }
     // a thread's sum saturates at B + 1: every prefix below the budget stays exact
     int te;
     const int pe = block_excl_scan<DT>(min(he[0] + he[1], B + 1), s_ired, &te);
     if (B > 0 && te <= B) {            // every eligible bucket is taken whole
-      if (tid == 0) { s_fc[0] = -1; s_fc[1] = te; }
+      if (tid == 0) { s_fc[0] = -1; s_fc[1] = te; s_fc[2] = INT_MIN; s_fc[3] = INT_MIN; }
     } else if (B > 0) {                // the bin where the keys above reach the budget
       int ce = pe;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        if (ce < B && he[j] >= B - ce) { s_fc[0] = NBIN - 1 - (2 * tid + j); s_fc[1] = ce; s_fc[2] = hc[j]; }
+        if (ce < B && he[j] >= B - ce) {
+          const int bin = NBIN - 1 - (2 * tid + j);
+          int lo, hi;
+          bin_range(bin, &lo, &hi);
+          s_fc[0] = bin; s_fc[1] = ce; s_fc[2] = lo; s_fc[3] = hi;
+        }
         ce = he[j] >= B - ce ? B : ce + he[j];
       }
     }
     __syncthreads();
-    const int cut = s_fc[0], above = s_fc[1], ncut = s_fc[2];
-    if (ncut <= BCAP) {                // uniform; else the general path below
-      constexpr int NBW = DT * PERT / 32;
-      int* ids = s_e;                  // [TCAP] taken bucket ids, any order; later output offsets
-      int* tks = s_e + TCAP;           // [TCAP] keys taken from them
-      int* kss = s_e + 2 * TCAP;       // [TCAP] their first key slots
-      int* stk = s_e + 3 * TCAP;       // [TCAP] keys taken, ascending bucket id
-      int* sks = s_e + 4 * TCAP;       // [TCAP] first key slots, ascending bucket id
-      unsigned* bm = reinterpret_cast<unsigned*>(s_e + 5 * TCAP);   // taken-id bitmap
-      int* wp = s_e + 5 * TCAP + NBW;                               // taken ids before each word
-      for (int w = tid; w < NBW; w += DT) bm[w] = 0u;
-      // one pass over the registers: above the cut bin taken whole, the cut bin collected
+    const int above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
+    constexpr int NBW = DT * PERT / 32;
+    int* ids = s_e;                    // [TCAP] taken bucket ids, any order; later output offsets
+    int* tks = s_e + TCAP;             // [TCAP] keys taken from them; later first key slots
+    int* sid = s_e + 2 * TCAP;         // [TCAP] taken bucket ids, ascending
+    int* stk = s_e + 3 * TCAP;         // [TCAP] keys taken, ascending bucket id
+    unsigned* bm = reinterpret_cast<unsigned*>(s_e + 4 * TCAP);     // taken-id bitmap
+    int* wp = s_e + 4 * TCAP + NBW;                                 // taken ids before each word
+    // bit u: bucket u*DT + tid lies above the cut bin / in it
+    unsigned m_above = 0, m_cut = 0;
+#pragma unroll
+    for (int u = 0; u < PERT; ++u) {
+      const bool el = ev[u] > 0;
+      m_above |= (el && scv[u] > hi_s ? 1u : 0u) << u;
+      m_cut |= (el && scv[u] >= lo_s && scv[u] <= hi_s ? 1u : 0u) << u;
+    }
+    // buckets above the cut: one slot reservation per wave (at most budget of
+    // them, each giving a key, so they fit in TCAP)
+    {
+      int wt;
+      const int wpre = wave_excl_scan(__popc(m_above), &wt);
+      int wb = 0;
+      if (lane == 0 && wt > 0) wb = atomicAdd(&s_nt, wt);
+      int pos = __shfl(wb, 0) + wpre;
 #pragma unroll
       for (int u = 0; u < PERT; ++u) {
-        if (ev[u] <= 0) continue;
-        const int j = u * DT + tid;
-        const int b = score_bin(scv[u]);
-        if (b > cut) {
-          const int pos = atomicAdd(&s_nt, 1);
-          if (pos < TCAP) { ids[pos] = j; tks[pos] = ev[u]; kss[pos] = ksv[u]; }
-        } else if (b == cut) {
-          const int pos = atomicAdd(&s_nb, 1);
-          if (pos < BCAP) { s_cq[pos] = order_key(scv[u], j); s_ci[pos] = j; s_ce[pos] = ev[u]; s_ck[pos] = ksv[u]; }
-        }
+        if ((m_above & (1u << u)) && pos < TCAP) { ids[pos] = u * DT + tid; tks[pos] = ev[u]; }
+        pos += (m_above >> u) & 1u;
       }
-      __syncthreads();
-      const int nb = min(s_nb, BCAP);
+    }
+    if (m_cut) {
+#pragma unroll
+      for (int u = 0; u < PERT; ++u) {
+        if (!(m_cut & (1u << u))) continue;
+        const int q = atomicAdd(&s_nb, 1);
+        if (q < BCAP) { s_cq[q] = order_key(scv[u], u * DT + tid); s_ci[q] = u * DT + tid; s_ce[q] = ev[u]; }
+      }
+    }
+    for (int w = tid; w < NBW; w += DT) bm[w] = 0u;
+    __syncthreads();
+    const int nb = s_nb;
+    if (nb <= BCAP) {                  // uniform; else the general path below
       if (nb > 0) {                    // uniform
         // rank in the cut bin (order keys are distinct): larger keys first
         if (tid < nb) {
@@ -275,11 +324,11 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
         const int tk = max(0, min(x, B - above - before));
         if (tk > 0) {
           const int sl = s_rs[tid];
-          const int pos = atomicAdd(&s_nt, 1);
-          if (pos < TCAP) { ids[pos] = s_ci[sl]; tks[pos] = tk; kss[pos] = s_ck[sl]; }
+          const int q = atomicAdd(&s_nt, 1);
+          if (q < TCAP) { ids[q] = s_ci[sl]; tks[q] = tk; }
         }
+        __syncthreads();
       }
-      __syncthreads();
       const int nt = min(s_nt, TCAP);
       // ascending ids: an entry's rank is the number of taken ids below it
       for (int i = tid; i < nt; i += DT) atomicOr(&bm[ids[i] >> 5], 1u << (ids[i] & 31));
@@ -291,8 +340,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       for (int i = tid; i < nt; i += DT) {
         const int id = ids[i], w = id >> 5;
         const int r = wp[w] + __popc(bm[w] & ((1u << (id & 31)) - 1u));
+        sid[r] = id;
         stk[r] = tks[i];
-        sks[r] = kss[i];
       }
       __syncthreads();
       // output offsets: thread tid sums entries [tid*ENT, tid*ENT + ENT)
@@ -304,13 +353,15 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
         loc += r < nt ? stk[r] : 0;
       }
       int out_total;
-      int off = block_excl_scan<DT>(loc, s_ired, &out_total);   // its barriers end the reads of ids
+      int off = block_excl_scan<DT>(loc, s_ired, &out_total);   // its barriers end the reads of ids, tks
       int* soff = ids;
+      int* sks = tks;
 #pragma unroll
       for (int k = 0; k < ENT; ++k) {
         const int r = tid * ENT + k;
         if (r < nt) { soff[r] = off; off += stk[r]; }
       }
+      for (int r = tid; r < nt; r += DT) sks[r] = W.kstart[base + sid[r]];
       __syncthreads();
       emit_keys(soff, sks, nt, out_total);
       finish_row(out_total);
@@ -527,6 +578,8 @@ size_t dec_layout(int32_t nseq, int32_t cap, DecWs* W, int32_t** flags, void* ws
   w.score = reinterpret_cast<int32_t*>(take(n * sizeof(int32_t)));
   w.elig = reinterpret_cast<int32_t*>(take(n * sizeof(int32_t)));
   w.kstart = reinterpret_cast<int32_t*>(take(n * sizeof(int32_t)));
+  w.n_part = (cap + DT - 1) / DT;
+  w.hpart = reinterpret_cast<int32_t*>(take((size_t)nseq * w.n_part * NBIN * sizeof(int32_t)));
   int32_t* f = reinterpret_cast<int32_t*>(take((size_t)nseq * sizeof(int32_t)));
   if (W) *W = w;
   if (flags) *flags = f;
@@ -563,7 +616,7 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   if (nmax > DT * PERT_MAX) return launch_select_multi(views, qpos, nseq, b, s);
   const bool small = nmax <= DT * 20;
   if (nmax > 0) {
-    hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + 255) / 256), (unsigned)nseq), dim3(256), 0,
+    hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
                        s, vs, b, W);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
