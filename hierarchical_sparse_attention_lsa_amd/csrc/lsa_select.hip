@@ -70,12 +70,14 @@ struct __attribute__((aligned(16))) SelLds {
 };
 
 
-// Per-launch index views: one shared index (prefill, nviews == 1) or one
-// index per workgroup (decode: workgroup b serves sequence b, one query).
+// Per-launch index views: one shared index (prefill, per_seq == 0) or one
+// index per workgroup (decode, per_seq == 1: workgroup b serves sequence b,
+// one query at position qpos[b], whatever the number of sequences).
 struct IdxViews {
   IdxView v[16];
   int32_t qpos[16];
   int32_t nviews;
+  int32_t per_seq;
 };
 
 // Runs f(bt, scores) for tiles first, first+step, ... < ntiles, with the
@@ -122,7 +124,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
   // this workgroup's index view, read from the kernel-argument segment (VS is
   // the first argument) so the runtime index does not copy VS to scratch
   const IdxViews* vsp = (const IdxViews*)__builtin_amdgcn_kernarg_segment_ptr();
-  const IdxView V = vsp->v[VS.nviews > 1 ? blockIdx.x : 0];
+  const IdxView V = vsp->v[VS.per_seq ? blockIdx.x : 0];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int q0 = blockIdx.x * NQ;
   const int nqt = min(NQ, A.nq - q0);
@@ -139,7 +141,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
   if (tid < QT) {
     const int qi = q0 + tid;
     const bool val = tid < nqt && (!A.only || A.only[qi]);
-    S.t[tid] = val ? max(0, VS.nviews > 1 ? vsp->qpos[blockIdx.x] : (A.qpos ? A.qpos[qi] : A.qpos_base + qi)) : -1;
+    S.t[tid] = val ? max(0, VS.per_seq ? vsp->qpos[blockIdx.x] : (A.qpos ? A.qpos[qi] : A.qpos_base + qi)) : -1;
     S.status[tid] = val ? ST_REFINE : ST_DONE;
     S.smax[tid] = INT_MIN; S.ssum[tid] = 0; S.sn[tid] = 0; S.above[tid] = 0;
     S.nfull[tid] = 0; S.ncand[tid] = 0; S.fullsum[tid] = 0; S.pbeta[tid] = -1; S.ptake[tid] = 0;
@@ -514,6 +516,7 @@ hipError_t launch_select_multi(const IdxView* views, const int32_t* qpos, int32_
     tree |= views[i].leafsup != nullptr;
   }
   vs.nviews = nseq;
+  vs.per_seq = 1;
   SelArgs b = a;
   b.nq = nseq;
   // tree and flat sequences are served by the tree kernel (flat ones have no super level)

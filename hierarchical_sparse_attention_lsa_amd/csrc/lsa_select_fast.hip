@@ -58,7 +58,6 @@ struct FastViews {                  // first kernel argument (read through the k
   IdxView v[16];
   int32_t qpos[16];
   int32_t nviews;
-  int32_t slots_per_view;           // decode: query slots per sequence
   int32_t view_per_query;           // Tree: query q uses view q at position qpos[q]
 };
 
@@ -133,15 +132,13 @@ __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>&
   }
 }
 
-// Prefill (nviews == 1): slot s of workgroup b is query b*QS + s.
-// Decode (nviews > 1): workgroup b serves query b alone (slot 0), on index b.
+// Prefill over one index: slot s of workgroup b is query b*QS + s.
 template <int FW, int QS>
 __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListWs W) {
   using C = Cfg<FW, QS>;
   __shared__ ScanLds<FW, QS> S;
   const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
-  const bool multi = VS.nviews > 1;
-  const IdxView V = vsp->v[multi ? blockIdx.x : 0];
+  const IdxView V = vsp->v[0];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int64_t lbase = (int64_t)blockIdx.x * QS;
   const int qgrp = wave % C::NQW;
@@ -151,9 +148,9 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   const int p = V.pool;
 
   for (int i = tid; i < QS; i += C::FT) {
-    int q = multi ? (i == 0 ? (int)blockIdx.x : -1) : (int)(lbase + i);
+    int q = (int)(lbase + i);
     if (q >= A.nq) q = -1;
-    const int t = q < 0 ? -1 : max(0, multi ? vsp->qpos[blockIdx.x] : (A.qpos ? A.qpos[q] : A.qpos_base + q));
+    const int t = q < 0 ? -1 : max(0, A.qpos ? A.qpos[q] : A.qpos_base + q);
     S.q[i] = q; S.t[i] = t;
     S.smax[i] = INT_MIN; S.ssum[i] = 0; S.sn[i] = 0;
     W.meta[2 * (lbase + i)] = q;
@@ -639,7 +636,7 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
   const int q = W.meta[2 * slot];
   if (q < 0) return;                 // uniform over the workgroup
   const int t = W.meta[2 * slot + 1];
-  const IdxView V = vsp->v[VS.nviews > 1 ? (int)(slot / VS.slots_per_view) : 0];
+  const IdxView V = vsp->v[0];
   const int B = budget_at(A, t);
   const int p = V.pool;
   const long long* lk = W.key + slot * LC;
@@ -934,7 +931,6 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
   memset(&vs, 0, sizeof vs);
   vs.v[0] = v;
   vs.nviews = 1;
-  vs.slots_per_view = (int32_t)slots;
   hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ>), dim3((unsigned)(slots / kPrefQ)), dim3(kPrefW * 64),
                      0, s, vs, a, W);
   hipError_t e = hipGetLastError();

@@ -644,6 +644,63 @@ def test_decode_tied_scores_and_small_budgets():
             assert np.array_equal(np.sort(idx[i, :n].cpu().numpy()), sel), f"seq {i} budget {budget}"
 
 
+def test_decode_large_indexes():
+    """Decode over indexes of about 19k, 22k and 25.6k buckets: 24 buckets per
+    select thread, 19 and 22 partial score histograms (not multiples of four),
+    and, past 24576 buckets, the hand-off to the prefill selection kernel."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("dec_large", 64, T=0, ncomp=128, block=64, buckets=32, iters=2, chunk=0,
+                    budget=512, window=64, sinks=4, Hq=4, Hkv=2, D=64)
+    steps = 2
+    # full blocks of 64 pooled vectors give 32 buckets each; tails are singletons
+    Ts = [4 * 64 * 594 + 4 * 17 + 1, 4 * 64 * 687 + 4 * 40 + 3, 4 * 64 * 800 + 11]
+    nbk = [594 * 32 + 17, 687 * 32 + 40, 800 * 32 + 2]
+    assert nbk[0] <= 20480 < nbk[1] <= 24576 < nbk[2]
+    cap = max(Ts) + steps
+    op = _oparams(wl)
+    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, cap)
+    gens = [S.Synth(wl, seq=i, data_cfg=64) for i in range(3)]
+    lat = [g.latk(0, cap) for g in gens]
+    K = torch.empty((3, cap, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    for i, g in enumerate(gens):
+        g.fill_rows("k", K[i], 0, chunk=1 << 16)
+        g.fill_rows("v", V[i], 0, chunk=1 << 16)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    caches = [dict() for _ in range(3)]
+    for batch in ([0, 1], [2]):
+        ixs = []
+        for i in batch:
+            ix = L.LsaIndex(ip, dev)
+            ix.build(lat[i][:Ts[i]].to(dev))
+            assert ix.info().n_bkt == nbk[i]
+            ixs.append(ix)
+        # one K/V cache per batch: the sequences of a decode step are rows of one tensor
+        Kb, Vb = K[batch].contiguous(), V[batch].contiguous()
+        ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, len(batch)),
+                         dtype=torch.uint8, device=dev)
+        for step in range(steps):
+            ts = [Ts[i] + step for i in batch]
+            lk_new = torch.stack([lat[i][t] for i, t in zip(batch, ts)])
+            lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i, t in zip(batch, ts)])
+            q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i, t in zip(batch, ts)])
+            print(f"decode batch {batch} step {step}", flush=True)
+            out = L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kb, Vb, cap, sp, ap, ws=ws)
+            idx, cnt = L.decode_selection(ws, len(batch), sp)
+            torch.cuda.synchronize()
+            for b, (i, t) in enumerate(zip(batch, ts)):
+                ref = O.build_index(lat[i].numpy(), t + 1, op, cache=caches[i])
+                sel = O.select(ref, lq[b].numpy(), t, osp)
+                n = int(cnt[b])
+                assert np.array_equal(np.sort(idx[b, :n].cpu().numpy()), sel), f"seq {i} step {step}"
+                err = normwise(out[b].cpu().numpy().astype(np.float64),
+                               oracle_attention(gens[i], wl, [t], [sel])[0])
+                assert err <= TOL, (i, step, err)
+
+
 def test_tree_decode_steps_match_oracle():
     """Decode on Tree indexes: sequences of different lengths, one without a
     complete group until its third step (its super level is built during
@@ -697,6 +754,51 @@ def test_tree_decode_steps_match_oracle():
     for i in range(len(Ts)):
         check_index(ixs[i].arrays(), O.build_index(lat[i].numpy(), Ts[i] + steps, op))
     assert max(errs) <= TOL
+
+
+def test_single_sequence_tree_decode_with_tied_scores():
+    """One sequence on a Tree index, first with a zero latent query (every
+    score tied), then an ordinary one: ties send the sequence to the exact
+    refinement, which must serve a batch of one at its own position."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("dec_tree1", 61, T=0, ncomp=64, block=64, buckets=16, iters=3, tree_group=4,
+                    tree_super=16, tree_iters=3, tree_top=5, chunk=0, budget=200, window=32,
+                    sinks=4, Hq=8, Hkv=2, D=64)
+    T0 = 2 * wl.pool * wl.block * wl.tree_group + 500
+    cap = T0 + 2
+    g = S.Synth(wl, seq=0, data_cfg=61)
+    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
+                       wl.tree_iters, cap)
+    lat = g.latk(0, cap)
+    ix = L.LsaIndex(ip, dev)
+    ix.build(lat[:T0].to(dev))
+    K = torch.empty((1, cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K[0], 0)
+    g.fill_rows("v", V[0], 0)
+    Kd, Vd = K.to(dev), V.to(dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, 1), dtype=torch.uint8,
+                     device=dev)
+    for step in range(2):
+        t = T0 + step
+        lq = g.latq_rows(torch.tensor([t]))
+        if step == 0:
+            lq.zero_()
+        q = g.q_rows(torch.tensor([t]))
+        out = L.decode_step([ix], lat[t:t + 1].to(dev), lq.to(dev), q.to(dev), Kd, Vd, cap, sp, ap,
+                            ws=ws)
+        idx, cnt = L.decode_selection(ws, 1, sp)
+        torch.cuda.synchronize()
+        sel = O.select(O.build_index(lat.numpy(), t + 1, _oparams(wl)), lq[0].numpy(), t, osp)
+        n = int(cnt[0])
+        assert np.array_equal(np.sort(idx[0, :n].cpu().numpy()), sel), f"step {step}"
+        err = normwise(out[0].cpu().numpy().astype(np.float64),
+                       oracle_attention(g, wl, [t], [sel])[0])
+        assert err <= TOL, (step, err)
 
 
 def test_api_errors_leave_index_unchanged(tiny):
