@@ -674,7 +674,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
     da.batched[i] = 1;
     any_batched = true;
   }
-  if (any_batched) LSA_HIP(launch_decode_append(da, d_latk_new, nseq, s), "decode append");
+  // (the batched append itself is enqueued by the selection below, first)
   for (int i = 0; i < nseq; ++i) {
     if (!da.batched[i]) continue;
     Index* h = as_index(hs[i]);
@@ -687,8 +687,11 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   IdxView views[16];
   for (int i = 0; i < nseq; ++i) {
     views[i] = view_of(as_index(hs[i]));
-    if (views[i].leafsup && views[i].n_sup > 2048)
+    if (views[i].leafsup && views[i].n_sup > 2048) {
+      // the counters above have advanced: the appended keys still go in
+      if (any_batched) LSA_HIP(launch_decode_append(da, d_latk_new, nseq, s), "decode append");
       return fail(LSA_E_UNSUPPORTED, "%d super clusters (at most 2048)", views[i].n_sup);
+    }
   }
   SelArgs a;
   memset(&a, 0, sizeof a);
@@ -696,7 +699,9 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
   a.early_budget = sp->early_budget; a.early_until = sp->early_until; a.tree2_top = sp->tree2_top;
   a.max_sel = max_sel; a.idx = idx; a.cnt = cnt; a.only = nullptr;
-  LSA_HIP(launch_select_dec(views, qpos, nseq, h0->max_bkt, a, selws, s), "decode select");
+  LSA_HIP(launch_select_dec(views, qpos, nseq, h0->max_bkt, a, selws, s, any_batched ? &da : nullptr,
+                            d_latk_new),
+          "decode append + select");
 
   // 3. split-K attention over each sequence's own rows, then the merge
   LSA_HIP(launch_attn(d_q, d_k, d_v, seq_stride_rows, seq_stride_rows, 1, idx, cnt, max_sel,

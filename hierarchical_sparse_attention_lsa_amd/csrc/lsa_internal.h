@@ -131,10 +131,14 @@ hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipS
 // flags: nseq ints of workspace
 hipError_t launch_select_tree_multi(const IdxView* views, const int32_t* qpos, int32_t nseq,
                                    const SelArgs& a, int32_t* flags, hipStream_t s);
-// decode: one query per sequence, each on its own index (max_bkt = bucket capacity)
+// decode: one query per sequence, each on its own index (max_bkt = bucket
+// capacity).  app (nullable): the one-key append of the batched sequences,
+// enqueued before the selection (fused into its first kernel where it can);
+// views describe the indexes after that append.
 size_t select_dec_ws_bytes(int32_t nseq, int64_t max_bkt);
 hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t nseq,
-                             int64_t max_bkt, const SelArgs& a, void* ws, hipStream_t s);
+                             int64_t max_bkt, const SelArgs& a, void* ws, hipStream_t s,
+                             const DecodeAppendArgs* app, const int8_t* app_src);
 
 size_t attn_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t splits);
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t kv_rows,

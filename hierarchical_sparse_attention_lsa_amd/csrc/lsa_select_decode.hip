@@ -93,10 +93,13 @@ struct DecWs {
 
 
 
+// crow: the bucket's centroid (global memory, or LDS for a bucket appended by
+// this workgroup); bi: its descriptor
 __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, const DecWs& W, int t,
-                                          int seq, int cap, int beta, int* hist) {
+                                          int seq, int cap, int beta, const int8_t* crow,
+                                          const BucketInfo& bi, int* hist) {
   const int* q4 = reinterpret_cast<const int*>(A.latq + (int64_t)seq * kDim);
-  const int4* c4 = reinterpret_cast<const int4*>(V.cent + (int64_t)beta * kDim);
+  const int4* c4 = reinterpret_cast<const int4*>(crow);
   int acc = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -106,7 +109,6 @@ __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, co
     acc = __builtin_amdgcn_sdot4(q4[4 * k + 2], c.z, acc, false);
     acc = __builtin_amdgcn_sdot4(q4[4 * k + 3], c.w, acc, false);
   }
-  const BucketInfo bi = load_bucket<false>(V, beta);
   int klo;
   const int e = eligible<false>(V, beta, bi, t, A.window, A.sinks, &klo);
   const int64_t at = (int64_t)seq * cap + beta;
@@ -116,16 +118,67 @@ __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, co
   if (e > 0) atomicAdd(&hist[score_bin(acc)], e);
 }
 
-__global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs W) {
+// The one-key append of each batched sequence is done here too (one launch
+// less per step): the key goes to the pending buffer, or, when it completes
+// a pooled group, the workgroup holding the new singleton bucket pools it,
+// writes the bucket and scores it from LDS.  No other workgroup reads the new
+// bucket, and the selection kernel runs after this one.
+__global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs W, DecodeAppendArgs D,
+                                                  const int8_t* __restrict__ src) {
   __shared__ int hist[NBIN];
+  __shared__ __attribute__((aligned(16))) int8_t s_pv[kDim];
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int seq = blockIdx.y;
   const IdxView V = vsp->v[seq];
-  if ((int)blockIdx.x * DT >= V.n_bkt) return;      // uniform: past this sequence's index
+  int beta_new = -1;
+  int64_t g_new = 0;
+  if (D.batched[seq]) {                                 // uniform
+    char* abase = D.arena[seq];
+    int8_t* pend = reinterpret_cast<int8_t*>(abase + D.off_pend) + (int64_t)D.pend_slot[seq] * D.p * kDim;
+    const int np = D.n_pend[seq];
+    if (np + 1 < D.p) {
+      if (blockIdx.x == 0 && threadIdx.x < kDim)
+        pend[np * kDim + threadIdx.x] = src[(int64_t)seq * kDim + threadIdx.x];
+    } else {
+      g_new = D.n_pool[seq];
+      const int64_t nf = D.n_full[seq];
+      const int64_t bn = nf * D.C + (g_new - nf * D.N);
+      if ((int64_t)blockIdx.x == bn / DT) {             // uniform
+        beta_new = (int)bn;
+        if (threadIdx.x < kDim) {
+          const int d = threadIdx.x;
+          int sum = src[(int64_t)seq * kDim + d];
+          for (int r = 0; r < np; ++r) sum += pend[r * kDim + d];
+          const int8_t pv = (int8_t)rhe_div(sum, D.p);
+          s_pv[d] = pv;
+          reinterpret_cast<int8_t*>(abase + D.off_pooled)[g_new * kDim + d] = pv;
+          reinterpret_cast<int8_t*>(abase + D.off_cent)[bn * kDim + d] = pv;
+          if (d == 0) {
+            reinterpret_cast<int32_t*>(abase + D.off_bcnt)[bn] = 1;
+            reinterpret_cast<int32_t*>(abase + D.off_boff)[bn] = (int32_t)g_new;
+            reinterpret_cast<int32_t*>(abase + D.off_bmem)[g_new] = (int32_t)g_new;
+            reinterpret_cast<int32_t*>(abase + D.off_bfirst)[bn] = (int32_t)g_new;
+            reinterpret_cast<int32_t*>(abase + D.off_blast)[bn] = (int32_t)g_new;
+          }
+        }
+      }
+    }
+  }
+  if ((int)blockIdx.x * DT >= V.n_bkt) return;          // uniform: past this sequence's index
   for (int b = threadIdx.x; b < NBIN; b += DT) hist[b] = 0;
-  __syncthreads();
+  __syncthreads();                                      // (also publishes the appended bucket here)
   const int beta = blockIdx.x * DT + threadIdx.x;
-  if (beta < V.n_bkt) score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta, hist);
+  if (beta < V.n_bkt) {
+    if (beta == beta_new) {
+      BucketInfo bi;
+      bi.first = bi.last = bi.off = (int)g_new;
+      bi.cnt = 1;
+      score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta, s_pv, bi, hist);
+    } else {
+      score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta, V.cent + (int64_t)beta * kDim,
+                load_bucket<false>(V, beta), hist);
+    }
+  }
   __syncthreads();
   // the whole histogram, zeros included: nothing has to be cleared beforehand
   int2* out = reinterpret_cast<int2*>(W.hpart + ((int64_t)seq * W.n_part + blockIdx.x) * NBIN);
@@ -593,7 +646,8 @@ size_t select_dec_ws_bytes(int32_t nseq, int64_t max_bkt) {
 }
 
 hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t nseq,
-                             int64_t max_bkt, const SelArgs& a, void* ws, hipStream_t s) {
+                             int64_t max_bkt, const SelArgs& a, void* ws, hipStream_t s,
+                             const DecodeAppendArgs* app, const int8_t* app_src) {
   if (nseq <= 0) return hipSuccess;
   DecViews vs;
   memset(&vs, 0, sizeof vs);
@@ -612,12 +666,20 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   DecWs W;
   int32_t* flags;
   dec_layout(nseq, vs.cap, &W, &flags, ws);
+  // the append rides on the score kernel; the other paths launch it first
+  const bool fused = !tree && nmax > 0 && nmax <= DT * PERT_MAX;
+  if (app && !fused) {
+    hipError_t e = launch_decode_append(*app, app_src, nseq, s);
+    if (e != hipSuccess) return e;
+  }
   if (tree) return launch_select_tree_multi(views, qpos, nseq, b, flags, s);
   if (nmax > DT * PERT_MAX) return launch_select_multi(views, qpos, nseq, b, s);
   const bool small = nmax <= DT * 20;
   if (nmax > 0) {
+    DecodeAppendArgs none;
+    memset(&none, 0, sizeof none);
     hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
-                       s, vs, b, W);
+                       s, vs, b, W, app ? *app : none, app_src);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -92,43 +92,62 @@ struct __attribute__((aligned(16))) ScanLds {
   int cnt[2][CHT * 16];
 };
 
+// Runs f(c, buf) for chunks c = c0, c0 + step, ... < nchunks with chunk c
+// staged in LDS buffer buf.  Two later chunks are in flight in registers
+// while f runs (stages A and B take turns, so no register copy waits on a
+// load), and each goes to the other LDS buffer after f.
 template <int FW, int QS, class F>
 __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>& S, int c0,
                                               int step, int nchunks, F&& f) {
   using C = Cfg<FW, QS>;
   const int tid = threadIdx.x;
   constexpr int PER = (CHT * 64 + C::FT - 1) / C::FT;
-  v4i r[PER];
-  int rc = 0;
-  auto gload = [&](int c) {
+  struct Stage {
+    v4i r[PER];
+    int rc;
+  };
+  auto gload = [&](Stage& st, int c) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int e = k * C::FT + tid;
       const int tile = c * CHT + e / 64, slot = e & 63;
       const int beta = tile * 16 + (slot & 15);
-      r[k] = (e < CHT * 64 && beta < V.n_bkt)
-                 ? *reinterpret_cast<const v4i*>(V.cent + (int64_t)beta * kDim + 16 * (slot >> 4))
-                 : v4i{0, 0, 0, 0};
+      st.r[k] = (e < CHT * 64 && beta < V.n_bkt)
+                    ? *reinterpret_cast<const v4i*>(V.cent + (int64_t)beta * kDim + 16 * (slot >> 4))
+                    : v4i{0, 0, 0, 0};
     }
     const int bb = c * CHT * 16 + tid;
-    rc = (tid < CHT * 16 && bb < V.n_bkt) ? V.bcnt[bb] : 0;
+    st.rc = (tid < CHT * 16 && bb < V.n_bkt) ? V.bcnt[bb] : 0;
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int k = 0; k < PER; ++k)
-      if (k * C::FT + tid < CHT * 64) S.cent[buf][k * C::FT + tid] = r[k];
-    if (tid < CHT * 16) S.cnt[buf][tid] = rc;
+      if (k * C::FT + tid < CHT * 64) S.cent[buf][k * C::FT + tid] = st.r[k];
+    if (tid < CHT * 16) S.cnt[buf][tid] = st.rc;
   };
-  if (c0 < nchunks) { gload(c0); swrite(0); }
+  Stage A, B;
+  if (c0 < nchunks) { gload(A, c0); swrite(A, 0); }
+  if (c0 + step < nchunks) gload(A, c0 + step);
+  if (c0 + 2 * step < nchunks) gload(B, c0 + 2 * step);
   __syncthreads();
   int buf = 0;
-  for (int c = c0; c < nchunks; c += step) {
-    const int cn = c + step;
-    if (cn < nchunks) gload(cn);
+  int c = c0;
+  // invariant at the top: chunk c in LDS[buf], A holds c + step, B holds c + 2 step
+  while (c < nchunks) {
     f(c, buf);
-    if (cn < nchunks) swrite(buf ^ 1);
+    if (c + step < nchunks) swrite(A, buf ^ 1);
     __syncthreads();
     buf ^= 1;
+    if (c + 3 * step < nchunks) gload(A, c + 3 * step);
+    c += step;
+    if (c >= nchunks) break;
+    // here B holds c + step and A c + 2 step
+    f(c, buf);
+    if (c + step < nchunks) swrite(B, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    if (c + 3 * step < nchunks) gload(B, c + 3 * step);
+    c += step;
   }
 }
 
