@@ -548,6 +548,58 @@ def test_decode_steps_match_oracle(early):
     assert max(errs) <= TOL
 
 
+def test_decode_block_completes_mid_run():
+    """Flat decode where one sequence's key completes a block (its append
+    re-clusters the block) while the others in the batch take the one-key
+    append inside the score kernel; index and selections match the oracle."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("dec_blk", 65, T=0, ncomp=64, block=64, buckets=16, iters=3, chunk=0,
+                    budget=150, window=24, sinks=2, Hq=4, Hkv=2, D=64)
+    kpb = wl.pool * wl.block                          # keys per block
+    Ts = [5 * kpb - 3, 3 * kpb + 37, 2 * kpb]         # seq 0 completes block 5 at its third key
+    steps = 7
+    cap = max(Ts) + steps
+    gens = [S.Synth(wl, seq=i, data_cfg=65) for i in range(len(Ts))]
+    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, cap)
+    op = _oparams(wl)
+    K = torch.empty((len(Ts), cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    ixs, lat = [], []
+    for i, g in enumerate(gens):
+        lk = g.latk(0, cap)
+        lat.append(lk)
+        ix = L.LsaIndex(ip, dev)
+        ix.build(lk[:Ts[i]].to(dev))
+        ixs.append(ix)
+        g.fill_rows("k", K[i], 0)
+        g.fill_rows("v", V[i], 0)
+    Kd, Vd = K.to(dev), V.to(dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, len(Ts)), dtype=torch.uint8,
+                     device=dev)
+    for step in range(steps):
+        ts = [T + step for T in Ts]
+        lk_new = torch.stack([lat[i][t] for i, t in enumerate(ts)])
+        lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        out = L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kd, Vd, cap, sp, ap, ws=ws)
+        idx, cnt = L.decode_selection(ws, len(Ts), sp)
+        torch.cuda.synchronize()
+        for i, t in enumerate(ts):
+            sel = O.select(O.build_index(lat[i].numpy(), t + 1, op), lq[i].numpy(), t, osp)
+            n = int(cnt[i])
+            assert np.array_equal(np.sort(idx[i, :n].cpu().numpy()), sel), f"seq {i} step {step}"
+            err = normwise(out[i].cpu().numpy().astype(np.float64),
+                           oracle_attention(gens[i], wl, [t], [sel])[0])
+            assert err <= TOL, (i, step, err)
+    assert ixs[0].info().n_full == 5
+    for i in range(len(Ts)):
+        check_index(ixs[i].arrays(), O.build_index(lat[i].numpy(), Ts[i] + steps, op))
+
+
 def test_decode_sixteen_sequences():
     """The largest decode batch: 16 sequences of different lengths."""
     dev = _dev()
