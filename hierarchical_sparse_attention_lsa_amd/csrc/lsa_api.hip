@@ -626,6 +626,16 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
       return fail(LSA_E_ARG, "sequence %d has different index params", i);
     if (h->T + 1 > h->prm.max_tokens) return fail(LSA_E_CAPACITY, "sequence %d is full", i);
     if (seq_stride_rows < h->T + 1) return fail(LSA_E_ARG, "seq_stride_rows < T + 1 for sequence %d", i);
+    if (h->prm.tree_group > 0) {
+      // super clusters after this key's append (it may complete a block, and
+      // with it a Tree group): the decode walk holds at most 2048
+      const int64_t np1 = h->T + 1 - h->n_pool * h->prm.pool;
+      const int64_t pool_after = h->n_pool + (np1 == h->prm.pool ? 1 : 0);
+      const int64_t grp_after = pool_after / h->prm.block / h->prm.tree_group;
+      if (grp_after * h->prm.tree_super > 2048)
+        return fail(LSA_E_UNSUPPORTED, "sequence %d: %lld super clusters (at most 2048 in decode)", i,
+                    (long long)(grp_after * h->prm.tree_super));
+    }
     for (int j = 0; j < i; ++j)
       if (hs[j] == hs[i]) return fail(LSA_E_ARG, "sequence %d repeats an index", i);
   }
@@ -688,7 +698,8 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   for (int i = 0; i < nseq; ++i) {
     views[i] = view_of(as_index(hs[i]));
     if (views[i].leafsup && views[i].n_sup > 2048) {
-      // the counters above have advanced: the appended keys still go in
+      // unreachable: rejected above before anything was enqueued; should it
+      // happen, the appended keys still go in, as the counters say
       if (any_batched) LSA_HIP(launch_decode_append(da, d_latk_new, nseq, s), "decode append");
       return fail(LSA_E_UNSUPPORTED, "%d super clusters (at most 2048)", views[i].n_sup);
     }
