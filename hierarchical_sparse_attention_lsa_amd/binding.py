@@ -52,6 +52,7 @@ class IndexInfo(ctypes.Structure):
 EXPORTS = {
     "lsa_status_str": (ctypes.c_char_p, [c_i32]),
     "lsa_last_error": (ctypes.c_char_p, []),
+    "lsa_check": (c_i32, [c_vp]),
     "lsa_index_sizeof": (c_sz, []),
     "lsa_index_bytes": (c_i32, [ctypes.POINTER(IndexParams), ctypes.POINTER(c_sz)]),
     "lsa_index_init": (c_i32, [c_vp, ctypes.POINTER(IndexParams), c_vp, c_sz]),
@@ -109,6 +110,12 @@ def _check(rc: int, what: str) -> None:
     if rc != 0:
         L = lib()
         raise LsaError(f"{what}: {L.lsa_status_str(rc).decode()}: {L.lsa_last_error().decode()}")
+
+
+def check(stream=None) -> None:
+    """Wait for the stream's work and raise LsaError if an earlier call's
+    kernels failed on the device."""
+    _check(lib().lsa_check(_stream(stream)), "lsa_check")
 
 
 def _ptr(t: Optional[torch.Tensor]):

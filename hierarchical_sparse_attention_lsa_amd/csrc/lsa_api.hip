@@ -348,6 +348,13 @@ const char* lsa_status_str(int status) {
 
 const char* lsa_last_error(void) { return g_err.c_str(); }
 
+int lsa_check(void* stream) {
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(LSA_E_HIP, "%s", hipGetErrorString(e));
+  return LSA_OK;
+}
+
 size_t lsa_index_sizeof(void) { return kIndexSizeof; }
 
 int lsa_index_bytes(const lsa_index_params* prm, size_t* bytes) {

@@ -150,6 +150,11 @@ typedef struct lsa_index_info {
 
 LSA_API const char* lsa_status_str(int status);
 LSA_API const char* lsa_last_error(void);
+/* Waits for the work enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and reports whether it ran: LSA_OK, or LSA_E_HIP with the HIP
+ * error in lsa_last_error() when an earlier call's kernels failed on the
+ * device (the calls themselves return once their work is enqueued). */
+LSA_API int lsa_check(void* stream);
 
 LSA_API size_t lsa_index_sizeof(void);
 /* Device arena bytes needed for an index with these params (LSA_E_ARG /

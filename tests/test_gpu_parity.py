@@ -154,6 +154,8 @@ def test_tiny_selection_bit_exact(tiny):
     idx3, cnt3 = ix.select(lq.to(dev), torch.tensor(pos, dtype=torch.int32, device=dev), sp,
                            use_workspace=False)
     assert torch.equal(idx, idx3) and torch.equal(cnt, cnt3)
+    # the enqueued work ran without a device-side error
+    L.check()
 
 
 def test_tiny_attention_within_tolerance(tiny):
