@@ -376,8 +376,20 @@ def bench_decode(args, dev):
     run()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t
+    # step roofline: the selected K/V rows of the last step plus every centroid scored,
+    # at the HBM peak (the kernels' launches and their ramps are what the rest is)
+    _, cnt = L.decode_selection(ws, wl.nseq, sp)
+    kv_bytes = int(cnt.sum().item()) * wl.Hkv * wl.D * 2 * 2
+    cent_bytes = sum(ix.info().n_bkt for ix in ixs) * 64
+    step_bytes = kv_bytes + cent_bytes
+    ms = dt * 1e3 / steps
+    roof_ms = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
     return {"sequences": wl.nseq, "context": wl.T, "steps": steps,
-            "ms_per_step": dt * 1e3 / steps, "tokens_per_s": wl.nseq * steps / dt}
+            "ms_per_step": ms, "tokens_per_s": wl.nseq * steps / dt,
+            "roofline": {"bound": "hbm", "algorithmic_bytes_per_step": step_bytes,
+                         "roof_ms": roof_ms, "frac": roof_ms / ms,
+                         "note": "selected K/V rows of every sequence + centroids scored, at the "
+                                 "8 TB/s peak, against the whole step (four kernels)"}}
 
 
 def cpu_baseline(res, workers_pool, n_sample=512):
@@ -655,7 +667,8 @@ def main():
     decode = None
     if not args.no_decode:
         decode = bench_decode(args, dev)
-        log(f"[bench] decode {decode['tokens_per_s']:.0f} tok/s ({decode['ms_per_step']:.3f} ms/step)")
+        log(f"[bench] decode {decode['tokens_per_s']:.0f} tok/s ({decode['ms_per_step']:.3f} ms/step, "
+            f"step roof {decode['roofline']['roof_ms'] * 1e3:.1f} us, frac {decode['roofline']['frac']:.2f})")
 
     train = None
     if not args.no_train:
