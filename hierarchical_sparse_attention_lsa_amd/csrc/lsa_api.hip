@@ -6,11 +6,31 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "lsa_internal.h"
 
 using namespace lsa;
+
+namespace lsa {
+
+hipError_t once_per_device(std::atomic<unsigned long long>& done, hipError_t (*set)()) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 64) return set();
+  const unsigned long long bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  static std::mutex m;
+  std::lock_guard<std::mutex> lock(m);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = set();
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
+}  // namespace lsa
 
 namespace {
 

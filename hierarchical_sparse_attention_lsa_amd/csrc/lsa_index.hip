@@ -488,16 +488,15 @@ hipError_t launch_kmeans(const int8_t* X, int32_t N, int32_t C, int32_t iters, i
                          int32_t* map_out, int32_t map_base, void* scratch,
                          size_t scratch_bytes, hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<unsigned long long> attr_done{0};
+  hipError_t ae = once_per_device(attr_done, []() {
     hipError_t e = hipFuncSetAttribute((const void*)k_kmeans,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)k_km_assign, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return hipFuncSetAttribute((const void*)k_km_assign, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               160 * 1024);
+  });
+  if (ae != hipSuccess) return ae;
   const size_t lds = kmeans_lds_bytes(N, C);
   const int W = km_parts(N);
   // few blocks: W workgroups per block, one launch pair per iteration

@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "../../include/lsa.h"
@@ -96,6 +98,12 @@ struct DecodeAppendArgs {
   int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast, off_pend;
   int32_t p, N, C;
 };
+
+// Runs set() once per device (the current one), whatever the number of host
+// threads calling; `done` is the caller's per-device bit set (devices 0..63;
+// on a higher device id set() runs on every call).  For kernel attributes,
+// which are set per device.
+hipError_t once_per_device(std::atomic<unsigned long long>& done, hipError_t (*set)());
 
 // ---- launchers (return hipError_t) ----
 hipError_t launch_decode_append(const DecodeAppendArgs& a, const int8_t* src, int nseq,

@@ -683,16 +683,15 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<unsigned long long> attr_done{0};
+  hipError_t ae = once_per_device(attr_done, []() {
     hipError_t e = hipFuncSetAttribute((const void*)k_dec_select<20>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(20));
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)k_dec_select<PERT_MAX>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(PERT_MAX));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return hipFuncSetAttribute((const void*)k_dec_select<PERT_MAX>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(PERT_MAX));
+  });
+  if (ae != hipSuccess) return ae;
   if (small)
     hipLaunchKernelGGL(k_dec_select<20>, dim3((unsigned)nseq), dim3(DT), dec_lds(20), s, vs, b, W, flags);
   else
