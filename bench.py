@@ -171,6 +171,9 @@ def bench_prefill(args, dev):
     achieved = abytes / (attn_ms * 1e-3) / 1e9
     res = {
         "wl": wl, "t0": t0, "n": n, "ms_per_step": ms_per_step, "phase_ms": ph.mean(0).tolist(),
+        "step_event_ms": {"median": float(np.median(ph.sum(1))), "min": float(ph.sum(1).min()),
+                          "attention_median": float(np.median(ph[:, 2])),
+                          "attention_min": float(ph[:, 2].min())},
         "attn_ms": attn_ms, "attn_bytes": abytes, "achieved_gbs": achieved,
         "build_ms": float(np.median(build_ms)), "fused_same": fused_same,
         "cnt_mean": float(cnt_h.mean()), "g": g, "latk": latk, "latq": latq, "idx": idx,
@@ -721,6 +724,7 @@ def main():
         "cpu_baseline": cpu,
         "phases_ms": {"append": res["phase_ms"][0], "select": res["phase_ms"][1],
                       "attention": res["phase_ms"][2]},
+        "step_event_ms": res["step_event_ms"],
         "fused_entry_point_identical": res["fused_same"],
         "selected_keys_per_query": res["cnt_mean"],
         "index_build_keys_per_s": wl.T / (res["build_ms"] * 1e-3),
