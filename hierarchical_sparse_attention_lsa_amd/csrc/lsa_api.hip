@@ -189,6 +189,7 @@ IdxView view_of(const Index* h) {
   v.blast = h->at<int32_t>(h->off_blast);
   v.n_bkt = (int32_t)h->n_bkt();
   v.pool = h->prm.pool;
+  v.n_pool = (int32_t)h->n_pool;
   v.dense = 0;
   if (h->prm.tree_group > 0 && h->n_grp > 0) {
     v.leafsup = h->at<int32_t>(h->off_leafsup);
@@ -760,6 +761,7 @@ int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, cons
   v.cent = d_latk;
   v.n_bkt = (int32_t)T;
   v.pool = 1;
+  v.n_pool = (int32_t)T;
   v.dense = 1;
   SelArgs a;
   a.latq = d_latq; a.qpos = d_qpos; a.qpos_base = 0; a.nq = nq;

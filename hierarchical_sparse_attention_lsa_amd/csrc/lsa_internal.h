@@ -66,6 +66,7 @@ struct IdxView {
   const int32_t* toff;    // first super slot in tmem
   const int32_t* tmem;    // super ids grouped by top node
   const int32_t* suptop;  // super -> top node id, or -1
+  int32_t n_pool;         // pooled vectors (keys [0, n_pool * pool) are in buckets)
 };
 
 struct SelArgs {

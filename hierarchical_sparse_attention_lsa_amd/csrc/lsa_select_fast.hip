@@ -66,7 +66,8 @@ struct ListWs {
   int32_t* elig;      // [slots][LC] eligible keys, then the taken keys
   int32_t* kstart;    // [slots][LC] member slot * p + offset of the first eligible key
   int32_t* nsub;      // [slots][64] sub-list sizes
-  int32_t* meta;      // [slots][2]  query index (-1: empty slot), position
+  int32_t* meta;      // [slots][3]  query index (-1: empty slot), position, 1: the list holds
+                      //             every bucket with an eligible key
   int32_t* flags;     // [nq] 1: recompute with the exact kernel
 };
 
@@ -90,6 +91,7 @@ struct __attribute__((aligned(16))) ScanLds {
   int nl[QS][NSUB];                 // sub-list sizes
   v4i cent[2][CHT * 64];
   int cnt[2][CHT * 16];
+  int2 fl[2][CHT * 16];             // first and last key position of each bucket (causal only)
 };
 
 // Runs f(c, buf) for chunks c = c0, c0 + step, ... < nchunks with chunk c
@@ -98,15 +100,16 @@ struct __attribute__((aligned(16))) ScanLds {
 // load), and each goes to the other LDS buffer after f.
 template <int FW, int QS, class F>
 __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>& S, int c0,
-                                              int step, int nchunks, F&& f) {
+                                              int step, int nchunks, bool causal, F&& f) {
   using C = Cfg<FW, QS>;
   const int tid = threadIdx.x;
   constexpr int PER = (CHT * 64 + C::FT - 1) / C::FT;
   struct Stage {
     v4i r[PER];
     int rc;
+    int2 rfl;
   };
-  auto gload = [&](Stage& st, int c) {
+  auto gload = [&](Stage& st, int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int e = k * C::FT + tid;
@@ -117,13 +120,18 @@ __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>&
                     : v4i{0, 0, 0, 0};
     }
     const int bb = c * CHT * 16 + tid;
-    st.rc = (tid < CHT * 16 && bb < V.n_bkt) ? V.bcnt[bb] : 0;
+    const bool in = tid < CHT * 16 && bb < V.n_bkt;
+    st.rc = in ? V.bcnt[bb] : 0;
+    // without causal staging every bucket reads as eligible from key 0 (the
+    // rule the threshold used before a query could precede most of the index)
+    st.rfl = (in && causal) ? make_int2(V.bfirst[bb] * V.pool, V.blast[bb] * V.pool + V.pool - 1)
+                            : make_int2(0, 0);
   };
-  auto swrite = [&](const Stage& st, int buf) {
+  auto swrite = [&](const Stage& st, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < PER; ++k)
       if (k * C::FT + tid < CHT * 64) S.cent[buf][k * C::FT + tid] = st.r[k];
-    if (tid < CHT * 16) S.cnt[buf][tid] = st.rc;
+    if (tid < CHT * 16) { S.cnt[buf][tid] = st.rc; S.fl[buf][tid] = st.rfl; }
   };
   Stage A, B;
   if (c0 < nchunks) { gload(A, c0); swrite(A, 0); }
@@ -172,12 +180,26 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     const int t = q < 0 ? -1 : max(0, A.qpos ? A.qpos[q] : A.qpos_base + q);
     S.q[i] = q; S.t[i] = t;
     S.smax[i] = INT_MIN; S.ssum[i] = 0; S.sn[i] = 0;
-    W.meta[2 * (lbase + i)] = q;
-    W.meta[2 * (lbase + i) + 1] = t;
+    W.meta[3 * (lbase + i)] = q;
+    W.meta[3 * (lbase + i) + 1] = t;
   }
   for (int e = tid; e < QS * NB2; e += C::FT) (&S.hist[0][0])[e] = 0;
   for (int e = tid; e < QS * NSUB; e += C::FT) (&S.nl[0][0])[e] = 0;
   __syncthreads();
+
+  // Causal staging (each bucket's key range, so the threshold counts only the
+  // keys a query may take and the lists skip buckets wholly past it) when more
+  // than 1/8 of the index's keys lie past the earliest query's long-range
+  // keys: a training-like batch.  Every wave finds the same answer.
+  bool causal;
+  {
+    int tm = INT_MAX;
+    for (int i = lane; i < QS; i += 64) tm = S.t[i] >= 0 ? min(tm, S.t[i]) : tm;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) tm = min(tm, __shfl_xor(tm, m));
+    const long long keys = (long long)V.n_pool * V.pool;
+    causal = tm != INT_MAX && keys - ((long long)tm - A.window) > keys / 8;
+  }
 
   v4i qa = {0, 0, 0, 0};
   {
@@ -190,12 +212,16 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   bool act[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) act[v] = S.t[qrow + v] >= 0;
+  // last long-range key position of each row's query (scalars: an array here
+  // would be placed in LDS by the compiler)
+  const int tl0 = S.t[qrow] - A.window, tl1 = S.t[qrow + 1] - A.window;
+  const int tl2 = S.t[qrow + 2] - A.window, tl3 = S.t[qrow + 3] - A.window;
 
   // ---- 1. sampled max / mean over non-empty buckets ----
   {
     int smax[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, sn[4] = {0, 0, 0, 0};
     long long ssum[4] = {0, 0, 0, 0};
-    stream_chunks(V, S, 0, sstep, nchunks, [&](int c, int buf) {
+    stream_chunks(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
       for (int tl = phase; tl < CHT; tl += C::PH) {
         const v4i z = {0, 0, 0, 0};
         const v4i sc = mfma_i8_16x16x64(qa, S.cent[buf][tl * 64 + lane], z);
@@ -235,20 +261,31 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
         while (s < 30 && (((hi[v] - lo[v] + 1) + (1 << s) - 1) >> s) > NB2) ++s;
       sh[v] = s;
     }
-    stream_chunks(V, S, 0, sstep, nchunks, [&](int c, int buf) {
+    stream_chunks(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
       for (int tl = phase; tl < CHT; tl += C::PH) {
         const v4i z = {0, 0, 0, 0};
         const v4i sc = mfma_i8_16x16x64(qa, S.cent[buf][tl * 64 + lane], z);
+        // a bucket counts with all its keys when they are all long-range for
+        // the query (the index may hold keys past it), else not at all
         const int w = S.cnt[buf][tl * 16 + col] * p;
+        const int kl = S.fl[buf][tl * 16 + col].y;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (sc[v] >= lo[v] && w > 0) atomicAdd(&S.hist[qrow + v][(hi[v] - sc[v]) >> sh[v]], w);
+        for (int v = 0; v < 4; ++v) {
+          const int tv = v == 0 ? tl0 : v == 1 ? tl1 : v == 2 ? tl2 : tl3;
+          if (sc[v] >= lo[v] && w > 0 && kl <= tv)
+            atomicAdd(&S.hist[qrow + v][(hi[v] - sc[v]) >> sh[v]], w);
+        }
       }
     });
+    // A query whose sample does not reach the target within [mean, max] takes
+    // every bucket with an eligible key into its list (TAKE_ALL: any score
+    // passes), and its list is then complete.
+    constexpr int TAKE_ALL = -(1 << 30);
     for (int qs = tid; qs < QS; qs += C::FT) {
-      int slo = INT_MAX;
+      int slo = INT_MAX, all = 0;
       if (S.t[qs] >= 0) {
-        slo = INT_MIN;
+        slo = TAKE_ALL;
+        all = 1;
         const int n = S.sn[qs];
         if (n > 0) {
           const int mx = S.smax[qs], mn = (int)(S.ssum[qs] / n);
@@ -257,14 +294,14 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           const int sampled = (nchunks + sstep - 1) / sstep;
           const long long target = (2ll * budget_at(A, S.t[qs]) * sampled + nchunks - 1) / nchunks;
           long long cum = 0;
-          slo = mn;
           for (int b = 0; b < NB2; ++b) {
             cum += S.hist[qs][b];
-            if (cum >= target) { slo = max(mn, mx - ((b + 1) << s) + 1); break; }
+            if (cum >= target) { slo = max(mn, mx - ((b + 1) << s) + 1); all = 0; break; }
           }
         }
       }
       S.slo[qs] = slo;
+      W.meta[3 * (lbase + qs) + 2] = all;
     }
     __syncthreads();
   }
@@ -286,7 +323,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
       slo[v] = act[v] ? S.slo[qrow + v] : (1 << 30);    // 1<<30: no score reaches it
       bias[v] = -slo[v];
     }
-    stream_chunks(V, S, 0, 1, nchunks, [&](int c, int buf) {
+    stream_chunks(V, S, 0, 1, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < TPW; g += 4) {
         int d[16];
@@ -322,11 +359,16 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           const int dk = (int)((z[1] & m3) | (z[0] & ~m3));
           const int v = k & 3, u = k >> 2;
           const int sv = (v & 2) ? ((v & 1) ? slo[3] : slo[2]) : ((v & 1) ? slo[1] : slo[0]);
+          const int tv = S.t[qrow + v] - A.window;   // (hits are rare: an LDS read is cheap)
           const int beta = (tb + C::PH * u) * 16 + col;
-          const int jl = beta & (NSUB - 1);
-          const int qs = qrow + v;
-          const int pos = atomicAdd(&S.nl[qs][jl], 1);
-          if (pos < SUBCAP) W.key[(lbase + qs) * LC + (int64_t)pos * NSUB + jl] = order_key(dk + sv, beta);
+          // a bucket whose first key is past the query's long-range range has no
+          // eligible key (first pooled id of bucket beta: chunk-local slot beta - c*CHT*16)
+          if (S.fl[buf][beta - c * CHT * 16].x <= tv) {
+            const int jl = beta & (NSUB - 1);
+            const int qs = qrow + v;
+            const int pos = atomicAdd(&S.nl[qs][jl], 1);
+            if (pos < SUBCAP) W.key[(lbase + qs) * LC + (int64_t)pos * NSUB + jl] = order_key(dk + sv, beta);
+          }
         }
       }
     });
@@ -652,9 +694,10 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
   const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int64_t slot = blockIdx.x;
-  const int q = W.meta[2 * slot];
+  const int q = W.meta[3 * slot];
   if (q < 0) return;                 // uniform over the workgroup
-  const int t = W.meta[2 * slot + 1];
+  const int t = W.meta[3 * slot + 1];
+  const bool complete = W.meta[3 * slot + 2] != 0;
   const IdxView V = vsp->v[0];
   const int B = budget_at(A, t);
   const int p = V.pool;
@@ -714,7 +757,7 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
       tot += in ? e[u] : 0;
     }
   }
-  ok = select_and_emit<TPQ>(L, V, A, q, t, ok, K, e, lo, hi, tot, false,
+  ok = select_and_emit<TPQ>(L, V, A, q, t, ok, K, e, lo, hi, tot, complete,
                            [&](int u) { return W.kstart[slot * LC + tid + RT * u]; });
   if (tid == 0) W.flags[q] = ok ? 0 : 1;
 }
@@ -928,7 +971,7 @@ size_t ws_layout(size_t slots, size_t nq, ListWs* W, void* base) {
   w.elig = reinterpret_cast<int32_t*>(take(slots * LC * sizeof(int32_t)));
   w.kstart = reinterpret_cast<int32_t*>(take(slots * LC * sizeof(int32_t)));
   w.nsub = reinterpret_cast<int32_t*>(take(slots * NSUB * sizeof(int32_t)));
-  w.meta = reinterpret_cast<int32_t*>(take(slots * 2 * sizeof(int32_t)));
+  w.meta = reinterpret_cast<int32_t*>(take(slots * 3 * sizeof(int32_t)));
   w.flags = reinterpret_cast<int32_t*>(take(nq * sizeof(int32_t)));
   if (W) *W = w;
   return o;
