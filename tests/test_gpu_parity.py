@@ -158,6 +158,28 @@ def test_tiny_selection_bit_exact(tiny):
     L.check()
 
 
+def test_select_every_position_as_a_query(tiny):
+    """A training-like batch: every position of the tiny context is a query over
+    the full index (most of the index lies past the early queries).  The list
+    path (causal scan) matches the exact kernel on all rows and the oracle on
+    a sample that includes the early positions."""
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    pos = torch.arange(wl.T, dtype=torch.int32)
+    lq = g.latq_rows(pos.to(torch.int64))
+    idx, cnt = ix.select(lq.to(dev), pos.to(dev), sp)
+    idx_x, cnt_x = ix.select(lq.to(dev), pos.to(dev), sp, use_workspace=False)
+    assert torch.equal(idx, idx_x) and torch.equal(cnt, cnt_x)
+    rng = np.random.default_rng(7)
+    sample = sorted(set(range(0, 1400, 7)) | set(rng.choice(wl.T, 300, replace=False).tolist()))
+    refs = [O.select(ref, lq[t].numpy(), t, osp) for t in sample]
+    check_selection(idx[sample], cnt[sample], refs, sp.max_sel)
+
+
 def test_tiny_attention_within_tolerance(tiny):
     wl, g, latk, ref, dev = tiny
     L = _L()
