@@ -165,6 +165,8 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
     }
   }
   if ((int)blockIdx.x * DT >= V.n_bkt) return;          // uniform: past this sequence's index
+  // the streaming select bins its own scores: no partial histograms for it
+  const bool want_hist = V.n_bkt <= DT * PERT_MAX;
   for (int b = threadIdx.x; b < NBIN; b += DT) hist[b] = 0;
   __syncthreads();                                      // (also publishes the appended bucket here)
   const int beta = blockIdx.x * DT + threadIdx.x;
@@ -179,12 +181,155 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
                 load_bucket<false>(V, beta), hist);
     }
   }
+  if (!want_hist) return;                               // uniform
   __syncthreads();
   // the whole histogram, zeros included: nothing has to be cleared beforehand
   int2* out = reinterpret_cast<int2*>(W.hpart + ((int64_t)seq * W.n_part + blockIdx.x) * NBIN);
   for (int b = threadIdx.x; b < NBIN / 2; b += DT) out[b] = make_int2(hist[2 * b], hist[2 * b + 1]);
 }
 
+
+// ---- pieces shared by the decode select kernels (one workgroup per sequence) ----
+
+// The window and the sinks after `out` taken keys, -1 padding, the count (wave 0).
+__device__ __forceinline__ void dec_finish_row(const SelArgs& A, int seq, int t, int out) {
+  const int lane = lane_id();
+  if ((threadIdx.x >> 6) != 0) return;
+  int32_t* row = A.idx + (int64_t)seq * A.max_sel;
+  const int wstart = max(0, t - A.window + 1);
+  const int ns = max(0, min(A.sinks, wstart));
+  const int nw = t - wstart + 1;
+  for (int k = lane; k < ns; k += 64) row[out + k] = k;
+  for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
+  const int totalk = out + ns + nw;
+  for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
+  if (lane == 0) A.cnt[seq] = totalk;
+}
+
+// out_total keys of the nt taken buckets listed in ascending id: bucket r
+// starts at output offset l_off[r] and first key slot l_ks[r]; one output key
+// per thread and round, four rounds in flight.
+__device__ __forceinline__ void dec_emit_keys(const IdxView& V, const SelArgs& A, int seq, const int* l_off,
+                                              const int* l_ks, int nt, int out_total) {
+  const int tid = threadIdx.x, p = V.pool;
+  int32_t* row = A.idx + (int64_t)seq * A.max_sel;
+  for (int o0 = tid; o0 < out_total; o0 += 4 * DT) {
+    int sl[4], g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = o0 + j * DT;
+      sl[j] = 0;
+      if (o < out_total) {
+        int a = 0, b = nt - 1;         // last entry with l_off <= o
+        while (a < b) {
+          const int m = (a + b + 1) >> 1;
+          if (l_off[m] <= o) a = m; else b = m - 1;
+        }
+        sl[j] = l_ks[a] + (o - l_off[a]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[j] = o0 + j * DT < out_total ? V.bmem[sl[j] / p] : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (o0 + j * DT < out_total) row[o0 + j * DT] = g[j] * p + sl[j] % p;
+  }
+}
+
+// LDS of the histogram path's tail.
+struct DecTail {
+  long long* cq;                    // [BCAP] order keys of the cutoff bin's buckets
+  int* ci;                          // [BCAP] their ids
+  int* ce;                          // [BCAP] their eligible keys
+  int* re;                          // [BCAP] eligible keys by rank
+  int* rs;                          // [BCAP] cutoff-bin slot by rank
+  int* ired;                        // [DW] block scan scratch
+  int* nt;                          // taken buckets so far
+  int* ids;                         // [TCAP] taken bucket ids, any order; later output offsets
+  int* tks;                         // [TCAP] keys taken from them; later first key slots
+  int* sid;                         // [TCAP] taken bucket ids, ascending
+  int* stk;                         // [TCAP] keys taken, ascending bucket id
+  unsigned* bm;                     // [nw] taken-id bitmap (cleared by the caller)
+  int* wp;                          // [nw] taken ids before each word
+};
+
+// On entry ids/tks hold the buckets taken whole (*nt of them, any order) and
+// cq/ci/ce the nb (<= BCAP) buckets of the cutoff bin.  Ranks the cutoff bin
+// by order key, takes its buckets in turn until the budget is met (the last
+// one cut at its lowest positions), orders every taken bucket by id through a
+// bitmap of nw words, gives them output offsets and writes the row.
+__device__ void dec_tail(const IdxView& V, const SelArgs& A, const int32_t* kstart, int seq, int t, int B,
+                         int above, int nb, int nw, const DecTail& L) {
+  const int tid = threadIdx.x;
+  if (nb > 0) {                        // uniform
+    // rank in the cut bin (order keys are distinct): larger keys first
+    if (tid < nb) {
+      const long long k = L.cq[tid];
+      int r = 0;
+      for (int i = 0; i < nb; ++i) r += L.cq[i] > k ? 1 : 0;
+      L.re[r] = L.ce[tid];
+      L.rs[r] = tid;
+    }
+    __syncthreads();
+    int tot;
+    const int x = tid < nb ? L.re[tid] : 0;
+    const int before = block_excl_scan<DT>(x, L.ired, &tot);
+    const int tk = max(0, min(x, B - above - before));
+    if (tk > 0) {
+      const int sl = L.rs[tid];
+      const int q = atomicAdd(L.nt, 1);
+      if (q < TCAP) { L.ids[q] = L.ci[sl]; L.tks[q] = tk; }
+    }
+    __syncthreads();
+  }
+  const int nt = min(*L.nt, TCAP);
+  // ascending ids: an entry's rank is the number of taken ids below it
+  for (int i = tid; i < nt; i += DT) atomicOr(&L.bm[L.ids[i] >> 5], 1u << (L.ids[i] & 31));
+  __syncthreads();
+  {                                    // word prefixes: thread tid takes words [tid*WPT, +WPT)
+    const int wpt = (nw + DT - 1) / DT;
+    int loc = 0;
+    for (int k = 0; k < wpt; ++k) {
+      const int w = tid * wpt + k;
+      loc += w < nw ? __popc(L.bm[w]) : 0;
+    }
+    int totw;
+    int pre = block_excl_scan<DT>(loc, L.ired, &totw);
+    for (int k = 0; k < wpt; ++k) {
+      const int w = tid * wpt + k;
+      if (w < nw) { L.wp[w] = pre; pre += __popc(L.bm[w]); }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nt; i += DT) {
+    const int id = L.ids[i], w = id >> 5;
+    const int r = L.wp[w] + __popc(L.bm[w] & ((1u << (id & 31)) - 1u));
+    L.sid[r] = id;
+    L.stk[r] = L.tks[i];
+  }
+  __syncthreads();
+  // output offsets: thread tid sums entries [tid*ENT, tid*ENT + ENT)
+  constexpr int ENT = TCAP / DT;
+  int loc = 0;
+#pragma unroll
+  for (int k = 0; k < ENT; ++k) {
+    const int r = tid * ENT + k;
+    loc += r < nt ? L.stk[r] : 0;
+  }
+  int out_total;
+  int off = block_excl_scan<DT>(loc, L.ired, &out_total);   // its barriers end the reads of ids, tks
+  int* soff = L.ids;
+  int* sks = L.tks;
+#pragma unroll
+  for (int k = 0; k < ENT; ++k) {
+    const int r = tid * ENT + k;
+    if (r < nt) { soff[r] = off; off += L.stk[r]; }
+  }
+  for (int r = tid; r < nt; r += DT) sks[r] = kstart[L.sid[r]];
+  __syncthreads();
+  dec_emit_keys(V, A, seq, soff, sks, nt, out_total);
+  dec_finish_row(A, seq, t, out_total);
+}
 
 // Order key from a score and a bucket id, recomputed where it is used: the
 // empty asm keeps the compiler from hoisting all of a thread's keys out of the
@@ -222,47 +367,6 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     if (tid == 0) flags[seq] = 1;
     return;
   }
-  int32_t* row = A.idx + (int64_t)seq * A.max_sel;
-  // the window and the sinks after `out` taken keys, -1 padding, the count
-  auto finish_row = [&](int out) {
-    if (wave == 0) {
-      const int wstart = max(0, t - A.window + 1);
-      const int ns = max(0, min(A.sinks, wstart));
-      const int nw = t - wstart + 1;
-      for (int k = lane; k < ns; k += 64) row[out + k] = k;
-      for (int k = lane; k < nw; k += 64) row[out + ns + k] = wstart + k;
-      const int totalk = out + ns + nw;
-      for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
-      if (lane == 0) A.cnt[seq] = totalk;
-    }
-  };
-  // out_total keys of the nt taken buckets listed in ascending id: bucket r
-  // starts at output offset l_off[r] and first key slot l_ks[r]; one output
-  // key per thread and round, four rounds in flight
-  auto emit_keys = [&](const int* l_off, const int* l_ks, int nt, int out_total) {
-    for (int o0 = tid; o0 < out_total; o0 += 4 * DT) {
-      int sl[4], g[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = o0 + j * DT;
-        sl[j] = 0;
-        if (o < out_total) {
-          int a = 0, b = nt - 1;       // last entry with l_off <= o
-          while (a < b) {
-            const int m = (a + b + 1) >> 1;
-            if (l_off[m] <= o) a = m; else b = m - 1;
-          }
-          sl[j] = l_ks[a] + (o - l_off[a]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) g[j] = o0 + j * DT < out_total ? V.bmem[sl[j] / p] : 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (o0 + j * DT < out_total) row[o0 + j * DT] = g[j] * p + sl[j] % p;
-    }
-  };
-
   // ---- fast path: the cutoff located in the score histogram ----
   // Buckets whose score bin lies above the bin where the eligible keys reach
   // the budget are taken whole; the buckets of that bin are ranked by order
@@ -361,63 +465,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     __syncthreads();
     const int nb = s_nb;
     if (nb <= BCAP) {                  // uniform; else the general path below
-      if (nb > 0) {                    // uniform
-        // rank in the cut bin (order keys are distinct): larger keys first
-        if (tid < nb) {
-          const long long k = s_cq[tid];
-          int r = 0;
-          for (int i = 0; i < nb; ++i) r += s_cq[i] > k ? 1 : 0;
-          s_re[r] = s_ce[tid];
-          s_rs[r] = tid;
-        }
-        __syncthreads();
-        int tot;
-        const int x = tid < nb ? s_re[tid] : 0;
-        const int before = block_excl_scan<DT>(x, s_ired, &tot);
-        const int tk = max(0, min(x, B - above - before));
-        if (tk > 0) {
-          const int sl = s_rs[tid];
-          const int q = atomicAdd(&s_nt, 1);
-          if (q < TCAP) { ids[q] = s_ci[sl]; tks[q] = tk; }
-        }
-        __syncthreads();
-      }
-      const int nt = min(s_nt, TCAP);
-      // ascending ids: an entry's rank is the number of taken ids below it
-      for (int i = tid; i < nt; i += DT) atomicOr(&bm[ids[i] >> 5], 1u << (ids[i] & 31));
-      __syncthreads();
-      int totw;
-      const int wpre = block_excl_scan<DT>(tid < NBW ? __popc(bm[tid]) : 0, s_ired, &totw);
-      if (tid < NBW) wp[tid] = wpre;
-      __syncthreads();
-      for (int i = tid; i < nt; i += DT) {
-        const int id = ids[i], w = id >> 5;
-        const int r = wp[w] + __popc(bm[w] & ((1u << (id & 31)) - 1u));
-        sid[r] = id;
-        stk[r] = tks[i];
-      }
-      __syncthreads();
-      // output offsets: thread tid sums entries [tid*ENT, tid*ENT + ENT)
-      constexpr int ENT = TCAP / DT;
-      int loc = 0;
-#pragma unroll
-      for (int k = 0; k < ENT; ++k) {
-        const int r = tid * ENT + k;
-        loc += r < nt ? stk[r] : 0;
-      }
-      int out_total;
-      int off = block_excl_scan<DT>(loc, s_ired, &out_total);   // its barriers end the reads of ids, tks
-      int* soff = ids;
-      int* sks = tks;
-#pragma unroll
-      for (int k = 0; k < ENT; ++k) {
-        const int r = tid * ENT + k;
-        if (r < nt) { soff[r] = off; off += stk[r]; }
-      }
-      for (int r = tid; r < nt; r += DT) sks[r] = W.kstart[base + sid[r]];
-      __syncthreads();
-      emit_keys(soff, sks, nt, out_total);
-      finish_row(out_total);
+      DecTail L{s_cq, s_ci, s_ce, s_re, s_rs, s_ired, &s_nt, ids, tks, sid, stk, bm, wp};
+      dec_tail(V, A, W.kstart + base, seq, t, B, above, nb, NBW, L);
       if (tid == 0) flags[seq] = 0;
       return;
     }
@@ -614,12 +663,147 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   }
   __syncthreads();
   if (ok) {
-    emit_keys(l_off, l_ks, nt, out_total);
-    finish_row(out_total);
+    dec_emit_keys(V, A, seq, l_off, l_ks, nt, out_total);
+    dec_finish_row(A, seq, t, out_total);
   }
   if (tid == 0) flags[seq] = ok ? 0 : 1;
 #undef KEY
 #undef E
+}
+
+// Indexes beyond the register-resident instance (more than DT * PERT_MAX
+// buckets, up to BIG_NW * 32): the same rule with the scores streamed from
+// the workspace twice, once into the LDS histogram of eligible keys per score
+// bin, once to classify against the cutoff bin's score range; then the shared
+// tail.  A cutoff bin of more than BCAP buckets flags the sequence for the
+// exact kernel.
+constexpr int BIG_NW = 10240;       // bitmap words: bucket ids below 327680
+constexpr int BIG_LDS = (4 * TCAP + 2 * BIG_NW) * 4;
+constexpr int BIG_U = 8;            // buckets per thread and batch (loads in flight)
+static_assert(NBIN <= 4 * TCAP, "the histogram fits in the list region");
+
+__global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, DecWs W,
+                                                       int32_t* __restrict__ flags) {
+  __shared__ int s_ired[DW];
+  __shared__ long long s_cq[BCAP];
+  __shared__ int s_ci[BCAP], s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
+  __shared__ int s_fc[4];              // cut bin, keys above it, its scores [lo, hi]
+  __shared__ int s_nt, s_nb;
+  extern __shared__ int s_e[];         // histogram, then ids, tks, sid, stk [TCAP], bm, wp [BIG_NW]
+  const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int seq = blockIdx.x;
+  const IdxView V = vsp->v[seq];
+  const int t = vsp->qpos[seq];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int B = budget_at(A, t);
+  const int n = V.n_bkt;
+  const int64_t base = (int64_t)seq * VS.cap;
+  if (n <= DT * PERT_MAX) return;      // uniform: k_dec_select serves it
+  if (n > BIG_NW * 32) {               // beyond the bitmap: the exact kernel serves it
+    if (tid == 0) flags[seq] = 1;
+    return;
+  }
+  const int32_t* sc = W.score + base;
+  const int32_t* el = W.elig + base;
+  int* hist = s_e;
+  for (int b = tid; b < NBIN; b += DT) hist[b] = 0;
+  if (tid == 0) { s_fc[0] = NBIN; s_fc[1] = 0; s_fc[2] = INT_MAX; s_fc[3] = INT_MAX; s_nt = 0; s_nb = 0; }
+  __syncthreads();
+  // pass 1: eligible keys per score bin.  Both passes run the same number of
+  // batches on every lane (the wave scans in pass 2 need every lane).
+  for (int j0 = 0; j0 < n; j0 += BIG_U * DT) {
+    int sv[BIG_U], ev[BIG_U];
+#pragma unroll
+    for (int u = 0; u < BIG_U; ++u) {
+      const int j = j0 + u * DT + tid;
+      sv[u] = j < n ? sc[j] : 0;
+      ev[u] = j < n ? el[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < BIG_U; ++u)
+      if (ev[u] > 0) atomicAdd(&hist[score_bin(sv[u])], ev[u]);
+  }
+  __syncthreads();
+  // the cutoff bin, as in k_dec_select
+  int he[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) he[j] = hist[NBIN - 1 - (2 * tid + j)];
+  int te;
+  const int pe = block_excl_scan<DT>(min(he[0] + he[1], B + 1), s_ired, &te);
+  if (B > 0 && te <= B) {
+    if (tid == 0) { s_fc[0] = -1; s_fc[1] = te; s_fc[2] = INT_MIN; s_fc[3] = INT_MIN; }
+  } else if (B > 0) {
+    int ce = pe;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (ce < B && he[j] >= B - ce) {
+        const int bin = NBIN - 1 - (2 * tid + j);
+        int lo, hi;
+        bin_range(bin, &lo, &hi);
+        s_fc[0] = bin; s_fc[1] = ce; s_fc[2] = lo; s_fc[3] = hi;
+      }
+      ce = he[j] >= B - ce ? B : ce + he[j];
+    }
+  }
+  __syncthreads();                     // (also ends the reads of hist)
+  const int above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
+  const int nw = (n + 31) / 32;
+  int* ids = s_e;
+  int* tks = s_e + TCAP;
+  int* sid = s_e + 2 * TCAP;
+  int* stk = s_e + 3 * TCAP;
+  unsigned* bm = reinterpret_cast<unsigned*>(s_e + 4 * TCAP);
+  int* wp = s_e + 4 * TCAP + BIG_NW;
+  for (int w = tid; w < nw; w += DT) bm[w] = 0u;
+  // pass 2: buckets above the cut bin are taken whole (slots reserved once per
+  // wave and batch); the cut bin's buckets are collected
+  for (int j0 = 0; j0 < n; j0 += BIG_U * DT) {
+    int sv[BIG_U], ev[BIG_U];
+#pragma unroll
+    for (int u = 0; u < BIG_U; ++u) {
+      const int j = j0 + u * DT + tid;
+      sv[u] = j < n ? sc[j] : 0;
+      ev[u] = j < n ? el[j] : 0;
+    }
+    unsigned m_above = 0, m_cut = 0;
+#pragma unroll
+    for (int u = 0; u < BIG_U; ++u) {
+      const bool e = ev[u] > 0;
+      m_above |= (e && sv[u] > hi_s ? 1u : 0u) << u;
+      m_cut |= (e && sv[u] >= lo_s && sv[u] <= hi_s ? 1u : 0u) << u;
+    }
+    int wt;
+    const int wpre = wave_excl_scan(__popc(m_above), &wt);
+    int wb = 0;
+    if (lane == 0 && wt > 0) wb = atomicAdd(&s_nt, wt);
+    int pos = __shfl(wb, 0) + wpre;
+#pragma unroll
+    for (int u = 0; u < BIG_U; ++u) {
+      if ((m_above & (1u << u)) && pos < TCAP) { ids[pos] = j0 + u * DT + tid; tks[pos] = ev[u]; }
+      pos += (m_above >> u) & 1u;
+    }
+    if (m_cut) {
+#pragma unroll
+      for (int u = 0; u < BIG_U; ++u) {
+        if (!(m_cut & (1u << u))) continue;
+        const int q = atomicAdd(&s_nb, 1);
+        if (q < BCAP) {
+          s_cq[q] = order_key(sv[u], j0 + u * DT + tid);
+          s_ci[q] = j0 + u * DT + tid;
+          s_ce[q] = ev[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int nb = s_nb;
+  if (nb > BCAP) {                     // many equal scores: the exact kernel serves it
+    if (tid == 0) flags[seq] = 1;
+    return;
+  }
+  DecTail L{s_cq, s_ci, s_ce, s_re, s_rs, s_ired, &s_nt, ids, tks, sid, stk, bm, wp};
+  dec_tail(V, A, W.kstart + base, seq, t, B, above, nb, nw, L);
+  if (tid == 0) flags[seq] = 0;
 }
 
 size_t dec_layout(int32_t nseq, int32_t cap, DecWs* W, int32_t** flags, void* ws) {
@@ -652,12 +836,13 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   DecViews vs;
   memset(&vs, 0, sizeof vs);
   bool tree = false;
-  int nmax = 0;
+  int nmax = 0, nmin = INT_MAX;
   for (int i = 0; i < nseq; ++i) {
     vs.v[i] = views[i];
     vs.qpos[i] = qpos[i];
     tree |= views[i].leafsup != nullptr;
     nmax = nmax > views[i].n_bkt ? nmax : views[i].n_bkt;
+    nmin = nmin < views[i].n_bkt ? nmin : views[i].n_bkt;
   }
   vs.nseq = nseq;
   vs.cap = (int32_t)max_bkt;
@@ -667,13 +852,14 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   int32_t* flags;
   dec_layout(nseq, vs.cap, &W, &flags, ws);
   // the append rides on the score kernel; the other paths launch it first
-  const bool fused = !tree && nmax > 0 && nmax <= DT * PERT_MAX;
+  const bool fused = !tree && nmax > 0 && nmax <= BIG_NW * 32;
   if (app && !fused) {
     hipError_t e = launch_decode_append(*app, app_src, nseq, s);
     if (e != hipSuccess) return e;
   }
   if (tree) return launch_select_tree_multi(views, qpos, nseq, b, flags, s);
-  if (nmax > DT * PERT_MAX) return launch_select_multi(views, qpos, nseq, b, s);
+  if (nmax > BIG_NW * 32) return launch_select_multi(views, qpos, nseq, b, s);
+  const bool big = nmax > DT * PERT_MAX;
   const bool small = nmax <= DT * 20;
   if (nmax > 0) {
     DecodeAppendArgs none;
@@ -692,6 +878,25 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
                                hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(PERT_MAX));
   });
   if (ae != hipSuccess) return ae;
+  if (big) {
+    // sequences above DT * PERT_MAX buckets: the streaming kernel (the other
+    // kernel flags them and returns; this one overwrites their flags); any
+    // sequence flagged then goes to the exact kernel
+    static std::atomic<unsigned long long> big_done{0};
+    ae = once_per_device(big_done, []() {
+      return hipFuncSetAttribute((const void*)k_dec_select_big, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 BIG_LDS);
+    });
+    if (ae != hipSuccess) return ae;
+    if (nmin <= DT * PERT_MAX)
+      hipLaunchKernelGGL(k_dec_select<PERT_MAX>, dim3((unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s, vs, b,
+                         W, flags);
+    hipLaunchKernelGGL(k_dec_select_big, dim3((unsigned)nseq), dim3(DT), BIG_LDS, s, vs, b, W, flags);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    b.only = flags;
+    return launch_select_multi(views, qpos, nseq, b, s);
+  }
   if (small)
     hipLaunchKernelGGL(k_dec_select<20>, dim3((unsigned)nseq), dim3(DT), dec_lds(20), s, vs, b, W, flags);
   else

@@ -723,22 +723,26 @@ def test_decode_tied_scores_and_small_budgets():
 def test_decode_large_indexes():
     """Decode over indexes of about 19k, 22k and 25.6k buckets: 24 buckets per
     select thread, 19 and 22 partial score histograms (not multiples of four),
-    and, past 24576 buckets, the hand-off to the prefill selection kernel."""
+    past 24576 buckets the streaming kernel (alone, and in a batch beside a
+    register-resident sequence), and a zero latent query on the large index
+    (every score tied: the exact kernel, one sequence at its own position)."""
     dev = _dev()
     L = _L()
     wl = S.Workload("dec_large", 64, T=0, ncomp=128, block=64, buckets=32, iters=2, chunk=0,
                     budget=512, window=64, sinks=4, Hq=4, Hkv=2, D=64)
     steps = 2
     # full blocks of 64 pooled vectors give 32 buckets each; tails are singletons
-    Ts = [4 * 64 * 594 + 4 * 17 + 1, 4 * 64 * 687 + 4 * 40 + 3, 4 * 64 * 800 + 11]
-    nbk = [594 * 32 + 17, 687 * 32 + 40, 800 * 32 + 2]
-    assert nbk[0] <= 20480 < nbk[1] <= 24576 < nbk[2]
+    # the last: 32776 buckets, not a multiple of the streaming kernel's 8192-bucket
+    # batch, so its final batch is partial for every lane but the first few
+    Ts = [4 * 64 * 594 + 4 * 17 + 1, 4 * 64 * 687 + 4 * 40 + 3, 4 * 64 * 800 + 11, 4 * 64 * 1024 + 4 * 8 + 1]
+    nbk = [594 * 32 + 17, 687 * 32 + 40, 800 * 32 + 2, 1024 * 32 + 8]
+    assert nbk[0] <= 20480 < nbk[1] <= 24576 < nbk[2] < nbk[3]
     cap = max(Ts) + steps
     op = _oparams(wl)
     ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, 0, 0, 0, cap)
-    gens = [S.Synth(wl, seq=i, data_cfg=64) for i in range(3)]
+    gens = [S.Synth(wl, seq=i, data_cfg=64) for i in range(4)]
     lat = [g.latk(0, cap) for g in gens]
-    K = torch.empty((3, cap, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    K = torch.empty((4, cap, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
     V = torch.empty_like(K)
     for i, g in enumerate(gens):
         g.fill_rows("k", K[i], 0, chunk=1 << 16)
@@ -746,8 +750,8 @@ def test_decode_large_indexes():
     sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
     osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
-    caches = [dict() for _ in range(3)]
-    for batch in ([0, 1], [2]):
+    caches = [dict() for _ in range(4)]
+    for batch in ([0, 1], [2], [1, 2], [3]):
         ixs = []
         for i in batch:
             ix = L.LsaIndex(ip, dev)
@@ -762,6 +766,8 @@ def test_decode_large_indexes():
             ts = [Ts[i] + step for i in batch]
             lk_new = torch.stack([lat[i][t] for i, t in zip(batch, ts)])
             lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i, t in zip(batch, ts)])
+            if batch == [2] and step == 1:
+                lq.zero_()
             q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i, t in zip(batch, ts)])
             print(f"decode batch {batch} step {step}", flush=True)
             out = L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kb, Vb, cap, sp, ap, ws=ws)
