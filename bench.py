@@ -337,8 +337,8 @@ def bench_train(args, dev, steps=3, warmup=1):
     return res
 
 
-def bench_decode(args, dev):
-    wl = S.WORKLOADS["decode_1m"]
+def bench_decode(args, dev, wl=None):
+    wl = wl or S.WORKLOADS["decode_1m"]
     cap = wl.T + wl.steps
     log(f"[bench] decode: {wl.nseq} sequences x {wl.T} keys, {wl.steps} steps")
     ixs, lat, gens = [], [], []
@@ -594,6 +594,9 @@ def main():
                     help="the whole context chunk by chunk (index grown from empty); prints its own line")
     ap.add_argument("--train", action="store_true",
                     help="only the 128k training step (forward + backward of one layer)")
+    ap.add_argument("--long-decode", action="store_true",
+                    help="decode at 2M, 4M and 10M keys per sequence (indexes beyond the "
+                         "register-resident select)")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only the decode benchmark (for rocprofv3 kernel traces)")
     ap.add_argument("--summarize-decode", nargs=2, metavar=("STATS", "COMMAND"),
@@ -618,7 +621,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     workers_pool = None
-    if not (args.no_cpu or args.profile or args.profile_decode or args.full_prefill or args.train):
+    if not (args.no_cpu or args.profile or args.profile_decode or args.full_prefill or args.train
+            or args.long_decode):
         # forked before anything touches the GPU; the workers only run the CPU oracle
         import multiprocessing as mp
         workers_pool = mp.get_context("fork").Pool(min(16, os.cpu_count() or 1))
@@ -641,6 +645,22 @@ def main():
         print(json.dumps({"metric": "LSA layer training step (fwd + bwd) tokens/s at 128k",
                           "value": tr["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
                           "data": "synthetic", "config": tr}), flush=True)
+        return
+    if args.long_decode:
+        import dataclasses
+        runs = []
+        for T, nseq in ((2 << 20, 4), (4 << 20, 4), (10 << 20, 2)):
+            wl = dataclasses.replace(S.WORKLOADS["decode_1m"], name=f"decode_{T >> 20}m", T=T, nseq=nseq,
+                                     steps=64)
+            d = bench_decode(args, dev, wl)
+            log(f"[bench] decode {T >> 20}M keys x {nseq}: {d['tokens_per_s']:.0f} tok/s "
+                f"({d['ms_per_step']:.3f} ms/step, frac {d['roofline']['frac']:.2f})")
+            runs.append(d)
+            torch.cuda.empty_cache()
+        print(json.dumps({"metric": "LSA decode tokens/s at long contexts", "value": runs[-1]["tokens_per_s"],
+                          "unit": "tokens/s", "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
+                          "config": {"workload": "decode at 2M / 4M / 10M keys per sequence", "runs": runs}}),
+              flush=True)
         return
     if args.profile_decode:
         d = bench_decode(args, dev)
