@@ -22,6 +22,9 @@
 //                 equal scores) takes the general path: histogram refinement
 //                 of the order-key range until the bracket holding the cutoff
 //                 has at most 256 entries, which are sorted.
+//   k_dec_select_big  the same rule for indexes beyond the registers (more
+//                 than 24576 buckets): the histogram summed from the partials,
+//                 the scores streamed once from the workspace to classify.
 #include <climits>
 #include <cstring>
 
@@ -165,8 +168,6 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
     }
   }
   if ((int)blockIdx.x * DT >= V.n_bkt) return;          // uniform: past this sequence's index
-  // the streaming select bins its own scores: no partial histograms for it
-  const bool want_hist = V.n_bkt <= DT * PERT_MAX;
   for (int b = threadIdx.x; b < NBIN; b += DT) hist[b] = 0;
   __syncthreads();                                      // (also publishes the appended bucket here)
   const int beta = blockIdx.x * DT + threadIdx.x;
@@ -181,7 +182,6 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
                 load_bucket<false>(V, beta), hist);
     }
   }
-  if (!want_hist) return;                               // uniform
   __syncthreads();
   // the whole histogram, zeros included: nothing has to be cleared beforehand
   int2* out = reinterpret_cast<int2*>(W.hpart + ((int64_t)seq * W.n_part + blockIdx.x) * NBIN);
@@ -672,15 +672,13 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
 }
 
 // Indexes beyond the register-resident instance (more than DT * PERT_MAX
-// buckets, up to BIG_NW * 32): the same rule with the scores streamed from
-// the workspace twice, once into the LDS histogram of eligible keys per score
-// bin, once to classify against the cutoff bin's score range; then the shared
-// tail.  A cutoff bin of more than BCAP buckets flags the sequence for the
-// exact kernel.
+// buckets, up to BIG_NW * 32): the same rule, with the histogram summed from
+// the score kernel's partials and the scores streamed from the workspace once
+// to classify against the cutoff bin's score range; then the shared tail.  A
+// cutoff bin of more than BCAP buckets flags the sequence for the exact kernel.
 constexpr int BIG_NW = 10240;       // bitmap words: bucket ids below 327680
 constexpr int BIG_LDS = (4 * TCAP + 2 * BIG_NW) * 4;
-constexpr int BIG_U = 8;            // buckets per thread and batch (loads in flight)
-static_assert(NBIN <= 4 * TCAP, "the histogram fits in the list region");
+constexpr int BIG_U = 16;           // buckets per thread and batch (loads in flight)
 
 __global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, DecWs W,
                                                        int32_t* __restrict__ flags) {
@@ -689,7 +687,7 @@ __global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, D
   __shared__ int s_ci[BCAP], s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
   __shared__ int s_fc[4];              // cut bin, keys above it, its scores [lo, hi]
   __shared__ int s_nt, s_nb;
-  extern __shared__ int s_e[];         // histogram, then ids, tks, sid, stk [TCAP], bm, wp [BIG_NW]
+  extern __shared__ int s_e[];         // ids, tks, sid, stk [TCAP], bm, wp [BIG_NW]
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int seq = blockIdx.x;
   const IdxView V = vsp->v[seq];
@@ -705,29 +703,27 @@ __global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, D
   }
   const int32_t* sc = W.score + base;
   const int32_t* el = W.elig + base;
-  int* hist = s_e;
-  for (int b = tid; b < NBIN; b += DT) hist[b] = 0;
   if (tid == 0) { s_fc[0] = NBIN; s_fc[1] = 0; s_fc[2] = INT_MAX; s_fc[3] = INT_MAX; s_nt = 0; s_nb = 0; }
-  __syncthreads();
-  // pass 1: eligible keys per score bin.  Both passes run the same number of
-  // batches on every lane (the wave scans in pass 2 need every lane).
-  for (int j0 = 0; j0 < n; j0 += BIG_U * DT) {
-    int sv[BIG_U], ev[BIG_U];
+  // bins from the top score down: thread tid takes bins NBIN-1-2tid (he[0])
+  // and NBIN-2-2tid (he[1]), summed over the score workgroups' partials
+  int he[2] = {0, 0};
+  {
+    const int nwg = (n + DT - 1) / DT;
+    const int2* hp = reinterpret_cast<const int2*>(W.hpart + (int64_t)seq * W.n_part * NBIN) + (NBIN / 2 - 1 - tid);
+    int w = 0;
+    for (; w + 8 <= nwg; w += 8) {
+      int2 x[8];
 #pragma unroll
-    for (int u = 0; u < BIG_U; ++u) {
-      const int j = j0 + u * DT + tid;
-      sv[u] = j < n ? sc[j] : 0;
-      ev[u] = j < n ? el[j] : 0;
+      for (int k = 0; k < 8; ++k) x[k] = hp[(int64_t)(w + k) * (NBIN / 2)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) { he[0] += x[k].y; he[1] += x[k].x; }
     }
-#pragma unroll
-    for (int u = 0; u < BIG_U; ++u)
-      if (ev[u] > 0) atomicAdd(&hist[score_bin(sv[u])], ev[u]);
+    for (; w < nwg; ++w) {
+      const int2 x = hp[(int64_t)w * (NBIN / 2)];
+      he[0] += x.y;
+      he[1] += x.x;
+    }
   }
-  __syncthreads();
-  // the cutoff bin, as in k_dec_select
-  int he[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) he[j] = hist[NBIN - 1 - (2 * tid + j)];
   int te;
   const int pe = block_excl_scan<DT>(min(he[0] + he[1], B + 1), s_ired, &te);
   if (B > 0 && te <= B) {
@@ -745,7 +741,7 @@ __global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, D
       ce = he[j] >= B - ce ? B : ce + he[j];
     }
   }
-  __syncthreads();                     // (also ends the reads of hist)
+  __syncthreads();
   const int above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
   const int nw = (n + 31) / 32;
   int* ids = s_e;
@@ -755,8 +751,9 @@ __global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, D
   unsigned* bm = reinterpret_cast<unsigned*>(s_e + 4 * TCAP);
   int* wp = s_e + 4 * TCAP + BIG_NW;
   for (int w = tid; w < nw; w += DT) bm[w] = 0u;
-  // pass 2: buckets above the cut bin are taken whole (slots reserved once per
-  // wave and batch); the cut bin's buckets are collected
+  // buckets above the cut bin are taken whole (slots reserved once per wave
+  // and batch); the cut bin's buckets are collected
+  // (every lane runs the same number of batches: the wave scan needs them all)
   for (int j0 = 0; j0 < n; j0 += BIG_U * DT) {
     int sv[BIG_U], ev[BIG_U];
 #pragma unroll
