@@ -11,6 +11,7 @@
 namespace lsa {
 
 constexpr int kDim = 64;          // latent dimension (bytes per latent row)
+constexpr int kSupMaskWords = 64; // Tree decode: one bit per super (at most 2048 supers)
 constexpr uint64_t kMagic = 0x4c53414d49333535ull;
 
 // Host descriptor behind the opaque lsa_index.
@@ -137,9 +138,11 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
 size_t select_tree_ws_bytes(int32_t nq);
 hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
 // Tree decode: query i is sequence i's new position on its own index (<= 16);
-// flags: nseq ints of workspace
+// flags: nseq ints of workspace (0 served, 1 for the exact kernel, 2 for the streaming
+// decode kernels with the chosen supers in supmask, kSupMaskWords per
+// sequence; supmask nullptr: no flag 2)
 hipError_t launch_select_tree_multi(const IdxView* views, const int32_t* qpos, int32_t nseq,
-                                   const SelArgs& a, int32_t* flags, hipStream_t s);
+                                   const SelArgs& a, int32_t* flags, uint32_t* supmask, hipStream_t s);
 // decode: one query per sequence, each on its own index (max_bkt = bucket
 // capacity).  app (nullable): the one-key append of the batched sequences,
 // enqueued before the selection (fused into its first kernel where it can);

@@ -92,6 +92,7 @@ struct DecWs {
   int32_t* hpart;                   // [nseq][cap / DT rounded up][NBIN] eligible keys per score bin,
                                     // one histogram per score workgroup
   int32_t n_part;                   // histograms per sequence
+  uint32_t* supmask;                // [nseq][kSupMaskWords] Tree: supers chosen
 };
 
 
@@ -100,7 +101,7 @@ struct DecWs {
 // this workgroup); bi: its descriptor
 __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, const DecWs& W, int t,
                                           int seq, int cap, int beta, const int8_t* crow,
-                                          const BucketInfo& bi, int* hist) {
+                                          const BucketInfo& bi, int* hist, bool cand) {
   const int* q4 = reinterpret_cast<const int*>(A.latq + (int64_t)seq * kDim);
   const int4* c4 = reinterpret_cast<const int4*>(crow);
   int acc = 0;
@@ -112,8 +113,8 @@ __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, co
     acc = __builtin_amdgcn_sdot4(q4[4 * k + 2], c.z, acc, false);
     acc = __builtin_amdgcn_sdot4(q4[4 * k + 3], c.w, acc, false);
   }
-  int klo;
-  const int e = eligible<false>(V, beta, bi, t, A.window, A.sinks, &klo);
+  int klo = 0;
+  const int e = cand ? eligible<false>(V, beta, bi, t, A.window, A.sinks, &klo) : 0;
   const int64_t at = (int64_t)seq * cap + beta;
   W.score[at] = acc;
   W.elig[at] = e;
@@ -126,13 +127,22 @@ __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, co
 // a pooled group, the workgroup holding the new singleton bucket pools it,
 // writes the bucket and scores it from LDS.  No other workgroup reads the new
 // bucket, and the selection kernel runs after this one.
+// tsel (nullable, Tree): only sequences with tsel[seq] == 2 are scored, and
+// only their candidate leaves count as eligible: the leaves of the supers in
+// W.supmask and the leaves outside complete groups.  No append then.
 __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs W, DecodeAppendArgs D,
-                                                  const int8_t* __restrict__ src) {
+                                                  const int8_t* __restrict__ src,
+                                                  const int32_t* __restrict__ tsel) {
   __shared__ int hist[NBIN];
   __shared__ __attribute__((aligned(16))) int8_t s_pv[kDim];
+  __shared__ unsigned s_mask[kSupMaskWords];
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int seq = blockIdx.y;
   const IdxView V = vsp->v[seq];
+  if (tsel) {                                           // uniform
+    if (tsel[seq] != 2) return;
+    if (threadIdx.x < kSupMaskWords) s_mask[threadIdx.x] = W.supmask[(int64_t)seq * kSupMaskWords + threadIdx.x];
+  }
   int beta_new = -1;
   int64_t g_new = 0;
   if (D.batched[seq]) {                                 // uniform
@@ -172,14 +182,19 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
   __syncthreads();                                      // (also publishes the appended bucket here)
   const int beta = blockIdx.x * DT + threadIdx.x;
   if (beta < V.n_bkt) {
+    bool cand = true;
+    if (tsel && beta < V.covered) {
+      const unsigned ls = (unsigned)V.leafsup[beta];
+      cand = ls < 32u * kSupMaskWords && ((s_mask[ls >> 5] >> (ls & 31)) & 1u);
+    }
     if (beta == beta_new) {
       BucketInfo bi;
       bi.first = bi.last = bi.off = (int)g_new;
       bi.cnt = 1;
-      score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta, s_pv, bi, hist);
+      score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta, s_pv, bi, hist, cand);
     } else {
       score_one(V, A, W, vsp->qpos[seq], seq, VS.cap, beta, V.cent + (int64_t)beta * kDim,
-                load_bucket<false>(V, beta), hist);
+                load_bucket<false>(V, beta), hist, cand);
     }
   }
   __syncthreads();
@@ -680,8 +695,10 @@ constexpr int BIG_NW = 10240;       // bitmap words: bucket ids below 327680
 constexpr int BIG_LDS = (4 * TCAP + 2 * BIG_NW) * 4;
 constexpr int BIG_U = 16;           // buckets per thread and batch (loads in flight)
 
+// tree != 0: serve exactly the sequences flagged 2 by the Tree kernel (any
+// size; the score kernel filtered their candidates), leaving the others.
 __global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, DecWs W,
-                                                       int32_t* __restrict__ flags) {
+                                                       int32_t* __restrict__ flags, int tree) {
   __shared__ int s_ired[DW];
   __shared__ long long s_cq[BCAP];
   __shared__ int s_ci[BCAP], s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
@@ -696,7 +713,11 @@ __global__ void __launch_bounds__(DT) k_dec_select_big(DecViews VS, SelArgs A, D
   const int B = budget_at(A, t);
   const int n = V.n_bkt;
   const int64_t base = (int64_t)seq * VS.cap;
-  if (n <= DT * PERT_MAX) return;      // uniform: k_dec_select serves it
+  if (tree) {                          // uniform
+    if (flags[seq] != 2) return;
+  } else if (n <= DT * PERT_MAX) {     // k_dec_select serves it
+    return;
+  }
   if (n > BIG_NW * 32) {               // beyond the bitmap: the exact kernel serves it
     if (tid == 0) flags[seq] = 1;
     return;
@@ -814,6 +835,7 @@ size_t dec_layout(int32_t nseq, int32_t cap, DecWs* W, int32_t** flags, void* ws
   w.kstart = reinterpret_cast<int32_t*>(take(n * sizeof(int32_t)));
   w.n_part = (cap + DT - 1) / DT;
   w.hpart = reinterpret_cast<int32_t*>(take((size_t)nseq * w.n_part * NBIN * sizeof(int32_t)));
+  w.supmask = reinterpret_cast<uint32_t*>(take((size_t)nseq * kSupMaskWords * sizeof(uint32_t)));
   int32_t* f = reinterpret_cast<int32_t*>(take((size_t)nseq * sizeof(int32_t)));
   if (W) *W = w;
   if (flags) *flags = f;
@@ -854,15 +876,37 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
     hipError_t e = launch_decode_append(*app, app_src, nseq, s);
     if (e != hipSuccess) return e;
   }
-  if (tree) return launch_select_tree_multi(views, qpos, nseq, b, flags, s);
+  static std::atomic<unsigned long long> big_done{0};
+  auto big_attr = []() {
+    return hipFuncSetAttribute((const void*)k_dec_select_big, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               BIG_LDS);
+  };
+  DecodeAppendArgs none;
+  memset(&none, 0, sizeof none);
+  if (tree) {
+    // the Tree kernel; sequences whose candidates overflow it (flag 2) go
+    // through the streaming pair on their candidate leaves; what is still
+    // flagged goes to the exact kernel
+    hipError_t e = launch_select_tree_multi(views, qpos, nseq, b, flags, W.supmask, s);
+    if (e != hipSuccess) return e;
+    if (nmax > 0 && nmax <= BIG_NW * 32) {
+      e = once_per_device(big_done, big_attr);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
+                         s, vs, b, W, none, (const int8_t*)nullptr, (const int32_t*)flags);
+      hipLaunchKernelGGL(k_dec_select_big, dim3((unsigned)nseq), dim3(DT), BIG_LDS, s, vs, b, W, flags, 1);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    b.only = flags;
+    return launch_select_multi(views, qpos, nseq, b, s);
+  }
   if (nmax > BIG_NW * 32) return launch_select_multi(views, qpos, nseq, b, s);
   const bool big = nmax > DT * PERT_MAX;
   const bool small = nmax <= DT * 20;
   if (nmax > 0) {
-    DecodeAppendArgs none;
-    memset(&none, 0, sizeof none);
     hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
-                       s, vs, b, W, app ? *app : none, app_src);
+                       s, vs, b, W, app ? *app : none, app_src, (const int32_t*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -879,16 +923,12 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
     // sequences above DT * PERT_MAX buckets: the streaming kernel (the other
     // kernel flags them and returns; this one overwrites their flags); any
     // sequence flagged then goes to the exact kernel
-    static std::atomic<unsigned long long> big_done{0};
-    ae = once_per_device(big_done, []() {
-      return hipFuncSetAttribute((const void*)k_dec_select_big, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 BIG_LDS);
-    });
+    ae = once_per_device(big_done, big_attr);
     if (ae != hipSuccess) return ae;
     if (nmin <= DT * PERT_MAX)
       hipLaunchKernelGGL(k_dec_select<PERT_MAX>, dim3((unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s, vs, b,
                          W, flags);
-    hipLaunchKernelGGL(k_dec_select_big, dim3((unsigned)nseq), dim3(DT), BIG_LDS, s, vs, b, W, flags);
+    hipLaunchKernelGGL(k_dec_select_big, dim3((unsigned)nseq), dim3(DT), BIG_LDS, s, vs, b, W, flags, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     b.only = flags;

@@ -857,7 +857,14 @@ __device__ __forceinline__ int nth_member(const int32_t* off, const int32_t* mem
   return mem[off[nodes[a]] + (f - pre[a])];
 }
 
-__global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, int32_t* flags) {
+static_assert(SUPN / 32 == kSupMaskWords, "Tree decode super mask size");
+
+// supmask (nullable, decode): a query whose supers were chosen but whose
+// candidates overflow the registers (or whose cut does not resolve here) gets
+// the chosen supers as a bit mask (kSupMaskWords words per query) and flag 2,
+// for the streaming decode kernels; other flagged queries get flag 1.
+__global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, int32_t* flags,
+                                                       uint32_t* supmask) {
   __shared__ ResolveLds L;
   __shared__ long long s_tmp[SUPN];
   __shared__ int s_sup[TOPCAP];       // selected supers
@@ -915,6 +922,7 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, 
     if (wave == 0) node_prefix(V.scnt, s_sup, Rs, s_pre);   // leaves of the taken supers
     __syncthreads();
   }
+  const bool supok = ok;               // uniform: the chosen supers are final
   const int nsel = ok && sup ? s_pre[TOPCAP] : 0;
   const int ncand = nsel + n_unc;
   ok = ok && ncand <= CPT * RT;
@@ -957,7 +965,18 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, 
   }
   ok = select_and_emit<CPT>(L, V, A, q, t, ok, K, e, lo, hi, tot, true,
                             [&](int u) { return ks[u]; });
-  if (tid == 0) flags[q] = ok ? 0 : 1;
+  const bool stream = supmask != nullptr && supok;   // uniform
+  if (stream) {
+    __shared__ unsigned s_mask[kSupMaskWords];
+    __syncthreads();
+    if (tid < kSupMaskWords) s_mask[tid] = 0u;
+    __syncthreads();
+    if (sup)
+      for (int j = tid; j < Rs; j += RT) atomicOr(&s_mask[s_sup[j] >> 5], 1u << (s_sup[j] & 31));
+    __syncthreads();
+    if (tid < kSupMaskWords) supmask[(int64_t)q * kSupMaskWords + tid] = s_mask[tid];
+  }
+  if (tid == 0) flags[q] = ok ? 0 : (stream ? 2 : 1);
 }
 
 constexpr int kPrefW = 8, kPrefQ = 64;     // prefill scan: 8 waves (two per query group), 64 query slots
@@ -1009,7 +1028,7 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
 size_t select_tree_ws_bytes(int32_t nq) { return ((size_t)nq * sizeof(int32_t) + 255) / 256 * 256; }
 
 hipError_t launch_select_tree_multi(const IdxView* views, const int32_t* qpos, int32_t nseq,
-                                   const SelArgs& a, int32_t* flags, hipStream_t s) {
+                                   const SelArgs& a, int32_t* flags, uint32_t* supmask, hipStream_t s) {
   if (nseq <= 0) return hipSuccess;
   if (nseq > 16) return hipErrorInvalidValue;
   FastViews vs;
@@ -1022,12 +1041,8 @@ hipError_t launch_select_tree_multi(const IdxView* views, const int32_t* qpos, i
   vs.view_per_query = 1;
   SelArgs b = a;
   b.nq = nseq;
-  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)nseq), dim3(RT), 0, s, vs, b, flags);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // exact refinement for the flagged sequences; other workgroups exit at once
-  b.only = flags;
-  return launch_select_multi(views, qpos, nseq, b, s);
+  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)nseq), dim3(RT), 0, s, vs, b, flags, supmask);
+  return hipGetLastError();
 }
 
 hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s) {
@@ -1037,7 +1052,8 @@ hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipS
   memset(&vs, 0, sizeof vs);
   vs.v[0] = v;
   vs.nviews = 1;
-  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)a.nq), dim3(RT), 0, s, vs, a, flags);
+  hipLaunchKernelGGL(k_tree_select, dim3((unsigned)a.nq), dim3(RT), 0, s, vs, a, flags,
+                     (uint32_t*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // exact refinement for the flagged queries; other workgroups exit at once

@@ -883,6 +883,64 @@ def test_single_sequence_tree_decode_with_tied_scores():
         assert err <= TOL, (step, err)
 
 
+def test_tree_decode_candidate_overflow():
+    """Tree decode where the chosen supers hold more leaves than the Tree
+    kernel's candidate list (72 of 96 supers, about 5000 leaves): that
+    sequence goes through the streaming pair restricted to its candidates,
+    batched with a sequence the Tree kernel serves; a zero query (every score
+    tied) then falls through to the exact kernel."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("dec_tree_ovf", 71, T=0, ncomp=64, block=64, buckets=16, iters=3, tree_group=64,
+                    tree_super=16, tree_iters=3, tree_top=72, chunk=0, budget=1500, window=32,
+                    sinks=4, Hq=8, Hkv=2, D=64)
+    kpg = wl.pool * wl.block * wl.tree_group           # keys per group
+    Ts = [6 * kpg + 300, kpg + 500]
+    steps = 3
+    cap = max(Ts) + steps
+    gens = [S.Synth(wl, seq=i, data_cfg=71) for i in range(len(Ts))]
+    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
+                       wl.tree_iters, cap)
+    op = _oparams(wl)
+    K = torch.empty((len(Ts), cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    ixs, lat = [], []
+    for i, g in enumerate(gens):
+        lk = g.latk(0, cap)
+        lat.append(lk)
+        ix = L.LsaIndex(ip, dev)
+        ix.build(lk[:Ts[i]].to(dev))
+        ixs.append(ix)
+        g.fill_rows("k", K[i], 0)
+        g.fill_rows("v", V[i], 0)
+    Kd, Vd = K.to(dev), V.to(dev)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, len(Ts)), dtype=torch.uint8,
+                     device=dev)
+    errs = []
+    for step in range(steps):
+        ts = [T + step for T in Ts]
+        lk_new = torch.stack([lat[i][t] for i, t in enumerate(ts)])
+        lq = torch.stack([gens[i].latq_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        if step == 0:
+            lq[0].zero_()
+        q = torch.stack([gens[i].q_rows(torch.tensor([t]))[0] for i, t in enumerate(ts)])
+        print(f"tree overflow decode step {step}", flush=True)
+        out = L.decode_step(ixs, lk_new.to(dev), lq.to(dev), q.to(dev), Kd, Vd, cap, sp, ap, ws=ws)
+        idx, cnt = L.decode_selection(ws, len(Ts), sp)
+        torch.cuda.synchronize()
+        for i, t in enumerate(ts):
+            ref = O.build_index(lat[i].numpy(), t + 1, op)
+            sel = O.select(ref, lq[i].numpy(), t, osp)
+            n = int(cnt[i])
+            assert np.array_equal(np.sort(idx[i, :n].cpu().numpy()), sel), f"seq {i} step {step}"
+            ro = oracle_attention(gens[i], wl, [t], [sel])[0]
+            errs.append(normwise(out[i].cpu().numpy().astype(np.float64), ro))
+    assert max(errs) <= TOL
+
+
 def test_api_errors_leave_index_unchanged(tiny):
     wl, g, latk, ref, dev = tiny
     L = _L()
