@@ -127,9 +127,10 @@ __device__ __forceinline__ void score_one(const IdxView& V, const SelArgs& A, co
 // a pooled group, the workgroup holding the new singleton bucket pools it,
 // writes the bucket and scores it from LDS.  No other workgroup reads the new
 // bucket, and the selection kernel runs after this one.
-// tsel (nullable, Tree): only sequences with tsel[seq] == 2 are scored, and
-// only their candidate leaves count as eligible: the leaves of the supers in
-// W.supmask and the leaves outside complete groups.  No append then.
+// TREE: only sequences with tsel[seq] == 2 are scored, and only their
+// candidate leaves count as eligible: the leaves of the supers in W.supmask
+// and the leaves outside complete groups.  No append then.
+template <bool TREE>
 __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs W, DecodeAppendArgs D,
                                                   const int8_t* __restrict__ src,
                                                   const int32_t* __restrict__ tsel) {
@@ -139,13 +140,13 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int seq = blockIdx.y;
   const IdxView V = vsp->v[seq];
-  if (tsel) {                                           // uniform
+  if (TREE) {
     if (tsel[seq] != 2) return;
     if (threadIdx.x < kSupMaskWords) s_mask[threadIdx.x] = W.supmask[(int64_t)seq * kSupMaskWords + threadIdx.x];
   }
   int beta_new = -1;
   int64_t g_new = 0;
-  if (D.batched[seq]) {                                 // uniform
+  if (!TREE && D.batched[seq]) {                        // uniform
     char* abase = D.arena[seq];
     int8_t* pend = reinterpret_cast<int8_t*>(abase + D.off_pend) + (int64_t)D.pend_slot[seq] * D.p * kDim;
     const int np = D.n_pend[seq];
@@ -183,7 +184,7 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
   const int beta = blockIdx.x * DT + threadIdx.x;
   if (beta < V.n_bkt) {
     bool cand = true;
-    if (tsel && beta < V.covered) {
+    if (TREE && beta < V.covered) {
       const unsigned ls = (unsigned)V.leafsup[beta];
       cand = ls < 32u * kSupMaskWords && ((s_mask[ls >> 5] >> (ls & 31)) & 1u);
     }
@@ -892,7 +893,7 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
     if (nmax > 0 && nmax <= BIG_NW * 32) {
       e = once_per_device(big_done, big_attr);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
+      hipLaunchKernelGGL(k_dec_score<true>, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
                          s, vs, b, W, none, (const int8_t*)nullptr, (const int32_t*)flags);
       hipLaunchKernelGGL(k_dec_select_big, dim3((unsigned)nseq), dim3(DT), BIG_LDS, s, vs, b, W, flags, 1);
       e = hipGetLastError();
@@ -905,7 +906,7 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   const bool big = nmax > DT * PERT_MAX;
   const bool small = nmax <= DT * 20;
   if (nmax > 0) {
-    hipLaunchKernelGGL(k_dec_score, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
+    hipLaunchKernelGGL(k_dec_score<false>, dim3((unsigned)((nmax + DT - 1) / DT), (unsigned)nseq), dim3(DT), 0,
                        s, vs, b, W, app ? *app : none, app_src, (const int32_t*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
