@@ -221,6 +221,70 @@ def test_decode_1m_256_steps(oracle_pool):
                 O.build_index(lat_h[0], cap, _oparams(wl), caches[0]))
 
 
+def test_tree_decode_2m_four_sequences(oracle_pool):
+    """Tree decode at 4 sequences x 2M keys (G=64, S=64, R=32): the 32 chosen
+    supers of 128 carry about 5000 leaves, more than the Tree kernel's
+    candidate list, so the streaming pair serves these sequences."""
+    import dataclasses
+    dev = _dev()
+    L = _L()
+    # same latents as decode_1m (the data depends on the workload's data id only)
+    wl = dataclasses.replace(S.WORKLOADS["decode_1m"], name="decode_tree_2m", T=2 << 20, nseq=4,
+                             steps=4, tree_group=64, tree_super=64, tree_iters=4, tree_top=32)
+    cap = wl.T + wl.steps
+    gens = [S.Synth(wl, seq=i) for i in range(wl.nseq)]
+    K = torch.empty((wl.nseq, cap, wl.Hkv, wl.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
+                       wl.tree_iters, cap)
+    ixs, lats = [], []
+    for i, g in enumerate(gens):
+        lk = g.latk(0, cap, device=dev, chunk=1 << 22)
+        lats.append(lk)
+        g.fill_rows("k", K[i], 0, chunk=1 << 18)
+        g.fill_rows("v", V[i], 0, chunk=1 << 18)
+        ix = L.LsaIndex(ip, dev)
+        ix.build(lk[:wl.T])
+        ixs.append(ix)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    ap32 = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap32, wl.nseq), dtype=torch.uint8,
+                     device=dev)
+    check_steps = {0, wl.steps - 1}
+    got = {}
+    for s in range(wl.steps):
+        t = wl.T + s
+        pos = torch.tensor([t], device=dev)
+        lk_new = torch.stack([lats[i][t] for i in range(wl.nseq)]).contiguous()
+        lq = torch.cat([gens[i].latq_rows(pos, device=dev) for i in range(wl.nseq)]).contiguous()
+        q = torch.cat([gens[i].q_rows(pos, device=dev) for i in range(wl.nseq)]).contiguous()
+        out = L.decode_step(ixs, lk_new, lq, q, K, V, cap, sp, ap32, ws=ws)
+        if s in check_steps:
+            idx, cnt = L.decode_selection(ws, wl.nseq, sp)
+            got[s] = (idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy())
+    torch.cuda.synchronize()
+    del K, V, lats
+    torch.cuda.empty_cache()
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    worst = 0.0
+    lat_h = []
+    for i in range(wl.nseq):
+        cache, lat0 = build_cache_parallel("decode_1m", wl.T, oracle_pool, seq=i)   # host-generated
+        lat_h.append(np.concatenate([lat0, gens[i].latk(wl.T, cap).numpy()]))
+        for s in sorted(check_steps):
+            t = wl.T + s
+            ref = O.build_index(lat_h[i], t + 1, _oparams(wl), cache)
+            lq = gens[i].latq_rows(torch.tensor([t])).numpy()[0]
+            sel = O.select(ref, lq, t, osp)
+            idx, cnt, out = got[s]
+            assert np.array_equal(np.sort(idx[i, :cnt[i]]), sel), f"sequence {i} step {s}"
+            ro = oracle_attention(gens[i], wl, [t], [sel])[0]
+            worst = max(worst, normwise(out[i].astype(np.float64), ro))
+    print(f"tree decode 2M: selections bit-exact at {len(check_steps)} steps x {wl.nseq} sequences, "
+          f"attention normwise error {worst:.3e}")
+    assert worst <= TOL
+
+
 def test_flat_1m_chunked_prefill_from_empty(oracle_1m):
     """The whole 1M context through lsa_prefill_chunk, 32 chunks from an empty
     index: the final index equals the oracle's build, and sampled queries of
