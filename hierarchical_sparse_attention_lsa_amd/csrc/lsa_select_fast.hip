@@ -391,6 +391,7 @@ constexpr int EPT = ECAP2 / RT;     // sorted taken buckets per thread
 // registers, in the same wave through shuffles, across waves through `tmp`.
 __device__ __forceinline__ int shfl_xor_t(int v, int m) { return __shfl_xor(v, m); }
 __device__ __forceinline__ long long shfl_xor_t(long long v, int m) { return shfl_xor_i64(v, m); }
+__device__ __forceinline__ unsigned shfl_xor_t(unsigned v, int m) { return (unsigned)__shfl_xor((int)v, m); }
 
 template <int N, class T>
 __device__ __forceinline__ void block_bitonic(T (&v)[N / RT], T* tmp) {
@@ -774,6 +775,7 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
 constexpr int SUPN = 2048;          // supers sorted per query (n_sup <= SUPN)
 constexpr int CPT = 16;             // candidate leaves per thread
 constexpr int TOPCAP = 256;         // tree_top served here
+constexpr int kTreeStreamMin = 1024; // decode: more candidates may go to the streaming pair
 
 __device__ __forceinline__ int dot64(const int (&qv)[16], const int8_t* c) {
   const int4* c4 = reinterpret_cast<const int4*>(c);
@@ -789,38 +791,51 @@ __device__ __forceinline__ int dot64(const int (&qv)[16], const int8_t* c) {
   return acc;
 }
 
+// Order of node `id` (< SUPN) with score s as 32 bits: (score desc, id asc)
+// is the descending order of this key.  A 64-dim int8 dot product lies in
+// [-1040384, 1048576], so s + 2^20 - 1 takes 21 bits and the id 11.
+static_assert(SUPN <= 2048, "node ids take 11 bits of the node key");
+__device__ __forceinline__ unsigned node_key(int s, int id) {
+  return ((unsigned)(s + (1 << 20) - 1) << 11) | (unsigned)(2047 - id);
+}
+
 // The R best of n nodes by (score desc, id asc): candidate c is node id_of(c)
-// with centroid cent[id]; out[r] = id of rank r (R <= n).  Every thread
-// reads its candidates before the sort's first barrier and writes after it.
+// with centroid cent[id]; out[r] = id of rank r (R <= n <= NS).  Every
+// thread reads its candidates before the sort's first barrier and writes
+// after it.
 template <int NS, class IdOf>
 __device__ __forceinline__ void top_nodes(const int8_t* cent, int n, IdOf id_of,
                                           const int (&qv)[16], int R, long long* tmp, int* out) {
   constexpr int PT = NS / RT;
   const int tid = threadIdx.x;
-  // ascending sort of -order key = (score desc, id asc)
-  long long v[PT];
+  // ascending sort of the complemented keys; padding (all ones) sorts last,
+  // above every real key's complement (real keys are at least 8191 << 11)
+  unsigned v[PT];
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int c = tid * PT + i;
-    long long key = LLONG_MAX;
+    unsigned key = 0xffffffffu;
     if (c < n) {
       const int id = id_of(c);
-      key = -order_key(dot64(qv, cent + (int64_t)id * kDim), id);
+      key = ~node_key(dot64(qv, cent + (int64_t)id * kDim), id);
     }
     v[i] = key;
   }
-  block_bitonic<NS>(v, tmp);
+  block_bitonic<NS>(v, reinterpret_cast<unsigned*>(tmp));
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int r = tid * PT + i;
-    if (r < R) out[r] = (int)(0xffffffffu - (unsigned)((-v[i]) & 0xffffffffll));
+    if (r < R) out[r] = 2047 - (int)(~v[i] & 2047u);
   }
 }
 
+// the smallest sort that holds the n nodes (n <= SUPN)
 template <class IdOf>
 __device__ __forceinline__ void top_nodes_any(const int8_t* cent, int n, IdOf id_of,
                                               const int (&qv)[16], int R, long long* tmp, int* out) {
-  if (n <= 1024) top_nodes<1024>(cent, n, id_of, qv, R, tmp, out);
+  if (n <= 256) top_nodes<256>(cent, n, id_of, qv, R, tmp, out);
+  else if (n <= 512) top_nodes<512>(cent, n, id_of, qv, R, tmp, out);
+  else if (n <= 1024) top_nodes<1024>(cent, n, id_of, qv, R, tmp, out);
   else top_nodes<SUPN>(cent, n, id_of, qv, R, tmp, out);
 }
 
@@ -925,7 +940,11 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, 
   const bool supok = ok;               // uniform: the chosen supers are final
   const int nsel = ok && sup ? s_pre[TOPCAP] : 0;
   const int ncand = nsel + n_unc;
-  ok = ok && ncand <= CPT * RT;
+  // decode: one workgroup scores about 256 candidates per round of dependent
+  // loads, the streaming pair every leaf at once over many workgroups; many
+  // candidates that are also a large share of the leaves go to the latter
+  const bool to_stream = supmask != nullptr && ncand > kTreeStreamMin && 8ll * ncand > V.n_bkt;
+  ok = ok && ncand <= CPT * RT && !to_stream;
 
   long long K[CPT];
   int e[CPT], ks[CPT];
