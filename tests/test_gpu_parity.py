@@ -447,6 +447,40 @@ def test_tree_index_and_selection():
         check_selection(idx, cnt, refs, sp.max_sel)
 
 
+def test_tree_selection_at_extreme_scores():
+    """Latent keys whose pooled vectors are all -128 or all 127, so leaf and
+    super centroids sit at the int8 extremes, and queries of all -128 / all
+    127 / mixed signs: scores reach 2^20 and -1040384, the ends of the range
+    the Tree kernel packs into its 32-bit node keys, with many equal scores
+    ordered by id."""
+    dev = _dev()
+    L = _L()
+    wl = S.Workload("tree_extreme", 72, T=3 * 4 * 64 * 4 + 100, ncomp=64, block=64, buckets=16,
+                    iters=3, tree_group=4, tree_super=16, tree_iters=3, tree_top=5, chunk=0,
+                    budget=300, window=32, sinks=4, Hq=4, Hkv=1, D=64)
+    rng = np.random.default_rng(72)
+    sign = rng.integers(0, 2, size=(wl.T + wl.pool - 1) // wl.pool)     # per pooled group
+    rows = np.where(np.repeat(sign, wl.pool)[:wl.T, None] == 1, 127, -128)
+    latk = torch.from_numpy(np.broadcast_to(rows, (wl.T, 64)).astype(np.int8).copy())
+    ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
+    assert ref.n_grp == 3
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    torch.cuda.synchronize()
+    check_index(ix.arrays(), ref)
+    pos = [wl.T - 1, wl.T - 50, 2000, 900]
+    qs = [np.full(64, -128), np.full(64, 127), np.where(np.arange(64) % 2 == 0, 127, -128),
+          np.zeros(64)]
+    lq = torch.from_numpy(np.stack([q for q in qs for _ in pos]).astype(np.int8))
+    qpos = pos * len(qs)
+    for R in (1, 5, 12):
+        sp = L.SelectParams(wl.budget, wl.window, wl.sinks, R)
+        osp = O.SelectParams(wl.budget, wl.window, wl.sinks, R)
+        idx, cnt = ix.select(lq.to(dev), torch.tensor(qpos, dtype=torch.int32, device=dev), sp)
+        refs = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(qpos)]
+        check_selection(idx, cnt, refs, sp.max_sel)
+
+
 TREE3 = S.Workload("tree3_small", 71, T=4 * 64 * 2 * 10 + 300, ncomp=96, block=64, buckets=32,
                    iters=3, tree_group=2, tree_super=16, tree_iters=3, tree_top=6, tree2_group=4,
                    tree2_super=16, tree2_iters=3, tree2_top=3, chunk=0, budget=300, window=64,
