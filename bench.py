@@ -359,7 +359,7 @@ def bench_decode(args, dev, wl=None):
     lk_new = torch.stack([lat[i][wl.T:wl.T + steps] for i in range(wl.nseq)], 1).contiguous()
     lq = torch.stack([gens[i].latq_rows(new_pos, device=dev) for i in range(wl.nseq)], 1).contiguous()
     qs = torch.stack([gens[i].q_rows(new_pos, device=dev) for i in range(wl.nseq)], 1).contiguous()
-    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top if wl.tree_group else 0)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
     out = torch.empty((wl.nseq, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
     wsb = L.workspace_bytes(L.binding.OP_DECODE, ixs[0].params, sp, ap, wl.nseq)
@@ -388,6 +388,7 @@ def bench_decode(args, dev, wl=None):
     ms = dt * 1e3 / steps
     roof_ms = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
     return {"sequences": wl.nseq, "context": wl.T, "steps": steps,
+            "index": f"Tree G={wl.tree_group} S={wl.tree_super} R={wl.tree_top}" if wl.tree_group else "Flat",
             "ms_per_step": ms, "tokens_per_s": wl.nseq * steps / dt,
             "roofline": {"bound": "hbm", "algorithmic_bytes_per_step": step_bytes,
                          "roof_ms": roof_ms, "frac": roof_ms / ms,
@@ -657,9 +658,21 @@ def main():
                 f"({d['ms_per_step']:.3f} ms/step, frac {d['roofline']['frac']:.2f})")
             runs.append(d)
             torch.cuda.empty_cache()
+        # the same sequences on a two-level Tree index (G=64, S=64, R=32)
+        tree_runs = []
+        for T, nseq in ((2 << 20, 4), (10 << 20, 2)):
+            wl = dataclasses.replace(S.WORKLOADS["decode_1m"], name=f"decode_tree_{T >> 20}m", T=T, nseq=nseq,
+                                     steps=64, tree_group=64, tree_super=64, tree_iters=4, tree_top=32)
+            d = bench_decode(args, dev, wl)
+            log(f"[bench] Tree decode {T >> 20}M keys x {nseq}: {d['tokens_per_s']:.0f} tok/s "
+                f"({d['ms_per_step']:.3f} ms/step)")
+            tree_runs.append(d)
+            torch.cuda.empty_cache()
         print(json.dumps({"metric": "LSA decode tokens/s at long contexts", "value": runs[-1]["tokens_per_s"],
                           "unit": "tokens/s", "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
-                          "config": {"workload": "decode at 2M / 4M / 10M keys per sequence", "runs": runs}}),
+                          "config": {"workload": "decode at 2M / 4M / 10M keys per sequence (Flat; value: 10M), "
+                                                 "and on a Tree index at 2M / 10M", "runs": runs,
+                                     "tree_runs": tree_runs}}),
               flush=True)
         return
     if args.profile_decode:
