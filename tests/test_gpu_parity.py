@@ -917,24 +917,27 @@ def test_single_sequence_tree_decode_with_tied_scores():
         assert err <= TOL, (step, err)
 
 
-def test_tree_decode_candidate_overflow():
-    """Tree decode where the chosen supers hold more leaves than the Tree
-    kernel's candidate list (72 of 96 supers, about 5000 leaves): that
-    sequence goes through the streaming pair restricted to its candidates,
-    batched with a sequence the Tree kernel serves; a zero query (every score
-    tied) then falls through to the exact kernel."""
+@pytest.mark.parametrize("levels", [2, 3])
+def test_tree_decode_candidate_overflow(levels):
+    """Tree decode where the chosen supers hold many leaves (two levels: 72
+    of 96 supers, about 5000 leaves, beyond the Tree kernel's candidate list;
+    three levels: the best 40 of the 12 supers under the 4 best of 16 top nodes
+    and the 32 supers under no top node, about 2400 leaves): that sequence
+    goes through the streaming pair restricted to its candidates, batched with
+    a sequence the Tree kernel serves; a zero query (every score tied) then
+    falls through to the exact kernel."""
     dev = _dev()
     L = _L()
+    t2 = dict(tree2_group=4, tree2_super=16, tree2_iters=3, tree2_top=4) if levels == 3 else {}
     wl = S.Workload("dec_tree_ovf", 71, T=0, ncomp=64, block=64, buckets=16, iters=3, tree_group=64,
-                    tree_super=16, tree_iters=3, tree_top=72, chunk=0, budget=1500, window=32,
-                    sinks=4, Hq=8, Hkv=2, D=64)
+                    tree_super=16, tree_iters=3, tree_top=72 if levels == 2 else 40, chunk=0,
+                    budget=1500, window=32, sinks=4, Hq=8, Hkv=2, D=64, **t2)
     kpg = wl.pool * wl.block * wl.tree_group           # keys per group
     Ts = [6 * kpg + 300, kpg + 500]
     steps = 3
     cap = max(Ts) + steps
     gens = [S.Synth(wl, seq=i, data_cfg=71) for i in range(len(Ts))]
-    ip = L.IndexParams(64, wl.pool, wl.block, wl.buckets, wl.iters, wl.tree_group, wl.tree_super,
-                       wl.tree_iters, cap)
+    ip = _iparams(wl, cap)
     op = _oparams(wl)
     K = torch.empty((len(Ts), cap, wl.Hkv, wl.D), dtype=torch.bfloat16)
     V = torch.empty_like(K)
@@ -948,8 +951,8 @@ def test_tree_decode_candidate_overflow():
         g.fill_rows("k", K[i], 0)
         g.fill_rows("v", V[i], 0)
     Kd, Vd = K.to(dev), V.to(dev)
-    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
-    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, 0, 0, wl.tree2_top)
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, tree2_top=wl.tree2_top)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
     ws = torch.empty(L.workspace_bytes(L.binding.OP_DECODE, ip, sp, ap, len(Ts)), dtype=torch.uint8,
                      device=dev)
