@@ -6,6 +6,8 @@ match the float64 oracle within 2e-3 normwise relative error
 kernel's float32 output, and the bf16 output must be the round-to-nearest-
 even of that float32 output.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -423,11 +425,14 @@ def test_dense_select_matches_oracle():
     check_selection(idx, cnt, refs, sp.max_sel)
 
 
-def test_tree_index_and_selection():
+@pytest.mark.parametrize("tree_iters", [3, 1])
+def test_tree_index_and_selection(tree_iters):
+    """Two-level Tree index and selections; the super level runs its own
+    iteration count (equal to, then different from, the leaf level's)."""
     dev = _dev()
     L = _L()
     wl = S.Workload("tree_small", 70, T=4 * 256 * 12 + 300, ncomp=128, block=256, buckets=32,
-                    iters=3, tree_group=4, tree_super=16, tree_iters=3, tree_top=5, chunk=0,
+                    iters=3, tree_group=4, tree_super=16, tree_iters=tree_iters, tree_top=5, chunk=0,
                     budget=500, window=64, sinks=4, Hq=4, Hkv=1, D=64)
     g = S.Synth(wl, data_cfg=70)
     latk = g.latk(0, wl.T)
@@ -485,15 +490,17 @@ TREE3 = S.Workload("tree3_small", 71, T=4 * 64 * 2 * 10 + 300, ncomp=96, block=6
                    iters=3, tree_group=2, tree_super=16, tree_iters=3, tree_top=6, tree2_group=4,
                    tree2_super=16, tree2_iters=3, tree2_top=3, chunk=0, budget=300, window=64,
                    sinks=4, Hq=4, Hkv=1, D=64)
+# the same shape with a different Lloyd iteration count on every level
+TREE3_ITERS = dataclasses.replace(TREE3, name="tree3_iters", iters=3, tree_iters=1, tree2_iters=2)
 
 
-def test_tree3_index_and_selection():
+@pytest.mark.parametrize("wl", [TREE3, TREE3_ITERS], ids=lambda w: w.name)
+def test_tree3_index_and_selection(wl):
     """Three-level Tree: 10 groups of 2 blocks, top groups of 4 groups (2
     complete, 2 groups and a partial block outside them).  Index bit-exact,
     selections of the fast Tree kernel and of the exact kernel bit-exact."""
     dev = _dev()
     L = _L()
-    wl = TREE3
     g = S.Synth(wl, data_cfg=71)
     latk = g.latk(0, wl.T)
     ref = O.build_index(latk.numpy(), wl.T, _oparams(wl))
@@ -517,12 +524,12 @@ def test_tree3_index_and_selection():
         ix.select(lq.to(dev), qd, L.SelectParams(wl.budget, wl.window, wl.sinks, 6))
 
 
-def test_tree3_append_equals_build_and_decode():
+@pytest.mark.parametrize("wl", [TREE3, TREE3_ITERS], ids=lambda w: w.name)
+def test_tree3_append_equals_build_and_decode(wl):
     """Appending key by key across a top-group completion gives the built
     index; decode steps on two sequences select the oracle's keys."""
     dev = _dev()
     L = _L()
-    wl = TREE3
     kpt = wl.pool * wl.block * wl.tree_group * wl.tree2_group     # keys per top group
     Ts = [kpt - 2, 2 * kpt + 77]
     steps = 5
@@ -824,7 +831,7 @@ def test_tree_decode_steps_match_oracle():
     dev = _dev()
     L = _L()
     wl = S.Workload("dec_tree", 61, T=0, ncomp=64, block=64, buckets=16, iters=3, tree_group=4,
-                    tree_super=16, tree_iters=3, tree_top=5, chunk=0, budget=200, window=32,
+                    tree_super=16, tree_iters=2, tree_top=5, chunk=0, budget=200, window=32,
                     sinks=4, Hq=8, Hkv=2, D=64)
     kpg = wl.pool * wl.block * wl.tree_group           # keys per group
     Ts = [kpg - 3, 2 * kpg + 500, 3 * kpg - 130]
@@ -928,9 +935,9 @@ def test_tree_decode_candidate_overflow(levels):
     falls through to the exact kernel."""
     dev = _dev()
     L = _L()
-    t2 = dict(tree2_group=4, tree2_super=16, tree2_iters=3, tree2_top=4) if levels == 3 else {}
+    t2 = dict(tree2_group=4, tree2_super=16, tree2_iters=1, tree2_top=4) if levels == 3 else {}
     wl = S.Workload("dec_tree_ovf", 71, T=0, ncomp=64, block=64, buckets=16, iters=3, tree_group=64,
-                    tree_super=16, tree_iters=3, tree_top=72 if levels == 2 else 40, chunk=0,
+                    tree_super=16, tree_iters=2, tree_top=72 if levels == 2 else 40, chunk=0,
                     budget=1500, window=32, sinks=4, Hq=8, Hkv=2, D=64, **t2)
     kpg = wl.pool * wl.block * wl.tree_group           # keys per group
     Ts = [6 * kpg + 300, kpg + 500]

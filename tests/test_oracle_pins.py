@@ -323,6 +323,59 @@ def test_tree3_candidates_against_brute_force():
         assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
 
 
+def _brute_lloyd(X, C, iters):
+    """Plain-Python Lloyd k-means: centroid c starts at vector c * (N // C);
+    each iteration assigns by brute force (lowest index on ties), then sets
+    every non-empty centroid to the exact rational mean of its members,
+    rounded half to even; an empty centroid is kept."""
+    rows = [[int(v) for v in r] for r in np.asarray(X).tolist()]
+    stride = len(rows) // C
+    mu = [rows[c * stride][:] for c in range(C)]
+    a = []
+    for _ in range(iters):
+        a = _brute_assign(np.array(rows), np.array(mu)).tolist()
+        for c in range(C):
+            mine = [r for r, ac in zip(rows, a) if ac == c]
+            if mine:
+                mu[c] = _frac_mean(mine)
+    return mu, a
+
+
+def test_tree_levels_use_their_own_iteration_counts():
+    """Leaf, super and top levels run 3, 1 and 2 Lloyd iterations: each upper
+    level equals a plain-Python Lloyd over the level below with its own count
+    (super members are leaf ids, top members super ids), and the other counts
+    give a different result on this input, so swapping them cannot pass."""
+    # 29 blocks of 16 pooled vectors (8 buckets each), groups of 4 blocks
+    # (6 supers), top groups of 3 groups (4 top nodes): 7 groups, 2 top groups
+    T = 4 * 16 * 29 + 37
+    latk = np.random.default_rng(32).integers(-40, 41, size=(T, 6))
+    prm = O.IndexParams(4, 16, 8, 3, 4, 6, 1, 3, 4, 2)
+    idx = O.build_index(latk, T, prm)
+    assert idx.n_full == 29 and idx.n_grp == 7 and idx.n_grp2 == 2
+    # leaf level: every block with its own count (3)
+    for b in range(idx.n_full):
+        mu, a = _brute_lloyd(idx.pooled[b * 16:(b + 1) * 16], 8, 3)
+        assert idx.centroids[b * 8:(b + 1) * 8].tolist() == mu
+    levels = (
+        ("super", idx.centroids, 4 * 8, 6, idx.n_grp, 1, idx.sup_centroids, idx.sup_members),
+        ("top", idx.sup_centroids, 3 * 6, 4, idx.n_grp2, 2, idx.top_centroids, idx.top_members),
+    )
+    for name, below, per_grp, S, n_grp, own, cent, members in levels:
+        differs = {k: False for k in (1, 2, 3) if k != own}
+        for g in range(n_grp):
+            X = below[g * per_grp:(g + 1) * per_grp]
+            mu, a = _brute_lloyd(X, S, own)
+            assert cent[g * S:(g + 1) * S].tolist() == mu, (name, g)
+            for c in range(S):
+                want = [g * per_grp + i for i, ac in enumerate(a) if ac == c]
+                assert members[g * S + c].tolist() == want, (name, g, c)
+            for k in differs:
+                mk, ak = _brute_lloyd(X, S, k)
+                differs[k] |= (mk != mu) or (ak != a)
+        assert all(differs.values()), (name, differs)
+
+
 def test_index_is_prefix_function():
     """The index over keys [0, T') depends only on those keys (cache-consistent)."""
     latk = np.random.default_rng(15).integers(-40, 41, size=(3000, 4))
