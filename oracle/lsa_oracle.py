@@ -35,6 +35,9 @@ key in ascending position up to the budget, the last bucket cut at its
 lowest positions; window = the w most recent keys including the query's own
 position; causal masking per key; one latent query per token shared by all
 its heads; softmax scale 1/sqrt(D); head h reads KV head floor(h*Hkv/Hq).
+The Tree walk takes its quota of best nodes per level and keeps taking the
+next best while the candidates hold fewer eligible keys than the budget, so
+a Tree query fills the same fixed number of keys as a Flat one.
 
 All index arithmetic is exact integer arithmetic (NumPy int64).  Integer dot
 products go through float64 matrix products, which are exact here because
@@ -283,29 +286,67 @@ def scores(cent: np.ndarray, q: np.ndarray) -> np.ndarray:
     return (cent.astype(np.float64) @ np.asarray(q, dtype=np.float64)).astype(np.int64)
 
 
-def candidates(idx: Index, q: np.ndarray, sp: SelectParams) -> np.ndarray:
-    """Bucket ids a query may draw from: all (Flat) or the Tree walk's leaves.
+def eligible_count(idx: Index, beta: int, t: int, sp: SelectParams) -> int:
+    """Number of long-range keys of bucket beta usable at position t."""
+    return int(eligible_keys(bucket_keys(idx, beta), t, sp).size)
 
-    Tree: the ``tree_top`` best super clusters by (score desc, id asc), the
-    union of their leaf members, plus every leaf not covered by a super
-    cluster (blocks outside complete groups and the tail).  With a third
-    level the super clusters ranked are only those under the ``tree2_top``
-    best top nodes, plus every super cluster not under a top node.
+
+def _walk(order: np.ndarray, quota: int, held: int, need: int, weight) -> List[int]:
+    """Nodes taken from ``order`` (best first): the first ``quota`` of them,
+    then the next ones while the eligible keys held (``held`` to start with,
+    plus ``weight(node)`` for every node taken) stay below ``need``."""
+    taken: List[int] = []
+    for n in order.tolist():
+        if len(taken) >= quota and held >= need:
+            break
+        taken.append(n)
+        held += weight(n)
+    return taken
+
+
+def candidates(idx: Index, q: np.ndarray, sp: SelectParams, t: int) -> np.ndarray:
+    """Bucket ids the query at position t may draw from: all (Flat) or the
+    leaves the Tree walk reaches.
+
+    Tree: super clusters are ranked by (score desc, id asc).  The walk takes
+    the ``tree_top`` best, then keeps taking the next best while the
+    candidate leaves (the members of the supers taken, plus every leaf not
+    covered by a super cluster: blocks outside complete groups and the tail)
+    hold fewer eligible long-range keys for t than the query's budget
+    ``sp.budget_at(t)``, so the budget is filled whenever the context holds
+    enough keys (the budget is a fixed number of keys per query: mauroscia.it,
+    D-LSA paragraph; sysnote.net, "What it changes").  With a third level the
+    same walk runs over the top nodes first (``tree2_top`` of them, more
+    while the supers under the nodes taken, plus the supers under no top
+    node and the uncovered leaves, hold fewer eligible keys than the budget),
+    and the super clusters ranked are only those under the top nodes taken
+    plus every super cluster not under a top node.
     """
     if idx.params.tree_group <= 0:
         return np.arange(idx.n_bkt, dtype=np.int64)
+    need = sp.budget_at(t)
+
+    def sup_weight(s: int) -> int:
+        return sum(eligible_count(idx, int(b), t, sp) for b in idx.sup_members[s])
+
+    loose = np.arange(idx.covered_leaves(), idx.n_bkt, dtype=np.int64)
+    held = sum(eligible_count(idx, int(b), t, sp) for b in loose)
     sup_ids = np.arange(idx.sup_centroids.shape[0], dtype=np.int64)
     if idx.params.tree2_group > 0:
+        loose_sup = np.arange(idx.covered_supers(), len(sup_ids), dtype=np.int64)
+        held_top = held + sum(sup_weight(int(s)) for s in loose_sup)
         ts = scores(idx.top_centroids, q)
-        top2 = np.lexsort((np.arange(len(ts)), -ts))[: sp.tree2_top]
-        sparts = [idx.top_members[n] for n in top2]
-        sparts.append(np.arange(idx.covered_supers(), len(sup_ids), dtype=np.int64))
+        top_order = np.lexsort((np.arange(len(ts)), -ts))
+        tops = _walk(top_order, sp.tree2_top, held_top, need,
+                     lambda n: sum(sup_weight(int(s)) for s in idx.top_members[n]))
+        sparts = [idx.top_members[n] for n in tops]
+        sparts.append(loose_sup)
         sup_ids = np.sort(np.concatenate(sparts))
     ss = scores(idx.sup_centroids[sup_ids], q)
     order = sup_ids[np.lexsort((sup_ids, -ss))]
-    top = order[: sp.tree_top]
-    parts = [idx.sup_members[s] for s in top]
-    parts.append(np.arange(idx.covered_leaves(), idx.n_bkt, dtype=np.int64))
+    taken = _walk(order, sp.tree_top, held, need, sup_weight)
+    parts = [idx.sup_members[s] for s in taken]
+    parts.append(loose)
     return np.sort(np.concatenate(parts)) if parts else np.zeros(0, np.int64)
 
 
@@ -318,7 +359,7 @@ def select(idx: Index, q: np.ndarray, t: int, sp: SelectParams) -> np.ndarray:
     at its lowest positions).  The window [t-w+1, t] and the sinks [0, sinks) are added;
     every key is <= t.
     """
-    cand = candidates(idx, q, sp)
+    cand = candidates(idx, q, sp, t)
     s = scores(idx.centroids[cand], q)
     order = cand[np.lexsort((cand, -s))]
     picked: List[np.ndarray] = []

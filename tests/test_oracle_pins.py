@@ -139,7 +139,7 @@ def _brute_select(idx, latk, q, t, sp):
     key asc), keep the first `budget` eligible keys; add window and sinks."""
     p = idx.params.pool
     pairs = []
-    cands = O.candidates(idx, q, sp)
+    cands = O.candidates(idx, q, sp, t)
     for beta in cands.tolist():
         s = sum(int(a) * int(b) for a, b in zip(q, idx.centroids[beta]))
         for g in idx.members[beta].tolist():
@@ -237,28 +237,112 @@ def test_tree_with_full_branching_equals_flat():
         assert np.array_equal(O.select(flat, q, t, sp_f), O.select(tree, q, t, sp_t))
 
 
-def test_tree_candidates_against_brute_force():
-    T = 4 * 16 * 6 + 50
+def _brute_tree_walk(tree, q, t, sp):
+    """Plain-Python Tree walk: nodes ranked by (score desc, id asc) with
+    scores summed term by term; a level takes its quota of nodes, then more
+    while the keys under the nodes taken (plus every key under no node of
+    that level) that satisfy sinks <= j <= t - window, counted one key id at
+    a time, stay below the budget.  Returns (candidate leaves, supers taken,
+    top nodes taken)."""
+    p = tree.params.pool
+    B = sp.budget_at(t)
+
+    def dot(a, b):
+        return sum(int(x) * int(y) for x, y in zip(a, b))
+
+    def n_elig(leaves):
+        return sum(1 for lf in leaves for g in tree.members[lf].tolist() for r in range(p)
+                   if sp.sinks <= g * p + r <= t - sp.window)
+
+    def leaves_of(sups):
+        return [lf for s in sups for lf in tree.sup_members[s].tolist()]
+
+    loose = list(range(tree.covered_leaves(), tree.n_bkt))
+    sups = list(range(len(tree.sup_centroids)))
+    tops = []
+    if tree.params.tree2_group > 0:
+        loose_sup = list(range(tree.covered_supers(), len(tree.sup_centroids)))
+        held = n_elig(loose) + n_elig(leaves_of(loose_sup))
+        for n in sorted(range(len(tree.top_centroids)), key=lambda n: (-dot(q, tree.top_centroids[n]), n)):
+            if len(tops) >= sp.tree2_top and held >= B:
+                break
+            tops.append(n)
+            held += n_elig(leaves_of(tree.top_members[n].tolist()))
+        sups = sorted({s for n in tops for s in tree.top_members[n].tolist()} | set(loose_sup))
+    held = n_elig(loose)
+    taken = []
+    for s in sorted(sups, key=lambda s: (-dot(q, tree.sup_centroids[s]), s)):
+        if len(taken) >= sp.tree_top and held >= B:
+            break
+        taken.append(s)
+        held += n_elig(tree.sup_members[s].tolist())
+    return sorted(set(loose) | set(leaves_of(taken))), taken, tops
+
+
+@pytest.mark.parametrize("nblk", [6, 7])
+def test_tree_candidates_against_brute_force(nblk):
+    """The walk against plain-Python enumeration, with budgets the best
+    tree_top supers already hold (no fill) and budgets they do not (the walk
+    continues in score order); both cases occur.  With 7 blocks the last one
+    is outside the complete groups: its leaves are candidates whose keys
+    count towards the budget from the start."""
+    T = 4 * 16 * nblk + 50
     latk = np.random.default_rng(13).integers(-30, 31, size=(T, 6))
     tree = O.build_index(latk, T, O.IndexParams(4, 16, 4, 2, 2, 3, 2))
     # every leaf of a complete group is in exactly one super cluster
     cov = np.sort(np.concatenate(tree.sup_members))
     assert cov.tolist() == list(range(tree.covered_leaves()))
     rng = np.random.default_rng(14)
+    filled = quota = 0
     for R in (1, 2, 4):
-        q = rng.integers(-30, 31, size=6)
-        ss = [(-sum(int(a) * int(b) for a, b in zip(q, m)), i)
-              for i, m in enumerate(tree.sup_centroids)]
-        top = [i for _, i in sorted(ss)[:R]]
-        want = set()
-        for s in top:
-            want |= set(tree.sup_members[s].tolist())
-        want |= set(range(tree.covered_leaves(), tree.n_bkt))
-        got = O.candidates(tree, q, O.SelectParams(tree_top=R))
-        assert got.tolist() == sorted(want)
-        t = T - 1
-        sp = O.SelectParams(budget=30, window=8, sinks=2, tree_top=R)
-        assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
+        for B in (8, 60, 200, 2000):
+            q = rng.integers(-30, 31, size=6)
+            t = T - 1 - int(rng.integers(0, 200))
+            sp = O.SelectParams(budget=B, window=8, sinks=2, tree_top=R)
+            want, taken, _ = _brute_tree_walk(tree, q, t, sp)
+            assert O.candidates(tree, q, sp, t).tolist() == want
+            # the same query with the budget equal to what the loose leaves and
+            # the best R + 1 supers hold: the walk stops right there
+            order = sorted(range(len(tree.sup_centroids)),
+                           key=lambda s: (-int(np.dot(q, tree.sup_centroids[s])), s))
+            leaves = list(range(tree.covered_leaves(), tree.n_bkt)) + \
+                [lf for s in order[:R + 1] for lf in tree.sup_members[s].tolist()]
+            exact = sum(len(O.eligible_keys(O.bucket_keys(tree, lf), t, sp)) for lf in leaves)
+            spx = O.SelectParams(budget=exact, window=8, sinks=2, tree_top=R)
+            want_x, taken_x, _ = _brute_tree_walk(tree, q, t, spx)
+            assert taken_x == order[:R + 1]
+            assert O.candidates(tree, q, spx, t).tolist() == want_x
+            assert O.candidates(tree, q, sp, t).tolist() == want
+            filled += len(taken) > R
+            quota += len(taken) == R
+            assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
+    assert filled and quota
+
+
+def test_tree_fill_count_and_minimal_walk():
+    """With the fill, a Tree selection holds exactly min(t + 1, B + w + s)
+    keys, as Flat does; the supers taken are a prefix of the score order,
+    and when the walk took more than tree_top of them, the last one was
+    needed to reach the budget."""
+    T = 4 * 16 * 6 + 50
+    latk = np.random.default_rng(15).integers(-30, 31, size=(T, 6))
+    tree = O.build_index(latk, T, O.IndexParams(4, 16, 4, 2, 2, 3, 2))
+    rng = np.random.default_rng(16)
+    p = tree.params.pool
+    for t in [0, 5, 9, 10, 40, 100, 250, 384, 385, T - 1] + rng.integers(0, T, 8).tolist():
+        for R, B in ((1, 30), (2, 120), (1, 400)):
+            q = rng.integers(-30, 31, size=6)
+            sp = O.SelectParams(budget=B, window=8, sinks=2, tree_top=R)
+            sel = O.select(tree, q, t, sp)
+            assert len(sel) == min(t + 1, B + 8 + 2), (t, R, B)
+            _, taken, _ = _brute_tree_walk(tree, q, t, sp)
+            order = sorted(range(9), key=lambda s: (-int(np.dot(q, tree.sup_centroids[s])), s))
+            assert taken == order[:len(taken)]
+            if len(taken) > R:
+                leaves = list(range(tree.covered_leaves(), tree.n_bkt)) + \
+                    [lf for s in taken[:-1] for lf in tree.sup_members[s].tolist()]
+                short = sum(len(O.eligible_keys(O.bucket_keys(tree, lf), t, sp)) for lf in leaves)
+                assert short < B
 
 
 def _tree3(seed):
@@ -301,26 +385,18 @@ def test_tree3_full_top_branching_equals_two_levels():
 def test_tree3_candidates_against_brute_force():
     T, latk, tree = _tree3(24)
     rng = np.random.default_rng(25)
-
-    def dot(a, b):
-        return sum(int(x) * int(y) for x, y in zip(a, b))
-
+    filled_top = 0
     for R2, R in ((1, 1), (1, 3), (2, 2), (3, 5)):
-        q = rng.integers(-30, 31, size=6)
-        tops = sorted((-dot(q, m), i) for i, m in enumerate(tree.top_centroids))[:R2]
-        sups = set()
-        for _, n in tops:
-            sups |= set(tree.top_members[n].tolist())
-        sups |= set(range(tree.covered_supers(), len(tree.sup_centroids)))
-        best = sorted((-dot(q, tree.sup_centroids[s]), s) for s in sups)[:R]
-        want = set()
-        for _, s in best:
-            want |= set(tree.sup_members[s].tolist())
-        want |= set(range(tree.covered_leaves(), tree.n_bkt))
-        sp = O.SelectParams(budget=30, window=8, sinks=2, tree_top=R, tree2_top=R2)
-        assert O.candidates(tree, q, sp).tolist() == sorted(want)
-        t = T - 1 - int(rng.integers(0, 100))
-        assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
+        for B in (10, 150, 1200):
+            q = rng.integers(-30, 31, size=6)
+            t = T - 1 - int(rng.integers(0, 100))
+            sp = O.SelectParams(budget=B, window=8, sinks=2, tree_top=R, tree2_top=R2)
+            want, _, tops = _brute_tree_walk(tree, q, t, sp)
+            filled_top += len(tops) > R2
+            assert O.candidates(tree, q, sp, t).tolist() == want
+            assert O.select(tree, q, t, sp).tolist() == _brute_select(tree, latk, q, t, sp)
+            assert len(O.select(tree, q, t, sp)) == min(t + 1, B + 8 + 2)
+    assert filled_top
 
 
 def _brute_lloyd(X, C, iters):
