@@ -127,6 +127,8 @@ void layout(const lsa_index_params& p, Index* h) {
   h->off_toff = o;   o = align_up(o + h->max_top * 4);
   h->off_tmem = o;   o = align_up(o + h->max_grp2 * p.tree2_group * p.tree_super * 4);
   h->off_suptop = o; o = align_up(o + (p.tree2_group > 0 ? h->max_sup * 4 : 0));
+  h->off_sblk = o;   o = align_up(o + h->max_sup * (p.tree_group + 1) * 4);
+  h->off_skey = o;   o = align_up(o + h->max_sup * (p.tree_group + 1) * 4);
   {
     size_t km = kmeans_scratch_bytes(p.block, p.buckets);
     if (p.tree_group > 0) {
@@ -199,6 +201,13 @@ IdxView view_of(const Index* h) {
     v.soff = h->at<int32_t>(h->off_soff);
     v.smem = h->at<int32_t>(h->off_smem);
     v.covered = (int32_t)(h->n_grp * h->prm.tree_group * h->prm.buckets);
+    v.sblk = h->at<int32_t>(h->off_sblk);
+    v.skey = h->at<int32_t>(h->off_skey);
+    v.tgroup = h->prm.tree_group;
+    v.tsuper = h->prm.tree_super;
+    v.bpb = h->prm.buckets;
+    v.tgroup2 = h->prm.tree2_group;
+    v.blk_keys = (int64_t)h->prm.block * h->prm.pool;
     if (h->prm.tree2_group > 0 && h->n_grp2 > 0) {
       v.n_top = (int32_t)(h->n_grp2 * h->prm.tree2_super);
       v.covered_sup = (int32_t)(h->n_grp2 * h->prm.tree2_group * h->prm.tree_super);
@@ -284,6 +293,11 @@ int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
                             h->at<int32_t>(h->off_leafsup), (int32_t)(g * S),
                             h->at<char>(h->off_kmws), (size_t)h->kmws_bytes, s),
               "tree kmeans");
+      LSA_HIP(launch_sup_tables(h->at<int32_t>(h->off_soff), h->at<int32_t>(h->off_scnt),
+                                h->at<int32_t>(h->off_smem), bcnt, (int32_t)(g * S),
+                                (int32_t)((ng_new - g) * S), S, G, C, p, h->at<int32_t>(h->off_sblk),
+                                h->at<int32_t>(h->off_skey), s),
+              "tree walk tables");
     }
   }
   int64_t ng2_new = h->n_grp2;
@@ -682,6 +696,17 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int p = h0->prm.pool, N = h0->prm.block;
 
+  // Every descriptor as it was: if any launch below fails, all of them are
+  // put back, so no sequence counts a key the device did not get.  (Arrays
+  // past the restored counters may hold partial writes; the next append
+  // rewrites them, and no kernel reads past the counters.)
+  Index saved[16];
+  for (int i = 0; i < nseq; ++i) saved[i] = *as_index(hs[i]);
+  auto restore_all = [&](int rc) {
+    for (int i = 0; i < nseq; ++i) *as_index(hs[i]) = saved[i];
+    return rc;
+  };
+
   // 1. append one key per sequence: one batched launch; a sequence whose key
   //    completes a block (a k-means is due) takes the general path
   DecodeAppendArgs da;
@@ -698,12 +723,13 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
     const int np = (int)(h->T - h->n_pool * p);
     const bool completes_group = np + 1 == p;
     const bool completes_block = completes_group && (h->n_pool + 1) % N == 0;
-    if (h->T == 0 && h->prm.tree_group > 0)
-      LSA_HIP(reset_tree_maps(h, s), "fill");
+    if (h->T == 0 && h->prm.tree_group > 0) {
+      hipError_t e = reset_tree_maps(h, s);
+      if (e != hipSuccess) return restore_all(hip_fail(e, "fill"));
+    }
     if (completes_block) {
-      Index saved = *h;
       int rc = append_impl(h, d_latk_new + (int64_t)i * kDim, 1, s);
-      if (rc != LSA_OK) { *h = saved; return rc; }
+      if (rc != LSA_OK) return restore_all(rc);
       continue;
     }
     da.arena[i] = h->arena;
@@ -725,12 +751,8 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   IdxView views[16];
   for (int i = 0; i < nseq; ++i) {
     views[i] = view_of(as_index(hs[i]));
-    if (views[i].leafsup && views[i].n_sup > 2048) {
-      // unreachable: rejected above before anything was enqueued; should it
-      // happen, the appended keys still go in, as the counters say
-      if (any_batched) LSA_HIP(launch_decode_append(da, d_latk_new, nseq, s), "decode append");
-      return fail(LSA_E_UNSUPPORTED, "%d super clusters (at most 2048)", views[i].n_sup);
-    }
+    if (views[i].leafsup && views[i].n_sup > 2048)   // unreachable: rejected above
+      return restore_all(fail(LSA_E_UNSUPPORTED, "%d super clusters (at most 2048)", views[i].n_sup));
   }
   SelArgs a;
   memset(&a, 0, sizeof a);
@@ -738,14 +760,14 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   a.budget = sp->budget; a.window = sp->window; a.sinks = sp->sinks; a.tree_top = sp->tree_top;
   a.early_budget = sp->early_budget; a.early_until = sp->early_until; a.tree2_top = sp->tree2_top;
   a.max_sel = max_sel; a.idx = idx; a.cnt = cnt; a.only = nullptr;
-  LSA_HIP(launch_select_dec(views, qpos, nseq, h0->max_bkt, a, selws, s, any_batched ? &da : nullptr,
-                            d_latk_new),
-          "decode append + select");
+  hipError_t e = launch_select_dec(views, qpos, nseq, h0->max_bkt, a, selws, s,
+                                  any_batched ? &da : nullptr, d_latk_new);
+  if (e != hipSuccess) return restore_all(hip_fail(e, "decode append + select"));
 
   // 3. split-K attention over each sequence's own rows, then the merge
-  LSA_HIP(launch_attn(d_q, d_k, d_v, seq_stride_rows, seq_stride_rows, 1, idx, cnt, max_sel,
-                      nseq, *ap, d_out, att, kDecodeSplits, s),
-          "decode attention");
+  e = launch_attn(d_q, d_k, d_v, seq_stride_rows, seq_stride_rows, 1, idx, cnt, max_sel, nseq, *ap,
+                  d_out, att, kDecodeSplits, s);
+  if (e != hipSuccess) return restore_all(hip_fail(e, "decode attention"));
   return LSA_OK;
 }
 

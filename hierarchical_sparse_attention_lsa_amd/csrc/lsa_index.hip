@@ -441,6 +441,64 @@ __global__ void __launch_bounds__(64) k_decode_append(DecodeAppendArgs a, const 
   }
 }
 
+// ---------------------------------------------------------------- Tree walk tables
+// For super s (group g = s / S, leaves of blocks g*G .. g*G + G - 1, leaf id
+// b*C + c for block b): sblk[s][k] = first slot of s's ascending member list
+// whose leaf lies in block g*G + k or later (sblk[s][G] = member count), and
+// skey[s][k] = keys of s's leaves in the group's blocks before k.  One wave
+// per super, lanes over k.
+__global__ void __launch_bounds__(64) k_sup_tables(const int32_t* __restrict__ soff,
+                                                   const int32_t* __restrict__ scnt,
+                                                   const int32_t* __restrict__ smem,
+                                                   const int32_t* __restrict__ bcnt, int s0, int S,
+                                                   int G, int C, int p, int32_t* __restrict__ sblk,
+                                                   int32_t* __restrict__ skey) {
+  const int s = s0 + blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t* mem = smem + soff[s];
+  const int n = scnt[s];
+  const int leaf0 = (s / S) * G * C;
+  int32_t* sb = sblk + (int64_t)s * (G + 1);
+  int32_t* sk = skey + (int64_t)s * (G + 1);
+  auto first_slot = [&](int k) {       // first member with leaf id >= leaf0 + k*C
+    int lo = 0, hi = n;
+    const int x = leaf0 + k * C;
+    while (lo < hi) {
+      const int m = (lo + hi) >> 1;
+      if (mem[m] < x) lo = m + 1; else hi = m;
+    }
+    return lo;
+  };
+  int carry = 0;
+  for (int k0 = 0; k0 <= G; k0 += 64) {
+    const int k = k0 + lane;
+    int a = 0, keys = 0;
+    if (k <= G) {
+      a = first_slot(k);
+      if (k < G) {
+        const int z = first_slot(k + 1);
+        for (int j = a; j < z; ++j) keys += bcnt[mem[j]] * p;
+      }
+    }
+    int tot;
+    const int ex = wave_excl_scan(keys, &tot);
+    if (k <= G) {
+      sb[k] = a;
+      sk[k] = carry + ex;
+    }
+    carry += tot;
+  }
+}
+
+hipError_t launch_sup_tables(const int32_t* soff, const int32_t* scnt, const int32_t* smem,
+                             const int32_t* bcnt, int32_t s0, int32_t nsup, int32_t S, int32_t G,
+                             int32_t C, int32_t p, int32_t* sblk, int32_t* skey, hipStream_t s) {
+  if (nsup <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sup_tables, dim3((unsigned)nsup), dim3(64), 0, s, soff, scnt, smem, bcnt, s0,
+                     S, G, C, p, sblk, skey);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_append(const DecodeAppendArgs& a, const int8_t* src, int nseq,
                                 hipStream_t s) {
   hipLaunchKernelGGL(k_decode_append, dim3(nseq), dim3(64), 0, s, a, src);

@@ -32,6 +32,7 @@ struct Index {
   int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast;
   int64_t off_scent, off_scnt, off_soff, off_smem, off_leafsup, off_pend;
   int64_t off_tcent, off_tcnt, off_toff, off_tmem, off_suptop;
+  int64_t off_sblk, off_skey;     // per super, per block of its group (Tree walk fill)
   int64_t off_kmws, kmws_bytes;   // k-means scratch (few-block clustering)
   int64_t used_bytes;
 
@@ -68,6 +69,17 @@ struct IdxView {
   const int32_t* tmem;    // super ids grouped by top node
   const int32_t* suptop;  // super -> top node id, or -1
   int32_t n_pool;         // pooled vectors (keys [0, n_pool * pool) are in buckets)
+  // Tree walk fill: per super s, G + 1 entries each (G = tgroup): sblk[s][k] is
+  // the first slot of s's member list (relative to soff[s]) whose leaf lies in
+  // block k of s's group or later, skey[s][k] the keys of s's leaves in blocks
+  // before k of the group
+  const int32_t* sblk;
+  const int32_t* skey;
+  int32_t tgroup;         // blocks per group (G)
+  int32_t tsuper;         // supers per group (S)
+  int32_t bpb;            // buckets per full block (C)
+  int32_t tgroup2;        // groups per top group (third level)
+  int64_t blk_keys;       // keys per block (block * pool)
 };
 
 struct SelArgs {
@@ -125,6 +137,10 @@ hipError_t launch_kmeans(const int8_t* X, int32_t N, int32_t C, int32_t iters, i
                          int32_t* mem_out, int32_t* first_out, int32_t* last_out,
                          int32_t* map_out, int32_t map_base, void* scratch,
                          size_t scratch_bytes, hipStream_t s);
+// Per-super tables of the Tree walk for supers [s0, s0 + nsup) (see IdxView).
+hipError_t launch_sup_tables(const int32_t* soff, const int32_t* scnt, const int32_t* smem,
+                             const int32_t* bcnt, int32_t s0, int32_t nsup, int32_t S, int32_t G,
+                             int32_t C, int32_t p, int32_t* sblk, int32_t* skey, hipStream_t s);
 hipError_t launch_tail(const int8_t* pooled, int64_t g0, int64_t g1, int64_t n_full, int32_t N,
                        int32_t C, int8_t* cent, int32_t* bcnt, int32_t* boff, int32_t* bmem,
                        int32_t* bfirst, int32_t* blast, hipStream_t s);

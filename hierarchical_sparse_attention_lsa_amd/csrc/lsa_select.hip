@@ -161,6 +161,8 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
     for (int qi = wave; qi < nqt; qi += SW) {
       long long* kk = S.u.supkeys[wave];
       const int8_t* qv = A.latq + (int64_t)(q0 + qi) * kDim;
+      const int tq = max(0, S.t[qi]);
+      const int need = budget_at(A, tq);
       if (V.n_top > 0) {
         for (int s = lane; s < ntp; s += 64) {
           long long key = LLONG_MAX;
@@ -177,10 +179,24 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         wave_bitonic(kk, ntp);
+        // the walk: the tree2_top best, then the next while the keys under the
+        // nodes taken, the supers under no top node and the uncovered leaves
+        // hold fewer eligible keys than the budget
         const int R2 = min(A.tree2_top, V.n_top);
-        for (int i = lane; i < R2; i += 64) {
-          const int s = (int)(0xffffffffu - (unsigned)((-kk[i]) & 0xffffffffll));
-          atomicOr(&S.supmask[qi][s >> 5], 1u << (s & 31));
+        long long held = loose_leaf_eligible(V, tq, A.window, A.sinks) +
+                         loose_sup_eligible(V, tq, A.window, A.sinks);
+        for (int base = 0; base < V.n_top; base += 64) {
+          const int i = base + lane;
+          int w = 0, n = -1;
+          if (i < V.n_top) {
+            n = (int)(0xffffffffu - (unsigned)((-kk[i]) & 0xffffffffll));
+            w = top_eligible(V, n, tq, A.window, A.sinks);
+          }
+          const long long inc = wave_incl_scan((long long)w, 0ll, [](long long a, long long b) { return a + b; });
+          if (n >= 0 && (i < R2 || held + inc - w < need))
+            atomicOr(&S.supmask[qi][n >> 5], 1u << (n & 31));
+          held += lane63(inc);
+          if (base + 64 >= R2 && held >= need) break;
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -210,12 +226,22 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       }
       wave_bitonic(kk, nsp);
+      // the walk: the tree_top best live supers (they sort first), then the
+      // next while the candidates hold fewer eligible keys than the budget
       const int R = min(A.tree_top, V.n_sup);
-      for (int i = lane; i < R; i += 64) {
-        if (kk[i] == LLONG_MAX) continue;  // fewer live supers than tree_top
-        const long long key = -kk[i];
-        const int s = (int)(0xffffffffu - (unsigned)(key & 0xffffffffll));
-        atomicOr(&S.supmask[qi][s >> 5], 1u << (s & 31));
+      long long held = loose_leaf_eligible(V, tq, A.window, A.sinks);
+      for (int base = 0; base < nsp; base += 64) {
+        const int i = base + lane;
+        int w = 0, sid = -1;
+        if (i < nsp && kk[i] != LLONG_MAX) {
+          sid = (int)(0xffffffffu - (unsigned)((-kk[i]) & 0xffffffffll));
+          w = sup_eligible(V, sid, tq, A.window, A.sinks);
+        }
+        const long long inc = wave_incl_scan((long long)w, 0ll, [](long long a, long long b) { return a + b; });
+        if (sid >= 0 && (i < R || held + inc - w < need))
+          atomicOr(&S.supmask[qi][sid >> 5], 1u << (sid & 31));
+        held += lane63(inc);
+        if (base + 64 >= R && held >= need) break;
       }
     }
     __syncthreads();
@@ -240,7 +266,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
       const int beta = bt * 16 + (lane & 15);
       if (beta >= V.n_bkt) return;
       const BucketInfo bi = load_bucket<DENSE>(V, beta);
-      const int sup = TREE ? V.leafsup[beta] : -1;
+      const int sup = TREE && beta < V.covered ? V.leafsup[beta] : -1;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         if (tq[v] < 0 || !is_cand(sup, qrow + v)) continue;
@@ -312,7 +338,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
       for (int v = 0; v < 4; ++v) any |= sc[v] >= slo[v];
       if (!any) return;
       const BucketInfo bi = load_bucket<DENSE>(V, beta);
-      const int sup = TREE ? V.leafsup[beta] : -1;
+      const int sup = TREE && beta < V.covered ? V.leafsup[beta] : -1;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         if (sc[v] < slo[v]) continue;
@@ -402,7 +428,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
       for (int v = 0; v < 4; ++v) any |= sc[v] >= slo[v];
       if (!any) return;
       const BucketInfo bi = load_bucket<DENSE>(V, beta);
-      const int sup = TREE ? V.leafsup[beta] : -1;
+      const int sup = TREE && beta < V.covered ? V.leafsup[beta] : -1;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         if (sc[v] < slo[v]) continue;

@@ -78,6 +78,79 @@ __device__ __forceinline__ int bucket_key(const IdxView& V, int beta, const Buck
   return V.bmem[b.off + k / p] * p + k % p;
 }
 
+// ---- Tree walk ("Prefrontal's Latent Sparse Attention speeds up one
+// attention layer 72x at 10M tokens", section "What it changes": a query
+// walks the cluster hierarchy down; the walk keeps taking the next best node
+// while the candidates hold fewer eligible keys than the query's budget,
+// since a query reads a fixed number of keys, mauroscia.it D-LSA paragraph).
+
+// Keys j in [a, b) with sinks <= j <= t - window.
+__device__ __forceinline__ long long span_eligible(long long a, long long b, int t, int window,
+                                                   int sinks) {
+  const long long lo = a > sinks ? a : (long long)sinks;
+  const long long hi = b - 1 < (long long)t - window ? b - 1 : (long long)t - window;
+  return hi >= lo ? hi - lo + 1 : 0;
+}
+
+// Eligible keys at t under super cluster s: the blocks of its group that lie
+// wholly inside [sinks, t - window] come from the key table, the (at most
+// two) blocks that hold an end of that range are counted leaf by leaf.
+__device__ __forceinline__ int sup_eligible(const IdxView& V, int s, int t, int window, int sinks) {
+  const long long lo = sinks, hi = (long long)t - window;
+  if (hi < lo) return 0;
+  const int G = V.tgroup;
+  const long long KB = V.blk_keys;
+  const long long b0 = (long long)(s / V.tsuper) * G;
+  const int32_t* sk = V.skey + (int64_t)s * (G + 1);
+  const long long g_lo = b0 * KB, g_hi = (b0 + G) * KB - 1;
+  if (g_hi < lo || g_lo > hi) return 0;
+  if (g_lo >= lo && g_hi <= hi) return sk[G];
+  long long f0 = (lo + KB - 1) / KB - b0, f1 = (hi + 1) / KB - b0;   // whole blocks [f0, f1)
+  f0 = f0 < 0 ? 0 : f0;
+  f1 = f1 > G ? G : f1;
+  int e = f1 > f0 ? sk[f1] - sk[f0] : 0;
+  const int32_t* sb = V.sblk + (int64_t)s * (G + 1);
+  const int32_t* mem = V.smem + V.soff[s];
+  const long long kl = lo / KB - b0, kh = hi / KB - b0;
+  for (int i = 0; i < 2; ++i) {
+    const long long k = i == 0 ? kl : kh;
+    if ((i == 1 && kh == kl) || k < 0 || k >= G || (k >= f0 && k < f1)) continue;
+    for (int j = sb[k]; j < sb[k + 1]; ++j) {
+      const int leaf = mem[j];
+      const BucketInfo bi = load_bucket<false>(V, leaf);
+      int klo;
+      e += eligible<false>(V, leaf, bi, t, window, sinks, &klo);
+    }
+  }
+  return e;
+}
+
+// Eligible keys at t under top node n (third level): the sum over its supers.
+__device__ __forceinline__ int top_eligible(const IdxView& V, int n, int t, int window, int sinks) {
+  const int32_t* m = V.tmem + V.toff[n];
+  const int c = V.tcnt[n];
+  int e = 0;
+  for (int j = 0; j < c; ++j) e += sup_eligible(V, m[j], t, window, sinks);
+  return e;
+}
+
+// Eligible keys at t of the leaves outside the complete groups (always
+// candidates): they cover keys [first key of the first uncovered block, n_pool * pool).
+__device__ __forceinline__ long long loose_leaf_eligible(const IdxView& V, int t, int window,
+                                                         int sinks) {
+  return span_eligible((long long)(V.covered / V.bpb) * V.blk_keys, (long long)V.n_pool * V.pool, t,
+                       window, sinks);
+}
+
+// Eligible keys at t under the supers outside the complete top groups (third
+// level): the keys of groups covered_sup / S .. n_sup / S - 1.
+__device__ __forceinline__ long long loose_sup_eligible(const IdxView& V, int t, int window,
+                                                        int sinks) {
+  const long long gk = (long long)V.tgroup * V.blk_keys;
+  return span_eligible((long long)(V.covered_sup / V.tsuper) * gk, (long long)(V.n_sup / V.tsuper) * gk,
+                       t, window, sinks);
+}
+
 // Bitonic sort (ascending) of n_pow2 int32 / int64 in LDS by one wave.
 template <class T>
 __device__ void wave_bitonic(T* a, int n) {

@@ -872,6 +872,26 @@ __device__ __forceinline__ int nth_member(const int32_t* off, const int32_t* mem
   return mem[off[nodes[a]] + (f - pre[a])];
 }
 
+// The walk over ranked nodes (ids[0..n) best first, n <= RT, out of `total`
+// nodes): the first min(quota, total), then more in order while the keys held
+// (`held`, plus w(id) of every node taken) stay below `need`.  Returns the
+// number taken, or -1 when the n ranked nodes do not reach `need` and more
+// nodes exist.  Every thread of the block must call it.
+template <class W>
+__device__ __forceinline__ int block_walk(const int* ids, int n, int total, int quota, long long held,
+                                          int need, W w, int* ired, long long* lred) {
+  const int tid = threadIdx.x;
+  const int x = tid < n ? w(ids[tid]) : 0;
+  int all;
+  const int ex = block_excl_scan<RT>(x, ired, &all);
+  const bool hit = tid < n && held + ex + x >= need;
+  const long long first = block_min_ll<RT>(hit ? tid : LLONG_MAX, lred);
+  const int base = min(quota, total);
+  if (held >= need) return base;
+  if (first != LLONG_MAX) return max(base, (int)first + 1);
+  return n == total ? total : -1;
+}
+
 static_assert(SUPN / 32 == kSupMaskWords, "Tree decode super mask size");
 
 // supmask (nullable, decode): a query whose supers were chosen but whose
@@ -907,30 +927,53 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, 
       qv[4 * k] = x.x; qv[4 * k + 1] = x.y; qv[4 * k + 2] = x.z; qv[4 * k + 3] = x.w;
     }
   }
-  int Rs = R;                          // supers taken (third level: at most R)
+  // The walk: a level takes its quota of best nodes, then the next best while
+  // the candidates hold fewer eligible keys than the budget.  The nodes are
+  // ranked up to TOPCAP deep; a walk that needs more goes to the exact kernel.
+  const int need = budget_at(A, t);
+  const long long held_leaf = sup ? loose_leaf_eligible(V, t, A.window, A.sinks) : 0;
+  int Rs = 0;                          // supers taken
   if (ok && sup && V.n_top > 0) {
-    // third level: the tree2_top best top nodes; candidate supers are their
-    // members and the supers under no top node
+    // third level: top nodes first; the supers ranked are the members of the
+    // top nodes taken and the supers under no top node
     const int R2 = min(A.tree2_top, V.n_top);
     ok = R2 >= 1 && R2 <= TOPCAP;
     if (ok) {
-      top_nodes_any(V.tcent, V.n_top, [](int c) { return c; }, qv, R2, s_tmp, s_sup);
+      const int nr2 = min(V.n_top, TOPCAP);
+      top_nodes_any(V.tcent, V.n_top, [](int c) { return c; }, qv, nr2, s_tmp, s_sup);
       __syncthreads();
-      if (wave == 0) node_prefix(V.tcnt, s_sup, R2, s_pre);
-      __syncthreads();
-      const int nsel2 = s_pre[TOPCAP];
-      const int ncs = nsel2 + (V.n_sup - V.covered_sup);
-      ok = ncs <= SUPN;
+      const long long held_top = held_leaf + loose_sup_eligible(V, t, A.window, A.sinks);
+      const int R2w = block_walk(s_sup, nr2, V.n_top, R2, held_top, need,
+                                 [&](int n) { return top_eligible(V, n, t, A.window, A.sinks); },
+                                 L.ired, L.red);
+      ok = R2w >= 0;
       if (ok) {
-        Rs = min(R, ncs);
-        top_nodes_any(V.scent, ncs, [&](int c) {
-          return c < nsel2 ? nth_member(V.toff, V.tmem, s_sup, s_pre, R2, c)
-                           : V.covered_sup + (c - nsel2);
-        }, qv, Rs, s_tmp, s_sup);
+        if (wave == 0) node_prefix(V.tcnt, s_sup, R2w, s_pre);
+        __syncthreads();
+        const int nsel2 = s_pre[TOPCAP];
+        const int ncs = nsel2 + (V.n_sup - V.covered_sup);
+        ok = ncs <= SUPN;
+        if (ok) {
+          const int nrs = min(ncs, TOPCAP);
+          top_nodes_any(V.scent, ncs, [&](int c) {
+            return c < nsel2 ? nth_member(V.toff, V.tmem, s_sup, s_pre, R2w, c)
+                             : V.covered_sup + (c - nsel2);
+          }, qv, nrs, s_tmp, s_sup);
+          __syncthreads();
+          Rs = block_walk(s_sup, nrs, ncs, R, held_leaf, need,
+                          [&](int sp) { return sup_eligible(V, sp, t, A.window, A.sinks); }, L.ired,
+                          L.red);
+          ok = Rs >= 0;
+        }
       }
     }
   } else if (ok && sup) {
-    top_nodes_any(V.scent, V.n_sup, [](int c) { return c; }, qv, R, s_tmp, s_sup);
+    const int nrs = min(V.n_sup, TOPCAP);
+    top_nodes_any(V.scent, V.n_sup, [](int c) { return c; }, qv, nrs, s_tmp, s_sup);
+    __syncthreads();
+    Rs = block_walk(s_sup, nrs, V.n_sup, R, held_leaf, need,
+                    [&](int sp) { return sup_eligible(V, sp, t, A.window, A.sinks); }, L.ired, L.red);
+    ok = Rs >= 0;
   }
   if (ok && sup) {
     __syncthreads();
