@@ -82,6 +82,10 @@ EXPORTS = {
                                 c_vp, c_sz, c_vp]),
     "lsa_dense_select": (c_i32, [c_vp, c_i64, c_vp, c_vp, c_i32, ctypes.POINTER(SelectParams),
                                  c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "lsa_decode_step_noalloc_max_bytes": (c_sz, []),
+    "lsa_decode_step_noalloc": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_i64, ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                        c_vp, c_vp]),
 }
 
 _lib = None
@@ -398,6 +402,24 @@ def decode_step(indexes: Sequence[LsaIndex], latk_new: torch.Tensor, latq: torch
     _check(lib().lsa_decode_step(hs, n, _ptr(latk_new), _ptr(latq), _ptr(q), _ptr(k), _ptr(v),
                                  seq_stride_rows, ctypes.byref(sp), ctypes.byref(ap), _ptr(out),
                                  _ptr(ws), ws.numel(), _stream(stream)), "lsa_decode_step")
+    return out
+
+
+def decode_step_noalloc(indexes: Sequence[LsaIndex], latk_new: torch.Tensor, latq: torch.Tensor,
+                        q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_stride_rows: int,
+                        sp: SelectParams, ap: AttnParams, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """lsa_decode_step_noalloc: decode_step with the library's own device
+    workspace; the caller passes the output buffer."""
+    n = len(indexes)
+    _need(latk_new, torch.int8, "latk_new", (n, 64))
+    _need(latq, torch.int8, "latq", (n, 64))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, torch.bfloat16, name)
+    _need(out, torch.float32 if ap.out_f32 else torch.bfloat16, "out", (n, ap.Hq, ap.D))
+    hs = (c_vp * n)(*[ctypes.cast(ix._desc, c_vp).value for ix in indexes])
+    _check(lib().lsa_decode_step_noalloc(hs, n, _ptr(latk_new), _ptr(latq), _ptr(q), _ptr(k), _ptr(v),
+                                         seq_stride_rows, ctypes.byref(sp), ctypes.byref(ap), _ptr(out),
+                                         _stream(stream)), "lsa_decode_step_noalloc")
     return out
 
 

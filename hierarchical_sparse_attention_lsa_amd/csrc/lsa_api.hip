@@ -50,6 +50,23 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(LSA_E_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+}  // namespace
+
+namespace lsa {
+int fail_status(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int fail_hip(hipError_t e, const char* where) { return hip_fail(e, where); }
+}  // namespace lsa
+
+namespace {
+
 #define LSA_HIP(call, where)                         \
   do {                                               \
     hipError_t e_ = (call);                          \

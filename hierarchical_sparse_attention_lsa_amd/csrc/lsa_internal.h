@@ -113,6 +113,11 @@ struct DecodeAppendArgs {
   int32_t p, N, C;
 };
 
+// Set the text lsa_last_error() reports and return `code` (LSA_E_HIP with
+// the runtime's error string for fail_hip).
+int fail_status(int code, const char* fmt, ...);
+int fail_hip(hipError_t e, const char* where);
+
 // Runs set() once per device (the current one), whatever the number of host
 // threads calling; `done` is the caller's per-device bit set (devices 0..63;
 // on a higher device id set() runs on every call).  For kernel attributes,

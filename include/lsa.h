@@ -281,6 +281,25 @@ LSA_API int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_
                             const lsa_select_params* sp, const lsa_attn_params* ap, void* d_out,
                             void* d_ws, size_t ws_bytes, void* stream);
 
+/* lsa_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as lsa_decode_step, without the
+ * workspace: the step runs in a device array inside the library, one per
+ * GPU, of lsa_decode_step_noalloc_max_bytes() bytes (64 MiB), held until the
+ * process ends.  A step that needs more workspace than that (see
+ * lsa_workspace_bytes with LSA_OP_DECODE) returns LSA_E_CAPACITY and
+ * enqueues nothing.  The call allocates nothing: no hipMalloc, no
+ * allocating library routine.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by
+ * the caller. */
+LSA_API size_t lsa_decode_step_noalloc_max_bytes(void);
+LSA_API int lsa_decode_step_noalloc(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new,
+                                    const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
+                                    const uint16_t* d_v, int64_t seq_stride_rows,
+                                    const lsa_select_params* sp, const lsa_attn_params* ap,
+                                    void* d_out, void* stream);
+
 /* Quadratic comparator: every long-range key scored on its own latent
  * (q . latk[j]), best `budget` by (score desc, position asc), plus window
  * and sinks.  Same output format as lsa_select. */
