@@ -370,16 +370,25 @@ def sparse_attn_bwd(index: "LsaIndex", q: torch.Tensor, k: torch.Tensor, v: torc
 
 
 def dense_select(latk: torch.Tensor, latq: torch.Tensor, qpos: torch.Tensor, sp: SelectParams,
-                 stream=None):
+                 ws: Optional[torch.Tensor] = None, use_workspace: bool = True, stream=None):
+    """The quadratic comparator.  With a workspace (allocated here unless given)
+    batches of 64 or more queries take the single thresholded scan; without
+    one (use_workspace=False) every query takes the exact kernel."""
     nq = latq.shape[0]
     _need(latk, torch.int8, "latk")
     _need(latq, torch.int8, "latq", (nq, 64))
     _need(qpos, torch.int32, "qpos", (nq,))
     idx = torch.empty((nq, sp.max_sel), dtype=torch.int32, device=latq.device)
     cnt = torch.empty((nq,), dtype=torch.int32, device=latq.device)
+    if use_workspace and ws is None:
+        ws = torch.empty(max(workspace_bytes(OP_DENSE, None, sp, None, nq), 256), dtype=torch.uint8,
+                         device=latq.device)
+    if not use_workspace:
+        ws = None
     _check(lib().lsa_dense_select(_ptr(latk), latk.shape[0], _ptr(latq), _ptr(qpos), nq,
-                                  ctypes.byref(sp), _ptr(idx), _ptr(cnt), None, 0,
-                                  _stream(stream)), "lsa_dense_select")
+                                  ctypes.byref(sp), _ptr(idx), _ptr(cnt), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)),
+           "lsa_dense_select")
     return idx, cnt
 
 

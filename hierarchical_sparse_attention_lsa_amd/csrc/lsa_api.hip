@@ -146,6 +146,7 @@ void layout(const lsa_index_params& p, Index* h) {
   h->off_suptop = o; o = align_up(o + (p.tree2_group > 0 ? h->max_sup * 4 : 0));
   h->off_sblk = o;   o = align_up(o + h->max_sup * (p.tree_group + 1) * 4);
   h->off_skey = o;   o = align_up(o + h->max_sup * (p.tree_group + 1) * 4);
+  h->off_bdesc = o;  o = align_up(o + h->max_bkt * 16);
   {
     size_t km = kmeans_scratch_bytes(p.block, p.buckets);
     if (p.tree_group > 0) {
@@ -206,6 +207,7 @@ IdxView view_of(const Index* h) {
   v.bmem = h->at<int32_t>(h->off_bmem);
   v.bfirst = h->at<int32_t>(h->off_bfirst);
   v.blast = h->at<int32_t>(h->off_blast);
+  v.bdesc = h->at<int4>(h->off_bdesc);
   v.n_bkt = (int32_t)h->n_bkt();
   v.pool = h->prm.pool;
   v.n_pool = (int32_t)h->n_pool;
@@ -262,6 +264,8 @@ hipError_t reset_tree_maps(Index* h, hipStream_t s) {
 int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
   const lsa_index_params& P = h->prm;
   const int p = P.pool, N = P.block, C = P.buckets;
+  if (n > 0 && reinterpret_cast<uintptr_t>(src) % 16)
+    return fail(LSA_E_ARG, "latent keys must be 16-byte aligned (pooling reads 16-byte words)");
   if (h->T + n > P.max_tokens)
     return fail(LSA_E_CAPACITY, "T %lld + %lld exceeds capacity %lld", (long long)h->T,
                 (long long)n, (long long)P.max_tokens);
@@ -296,6 +300,11 @@ int append_impl(Index* h, const int8_t* src, int64_t n, hipStream_t s) {
   const int64_t t0 = nf_new == nf_old ? g0 : nf_new * N;
   LSA_HIP(launch_tail(pooled, t0, n_pool, nf_new, N, C, cent, bcnt, boff, bmem, bfirst, blast, s),
           "tail");
+  // packed descriptors of every bucket this append wrote: the blocks it
+  // completed and the tail singletons
+  LSA_HIP(launch_pack_desc(bfirst, blast, bcnt, boff, nf_old * C,
+                           nf_new * C + (n_pool - nf_new * N), h->at<int4>(h->off_bdesc), s),
+          "descriptors");
   int64_t ng_new = h->n_grp;
   if (P.tree_group > 0) {
     const int G = P.tree_group, S = P.tree_super;
@@ -461,10 +470,10 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
   if (n < 0) return fail(LSA_E_ARG, "n < 0");
   (void)iprm;
   switch (op) {
-    case LSA_OP_BUILD: case LSA_OP_APPEND: case LSA_OP_ATTN: case LSA_OP_DENSE:
+    case LSA_OP_BUILD: case LSA_OP_APPEND: case LSA_OP_ATTN:
       *bytes = 0;
       return LSA_OK;
-    case LSA_OP_SELECT:
+    case LSA_OP_SELECT: case LSA_OP_DENSE:
       *bytes = select_fast_ws_bytes((int32_t)n);
       return LSA_OK;
     case LSA_OP_PREFILL: {
@@ -730,7 +739,7 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
   memset(&da, 0, sizeof da);
   da.off_pooled = h0->off_pooled; da.off_cent = h0->off_cent; da.off_bcnt = h0->off_bcnt;
   da.off_boff = h0->off_boff; da.off_bmem = h0->off_bmem; da.off_bfirst = h0->off_bfirst;
-  da.off_blast = h0->off_blast; da.off_pend = h0->off_pend;
+  da.off_blast = h0->off_blast; da.off_pend = h0->off_pend; da.off_bdesc = h0->off_bdesc;
   da.p = p; da.N = N; da.C = h0->prm.buckets;
   int32_t qpos[16];
   bool any_batched = false;
@@ -791,7 +800,6 @@ int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_latk_new
 int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, const int32_t* d_qpos,
                      int32_t nq, const lsa_select_params* sp, int32_t* d_idx, int32_t* d_cnt,
                      void* d_ws, size_t ws_bytes, void* stream) {
-  (void)d_ws; (void)ws_bytes;
   if (int e = check_select_params(sp, false)) return e;
   if (T < 0 || T > INT32_MAX - 64 || nq < 0) return fail(LSA_E_ARG, "bad T / nq");
   if (nq > 0 && (!d_latk || !d_latq || !d_qpos || !d_idx || !d_cnt)) return fail(LSA_E_ARG, "NULL buffer");
@@ -808,7 +816,13 @@ int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, cons
   a.early_budget = sp->early_budget; a.early_until = sp->early_until; a.tree2_top = sp->tree2_top;
   a.max_sel = max_sel_of(sp);
   a.idx = d_idx; a.cnt = d_cnt; a.only = nullptr;
-  LSA_HIP(launch_select(v, a, nullptr, static_cast<hipStream_t>(stream)), "dense select");
+  // large batches with a workspace: one thresholded int8-MFMA pass over all
+  // latents, then an exact top-budget per query (the exact kernel serves the
+  // few queries whose list cannot hold the cutoff); otherwise the exact kernel
+  if (nq >= kFastSelectMinQ && d_ws && ws_bytes >= select_fast_ws_bytes(nq))
+    LSA_HIP(launch_select_fast(v, a, d_ws, static_cast<hipStream_t>(stream)), "dense select");
+  else
+    LSA_HIP(launch_select(v, a, nullptr, static_cast<hipStream_t>(stream)), "dense select");
   return LSA_OK;
 }
 

@@ -19,27 +19,38 @@ namespace lsa {
 // ---------------------------------------------------------------- pooling
 // Pooled vector g = round-half-even mean of rows g*p .. g*p+p-1 of the
 // virtual sequence (pend[0..n_pend) ++ src[0..n_src)).  One thread per
-// (pooled vector, 4 dims): 16 threads read a 64-byte row.
+// (pooled vector, 16 dims): 16-byte loads, four threads per 64-byte row.
+__device__ __forceinline__ int sbyte(int w, int j) { return (w << (24 - 8 * j)) >> 24; }
+
 __global__ void __launch_bounds__(256) k_pool(const int8_t* __restrict__ pend, int n_pend,
                                               const int8_t* __restrict__ src, int p,
                                               int8_t* __restrict__ out, int64_t n_groups) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t g = t >> 4;
-  const int c = (int)(t & 15) * 4;
+  const int64_t g = t >> 2;
+  const int c = (int)(t & 3) * 16;
   if (g >= n_groups) return;
-  int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+  int acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0;
   for (int r = 0; r < p; ++r) {
     const int64_t row = g * p + r;
     const int8_t* rp = row < n_pend ? pend + row * kDim : src + (row - n_pend) * kDim;
-    const char4 v = *reinterpret_cast<const char4*>(rp + c);
-    s0 += v.x; s1 += v.y; s2 += v.z; s3 += v.w;
+    const int4 v = *reinterpret_cast<const int4*>(rp + c);
+    const int w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[4 * k + j] += sbyte(w[k], j);
   }
-  char4 o;
-  o.x = (signed char)rhe_div(s0, p);
-  o.y = (signed char)rhe_div(s1, p);
-  o.z = (signed char)rhe_div(s2, p);
-  o.w = (signed char)rhe_div(s3, p);
-  *reinterpret_cast<char4*>(out + g * kDim + c) = o;
+  int o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    unsigned x = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x |= ((unsigned)rhe_div(acc[4 * k + j], p) & 0xffu) << (8 * j);
+    o[k] = (int)x;
+  }
+  *reinterpret_cast<int4*>(out + g * kDim + c) = make_int4(o[0], o[1], o[2], o[3]);
 }
 
 // Copy the last `keep` rows of (pend ++ src) into dst.
@@ -149,13 +160,20 @@ k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0
       for (int d = 0; d < kDim; ++d) { const int m = mu[c * kDim + d]; s += m * m; }
       musq[c] = s;
     }
+    // cluster sums laid out [dim][cluster]: the lanes of one LDS atomic below
+    // add to one dim of their rows' clusters, so their banks follow the clusters
+    for (int e = tid; e < C * kDim; e += kKmThreads) sums[e] = 0;
+    for (int e = tid; e < C; e += kKmThreads) counts[e] = 0;
     __syncthreads();
 
-    // ---- assign: 16-row tiles, all C centroids per tile ----
+    // ---- assign (16-row tiles, all C centroids per tile), with the update's
+    // sums taken from the rows the MFMA operand already holds ----
     const int ntile = N >> 4;
+    const int8_t* xl = X + (int64_t)(lane & 15) * kDim + 16 * (lane >> 4);
+    v4i a_next = wave < ntile ? *reinterpret_cast<const v4i*>(xl + (int64_t)wave * 16 * kDim) : v4i{0, 0, 0, 0};
     for (int rt = wave; rt < ntile; rt += kKmWaves) {
-      const v4i a = *reinterpret_cast<const v4i*>(X + (int64_t)(rt * 16 + (lane & 15)) * kDim +
-                                                  16 * (lane >> 4));
+      const v4i a = a_next;
+      if (rt + kKmWaves < ntile) a_next = *reinterpret_cast<const v4i*>(xl + (int64_t)(rt + kKmWaves) * 16 * kDim);
       int best[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
       int bidx[4] = {0, 0, 0, 0};
       for (int ct = 0; ct < (C >> 4); ++ct) {
@@ -183,22 +201,26 @@ k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0
 #pragma unroll
         for (int v = 0; v < 4; ++v) assign[rt * 16 + 4 * (lane >> 4) + v] = (uint16_t)bidx[v];
       }
-    }
-    for (int e = tid; e < C * kDim; e += kKmThreads) sums[e] = 0;
-    for (int e = tid; e < C; e += kKmThreads) counts[e] = 0;
-    __syncthreads();
-
-    // ---- update: per-cluster integer sums, rounded means ----
-    for (int i = wave; i < N; i += kKmWaves) {
-      const int c = assign[i];
-      atomicAdd(&sums[c * kDim + lane], (int)X[(int64_t)i * kDim + lane]);
-      if (lane == 0) atomicAdd(&counts[c], 1);
+      // this lane's operand row is lane % 16 (bytes 16 * (lane / 16) ..); its
+      // cluster sits in lanes 16 * (row / 4) .., value row % 4
+      const int r = lane & 15, src = 16 * (r >> 2);
+      const int c0 = __shfl(bidx[0], src), c1 = __shfl(bidx[1], src);
+      const int c2 = __shfl(bidx[2], src), c3 = __shfl(bidx[3], src);
+      const int cr = (r & 2) ? ((r & 1) ? c3 : c2) : ((r & 1) ? c1 : c0);
+      if (lane < 16) atomicAdd(&counts[cr], 1);
+      int32_t* sd = sums + (16 * (lane >> 4)) * C + cr;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int w4 = a[k];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) atomicAdd(&sd[(4 * k + j) * C], (w4 << (24 - 8 * j)) >> 24);
+      }
     }
     __syncthreads();
     for (int e = tid; e < C * kDim; e += kKmThreads) {
-      const int c = e / kDim;
+      const int c = e >> 6, d = e & 63;
       const int n = counts[c];
-      if (n > 0) mu[e] = (int8_t)rhe_div(sums[e], n);
+      if (n > 0) mu[e] = (int8_t)rhe_div(sums[d * C + c], n);
     }
     __syncthreads();
   }
@@ -371,19 +393,26 @@ __global__ void __launch_bounds__(kKmAT) k_km_assign(const int8_t* __restrict__ 
 #pragma unroll
       for (int v = 0; v < 4; ++v) S.asg[(int64_t)b * N + row + 4 * (lane >> 4) + v] = (uint16_t)bidx[v];
     }
-    // the tile's 16 rows join their clusters' sums (lane = dimension)
+    // the tile's rows join their clusters' sums ([dim][cluster]), from the
+    // operand bytes this lane holds: row lane % 16, dims 16 * (lane / 16) ..
+    const int r = lane & 15, src = 16 * (r >> 2);
+    const int c0 = __shfl(bidx[0], src), c1 = __shfl(bidx[1], src);
+    const int c2 = __shfl(bidx[2], src), c3 = __shfl(bidx[3], src);
+    const int cr = (r & 2) ? ((r & 1) ? c3 : c2) : ((r & 1) ? c1 : c0);
+    if (lane < 16) atomicAdd(&cnts[cr], 1);
+    int32_t* sd = sums + (16 * (lane >> 4)) * C + cr;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = __shfl(bidx[r & 3], (r >> 2) * 16);
-      atomicAdd(&sums[c * kDim + lane], (int)X[(int64_t)(row + r) * kDim + lane]);
-      if (lane == 0) atomicAdd(&cnts[c], 1);
+    for (int k = 0; k < 4; ++k) {
+      const int w4 = a[k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) atomicAdd(&sd[(4 * k + j) * C], (w4 << (24 - 8 * j)) >> 24);
     }
   }
   __syncthreads();
   int32_t* part = S.part + ((int64_t)b * W + w) * C * 65;
   for (int e = tid; e < C * 65; e += kKmAT) {
     const int c = e / 65, d = e % 65;
-    part[e] = d < kDim ? sums[c * kDim + d] : cnts[c];
+    part[e] = d < kDim ? sums[d * C + c] : cnts[c];
   }
 }
 
@@ -438,7 +467,24 @@ __global__ void __launch_bounds__(64) k_decode_append(DecodeAppendArgs a, const 
     reinterpret_cast<int32_t*>(base + a.off_bmem)[g] = (int32_t)g;
     reinterpret_cast<int32_t*>(base + a.off_bfirst)[beta] = (int32_t)g;
     reinterpret_cast<int32_t*>(base + a.off_blast)[beta] = (int32_t)g;
+    reinterpret_cast<int4*>(base + a.off_bdesc)[beta] = make_int4((int)g, (int)g, 1, (int)g);
   }
+}
+
+// ---------------------------------------------------------------- packed descriptors
+__global__ void k_pack_desc(const int32_t* __restrict__ bfirst, const int32_t* __restrict__ blast,
+                            const int32_t* __restrict__ bcnt, const int32_t* __restrict__ boff,
+                            int64_t b0, int64_t b1, int4* __restrict__ bdesc) {
+  const int64_t b = b0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < b1) bdesc[b] = make_int4(bfirst[b], blast[b], bcnt[b], boff[b]);
+}
+
+hipError_t launch_pack_desc(const int32_t* bfirst, const int32_t* blast, const int32_t* bcnt,
+                            const int32_t* boff, int64_t b0, int64_t b1, int4* bdesc, hipStream_t s) {
+  if (b1 <= b0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_desc, dim3((unsigned)((b1 - b0 + 255) / 256)), dim3(256), 0, s, bfirst, blast,
+                     bcnt, boff, b0, b1, bdesc);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- Tree walk tables
@@ -510,7 +556,7 @@ hipError_t launch_pool(const int8_t* pend, int32_t n_pend, const int8_t* src, in
                        int32_t p, int8_t* pooled_out, int64_t n_groups, hipStream_t s) {
   (void)n_src;
   if (n_groups <= 0) return hipSuccess;
-  const int64_t threads = n_groups * 16;
+  const int64_t threads = n_groups * 4;
   const unsigned grid = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL(k_pool, dim3(grid), dim3(256), 0, s, pend, n_pend, src, p, pooled_out,
                      n_groups);

@@ -33,6 +33,7 @@ struct Index {
   int64_t off_scent, off_scnt, off_soff, off_smem, off_leafsup, off_pend;
   int64_t off_tcent, off_tcnt, off_toff, off_tmem, off_suptop;
   int64_t off_sblk, off_skey;     // per super, per block of its group (Tree walk fill)
+  int64_t off_bdesc;              // per bucket {first, last, count, offset}, packed
   int64_t off_kmws, kmws_bytes;   // k-means scratch (few-block clustering)
   int64_t used_bytes;
 
@@ -50,6 +51,7 @@ struct IdxView {
   const int32_t* bmem;    // member pooled ids
   const int32_t* bfirst;  // first member pooled id
   const int32_t* blast;   // last member pooled id
+  const int4* bdesc;      // the four above, packed per bucket: {first, last, count, offset}
   const int32_t* leafsup; // leaf -> super id (Tree) or nullptr
   int32_t n_bkt;
   int32_t pool;
@@ -110,6 +112,7 @@ struct DecodeAppendArgs {
   int32_t pend_slot[16];
   int32_t batched[16];
   int64_t off_pooled, off_cent, off_bcnt, off_boff, off_bmem, off_bfirst, off_blast, off_pend;
+  int64_t off_bdesc;
   int32_t p, N, C;
 };
 
@@ -146,6 +149,9 @@ hipError_t launch_kmeans(const int8_t* X, int32_t N, int32_t C, int32_t iters, i
 hipError_t launch_sup_tables(const int32_t* soff, const int32_t* scnt, const int32_t* smem,
                              const int32_t* bcnt, int32_t s0, int32_t nsup, int32_t S, int32_t G,
                              int32_t C, int32_t p, int32_t* sblk, int32_t* skey, hipStream_t s);
+// Packed descriptors bdesc[b] = {bfirst, blast, bcnt, boff}[b] for buckets [b0, b1).
+hipError_t launch_pack_desc(const int32_t* bfirst, const int32_t* blast, const int32_t* bcnt,
+                            const int32_t* boff, int64_t b0, int64_t b1, int4* bdesc, hipStream_t s);
 hipError_t launch_tail(const int8_t* pooled, int64_t g0, int64_t g1, int64_t n_full, int32_t N,
                        int32_t C, int8_t* cent, int32_t* bcnt, int32_t* boff, int32_t* bmem,
                        int32_t* bfirst, int32_t* blast, hipStream_t s);

@@ -10,9 +10,10 @@
 namespace {
 
 // Workspace of the no-allocation decode step: each GPU the library runs on
-// holds one copy of it until the process ends.  64 MiB covers 16 sequences
-// of 10 * 2^20 keys at a 4096 + 512 + 4 key budget with GQA 32/8, D = 128.
-constexpr size_t kScratchBytes = 64ull << 20;
+// holds one copy of it until the process ends.  128 MiB covers 16 sequences
+// of 10 * 2^20 keys at a 4096 + 512 + 4 key budget with GQA 32/8, D = 128
+// (that step needs 84 MiB).
+constexpr size_t kScratchBytes = 128ull << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // Device address of this GPU's copy of `scratch`, looked up once per device

@@ -63,10 +63,11 @@ template <bool DENSE>
 __device__ __forceinline__ BucketInfo load_bucket(const IdxView& V, int beta) {
   BucketInfo b;
   if (DENSE || beta >= V.n_bkt) { b.first = beta; b.last = beta; b.cnt = beta < V.n_bkt; b.off = beta; return b; }
-  b.first = V.bfirst[beta];
-  b.last = V.blast[beta];
-  b.cnt = V.bcnt[beta];
-  b.off = V.boff[beta];
+  const int4 d = V.bdesc[beta];        // one 16-byte load: {first, last, count, offset}
+  b.first = d.x;
+  b.last = d.y;
+  b.cnt = d.z;
+  b.off = d.w;
   return b;
 }
 

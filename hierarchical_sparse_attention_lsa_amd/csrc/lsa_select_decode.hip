@@ -93,6 +93,9 @@ struct DecWs {
                                     // one histogram per score workgroup
   int32_t n_part;                   // histograms per sequence
   uint32_t* supmask;                // [nseq][kSupMaskWords] Tree: supers chosen
+  int32_t* above;                   // [nseq] keys above the cutoff bin (slice workgroups -> finish)
+  long long* cand;                  // [nseq][PERT_MAX][BCAP] cutoff-bin order keys per slice
+  int32_t* ncand;                   // [nseq][PERT_MAX] cutoff-bin buckets per slice
 };
 
 
@@ -173,6 +176,7 @@ __global__ void __launch_bounds__(DT) k_dec_score(DecViews VS, SelArgs A, DecWs 
             reinterpret_cast<int32_t*>(abase + D.off_bmem)[g_new] = (int32_t)g_new;
             reinterpret_cast<int32_t*>(abase + D.off_bfirst)[bn] = (int32_t)g_new;
             reinterpret_cast<int32_t*>(abase + D.off_blast)[bn] = (int32_t)g_new;
+            reinterpret_cast<int4*>(abase + D.off_bdesc)[bn] = make_int4((int)g_new, (int)g_new, 1, (int)g_new);
           }
         }
       }
@@ -222,14 +226,15 @@ __device__ __forceinline__ void dec_finish_row(const SelArgs& A, int seq, int t,
   if (lane == 0) A.cnt[seq] = totalk;
 }
 
-// out_total keys of the nt taken buckets listed in ascending id: bucket r
-// starts at output offset l_off[r] and first key slot l_ks[r]; one output key
-// per thread and round, four rounds in flight.
+// Output slots [o_begin, out_total) from the nt taken buckets listed in
+// ascending output offset: bucket r starts at output offset l_off[r] (the
+// first at o_begin) and first key slot l_ks[r]; one output key per thread
+// and round, four rounds in flight.
 __device__ __forceinline__ void dec_emit_keys(const IdxView& V, const SelArgs& A, int seq, const int* l_off,
-                                              const int* l_ks, int nt, int out_total) {
+                                              const int* l_ks, int nt, int out_total, int o_begin = 0) {
   const int tid = threadIdx.x, p = V.pool;
   int32_t* row = A.idx + (int64_t)seq * A.max_sel;
-  for (int o0 = tid; o0 < out_total; o0 += 4 * DT) {
+  for (int o0 = o_begin + tid; o0 < out_total; o0 += 4 * DT) {
     int sl[4], g[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -357,7 +362,9 @@ __device__ __forceinline__ long long rebuilt_key(int s, int beta) {
 
 // PERT buckets per thread: the smallest instance that holds the index is
 // launched, since every pass costs VALU time per slot, used or not.
-template <int PERT>
+// FINISH = false: one workgroup per slice of DT buckets (grid slices x
+// sequences); FINISH = true: one workgroup per sequence, after them.
+template <int PERT, bool FINISH>
 __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs W,
                                                    int32_t* __restrict__ flags) {
   constexpr int kListCap = list_cap(PERT);
@@ -371,7 +378,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   __shared__ long long s_r3[DW][3];
   extern __shared__ int s_e[];         // [bucket id]: eligible keys, later the keys taken
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
-  const int seq = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int slice = blockIdx.x;        // buckets slice*DT .. slice*DT + DT - 1
   const IdxView V = vsp->v[seq];
   const int t = vsp->qpos[seq];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -379,44 +387,53 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   const int n = V.n_bkt;
   const int p = V.pool;
   const int64_t base = (int64_t)seq * VS.cap;
+  const int nsl = max(1, (n + DT - 1) / DT);
+  if (slice >= nsl) return;            // uniform: past this sequence's index
   if (n > DT * PERT) {                 // too large for registers: the exact kernel serves it
-    if (tid == 0) flags[seq] = 1;
+    if (!FINISH && slice == 0 && tid == 0) flags[seq] = 1;
     return;
   }
   // ---- fast path: the cutoff located in the score histogram ----
   // Buckets whose score bin lies above the bin where the eligible keys reach
   // the budget are taken whole; the buckets of that bin are ranked by order
-  // key and taken in turn, the last one cut.  A cutoff bin of more than BCAP
-  // buckets (many equal or near-equal scores) leaves it to the general path.
-  {
+  // key and taken in turn, the last one cut.  Every slice's workgroup finds
+  // the cut bin from the summed partial histograms, writes the keys of its
+  // own buckets above it (slices in order, ids ascending within a slice: the
+  // earlier slices' keys above the cut give its output offset) and lists its
+  // cutoff-bin buckets; the finishing workgroup of the sequence ranks the
+  // cutoff bin, writes its keys, the sinks and the window.  A cutoff bin of
+  // more than BCAP buckets (many equal or near-equal scores) leaves the whole
+  // row to the general path below, run by the finishing workgroup.
+  int* l_off = s_e;                    // taken buckets: output offset, first key slot
+  int* l_ks = s_e + DT;
+  __shared__ int s_nt, s_nb;
+  __shared__ int s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
+  if (!FINISH) {
     __shared__ int s_fc[4];            // cut bin, keys above it, its scores [lo, hi]
-    __shared__ int s_nt, s_nb;
-    __shared__ int s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
-    int scv[PERT], ev[PERT];
-#pragma unroll
-    for (int u = 0; u < PERT; ++u) {
-      const int j = u * DT + tid;
-      scv[u] = j < n ? W.score[base + j] : 0;
-      ev[u] = j < n ? W.elig[base + j] : 0;
-    }
     // bins from the top score down: thread tid takes bins NBIN-1-2tid (he[0])
-    // and NBIN-2-2tid (he[1]), summed over the score workgroups
-    int he[2] = {0, 0};
+    // and NBIN-2-2tid (he[1]), summed over the score workgroups (the slices),
+    // and the same over the slices before this one (hb) and this one (hm)
+    int he[2] = {0, 0}, hb[2] = {0, 0}, hm[2] = {0, 0};
     {
-      const int nwg = (n + DT - 1) / DT;
       const int2* hp = reinterpret_cast<const int2*>(W.hpart + (int64_t)seq * W.n_part * NBIN) + (NBIN / 2 - 1 - tid);
+      const int nh = (n + DT - 1) / DT;    // score workgroups that wrote a histogram (0 for an empty index)
       int w = 0;
-      for (; w + 4 <= nwg; w += 4) {
+      for (; w + 4 <= nh; w += 4) {
         int2 x[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[k] = hp[(int64_t)(w + k) * (NBIN / 2)];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) { he[0] += x[k].y; he[1] += x[k].x; }
+        for (int k = 0; k < 4; ++k) {
+          he[0] += x[k].y; he[1] += x[k].x;
+          if (w + k < slice) { hb[0] += x[k].y; hb[1] += x[k].x; }
+          if (w + k == slice) { hm[0] = x[k].y; hm[1] = x[k].x; }
+        }
       }
-      for (; w < nwg; ++w) {
+      for (; w < nh; ++w) {
         const int2 x = hp[(int64_t)w * (NBIN / 2)];
-        he[0] += x.y;
-        he[1] += x.x;
+        he[0] += x.y; he[1] += x.x;
+        if (w < slice) { hb[0] += x.y; hb[1] += x.x; }
+        if (w == slice) { hm[0] = x.y; hm[1] = x.x; }
       }
     }
     if (tid == 0) { s_fc[0] = NBIN; s_fc[1] = 0; s_fc[2] = INT_MAX; s_fc[3] = INT_MAX; s_nt = 0; s_nb = 0; }
@@ -439,50 +456,101 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       }
     }
     __syncthreads();
-    const int above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
-    constexpr int NBW = DT * PERT / 32;
-    int* ids = s_e;                    // [TCAP] taken bucket ids, any order; later output offsets
-    int* tks = s_e + TCAP;             // [TCAP] keys taken from them; later first key slots
-    int* sid = s_e + 2 * TCAP;         // [TCAP] taken bucket ids, ascending
-    int* stk = s_e + 3 * TCAP;         // [TCAP] keys taken, ascending bucket id
-    unsigned* bm = reinterpret_cast<unsigned*>(s_e + 4 * TCAP);     // taken-id bitmap
-    int* wp = s_e + 4 * TCAP + NBW;                                 // taken ids before each word
-    // bit u: bucket u*DT + tid lies above the cut bin / in it
-    unsigned m_above = 0, m_cut = 0;
+    const int cut = s_fc[0], above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
+    // keys above the cut bin in the earlier slices (this slice's output
+    // offset) and in this one; both at most the budget
+    long long pk = 0;
 #pragma unroll
-    for (int u = 0; u < PERT; ++u) {
-      const bool el = ev[u] > 0;
-      m_above |= (el && scv[u] > hi_s ? 1u : 0u) << u;
-      m_cut |= (el && scv[u] >= lo_s && scv[u] <= hi_s ? 1u : 0u) << u;
-    }
-    // buckets above the cut: one slot reservation per wave (at most budget of
-    // them, each giving a key, so they fit in TCAP)
+    for (int j = 0; j < 2; ++j)
+      if (NBIN - 1 - (2 * tid + j) > cut) pk += ((long long)hb[j] << 32) | (long long)hm[j];
+    pk = block_sum_ll<DT>(pk, s_red);
+    const int before = (int)(pk >> 32), mine = (int)(pk & 0xffffffffll);
+    // this slice's bucket of the thread, above the cut bin or in it
+    const int j = slice * DT + tid;
+    const int scv = j < n ? W.score[base + j] : 0;
+    const int ev = j < n ? W.elig[base + j] : 0;
+    const bool is_above = ev > 0 && scv > hi_s;
+    const bool is_cut = ev > 0 && scv >= lo_s && scv <= hi_s;
+    // taken buckets in id order: output offset and first key slot (LDS)
     {
-      int wt;
-      const int wpre = wave_excl_scan(__popc(m_above), &wt);
-      int wb = 0;
-      if (lane == 0 && wt > 0) wb = atomicAdd(&s_nt, wt);
-      int pos = __shfl(wb, 0) + wpre;
-#pragma unroll
-      for (int u = 0; u < PERT; ++u) {
-        if ((m_above & (1u << u)) && pos < TCAP) { ids[pos] = u * DT + tid; tks[pos] = ev[u]; }
-        pos += (m_above >> u) & 1u;
+      int tot;
+      const int pre = block_excl_scan<DT>(is_above ? (ev << 16) | 1 : 0, s_ired, &tot);
+      if (is_above) {
+        l_off[pre & 0xffff] = before + (pre >> 16);
+        l_ks[pre & 0xffff] = W.kstart[base + j];
       }
-    }
-    if (m_cut) {
-#pragma unroll
-      for (int u = 0; u < PERT; ++u) {
-        if (!(m_cut & (1u << u))) continue;
+      if (is_cut) {
         const int q = atomicAdd(&s_nb, 1);
-        if (q < BCAP) { s_cq[q] = order_key(scv[u], u * DT + tid); s_ci[q] = u * DT + tid; s_ce[q] = ev[u]; }
+        if (q < BCAP) W.cand[((int64_t)seq * PERT_MAX + slice) * BCAP + q] = order_key(scv, j);
+      }
+      __syncthreads();
+      dec_emit_keys(V, A, seq, l_off, l_ks, tot & 0xffff, before + mine, before);
+      if (tid == 0) W.ncand[seq * PERT_MAX + slice] = s_nb;
+      if (slice == 0 && tid == 0) W.above[seq] = above;
+    }
+    return;
+  }
+  // ---- the finishing workgroup of the sequence ----
+  {
+    const int above = W.above[seq];
+    // the cutoff bin's buckets of every slice (order key, id, eligible keys)
+    if (tid == 0) s_nb = 0;
+    __syncthreads();
+    if (tid < nsl) {
+      const int c = W.ncand[seq * PERT_MAX + tid];
+      int at = 0;
+      if (c > 0) at = atomicAdd(&s_nb, c);
+      for (int k = 0; k < c && at + k < BCAP && k < BCAP; ++k) {
+        const long long kk = W.cand[((int64_t)seq * PERT_MAX + tid) * BCAP + k];
+        s_cq[at + k] = kk;
+        s_ci[at + k] = (int)(0xffffffffu - (unsigned)(kk & 0xffffffffll));
       }
     }
-    for (int w = tid; w < NBW; w += DT) bm[w] = 0u;
     __syncthreads();
     const int nb = s_nb;
     if (nb <= BCAP) {                  // uniform; else the general path below
-      DecTail L{s_cq, s_ci, s_ce, s_re, s_rs, s_ired, &s_nt, ids, tks, sid, stk, bm, wp};
-      dec_tail(V, A, W.kstart + base, seq, t, B, above, nb, NBW, L);
+      if (tid < nb) s_ce[tid] = W.elig[base + s_ci[tid]];
+      __syncthreads();
+      // rank in the cut bin (order keys are distinct): larger keys first
+      if (tid < nb) {
+        const long long k = s_cq[tid];
+        int r = 0;
+        for (int i = 0; i < nb; ++i) r += s_cq[i] > k ? 1 : 0;
+        s_re[r] = s_ce[tid];
+        s_rs[r] = tid;
+      }
+      __syncthreads();
+      int tot;
+      const int x = tid < nb ? s_re[tid] : 0;
+      const int bef = block_excl_scan<DT>(x, s_ired, &tot);
+      const int tk = max(0, min(x, B - above - bef));
+      // the taken ones (a prefix of the ranks), ordered by id: rank by id among them
+      int* t_id = s_e + 2 * DT;
+      int* t_tk = s_e + 3 * DT;
+      if (tid < nb) { t_id[tid] = tk > 0 ? s_ci[s_rs[tid]] : INT_MAX; t_tk[tid] = tk; }
+      __syncthreads();
+      int my_id = INT_MAX, my_tk = 0, r = 0;
+      if (tid < nb && t_tk[tid] > 0) {
+        my_id = t_id[tid];
+        my_tk = t_tk[tid];
+        for (int i = 0; i < nb; ++i) r += t_id[i] < my_id ? 1 : 0;
+      }
+      __syncthreads();
+      if (my_tk > 0) { t_id[r] = my_id; t_tk[r] = my_tk; }
+      int nt_cut;
+      const int ncut = __syncthreads_count(my_tk > 0);
+      nt_cut = ncut;
+      // output offsets after the keys above the cut bin, in id order
+      const int xo = tid < nt_cut ? t_tk[tid] : 0;
+      int cut_total;
+      const int ob = block_excl_scan<DT>(xo, s_ired, &cut_total);
+      if (tid < nt_cut) {
+        l_off[tid] = above + ob;
+        l_ks[tid] = W.kstart[base + t_id[tid]];
+      }
+      __syncthreads();
+      dec_emit_keys(V, A, seq, l_off, l_ks, nt_cut, above + cut_total, above);
+      dec_finish_row(A, seq, t, above + cut_total);
       if (tid == 0) flags[seq] = 0;
       return;
     }
@@ -665,8 +733,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   const int out_total = packed_total >> 16, nt = packed_total & 0xffff;
   const bool ok = !overflow && nt <= kListCap;
   // list of taken buckets (output offset, first key slot), ascending ids, over s_e
-  int* l_off = s_e;
-  int* l_ks = s_e + kListCap;
+  l_off = s_e;
+  l_ks = s_e + kListCap;
   if (ok) {
 #pragma unroll
     for (int u = 0; u < PERT; ++u) {
@@ -837,6 +905,9 @@ size_t dec_layout(int32_t nseq, int32_t cap, DecWs* W, int32_t** flags, void* ws
   w.n_part = (cap + DT - 1) / DT;
   w.hpart = reinterpret_cast<int32_t*>(take((size_t)nseq * w.n_part * NBIN * sizeof(int32_t)));
   w.supmask = reinterpret_cast<uint32_t*>(take((size_t)nseq * kSupMaskWords * sizeof(uint32_t)));
+  w.above = reinterpret_cast<int32_t*>(take((size_t)nseq * sizeof(int32_t)));
+  w.cand = reinterpret_cast<long long*>(take((size_t)nseq * PERT_MAX * BCAP * sizeof(long long)));
+  w.ncand = reinterpret_cast<int32_t*>(take((size_t)nseq * PERT_MAX * sizeof(int32_t)));
   int32_t* f = reinterpret_cast<int32_t*>(take((size_t)nseq * sizeof(int32_t)));
   if (W) *W = w;
   if (flags) *flags = f;
@@ -913,33 +984,46 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   }
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t ae = once_per_device(attr_done, []() {
-    hipError_t e = hipFuncSetAttribute((const void*)k_dec_select<20>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_dec_select<20, true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(20));
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)k_dec_select<PERT_MAX>,
+    return hipFuncSetAttribute((const void*)k_dec_select<PERT_MAX, true>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(PERT_MAX));
   });
   if (ae != hipSuccess) return ae;
+  // one workgroup per slice of DT buckets of each sequence, then one per
+  // sequence to finish its row (the slice kernel's LDS: two lists of DT)
+  constexpr int kSliceLds = 2 * DT * 4;
+  const unsigned nslx = (unsigned)max(1, min((nmax + DT - 1) / DT, PERT_MAX));
   if (big) {
     // sequences above DT * PERT_MAX buckets: the streaming kernel (the other
-    // kernel flags them and returns; this one overwrites their flags); any
+    // kernels flag them and return; this one overwrites their flags); any
     // sequence flagged then goes to the exact kernel
     ae = once_per_device(big_done, big_attr);
     if (ae != hipSuccess) return ae;
-    if (nmin <= DT * PERT_MAX)
-      hipLaunchKernelGGL(k_dec_select<PERT_MAX>, dim3((unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s, vs, b,
-                         W, flags);
+    if (nmin <= DT * PERT_MAX) {
+      hipLaunchKernelGGL((k_dec_select<PERT_MAX, false>), dim3(nslx, (unsigned)nseq), dim3(DT), kSliceLds, s,
+                         vs, b, W, flags);
+      hipLaunchKernelGGL((k_dec_select<PERT_MAX, true>), dim3(1, (unsigned)nseq), dim3(DT), dec_lds(PERT_MAX),
+                         s, vs, b, W, flags);
+    }
     hipLaunchKernelGGL(k_dec_select_big, dim3((unsigned)nseq), dim3(DT), BIG_LDS, s, vs, b, W, flags, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     b.only = flags;
     return launch_select_multi(views, qpos, nseq, b, s);
   }
-  if (small)
-    hipLaunchKernelGGL(k_dec_select<20>, dim3((unsigned)nseq), dim3(DT), dec_lds(20), s, vs, b, W, flags);
-  else
-    hipLaunchKernelGGL(k_dec_select<PERT_MAX>, dim3((unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s, vs, b,
-                       W, flags);
+  if (small) {
+    hipLaunchKernelGGL((k_dec_select<20, false>), dim3(nslx, (unsigned)nseq), dim3(DT), kSliceLds, s, vs, b, W,
+                       flags);
+    hipLaunchKernelGGL((k_dec_select<20, true>), dim3(1, (unsigned)nseq), dim3(DT), dec_lds(20), s, vs, b, W,
+                       flags);
+  } else {
+    hipLaunchKernelGGL((k_dec_select<PERT_MAX, false>), dim3(nslx, (unsigned)nseq), dim3(DT), kSliceLds, s, vs,
+                       b, W, flags);
+    hipLaunchKernelGGL((k_dec_select<PERT_MAX, true>), dim3(1, (unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s,
+                       vs, b, W, flags);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // The bracket always fits: every refinement pass narrows the key range by

@@ -15,9 +15,9 @@
 //      mean and max; the threshold slo is set where the sample predicts
 //      about twice the budget above it;
 //   3. full pass: every (query, bucket) with score >= slo is appended to the
-//      query's list -- 64 sub-lists per query, one per bucket id residue
-//      mod 64, each filled in ascending id order by a single lane (no
-//      atomics).
+//      query's list, one contiguous array per query with its length in LDS
+//      (a workgroup keeps one partly written line per query open, so the L2
+//      merges the rare 8-byte appends into whole lines).
 //   The centroids and bucket sizes stream through LDS in double-buffered
 //   chunks (each centroid byte is read once per workgroup, all lanes keep
 //   loads in flight) and the full pass is MFMA + compare + rare store.
@@ -46,9 +46,7 @@ using namespace sel;
 
 constexpr int CHT = 16;             // centroid tiles (16 buckets each) per staged chunk
 constexpr int NB2 = 32;             // sample histogram bins
-constexpr int NSUB = 64;            // sub-lists per query (bucket id mod 64)
-constexpr int LC = 8192;            // list entries per query slot (128 per sub-list)
-constexpr int SUBCAP = LC / NSUB;
+constexpr int LC = 8192;            // list entries per query slot
 constexpr int RB = 256;             // list histogram bins
 constexpr int RCAP = 256;           // bracket entries resolved by sorting
 constexpr int ECAP = 1024;          // taken buckets per query (else the exact kernel)
@@ -62,10 +60,10 @@ struct FastViews {                  // first kernel argument (read through the k
 };
 
 struct ListWs {
-  long long* key;     // [slots][LC] order keys, sub-list j entry k at k*64 + j
+  long long* key;     // [slots][LC] order keys
   int32_t* elig;      // [slots][LC] eligible keys, then the taken keys
   int32_t* kstart;    // [slots][LC] member slot * p + offset of the first eligible key
-  int32_t* nsub;      // [slots][64] sub-list sizes
+  int32_t* nlist;     // [slots] list lengths (may exceed LC: overflow)
   int32_t* meta;      // [slots][3]  query index (-1: empty slot), position, 1: the list holds
                       //             every bucket with an eligible key
   int32_t* flags;     // [nq] 1: recompute with the exact kernel
@@ -86,9 +84,10 @@ struct __attribute__((aligned(16))) ScanLds {
   int smax[QS];
   int sn[QS];
   int slo[QS];
+  int rhi[QS], rsh[QS], rabove[QS], rtarget[QS];   // second-level bins of the crossing bin
   long long ssum[QS];
   int hist[QS][NB2];
-  int nl[QS][NSUB];                 // sub-list sizes
+  int nl[QS];                       // list lengths
   v4i cent[2][CHT * 64];
   int cnt[2][CHT * 16];
   int2 fl[2][CHT * 16];             // first and last key position of each bucket (causal only)
@@ -98,7 +97,9 @@ struct __attribute__((aligned(16))) ScanLds {
 // staged in LDS buffer buf.  Two later chunks are in flight in registers
 // while f runs (stages A and B take turns, so no register copy waits on a
 // load), and each goes to the other LDS buffer after f.
-template <int FW, int QS, class F>
+// DENSE: the "centroids" are the latent keys themselves, each its own bucket
+// of one key (pool 1): no bucket records are read.
+template <bool DENSE, int FW, int QS, class F>
 __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>& S, int c0,
                                               int step, int nchunks, bool causal, F&& f) {
   using C = Cfg<FW, QS>;
@@ -121,11 +122,12 @@ __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>&
     }
     const int bb = c * CHT * 16 + tid;
     const bool in = tid < CHT * 16 && bb < V.n_bkt;
-    st.rc = in ? V.bcnt[bb] : 0;
+    st.rc = in ? (DENSE ? 1 : V.bcnt[bb]) : 0;
     // without causal staging every bucket reads as eligible from key 0 (the
     // rule the threshold used before a query could precede most of the index)
-    st.rfl = (in && causal) ? make_int2(V.bfirst[bb] * V.pool, V.blast[bb] * V.pool + V.pool - 1)
-                            : make_int2(0, 0);
+    if (DENSE) st.rfl = (in && causal) ? make_int2(bb, bb) : make_int2(0, 0);
+    else st.rfl = (in && causal) ? make_int2(V.bfirst[bb] * V.pool, V.blast[bb] * V.pool + V.pool - 1)
+                                 : make_int2(0, 0);
   };
   auto swrite = [&](const Stage& st, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -159,8 +161,11 @@ __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>&
   }
 }
 
-// Prefill over one index: slot s of workgroup b is query b*QS + s.
-template <int FW, int QS>
+// Prefill over one index: slot s of workgroup b is query b*QS + s.  DENSE:
+// the quadratic comparator (every long-range key scored on its own latent);
+// only eligible keys join the lists, and the sample is denser (the cut is a
+// few thousand keys out of millions).
+template <int FW, int QS, bool DENSE>
 __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListWs W) {
   using C = Cfg<FW, QS>;
   __shared__ ScanLds<FW, QS> S;
@@ -184,7 +189,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     W.meta[3 * (lbase + i) + 1] = t;
   }
   for (int e = tid; e < QS * NB2; e += C::FT) (&S.hist[0][0])[e] = 0;
-  for (int e = tid; e < QS * NSUB; e += C::FT) (&S.nl[0][0])[e] = 0;
+  for (int e = tid; e < QS; e += C::FT) S.nl[e] = 0;
   __syncthreads();
 
   // Causal staging (each bucket's key range, so the threshold counts only the
@@ -208,7 +213,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   }
   const int ntiles = (V.n_bkt + 15) >> 4;
   const int nchunks = (ntiles + CHT - 1) / CHT;
-  const int sstep = max(1, nchunks / SAMPLE_CHUNKS);
+  const int sstep = max(1, nchunks / (DENSE ? 10 * SAMPLE_CHUNKS : SAMPLE_CHUNKS));
   bool act[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) act[v] = S.t[qrow + v] >= 0;
@@ -221,7 +226,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   {
     int smax[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, sn[4] = {0, 0, 0, 0};
     long long ssum[4] = {0, 0, 0, 0};
-    stream_chunks(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
+    stream_chunks<DENSE>(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
       for (int tl = phase; tl < CHT; tl += C::PH) {
         const v4i z = {0, 0, 0, 0};
         const v4i sc = mfma_i8_16x16x64(qa, S.cent[buf][tl * 64 + lane], z);
@@ -247,7 +252,30 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     __syncthreads();
   }
 
-  // ---- 2. sampled key-count histogram in [mean, max] -> threshold ----
+  // ---- 2. sampled key-count histograms -> threshold ----
+  // The sampled buckets' keys are binned by score (NB2 bins), first over
+  // [mean, max]; the bin where the count from the top reaches the target is
+  // then binned again, NB2 times finer, in a second sampled pass, so the
+  // threshold sits within 1/NB2^2 of that range of the predicted cut.  A
+  // bucket counts with all its keys when they are all long-range for the
+  // query (the index may hold keys past it), else not at all.
+  auto sample_hist = [&](const int (&lo)[4], const int (&hi)[4], const int (&sh)[4]) __attribute__((always_inline)) {
+    stream_chunks<DENSE>(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
+      for (int tl = phase; tl < CHT; tl += C::PH) {
+        const v4i z = {0, 0, 0, 0};
+        const v4i sc = mfma_i8_16x16x64(qa, S.cent[buf][tl * 64 + lane], z);
+        const int w = S.cnt[buf][tl * 16 + col] * p;
+        const int kl = S.fl[buf][tl * 16 + col].y;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tv = v == 0 ? tl0 : v == 1 ? tl1 : v == 2 ? tl2 : tl3;
+          if (sc[v] >= lo[v] && sc[v] <= hi[v] && w > 0 && kl <= tv)
+            atomicAdd(&S.hist[qrow + v][(hi[v] - sc[v]) >> sh[v]], w);
+        }
+      }
+    });
+  };
+  constexpr int TAKE_ALL = -(1 << 30);
   {
     int lo[4], hi[4], sh[4];
 #pragma unroll
@@ -261,28 +289,13 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
         while (s < 30 && (((hi[v] - lo[v] + 1) + (1 << s) - 1) >> s) > NB2) ++s;
       sh[v] = s;
     }
-    stream_chunks(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
-      for (int tl = phase; tl < CHT; tl += C::PH) {
-        const v4i z = {0, 0, 0, 0};
-        const v4i sc = mfma_i8_16x16x64(qa, S.cent[buf][tl * 64 + lane], z);
-        // a bucket counts with all its keys when they are all long-range for
-        // the query (the index may hold keys past it), else not at all
-        const int w = S.cnt[buf][tl * 16 + col] * p;
-        const int kl = S.fl[buf][tl * 16 + col].y;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tv = v == 0 ? tl0 : v == 1 ? tl1 : v == 2 ? tl2 : tl3;
-          if (sc[v] >= lo[v] && w > 0 && kl <= tv)
-            atomicAdd(&S.hist[qrow + v][(hi[v] - sc[v]) >> sh[v]], w);
-        }
-      }
-    });
+    sample_hist(lo, hi, sh);
     // A query whose sample does not reach the target within [mean, max] takes
     // every bucket with an eligible key into its list (TAKE_ALL: any score
     // passes), and its list is then complete.
-    constexpr int TAKE_ALL = -(1 << 30);
     for (int qs = tid; qs < QS; qs += C::FT) {
       int slo = INT_MAX, all = 0;
+      S.rsh[qs] = -1;                  // no second-level pass
       if (S.t[qs] >= 0) {
         slo = TAKE_ALL;
         all = 1;
@@ -292,16 +305,60 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           int s = 0;
           while (s < 30 && (((mx - mn + 1) + (1 << s) - 1) >> s) > NB2) ++s;
           const int sampled = (nchunks + sstep - 1) / sstep;
-          const long long target = (2ll * budget_at(A, S.t[qs]) * sampled + nchunks - 1) / nchunks;
+          // twice the budget (Flat: buckets hold tens of keys, so the list is a
+          // few hundred entries); 1.5 times for the dense scan, whose entries
+          // are single keys and whose list holds LC of them
+          const long long want = DENSE ? 3ll * budget_at(A, S.t[qs]) / 2 : 2ll * budget_at(A, S.t[qs]);
+          const long long target = (want * sampled + nchunks - 1) / nchunks;
           long long cum = 0;
           for (int b = 0; b < NB2; ++b) {
-            cum += S.hist[qs][b];
-            if (cum >= target) { slo = max(mn, mx - ((b + 1) << s) + 1); all = 0; break; }
+            const int hb = S.hist[qs][b];
+            cum += hb;
+            if (cum >= target) {
+              slo = max(mn, mx - ((b + 1) << s) + 1);
+              all = 0;
+              if (s > 0) {             // the crossing bin [slo, mx - (b << s)], binned finer
+                const int bhi = mx - (b << s);
+                int s2 = 0;
+                while (s2 < 30 && (((bhi - slo + 1) + (1 << s2) - 1) >> s2) > NB2) ++s2;
+                S.rhi[qs] = bhi; S.rsh[qs] = s2;
+                S.rabove[qs] = (int)min(cum - hb, (long long)INT_MAX);
+                S.rtarget[qs] = (int)min(target, (long long)INT_MAX);
+              }
+              break;
+            }
           }
         }
       }
       S.slo[qs] = slo;
       W.meta[3 * (lbase + qs) + 2] = all;
+    }
+    __syncthreads();
+  }
+  {
+    // second-level bins of each query's crossing bin (queries without one
+    // take part with an empty range)
+    for (int e = tid; e < QS * NB2; e += C::FT) (&S.hist[0][0])[e] = 0;
+    __syncthreads();
+    int lo[4], hi[4], sh[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qs = qrow + v;
+      const bool two = act[v] && S.rsh[qs] >= 0;
+      lo[v] = two ? S.slo[qs] : INT_MAX;
+      hi[v] = two ? S.rhi[qs] : INT_MIN;
+      sh[v] = two ? S.rsh[qs] : 0;
+    }
+    sample_hist(lo, hi, sh);
+    __syncthreads();
+    for (int qs = tid; qs < QS; qs += C::FT) {
+      if (S.t[qs] < 0 || S.rsh[qs] < 0) continue;
+      long long cum = S.rabove[qs];
+      const int bhi = S.rhi[qs], s2 = S.rsh[qs];
+      for (int b = 0; b < NB2; ++b) {
+        cum += S.hist[qs][b];
+        if (cum >= S.rtarget[qs]) { S.slo[qs] = max(S.slo[qs], bhi - ((b + 1) << s2) + 1); break; }
+      }
     }
     __syncthreads();
   }
@@ -311,8 +368,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   // its result is >= 0.  Per group of four tiles a lane folds the sign bits
   // of its 16 results into a mask (one alignbit each); only lanes with hits
   // loop over them (about one pair in a hundred), picking the result with a
-  // select tree and taking a slot of the sub-list (bucket id mod 64) from an
-  // LDS counter.
+  // select tree and taking the query's next list slot from an LDS counter.
   {
     constexpr int TPW = CHT / C::PH;    // this wave's tiles per chunk: phase, phase + PH, ...
     static_assert(TPW % 4 == 0, "the full pass takes groups of four of a wave's tiles");
@@ -323,7 +379,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
       slo[v] = act[v] ? S.slo[qrow + v] : (1 << 30);    // 1<<30: no score reaches it
       bias[v] = -slo[v];
     }
-    stream_chunks(V, S, 0, 1, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
+    stream_chunks<DENSE>(V, S, 0, 1, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < TPW; g += 4) {
         int d[16];
@@ -362,18 +418,17 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           const int tv = S.t[qrow + v] - A.window;   // (hits are rare: an LDS read is cheap)
           const int beta = (tb + C::PH * u) * 16 + col;
           // a bucket whose first key is past the query's long-range range has no
-          // eligible key (first pooled id of bucket beta: chunk-local slot beta - c*CHT*16)
-          if (S.fl[buf][beta - c * CHT * 16].x <= tv) {
-            const int jl = beta & (NSUB - 1);
+          // eligible key (first pooled id of bucket beta: chunk-local slot beta - c*CHT*16);
+          // a dense key joins only when it is eligible itself
+          if (DENSE ? (beta >= A.sinks && beta <= tv) : S.fl[buf][beta - c * CHT * 16].x <= tv) {
             const int qs = qrow + v;
-            const int pos = atomicAdd(&S.nl[qs][jl], 1);
-            if (pos < SUBCAP) W.key[(lbase + qs) * LC + (int64_t)pos * NSUB + jl] = order_key(dk + sv, beta);
+            const int pos = atomicAdd(&S.nl[qs], 1);
+            if (pos < LC) W.key[(lbase + qs) * LC + pos] = order_key(dk + sv, beta);
           }
         }
       }
     });
-    for (int e = tid; e < QS * NSUB; e += C::FT)
-      W.nsub[(lbase + e / NSUB) * NSUB + e % NSUB] = (&S.nl[0][0])[e];
+    for (int e = tid; e < QS; e += C::FT) W.nlist[lbase + e] = S.nl[e];
   }
 }
 
@@ -691,7 +746,6 @@ __device__ __forceinline__ bool select_and_emit(ResolveLds& L, const IdxView& V,
 
 __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, ListWs W) {
   __shared__ ResolveLds L;
-  __shared__ int s_pre[NSUB + 1];    // entries before sub-list j
   const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int64_t slot = blockIdx.x;
@@ -703,19 +757,10 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
   const int B = budget_at(A, t);
   const int p = V.pool;
   const long long* lk = W.key + slot * LC;
-  int len = 0;
-  if (wave == 0) {
-    len = W.nsub[slot * NSUB + lane];
-    int all;
-    const int ex = wave_excl_scan(min(len, SUBCAP), &all);
-    s_pre[lane] = ex;
-    if (lane == 63) s_pre[NSUB] = all;
-  }
+  const int ntot = W.nlist[slot];
   if (tid == 0) { L.nc = 0; L.nt = 0; }
-  // a sub-list that overflowed, or more entries than the registers hold: exact kernel
-  bool ok = __syncthreads_or(len > SUBCAP) == 0;
-  const int ntot = s_pre[NSUB];
-  ok = ok && B > 0 && ntot <= KCAP;
+  // more entries than the registers hold (or than the list kept): exact kernel
+  bool ok = B > 0 && ntot <= KCAP;
 
   // entries, their eligible keys and first key slots (all loads of a thread in flight together)
   // (the first key slot of entry f goes to kstart[f])
@@ -725,16 +770,8 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
   if (ok) {
 #pragma unroll
     for (int u = 0; u < TPQ; ++u) {
-      const int f = tid + RT * u;    // entry number -> (sub-list a, position f - s_pre[a])
-      K[u] = LLONG_MIN;
-      if (f < ntot) {
-        int a = 0, b = NSUB - 1;     // last sub-list starting at or before f
-        while (a < b) {
-          const int m = (a + b + 1) >> 1;
-          if (s_pre[m] <= f) a = m; else b = m - 1;
-        }
-        K[u] = lk[(f - s_pre[a]) * NSUB + a];
-      }
+      const int f = tid + RT * u;
+      K[u] = f < ntot ? lk[f] : LLONG_MIN;
     }
     BucketInfo bi[TPQ];
 #pragma unroll
@@ -761,6 +798,157 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
   ok = select_and_emit<TPQ>(L, V, A, q, t, ok, K, e, lo, hi, tot, complete,
                            [&](int u) { return W.kstart[slot * LC + tid + RT * u]; });
   if (tid == 0) W.flags[q] = ok ? 0 : 1;
+}
+
+// Dense comparator resolve: one RT-thread workgroup per query slot.  Each
+// list entry is one eligible key with its order key (score desc, position
+// asc); the query keeps its budget's largest keys.  A histogram bracket
+// narrows to at most RCAP entries around the cutoff, which one wave sorts;
+// the kept keys are sorted by position and written, then the sinks and the
+// window.  A list that overflowed, or holds fewer than the budget without
+// being complete, flags the query for the exact kernel.
+constexpr int DPT = LC / RT;        // list entries per thread
+constexpr int DKEEP = 4096;         // budget <= 4096
+static_assert(DKEEP % RT == 0, "kept keys sort");
+
+__global__ void __launch_bounds__(RT) k_dense_resolve(SelArgs A, ListWs W) {
+  __shared__ int s_h[RB];
+  __shared__ long long s_red[RT / 64];
+  __shared__ int s_ired[RT / 64];
+  __shared__ long long s_cq[RCAP];
+  __shared__ int s_nc, s_cut;
+  __shared__ int s_keys[DKEEP];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int64_t slot = blockIdx.x;
+  const int q = W.meta[3 * slot];
+  if (q < 0) return;                 // uniform over the workgroup
+  const int t = W.meta[3 * slot + 1];
+  const bool complete = W.meta[3 * slot + 2] != 0;
+  const int B = budget_at(A, t);
+  const int ntot = W.nlist[slot];
+  if (ntot > LC || (ntot < B && !complete)) {
+    if (tid == 0) W.flags[q] = 1;
+    return;
+  }
+  const long long* lk = W.key + slot * LC;
+  long long K[DPT];
+#pragma unroll
+  for (int u = 0; u < DPT; ++u) {
+    const int f = tid + RT * u;
+    K[u] = f < ntot ? lk[f] : LLONG_MIN;
+  }
+  const int take = min(B, ntot);
+  long long cut = LLONG_MIN + 1;     // keys >= cut are kept; padding (LLONG_MIN) never is
+  if (take < ntot) {
+    long long lo = LLONG_MAX, hi = LLONG_MIN;
+#pragma unroll
+    for (int u = 0; u < DPT; ++u) {
+      if (K[u] == LLONG_MIN) continue;
+      lo = min(lo, K[u]);
+      hi = max(hi, K[u]);
+    }
+    lo = block_min_ll<RT>(lo, s_red);
+    hi = block_max_ll<RT>(hi, s_red);
+    for (int pass = 0; pass < 8; ++pass) {
+      const long long range = hi - lo + 1;
+      int sh = 0;
+      while (sh < 62 && ((range + (1ll << sh) - 1) >> sh) > RB) ++sh;
+      for (int i = tid; i < RB; i += RT) s_h[i] = 0;
+      __syncthreads();
+      long long ab = 0;
+#pragma unroll
+      for (int u = 0; u < DPT; ++u) {
+        if (K[u] == LLONG_MIN) continue;
+        if (K[u] > hi) { ++ab; continue; }
+        if (K[u] >= lo) atomicAdd(&s_h[(int)((hi - K[u]) >> sh)], 1);
+      }
+      ab = block_sum_ll<RT>(ab, s_red);
+      if (wave == 0) {
+        int h[RB / 64], loc = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) { h[k] = s_h[(RB / 64) * lane + k]; loc += h[k]; }
+        int wt;
+        const int ex = wave_excl_scan(loc, &wt);
+        long long cum = ab + ex;
+        int found = -1, fb = 0;
+#pragma unroll
+        for (int k = 0; k < RB / 64; ++k) {
+          if (found < 0 && cum + h[k] >= take) { found = (RB / 64) * lane + k; fb = h[k]; }
+          cum += h[k];
+        }
+        const unsigned long long mk = __ballot(found >= 0);
+        const int src = mk ? __ffsll((long long)mk) - 1 : 0;
+        const int bsel = __shfl(found, src), nbsel = __shfl(fb, src);
+        if (lane == 0) { s_cut = bsel; s_nc = nbsel; }
+      }
+      __syncthreads();
+      const int bin = s_cut, nb = s_nc;
+      __syncthreads();
+      // (the bracket always holds the cutoff: bin >= 0)
+      const long long nhi = hi - ((long long)bin << sh);
+      long long nlo = hi - ((long long)(bin + 1) << sh) + 1;
+      if (nlo < lo) nlo = lo;
+      lo = nlo;
+      hi = nhi;
+      if (nb <= RCAP) break;
+    }
+    // the bracket's entries, sorted descending; the cutoff is the one that
+    // completes `take` with the entries above the bracket
+    if (tid == 0) s_nc = 0;
+    __syncthreads();
+    long long ab = 0;
+#pragma unroll
+    for (int u = 0; u < DPT; ++u) {
+      if (K[u] == LLONG_MIN) continue;
+      if (K[u] > hi) { ++ab; continue; }
+      if (K[u] >= lo) {
+        const int c = atomicAdd(&s_nc, 1);
+        if (c < RCAP) s_cq[c] = -K[u];
+      }
+    }
+    ab = block_sum_ll<RT>(ab, s_red);
+    const int nc = min(s_nc, RCAP);
+    if (wave == 0) {
+      int np = 1;
+      while (np < nc) np <<= 1;
+      for (int i = nc + lane; i < np; i += 64) s_cq[i] = LLONG_MAX;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      wave_bitonic(s_cq, np);
+    }
+    __syncthreads();
+    cut = -s_cq[take - (int)ab - 1];
+  }
+  // kept keys, compacted in thread order, then sorted by position
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < DPT; ++u) mine += K[u] >= cut ? 1 : 0;
+  int total;
+  int at = block_excl_scan<RT>(mine, s_ired, &total);
+#pragma unroll
+  for (int u = 0; u < DPT; ++u)
+    if (K[u] >= cut) s_keys[at++] = (int)(0xffffffffu - (unsigned)(K[u] & 0xffffffffll));
+  __syncthreads();
+  constexpr int KPT = DKEEP / RT;
+  int v[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) v[i] = tid * KPT + i < total ? s_keys[tid * KPT + i] : INT_MAX;
+  block_bitonic<DKEEP>(v, s_keys);
+  int32_t* row = A.idx + (int64_t)q * A.max_sel;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (tid * KPT + i < total) row[tid * KPT + i] = v[i];
+  if (wave == 0) {
+    const int wstart = max(0, t - A.window + 1);
+    const int ns = max(0, min(A.sinks, wstart));
+    const int nw = t - wstart + 1;
+    for (int k = lane; k < ns; k += 64) row[total + k] = k;
+    for (int k = lane; k < nw; k += 64) row[total + ns + k] = wstart + k;
+    const int totalk = total + ns + nw;
+    for (int k = totalk + lane; k < A.max_sel; k += 64) row[k] = -1;
+    if (lane == 0) A.cnt[q] = totalk;
+  }
+  if (tid == 0) W.flags[q] = 0;
 }
 
 // Tree selection ("Prefrontal's Latent Sparse Attention speeds up one
@@ -1051,7 +1239,7 @@ size_t ws_layout(size_t slots, size_t nq, ListWs* W, void* base) {
   w.key = reinterpret_cast<long long*>(take(slots * LC * sizeof(long long)));
   w.elig = reinterpret_cast<int32_t*>(take(slots * LC * sizeof(int32_t)));
   w.kstart = reinterpret_cast<int32_t*>(take(slots * LC * sizeof(int32_t)));
-  w.nsub = reinterpret_cast<int32_t*>(take(slots * NSUB * sizeof(int32_t)));
+  w.nlist = reinterpret_cast<int32_t*>(take(slots * sizeof(int32_t)));
   w.meta = reinterpret_cast<int32_t*>(take(slots * 3 * sizeof(int32_t)));
   w.flags = reinterpret_cast<int32_t*>(take(nq * sizeof(int32_t)));
   if (W) *W = w;
@@ -1074,7 +1262,19 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
   memset(&vs, 0, sizeof vs);
   vs.v[0] = v;
   vs.nviews = 1;
-  hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ>), dim3((unsigned)(slots / kPrefQ)), dim3(kPrefW * 64),
+  if (v.dense) {
+    hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ, true>), dim3((unsigned)(slots / kPrefQ)), dim3(kPrefW * 64),
+                       0, s, vs, a, W);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_dense_resolve, dim3((unsigned)slots), dim3(RT), 0, s, a, W);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SelArgs b = a;
+    b.only = W.flags;
+    return launch_select(v, b, nullptr, s);
+  }
+  hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ, false>), dim3((unsigned)(slots / kPrefQ)), dim3(kPrefW * 64),
                      0, s, vs, a, W);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -175,7 +175,9 @@ LSA_API int lsa_workspace_bytes(int op, const lsa_index_params* iprm,
                                 int64_t n, size_t* bytes);
 
 /* Build the index over keys [0, T) from scratch (pool, block k-means, tail
- * singletons, Tree super level).  d_latk: int8 [T][64]. */
+ * singletons, Tree super level).  d_latk: int8 [T][64], 16-byte aligned
+ * (LSA_E_ARG otherwise; the same holds for the latent keys of
+ * lsa_append_keys, lsa_prefill_chunk and lsa_decode_step). */
 LSA_API int lsa_build_index(lsa_index* h, const int8_t* d_latk, int64_t T, void* d_ws,
                             size_t ws_bytes, void* stream);
 
@@ -285,7 +287,7 @@ LSA_API int lsa_decode_step(lsa_index* const* hs, int32_t nseq, const int8_t* d_
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments and results as lsa_decode_step, without the
  * workspace: the step runs in a device array inside the library, one per
- * GPU, of lsa_decode_step_noalloc_max_bytes() bytes (64 MiB), held until the
+ * GPU, of lsa_decode_step_noalloc_max_bytes() bytes (128 MiB), held until the
  * process ends.  A step that needs more workspace than that (see
  * lsa_workspace_bytes with LSA_OP_DECODE) returns LSA_E_CAPACITY and
  * enqueues nothing.  The call allocates nothing: no hipMalloc, no
@@ -302,7 +304,10 @@ LSA_API int lsa_decode_step_noalloc(lsa_index* const* hs, int32_t nseq, const in
 
 /* Quadratic comparator: every long-range key scored on its own latent
  * (q . latk[j]), best `budget` by (score desc, position asc), plus window
- * and sinks.  Same output format as lsa_select. */
+ * and sinks.  Same output format as lsa_select.  With a workspace of
+ * lsa_workspace_bytes(LSA_OP_DENSE, .., nq) bytes and nq >= 64 it runs as
+ * one thresholded int8-MFMA scan of all latents plus an exact top-budget per
+ * query; without, every query takes the exact refinement kernel. */
 LSA_API int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq,
                              const int32_t* d_qpos, int32_t nq, const lsa_select_params* sp,
                              int32_t* d_idx, int32_t* d_cnt, void* d_ws, size_t ws_bytes,
