@@ -3,10 +3,19 @@
 Each test runs the path the benchmark times (index prebuilt over the context
 before the chunk, then the fused prefill-chunk entry point; or 256 decode
 steps) and checks, against the CPU oracle built block by block in worker
-processes: every block's centroids and member lists bit-exactly, the
-selected key sets of a sample of queries bit-exactly, and the attention of a
-smaller sample within 2e-3 normwise (float32 output of the same kernel, with
-the bf16 output equal to its round-to-nearest-even).
+processes:
+* every block's centroids and member lists bit-exactly;
+* every selection row: the key count (min(t + 1, budget + window + sinks)),
+  distinct keys, causality, window and sinks present, -1 padding, and the
+  row equal to the GPU exact kernel's on the same index;
+* the selected key sets of 1024 queries bit-exactly against the oracle
+  (first, last and block-boundary queries included);
+* the attention of 1024 queries within 2e-3 normwise (float32 output of the
+  same kernel), with the bf16 output equal to its round-to-nearest-even;
+* decode: every (sequence, step) query of the 256 steps, selection and
+  attention.
+The oracle's selections and attention outputs are computed in the worker
+pool (oracle/parallel_refs.py).
 """
 import numpy as np
 import pytest
@@ -15,6 +24,7 @@ import torch
 import lsa_synth as S
 import oracle as O
 from oracle.parallel_build import build_cache_parallel
+from oracle.parallel_refs import decode_many, select_many
 
 from test_gpu_parity import (TOL, check_index, normwise, oracle_attention, rne_bf16_bits)
 
@@ -40,14 +50,18 @@ def _oparams(wl):
 def _sample_positions(wl, n_sel, seed):
     n, t0 = wl.chunk, wl.T - wl.chunk
     kpb = wl.pool * wl.block
-    fixed = [0, 1, n - 1, n - 2, kpb - 1, kpb, kpb + 1, n // 2 - 1, n // 2]
+    fixed = sorted(set(i for i in [0, 1, n - 1, n - 2, kpb - 1, kpb, kpb + 1, n // 2 - 1, n // 2]
+                       if 0 <= i < n))
     rng = np.random.default_rng(seed)
-    rest = rng.choice(n, n_sel - len(fixed), replace=False).tolist()
-    return sorted(set(i for i in fixed + rest if 0 <= i < n))
+    others = np.setdiff1d(np.arange(n), fixed)
+    rest = rng.choice(others, n_sel - len(fixed), replace=False).tolist()
+    return sorted(fixed + rest)
 
 
 def _gpu_prefill(wl, dev, out_f32_too=True, early=(0, 0)):
-    """The benchmarked step: prebuilt index, then lsa_prefill_chunk (bf16 out)."""
+    """The benchmarked step: prebuilt index, then lsa_prefill_chunk (bf16 out);
+    the same chunk again with a float32 output; and the exact selection
+    kernel's rows for the chunk's queries on the same index."""
     L = _L()
     g = S.Synth(wl)
     n, t0 = wl.chunk, wl.T - wl.chunk
@@ -74,32 +88,90 @@ def _gpu_prefill(wl, dev, out_f32_too=True, early=(0, 0)):
         ix.restore(snap)
         o32 = ix.prefill_chunk(latk[t0:], latq, q, K, V, sp,
                                L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0))
+    qpos = torch.arange(t0, wl.T, dtype=torch.int32, device=dev)
+    idx_x, cnt_x = ix.select(latq, qpos, sp, use_workspace=False)
     torch.cuda.synchronize()
     res = dict(g=g, idx=idx.cpu().numpy(), cnt=cnt.cpu().numpy(), o16=o16, o32=o32,
+               idx_exact=idx_x.cpu().numpy(), cnt_exact=cnt_x.cpu().numpy(),
                arrays={k: v.cpu() for k, v in ix.arrays().items()})
     del K, V, latk
     torch.cuda.empty_cache()
     return res
 
 
-def _check_prefill(wl, res, ref, n_sel, n_att, seed, early=(0, 0)):
+def oracle_attention_rows(g, wl, positions, sels, dev, label):
+    """Float64 oracle attention of the query at positions[i] over the rows
+    sels[i].  Q, K and V rows come from the workload's seeded generator run on
+    the device (the counter-based generator gives the same bits on the host,
+    checked here on the first query's rows), then the oracle runs on the host."""
+    out = []
+    for i, (t, sel) in enumerate(zip(positions, sels)):
+        rows = torch.from_numpy(np.asarray(sel, dtype=np.int64)).to(dev)
+        kb, vb = g.k_rows(rows, device=dev).cpu(), g.v_rows(rows, device=dev).cpu()
+        qb = g.q_rows(torch.tensor([t], device=dev), device=dev).cpu()
+        if i == 0:
+            r8 = torch.from_numpy(np.asarray(sel[:8], dtype=np.int64))
+            assert torch.equal(kb[:8].view(torch.int16), g.k_rows(r8).view(torch.int16))
+            assert torch.equal(vb[:8].view(torch.int16), g.v_rows(r8).view(torch.int16))
+            assert torch.equal(qb.view(torch.int16), g.q_rows(torch.tensor([t])).view(torch.int16))
+        K = O.bf16_to_f64(kb.view(torch.int16).numpy())
+        V = O.bf16_to_f64(vb.view(torch.int16).numpy())
+        q = O.bf16_to_f64(qb.view(torch.int16).numpy())[0]
+        out.append(O.attend(q, K, V, wl.Hkv))
+        if (i + 1) % 256 == 0:
+            print(f"  {label}: oracle attention {i + 1}/{len(positions)}", flush=True)
+    return np.stack(out)
+
+
+def check_rows(idx, cnt, positions, budgets, window, sinks):
+    """Every selection row: count = min(t + 1, budget + window + sinks),
+    distinct keys in [0, t], the window and the sinks present, -1 padding."""
+    t = np.asarray(positions, dtype=np.int64)
+    want = np.minimum(t + 1, np.asarray(budgets) + window + sinks)
+    assert np.array_equal(cnt, want), f"{int((cnt != want).sum())} rows with a wrong key count"
+    width = idx.shape[1]
+    live = np.arange(width)[None, :] < cnt[:, None]
+    assert (idx[~live] == -1).all(), "padding"
+    big = np.iinfo(np.int32).max
+    srt = np.sort(np.where(live, idx, big), axis=1)
+    assert (srt[:, 0] >= 0).all()
+    lv = np.arange(width)[None, :] < cnt[:, None]
+    assert (np.diff(srt, axis=1)[lv[:, 1:]] > 0).all(), "repeated keys"
+    last = np.take_along_axis(srt, (cnt - 1)[:, None].astype(np.int64), axis=1)[:, 0]
+    assert (last <= t).all(), "a key past its query"
+    in_win = (srt >= (t - window + 1)[:, None]) & (srt <= t[:, None])
+    assert np.array_equal(in_win.sum(1), np.minimum(window, t + 1)), "window"
+    assert np.array_equal((srt < sinks).sum(1), np.minimum(sinks, t + 1)), "sinks"
+
+
+def _check_prefill(wl, res, ref, pool, n_sel, n_att, seed, early=(0, 0)):
     n, t0 = wl.chunk, wl.T - wl.chunk
     check_index(res["arrays"], ref)
+    print(f"  {wl.name}: index bit-exact", flush=True)
     osp = O.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top, *early, wl.tree2_top)
+    positions = np.arange(t0, wl.T)
+    check_rows(res["idx"], res["cnt"], positions, [osp.budget_at(int(t)) for t in positions],
+               wl.window, wl.sinks)
+    assert np.array_equal(res["cnt"], res["cnt_exact"]) and np.array_equal(res["idx"], res["idx_exact"]), \
+        f"{int((res['idx'] != res['idx_exact']).any(1).sum())} rows differ from the exact kernel's"
+    print(f"  {wl.name}: all {n} rows valid and equal to the exact kernel's", flush=True)
     pos = _sample_positions(wl, n_sel, seed)
     latq = res["g"].latq_rows(torch.tensor([t0 + i for i in pos])).numpy()   # host-generated
-    sels = {}
-    for j, i in enumerate(pos):
-        ref_sel = O.select(ref, latq[j], t0 + i, osp)
+    sels = select_many(pool, ref, latq, [t0 + i for i in pos], osp)
+    for i, ref_sel in zip(pos, sels):
         got = np.sort(res["idx"][i, :res["cnt"][i]])
         assert np.array_equal(got, ref_sel), f"query at position {t0 + i}"
-        assert (res["idx"][i, res["cnt"][i]:] == -1).all()
-        sels[i] = ref_sel
+    print(f"  {wl.name}: {len(pos)} selections bit-exact", flush=True)
     att = pos[:: max(1, len(pos) // n_att)][:n_att]
-    refo = oracle_attention(res["g"], wl, [t0 + i for i in att], [sels[i] for i in att])
+    bysel = dict(zip(pos, sels))
+    refo = oracle_attention_rows(res["g"], wl, [t0 + i for i in att], [bysel[i] for i in att],
+                                 torch.device("cuda:0"), wl.name)
     o32 = res["o32"].cpu().numpy()[att].astype(np.float64)
     err = normwise(o32, refo)
-    print(f"{wl.name}: {len(pos)} selections bit-exact, attention normwise error {err:.3e}")
+    per_th = float((np.abs(o32 - refo).max(-1) / np.abs(refo).max(-1)).max())
+    print(f"{wl.name}: {n} rows checked (count, causality, window, sinks; equal to the exact kernel), "
+          f"{len(pos)} selections bit-exact, attention of {len(att)} queries: normwise error {err:.3e}, "
+          f"worst (token, head) {per_th:.3e}")
     assert err <= TOL
     o16 = res["o16"].view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(o16, rne_bf16_bits(res["o32"].cpu().numpy()))
@@ -115,13 +187,13 @@ def oracle_1m(oracle_pool):
 # (early_budget, early_until): the second keeps 2048 long-range keys for the
 # first half of the chunk and the full budget from the middle on
 @pytest.mark.parametrize("early", [(0, 0), (2048, (1 << 20) - (1 << 14))])
-def test_flat_1m_prefill_chunk(oracle_1m, early):
+def test_flat_1m_prefill_chunk(oracle_1m, oracle_pool, early):
     dev = _dev()
     wl = S.WORKLOADS["flat_1m"]
     res = _gpu_prefill(wl, dev, early=early)
     cache, latk = oracle_1m
     ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
-    _check_prefill(wl, res, ref, n_sel=160, n_att=24, seed=1 + early[0], early=early)
+    _check_prefill(wl, res, ref, oracle_pool, n_sel=1024, n_att=1024, seed=1 + early[0], early=early)
 
 
 @pytest.fixture(scope="module")
@@ -131,33 +203,33 @@ def oracle_10m(oracle_pool):
     return cache, latk
 
 
-def test_flat_10m_prefill_chunk(oracle_10m):
+def test_flat_10m_prefill_chunk(oracle_10m, oracle_pool):
     dev = _dev()
     wl = S.WORKLOADS["flat_10m"]
     res = _gpu_prefill(wl, dev)
     cache, latk = oracle_10m
     ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
-    _check_prefill(wl, res, ref, n_sel=128, n_att=16, seed=2)
+    _check_prefill(wl, res, ref, oracle_pool, n_sel=1024, n_att=1024, seed=2)
 
 
-def test_tree_10m_prefill_chunk(oracle_10m):
+def test_tree_10m_prefill_chunk(oracle_10m, oracle_pool):
     dev = _dev()
     wl = S.WORKLOADS["tree_10m"]
     res = _gpu_prefill(wl, dev)
     cache, latk = oracle_10m
     ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
     assert ref.n_grp == 10 and ref.sup_centroids.shape[0] == 640
-    _check_prefill(wl, res, ref, n_sel=96, n_att=12, seed=3)
+    _check_prefill(wl, res, ref, oracle_pool, n_sel=1024, n_att=1024, seed=3)
 
 
-def test_tree3_10m_prefill_chunk(oracle_10m):
+def test_tree3_10m_prefill_chunk(oracle_10m, oracle_pool):
     dev = _dev()
     wl = S.WORKLOADS["tree3_10m"]
     res = _gpu_prefill(wl, dev)
     cache, latk = oracle_10m
     ref = O.build_index(latk, wl.T, _oparams(wl), dict(cache))
     assert ref.n_grp2 == 2 and ref.top_centroids.shape[0] == 64
-    _check_prefill(wl, res, ref, n_sel=96, n_att=12, seed=4)
+    _check_prefill(wl, res, ref, oracle_pool, n_sel=256, n_att=256, seed=4)
 
 
 def test_decode_1m_256_steps(oracle_pool):
@@ -181,8 +253,7 @@ def test_decode_1m_256_steps(oracle_pool):
     ap32 = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
     wsb = L.workspace_bytes(L.binding.OP_DECODE, ixs[0].params, sp, ap32, wl.nseq)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    check_steps = {0, 1, 3, 4, wl.steps - 1}
-    got = {}
+    got = []
     new_pos = torch.arange(wl.T, cap, device=dev)
     lq_all = torch.stack([gens[i].latq_rows(new_pos, device=dev) for i in range(wl.nseq)], 1)
     q_all = torch.stack([gens[i].q_rows(new_pos, device=dev) for i in range(wl.nseq)], 1)
@@ -191,34 +262,44 @@ def test_decode_1m_256_steps(oracle_pool):
         lk_new = torch.stack([lats[i][t] for i in range(wl.nseq)]).contiguous()
         out = L.decode_step(ixs, lk_new, lq_all[s].contiguous(), q_all[s].contiguous(), K, V, cap,
                             sp, ap32, ws=ws)
-        if s in check_steps:
-            idx, cnt = L.decode_selection(ws, wl.nseq, sp)
-            got[s] = (idx.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy())
+        idx, cnt = L.decode_selection(ws, wl.nseq, sp)
+        got.append((idx.clone(), cnt.clone(), out.clone()))
     torch.cuda.synchronize()
+    got = [(a.cpu().numpy(), b.cpu().numpy(), c.cpu().numpy()) for a, b, c in got]
+    final_arrays = {k: v.cpu() for k, v in ixs[0].arrays().items()}
     del K, V, lats
     torch.cuda.empty_cache()
     osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
-    worst = 0.0
-    caches, lat_h = [], []
+    # every step's rows: count, causality, window, sinks, padding
+    for s in range(wl.steps):
+        idx, cnt, _ = got[s]
+        check_rows(idx, cnt, [wl.T + s] * wl.nseq, [wl.budget] * wl.nseq, wl.window, wl.sinks)
+    caches, lat0 = [], None
     for i in range(wl.nseq):
-        cache, lat0 = build_cache_parallel(wl.name, wl.T, oracle_pool, seq=i)   # host-generated
+        cache, lat_i = build_cache_parallel(wl.name, wl.T, oracle_pool, seq=i)   # host-generated
         caches.append(cache)
-        lat_h.append(np.concatenate([lat0, gens[i].latk(wl.T, cap).numpy()]))
-        for s in sorted(check_steps):
-            t = wl.T + s
-            ref = O.build_index(lat_h[i], t + 1, _oparams(wl), cache)
-            lq = gens[i].latq_rows(torch.tensor([t])).numpy()[0]
-            sel = O.select(ref, lq, t, osp)
+        print(f"  decode: sequence {i}: oracle blocks clustered", flush=True)
+        if i == 0:
+            lat0 = np.concatenate([lat_i, gens[0].latk(wl.T, cap).numpy()])
+    print("  decode: oracle indexes built", flush=True)
+    refs = decode_many(oracle_pool, wl.name, wl.T, wl.steps, _oparams(wl), osp, caches)
+    worst, worst_th = 0.0, 0.0
+    for i in range(wl.nseq):
+        sels = refs[i]
+        for s in range(wl.steps):
             idx, cnt, out = got[s]
-            assert np.array_equal(np.sort(idx[i, :cnt[i]]), sel), f"sequence {i} step {s}"
-            ro = oracle_attention(gens[i], wl, [t], [sel])[0]
-            worst = max(worst, normwise(out[i].astype(np.float64), ro))
-    print(f"decode: selections bit-exact at {len(check_steps)} steps x {wl.nseq} sequences, "
-          f"attention normwise error {worst:.3e}")
+            assert np.array_equal(np.sort(idx[i, :cnt[i]]), sels[s]), f"sequence {i} step {s}"
+        print(f"  decode: sequence {i}: {wl.steps} selections bit-exact", flush=True)
+        outs = oracle_attention_rows(gens[i], wl, [wl.T + s for s in range(wl.steps)], sels,
+                                     torch.device("cuda:0"), f"decode sequence {i}")
+        o = np.stack([got[s][2][i] for s in range(wl.steps)]).astype(np.float64)
+        worst = max(worst, normwise(o, outs))
+        worst_th = max(worst_th, float((np.abs(o - outs).max(-1) / np.abs(outs).max(-1)).max()))
+    print(f"decode: selections bit-exact at all {wl.steps} steps x {wl.nseq} sequences, attention "
+          f"normwise error {worst:.3e} (worst (token, head) {worst_th:.3e})")
     assert worst <= TOL
     # the last step's index equals the oracle's over all keys
-    check_index({k: v.cpu() for k, v in ixs[0].arrays().items()},
-                O.build_index(lat_h[0], cap, _oparams(wl), caches[0]))
+    check_index(final_arrays, O.build_index(lat0, cap, _oparams(wl), caches[0]))
 
 
 def test_tree_decode_2m_four_sequences(oracle_pool):

@@ -425,6 +425,34 @@ def test_dense_select_matches_oracle():
     check_selection(idx, cnt, refs, sp.max_sel)
 
 
+@pytest.mark.parametrize("early", [(0, 0), (150, 4000)])
+def test_dense_select_scan_path(early):
+    """The comparator's thresholded scan (batches of 64 or more queries with a
+    workspace) against the oracle and against the exact kernel, with queries
+    near the start of the context (lists that hold every eligible key) and
+    the position-dependent budget switching inside the batch."""
+    dev = _dev()
+    L = _L()
+    wl = S.WORKLOADS["tiny_flat"]
+    g = S.Synth(wl)
+    T = 12000
+    latk = g.latk(0, T)
+    rng = np.random.default_rng(81)
+    pos = sorted(set([5, 130, 131, 600, 1100, 3999, 4000, 4001, T - 1] + rng.integers(0, T, 180).tolist()))
+    lq = g.latq_rows(torch.tensor(pos))
+    sp = L.SelectParams(300, 128, 4, 0, *early)
+    osp = O.SelectParams(300, 128, 4, 0, *early)
+    qp = torch.tensor(pos, dtype=torch.int32, device=dev)
+    idx, cnt = L.dense_select(latk.to(dev), lq.to(dev), qp, sp)
+    refs = [O.dense_select(latk.numpy(), lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    check_selection(idx, cnt, refs, sp.max_sel)
+    idx2, cnt2 = L.dense_select(latk.to(dev), lq.to(dev), qp, sp, use_workspace=False)
+    assert torch.equal(cnt, cnt2)
+    for i in range(len(pos)):
+        n = int(cnt[i])
+        assert torch.equal(torch.sort(idx[i, :n]).values, torch.sort(idx2[i, :n]).values), pos[i]
+
+
 @pytest.mark.parametrize("tree_iters", [3, 1])
 def test_tree_index_and_selection(tree_iters):
     """Two-level Tree index and selections; the super level runs its own

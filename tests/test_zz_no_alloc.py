@@ -55,7 +55,12 @@ def test_noalloc_decode_matches_decode_step():
     Kd, Vd = K.to(dev), V.to(dev)
     sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
-    assert L.lib().lsa_decode_step_noalloc_max_bytes() == 64 << 20
+    assert L.lib().lsa_decode_step_noalloc_max_bytes() == 128 << 20
+    # the stated coverage: 16 sequences of 10 * 2^20 keys at 4096 + 512 + 4, GQA 32/8, D = 128
+    big = L.IndexParams(64, 4, 4096, 256, 4, 0, 0, 0, 10 * 2 ** 20 + 256)
+    need = L.workspace_bytes(L.binding.OP_DECODE, big, L.SelectParams(4096, 512, 4, 0),
+                             L.AttnParams(32, 8, 128, 0, 0.0), 16)
+    assert need <= L.lib().lsa_decode_step_noalloc_max_bytes()
     # call 1: all three sequences; call 2: a smaller batch (sequences 0 and 2)
     for step, members in ((0, [0, 1, 2]), (1, [0, 2])):
         t = wl.T + step
@@ -83,7 +88,7 @@ def test_noalloc_decode_refuses_an_oversized_step():
     dev = _dev()
     L = _L()
     wl = S.Workload("dec_noalloc_big", 63, T=600, ncomp=16, block=64, buckets=16, iters=2, chunk=0,
-                    budget=64, window=1 << 20, sinks=4, Hq=8, Hkv=2, D=128, nseq=16, steps=1)
+                    budget=64, window=1 << 20, sinks=4, Hq=16, Hkv=16, D=128, nseq=16, steps=1)
     g = S.Synth(wl, seq=0, data_cfg=63)
     lk = g.latk(0, wl.T + 1)
     ixs = []
