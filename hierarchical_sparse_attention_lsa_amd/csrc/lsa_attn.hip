@@ -110,8 +110,24 @@ __device__ __forceinline__ void tile_load(TileRegs<D>& T, const uint16_t* kbase,
   }
 }
 
+// The query operand of the QK^T MFMAs (B: lane l supplies column l % 16,
+// head-dim elements 32 kk + 8 (l / 16) ..), from registers or from LDS.
 template <int D>
-__device__ __forceinline__ void tile_compute(const v8bf (&qb)[D / 32], const TileRegs<D>& T,
+struct QRegs {
+  v8bf b[D / 32];
+  __device__ __forceinline__ v8bf operator()(int kk) const { return b[kk]; }
+};
+constexpr int qrow_bytes(int D) { return D * 2 + 16; }       // padded LDS row of one column
+template <int D>
+struct QLds {
+  const char* p;                    // this lane's column row + its 16-byte group
+  __device__ __forceinline__ v8bf operator()(int kk) const {
+    return *reinterpret_cast<const v8bf*>(p + 64 * kk);
+  }
+};
+
+template <int D, class QOp>
+__device__ __forceinline__ void tile_compute(const QOp& qb, const TileRegs<D>& T,
                                              unsigned vmask, float scale_log2, char* vl,
                                              v4f (&o)[D / 16], float& m_run, float& l_run) {
   constexpr int NKK = D / 32;
@@ -126,7 +142,7 @@ __device__ __forceinline__ void tile_compute(const v8bf (&qb)[D / 32], const Til
   // S^T[key][column]
   v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_16x16x32(T.ka[kk], qb[kk], s);
+  for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_16x16x32(T.ka[kk], qb(kk), s);
 
 #pragma unroll
   for (int i = 0; i < VLD; ++i) {
@@ -197,8 +213,8 @@ __device__ __forceinline__ void tile_compute(const v8bf (&qb)[D / 32], const Til
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
-__device__ __forceinline__ void attn_tile(const v8bf (&qb)[D / 32], const uint16_t* kbase,
+template <int D, class QOp>
+__device__ __forceinline__ void attn_tile(const QOp& qb, const uint16_t* kbase,
                                           const uint16_t* vbase, int64_t rowstride, int r,
                                           unsigned vmask, float scale_log2, char* vl,
                                           v4f (&o)[D / 16], float& m_run, float& l_run) {
@@ -232,14 +248,14 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
   const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
 
   // query heads of this group as the B operand (zero for padded heads)
-  v8bf qb[NKK];
+  QRegs<D> qb;
   {
     const bool hv = hl < G;
     const uint16_t* qp = a.q + ((int64_t)q * a.Hq + (int64_t)g * G + (hv ? hl : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       v4i raw = hv ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
-      qb[kk] = __builtin_bit_cast(v8bf, raw);
+      qb.b[kk] = __builtin_bit_cast(v8bf, raw);
     }
   }
 
@@ -296,6 +312,7 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   constexpr int NB = D / 16;
   constexpr int VROW = D * 2 + 16;
   __shared__ __attribute__((aligned(16))) char vlds[AW][KT * VROW];
+  __shared__ __attribute__((aligned(16))) char qlds[AW][16 * qrow_bytes(D)];
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -317,16 +334,22 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   const int64_t rowstride = (int64_t)a.Hkv * D;
   const int64_t rmax = a.kv_rows - 1;
 
-  // query operand: column hl = (query q0 + jc, head g*G + hc)
-  v8bf qb[NKK];
+  // query operand: column hl = (query q0 + jc, head g*G + hc), staged in
+  // this wave's LDS rows (registers held across the whole walk would leave
+  // too few for the K/V loads in flight)
+  char* ql = qlds[wave];
   {
     const uint16_t* qp = a.q + ((int64_t)(q0 + (cval ? jc : 0)) * a.Hq + (int64_t)g * G + hc) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       v4i raw = cval ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
-      qb[kk] = __builtin_bit_cast(v8bf, raw);
+      *reinterpret_cast<v4i*>(ql + hl * qrow_bytes(D) + (32 * kk + 8 * grp) * 2) = raw;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const QLds<D> qb{ql + hl * qrow_bytes(D) + 16 * grp};
 
   v4f o[NB];
 #pragma unroll
@@ -477,14 +500,14 @@ __global__ void __launch_bounds__(AT) k_attn_dec(AttnArgs a) {
     return m;
   };
 
-  v8bf qb[NKK];
+  QRegs<D> qb;
   {
     const bool hv = hl < G;
     const uint16_t* qp = a.q + ((int64_t)q * a.Hq + (int64_t)g * G + (hv ? hl : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       v4i raw = hv ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
-      qb[kk] = __builtin_bit_cast(v8bf, raw);
+      qb.b[kk] = __builtin_bit_cast(v8bf, raw);
     }
   }
   v4f o[NB];

@@ -96,19 +96,136 @@ __global__ void k_tail(const int8_t* __restrict__ pooled, int64_t g0, int64_t g1
 //   update   mu_c = round-half-even(sum of members / count) when non-empty
 // then writes a stable member list (members of each cluster in ascending
 // row order), counts, offsets, first/last member and the centroids.
-constexpr int kKmWaves = 8;
+constexpr int kKmWaves = 16;
 constexpr int kKmThreads = kKmWaves * 64;
 
 __host__ __device__ inline size_t kmeans_lds_bytes(int N, int C) {
   size_t b = 0;
   b += (size_t)C * kDim;                 // mu int8
-  b += (size_t)C * 4;                    // |mu|^2
+  b += (size_t)C * 4;                    // argmin key bias per centroid
   b += (size_t)C * kDim * 4;             // sums (reused for first/last rows)
   b += (size_t)C * 4;                    // counts
   b += (size_t)C * 4;                    // exclusive offsets
   b += (size_t)kKmWaves * C * 4;         // per-wave counts / cursors
   b += ((size_t)N * 2 + 15) / 16 * 16;   // assignments (uint16)
   return b;
+}
+
+// Argmin key of a (row x, centroid c) pair, larger = nearer:
+//   256 * (2 x.mu_c - |mu_c|^2) + (255 - c)
+// orders by |x - mu_c|^2 - |x|^2 = |mu_c|^2 - 2 x.mu_c ascending, then by c
+// ascending (C <= 256).  |x.mu_c| <= 64 * 128 * 128 = 2^20 and |mu_c|^2 <=
+// 2^20, so the key lies in (-2^30, 2^30).  km_bias(c) = 255 - c - 256 |mu_c|^2
+// is kept per centroid, and a key is one shift-add of the MFMA dot product.
+__device__ __forceinline__ int km_bias(const int8_t* m, int c) {
+  const int4* m4 = reinterpret_cast<const int4*>(m);
+  int sq = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int4 v = m4[k];
+    sq = __builtin_amdgcn_sdot4(v.x, v.x, sq, false);
+    sq = __builtin_amdgcn_sdot4(v.y, v.y, sq, false);
+    sq = __builtin_amdgcn_sdot4(v.z, v.z, sq, false);
+    sq = __builtin_amdgcn_sdot4(v.w, v.w, sq, false);
+  }
+  return 255 - c - 256 * sq;
+}
+__device__ __forceinline__ int km_key(int dot, int bias) { return (int)((unsigned)dot << 9) + bias; }
+
+// Nearest centroid (lowest index on ties) of the 16 rows of one tile: lane l
+// supplies the MFMA operand of row l % 16, bytes 16 * (l / 16) ..; every
+// lane of the 16-lane group g receives the clusters of rows 4g .. 4g + 3.
+__device__ __forceinline__ void km_nearest(v4i a, const int8_t* mu, const int* bias, int C, int cl[4]) {
+  const int lane = lane_id();
+  const int8_t* mp = mu + (lane & 15) * kDim + 16 * (lane >> 4);
+  const int* bp = bias + (lane & 15);
+  const v4i z = {0, 0, 0, 0};
+  int best[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+  const int nct = C >> 4;
+  int ct = 0;
+  for (; ct + 3 < nct; ct += 4) {
+    v4i bq[4], d[4];
+    int k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bq[u] = *reinterpret_cast<const v4i*>(mp + (ct + u) * 16 * kDim);
+      k[u] = bp[(ct + u) * 16];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[u] = mfma_i8_16x16x64(a, bq[u], z);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      best[v] = max(best[v], max(km_key(d[0][v], k[0]), km_key(d[1][v], k[1])));
+      best[v] = max(best[v], max(km_key(d[2][v], k[2]), km_key(d[3][v], k[3])));
+    }
+  }
+  for (; ct < nct; ++ct) {
+    const v4i b0 = *reinterpret_cast<const v4i*>(mp + ct * 16 * kDim);
+    const int k0 = bp[ct * 16];
+    const v4i d0 = mfma_i8_16x16x64(a, b0, z);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) best[v] = max(best[v], km_key(d0[v], k0));
+  }
+  // lane l holds centroid l % 16 of its group's rows: maximum over the 16
+  // lanes (quad swaps, then half-row and row mirrors)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    int x = best[v];
+    x = max(x, dpp_move<0xB1, 0xf>(INT_MIN, x));
+    x = max(x, dpp_move<0x4E, 0xf>(INT_MIN, x));
+    x = max(x, dpp_move<0x141, 0xf>(INT_MIN, x));
+    x = max(x, dpp_move<0x140, 0xf>(INT_MIN, x));
+    cl[v] = 255 - (x & 255);
+  }
+}
+
+// Cluster of the row whose operand this lane holds (row l % 16), from the
+// km_nearest results: that row's cluster sits in lanes 16 * (row / 4) ..,
+// value row % 4.
+__device__ __forceinline__ int km_row_cluster(const int cl[4]) {
+  const int lane = lane_id(), r = lane & 15;
+  // cl[lane % 4] as bit selects (a select over the array by a run-time index
+  // would be placed in scratch memory)
+  const int m0 = -(lane & 1), m1 = -((lane >> 1) & 1);
+  const int c0 = cl[0], c1 = cl[1], c2 = cl[2], c3 = cl[3];
+  const int x01 = c0 ^ ((c0 ^ c1) & m0), x23 = c2 ^ ((c2 ^ c3) & m0);
+  const int sel = x01 ^ ((x01 ^ x23) & m1);
+  return __shfl(sel, 16 * (r >> 2) + (r & 3));
+}
+
+// Cluster sums laid out [dim][cluster], the cluster index of dims 16g ..
+// 16g + 15 XOR-ed with 8g (within what C allows): the lanes of one LDS
+// atomic add to one dim of each group's rows, so the four groups adding to
+// the same cluster land on different banks.
+__device__ __forceinline__ int km_sum_at(int d, int c, int C) {
+  const int xm = (C & 31) ? 8 : 24;
+  return d * C + (c ^ (((d >> 4) << 3) & xm));
+}
+
+// The tile's 16 rows join their clusters' sums and counts, from the operand
+// bytes this lane holds (row l % 16, dims 16 * (l / 16) ..).
+__device__ __forceinline__ void km_accumulate(v4i a, int cr, int C, int* sums, int* counts) {
+  const int lane = lane_id(), g = lane >> 4;
+  if (lane < 16) atomicAdd(&counts[cr], 1);
+  int* sd = sums + km_sum_at(16 * g, cr, C);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int w4 = a[k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) atomicAdd(&sd[(4 * k + j) * C], (w4 << (24 - 8 * j)) >> 24);
+  }
+}
+
+// Round-half-even of s / n for |s| <= 128 n (a mean of int8 values), n > 0,
+// with rn ~ 1/n: |s/n| <= 128, so the float quotient is within 2^-14 of the
+// exact one and its floor within one of the exact floor; the remainder
+// corrects it.
+__device__ __forceinline__ int rhe_div_small(int s, int n, float rn) {
+  int q = (int)floorf((float)s * rn);
+  int r = s - q * n;
+  if (r < 0) { q -= 1; r += n; } else if (r >= n) { q += 1; r -= n; }
+  const int twice = 2 * r;
+  return q + ((twice > n) | ((twice == n) & (q & 1)));
 }
 
 // mu_in / asg_in (members mode, iters = 0): the final centroids and
@@ -123,8 +240,8 @@ k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0
          const uint16_t* __restrict__ asg_in) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int8_t* mu = reinterpret_cast<int8_t*>(smem);
-  int32_t* musq = reinterpret_cast<int32_t*>(mu + (size_t)C * kDim);
-  int32_t* sums = musq + C;
+  int32_t* bias = reinterpret_cast<int32_t*>(mu + (size_t)C * kDim);
+  int32_t* sums = bias + C;
   int32_t* counts = sums + C * kDim;
   int32_t* offs = counts + C;
   int32_t* cw = offs + C;
@@ -143,84 +260,72 @@ k_kmeans(const int8_t* __restrict__ X_all, int N, int C, int iters, int64_t row0
     const int8_t* src = mu_in ? mu_in + ((int64_t)blk * C + c) * kDim : X + (int64_t)c * stride * kDim;
     reinterpret_cast<int4*>(mu + c * kDim)[part] = reinterpret_cast<const int4*>(src)[part];
   }
+  for (int e = tid; e < C; e += kKmThreads) counts[e] = 0;
+  if (iters > 0)
+    for (int e = tid; e < C * kDim; e += kKmThreads) sums[e] = 0;
+  __syncthreads();
   if (asg_in) {
-    for (int e = tid; e < C; e += kKmThreads) counts[e] = 0;
-    __syncthreads();
     for (int i = tid; i < N; i += kKmThreads) {
       const uint16_t c = asg_in[(int64_t)blk * N + i];
       assign[i] = c;
       atomicAdd(&counts[c], 1);
     }
   }
+  for (int c = tid; c < C; c += kKmThreads) bias[c] = km_bias(mu + c * kDim, c);
   __syncthreads();
 
   for (int it = 0; it < iters; ++it) {
-    for (int c = tid; c < C; c += kKmThreads) {
-      int s = 0;
-      for (int d = 0; d < kDim; ++d) { const int m = mu[c * kDim + d]; s += m * m; }
-      musq[c] = s;
-    }
-    // cluster sums laid out [dim][cluster]: the lanes of one LDS atomic below
-    // add to one dim of their rows' clusters, so their banks follow the clusters
-    for (int e = tid; e < C * kDim; e += kKmThreads) sums[e] = 0;
-    for (int e = tid; e < C; e += kKmThreads) counts[e] = 0;
-    __syncthreads();
-
-    // ---- assign (16-row tiles, all C centroids per tile), with the update's
-    // sums taken from the rows the MFMA operand already holds ----
+    // ---- assign (16-row tiles, all C centroids per tile), each row added to
+    // its cluster's sums from the MFMA operand the lane already holds ----
     const int ntile = N >> 4;
     const int8_t* xl = X + (int64_t)(lane & 15) * kDim + 16 * (lane >> 4);
     v4i a_next = wave < ntile ? *reinterpret_cast<const v4i*>(xl + (int64_t)wave * 16 * kDim) : v4i{0, 0, 0, 0};
     for (int rt = wave; rt < ntile; rt += kKmWaves) {
       const v4i a = a_next;
       if (rt + kKmWaves < ntile) a_next = *reinterpret_cast<const v4i*>(xl + (int64_t)(rt + kKmWaves) * 16 * kDim);
-      int best[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-      int bidx[4] = {0, 0, 0, 0};
-      for (int ct = 0; ct < (C >> 4); ++ct) {
-        const int c = ct * 16 + (lane & 15);
-        const v4i b = *reinterpret_cast<const v4i*>(mu + c * kDim + 16 * (lane >> 4));
-        const v4i z = {0, 0, 0, 0};
-        const v4i dot = mfma_i8_16x16x64(a, b, z);
-        const int msq = musq[c];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int d = msq - 2 * dot[v];
-          if (d < best[v]) { best[v] = d; bidx[v] = c; }
-        }
-      }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int ob = __shfl_xor(best[v], m);
-          const int oi = __shfl_xor(bidx[v], m);
-          if (ob < best[v] || (ob == best[v] && oi < bidx[v])) { best[v] = ob; bidx[v] = oi; }
-        }
-      }
-      if ((lane & 15) == 0) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) assign[rt * 16 + 4 * (lane >> 4) + v] = (uint16_t)bidx[v];
-      }
-      // this lane's operand row is lane % 16 (bytes 16 * (lane / 16) ..); its
-      // cluster sits in lanes 16 * (row / 4) .., value row % 4
-      const int r = lane & 15, src = 16 * (r >> 2);
-      const int c0 = __shfl(bidx[0], src), c1 = __shfl(bidx[1], src);
-      const int c2 = __shfl(bidx[2], src), c3 = __shfl(bidx[3], src);
-      const int cr = (r & 2) ? ((r & 1) ? c3 : c2) : ((r & 1) ? c1 : c0);
-      if (lane < 16) atomicAdd(&counts[cr], 1);
-      int32_t* sd = sums + (16 * (lane >> 4)) * C + cr;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int w4 = a[k];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) atomicAdd(&sd[(4 * k + j) * C], (w4 << (24 - 8 * j)) >> 24);
-      }
+      int cl[4];
+      km_nearest(a, mu, bias, C, cl);
+      const int cr = km_row_cluster(cl);
+      if (lane < 16) assign[rt * 16 + lane] = (uint16_t)cr;
+      km_accumulate(a, cr, C, sums, counts);
     }
     __syncthreads();
-    for (int e = tid; e < C * kDim; e += kKmThreads) {
-      const int c = e >> 6, d = e & 63;
+    // ---- update: one task per (cluster, 16 dims); the four tasks of a
+    // cluster are the lanes of one quad.  Sums are cleared as they are read;
+    // the last iteration's counts stay for the member lists. ----
+    for (int task = tid; task < C * 4; task += kKmThreads) {
+      const int c = task >> 2, ch = task & 3;
       const int n = counts[c];
-      if (n > 0) mu[e] = (int8_t)rhe_div(sums[d * C + c], n);
+      int4* mp = reinterpret_cast<int4*>(mu + c * kDim + 16 * ch);
+      int4 m = *mp;
+      if (n > 0) {
+        const float rn = __builtin_amdgcn_rcpf((float)n);
+        int w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          unsigned x = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            int* sp = sums + km_sum_at(16 * ch + 4 * k + j, c, C);
+            x |= ((unsigned)rhe_div_small(*sp, n, rn) & 0xffu) << (8 * j);
+            *sp = 0;
+          }
+          w[k] = (int)x;
+        }
+        m = make_int4(w[0], w[1], w[2], w[3]);
+        *mp = m;
+      }
+      int sq = 0;
+      sq = __builtin_amdgcn_sdot4(m.x, m.x, sq, false);
+      sq = __builtin_amdgcn_sdot4(m.y, m.y, sq, false);
+      sq = __builtin_amdgcn_sdot4(m.z, m.z, sq, false);
+      sq = __builtin_amdgcn_sdot4(m.w, m.w, sq, false);
+      sq += dpp_move<0xB1, 0xf>(0, sq);
+      sq += dpp_move<0x4E, 0xf>(0, sq);
+      if (ch == 0) {
+        bias[c] = 255 - c - 256 * sq;
+        if (it + 1 < iters) counts[c] = 0;
+      }
     }
     __syncthreads();
   }
@@ -340,8 +445,8 @@ __global__ void __launch_bounds__(kKmAT) k_km_assign(const int8_t* __restrict__ 
                                                      int W, int it, KmScratch S) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int8_t* mu = reinterpret_cast<int8_t*>(smem);
-  int32_t* musq = reinterpret_cast<int32_t*>(mu + (size_t)C * kDim);
-  int32_t* sums = musq + C;
+  int32_t* bias = reinterpret_cast<int32_t*>(mu + (size_t)C * kDim);
+  int32_t* sums = bias + C;
   int32_t* cnts = sums + C * kDim;
   const int b = blockIdx.x / W, w = blockIdx.x % W;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -355,64 +460,24 @@ __global__ void __launch_bounds__(kKmAT) k_km_assign(const int8_t* __restrict__ 
   for (int e = tid; e < C * kDim; e += kKmAT) sums[e] = 0;
   for (int e = tid; e < C; e += kKmAT) cnts[e] = 0;
   __syncthreads();
-  for (int c = tid; c < C; c += kKmAT) {
-    int sq = 0;
-    for (int d = 0; d < kDim; ++d) { const int m = mu[c * kDim + d]; sq += m * m; }
-    musq[c] = sq;
-  }
+  for (int c = tid; c < C; c += kKmAT) bias[c] = km_bias(mu + c * kDim, c);
   __syncthreads();
   const int rows = N / W;
   const int r0 = w * rows;
   for (int rt = wave; rt < rows / 16; rt += kKmAT / 64) {
     const int row = r0 + rt * 16;
     const v4i a = *reinterpret_cast<const v4i*>(X + (int64_t)(row + (lane & 15)) * kDim + 16 * (lane >> 4));
-    int best[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-    int bidx[4] = {0, 0, 0, 0};
-    for (int ct = 0; ct < (C >> 4); ++ct) {
-      const int c = ct * 16 + (lane & 15);
-      const v4i bv = *reinterpret_cast<const v4i*>(mu + c * kDim + 16 * (lane >> 4));
-      const v4i z = {0, 0, 0, 0};
-      const v4i dot = mfma_i8_16x16x64(a, bv, z);
-      const int msq = musq[c];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int d = msq - 2 * dot[v];
-        if (d < best[v]) { best[v] = d; bidx[v] = c; }
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ob = __shfl_xor(best[v], m);
-        const int oi = __shfl_xor(bidx[v], m);
-        if (ob < best[v] || (ob == best[v] && oi < bidx[v])) { best[v] = ob; bidx[v] = oi; }
-      }
-    }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) S.asg[(int64_t)b * N + row + 4 * (lane >> 4) + v] = (uint16_t)bidx[v];
-    }
-    // the tile's rows join their clusters' sums ([dim][cluster]), from the
-    // operand bytes this lane holds: row lane % 16, dims 16 * (lane / 16) ..
-    const int r = lane & 15, src = 16 * (r >> 2);
-    const int c0 = __shfl(bidx[0], src), c1 = __shfl(bidx[1], src);
-    const int c2 = __shfl(bidx[2], src), c3 = __shfl(bidx[3], src);
-    const int cr = (r & 2) ? ((r & 1) ? c3 : c2) : ((r & 1) ? c1 : c0);
-    if (lane < 16) atomicAdd(&cnts[cr], 1);
-    int32_t* sd = sums + (16 * (lane >> 4)) * C + cr;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int w4 = a[k];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) atomicAdd(&sd[(4 * k + j) * C], (w4 << (24 - 8 * j)) >> 24);
-    }
+    int cl[4];
+    km_nearest(a, mu, bias, C, cl);
+    const int cr = km_row_cluster(cl);
+    if (lane < 16) S.asg[(int64_t)b * N + row + lane] = (uint16_t)cr;
+    km_accumulate(a, cr, C, sums, cnts);
   }
   __syncthreads();
   int32_t* part = S.part + ((int64_t)b * W + w) * C * 65;
   for (int e = tid; e < C * 65; e += kKmAT) {
     const int c = e / 65, d = e % 65;
-    part[e] = d < kDim ? sums[d * C + c] : cnts[c];
+    part[e] = d < kDim ? sums[km_sum_at(d, c, C)] : cnts[c];
   }
 }
 
