@@ -473,8 +473,11 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
     case LSA_OP_BUILD: case LSA_OP_APPEND: case LSA_OP_ATTN:
       *bytes = 0;
       return LSA_OK;
-    case LSA_OP_SELECT: case LSA_OP_DENSE:
+    case LSA_OP_SELECT:
       *bytes = select_fast_ws_bytes((int32_t)n);
+      return LSA_OK;
+    case LSA_OP_DENSE:
+      *bytes = dense_ws_bytes((int32_t)n);
       return LSA_OK;
     case LSA_OP_PREFILL: {
       if (int e = check_select_params(sprm, false)) return e;
@@ -816,11 +819,12 @@ int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq, cons
   a.early_budget = sp->early_budget; a.early_until = sp->early_until; a.tree2_top = sp->tree2_top;
   a.max_sel = max_sel_of(sp);
   a.idx = d_idx; a.cnt = d_cnt; a.only = nullptr;
-  // large batches with a workspace: one thresholded int8-MFMA pass over all
-  // latents, then an exact top-budget per query (the exact kernel serves the
-  // few queries whose list cannot hold the cutoff); otherwise the exact kernel
-  if (nq >= kFastSelectMinQ && d_ws && ws_bytes >= select_fast_ws_bytes(nq))
-    LSA_HIP(launch_select_fast(v, a, d_ws, static_cast<hipStream_t>(stream)), "dense select");
+  // large batches with a workspace: a sampled threshold per query, one
+  // thresholded int8-MFMA pass over all latents, then an exact top-budget per
+  // query (the exact kernel serves the few queries whose lists cannot hold the
+  // cutoff); otherwise the exact kernel
+  if (nq >= kFastSelectMinQ && d_ws && ws_bytes >= dense_ws_bytes(nq))
+    LSA_HIP(launch_dense_select(v, a, d_ws, static_cast<hipStream_t>(stream)), "dense select");
   else
     LSA_HIP(launch_select(v, a, nullptr, static_cast<hipStream_t>(stream)), "dense select");
   return LSA_OK;

@@ -161,6 +161,8 @@ hipError_t launch_select(const IdxView& v, const SelArgs& a, void* ws, hipStream
 // large Flat batches: list-based single full pass (+ exact kernel for flagged queries)
 size_t select_fast_ws_bytes(int32_t nq);
 hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
+size_t dense_ws_bytes(int32_t nq);
+hipError_t launch_dense_select(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);
 // Tree selection, one workgroup per query; workspace: select_tree_ws_bytes(nq)
 size_t select_tree_ws_bytes(int32_t nq);
 hipError_t launch_select_tree(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s);

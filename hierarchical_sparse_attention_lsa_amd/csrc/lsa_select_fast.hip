@@ -67,7 +67,16 @@ struct ListWs {
   int32_t* meta;      // [slots][3]  query index (-1: empty slot), position, 1: the list holds
                       //             every bucket with an eligible key
   int32_t* flags;     // [nq] 1: recompute with the exact kernel
+  int32_t* slo;       // dense: [slots] score threshold of each query (sample kernel -> scan)
 };
+
+// Dense comparator lists: the scan is split over kDenseSplit ranges of the
+// keys, and each (query, range) appends to its own sub-list of kDenseSub
+// entries, so no counter is shared between workgroups.  A query holds up to
+// 4x the largest budget; its threshold aims at 2x.
+constexpr int kDenseSplit = 8;
+constexpr int kDenseList = 16384;
+constexpr int kDenseSub = kDenseList / kDenseSplit;
 
 template <int FW, int QS>
 struct Cfg {
@@ -165,14 +174,22 @@ __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>&
 // the quadratic comparator (every long-range key scored on its own latent);
 // only eligible keys join the lists, and the sample is denser (the cut is a
 // few thousand keys out of millions).
-template <int FW, int QS, bool DENSE>
+// MODE 0: all phases in one workgroup per query tile (Flat).  The dense
+// comparator splits them: MODE 1 runs the sampled passes and stores each
+// query's threshold; MODE 2 runs the full pass over one of kDenseSplit key
+// ranges per workgroup (grid: ranges x query tiles, range-major, so the
+// workgroups resident together stream the same latents and share them in L2).
+template <int FW, int QS, bool DENSE, int MODE = 0>
 __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListWs W) {
   using C = Cfg<FW, QS>;
+  static_assert(MODE == 0 || DENSE, "only the dense scan is split");
   __shared__ ScanLds<FW, QS> S;
   const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const IdxView V = vsp->v[0];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int64_t lbase = (int64_t)blockIdx.x * QS;
+  const int nqt = MODE == 2 ? (int)gridDim.x / kDenseSplit : (int)gridDim.x;
+  const int krange = MODE == 2 ? (int)blockIdx.x / nqt : 0;
+  const int64_t lbase = (int64_t)(MODE == 2 ? (int)blockIdx.x % nqt : (int)blockIdx.x) * QS;
   const int qgrp = wave % C::NQW;
   const int phase = wave / C::NQW;
   const int qrow = qgrp * 16 + 4 * (lane >> 4);    // slot of score row v = 0
@@ -185,8 +202,10 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     const int t = q < 0 ? -1 : max(0, A.qpos ? A.qpos[q] : A.qpos_base + q);
     S.q[i] = q; S.t[i] = t;
     S.smax[i] = INT_MIN; S.ssum[i] = 0; S.sn[i] = 0;
-    W.meta[3 * (lbase + i)] = q;
-    W.meta[3 * (lbase + i) + 1] = t;
+    if (MODE != 2) {
+      W.meta[3 * (lbase + i)] = q;
+      W.meta[3 * (lbase + i) + 1] = t;
+    }
   }
   for (int e = tid; e < QS * NB2; e += C::FT) (&S.hist[0][0])[e] = 0;
   for (int e = tid; e < QS; e += C::FT) S.nl[e] = 0;
@@ -222,6 +241,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   const int tl0 = S.t[qrow] - A.window, tl1 = S.t[qrow + 1] - A.window;
   const int tl2 = S.t[qrow + 2] - A.window, tl3 = S.t[qrow + 3] - A.window;
 
+  if constexpr (MODE != 2) {
   // ---- 1. sampled max / mean over non-empty buckets ----
   {
     int smax[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, sn[4] = {0, 0, 0, 0};
@@ -306,9 +326,8 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           while (s < 30 && (((mx - mn + 1) + (1 << s) - 1) >> s) > NB2) ++s;
           const int sampled = (nchunks + sstep - 1) / sstep;
           // twice the budget (Flat: buckets hold tens of keys, so the list is a
-          // few hundred entries); 1.5 times for the dense scan, whose entries
-          // are single keys and whose list holds LC of them
-          const long long want = DENSE ? 3ll * budget_at(A, S.t[qs]) / 2 : 2ll * budget_at(A, S.t[qs]);
+          // few hundred entries; dense: single keys, a list holds 4x the budget)
+          const long long want = 2ll * budget_at(A, S.t[qs]);
           const long long target = (want * sampled + nchunks - 1) / nchunks;
           long long cum = 0;
           for (int b = 0; b < NB2; ++b) {
@@ -362,6 +381,14 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     }
     __syncthreads();
   }
+  if (MODE == 1) {
+    for (int qs = tid; qs < QS; qs += C::FT) W.slo[lbase + qs] = S.slo[qs];
+    return;
+  }
+  } else {
+    for (int qs = tid; qs < QS; qs += C::FT) S.slo[qs] = W.slo[lbase + qs];
+    __syncthreads();
+  }
 
   // ---- 3. full pass: buckets at or above the threshold join the lists ----
   // The MFMA starts from -threshold, so a (query, bucket) pair is a hit when
@@ -379,7 +406,14 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
       slo[v] = act[v] ? S.slo[qrow + v] : (1 << 30);    // 1<<30: no score reaches it
       bias[v] = -slo[v];
     }
-    stream_chunks<DENSE>(V, S, 0, 1, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
+    // MODE 2: chunks [cb, ce) of this workgroup's key range, and the
+    // (query, range) sub-list
+    const int cb = MODE == 2 ? (int)((int64_t)krange * nchunks / kDenseSplit) : 0;
+    const int ce = MODE == 2 ? (int)((int64_t)(krange + 1) * nchunks / kDenseSplit) : nchunks;
+    constexpr int lcap = MODE == 2 ? kDenseSub : LC;
+    const int64_t lstride = MODE == 2 ? kDenseList : LC;
+    const int64_t loff = MODE == 2 ? (int64_t)krange * kDenseSub : 0;
+    stream_chunks<DENSE>(V, S, cb, 1, ce, causal, [&](int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < TPW; g += 4) {
         int d[16];
@@ -414,8 +448,10 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           for (int i = 0; i < 2; ++i) z[i] = (y[2 * i + 1] & m2) | (y[2 * i] & ~m2);
           const int dk = (int)((z[1] & m3) | (z[0] & ~m3));
           const int v = k & 3, u = k >> 2;
-          const int sv = (v & 2) ? ((v & 1) ? slo[3] : slo[2]) : ((v & 1) ? slo[1] : slo[0]);
-          const int tv = S.t[qrow + v] - A.window;   // (hits are rare: an LDS read is cheap)
+          // the row's threshold and position from LDS (hits are rare; a select
+          // over slo[] by a run-time v would be placed in scratch memory)
+          const int sv = S.slo[qrow + v];
+          const int tv = S.t[qrow + v] - A.window;
           const int beta = (tb + C::PH * u) * 16 + col;
           // a bucket whose first key is past the query's long-range range has no
           // eligible key (first pooled id of bucket beta: chunk-local slot beta - c*CHT*16);
@@ -423,12 +459,13 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           if (DENSE ? (beta >= A.sinks && beta <= tv) : S.fl[buf][beta - c * CHT * 16].x <= tv) {
             const int qs = qrow + v;
             const int pos = atomicAdd(&S.nl[qs], 1);
-            if (pos < LC) W.key[(lbase + qs) * LC + pos] = order_key(dk + sv, beta);
+            if (pos < lcap) W.key[(lbase + qs) * lstride + loff + pos] = order_key(dk + sv, beta);
           }
         }
       }
     });
-    for (int e = tid; e < QS; e += C::FT) W.nlist[lbase + e] = S.nl[e];
+    for (int e = tid; e < QS; e += C::FT)
+      W.nlist[MODE == 2 ? (lbase + e) * kDenseSplit + krange : lbase + e] = S.nl[e];
   }
 }
 
@@ -448,9 +485,9 @@ __device__ __forceinline__ int shfl_xor_t(int v, int m) { return __shfl_xor(v, m
 __device__ __forceinline__ long long shfl_xor_t(long long v, int m) { return shfl_xor_i64(v, m); }
 __device__ __forceinline__ unsigned shfl_xor_t(unsigned v, int m) { return (unsigned)__shfl_xor((int)v, m); }
 
-template <int N, class T>
-__device__ __forceinline__ void block_bitonic(T (&v)[N / RT], T* tmp) {
-  constexpr int PT = N / RT;
+template <int N, class T, int NT = RT>
+__device__ __forceinline__ void block_bitonic(T (&v)[N / NT], T* tmp) {
+  constexpr int PT = N / NT;
   const int tid = threadIdx.x;
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -800,21 +837,24 @@ __global__ void __launch_bounds__(RT, 4) k_resolve(FastViews VS, SelArgs A, List
   if (tid == 0) W.flags[q] = ok ? 0 : 1;
 }
 
-// Dense comparator resolve: one RT-thread workgroup per query slot.  Each
+// Dense comparator resolve: one RTD-thread workgroup per query slot.  Each
 // list entry is one eligible key with its order key (score desc, position
-// asc); the query keeps its budget's largest keys.  A histogram bracket
-// narrows to at most RCAP entries around the cutoff, which one wave sorts;
-// the kept keys are sorted by position and written, then the sinks and the
-// window.  A list that overflowed, or holds fewer than the budget without
-// being complete, flags the query for the exact kernel.
-constexpr int DPT = LC / RT;        // list entries per thread
-constexpr int DKEEP = 4096;         // budget <= 4096
-static_assert(DKEEP % RT == 0, "kept keys sort");
+// asc), in the query's kDenseSplit sub-lists; the query keeps its budget's
+// largest keys (the result does not depend on the entries' order).  A
+// histogram bracket narrows to at most RCAP entries around the cutoff, which
+// one wave sorts; the kept keys are sorted by position and written, then the
+// sinks and the window.  A sub-list that overflowed, or lists holding fewer
+// than the budget without being complete, flag the query for the exact kernel.
+constexpr int RTD = 512;
+constexpr int DPT = kDenseList / RTD;   // list entries per thread
+constexpr int DSUB = kDenseSub / RTD;   // of them per sub-list
+constexpr int DKEEP = 4096;             // budget <= 4096
+static_assert(DKEEP % RTD == 0 && kDenseSub % RTD == 0, "list and kept-key shapes");
 
-__global__ void __launch_bounds__(RT) k_dense_resolve(SelArgs A, ListWs W) {
+__global__ void __launch_bounds__(RTD) k_dense_resolve(SelArgs A, ListWs W) {
   __shared__ int s_h[RB];
-  __shared__ long long s_red[RT / 64];
-  __shared__ int s_ired[RT / 64];
+  __shared__ long long s_red[RTD / 64];
+  __shared__ int s_ired[RTD / 64];
   __shared__ long long s_cq[RCAP];
   __shared__ int s_nc, s_cut;
   __shared__ int s_keys[DKEEP];
@@ -825,17 +865,25 @@ __global__ void __launch_bounds__(RT) k_dense_resolve(SelArgs A, ListWs W) {
   const int t = W.meta[3 * slot + 1];
   const bool complete = W.meta[3 * slot + 2] != 0;
   const int B = budget_at(A, t);
-  const int ntot = W.nlist[slot];
-  if (ntot > LC || (ntot < B && !complete)) {
+  int nsub[kDenseSplit], ntot = 0;
+  bool over = false;
+#pragma unroll
+  for (int k = 0; k < kDenseSplit; ++k) {
+    nsub[k] = W.nlist[slot * kDenseSplit + k];
+    ntot += min(nsub[k], kDenseSub);
+    over |= nsub[k] > kDenseSub;
+  }
+  if (over || (ntot < B && !complete)) {
     if (tid == 0) W.flags[q] = 1;
     return;
   }
-  const long long* lk = W.key + slot * LC;
+  // entry u of this thread: sub-list u / DSUB, offset tid + RTD * (u % DSUB)
+  const long long* lk = W.key + slot * kDenseList;
   long long K[DPT];
 #pragma unroll
   for (int u = 0; u < DPT; ++u) {
-    const int f = tid + RT * u;
-    K[u] = f < ntot ? lk[f] : LLONG_MIN;
+    const int k = u / DSUB, f = tid + RTD * (u % DSUB);
+    K[u] = f < nsub[k] ? lk[k * kDenseSub + f] : LLONG_MIN;
   }
   const int take = min(B, ntot);
   long long cut = LLONG_MIN + 1;     // keys >= cut are kept; padding (LLONG_MIN) never is
@@ -847,13 +895,13 @@ __global__ void __launch_bounds__(RT) k_dense_resolve(SelArgs A, ListWs W) {
       lo = min(lo, K[u]);
       hi = max(hi, K[u]);
     }
-    lo = block_min_ll<RT>(lo, s_red);
-    hi = block_max_ll<RT>(hi, s_red);
+    lo = block_min_ll<RTD>(lo, s_red);
+    hi = block_max_ll<RTD>(hi, s_red);
     for (int pass = 0; pass < 8; ++pass) {
       const long long range = hi - lo + 1;
       int sh = 0;
       while (sh < 62 && ((range + (1ll << sh) - 1) >> sh) > RB) ++sh;
-      for (int i = tid; i < RB; i += RT) s_h[i] = 0;
+      for (int i = tid; i < RB; i += RTD) s_h[i] = 0;
       __syncthreads();
       long long ab = 0;
 #pragma unroll
@@ -862,7 +910,7 @@ __global__ void __launch_bounds__(RT) k_dense_resolve(SelArgs A, ListWs W) {
         if (K[u] > hi) { ++ab; continue; }
         if (K[u] >= lo) atomicAdd(&s_h[(int)((hi - K[u]) >> sh)], 1);
       }
-      ab = block_sum_ll<RT>(ab, s_red);
+      ab = block_sum_ll<RTD>(ab, s_red);
       if (wave == 0) {
         int h[RB / 64], loc = 0;
 #pragma unroll
@@ -906,7 +954,7 @@ __global__ void __launch_bounds__(RT) k_dense_resolve(SelArgs A, ListWs W) {
         if (c < RCAP) s_cq[c] = -K[u];
       }
     }
-    ab = block_sum_ll<RT>(ab, s_red);
+    ab = block_sum_ll<RTD>(ab, s_red);
     const int nc = min(s_nc, RCAP);
     if (wave == 0) {
       int np = 1;
@@ -924,16 +972,16 @@ __global__ void __launch_bounds__(RT) k_dense_resolve(SelArgs A, ListWs W) {
 #pragma unroll
   for (int u = 0; u < DPT; ++u) mine += K[u] >= cut ? 1 : 0;
   int total;
-  int at = block_excl_scan<RT>(mine, s_ired, &total);
+  int at = block_excl_scan<RTD>(mine, s_ired, &total);
 #pragma unroll
   for (int u = 0; u < DPT; ++u)
     if (K[u] >= cut) s_keys[at++] = (int)(0xffffffffu - (unsigned)(K[u] & 0xffffffffll));
   __syncthreads();
-  constexpr int KPT = DKEEP / RT;
+  constexpr int KPT = DKEEP / RTD;
   int v[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) v[i] = tid * KPT + i < total ? s_keys[tid * KPT + i] : INT_MAX;
-  block_bitonic<DKEEP>(v, s_keys);
+  block_bitonic<DKEEP, int, RTD>(v, s_keys);
   int32_t* row = A.idx + (int64_t)q * A.max_sel;
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
@@ -1242,6 +1290,25 @@ size_t ws_layout(size_t slots, size_t nq, ListWs* W, void* base) {
   w.nlist = reinterpret_cast<int32_t*>(take(slots * sizeof(int32_t)));
   w.meta = reinterpret_cast<int32_t*>(take(slots * 3 * sizeof(int32_t)));
   w.flags = reinterpret_cast<int32_t*>(take(nq * sizeof(int32_t)));
+  w.slo = nullptr;
+  if (W) *W = w;
+  return o;
+}
+
+// Dense comparator: [slots][kDenseList] order keys in kDenseSplit sub-lists,
+// [slots][kDenseSplit] sub-list lengths, meta, thresholds, flags.
+size_t dense_layout(size_t slots, size_t nq, ListWs* W, void* base) {
+  char* p = static_cast<char*>(base);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { char* r = p ? p + o : nullptr; o += (bytes + 255) / 256 * 256; return r; };
+  ListWs w;
+  w.key = reinterpret_cast<long long*>(take(slots * kDenseList * sizeof(long long)));
+  w.elig = nullptr;
+  w.kstart = nullptr;
+  w.nlist = reinterpret_cast<int32_t*>(take(slots * kDenseSplit * sizeof(int32_t)));
+  w.meta = reinterpret_cast<int32_t*>(take(slots * 3 * sizeof(int32_t)));
+  w.slo = reinterpret_cast<int32_t*>(take(slots * sizeof(int32_t)));
+  w.flags = reinterpret_cast<int32_t*>(take(nq * sizeof(int32_t)));
   if (W) *W = w;
   return o;
 }
@@ -1262,18 +1329,6 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
   memset(&vs, 0, sizeof vs);
   vs.v[0] = v;
   vs.nviews = 1;
-  if (v.dense) {
-    hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ, true>), dim3((unsigned)(slots / kPrefQ)), dim3(kPrefW * 64),
-                       0, s, vs, a, W);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_dense_resolve, dim3((unsigned)slots), dim3(RT), 0, s, a, W);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    SelArgs b = a;
-    b.only = W.flags;
-    return launch_select(v, b, nullptr, s);
-  }
   hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ, false>), dim3((unsigned)(slots / kPrefQ)), dim3(kPrefW * 64),
                      0, s, vs, a, W);
   hipError_t e = hipGetLastError();
@@ -1282,6 +1337,39 @@ hipError_t launch_select_fast(const IdxView& v, const SelArgs& a, void* ws, hipS
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // exact refinement for the (rare) flagged queries; other workgroups exit at once
+  SelArgs b = a;
+  b.only = W.flags;
+  return launch_select(v, b, nullptr, s);
+}
+
+size_t dense_ws_bytes(int32_t nq) {
+  const size_t slots = ((size_t)nq + kPrefQ - 1) / kPrefQ * kPrefQ;
+  return dense_layout(slots, nq, nullptr, nullptr);
+}
+
+// The dense comparator: per query tile the sampled threshold, then the full
+// pass split over key ranges, the exact top-budget per query, and the exact
+// kernel for the (rare) flagged queries.
+hipError_t launch_dense_select(const IdxView& v, const SelArgs& a, void* ws, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  const size_t slots = ((size_t)a.nq + kPrefQ - 1) / kPrefQ * kPrefQ;
+  const unsigned nqt = (unsigned)(slots / kPrefQ);
+  ListWs W;
+  dense_layout(slots, a.nq, &W, ws);
+  FastViews vs;
+  memset(&vs, 0, sizeof vs);
+  vs.v[0] = v;
+  vs.nviews = 1;
+  hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ, true, 1>), dim3(nqt), dim3(kPrefW * 64), 0, s, vs, a, W);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_scan<kPrefW, kPrefQ, true, 2>), dim3(nqt * kDenseSplit), dim3(kPrefW * 64), 0, s, vs,
+                     a, W);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dense_resolve, dim3((unsigned)slots), dim3(RTD), 0, s, a, W);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   SelArgs b = a;
   b.only = W.flags;
   return launch_select(v, b, nullptr, s);

@@ -306,8 +306,9 @@ LSA_API int lsa_decode_step_noalloc(lsa_index* const* hs, int32_t nseq, const in
  * (q . latk[j]), best `budget` by (score desc, position asc), plus window
  * and sinks.  Same output format as lsa_select.  With a workspace of
  * lsa_workspace_bytes(LSA_OP_DENSE, .., nq) bytes and nq >= 64 it runs as
- * one thresholded int8-MFMA scan of all latents plus an exact top-budget per
- * query; without, every query takes the exact refinement kernel. */
+ * a sampled score threshold per query, one thresholded int8-MFMA scan of all
+ * latents (split over key ranges) and an exact top-budget per query; without,
+ * every query takes the exact refinement kernel. */
 LSA_API int lsa_dense_select(const int8_t* d_latk, int64_t T, const int8_t* d_latq,
                              const int32_t* d_qpos, int32_t nq, const lsa_select_params* sp,
                              int32_t* d_idx, int32_t* d_cnt, void* d_ws, size_t ws_bytes,
