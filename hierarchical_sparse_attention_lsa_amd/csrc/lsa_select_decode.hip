@@ -12,16 +12,21 @@
 //                 for the new position and its first key slot go to the
 //                 workspace, and each workgroup writes its histogram of
 //                 eligible keys over score bins (a log scale of the score);
-//   k_dec_select  one 1024-thread workgroup per sequence sums the partial
-//                 histograms; the bin where the eligible keys reach the
-//                 budget is the cutoff bin: buckets above it are taken whole,
-//                 its own (few) buckets are ranked by order key and taken in
-//                 turn.  The taken buckets are put in ascending id order
-//                 through a bitmap, and a prefix sum gives each its output
-//                 offset.  A cutoff bin with more than BCAP buckets (many
-//                 equal scores) takes the general path: histogram refinement
-//                 of the order-key range until the bracket holding the cutoff
-//                 has at most 256 entries, which are sorted.
+//   k_dec_select  one 1024-thread workgroup per slice of 1024 buckets of a
+//                 sequence sums the partial histograms; the bin where the
+//                 eligible keys reach the budget is the cutoff bin.  Buckets
+//                 above it are taken whole: each slice writes its own, in
+//                 ascending id order, after the earlier slices' (whose key
+//                 counts the histograms give).  One more workgroup per
+//                 sequence, alongside the slices, finds the same cutoff bin,
+//                 gathers its (few) buckets, ranks them by order
+//                 key, takes them in turn and writes their keys in id order
+//                 after all the keys above the bin, then the sinks and the
+//                 window.  A cutoff bin with more than BCAP buckets (many
+//                 equal scores) takes the general path for those keys:
+//                 histogram refinement of the order-key range until the
+//                 bracket holding the cutoff has at most 256 entries, which
+//                 are sorted.
 //   k_dec_select_big  the same rule for indexes beyond the registers (more
 //                 than 24576 buckets): the histogram summed from the partials,
 //                 the scores streamed once from the workspace to classify.
@@ -93,9 +98,6 @@ struct DecWs {
                                     // one histogram per score workgroup
   int32_t n_part;                   // histograms per sequence
   uint32_t* supmask;                // [nseq][kSupMaskWords] Tree: supers chosen
-  int32_t* above;                   // [nseq] keys above the cutoff bin (slice workgroups -> finish)
-  long long* cand;                  // [nseq][PERT_MAX][BCAP] cutoff-bin order keys per slice
-  int32_t* ncand;                   // [nseq][PERT_MAX] cutoff-bin buckets per slice
 };
 
 
@@ -361,10 +363,11 @@ __device__ __forceinline__ long long rebuilt_key(int s, int beta) {
 }
 
 // PERT buckets per thread: the smallest instance that holds the index is
-// launched, since every pass costs VALU time per slot, used or not.
-// FINISH = false: one workgroup per slice of DT buckets (grid slices x
-// sequences); FINISH = true: one workgroup per sequence, after them.
-template <int PERT, bool FINISH>
+// launched, since every pass costs VALU time per slot, used or not.  One
+// workgroup per slice of DT buckets (grid: slices + 1 x sequences); the last
+// workgroup of each sequence's row of the grid finishes the row, alongside
+// the slices.
+template <int PERT>
 __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs W,
                                                    int32_t* __restrict__ flags) {
   constexpr int kListCap = list_cap(PERT);
@@ -379,7 +382,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   extern __shared__ int s_e[];         // [bucket id]: eligible keys, later the keys taken
   const DecViews* vsp = (const DecViews*)__builtin_amdgcn_kernarg_segment_ptr();
   const int seq = blockIdx.y;
-  const int slice = blockIdx.x;        // buckets slice*DT .. slice*DT + DT - 1
+  const bool fin = blockIdx.x == gridDim.x - 1;     // the finishing workgroup
+  const int slice = fin ? -1 : (int)blockIdx.x;    // buckets slice*DT .. slice*DT + DT - 1
   const IdxView V = vsp->v[seq];
   const int t = vsp->qpos[seq];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -390,7 +394,7 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   const int nsl = max(1, (n + DT - 1) / DT);
   if (slice >= nsl) return;            // uniform: past this sequence's index
   if (n > DT * PERT) {                 // too large for registers: the exact kernel serves it
-    if (!FINISH && slice == 0 && tid == 0) flags[seq] = 1;
+    if (fin && tid == 0) flags[seq] = 1;
     return;
   }
   // ---- fast path: the cutoff located in the score histogram ----
@@ -399,17 +403,17 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   // key and taken in turn, the last one cut.  Every slice's workgroup finds
   // the cut bin from the summed partial histograms, writes the keys of its
   // own buckets above it (slices in order, ids ascending within a slice: the
-  // earlier slices' keys above the cut give its output offset) and lists its
-  // cutoff-bin buckets; the finishing workgroup of the sequence ranks the
-  // cutoff bin, writes its keys, the sinks and the window.  A cutoff bin of
-  // more than BCAP buckets (many equal or near-equal scores) leaves the whole
-  // row to the general path below, run by the finishing workgroup.
+  // earlier slices' keys above the cut give its output offset).  The
+  // finishing workgroup finds the same cut bin, collects its buckets over the
+  // whole sequence, ranks them, writes their keys after all the keys above the
+  // bin, then the sinks and the window.  A cutoff bin of more than BCAP buckets (many equal
+  // or near-equal scores) takes the general path below for those keys.
   int* l_off = s_e;                    // taken buckets: output offset, first key slot
   int* l_ks = s_e + DT;
   __shared__ int s_nt, s_nb;
   __shared__ int s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
-  if (!FINISH) {
-    __shared__ int s_fc[4];            // cut bin, keys above it, its scores [lo, hi]
+  __shared__ int s_fc[4];              // cut bin, keys above it, its scores [lo, hi]
+  {
     // bins from the top score down: thread tid takes bins NBIN-1-2tid (he[0])
     // and NBIN-2-2tid (he[1]), summed over the score workgroups (the slices),
     // and the same over the slices before this one (hb) and this one (hm)
@@ -456,7 +460,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       }
     }
     __syncthreads();
-    const int cut = s_fc[0], above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
+    if (fin) goto finish;              // uniform
+    const int cut = s_fc[0], hi_s = s_fc[3];
     // keys above the cut bin in the earlier slices (this slice's output
     // offset) and in this one; both at most the budget
     long long pk = 0;
@@ -470,7 +475,6 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     const int scv = j < n ? W.score[base + j] : 0;
     const int ev = j < n ? W.elig[base + j] : 0;
     const bool is_above = ev > 0 && scv > hi_s;
-    const bool is_cut = ev > 0 && scv >= lo_s && scv <= hi_s;
     // taken buckets in id order: output offset and first key slot (LDS)
     {
       int tot;
@@ -479,38 +483,38 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
         l_off[pre & 0xffff] = before + (pre >> 16);
         l_ks[pre & 0xffff] = W.kstart[base + j];
       }
-      if (is_cut) {
-        const int q = atomicAdd(&s_nb, 1);
-        if (q < BCAP) W.cand[((int64_t)seq * PERT_MAX + slice) * BCAP + q] = order_key(scv, j);
-      }
       __syncthreads();
       dec_emit_keys(V, A, seq, l_off, l_ks, tot & 0xffff, before + mine, before);
-      if (tid == 0) W.ncand[seq * PERT_MAX + slice] = s_nb;
-      if (slice == 0 && tid == 0) W.above[seq] = above;
     }
-    return;
   }
-  // ---- the finishing workgroup of the sequence ----
+  return;
+finish:
+  // ---- the finishing workgroup: the cutoff bin and the rest of the row ----
+  const int above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
   {
-    const int above = W.above[seq];
-    // the cutoff bin's buckets of every slice (order key, id, eligible keys)
+    // the sequence's buckets in the cutoff bin: thread tid reads buckets
+    // u*DT + tid (all loads in flight before the first use)
+    int sc[PERT], ev[PERT];
+#pragma unroll
+    for (int u = 0; u < PERT; ++u) {
+      const int j = u * DT + tid;
+      sc[u] = j < n ? W.score[base + j] : 0;
+      ev[u] = j < n ? W.elig[base + j] : 0;
+    }
     if (tid == 0) s_nb = 0;
     __syncthreads();
-    if (tid < nsl) {
-      const int c = W.ncand[seq * PERT_MAX + tid];
-      int at = 0;
-      if (c > 0) at = atomicAdd(&s_nb, c);
-      for (int k = 0; k < c && at + k < BCAP && k < BCAP; ++k) {
-        const long long kk = W.cand[((int64_t)seq * PERT_MAX + tid) * BCAP + k];
-        s_cq[at + k] = kk;
-        s_ci[at + k] = (int)(0xffffffffu - (unsigned)(kk & 0xffffffffll));
+#pragma unroll
+    for (int u = 0; u < PERT; ++u) {
+      if (ev[u] > 0 && sc[u] >= lo_s && sc[u] <= hi_s) {
+        const int q = atomicAdd(&s_nb, 1);
+        if (q < BCAP) { s_cq[q] = order_key(sc[u], u * DT + tid); s_ci[q] = u * DT + tid; s_ce[q] = ev[u]; }
       }
     }
     __syncthreads();
+  }
+  {
     const int nb = s_nb;
     if (nb <= BCAP) {                  // uniform; else the general path below
-      if (tid < nb) s_ce[tid] = W.elig[base + s_ci[tid]];
-      __syncthreads();
       // rank in the cut bin (order keys are distinct): larger keys first
       if (tid < nb) {
         const long long k = s_cq[tid];
@@ -555,9 +559,11 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       return;
     }
   }
-  // thread tid holds the scores of buckets u*DT + tid (coalesced loads; the
-  // order key is rebuilt from the score and the implicit bucket id); the
-  // eligible counts sit in LDS indexed by bucket id
+  // General path: the exact cutoff by histogram refinement of the order keys
+  // over every bucket (thread tid holds the scores of buckets u*DT + tid, the
+  // order key rebuilt from the score and the implicit bucket id; the eligible
+  // counts sit in LDS indexed by bucket id); only the cutoff bin's buckets are
+  // written here, after the `above` keys the slices wrote.
   int sc[PERT];
 #define KEY(u) rebuilt_key(sc[u], (u) * DT + tid)
 #define E(u) s_e[(u) * DT + tid]
@@ -582,6 +588,7 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       sc[u] = j < n ? W.score[base + j] : 0;
       ev[u] = j < n ? W.elig[base + j] : 0;
     }
+    __syncthreads();                   // the fast path's reads of s_e are over
 #pragma unroll
     for (int u = 0; u < PERT; ++u) {   // branch-free: selects, no divergent blocks
       E(u) = ev[u];
@@ -708,11 +715,18 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
     }
   }
   __syncthreads();
-  // keys taken per bucket: whole above the bracket, as the walk set them inside it
-  each([&](int u, int eu) {
-    const long long ku = KEY(u);
-    E(u) = (eu > 0 && ku >= lo) ? eu : 0;
-  });
+  // keys taken per bucket: whole above the bracket, as the walk set them inside
+  // it; the buckets above the cutoff bin are the slices' (written already).
+  // (The bin's bounds are read back from LDS here: registers are short.)
+  {
+    // score <= the bin's top score exactly when the order key is <= that of
+    // (top score, bucket 0), the largest key with that score
+    const long long khs = order_key(s_fc[3], 0);
+    each([&](int u, int eu) {
+      const long long ku = KEY(u);
+      E(u) = (eu > 0 && ku >= lo && ku <= khs) ? eu : 0;
+    });
+  }
   __syncthreads();
   // output offsets in ascending bucket id: thread tid sums ids
   // [tid*PERT, tid*PERT + PERT), block scans join the chunks
@@ -729,8 +743,9 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   int packed_total;
   // (an overflowed bracket leaves more keys here; that result is discarded)
   const int packed = block_excl_scan<DT>((min(mine, 4096) << 16) | mcnt, s_ired, &packed_total);
-  int off = packed >> 16, rank = packed & 0xffff;     // the scan's barriers end all reads of s_e
-  const int out_total = packed_total >> 16, nt = packed_total & 0xffff;
+  const int gab = s_fc[1];             // keys above the cutoff bin
+  int off = gab + (packed >> 16), rank = packed & 0xffff;   // the scan's barriers end all reads of s_e
+  const int out_total = gab + (packed_total >> 16), nt = packed_total & 0xffff;
   const bool ok = !overflow && nt <= kListCap;
   // list of taken buckets (output offset, first key slot), ascending ids, over s_e
   l_off = s_e;
@@ -747,7 +762,7 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   }
   __syncthreads();
   if (ok) {
-    dec_emit_keys(V, A, seq, l_off, l_ks, nt, out_total);
+    dec_emit_keys(V, A, seq, l_off, l_ks, nt, out_total, gab);
     dec_finish_row(A, seq, t, out_total);
   }
   if (tid == 0) flags[seq] = ok ? 0 : 1;
@@ -905,9 +920,6 @@ size_t dec_layout(int32_t nseq, int32_t cap, DecWs* W, int32_t** flags, void* ws
   w.n_part = (cap + DT - 1) / DT;
   w.hpart = reinterpret_cast<int32_t*>(take((size_t)nseq * w.n_part * NBIN * sizeof(int32_t)));
   w.supmask = reinterpret_cast<uint32_t*>(take((size_t)nseq * kSupMaskWords * sizeof(uint32_t)));
-  w.above = reinterpret_cast<int32_t*>(take((size_t)nseq * sizeof(int32_t)));
-  w.cand = reinterpret_cast<long long*>(take((size_t)nseq * PERT_MAX * BCAP * sizeof(long long)));
-  w.ncand = reinterpret_cast<int32_t*>(take((size_t)nseq * PERT_MAX * sizeof(int32_t)));
   int32_t* f = reinterpret_cast<int32_t*>(take((size_t)nseq * sizeof(int32_t)));
   if (W) *W = w;
   if (flags) *flags = f;
@@ -984,46 +996,36 @@ hipError_t launch_select_dec(const IdxView* views, const int32_t* qpos, int32_t 
   }
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t ae = once_per_device(attr_done, []() {
-    hipError_t e = hipFuncSetAttribute((const void*)k_dec_select<20, true>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_dec_select<20>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(20));
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)k_dec_select<PERT_MAX, true>,
+    return hipFuncSetAttribute((const void*)k_dec_select<PERT_MAX>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, dec_lds(PERT_MAX));
   });
   if (ae != hipSuccess) return ae;
-  // one workgroup per slice of DT buckets of each sequence, then one per
-  // sequence to finish its row (the slice kernel's LDS: two lists of DT)
-  constexpr int kSliceLds = 2 * DT * 4;
-  const unsigned nslx = (unsigned)max(1, min((nmax + DT - 1) / DT, PERT_MAX));
+  // one workgroup per slice of DT buckets of each sequence, and one more
+  // (the last) that finishes the row
+  const unsigned nslx = (unsigned)max(1, min((nmax + DT - 1) / DT, PERT_MAX)) + 1;
   if (big) {
     // sequences above DT * PERT_MAX buckets: the streaming kernel (the other
     // kernels flag them and return; this one overwrites their flags); any
     // sequence flagged then goes to the exact kernel
     ae = once_per_device(big_done, big_attr);
     if (ae != hipSuccess) return ae;
-    if (nmin <= DT * PERT_MAX) {
-      hipLaunchKernelGGL((k_dec_select<PERT_MAX, false>), dim3(nslx, (unsigned)nseq), dim3(DT), kSliceLds, s,
+    if (nmin <= DT * PERT_MAX)
+      hipLaunchKernelGGL((k_dec_select<PERT_MAX>), dim3(nslx, (unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s,
                          vs, b, W, flags);
-      hipLaunchKernelGGL((k_dec_select<PERT_MAX, true>), dim3(1, (unsigned)nseq), dim3(DT), dec_lds(PERT_MAX),
-                         s, vs, b, W, flags);
-    }
     hipLaunchKernelGGL(k_dec_select_big, dim3((unsigned)nseq), dim3(DT), BIG_LDS, s, vs, b, W, flags, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     b.only = flags;
     return launch_select_multi(views, qpos, nseq, b, s);
   }
-  if (small) {
-    hipLaunchKernelGGL((k_dec_select<20, false>), dim3(nslx, (unsigned)nseq), dim3(DT), kSliceLds, s, vs, b, W,
-                       flags);
-    hipLaunchKernelGGL((k_dec_select<20, true>), dim3(1, (unsigned)nseq), dim3(DT), dec_lds(20), s, vs, b, W,
-                       flags);
-  } else {
-    hipLaunchKernelGGL((k_dec_select<PERT_MAX, false>), dim3(nslx, (unsigned)nseq), dim3(DT), kSliceLds, s, vs,
+  if (small)
+    hipLaunchKernelGGL((k_dec_select<20>), dim3(nslx, (unsigned)nseq), dim3(DT), dec_lds(20), s, vs, b, W, flags);
+  else
+    hipLaunchKernelGGL((k_dec_select<PERT_MAX>), dim3(nslx, (unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s, vs,
                        b, W, flags);
-    hipLaunchKernelGGL((k_dec_select<PERT_MAX, true>), dim3(1, (unsigned)nseq), dim3(DT), dec_lds(PERT_MAX), s,
-                       vs, b, W, flags);
-  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // The bracket always fits: every refinement pass narrows the key range by

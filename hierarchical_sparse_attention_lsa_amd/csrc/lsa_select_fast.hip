@@ -399,13 +399,18 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   {
     constexpr int TPW = CHT / C::PH;    // this wave's tiles per chunk: phase, phase + PH, ...
     static_assert(TPW % 4 == 0, "the full pass takes groups of four of a wave's tiles");
-    int slo[4];
     v4i bias;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      slo[v] = act[v] ? S.slo[qrow + v] : (1 << 30);    // 1<<30: no score reaches it
-      bias[v] = -slo[v];
-    }
+    for (int v = 0; v < 4; ++v) bias[v] = act[v] ? -S.slo[qrow + v] : -(1 << 30);   // 1<<30: no score reaches it
+    // each row's threshold as a scalar (selected by a run-time row below; an
+    // array would be placed in scratch memory)
+    const int sl0 = S.slo[qrow], sl1 = S.slo[qrow + 1], sl2 = S.slo[qrow + 2], sl3 = S.slo[qrow + 3];
+    // Without causal staging every bucket's first key reads as 0, so a hit is
+    // kept exactly when its row has long-range keys: one mask per group.
+    unsigned rows_ok = 0;
+    if (!DENSE && !causal)
+      rows_ok = (tl0 >= 0 ? 0x1111u : 0u) | (tl1 >= 0 ? 0x2222u : 0u) | (tl2 >= 0 ? 0x4444u : 0u) |
+                (tl3 >= 0 ? 0x8888u : 0u);
     // MODE 2: chunks [cb, ce) of this workgroup's key range, and the
     // (query, range) sub-list
     const int cb = MODE == 2 ? (int)((int64_t)krange * nchunks / kDenseSplit) : 0;
@@ -427,6 +432,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
 #pragma unroll
         for (int k = 15; k >= 0; --k) miss = __builtin_amdgcn_alignbit(miss, (unsigned)d[k], 31);
         unsigned hits = ~miss & 0xffffu;
+        if (!DENSE && !causal) hits &= rows_ok;
         const int tb = c * CHT + phase + C::PH * g;   // tile of u: tb + PH * u
         if ((c + 1) * CHT * 16 > V.n_bkt) {           // last chunk: no buckets past the end
 #pragma unroll
@@ -448,15 +454,21 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
           for (int i = 0; i < 2; ++i) z[i] = (y[2 * i + 1] & m2) | (y[2 * i] & ~m2);
           const int dk = (int)((z[1] & m3) | (z[0] & ~m3));
           const int v = k & 3, u = k >> 2;
-          // the row's threshold and position from LDS (hits are rare; a select
-          // over slo[] by a run-time v would be placed in scratch memory)
-          const int sv = S.slo[qrow + v];
-          const int tv = S.t[qrow + v] - A.window;
+          // row v's threshold and last long-range position, as bit selects (a
+          // select chain or an array indexed by v is turned into a table in
+          // scratch memory)
+          const int r0 = -(v & 1), r1 = -((v >> 1) & 1);
+          const int s01 = sl0 ^ ((sl0 ^ sl1) & r0), s23 = sl2 ^ ((sl2 ^ sl3) & r0);
+          const int t01 = tl0 ^ ((tl0 ^ tl1) & r0), t23 = tl2 ^ ((tl2 ^ tl3) & r0);
+          const int sv = s01 ^ ((s01 ^ s23) & r1);
+          const int tv = t01 ^ ((t01 ^ t23) & r1);
           const int beta = (tb + C::PH * u) * 16 + col;
           // a bucket whose first key is past the query's long-range range has no
-          // eligible key (first pooled id of bucket beta: chunk-local slot beta - c*CHT*16);
+          // eligible key (first pooled id of bucket beta: chunk-local slot beta - c*CHT*16;
+          // without causal staging rows_ok has filtered the hits already);
           // a dense key joins only when it is eligible itself
-          if (DENSE ? (beta >= A.sinks && beta <= tv) : S.fl[buf][beta - c * CHT * 16].x <= tv) {
+          if (DENSE ? (beta >= A.sinks && beta <= tv)
+                    : (!causal || S.fl[buf][beta - c * CHT * 16].x <= tv)) {
             const int qs = qrow + v;
             const int pos = atomicAdd(&S.nl[qs], 1);
             if (pos < lcap) W.key[(lbase + qs) * lstride + loff + pos] = order_key(dk + sv, beta);
