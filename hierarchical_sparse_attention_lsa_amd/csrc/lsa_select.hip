@@ -190,7 +190,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
           int w = 0, n = -1;
           if (i < V.n_top) {
             n = (int)(0xffffffffu - (unsigned)((-kk[i]) & 0xffffffffll));
-            w = top_eligible(V, n, tq, A.window, A.sinks);
+            w = top_eligible(V, n, tq, A.window, A.sinks, need);
           }
           const long long inc = wave_incl_scan((long long)w, 0ll, [](long long a, long long b) { return a + b; });
           if (n >= 0 && (i < R2 || held + inc - w < need))

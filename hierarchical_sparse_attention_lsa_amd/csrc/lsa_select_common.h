@@ -126,12 +126,17 @@ __device__ __forceinline__ int sup_eligible(const IdxView& V, int s, int t, int 
   return e;
 }
 
-// Eligible keys at t under top node n (third level): the sum over its supers.
-__device__ __forceinline__ int top_eligible(const IdxView& V, int n, int t, int window, int sinks) {
+// Eligible keys at t under top node n (third level): the sum over its
+// supers, stopped once it reaches `cap`.  The walks only ask whether a prefix
+// of these weights reaches the budget, so with cap = the budget a weight that
+// is exact below it and at least the budget otherwise gives the same answers;
+// a top node typically holds far more keys than the budget, and one or two of
+// its supers settle it.
+__device__ __forceinline__ int top_eligible(const IdxView& V, int n, int t, int window, int sinks, int cap) {
   const int32_t* m = V.tmem + V.toff[n];
   const int c = V.tcnt[n];
   int e = 0;
-  for (int j = 0; j < c; ++j) e += sup_eligible(V, m[j], t, window, sinks);
+  for (int j = 0; j < c && e < cap; ++j) e += sup_eligible(V, m[j], t, window, sinks);
   return e;
 }
 

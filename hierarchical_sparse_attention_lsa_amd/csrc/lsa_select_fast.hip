@@ -1192,7 +1192,7 @@ __global__ void __launch_bounds__(RT, 4) k_tree_select(FastViews VS, SelArgs A, 
       __syncthreads();
       const long long held_top = held_leaf + loose_sup_eligible(V, t, A.window, A.sinks);
       const int R2w = block_walk(s_sup, nr2, V.n_top, R2, held_top, need,
-                                 [&](int n) { return top_eligible(V, n, t, A.window, A.sinks); },
+                                 [&](int n) { return top_eligible(V, n, t, A.window, A.sinks, need); },
                                  L.ired, L.red);
       ok = R2w >= 0;
       if (ok) {
