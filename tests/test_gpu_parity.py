@@ -453,6 +453,28 @@ def test_dense_select_scan_path(early):
         assert torch.equal(torch.sort(idx[i, :n]).values, torch.sort(idx2[i, :n]).values), pos[i]
 
 
+def test_dense_select_scan_path_overflow():
+    """Every latent key the same: all of a query's scores tie, every key
+    passes its threshold and each of its key-range sub-lists overflows, so the
+    exact kernel serves every query; ties go to the lowest positions."""
+    dev = _dev()
+    L = _L()
+    T = 40000
+    row = torch.arange(64, dtype=torch.int64).remainder(23).sub(11).to(torch.int8)
+    latk = row.repeat(T, 1)
+    wl = S.WORKLOADS["tiny_flat"]
+    g = S.Synth(wl)
+    rng = np.random.default_rng(7)
+    pos = sorted(set(rng.integers(20000, T, 70).tolist()) | {T - 1})
+    lq = g.latq_rows(torch.tensor(pos))
+    sp = L.SelectParams(300, 128, 4, 0)
+    osp = O.SelectParams(300, 128, 4)
+    qp = torch.tensor(pos, dtype=torch.int32, device=dev)
+    idx, cnt = L.dense_select(latk.to(dev), lq.to(dev), qp, sp)
+    refs = [O.dense_select(latk.numpy(), lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    check_selection(idx, cnt, refs, sp.max_sel)
+
+
 @pytest.mark.parametrize("tree_iters", [3, 1])
 def test_tree_index_and_selection(tree_iters):
     """Two-level Tree index and selections; the super level runs its own
