@@ -103,12 +103,12 @@ struct __attribute__((aligned(16))) ScanLds {
 };
 
 // Runs f(c, buf) for chunks c = c0, c0 + step, ... < nchunks with chunk c
-// staged in LDS buffer buf.  Two later chunks are in flight in registers
-// while f runs (stages A and B take turns, so no register copy waits on a
+// staged in LDS buffer buf.  NSTG later chunks are in flight in registers
+// while f runs (the stages take turns, so no register copy waits on a
 // load), and each goes to the other LDS buffer after f.
 // DENSE: the "centroids" are the latent keys themselves, each its own bucket
 // of one key (pool 1): no bucket records are read.
-template <bool DENSE, int FW, int QS, class F>
+template <bool DENSE, int NSTG, int FW, int QS, class F>
 __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>& S, int c0,
                                               int step, int nchunks, bool causal, F&& f) {
   using C = Cfg<FW, QS>;
@@ -144,29 +144,27 @@ __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>&
       if (k * C::FT + tid < CHT * 64) S.cent[buf][k * C::FT + tid] = st.r[k];
     if (tid < CHT * 16) { S.cnt[buf][tid] = st.rc; S.fl[buf][tid] = st.rfl; }
   };
-  Stage A, B;
-  if (c0 < nchunks) { gload(A, c0); swrite(A, 0); }
-  if (c0 + step < nchunks) gload(A, c0 + step);
-  if (c0 + 2 * step < nchunks) gload(B, c0 + 2 * step);
+  Stage st[NSTG];
+  if (c0 < nchunks) { gload(st[0], c0); swrite(st[0], 0); }
+#pragma unroll
+  for (int k = 0; k < NSTG; ++k)
+    if (c0 + (k + 1) * step < nchunks) gload(st[k], c0 + (k + 1) * step);
   __syncthreads();
   int buf = 0;
   int c = c0;
-  // invariant at the top: chunk c in LDS[buf], A holds c + step, B holds c + 2 step
+  // invariant at the top of step k: chunk c in LDS[buf], stage (k + j) % NSTG
+  // holds chunk c + (j + 1) step for j < NSTG
   while (c < nchunks) {
-    f(c, buf);
-    if (c + step < nchunks) swrite(A, buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    if (c + 3 * step < nchunks) gload(A, c + 3 * step);
-    c += step;
-    if (c >= nchunks) break;
-    // here B holds c + step and A c + 2 step
-    f(c, buf);
-    if (c + step < nchunks) swrite(B, buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    if (c + 3 * step < nchunks) gload(B, c + 3 * step);
-    c += step;
+#pragma unroll
+    for (int k = 0; k < NSTG; ++k) {
+      f(c, buf);
+      if (c + step < nchunks) swrite(st[k], buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      if (c + (NSTG + 1) * step < nchunks) gload(st[k], c + (NSTG + 1) * step);
+      c += step;
+      if (c >= nchunks) break;
+    }
   }
 }
 
@@ -182,6 +180,9 @@ __device__ __forceinline__ void stream_chunks(const IdxView& V, ScanLds<FW, QS>&
 template <int FW, int QS, bool DENSE, int MODE = 0>
 __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListWs W) {
   using C = Cfg<FW, QS>;
+  // chunks in flight in registers: three where registers allow it without
+  // costing occupancy, two for the dense full pass (three workgroups per CU)
+  constexpr int kStages = 4;
   static_assert(MODE == 0 || DENSE, "only the dense scan is split");
   __shared__ ScanLds<FW, QS> S;
   const FastViews* vsp = (const FastViews*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -246,7 +247,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   {
     int smax[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN}, sn[4] = {0, 0, 0, 0};
     long long ssum[4] = {0, 0, 0, 0};
-    stream_chunks<DENSE>(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
+    stream_chunks<DENSE, kStages>(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
       for (int tl = phase; tl < CHT; tl += C::PH) {
         const v4i z = {0, 0, 0, 0};
         const v4i sc = mfma_i8_16x16x64(qa, S.cent[buf][tl * 64 + lane], z);
@@ -280,7 +281,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
   // bucket counts with all its keys when they are all long-range for the
   // query (the index may hold keys past it), else not at all.
   auto sample_hist = [&](const int (&lo)[4], const int (&hi)[4], const int (&sh)[4]) __attribute__((always_inline)) {
-    stream_chunks<DENSE>(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
+    stream_chunks<DENSE, kStages>(V, S, 0, sstep, nchunks, causal, [&](int c, int buf) __attribute__((always_inline)) {
       for (int tl = phase; tl < CHT; tl += C::PH) {
         const v4i z = {0, 0, 0, 0};
         const v4i sc = mfma_i8_16x16x64(qa, S.cent[buf][tl * 64 + lane], z);
@@ -418,7 +419,7 @@ __global__ void __launch_bounds__(FW * 64) k_scan(FastViews VS, SelArgs A, ListW
     constexpr int lcap = MODE == 2 ? kDenseSub : LC;
     const int64_t lstride = MODE == 2 ? kDenseList : LC;
     const int64_t loff = MODE == 2 ? (int64_t)krange * kDenseSub : 0;
-    stream_chunks<DENSE>(V, S, cb, 1, ce, causal, [&](int c, int buf) __attribute__((always_inline)) {
+    stream_chunks<DENSE, kStages>(V, S, cb, 1, ce, causal, [&](int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < TPW; g += 4) {
         int d[16];
