@@ -413,11 +413,11 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
   __shared__ int s_nt, s_nb;
   __shared__ int s_ce[BCAP], s_re[BCAP], s_rs[BCAP];
   __shared__ int s_fc[4];              // cut bin, keys above it, its scores [lo, hi]
+  // bins from the top score down: thread tid takes bins NBIN-1-2tid (he[0])
+  // and NBIN-2-2tid (he[1]), summed over the score workgroups (the slices),
+  // and the same over the slices before this one (hb) and this one (hm)
+  int he[2] = {0, 0}, hb[2] = {0, 0}, hm[2] = {0, 0};
   {
-    // bins from the top score down: thread tid takes bins NBIN-1-2tid (he[0])
-    // and NBIN-2-2tid (he[1]), summed over the score workgroups (the slices),
-    // and the same over the slices before this one (hb) and this one (hm)
-    int he[2] = {0, 0}, hb[2] = {0, 0}, hm[2] = {0, 0};
     {
       const int2* hp = reinterpret_cast<const int2*>(W.hpart + (int64_t)seq * W.n_part * NBIN) + (NBIN / 2 - 1 - tid);
       const int nh = (n + DT - 1) / DT;    // score workgroups that wrote a histogram (0 for an empty index)
@@ -460,7 +460,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       }
     }
     __syncthreads();
-    if (fin) goto finish;              // uniform
+  }
+  if (!fin) {                          // uniform: a slice's workgroup
     const int cut = s_fc[0], hi_s = s_fc[3];
     // keys above the cut bin in the earlier slices (this slice's output
     // offset) and in this one; both at most the budget
@@ -486,9 +487,8 @@ __global__ void __launch_bounds__(DT) k_dec_select(DecViews VS, SelArgs A, DecWs
       __syncthreads();
       dec_emit_keys(V, A, seq, l_off, l_ks, tot & 0xffff, before + mine, before);
     }
+    return;
   }
-  return;
-finish:
   // ---- the finishing workgroup: the cutoff bin and the rest of the row ----
   const int above = s_fc[1], lo_s = s_fc[2], hi_s = s_fc[3];
   {
