@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "liblsa_hip.so")
 
 c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
-OP_BUILD, OP_APPEND, OP_SELECT, OP_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE, OP_ATTN_BWD = range(8)
+(OP_BUILD, OP_APPEND, OP_SELECT, OP_ATTN, OP_PREFILL, OP_DECODE, OP_DENSE, OP_ATTN_BWD,
+ OP_ATTN_GROUPED) = range(9)
 
 
 class IndexParams(ctypes.Structure):
@@ -68,6 +69,9 @@ EXPORTS = {
     "lsa_sparse_attn_window": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                        ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                        c_vp, c_vp]),
+    "lsa_sparse_attn_grouped": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
+                                        ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                        c_vp, c_vp, c_sz, c_vp]),
     "lsa_sparse_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                     ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                     c_vp, c_vp, c_vp]),
@@ -311,6 +315,30 @@ def sparse_attn_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: t
     _check(lib().lsa_sparse_attn_window(_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt),
                                         idx.shape[1], nq, qpos0, ctypes.byref(sp), ctypes.byref(ap),
                                         _ptr(out), _stream(stream)), "lsa_sparse_attn_window")
+    return out
+
+
+def sparse_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                        cnt: torch.Tensor, qpos0: int, sp: SelectParams, ap: AttnParams,
+                        out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """sparse_attn_window with each group of 16/G queries (ordered by their
+    rows' first key) reading the union of its long-range keys once."""
+    nq = q.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, torch.bfloat16, name)
+    _need(idx, torch.int32, "idx")
+    _need(cnt, torch.int32, "cnt", (nq,))
+    if out is None:
+        out = torch.empty((nq, ap.Hq, ap.D), dtype=torch.float32 if ap.out_f32 else torch.bfloat16,
+                          device=q.device)
+    wsb = workspace_bytes(OP_ATTN_GROUPED, None, sp, ap, nq)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().lsa_sparse_attn_grouped(_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt),
+                                         idx.shape[1], nq, qpos0, ctypes.byref(sp), ctypes.byref(ap),
+                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "lsa_sparse_attn_grouped")
     return out
 
 

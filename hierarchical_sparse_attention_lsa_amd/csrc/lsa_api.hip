@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -481,8 +482,20 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
       return LSA_OK;
     case LSA_OP_PREFILL: {
       if (int e = check_select_params(sprm, false)) return e;
-      *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4) +
-               select_fast_ws_bytes((int32_t)n);
+      size_t phase = select_fast_ws_bytes((int32_t)n);
+      if (aprm) {
+        if (int e = check_attn_params(aprm)) return e;
+        if (grouped_attn_ok(*aprm, sprm->budget, 1))
+          phase = std::max(phase, attn_grouped_ws_bytes((int32_t)n, *aprm, sprm->budget));
+      }
+      *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4) + phase;
+      return LSA_OK;
+    }
+    case LSA_OP_ATTN_GROUPED: {
+      if (int e = check_select_params(sprm, false)) return e;
+      if (int e = check_attn_params(aprm)) return e;
+      if (n > INT32_MAX) return fail(LSA_E_ARG, "n > INT32_MAX");
+      *bytes = attn_grouped_ws_bytes((int32_t)n, *aprm, sprm->budget);
       return LSA_OK;
     }
     case LSA_OP_DECODE: {
@@ -590,6 +603,25 @@ int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, const uint1
   return LSA_OK;
 }
 
+int lsa_sparse_attn_grouped(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                            int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                            int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
+                            const lsa_attn_params* ap, void* d_out, void* d_ws, size_t ws_bytes,
+                            void* stream) {
+  if (int e = check_window_attn(kv_rows, max_sel, nq, qpos0, sp, ap)) return e;
+  if (!grouped_attn_ok(*ap, sp->budget, kv_rows))
+    return fail(LSA_E_UNSUPPORTED, "grouped attention needs D in {64, 128}, Hq/Hkv in {4, 8, 16}, "
+                "(16 / (Hq/Hkv)) * budget <= 16384 and kv_rows < 2^29");
+  if (nq == 0) return LSA_OK;
+  if (!d_q || !d_k || !d_v || !d_idx || !d_cnt || !d_out) return fail(LSA_E_ARG, "NULL buffer");
+  const size_t need = attn_grouped_ws_bytes(nq, *ap, sp->budget);
+  if (!d_ws || ws_bytes < need) return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
+  LSA_HIP(launch_attn_grouped(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp->window,
+                              sp->sinks, sp->budget, *ap, d_out, d_ws, static_cast<hipStream_t>(stream)),
+          "grouped attention");
+  return LSA_OK;
+}
+
 int lsa_sparse_attn_fwd(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
                         int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
                         int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
@@ -673,6 +705,13 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
   rc = select_impl(h, d_latq, nullptr, (int32_t)t0, (int32_t)n_chunk, sp, idx, cnt, sel_ws,
                    select_fast_ws_bytes((int32_t)n_chunk), s);
   if (rc != LSA_OK) return rc;
+  if (grouped_attn_ok(*ap, sp->budget, kv_rows) &&
+      ws_bytes - a_idx >= attn_grouped_ws_bytes((int32_t)n_chunk, *ap, sp->budget)) {
+    LSA_HIP(launch_attn_grouped(d_q, d_k, d_v, kv_rows, idx, cnt, max_sel, (int32_t)n_chunk, t0,
+                                sp->window, sp->sinks, sp->budget, *ap, d_out, sel_ws, s),
+            "grouped attention");
+    return LSA_OK;
+  }
   LSA_HIP(launch_attn_window(d_q, d_k, d_v, kv_rows, idx, cnt, max_sel, (int32_t)n_chunk, t0,
                              sp->window, sp->sinks, *ap, d_out, nullptr, s),
           "attention");

@@ -24,9 +24,11 @@
 // overlap.
 #include <climits>
 #include <cstring>
+#include <utility>
 
 #include "lsa_device.h"
 #include "lsa_internal.h"
+#include "lsa_select_common.h"
 
 namespace lsa {
 
@@ -59,6 +61,15 @@ struct AttnArgs {
   int32_t window, sinks;
   int32_t qpw;               // queries per wave (16 / G)
   float* lse;                // nullable [nq][Hq]: natural log-sum-exp of the scaled logits
+  // grouped mode: a wave's queries are perm[gi*qpw ..]; their long-range rows
+  // are the union urow[gi][0 .. ucnt[gi]) with umask bit j set for the
+  // group's query j; the sinks and window come from the window partials
+  // (part_o [nq][Hq][D], part_ml [nq][Hq][2])
+  const int32_t* perm;
+  const int32_t* urow;
+  const uint8_t* umask;
+  const int32_t* ucnt;
+  int32_t ucap;
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int nwg) {
@@ -306,7 +317,10 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
 // group's sinks and windows once, as contiguous K/V rows, each column masked
 // to its own query's sinks and window.  Per query the result is the same
 // attention over the same key set; only the summation order differs.
-template <int D, bool OUT_F32>
+// WIN = 1: only the sinks and the window (phase 2), the unnormalised result
+// and (max, sum) per (query, head) to part_o / part_ml for the grouped
+// long-range kernel.
+template <int D, bool OUT_F32, int WIN = 0>
 __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   constexpr int NKK = D / 32;
   constexpr int NB = D / 16;
@@ -367,7 +381,7 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   auto nsink_of = [&](int ws) { return max(0, min(a.sinks, ws)); };
 
   // 1. long-range keys of each query: the row's entries before its sinks and window
-  for (int j = 0; j < nqw; ++j) {
+  for (int j = 0; j < (WIN ? 0 : nqw); ++j) {
     const int q = q0 + j;
     const int t = tq0 + j;
     const int ws = wstart_of(t);
@@ -422,11 +436,309 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
     const float mh = __shfl(m_run, col);
     const int j = col / G, h = col % G;
     if (j >= nqw) continue;
+    if (WIN) {                         // partial result of the sinks and window
+      const int64_t pr = (int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) a.part_o[pr * D + 16 * nb + hl] = o[nb][v];
+      if (hl == 0) { a.part_ml[2 * pr] = mh; a.part_ml[2 * pr + 1] = lh; }
+      continue;
+    }
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     const int64_t ob = ((int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h) * D;
     // log-sum-exp: m_run and l_run are in the log2 domain of the scaled logits
     if (a.lse && hl == 0) a.lse[(int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h] =
         (mh + __log2f(lh)) * 0.6931471805599453f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float val = o[nb][v] * inv;
+      if (OUT_F32) reinterpret_cast<float*>(a.out)[ob + 16 * nb + hl] = val;
+      else reinterpret_cast<uint16_t*>(a.out)[ob + 16 * nb + hl] = (uint16_t)f32_to_bf16_bits(val);
+    }
+  }
+}
+
+// ---- grouped long-range attention ----
+// Queries with similar selections share most of their long-range keys (the
+// select writes a row's best bucket first, so equal first keys mean the same
+// best bucket).  The queries are sorted by (first long-range key, index) and
+// taken qpw at a time; each group's long-range rows are merged into one list
+// with a mask of the queries that selected each row, so a shared K/V row is
+// read once per group instead of once per query.  The sinks and window are
+// attended separately, in position order (k_attn_win<.., 1>), and the grouped
+// kernel starts each query's softmax state from that partial result.
+
+// Long-range entries of a row: the select's rows end with the sinks and window.
+__device__ __forceinline__ int long_range_count(const AttnArgs& a, int q) {
+  const int t = (int)a.qpos0 + q;
+  const int ws = max(0, t - a.window + 1);
+  const int nfix = max(0, min(a.sinks, ws)) + (t - ws + 1);
+  return max(0, min(a.cnt[q], a.max_sel) - nfix);
+}
+
+// Sort key of query q: (first long-range key, q); padding sorts last.
+__global__ void k_grp_key(AttnArgs a, unsigned long long* keys, int n_pad) {
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_pad) return;
+  unsigned long long k = ~0ull;
+  if (q < a.nq) {
+    const int first = long_range_count(a, q) > 0 ? a.idx[(int64_t)q * a.max_sel] : 0x7fffffff;
+    k = ((unsigned long long)(unsigned)first << 32) | (unsigned)q;
+  }
+  keys[q] = k;
+}
+
+// Ascending bitonic sort of each run of GS_TILE keys (GS_T threads, two each).
+constexpr int GS_T = 1024, GS_TILE = 2 * GS_T;
+__global__ void __launch_bounds__(GS_T) k_grp_sort_tile(unsigned long long* keys) {
+  __shared__ unsigned long long s[GS_TILE];
+  unsigned long long* base = keys + (int64_t)blockIdx.x * GS_TILE;
+  const int tid = threadIdx.x;
+  s[tid] = base[tid];
+  s[tid + GS_T] = base[tid + GS_T];
+  __syncthreads();
+  for (int k = 2; k <= GS_TILE; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < GS_TILE; i += GS_T) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long x = s[i], y = s[ixj];
+          if ((x > y) == ((i & k) == 0)) { s[i] = y; s[ixj] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  base[tid] = s[tid];
+  base[tid + GS_T] = s[tid + GS_T];
+}
+
+// Merge sorted runs of w keys pairwise into runs of 2w: a key's output slot
+// is its index in its run plus the number of keys of the partner run that go
+// before it (smaller ones; for the right run also equal ones, so equal keys
+// such as the padding keep distinct slots).
+__global__ void k_grp_merge(const unsigned long long* in, unsigned long long* out, int n, int w) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int r = i / w, o = i % w;
+  const bool right = r & 1;
+  const unsigned long long x = in[i];
+  const unsigned long long* other = in + (int64_t)(r ^ 1) * w;
+  int lo = 0, hi = w;
+  while (lo < hi) {
+    const int m = (lo + hi) >> 1;
+    if (other[m] < x || (right && other[m] == x)) lo = m + 1; else hi = m;
+  }
+  out[(int64_t)(r & ~1) * w + o + lo] = x;
+}
+
+__global__ void k_grp_perm(const unsigned long long* keys, int32_t* perm, int nq) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nq) perm[i] = (int32_t)(keys[i] & 0xffffffffull);
+}
+
+// Union of a group's long-range rows: the keys, tagged with the query's slot
+// in the group (key << 2 | slot), sorted; equal keys become one row whose
+// mask has a bit per slot (a row holds a key at most once, so a run of equal
+// keys is at most qpw <= 4 long).  One workgroup of GU_T threads per group;
+// N = the sort size, at least qpw times the per-query cap.  A group with a
+// row over the cap gets ucnt = -1 and is walked row by row instead.
+constexpr int GU_T = 1024;
+template <int N>
+__global__ void __launch_bounds__(GU_T) k_grp_union(AttnArgs a, int lcap, int32_t* urow,
+                                                    uint8_t* umask, int32_t* ucnt) {
+  constexpr int PT = N / GU_T;
+  __shared__ unsigned s[N];
+  __shared__ int red[GU_T / 64];
+  const int tid = threadIdx.x;
+  const int gi = blockIdx.x;
+  const int QPW = a.qpw;
+  int qs[4] = {0, 0, 0, 0}, pre[5] = {0, 0, 0, 0, 0};
+  bool over = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = gi * QPW + j;
+    const bool in = j < QPW && slot < a.nq;
+    qs[j] = in ? a.perm[slot] : 0;
+    const int n = in ? long_range_count(a, qs[j]) : 0;
+    over |= n > lcap;
+    pre[j + 1] = pre[j] + n;
+  }
+  if (over) {                          // block-uniform
+    if (tid == 0) ucnt[gi] = -1;
+    return;
+  }
+  const int total = pre[4];            // <= 4 * lcap <= N
+  unsigned v[PT];
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int e = tid * PT + k;
+    unsigned x = 0xffffffffu;
+    if (e < total) {
+      const int j = (e >= pre[1]) + (e >= pre[2]) + (e >= pre[3]);
+      const int qj = j == 0 ? qs[0] : j == 1 ? qs[1] : j == 2 ? qs[2] : qs[3];
+      const int pj = j == 0 ? pre[0] : j == 1 ? pre[1] : j == 2 ? pre[2] : pre[3];
+      const int key = a.idx[(int64_t)qj * a.max_sel + (e - pj)];
+      x = ((unsigned)min(max(key, 0), (int)(a.kv_rows - 1)) << 2) | (unsigned)j;
+    }
+    v[k] = x;
+  }
+  sel::block_bitonic<N, GU_T>(v, s);
+  __syncthreads();                     // the sort's last reads of s are done
+#pragma unroll
+  for (int k = 0; k < PT; ++k) s[tid * PT + k] = v[k];
+  __syncthreads();
+  // heads of runs of equal keys, and each head's mask of slots
+  int heads = 0;
+  unsigned hm[PT];
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int i = tid * PT + k;
+    const unsigned x = v[k];
+    const bool head = x != 0xffffffffu && (i == 0 || (s[i - 1] >> 2) != (x >> 2));
+    unsigned m = 0;
+    if (head) {
+      m = 1u << (x & 3u);
+#pragma unroll
+      for (int d = 1; d < 4; ++d) {
+        const unsigned y = i + d < N ? s[i + d] : 0xffffffffu;
+        if (y != 0xffffffffu && (y >> 2) == (x >> 2)) m |= 1u << (y & 3u);
+      }
+    }
+    hm[k] = m;
+    heads += head ? 1 : 0;
+  }
+  int nh;
+  int pos = sel::block_excl_scan<GU_T>(heads, red, &nh);
+  int32_t* ur = urow + (int64_t)gi * a.ucap;
+  uint8_t* um = umask + (int64_t)gi * a.ucap;
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    if (hm[k]) {
+      ur[pos] = (int32_t)(v[k] >> 2);
+      um[pos] = (uint8_t)hm[k];
+      ++pos;
+    }
+  }
+  if (tid == 0) ucnt[gi] = nh;
+}
+
+// One wave per (group, KV head): the group's qpw queries x G heads are the
+// 16 columns; the state starts from the sinks-and-window partial, then the
+// union rows are walked once, each column masked to the rows its query took.
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(AT, 4) k_attn_grp(AttnArgs a) {
+  constexpr int NKK = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int VROW = D * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char vlds[AW][KT * VROW];
+  __shared__ __attribute__((aligned(16))) char qlds[AW][16 * qrow_bytes(D)];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int nwg = gridDim.x;
+  const int item = xcd_remap(blockIdx.x, nwg) * AW + wave;
+  const int QPW = a.qpw;
+  const int ngrp = (a.nq + QPW - 1) / QPW;
+  if (item >= ngrp * a.Hkv) return;
+  const int g = item % a.Hkv;
+  const int gi = item / a.Hkv;
+  const int G = a.G;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  // this lane's column: query slot jc of the group, head hc of the KV group
+  const int jc = hl / G, hc = hl % G;
+  const int slot = gi * QPW + jc;
+  const bool cval = jc < QPW && slot < a.nq;
+  const int qc = cval ? a.perm[slot] : 0;
+
+  const int64_t rowstride = (int64_t)a.Hkv * D;
+  const int64_t rmax = a.kv_rows - 1;
+
+  char* ql = qlds[wave];
+  {
+    const uint16_t* qp = a.q + ((int64_t)qc * a.Hq + (int64_t)g * G + hc) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      v4i raw = cval ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
+      *reinterpret_cast<v4i*>(ql + hl * qrow_bytes(D) + (32 * kk + 8 * grp) * 2) = raw;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const QLds<D> qb{ql + hl * qrow_bytes(D) + 16 * grp};
+
+  // state of the sinks and window: o for columns 4*grp + v, (m, l) for column hl
+  v4f o[NB];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int col = 4 * grp + v;
+    const int qv = __shfl(qc, col);
+    const bool vv = __shfl((int)cval, col) != 0;
+    const int64_t pr = (int64_t)qv * a.Hq + (int64_t)g * G + col % G;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb][v] = vv ? a.part_o[pr * D + 16 * nb + hl] : 0.f;
+  }
+  float m_run = -1e30f, l_run = 0.f;
+  if (cval) {
+    const int64_t pr = (int64_t)qc * a.Hq + (int64_t)g * G + hc;
+    m_run = a.part_ml[2 * pr];
+    l_run = grp == 0 ? a.part_ml[2 * pr + 1] : 0.f;   // the lanes' partial sums are added at the end
+  }
+
+  char* vl = vlds[wave];
+  const uint16_t* kbase = a.k + (int64_t)g * D;
+  const uint16_t* vbase = a.v + (int64_t)g * D;
+  const int nu = a.ucnt[gi];
+  if (nu >= 0) {
+    const int32_t* ur = a.urow + (int64_t)gi * a.ucap;
+    const uint8_t* um = a.umask + (int64_t)gi * a.ucap;
+    for (int kb = 0; kb < nu; kb += KT) {
+      const int s = kb + hl;
+      int r = s < nu ? ur[s] : 0;
+      r = (int)min((int64_t)max(r, 0), rmax);
+      // masks of union rows kb + 4 grp .. +3 (ucap is a multiple of 4)
+      const int k4 = kb + 4 * grp;
+      const unsigned m4 = k4 < nu ? *reinterpret_cast<const unsigned*>(um + k4) : 0u;
+      unsigned vmask = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bool in = cval && k4 + v < nu && ((m4 >> (8 * v + jc)) & 1u);
+        vmask |= (in ? 1u : 0u) << v;
+      }
+      attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
+    }
+  } else {
+    // a row over the union cap: each query's long-range keys in turn
+    for (int j = 0; j < QPW; ++j) {
+      const int sl = gi * QPW + j;
+      if (sl >= a.nq) break;
+      const int q = a.perm[sl];
+      const int nlr = long_range_count(a, q);
+      const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
+      const bool mine = cval && jc == j;
+      for (int kb = 0; kb < nlr; kb += KT) {
+        const int slot = kb + hl;
+        int r = slot < nlr ? idxrow[slot] : 0;
+        r = (int)min((int64_t)max(r, 0), rmax);
+        unsigned vmask = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vmask |= (mine && kb + 4 * grp + v < nlr ? 1u : 0u) << v;
+        attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
+      }
+    }
+  }
+
+  l_run = finish_l(l_run);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int col = 4 * grp + v;
+    const float lh = __shfl(l_run, col);
+    const int qv = __shfl(qc, col);
+    const bool vv = __shfl((int)cval, col) != 0;
+    if (!vv) continue;
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const int64_t ob = ((int64_t)qv * a.Hq + (int64_t)g * G + col % G) * D;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float val = o[nb][v] * inv;
@@ -688,6 +1000,131 @@ hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16
   } else {
     if (f32) hipLaunchKernelGGL((k_attn_win<64, true>), dim3(grid), dim3(AT), 0, s, a);
     else hipLaunchKernelGGL((k_attn_win<64, false>), dim3(grid), dim3(AT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr int kGrpMinSort = GS_TILE;
+int grp_sort_n(int32_t nq) {
+  int n = kGrpMinSort;
+  while (n < nq) n <<= 1;
+  return n;
+}
+int grp_union_n(int qpw, int32_t lcap) {
+  int n = GU_T;
+  while (n < qpw * lcap) n <<= 1;
+  return n;
+}
+struct GrpLayout {
+  size_t keys_a, keys_b, perm, part_o, part_ml, urow, umask, ucnt, total;
+  int n_pad, qpw, ngrp, ucap;
+};
+GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
+  GrpLayout L;
+  const int G = ap.Hq / ap.Hkv;
+  L.qpw = 16 / G;
+  L.n_pad = grp_sort_n(nq);
+  L.ngrp = (nq + L.qpw - 1) / L.qpw;
+  L.ucap = (L.qpw * lcap + 3) & ~3;
+  size_t o = 0;
+  L.keys_a = o; o += al256((size_t)L.n_pad * 8);
+  L.keys_b = o; o += al256((size_t)L.n_pad * 8);
+  L.perm = o; o += al256((size_t)nq * 4);
+  L.part_o = o; o += al256((size_t)nq * ap.Hq * ap.D * 4);
+  L.part_ml = o; o += al256((size_t)nq * ap.Hq * 2 * 4);
+  L.urow = o; o += al256((size_t)L.ngrp * L.ucap * 4);
+  L.umask = o; o += al256((size_t)L.ngrp * L.ucap);
+  L.ucnt = o; o += al256((size_t)L.ngrp * 4);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows) {
+  if (ap.D != 64 && ap.D != 128) return false;
+  if (ap.Hkv <= 0 || ap.Hq % ap.Hkv != 0) return false;
+  const int G = ap.Hq / ap.Hkv;
+  if (G != 4 && G != 8 && G != 16) return false;
+  if (lcap < 1 || (16 / G) * (int64_t)lcap > 16384) return false;
+  return kv_rows >= 1 && kv_rows < (int64_t)1 << 29;     // key << 2 | slot fits 31 bits
+}
+
+size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
+  if (nq <= 0) return 0;
+  return grp_layout(nq, ap, lcap).total;
+}
+
+hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
+                               int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
+                               int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
+                               void* ws, hipStream_t s) {
+  if (nq <= 0) return hipSuccess;
+  if (!grouped_attn_ok(ap, lcap, kv_rows)) return hipErrorInvalidValue;
+  const GrpLayout L = grp_layout(nq, ap, lcap);
+  char* w = static_cast<char*>(ws);
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q; a.k = k; a.v = v; a.kv_rows = kv_rows; a.seq_stride_rows = 0; a.qdiv = 1;
+  a.idx = idx; a.cnt = cnt; a.max_sel = max_sel; a.nq = nq;
+  a.Hq = ap.Hq; a.Hkv = ap.Hkv; a.G = ap.Hq / ap.Hkv;
+  a.splits = 1;
+  const float scale = ap.scale > 0.f ? ap.scale : 1.0f / sqrtf((float)ap.D);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.qpos0 = qpos0; a.window = window; a.sinks = sinks;
+  a.qpw = L.qpw;
+  a.part_o = reinterpret_cast<float*>(w + L.part_o);
+  a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+  int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
+  int32_t* urow = reinterpret_cast<int32_t*>(w + L.urow);
+  uint8_t* umask = reinterpret_cast<uint8_t*>(w + L.umask);
+  int32_t* ucnt = reinterpret_cast<int32_t*>(w + L.ucnt);
+  a.perm = perm; a.urow = urow; a.umask = umask; a.ucnt = ucnt; a.ucap = L.ucap;
+  const unsigned grid = (unsigned)(((size_t)L.ngrp * ap.Hkv + AW - 1) / AW);
+  const bool f32 = ap.out_f32 != 0;
+
+  // 1. sinks and window of every query, in position order, as partials
+  if (ap.D == 128) hipLaunchKernelGGL((k_attn_win<128, false, 1>), dim3(grid), dim3(AT), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_win<64, false, 1>), dim3(grid), dim3(AT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // 2. the order of the queries: sort (first long-range key, query)
+  unsigned long long* ka = reinterpret_cast<unsigned long long*>(w + L.keys_a);
+  unsigned long long* kb = reinterpret_cast<unsigned long long*>(w + L.keys_b);
+  hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, a, ka, L.n_pad);
+  hipLaunchKernelGGL(k_grp_sort_tile, dim3(L.n_pad / GS_TILE), dim3(GS_T), 0, s, ka);
+  for (int wd = GS_TILE; wd < L.n_pad; wd <<= 1) {
+    hipLaunchKernelGGL(k_grp_merge, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, ka, kb, L.n_pad, wd);
+    std::swap(ka, kb);
+  }
+  hipLaunchKernelGGL(k_grp_perm, dim3((nq + 255) / 256), dim3(256), 0, s, ka, perm, nq);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // 3. the groups' unions of long-range rows
+  const int un = grp_union_n(L.qpw, lcap);
+  switch (un) {
+    case 1024: hipLaunchKernelGGL((k_grp_union<1024>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+    case 2048: hipLaunchKernelGGL((k_grp_union<2048>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+    case 4096: hipLaunchKernelGGL((k_grp_union<4096>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+    case 8192: hipLaunchKernelGGL((k_grp_union<8192>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+    case 16384: hipLaunchKernelGGL((k_grp_union<16384>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+    default: return hipErrorInvalidValue;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // 4. the unions, each column masked to its query's rows, on top of the partials
+  if (ap.D == 128) {
+    if (f32) hipLaunchKernelGGL((k_attn_grp<128, true>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_grp<128, false>), dim3(grid), dim3(AT), 0, s, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((k_attn_grp<64, true>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_grp<64, false>), dim3(grid), dim3(AT), 0, s, a);
   }
   return hipGetLastError();
 }

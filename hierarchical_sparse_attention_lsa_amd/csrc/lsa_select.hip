@@ -59,6 +59,7 @@ struct __attribute__((aligned(16))) SelLds {
   int sn[QT];
   int nfull[QT], ncand[QT], fullsum[QT];
   int pbeta[QT], ptake[QT];
+  long long topk[QT];      // order key of the best taken bucket (LLONG_MIN: none)
   int any_refine;
   unsigned supmask[QT][MAXSUPW];
   union {
@@ -145,6 +146,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
     S.status[tid] = val ? ST_REFINE : ST_DONE;
     S.smax[tid] = INT_MIN; S.ssum[tid] = 0; S.sn[tid] = 0; S.above[tid] = 0;
     S.nfull[tid] = 0; S.ncand[tid] = 0; S.fullsum[tid] = 0; S.pbeta[tid] = -1; S.ptake[tid] = 0;
+    S.topk[tid] = LLONG_MIN;
     S.lo[tid] = KMINP; S.hi[tid] = KMAXP;
     if (val && budget_at(A, S.t[tid]) <= 0) { S.status[tid] = ST_DONE; S.lo[tid] = KMAXP + 1; S.hi[tid] = KMAXP; }
   }
@@ -443,6 +445,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
           const int j = atomicAdd(&S.nfull[qi], 1);
           A.idx[(int64_t)(q0 + qi) * A.max_sel + j] = beta;
           atomicAdd(&S.fullsum[qi], e);
+          atomicMax(&S.topk[qi], K);
         } else {
           const int c = atomicAdd(&S.ncand[qi], 1);
           if (c < CAP) S.u.cand[qi][c] = -K;      // ascending sort = K descending
@@ -475,6 +478,7 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
         int tot;
         const int before = wave_excl_scan(e, &tot);
         const int take = min(e, max(0, need - before));
+        if (i == 0 && take > 0) atomicMax(&S.topk[qi], -cq[0]);   // the bracket's best
         if (take > 0) {
           if (take == e) {
             const int j = atomicAdd(&S.nfull[qi], 1);
@@ -499,8 +503,10 @@ __global__ void __launch_bounds__(SW * 64) k_select(IdxViews VS, SelArgs A) {
     const int n = nfull + (pb >= 0 ? 1 : 0);
     for (int i = lane; i < n; i += 64) em[i] = i < nfull ? A.idx[row + i] : pb;
     __builtin_amdgcn_wave_barrier();
+    const long long tk = S.topk[qi];
+    const int top = DENSE || tk == LLONG_MIN ? -1 : (int)(0xffffffffu - (unsigned)(tk & 0xffffffffll));
     emit_row<DENSE>(V, em, n, pb, S.ptake[qi], S.t[qi], A.window, A.sinks, A.max_sel,
-                    A.idx + row, A.cnt + q0 + qi);
+                    A.idx + row, A.cnt + q0 + qi, top);
   }
 }
 

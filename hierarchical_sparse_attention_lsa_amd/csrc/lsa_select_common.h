@@ -216,6 +216,46 @@ __device__ __forceinline__ long long block_max_ll(long long x, long long* red) {
   return s;
 }
 
+// Ascending bitonic sort of a block's N values, N / NT consecutive ones per
+// thread (element tid*(N/NT) + i in v[i]): partners in the same thread swap
+// in registers, in the same wave through shuffles, across waves through
+// `tmp` (N values of LDS).
+__device__ __forceinline__ int shfl_xor_t(int v, int m) { return __shfl_xor(v, m); }
+__device__ __forceinline__ long long shfl_xor_t(long long v, int m) { return shfl_xor_i64(v, m); }
+__device__ __forceinline__ unsigned shfl_xor_t(unsigned v, int m) { return (unsigned)__shfl_xor((int)v, m); }
+
+template <int N, int NT, class T>
+__device__ __forceinline__ void block_bitonic(T (&v)[N / NT], T* tmp) {
+  constexpr int PT = N / NT;
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      T pv[PT];
+      if (j < PT) {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) pv[i] = v[i ^ j];
+      } else if (j < PT * 64) {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) pv[i] = shfl_xor_t(v[i], j / PT);
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PT; ++i) tmp[tid * PT + i] = v[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PT; ++i) pv[i] = tmp[(tid * PT + i) ^ j];
+      }
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int e = tid * PT + i;
+        const bool up = (e & k) == 0, lower = (e & j) == 0;
+        const T mn = min(v[i], pv[i]), mx = max(v[i], pv[i]);
+        v[i] = (up == lower) ? mn : mx;
+      }
+    }
+  }
+}
+
 // Exclusive prefix sum over the block in thread order; *total = block sum.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int x, int* red, int* total) {
@@ -236,18 +276,21 @@ __device__ __forceinline__ int block_excl_scan(int x, int* red, int* total) {
 }
 
 // Writes one query's selection row: the taken buckets em[0..n) (bucket ids,
-// any order; `pb` is the one cut bucket, taking `ptake` keys, or -1) in
-// ascending id order with their eligible keys in ascending position, then
-// the sinks not covered by the window, then the window, then -1 padding.
-// Every selection path writes rows in this order.  `em` must have room for
-// the next power of two >= n.  One wave.
+// any order; `pb` is the one cut bucket, taking `ptake` keys, or -1), bucket
+// `top` first (the best-scoring taken one; -1: none) and the others in
+// ascending id order, each with its eligible keys in ascending position,
+// then the sinks not covered by the window, then the window, then -1
+// padding.  The bucket-list paths write rows in this order.  `em` must have
+// room for the next power of two >= n.  One wave.
 template <bool DENSE>
 __device__ void emit_row(const IdxView& V, int* em, int n, int pb, int ptake, int t, int window,
-                         int sinks, int max_sel, int32_t* __restrict__ row, int32_t* cnt_out) {
+                         int sinks, int max_sel, int32_t* __restrict__ row, int32_t* cnt_out,
+                         int top) {
   const int lane = lane_id();
   int np = 1;
   while (np < n) np <<= 1;
   for (int i = n + lane; i < np; i += 64) em[i] = INT_MAX;
+  for (int i = lane; i < n; i += 64) em[i] = em[i] == top ? -1 : em[i];   // sorts first
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   if (n > 1) wave_bitonic(em, np);
@@ -257,7 +300,7 @@ __device__ void emit_row(const IdxView& V, int* em, int n, int pb, int ptake, in
     int beta = -1, take = 0, klo = 0;
     BucketInfo bi = {0, 0, 0, 0};
     if (i < n) {
-      beta = em[i];
+      beta = em[i] < 0 ? top : em[i];
       bi = load_bucket<DENSE>(V, beta);
       const int e = eligible<DENSE>(V, beta, bi, t, window, sinks, &klo);
       take = beta == pb ? ptake : e;

@@ -26,10 +26,13 @@
 //   eligible key counts of the entries; if they reach the budget the cutoff
 //   is in the list: histogram refinement finds a bracket of <= 256 entries,
 //   entries above it are taken whole, the bracket is sorted and taken in
-//   order with the last bucket cut; the taken buckets are sorted by id
-//   (bitonic, in registers) and their keys written, every thread on its own
-//   output slots (ascending bucket ids keep each query's gather walking the
-//   KV cache once from start to end).  A query whose list overflowed or
+//   order with the last bucket cut; the taken buckets are sorted, the
+//   best-scoring one first and the rest by id (bitonic, in registers), and
+//   their keys written, every thread on its own output slots (ascending
+//   bucket ids keep each query's gather walking the KV cache once from start
+//   to end; the first key of a row names the query's best bucket, which the
+//   grouped attention uses to put queries with similar selections together).
+//   A query whose list overflowed or
 //   falls short of the budget is flagged and the exact refinement kernel
 //   recomputes it.
 // The dense per-key comparator reuses k_scan with every latent key its own
@@ -494,45 +497,6 @@ constexpr int KCAP = TPQ * RT;      // entries per query (else the exact kernel)
 constexpr int ECAP2 = 1024;         // taken buckets per query (else the exact kernel)
 constexpr int EPT = ECAP2 / RT;     // sorted taken buckets per thread
 
-// Ascending bitonic sort of the block's ECAP2 values, EPT consecutive ones per
-// thread (element tid*EPT + i in v[i]): partners in the same thread swap in
-// registers, in the same wave through shuffles, across waves through `tmp`.
-__device__ __forceinline__ int shfl_xor_t(int v, int m) { return __shfl_xor(v, m); }
-__device__ __forceinline__ long long shfl_xor_t(long long v, int m) { return shfl_xor_i64(v, m); }
-__device__ __forceinline__ unsigned shfl_xor_t(unsigned v, int m) { return (unsigned)__shfl_xor((int)v, m); }
-
-template <int N, class T, int NT = RT>
-__device__ __forceinline__ void block_bitonic(T (&v)[N / NT], T* tmp) {
-  constexpr int PT = N / NT;
-  const int tid = threadIdx.x;
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      T pv[PT];
-      if (j < PT) {
-#pragma unroll
-        for (int i = 0; i < PT; ++i) pv[i] = v[i ^ j];
-      } else if (j < PT * 64) {
-#pragma unroll
-        for (int i = 0; i < PT; ++i) pv[i] = shfl_xor_t(v[i], j / PT);
-      } else {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < PT; ++i) tmp[tid * PT + i] = v[i];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < PT; ++i) pv[i] = tmp[(tid * PT + i) ^ j];
-      }
-#pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int e = tid * PT + i;
-        const bool up = (e & k) == 0, lower = (e & j) == 0;
-        const T mn = min(v[i], pv[i]), mx = max(v[i], pv[i]);
-        v[i] = (up == lower) ? mn : mx;
-      }
-    }
-  }
-}
-
 // Shared tail of the list resolve and the Tree select: exact selection over
 // the entries a workgroup of RT threads holds in registers (order keys K,
 // eligible key counts e; entries with e <= 0 take no part), then the row.
@@ -566,6 +530,9 @@ __device__ __forceinline__ bool select_and_emit(ResolveLds& L, const IdxView& V,
   tot = block_sum_ll<RT>(tot, L.red);
   lo = block_min_ll<RT>(lo, L.red);
   hi = block_max_ll<RT>(hi, L.red);
+  // the best-scoring eligible bucket (always taken when anything is): its
+  // keys go first in the row, so a row's first long-range key names it
+  const int top_id = hi == LLONG_MIN ? -1 : (int)(0xffffffffu - (unsigned)(hi & 0xffffffffll));
   bool all = false;
   if (complete && tot <= B) {         // every eligible candidate is taken whole
     all = true;
@@ -696,24 +663,31 @@ __device__ __forceinline__ bool select_and_emit(ResolveLds& L, const IdxView& V,
 
   int32_t* row = A.idx + (int64_t)q * A.max_sel;
   if (ok) {
-    // taken buckets in ascending id order (padding sorts last); entry r of
-    // L.key is (id << 32 | r).  Ids below 2^21 sort as 32-bit (id << 10 | r).
+    // taken buckets: the best-scoring one first, then ascending id order
+    // (padding sorts last); entry r of L.key is (id << 32 | r).  The sort key
+    // is (id + 1, r), and (0, r) for the best bucket; ids below 2^21 - 1 sort
+    // as 32-bit ((id + 1) << 10 | r).
     int src[EPT];
-    if (V.n_bkt < (1 << 21)) {
+    if (V.n_bkt < (1 << 21) - 1) {
       int v[EPT];
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
         const int e = tid * EPT + i;
-        v[i] = e < nt ? (int)(((L.key[e] >> 32) << 10) | (L.key[e] & (ECAP2 - 1))) : INT_MAX;
+        const int id = e < nt ? (int)(L.key[e] >> 32) : 0;
+        v[i] = e < nt ? (int)(((id == top_id ? 0 : id + 1) << 10) | (L.key[e] & (ECAP2 - 1))) : INT_MAX;
       }
-      block_bitonic<ECAP2>(v, reinterpret_cast<int*>(L.key));
+      block_bitonic<ECAP2, RT>(v, reinterpret_cast<int*>(L.key));
 #pragma unroll
       for (int i = 0; i < EPT; ++i) src[i] = v[i] & (ECAP2 - 1);
     } else {
       long long v[EPT];
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) v[i] = tid * EPT + i < nt ? L.key[tid * EPT + i] : LLONG_MAX;
-      block_bitonic<ECAP2>(v, L.key);
+      for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        const long long id = e < nt ? (L.key[e] >> 32) : 0;
+        v[i] = e < nt ? (((id == top_id ? 0ll : id + 1) << 32) | (L.key[e] & 0xffffffffll)) : LLONG_MAX;
+      }
+      block_bitonic<ECAP2, RT>(v, L.key);
 #pragma unroll
       for (int i = 0; i < EPT; ++i) src[i] = (int)(v[i] & 0xffffffffll);
     }
@@ -997,7 +971,7 @@ __global__ void __launch_bounds__(RTD) k_dense_resolve(SelArgs A, ListWs W) {
   int v[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) v[i] = tid * KPT + i < total ? s_keys[tid * KPT + i] : INT_MAX;
-  block_bitonic<DKEEP, int, RTD>(v, s_keys);
+  block_bitonic<DKEEP, RTD>(v, s_keys);
   int32_t* row = A.idx + (int64_t)q * A.max_sel;
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
@@ -1073,7 +1047,7 @@ __device__ __forceinline__ void top_nodes(const int8_t* cent, int n, IdOf id_of,
     }
     v[i] = key;
   }
-  block_bitonic<NS>(v, reinterpret_cast<unsigned*>(tmp));
+  block_bitonic<NS, RT>(v, reinterpret_cast<unsigned*>(tmp));
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int r = tid * PT + i;

@@ -39,9 +39,13 @@
  *     floor(h * Hkv / Hq).
  *   - Selected key lists are int32 rows of `max_sel` = budget + window + sinks
  *     entries: `cnt[i]` distinct key positions followed by -1 padding.  The
- *     row is a set written in a fixed order: the taken buckets in ascending
- *     id, each with its eligible keys in ascending position, then the sinks
- *     not in the window, then the window.
+ *     row is a set written in a fixed order: the taken buckets, each with
+ *     its eligible keys in ascending position, then the sinks not in the
+ *     window, then the window.  lsa_select and lsa_prefill_chunk write the
+ *     best-scoring taken bucket first and the others in ascending id (the
+ *     grouped attention puts queries with equal first keys together); the
+ *     decode step writes them in ascending id, and lsa_dense_select (one key
+ *     a "bucket") its keys in an order of its own.
  */
 #ifndef LSA_H
 #define LSA_H
@@ -73,7 +77,8 @@ enum {
   LSA_OP_PREFILL = 4,  /* n = chunk length */
   LSA_OP_DECODE = 5,   /* n = sequences */
   LSA_OP_DENSE = 6,    /* n = queries */
-  LSA_OP_ATTN_BWD = 7  /* n = queries; index, select and attention params */
+  LSA_OP_ATTN_BWD = 7, /* n = queries; index, select and attention params */
+  LSA_OP_ATTN_GROUPED = 8  /* n = queries; select and attention params */
 };
 
 /* Index shape.  dim must be 64.  pool >= 1.  block (pooled vectors per
@@ -168,8 +173,10 @@ LSA_API int lsa_index_get_info(const lsa_index* h, lsa_index_info* out);
 
 /* Workspace bytes for `op` with `n` as documented in the LSA_OP_* enum.
  * Index params are needed for BUILD/APPEND/PREFILL/DECODE/SELECT, select
- * params for SELECT/PREFILL/DECODE/DENSE, attention params for
- * ATTN/PREFILL/DECODE; unused ones may be NULL. */
+ * params for SELECT/PREFILL/DECODE/DENSE/ATTN_GROUPED, attention params for
+ * ATTN/DECODE/ATTN_GROUPED; unused ones may be NULL.  For PREFILL the
+ * attention params are optional: given, the size also covers the grouped
+ * attention the chunk then runs. */
 LSA_API int lsa_workspace_bytes(int op, const lsa_index_params* iprm,
                                 const lsa_select_params* sprm, const lsa_attn_params* aprm,
                                 int64_t n, size_t* bytes);
@@ -224,6 +231,27 @@ LSA_API int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, con
                                    const lsa_select_params* sp, const lsa_attn_params* ap,
                                    void* d_out, void* stream);
 
+/* lsa_sparse_attn_window with the long-range keys read once per group of
+ * queries that share them.  Queries are ordered by the first entry of their
+ * rows (on rows from the Flat list path, the first key of the best-scoring
+ * bucket) and taken 16/G at a time; each group's long-range entries are
+ * merged into one sorted list with a mask of the queries that hold each key,
+ * and the group walks that list once with each query's softmax masked to
+ * its own keys, on top of its sinks and window (attended first, as in
+ * lsa_sparse_attn_window).  Same attention over the same key set per query;
+ * only the summation order differs.  Needs D in {64, 128}, G = Hq/Hkv in {4,
+ * 8, 16}, (16/G) * budget <= 16384 and kv_rows < 2^29 (else
+ * LSA_E_UNSUPPORTED), and a workspace of lsa_workspace_bytes(
+ * LSA_OP_ATTN_GROUPED, .., nq) bytes (else LSA_E_CAPACITY).  A group holding
+ * a row with more than `budget` long-range entries is walked row by row.
+ * (Grouping queries is this library's design; the pages fix only what each
+ * query attends to.) */
+LSA_API int lsa_sparse_attn_grouped(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                                    int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                                    int32_t max_sel, int32_t nq, int64_t qpos0,
+                                    const lsa_select_params* sp, const lsa_attn_params* ap,
+                                    void* d_out, void* d_ws, size_t ws_bytes, void* stream);
+
 /* Training forward: lsa_sparse_attn_window that also stores, per (query,
  * head), the natural log of the softmax denominator over the query's
  * selected keys, lse = log sum_j exp(scale * q . k_j): d_lse float32
@@ -262,7 +290,10 @@ LSA_API int lsa_sparse_attn_bwd(const lsa_index* h, const uint16_t* d_q, const u
  * index that already holds the chunk's keys), attend.  The caller has
  * written K/V rows up to T_old+n_chunk.  d_idx_opt / d_cnt_opt (nullable)
  * receive the selection; otherwise it lives in the workspace.  Attention
- * runs as lsa_sparse_attn_window. */
+ * runs as lsa_sparse_attn_grouped when the shape allows it and the
+ * workspace holds lsa_workspace_bytes(LSA_OP_PREFILL, .., ap, n_chunk) (the
+ * attention params make that size cover the grouped attention), else as
+ * lsa_sparse_attn_window. */
 LSA_API int lsa_prefill_chunk(lsa_index* h, const int8_t* d_latk_chunk, int64_t n_chunk,
                               const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
                               const uint16_t* d_v, int64_t kv_rows, const lsa_select_params* sp,

@@ -351,6 +351,129 @@ def test_window_attention_matches_oracle(case):
     assert err <= TOL and err_generic <= TOL
     assert np.array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16),
                           rne_bf16_bits(o32.cpu().numpy()))
+    if Hq // Hkv in (4, 8, 16):
+        # grouped: the same rows, long-range keys read once per group of queries
+        gr32 = L.sparse_attn_grouped(qd, Kd, Vd, idd, cd, qpos0, sp, L.AttnParams(Hq, Hkv, D, 1, 0.0))
+        gr16 = L.sparse_attn_grouped(qd, Kd, Vd, idd, cd, qpos0, sp, L.AttnParams(Hq, Hkv, D, 0, 0.0))
+        err_g = normwise(gr32.cpu().numpy().astype(np.float64), refo)
+        print(f"  grouped kernel {err_g:.3e}")
+        assert err_g <= TOL
+        assert np.array_equal(gr16.view(torch.int16).cpu().numpy().view(np.uint16),
+                              rne_bf16_bits(gr32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 1, 64), (8, 1, 128), (32, 2, 64)])
+def test_grouped_attention_on_select_rows(tiny, Hq, Hkv, D):
+    """lsa_sparse_attn_grouped on rows the Flat list path wrote (best bucket
+    first, so neighbouring queries in the sorted order share most keys), for
+    5000 queries (several sort tiles and merge passes, a ragged last group):
+    every output against the window kernel's, sampled queries against the
+    oracle on the oracle's own selections.  Then with the per-query union cap
+    (the select budget) below some rows' long-range counts: those groups are
+    walked row by row."""
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    wl = dataclasses.replace(wl, Hq=Hq, Hkv=Hkv, D=D)
+    g = S.Synth(wl)
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    qpos0, nq = 11000, 5000
+    pos = torch.arange(qpos0, qpos0 + nq)
+    lq = g.latq_rows(pos)
+    eb, eu = 300, qpos0 + 1700          # the first 1700 queries take 300 long-range keys
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0, eb, eu)
+    idx, cnt = ix.select(lq.to(dev), pos.to(torch.int32).to(dev), sp)
+    q = g.q_rows(pos).to(dev)
+    K = torch.empty((wl.T, Hkv, D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0)
+    g.fill_rows("v", V, 0)
+    K, V = K.to(dev), V.to(dev)
+    ap32 = L.AttnParams(Hq, Hkv, D, 1, 0.0)
+    win = L.sparse_attn_window(q, K, V, idx, cnt, qpos0, sp, ap32)
+    grp = L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, ap32)
+    gr16 = L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, L.AttnParams(Hq, Hkv, D, 0, 0.0))
+    # a cap of 300: the later queries' 1024-key rows go row by row
+    sp_cap = L.SelectParams(eb, wl.window, wl.sinks, 0)
+    cap = L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp_cap, ap32)
+    torch.cuda.synchronize()
+    w = win.cpu().numpy().astype(np.float64)
+    for name, o in (("grouped", grp), ("grouped, capped unions", cap)):
+        e = normwise(o.cpu().numpy().astype(np.float64), w)
+        print(f"{name} vs window kernel, {nq} queries: {e:.3e}")
+        assert e <= TOL
+    assert np.array_equal(gr16.view(torch.int16).cpu().numpy().view(np.uint16),
+                          rne_bf16_bits(grp.cpu().numpy()))
+    rng = np.random.default_rng(7)
+    samp = sorted(set([0, 1, 1699, 1700, nq - 1] + rng.choice(nq, 40, replace=False).tolist()))
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks, 0, eb, eu)
+    sels = [O.select(ref, lq[i].numpy(), qpos0 + i, osp) for i in samp]
+    check_selection(idx[samp], cnt[samp], sels, sp.max_sel)
+    refo = oracle_attention(g, wl, [qpos0 + i for i in samp], sels)
+    for name, o in (("grouped", grp), ("grouped, capped unions", cap)):
+        e = normwise(o.cpu().numpy()[samp].astype(np.float64), refo)
+        print(f"{name} vs oracle, {len(samp)} queries: {e:.3e}")
+        assert e <= TOL
+
+
+def test_grouped_attention_identical_rows():
+    """Every query of a group holding the same long-range keys (each union
+    row masked for all its queries), rows shorter than a tile, and queries
+    with no long-range key at all (first positions)."""
+    dev = _dev()
+    L = _L()
+    Hq, Hkv, D, budget, window, sinks = 8, 2, 64, 40, 16, 2
+    wl = S.Workload("grp", 91, T=2048, ncomp=16, block=64, buckets=16, iters=2, chunk=0,
+                    budget=budget, window=window, sinks=sinks, Hq=Hq, Hkv=Hkv, D=D)
+    g = S.Synth(wl, data_cfg=91)
+    qpos0, nq = 0, 300
+    rng = np.random.default_rng(3)
+    shared = [np.sort(rng.choice(800, size=int(rng.integers(1, budget + 1)), replace=False))
+              for _ in range(8)]
+    idx = torch.full((nq, wl.max_sel), -1, dtype=torch.int32)
+    cnt = torch.zeros(nq, dtype=torch.int32)
+    sels = []
+    for i in range(nq):
+        t = qpos0 + i
+        ws = max(0, t - window + 1)
+        ns = max(0, min(sinks, ws))
+        fixed = list(range(ns)) + list(range(ws, t + 1))
+        lr = [k for k in shared[(i // 37) % 8].tolist() if k < ws and k >= ns] if t >= 40 else []
+        row = np.array(lr + fixed, dtype=np.int32)
+        idx[i, :len(row)] = torch.from_numpy(row)
+        cnt[i] = len(row)
+        sels.append(np.sort(row.astype(np.int64)))
+    pos = list(range(qpos0, qpos0 + nq))
+    q = g.q_rows(torch.tensor(pos))
+    K = torch.empty((wl.T, Hkv, D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0)
+    g.fill_rows("v", V, 0)
+    sp = L.SelectParams(budget, window, sinks, 0)
+    o = L.sparse_attn_grouped(q.to(dev), K.to(dev), V.to(dev), idx.to(dev), cnt.to(dev), qpos0, sp,
+                              L.AttnParams(Hq, Hkv, D, 1, 0.0))
+    err = normwise(o.cpu().numpy().astype(np.float64), oracle_attention(g, wl, pos, sels))
+    print(f"grouped attention, identical rows: {err:.3e}")
+    assert err <= TOL
+
+
+def test_grouped_attention_rejects():
+    """Shapes the grouped kernel does not take are refused on the host."""
+    _dev()
+    L = _L()
+    sp = L.SelectParams(4096, 512, 4, 0)
+    for ap in (L.AttnParams(8, 8, 128, 0, 0.0), L.AttnParams(6, 2, 64, 0, 0.0),
+               L.AttnParams(8, 1, 64, 0, 0.0)):
+        n = 16
+        q = torch.zeros((n, ap.Hq, ap.D), dtype=torch.bfloat16, device="cuda")
+        kv = torch.zeros((64, ap.Hkv, ap.D), dtype=torch.bfloat16, device="cuda")
+        idx = torch.full((n, sp.max_sel), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.ones(n, dtype=torch.int32, device="cuda")
+        if ap.Hq // ap.Hkv == 8:        # G = 8 with a 4096 budget: 2 x 4096 fits; G = 1, 3 do not
+            L.sparse_attn_grouped(q, kv, kv, idx, cnt, 0, sp, ap)
+            continue
+        with pytest.raises(L.LsaError):
+            L.sparse_attn_grouped(q, kv, kv, idx, cnt, 0, sp, ap)
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
