@@ -37,7 +37,7 @@ import lsa_synth as S  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_OPS = 5.0e15          # dense int8 MFMA, ops/s
 ATTN_SRC = os.path.join(ROOT, "hierarchical_sparse_attention_lsa_amd", "csrc", "lsa_attn.hip")
-ATTN_KERNEL = "k_attn_win<128, false>"
+ATTN_KERNEL = "k_attn_grp<128, false>"
 
 
 def log(*a):
@@ -92,6 +92,48 @@ def attn_algorithmic_bytes(wl, t0, n, cnt: np.ndarray) -> float:
     return float(lr.sum() * row + span * row + lr.sum() * 4 + n * 4 + qo)
 
 
+def grouped_unions(wl, t0, idx_h: np.ndarray, cnt_h: np.ndarray):
+    """Host recount of the grouped attention's work: queries ordered by the
+    first long-range key of their rows (then by index), taken 16/G at a time;
+    each group's union is the set of distinct long-range keys of its rows.
+    Returns (union rows per group, long-range entries per query)."""
+    n = idx_h.shape[0]
+    t = np.arange(t0, t0 + n)
+    wstart = np.maximum(0, t - wl.window + 1)
+    lr = cnt_h.astype(np.int64) - (np.maximum(0, np.minimum(wl.sinks, wstart)) + (t - wstart + 1))
+    first = np.where(lr > 0, idx_h[:, 0].astype(np.int64), 2 ** 31 - 1)
+    order = np.lexsort((np.arange(n), first))
+    qpw = 16 // (wl.Hq // wl.Hkv)
+    unions = []
+    for g0 in range(0, n, qpw):
+        qs = order[g0:g0 + qpw]
+        unions.append(np.unique(np.concatenate([idx_h[q, :lr[q]] for q in qs])).size)
+    return np.asarray(unions, dtype=np.int64), lr
+
+
+def grouped_attn_bytes(wl, t0, n, unions: np.ndarray):
+    """Algorithmic HBM bytes of the grouped attention over a chunk.
+
+    walk (k_attn_grp, one launch): every union row's K and V for all KV
+    heads, its index entry and mask (5 bytes), the sinks-and-window partials
+    (float32 output + max + sum per query head), Q, and the output.
+    prepare: the sinks-and-window phase reads the chunk's window span (and
+    sinks) once, Q, and writes the partials; the sort and union kernels read
+    the rows' long-range parts and write the unions (counted as union rows x
+    5 bytes written; the row reads are in `walk`'s index term's order of
+    magnitude and left out)."""
+    row = wl.Hkv * wl.D * 2 * 2
+    heads = n * wl.Hq
+    partials = heads * (wl.D + 2) * 4
+    q_bytes = heads * wl.D * 2
+    o_bytes = heads * wl.D * 2
+    u = int(unions.sum())
+    walk = u * row + u * 5 + partials + q_bytes + o_bytes + n * 4 + len(unions) * 4
+    span = (t0 + n - max(0, t0 - wl.window + 1)) + min(wl.sinks, max(0, t0 - wl.window + 1))
+    prepare = span * row + q_bytes + partials + u * 5
+    return float(walk), float(prepare)
+
+
 def bench_prefill(args, dev):
     wl = S.WORKLOADS[args.config]
     n = wl.chunk
@@ -131,7 +173,12 @@ def bench_prefill(args, dev):
     lk_chunk = latk[t0:]
     sel_ws = torch.empty(max(L.workspace_bytes(L.binding.OP_SELECT, ix.params, sp, None, n), 256),
                          dtype=torch.uint8, device=dev)
+    grp_ws = torch.empty(L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap, n),
+                         dtype=torch.uint8, device=dev)
 
+    # one step: append the chunk, select, attend (grouped: prepare, then the
+    # long-range walk); every call on torch's current stream, where the events
+    # are recorded
     def step(evs=None):
         ix.restore(snap)
         if evs: evs[0].record()
@@ -139,22 +186,37 @@ def bench_prefill(args, dev):
         if evs: evs[1].record()
         ix.select(latq, qpos, sp, idx=idx, cnt=cnt, ws=sel_ws)
         if evs: evs[2].record()
-        L.sparse_attn_window(q, K, V, idx, cnt, t0, sp, ap, out=out)
+        L.sparse_attn_grouped(q, K, V, idx, cnt, t0, sp, ap, ws=grp_ws, part="prepare")
         if evs: evs[3].record()
+        L.sparse_attn_grouped(q, K, V, idx, cnt, t0, sp, ap, out=out, ws=grp_ws, part="walk")
+        if evs: evs[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-                   for e in evs])
+    ph4 = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
+    ph = np.stack([ph4[:, 0], ph4[:, 1], ph4[:, 2] + ph4[:, 3]], axis=1)
     ms_per_step = wall * 1e3 / args.steps
+
+    # context: the ungrouped window-sharing kernel on the same rows
+    out_w = torch.empty_like(out)
+    L.sparse_attn_window(q, K, V, idx, cnt, t0, sp, ap, out=out_w)
+    ew = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    win_ms = []
+    for _ in range(2):
+        ew[0].record()
+        L.sparse_attn_window(q, K, V, idx, cnt, t0, sp, ap, out=out_w)
+        ew[1].record()
+        torch.cuda.synchronize()
+        win_ms.append(ew[0].elapsed_time(ew[1]))
+    del out_w
 
     # the fused entry point gives the same selection and output
     ix.restore(snap)
@@ -166,15 +228,26 @@ def bench_prefill(args, dev):
                       torch.equal(out2.view(torch.int16), out.view(torch.int16)))
 
     cnt_h = cnt.cpu().numpy()
-    attn_ms = float(ph[:, 2].mean())
-    abytes = attn_algorithmic_bytes(wl, t0, n, cnt_h)
-    achieved = abytes / (attn_ms * 1e-3) / 1e9
+    unions, lr = grouped_unions(wl, t0, idx.cpu().numpy(), cnt_h)
+    walk_bytes, prep_bytes = grouped_attn_bytes(wl, t0, n, unions)
+    attn_ms = float(ph4[:, 3].mean())                  # the long-range walk: one launch
+    achieved = walk_bytes / (attn_ms * 1e-3) / 1e9
+    per_query = attn_algorithmic_bytes(wl, t0, n, cnt_h)
     res = {
         "wl": wl, "t0": t0, "n": n, "ms_per_step": ms_per_step, "phase_ms": ph.mean(0).tolist(),
         "step_event_ms": {"median": float(np.median(ph.sum(1))), "min": float(ph.sum(1).min()),
                           "attention_median": float(np.median(ph[:, 2])),
                           "attention_min": float(ph[:, 2].min())},
-        "attn_ms": attn_ms, "attn_bytes": abytes, "achieved_gbs": achieved,
+        "attn_ms": attn_ms, "attn_bytes": walk_bytes, "achieved_gbs": achieved,
+        "attn_phase_bytes": walk_bytes + prep_bytes,
+        "grouped": {"prepare_ms": float(ph4[:, 2].mean()), "walk_ms": attn_ms,
+                    "union_rows": int(unions.sum()), "long_range_entries": int(lr.sum()),
+                    "union_fraction": float(unions.sum() / max(1, lr.sum())),
+                    "groups": int(len(unions)), "prepare_algorithmic_bytes": prep_bytes,
+                    "ungrouped_window_kernel_ms": float(np.median(win_ms)),
+                    "per_query_algorithmic_bytes": per_query,
+                    "per_query_bytes_over_attention_phase_gbs":
+                        per_query / (float(ph[:, 2].mean()) * 1e-3) / 1e9},
         "build_ms": float(np.median(build_ms)), "fused_same": fused_same,
         "cnt_mean": float(cnt_h.mean()), "g": g, "latk": latk, "latq": latq, "idx": idx,
         "cnt": cnt, "out": out, "K": K, "V": V, "q": q, "ix": ix, "snap": snap, "sp": sp,
@@ -202,6 +275,8 @@ def bench_tree_same_data(res, dev, steps, warmup, name="tree_10m"):
     qpos = torch.arange(t0, wl.T, dtype=torch.int32, device=dev)
     ws = torch.empty(max(L.workspace_bytes(L.binding.OP_SELECT, ix.params, sp, None, n), 256),
                      dtype=torch.uint8, device=dev)
+    gws = torch.empty(L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap, n), dtype=torch.uint8,
+                      device=dev)
     lk_chunk = res["latk"][t0:]
 
     def step(e=None):
@@ -211,7 +286,7 @@ def bench_tree_same_data(res, dev, steps, warmup, name="tree_10m"):
         if e: e[1].record()
         ix.select(res["latq"], qpos, sp, idx=idx, cnt=cnt, ws=ws)
         if e: e[2].record()
-        L.sparse_attn_window(res["q"], res["K"], res["V"], idx, cnt, t0, sp, ap, out=out)
+        L.sparse_attn_grouped(res["q"], res["K"], res["V"], idx, cnt, t0, sp, ap, out=out, ws=gws)
         if e: e[3].record()
 
     for _ in range(warmup):
@@ -226,15 +301,17 @@ def bench_tree_same_data(res, dev, steps, warmup, name="tree_10m"):
     ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                    for e in evs]).mean(0)
     cnt_h = cnt.cpu().numpy()
-    abytes = attn_algorithmic_bytes(wl, t0, n, cnt_h)
-    del idx, out, ws
+    unions, _ = grouped_unions(wl, t0, idx.cpu().numpy(), cnt_h)
+    walk_b, prep_b = grouped_attn_bytes(wl, t0, n, unions)
+    del idx, out, ws, gws
     return {"workload": name, "index": f"Flat leaves + Tree G={wl.tree_group} S={wl.tree_super} "
                                         f"R={wl.tree_top} (walk fills the budget)",
             "ms_per_step": ms, "queries_per_s": n / (ms * 1e-3),
             "phases_ms": {"append": float(ph[0]), "select": float(ph[1]), "attention": float(ph[2])},
             "selected_keys_per_query": {"mean": float(cnt_h.mean()), "min": int(cnt_h.min()),
                                         "budget": wl.max_sel},
-            "attention_frac": abytes / (ph[2] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "attention_phase_frac": (walk_b + prep_b) / (ph[2] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "union_fraction": float(unions.sum()) / float(res["grouped"]["long_range_entries"])}
 
 
 def measured_copy_gbs(dev, nbytes=2 << 30):
@@ -257,12 +334,13 @@ def measured_copy_gbs(dev, nbytes=2 << 30):
 
 
 def layer_roof_ms(wl, res):
-    """Roofline time of the whole chunk step: attention bytes at the HBM peak plus
-    the query x centroid scoring at the int8 MFMA peak (append and the rest of
-    the selection are latency terms with no bandwidth floor of note)."""
+    """Roofline time of the whole chunk step: the grouped attention's bytes (the
+    walk's union rows and the sinks-and-window phase) at the HBM peak plus the
+    query x centroid scoring at the int8 MFMA peak (append and the rest of the
+    selection are latency terms with no bandwidth floor of note)."""
     n_bkt = (wl.T // wl.pool // wl.block) * wl.buckets
     score_ops = 2.0 * res["n"] * n_bkt * 64
-    return res["attn_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3 + score_ops / INT8_PEAK_OPS * 1e3
+    return res["attn_phase_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3 + score_ops / INT8_PEAK_OPS * 1e3
 
 
 def build_roof_ms(wl) -> float:
@@ -542,7 +620,7 @@ def cpu_baseline(res, workers_pool, n_sample=512):
     ref = np.stack(outs)
     err = float(np.abs(o - ref).max() / np.abs(ref).max())
     ap32 = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
-    o32 = L.sparse_attn_window(res["q"], res["K"], res["V"], res["idx"], res["cnt"], t0, res["sp"], ap32)
+    o32 = L.sparse_attn_grouped(res["q"], res["K"], res["V"], res["idx"], res["cnt"], t0, res["sp"], ap32)
     o32 = o32[torch.from_numpy(sel_i).to(o32.device)].cpu().numpy().astype(np.float64)
     err32 = float(np.abs(o32 - ref).max() / np.abs(ref).max())
     per_th = np.abs(o32 - ref).max(-1) / np.abs(ref).max(-1)        # per (token, head)
@@ -611,7 +689,9 @@ PMC_PASSES = {
 }
 N_SIMD = 1024                    # 256 CUs x 4 SIMDs
 # (label, kernel-name substring) of the kernels the prefill summary reports
-PREFILL_KERNELS = [("attention", ATTN_KERNEL), ("select: scan", "k_scan<"),
+PREFILL_KERNELS = [("attention", ATTN_KERNEL),
+                   ("attention: sinks and window", "k_attn_win<128, false, 1>"),
+                   ("attention: unions", "k_grp_union<"), ("select: scan", "k_scan<"),
                    ("select: resolve", "k_resolve("), ("index: k-means", "k_kmeans("),
                    ("index: pool", "k_pool("), ("calibration copy", "__amd_rocclr_copyBuffer")]
 
@@ -974,7 +1054,8 @@ def main():
                       if wl.tree2_group else ""),
                    "select": f"{wl.budget}+{wl.window}+{wl.sinks}",
                    "attention": f"GQA {wl.Hq}/{wl.Hkv} D={wl.D} bf16"},
-        "roofline": {"kernel": f"{ATTN_KERNEL} (sparse GQA attention, shared windows)", "bound": "hbm",
+        "roofline": {"kernel": f"{ATTN_KERNEL} (sparse GQA attention, grouped long-range walk)",
+                     "bound": "hbm",
                      "achieved": res["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": res["achieved_gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "dram_bytes_per_launch": dram,
@@ -989,6 +1070,7 @@ def main():
         "cpu_baseline": cpu,
         "phases_ms": {"append": res["phase_ms"][0], "select": res["phase_ms"][1],
                       "attention": res["phase_ms"][2]},
+        "grouped_attention": res["grouped"],
         "step_event_ms": res["step_event_ms"],
         "fused_entry_point_identical": res["fused_same"],
         "select_roofline": {"roof_ms": select_roof_ms(wl, res["n"]), "measured_ms": res["phase_ms"][1],

@@ -72,6 +72,12 @@ EXPORTS = {
     "lsa_sparse_attn_grouped": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                         ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                         c_vp, c_vp, c_sz, c_vp]),
+    "lsa_attn_grouped_prepare": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
+                                         ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                         c_vp, c_sz, c_vp]),
+    "lsa_attn_grouped_walk": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
+                                      ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                      c_vp, c_vp, c_sz, c_vp]),
     "lsa_sparse_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                     ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                     c_vp, c_vp, c_vp]),
@@ -321,24 +327,36 @@ def sparse_attn_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: t
 def sparse_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                         cnt: torch.Tensor, qpos0: int, sp: SelectParams, ap: AttnParams,
                         out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                        stream=None) -> torch.Tensor:
+                        stream=None, part: str = "all") -> torch.Tensor:
     """sparse_attn_window with each group of 16/G queries (ordered by their
-    rows' first key) reading the union of its long-range keys once."""
+    rows' first key) reading the union of its long-range keys once.  part:
+    "all", or "prepare" then "walk" with the same workspace `ws`."""
     nq = q.shape[0]
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, torch.bfloat16, name)
     _need(idx, torch.int32, "idx")
     _need(cnt, torch.int32, "cnt", (nq,))
-    if out is None:
+    if out is None and part != "prepare":
         out = torch.empty((nq, ap.Hq, ap.D), dtype=torch.float32 if ap.out_f32 else torch.bfloat16,
                           device=q.device)
     wsb = workspace_bytes(OP_ATTN_GROUPED, None, sp, ap, nq)
     if ws is None or ws.numel() < wsb:
+        if part != "all":
+            raise LsaError(f"sparse_attn_grouped part {part!r} needs a workspace of {wsb} bytes")
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().lsa_sparse_attn_grouped(_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt),
-                                         idx.shape[1], nq, qpos0, ctypes.byref(sp), ctypes.byref(ap),
-                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
-           "lsa_sparse_attn_grouped")
+    common = (_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt), idx.shape[1], nq, qpos0,
+              ctypes.byref(sp), ctypes.byref(ap))
+    if part == "all":
+        _check(lib().lsa_sparse_attn_grouped(*common, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+               "lsa_sparse_attn_grouped")
+    elif part == "prepare":
+        _check(lib().lsa_attn_grouped_prepare(*common, _ptr(ws), ws.numel(), _stream(stream)),
+               "lsa_attn_grouped_prepare")
+    elif part == "walk":
+        _check(lib().lsa_attn_grouped_walk(*common, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+               "lsa_attn_grouped_walk")
+    else:
+        raise ValueError(f"part {part!r}")
     return out
 
 

@@ -536,90 +536,111 @@ __global__ void k_grp_perm(const unsigned long long* keys, int32_t* perm, int nq
   if (i < nq) perm[i] = (int32_t)(keys[i] & 0xffffffffull);
 }
 
-// Union of a group's long-range rows: the keys, tagged with the query's slot
-// in the group (key << 2 | slot), sorted; equal keys become one row whose
-// mask has a bit per slot (a row holds a key at most once, so a run of equal
-// keys is at most qpw <= 4 long).  One workgroup of GU_T threads per group;
-// N = the sort size, at least qpw times the per-query cap.  A group with a
-// row over the cap gets ucnt = -1 and is walked row by row instead.
+// Union of a group's long-range rows, one workgroup of GU_T threads per
+// group.  An LDS hash set (linear probing) holds word (key << 4 | mask), one
+// mask bit per query slot of the group.  The group's queries are taken one
+// after another, 1024 entries at a time: a key already in the set gets the
+// query's bit, a new key is inserted with it and appended to the union at
+// the next free position (a block scan keeps row order), so the union is the
+// first query's row, then the second's new keys, ... - the same order on
+// every run.  A row holds a key at most once, so within one query no two
+// entries race for the same key; the slots that colliding keys land in may
+// vary, the set's contents and the union's order do not.  TS: table slots,
+// a power of two >= 2 x qpw x lcap.  A group with a row over the cap gets
+// ucnt = -1 and is walked row by row instead.
 constexpr int GU_T = 1024;
-template <int N>
+constexpr int GU_MAXIT = 16;           // 1024-entry chunks per group (qpw x lcap <= 16384)
+template <int TS>
 __global__ void __launch_bounds__(GU_T) k_grp_union(AttnArgs a, int lcap, int32_t* urow,
                                                     uint8_t* umask, int32_t* ucnt) {
-  constexpr int PT = N / GU_T;
-  __shared__ unsigned s[N];
+  constexpr unsigned EMPTY = 0xffffffffu;
+  constexpr int LOG_TS = __builtin_ctz(TS);
+  __shared__ unsigned tab[TS];
   __shared__ int red[GU_T / 64];
   const int tid = threadIdx.x;
   const int gi = blockIdx.x;
   const int QPW = a.qpw;
-  int qs[4] = {0, 0, 0, 0}, pre[5] = {0, 0, 0, 0, 0};
+  int qs[4] = {0, 0, 0, 0}, nl[4] = {0, 0, 0, 0};
   bool over = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = gi * QPW + j;
     const bool in = j < QPW && slot < a.nq;
     qs[j] = in ? a.perm[slot] : 0;
-    const int n = in ? long_range_count(a, qs[j]) : 0;
-    over |= n > lcap;
-    pre[j + 1] = pre[j] + n;
+    nl[j] = in ? long_range_count(a, qs[j]) : 0;
+    over |= nl[j] > lcap;
   }
   if (over) {                          // block-uniform
     if (tid == 0) ucnt[gi] = -1;
     return;
   }
-  const int total = pre[4];            // <= 4 * lcap <= N
-  unsigned v[PT];
+  // every chunk's entries first (all loads in flight at once): chunk k is
+  // entries c0 .. c0+1023 of slot j's row, chunks of slot j after those of
+  // the slots before it
+  int cc[5] = {0, 0, 0, 0, 0};
 #pragma unroll
-  for (int k = 0; k < PT; ++k) {
-    const int e = tid * PT + k;
-    unsigned x = 0xffffffffu;
-    if (e < total) {
-      const int j = (e >= pre[1]) + (e >= pre[2]) + (e >= pre[3]);
+  for (int j = 0; j < 4; ++j) cc[j + 1] = cc[j] + (nl[j] + GU_T - 1) / GU_T;
+  const int nch = cc[4];               // <= GU_MAXIT
+  int ent[GU_MAXIT];
+#pragma unroll
+  for (int k = 0; k < GU_MAXIT; ++k) {
+    ent[k] = -1;
+    if (k < nch) {
+      const int j = (k >= cc[1]) + (k >= cc[2]) + (k >= cc[3]);
+      const int c0 = (k - (j == 0 ? cc[0] : j == 1 ? cc[1] : j == 2 ? cc[2] : cc[3])) * GU_T;
       const int qj = j == 0 ? qs[0] : j == 1 ? qs[1] : j == 2 ? qs[2] : qs[3];
-      const int pj = j == 0 ? pre[0] : j == 1 ? pre[1] : j == 2 ? pre[2] : pre[3];
-      const int key = a.idx[(int64_t)qj * a.max_sel + (e - pj)];
-      x = ((unsigned)min(max(key, 0), (int)(a.kv_rows - 1)) << 2) | (unsigned)j;
+      const int nj = j == 0 ? nl[0] : j == 1 ? nl[1] : j == 2 ? nl[2] : nl[3];
+      const int e = c0 + tid;
+      if (e < nj) ent[k] = min(max(a.idx[(int64_t)qj * a.max_sel + e], 0), (int)(a.kv_rows - 1));
     }
-    v[k] = x;
   }
-  sel::block_bitonic<N, GU_T>(v, s);
-  __syncthreads();                     // the sort's last reads of s are done
-#pragma unroll
-  for (int k = 0; k < PT; ++k) s[tid * PT + k] = v[k];
+  {
+    const uint4 e4 = {EMPTY, EMPTY, EMPTY, EMPTY};
+    for (int i = tid; i < TS / 4; i += GU_T) reinterpret_cast<uint4*>(tab)[i] = e4;
+  }
   __syncthreads();
-  // heads of runs of equal keys, and each head's mask of slots
-  int heads = 0;
-  unsigned hm[PT];
-#pragma unroll
-  for (int k = 0; k < PT; ++k) {
-    const int i = tid * PT + k;
-    const unsigned x = v[k];
-    const bool head = x != 0xffffffffu && (i == 0 || (s[i - 1] >> 2) != (x >> 2));
-    unsigned m = 0;
-    if (head) {
-      m = 1u << (x & 3u);
-#pragma unroll
-      for (int d = 1; d < 4; ++d) {
-        const unsigned y = i + d < N ? s[i + d] : 0xffffffffu;
-        if (y != 0xffffffffu && (y >> 2) == (x >> 2)) m |= 1u << (y & 3u);
-      }
-    }
-    hm[k] = m;
-    heads += head ? 1 : 0;
-  }
-  int nh;
-  int pos = sel::block_excl_scan<GU_T>(heads, red, &nh);
+
   int32_t* ur = urow + (int64_t)gi * a.ucap;
   uint8_t* um = umask + (int64_t)gi * a.ucap;
+  int own_slot[GU_MAXIT], own_pos[GU_MAXIT];   // this thread's appended keys
+  int nu = 0;                                   // union length so far (block-uniform)
 #pragma unroll
-  for (int k = 0; k < PT; ++k) {
-    if (hm[k]) {
-      ur[pos] = (int32_t)(v[k] >> 2);
-      um[pos] = (uint8_t)hm[k];
-      ++pos;
+  for (int k = 0; k < GU_MAXIT; ++k) {
+    own_slot[k] = -1;
+    own_pos[k] = 0;
+    if (k < nch) {
+      const int j = (k >= cc[1]) + (k >= cc[2]) + (k >= cc[3]);
+      const unsigned bit = 1u << j;
+      int slot = -1;
+      bool fresh = false;
+      const unsigned key = (unsigned)ent[k];
+      if (ent[k] >= 0) {
+        unsigned h = (key * 0x9E3779B1u) >> (32 - LOG_TS);
+        for (;;) {                     // ends: the table is at most half full
+          const unsigned w = tab[h];
+          if (w != EMPTY && (w >> 4) == key) { atomicOr(&tab[h], bit); slot = (int)h; break; }
+          if (w == EMPTY) {
+            if (atomicCAS(&tab[h], EMPTY, (key << 4) | bit) == EMPTY) { slot = (int)h; fresh = true; break; }
+            continue;                  // another key took the slot: look at it again
+          }
+          h = (h + 1) & (TS - 1);
+        }
+      }
+      int tot;
+      const int pos = nu + sel::block_excl_scan<GU_T>(fresh ? 1 : 0, red, &tot);
+      if (fresh) {
+        ur[pos] = (int32_t)key;
+        own_slot[k] = slot;
+        own_pos[k] = pos;
+      }
+      nu += tot;
     }
   }
-  if (tid == 0) ucnt[gi] = nh;
+  __syncthreads();                     // every bit is in the table
+#pragma unroll
+  for (int k = 0; k < GU_MAXIT; ++k)
+    if (own_slot[k] >= 0) um[own_pos[k]] = (uint8_t)(tab[own_slot[k]] & 15u);
+  if (tid == 0) ucnt[gi] = nu;
 }
 
 // One wave per (group, KV head): the group's qpw queries x G heads are the
@@ -1012,9 +1033,9 @@ int grp_sort_n(int32_t nq) {
   while (n < nq) n <<= 1;
   return n;
 }
-int grp_union_n(int qpw, int32_t lcap) {
-  int n = GU_T;
-  while (n < qpw * lcap) n <<= 1;
+int grp_table_n(int qpw, int32_t lcap) {    // hash slots: at least twice the entries
+  int n = 2048;
+  while (n < 2 * qpw * lcap) n <<= 1;
   return n;
 }
 struct GrpLayout {
@@ -1048,7 +1069,7 @@ bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows) {
   const int G = ap.Hq / ap.Hkv;
   if (G != 4 && G != 8 && G != 16) return false;
   if (lcap < 1 || (16 / G) * (int64_t)lcap > 16384) return false;
-  return kv_rows >= 1 && kv_rows < (int64_t)1 << 29;     // key << 2 | slot fits 31 bits
+  return kv_rows >= 1 && kv_rows < (int64_t)1 << 28;     // key << 4 | mask fits 32 bits
 }
 
 size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
@@ -1060,7 +1081,7 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                                int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
                                int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
-                               void* ws, hipStream_t s) {
+                               void* ws, int parts, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   if (!grouped_attn_ok(ap, lcap, kv_rows)) return hipErrorInvalidValue;
   const GrpLayout L = grp_layout(nq, ap, lcap);
@@ -1086,37 +1107,41 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
   const unsigned grid = (unsigned)(((size_t)L.ngrp * ap.Hkv + AW - 1) / AW);
   const bool f32 = ap.out_f32 != 0;
 
-  // 1. sinks and window of every query, in position order, as partials
-  if (ap.D == 128) hipLaunchKernelGGL((k_attn_win<128, false, 1>), dim3(grid), dim3(AT), 0, s, a);
-  else hipLaunchKernelGGL((k_attn_win<64, false, 1>), dim3(grid), dim3(AT), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (parts & kGroupedPrepare) {
+    // 1. sinks and window of every query, in position order, as partials
+    if (ap.D == 128) hipLaunchKernelGGL((k_attn_win<128, false, 1>), dim3(grid), dim3(AT), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_win<64, false, 1>), dim3(grid), dim3(AT), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
 
-  // 2. the order of the queries: sort (first long-range key, query)
-  unsigned long long* ka = reinterpret_cast<unsigned long long*>(w + L.keys_a);
-  unsigned long long* kb = reinterpret_cast<unsigned long long*>(w + L.keys_b);
-  hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, a, ka, L.n_pad);
-  hipLaunchKernelGGL(k_grp_sort_tile, dim3(L.n_pad / GS_TILE), dim3(GS_T), 0, s, ka);
-  for (int wd = GS_TILE; wd < L.n_pad; wd <<= 1) {
-    hipLaunchKernelGGL(k_grp_merge, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, ka, kb, L.n_pad, wd);
-    std::swap(ka, kb);
-  }
-  hipLaunchKernelGGL(k_grp_perm, dim3((nq + 255) / 256), dim3(256), 0, s, ka, perm, nq);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    // 2. the order of the queries: sort (first long-range key, query)
+    unsigned long long* ka = reinterpret_cast<unsigned long long*>(w + L.keys_a);
+    unsigned long long* kb = reinterpret_cast<unsigned long long*>(w + L.keys_b);
+    hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, a, ka, L.n_pad);
+    hipLaunchKernelGGL(k_grp_sort_tile, dim3(L.n_pad / GS_TILE), dim3(GS_T), 0, s, ka);
+    for (int wd = GS_TILE; wd < L.n_pad; wd <<= 1) {
+      hipLaunchKernelGGL(k_grp_merge, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, ka, kb, L.n_pad, wd);
+      std::swap(ka, kb);
+    }
+    hipLaunchKernelGGL(k_grp_perm, dim3((nq + 255) / 256), dim3(256), 0, s, ka, perm, nq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
 
-  // 3. the groups' unions of long-range rows
-  const int un = grp_union_n(L.qpw, lcap);
-  switch (un) {
-    case 1024: hipLaunchKernelGGL((k_grp_union<1024>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-    case 2048: hipLaunchKernelGGL((k_grp_union<2048>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-    case 4096: hipLaunchKernelGGL((k_grp_union<4096>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-    case 8192: hipLaunchKernelGGL((k_grp_union<8192>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-    case 16384: hipLaunchKernelGGL((k_grp_union<16384>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-    default: return hipErrorInvalidValue;
+    // 3. the groups' unions of long-range rows
+    const int ts = grp_table_n(L.qpw, lcap);
+    switch (ts) {
+      case 2048: hipLaunchKernelGGL((k_grp_union<2048>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+      case 4096: hipLaunchKernelGGL((k_grp_union<4096>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+      case 8192: hipLaunchKernelGGL((k_grp_union<8192>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+      case 16384: hipLaunchKernelGGL((k_grp_union<16384>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+      case 32768: hipLaunchKernelGGL((k_grp_union<32768>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+      default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!(parts & kGroupedWalk)) return hipSuccess;
 
   // 4. the unions, each column masked to its query's rows, on top of the partials
   if (ap.D == 128) {

@@ -202,11 +202,14 @@ hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16
 // (a group with a longer row is walked row by row).
 bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows);
 size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap);
+// parts: kGroupedPrepare (sinks-and-window partials, query order, unions into
+// the workspace) and / or kGroupedWalk (the long-range walk from them).
+constexpr int kGroupedPrepare = 1, kGroupedWalk = 2;
 hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                                int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
                                int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
-                               void* ws, hipStream_t s);
+                               void* ws, int parts, hipStream_t s);
 
 // Backward of the sparse attention (dQ, dK, dV) over rows the select wrote
 // for consecutive query positions qpos0.., with the index they came from.

@@ -235,12 +235,13 @@ LSA_API int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, con
  * queries that share them.  Queries are ordered by the first entry of their
  * rows (on rows from the Flat list path, the first key of the best-scoring
  * bucket) and taken 16/G at a time; each group's long-range entries are
- * merged into one sorted list with a mask of the queries that hold each key,
- * and the group walks that list once with each query's softmax masked to
- * its own keys, on top of its sinks and window (attended first, as in
+ * merged into one list of distinct keys (the first query's row, then each
+ * next query's keys not yet in it) with a mask of the queries that hold each
+ * key, and the group walks that list once with each query's softmax masked
+ * to its own keys, on top of its sinks and window (attended first, as in
  * lsa_sparse_attn_window).  Same attention over the same key set per query;
- * only the summation order differs.  Needs D in {64, 128}, G = Hq/Hkv in {4,
- * 8, 16}, (16/G) * budget <= 16384 and kv_rows < 2^29 (else
+ * only the summation order differs, and it is the same on every call.  Needs D in {64, 128}, G = Hq/Hkv in {4,
+ * 8, 16}, (16/G) * budget <= 16384 and kv_rows < 2^28 (else
  * LSA_E_UNSUPPORTED), and a workspace of lsa_workspace_bytes(
  * LSA_OP_ATTN_GROUPED, .., nq) bytes (else LSA_E_CAPACITY).  A group holding
  * a row with more than `budget` long-range entries is walked row by row.
@@ -251,6 +252,23 @@ LSA_API int lsa_sparse_attn_grouped(const uint16_t* d_q, const uint16_t* d_k, co
                                     int32_t max_sel, int32_t nq, int64_t qpos0,
                                     const lsa_select_params* sp, const lsa_attn_params* ap,
                                     void* d_out, void* d_ws, size_t ws_bytes, void* stream);
+
+/* The two halves of lsa_sparse_attn_grouped, same arguments (prepare takes
+ * no output), enqueued one after the other on one stream with the same
+ * workspace: prepare attends every query's sinks and window into partial
+ * results and builds the query order and the groups' unions in the
+ * workspace; walk reads them, attends the unions and writes d_out.  The
+ * split lets a caller time or schedule the long-range walk on its own. */
+LSA_API int lsa_attn_grouped_prepare(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                                     int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                                     int32_t max_sel, int32_t nq, int64_t qpos0,
+                                     const lsa_select_params* sp, const lsa_attn_params* ap,
+                                     void* d_ws, size_t ws_bytes, void* stream);
+LSA_API int lsa_attn_grouped_walk(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
+                                  int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
+                                  int32_t max_sel, int32_t nq, int64_t qpos0,
+                                  const lsa_select_params* sp, const lsa_attn_params* ap,
+                                  void* d_out, void* d_ws, size_t ws_bytes, void* stream);
 
 /* Training forward: lsa_sparse_attn_window that also stores, per (query,
  * head), the natural log of the softmax denominator over the query's

@@ -404,6 +404,13 @@ def test_grouped_attention_on_select_rows(tiny, Hq, Hkv, D):
         assert e <= TOL
     assert np.array_equal(gr16.view(torch.int16).cpu().numpy().view(np.uint16),
                           rne_bf16_bits(grp.cpu().numpy()))
+    # the two halves in turn give the same bits, and so does a second call
+    ws = torch.empty(L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap32, nq), dtype=torch.uint8,
+                     device=dev)
+    L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, ap32, ws=ws, part="prepare")
+    halves = L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, ap32, ws=ws, part="walk")
+    again = L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, ap32)
+    assert torch.equal(halves, grp) and torch.equal(again, grp)
     rng = np.random.default_rng(7)
     samp = sorted(set([0, 1, 1699, 1700, nq - 1] + rng.choice(nq, 40, replace=False).tolist()))
     osp = O.SelectParams(wl.budget, wl.window, wl.sinks, 0, eb, eu)
