@@ -92,17 +92,32 @@ def attn_algorithmic_bytes(wl, t0, n, cnt: np.ndarray) -> float:
     return float(lr.sum() * row + span * row + lr.sum() * 4 + n * 4 + qo)
 
 
+def _grp_mix(x: np.ndarray) -> np.ndarray:
+    """The grouped attention's 32-bit mix (uint32 arithmetic, wrapping)."""
+    x = x.astype(np.uint64)
+    m = np.uint64(0xFFFFFFFF)
+    x = (x * np.uint64(0x9E3779B1)) & m
+    x ^= x >> np.uint64(15)
+    x = (x * np.uint64(0x85EBCA6B)) & m
+    x ^= x >> np.uint64(13)
+    return x
+
+
 def grouped_unions(wl, t0, idx_h: np.ndarray, cnt_h: np.ndarray):
     """Host recount of the grouped attention's work: queries ordered by the
-    first long-range key of their rows (then by index), taken 16/G at a time;
-    each group's union is the set of distinct long-range keys of its rows.
-    Returns (union rows per group, long-range entries per query)."""
+    first long-range key of their rows, then by the row's MinHash (the
+    smallest mix of its pooled-group ids, top 16 bits), then by index, taken
+    16/G at a time; each group's union is the set of distinct long-range keys
+    of its rows.  Returns (union rows per group, long-range entries per query)."""
     n = idx_h.shape[0]
+    assert n < (1 << 20) - 1, "the MinHash order applies below 2^20 queries"
     t = np.arange(t0, t0 + n)
     wstart = np.maximum(0, t - wl.window + 1)
     lr = cnt_h.astype(np.int64) - (np.maximum(0, np.minimum(wl.sinks, wstart)) + (t - wstart + 1))
-    first = np.where(lr > 0, idx_h[:, 0].astype(np.int64), 2 ** 31 - 1)
-    order = np.lexsort((np.arange(n), first))
+    first = np.where(lr > 0, idx_h[:, 0].astype(np.int64), (1 << 28) - 1)
+    mh = np.array([int(_grp_mix(idx_h[q, :lr[q]].astype(np.uint64) >> np.uint64(2)).min()) >> 16
+                   if lr[q] > 0 else 0xFFFF for q in range(n)], dtype=np.int64)
+    order = np.lexsort((np.arange(n), mh, first))
     qpw = 16 // (wl.Hq // wl.Hkv)
     unions = []
     for g0 in range(0, n, qpw):

@@ -460,8 +460,8 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
 // ---- grouped long-range attention ----
 // Queries with similar selections share most of their long-range keys (the
 // select writes a row's best bucket first, so equal first keys mean the same
-// best bucket).  The queries are sorted by (first long-range key, index) and
-// taken qpw at a time; each group's long-range rows are merged into one list
+// best bucket).  The queries are sorted by (first long-range key, MinHash of
+// the row, index) and taken qpw at a time; each group's long-range rows are merged into one list
 // with a mask of the queries that selected each row, so a shared K/V row is
 // read once per group instead of once per query.  The sinks and window are
 // attended separately, in position order (k_attn_win<.., 1>), and the grouped
@@ -475,16 +475,42 @@ __device__ __forceinline__ int long_range_count(const AttnArgs& a, int q) {
   return max(0, min(a.cnt[q], a.max_sel) - nfix);
 }
 
-// Sort key of query q: (first long-range key, q); padding sorts last.
-__global__ void k_grp_key(AttnArgs a, unsigned long long* keys, int n_pad) {
-  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+// Sort key of query q, one wave per query: (first long-range key, MinHash of
+// the row, q) packed as 28 + 16 + 20 bits when the chunk has fewer than 2^20
+// queries (the MinHash - the smallest of a fixed 32-bit mix over the row's
+// pooled-group ids - puts rows with the same best bucket and more keys in
+// common next to each other), else (first key, q) as 32 + 32 bits.  Rows
+// without long-range keys take first key 2^28 - 1; padding sorts last.
+constexpr int kGrpMhBits = 20;         // query bits of the MinHash key
+__device__ __forceinline__ unsigned grp_mix(unsigned x) {
+  x *= 0x9E3779B1u;
+  x ^= x >> 15;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  return x;
+}
+__global__ void __launch_bounds__(256) k_grp_key(AttnArgs a, unsigned long long* keys, int n_pad,
+                                                 int use_mh) {
+  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
   if (q >= n_pad) return;
   unsigned long long k = ~0ull;
   if (q < a.nq) {
-    const int first = long_range_count(a, q) > 0 ? a.idx[(int64_t)q * a.max_sel] : 0x7fffffff;
-    k = ((unsigned long long)(unsigned)first << 32) | (unsigned)q;
+    const int nlr = long_range_count(a, q);
+    const int32_t* row = a.idx + (int64_t)q * a.max_sel;
+    const int kmax = (int)(a.kv_rows - 1);
+    const unsigned first = nlr > 0 ? (unsigned)min(max(row[0], 0), kmax) : (1u << 28) - 1;
+    if (use_mh) {
+      unsigned m = 0xffffffffu;
+      for (int e = lane; e < nlr; e += 64) m = min(m, grp_mix((unsigned)min(max(row[e], 0), kmax) >> 2));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) m = min(m, (unsigned)__shfl_xor((int)m, o));
+      k = ((unsigned long long)first << 36) | ((unsigned long long)(m >> 16) << kGrpMhBits) | (unsigned)q;
+    } else {
+      k = ((unsigned long long)first << 32) | (unsigned)q;
+    }
   }
-  keys[q] = k;
+  if (lane == 0) keys[q] = k;
 }
 
 // Ascending bitonic sort of each run of GS_TILE keys (GS_T threads, two each).
@@ -531,41 +557,42 @@ __global__ void k_grp_merge(const unsigned long long* in, unsigned long long* ou
   out[(int64_t)(r & ~1) * w + o + lo] = x;
 }
 
-__global__ void k_grp_perm(const unsigned long long* keys, int32_t* perm, int nq) {
+__global__ void k_grp_perm(const unsigned long long* keys, int32_t* perm, int nq, int use_mh) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nq) perm[i] = (int32_t)(keys[i] & 0xffffffffull);
+  const unsigned long long qmask = use_mh ? (1ull << kGrpMhBits) - 1 : 0xffffffffull;
+  if (i < nq) perm[i] = (int32_t)(keys[i] & qmask);
 }
 
 // Union of a group's long-range rows, one workgroup of GU_T threads per
 // group.  An LDS hash set (linear probing) holds word (key << 4 | mask), one
-// mask bit per query slot of the group.  The group's queries are taken one
-// after another, 1024 entries at a time: a key already in the set gets the
-// query's bit, a new key is inserted with it and appended to the union at
-// the next free position (a block scan keeps row order), so the union is the
-// first query's row, then the second's new keys, ... - the same order on
-// every run.  A row holds a key at most once, so within one query no two
-// entries race for the same key; the slots that colliding keys land in may
-// vary, the set's contents and the union's order do not.  TS: table slots,
-// a power of two >= 2 x qpw x lcap.  A group with a row over the cap gets
+// mask bit per query slot of the group.  The group's QP queries are taken
+// one after another: a key already in the set gets the query's bit, a new
+// key is inserted with it and appended to the union at the next free
+// position (a block scan keeps row order), so the union is the first query's
+// row, then the second's new keys, ... - the same order on every call.  A
+// row holds a key at most once, so all of one query's entries are probed at
+// once without two of them racing for the same key; the slots that colliding
+// keys land in may vary, the set's contents and the union's order do not.
+// TS: table slots, >= 2 x QP x lcap; thread t holds entries t*EPT .. +EPT-1
+// of each row (EPT x GU_T >= lcap).  A group with a row over the cap gets
 // ucnt = -1 and is walked row by row instead.
 constexpr int GU_T = 1024;
-constexpr int GU_MAXIT = 16;           // 1024-entry chunks per group (qpw x lcap <= 16384)
-template <int TS>
+template <int TS, int QP>
 __global__ void __launch_bounds__(GU_T) k_grp_union(AttnArgs a, int lcap, int32_t* urow,
                                                     uint8_t* umask, int32_t* ucnt) {
   constexpr unsigned EMPTY = 0xffffffffu;
   constexpr int LOG_TS = __builtin_ctz(TS);
+  constexpr int EPT = TS / (2 * GU_T * QP) > 0 ? TS / (2 * GU_T * QP) : 1;
   __shared__ unsigned tab[TS];
   __shared__ int red[GU_T / 64];
   const int tid = threadIdx.x;
   const int gi = blockIdx.x;
-  const int QPW = a.qpw;
-  int qs[4] = {0, 0, 0, 0}, nl[4] = {0, 0, 0, 0};
+  int qs[QP], nl[QP];
   bool over = false;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int slot = gi * QPW + j;
-    const bool in = j < QPW && slot < a.nq;
+  for (int j = 0; j < QP; ++j) {
+    const int slot = gi * QP + j;
+    const bool in = slot < a.nq;
     qs[j] = in ? a.perm[slot] : 0;
     nl[j] = in ? long_range_count(a, qs[j]) : 0;
     over |= nl[j] > lcap;
@@ -574,24 +601,15 @@ __global__ void __launch_bounds__(GU_T) k_grp_union(AttnArgs a, int lcap, int32_
     if (tid == 0) ucnt[gi] = -1;
     return;
   }
-  // every chunk's entries first (all loads in flight at once): chunk k is
-  // entries c0 .. c0+1023 of slot j's row, chunks of slot j after those of
-  // the slots before it
-  int cc[5] = {0, 0, 0, 0, 0};
+  // every entry first, all loads in flight at once
+  int ent[QP][EPT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cc[j + 1] = cc[j] + (nl[j] + GU_T - 1) / GU_T;
-  const int nch = cc[4];               // <= GU_MAXIT
-  int ent[GU_MAXIT];
+  for (int j = 0; j < QP; ++j) {
+    const int32_t* row = a.idx + (int64_t)qs[j] * a.max_sel;
 #pragma unroll
-  for (int k = 0; k < GU_MAXIT; ++k) {
-    ent[k] = -1;
-    if (k < nch) {
-      const int j = (k >= cc[1]) + (k >= cc[2]) + (k >= cc[3]);
-      const int c0 = (k - (j == 0 ? cc[0] : j == 1 ? cc[1] : j == 2 ? cc[2] : cc[3])) * GU_T;
-      const int qj = j == 0 ? qs[0] : j == 1 ? qs[1] : j == 2 ? qs[2] : qs[3];
-      const int nj = j == 0 ? nl[0] : j == 1 ? nl[1] : j == 2 ? nl[2] : nl[3];
-      const int e = c0 + tid;
-      if (e < nj) ent[k] = min(max(a.idx[(int64_t)qj * a.max_sel + e], 0), (int)(a.kv_rows - 1));
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid * EPT + i;
+      ent[j][i] = e < nl[j] ? min(max(row[e], 0), (int)(a.kv_rows - 1)) : -1;
     }
   }
   {
@@ -602,44 +620,47 @@ __global__ void __launch_bounds__(GU_T) k_grp_union(AttnArgs a, int lcap, int32_
 
   int32_t* ur = urow + (int64_t)gi * a.ucap;
   uint8_t* um = umask + (int64_t)gi * a.ucap;
-  int own_slot[GU_MAXIT], own_pos[GU_MAXIT];   // this thread's appended keys
+  int own_slot[QP][EPT], own_pos[QP][EPT];    // this thread's appended keys
   int nu = 0;                                   // union length so far (block-uniform)
 #pragma unroll
-  for (int k = 0; k < GU_MAXIT; ++k) {
-    own_slot[k] = -1;
-    own_pos[k] = 0;
-    if (k < nch) {
-      const int j = (k >= cc[1]) + (k >= cc[2]) + (k >= cc[3]);
-      const unsigned bit = 1u << j;
-      int slot = -1;
-      bool fresh = false;
-      const unsigned key = (unsigned)ent[k];
-      if (ent[k] >= 0) {
-        unsigned h = (key * 0x9E3779B1u) >> (32 - LOG_TS);
-        for (;;) {                     // ends: the table is at most half full
-          const unsigned w = tab[h];
-          if (w != EMPTY && (w >> 4) == key) { atomicOr(&tab[h], bit); slot = (int)h; break; }
-          if (w == EMPTY) {
-            if (atomicCAS(&tab[h], EMPTY, (key << 4) | bit) == EMPTY) { slot = (int)h; fresh = true; break; }
-            continue;                  // another key took the slot: look at it again
+  for (int j = 0; j < QP; ++j) {
+    const unsigned bit = 1u << j;
+    int fresh = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      own_slot[j][i] = -1;
+      if (ent[j][i] < 0) continue;
+      const unsigned key = (unsigned)ent[j][i];
+      unsigned h = (key * 0x9E3779B1u) >> (32 - LOG_TS);
+      for (;;) {                       // ends: the table is at most half full
+        const unsigned w = tab[h];
+        if (w != EMPTY && (w >> 4) == key) { atomicOr(&tab[h], bit); break; }
+        if (w == EMPTY) {
+          if (atomicCAS(&tab[h], EMPTY, (key << 4) | bit) == EMPTY) {
+            own_slot[j][i] = (int)h;
+            ++fresh;
+            break;
           }
-          h = (h + 1) & (TS - 1);
+          continue;                    // another key took the slot: look at it again
         }
+        h = (h + 1) & (TS - 1);
       }
-      int tot;
-      const int pos = nu + sel::block_excl_scan<GU_T>(fresh ? 1 : 0, red, &tot);
-      if (fresh) {
-        ur[pos] = (int32_t)key;
-        own_slot[k] = slot;
-        own_pos[k] = pos;
-      }
-      nu += tot;
     }
+    int tot;
+    int pos = nu + sel::block_excl_scan<GU_T>(fresh, red, &tot);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      own_pos[j][i] = pos;
+      if (own_slot[j][i] >= 0) ur[pos++] = ent[j][i];
+    }
+    nu += tot;
   }
   __syncthreads();                     // every bit is in the table
 #pragma unroll
-  for (int k = 0; k < GU_MAXIT; ++k)
-    if (own_slot[k] >= 0) um[own_pos[k]] = (uint8_t)(tab[own_slot[k]] & 15u);
+  for (int j = 0; j < QP; ++j)
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      if (own_slot[j][i] >= 0) um[own_pos[j][i]] = (uint8_t)(tab[own_slot[j][i]] & 15u);
   if (tid == 0) ucnt[gi] = nu;
 }
 
@@ -1115,29 +1136,40 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    // 2. the order of the queries: sort (first long-range key, query)
+    // 2. the order of the queries: sort (first long-range key, MinHash, query)
     unsigned long long* ka = reinterpret_cast<unsigned long long*>(w + L.keys_a);
     unsigned long long* kb = reinterpret_cast<unsigned long long*>(w + L.keys_b);
-    hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, a, ka, L.n_pad);
+    const int use_mh = nq < (1 << kGrpMhBits) - 1 ? 1 : 0;
+    hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 3) / 4), dim3(256), 0, s, a, ka, L.n_pad, use_mh);
     hipLaunchKernelGGL(k_grp_sort_tile, dim3(L.n_pad / GS_TILE), dim3(GS_T), 0, s, ka);
     for (int wd = GS_TILE; wd < L.n_pad; wd <<= 1) {
       hipLaunchKernelGGL(k_grp_merge, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, ka, kb, L.n_pad, wd);
       std::swap(ka, kb);
     }
-    hipLaunchKernelGGL(k_grp_perm, dim3((nq + 255) / 256), dim3(256), 0, s, ka, perm, nq);
+    hipLaunchKernelGGL(k_grp_perm, dim3((nq + 255) / 256), dim3(256), 0, s, ka, perm, nq, use_mh);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     // 3. the groups' unions of long-range rows
     const int ts = grp_table_n(L.qpw, lcap);
+#define LSA_UNION(TS_, QP_) \
+    hipLaunchKernelGGL((k_grp_union<TS_, QP_>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt)
+#define LSA_UNION_QP(TS_)                 \
+    switch (L.qpw) {                      \
+      case 4: LSA_UNION(TS_, 4); break;   \
+      case 2: LSA_UNION(TS_, 2); break;   \
+      default: LSA_UNION(TS_, 1); break;  \
+    }
     switch (ts) {
-      case 2048: hipLaunchKernelGGL((k_grp_union<2048>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-      case 4096: hipLaunchKernelGGL((k_grp_union<4096>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-      case 8192: hipLaunchKernelGGL((k_grp_union<8192>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-      case 16384: hipLaunchKernelGGL((k_grp_union<16384>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
-      case 32768: hipLaunchKernelGGL((k_grp_union<32768>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt); break;
+      case 2048: LSA_UNION_QP(2048); break;
+      case 4096: LSA_UNION_QP(4096); break;
+      case 8192: LSA_UNION_QP(8192); break;
+      case 16384: LSA_UNION_QP(16384); break;
+      case 32768: LSA_UNION_QP(32768); break;
       default: return hipErrorInvalidValue;
     }
+#undef LSA_UNION_QP
+#undef LSA_UNION
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

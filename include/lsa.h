@@ -233,8 +233,8 @@ LSA_API int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, con
 
 /* lsa_sparse_attn_window with the long-range keys read once per group of
  * queries that share them.  Queries are ordered by the first entry of their
- * rows (on rows from the Flat list path, the first key of the best-scoring
- * bucket) and taken 16/G at a time; each group's long-range entries are
+ * rows (on rows from lsa_select, the first key of the best-scoring bucket),
+ * then by a MinHash of the row, and taken 16/G at a time; each group's long-range entries are
  * merged into one list of distinct keys (the first query's row, then each
  * next query's keys not yet in it) with a mask of the queries that hold each
  * key, and the group walks that list once with each query's softmax masked
