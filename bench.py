@@ -135,8 +135,7 @@ def grouped_attn_bytes(wl, t0, n, unions: np.ndarray):
     prepare: the sinks-and-window phase reads the chunk's window span (and
     sinks) once, Q, and writes the partials; the sort and union kernels read
     the rows' long-range parts and write the unions (counted as union rows x
-    5 bytes written; the row reads are in `walk`'s index term's order of
-    magnitude and left out)."""
+    5 bytes written; the row reads are of the same order and left out)."""
     row = wl.Hkv * wl.D * 2 * 2
     heads = n * wl.Hq
     partials = heads * (wl.D + 2) * 4
