@@ -451,9 +451,10 @@ def bench_full_prefill(args, dev):
 
 def bench_train(args, dev, steps=3, warmup=1):
     """One attention layer's training step at 128k context, every position a
-    query: index build over all keys, selection, forward with log-sum-exp,
-    backward (dQ, dK, dV) from a synthetic upstream gradient.  Phases are
-    timed with events on the stream the kernels run on."""
+    query: index build over all keys, selection, forward with log-sum-exp
+    (the grouped attention), backward (dQ, dK, dV) from a synthetic upstream
+    gradient.  Phases are timed with events on the stream the kernels run
+    on."""
     wl = S.WORKLOADS["train_128k"]
     T = wl.T
     log(f"[train] generating {wl.name}: T={T}, every position a query")
@@ -479,6 +480,8 @@ def bench_train(args, dev, steps=3, warmup=1):
                          dtype=torch.uint8, device=dev)
     bwd_ws = torch.empty(L.workspace_bytes(L.binding.OP_ATTN_BWD, ix.params, sp, ap, T),
                          dtype=torch.uint8, device=dev)
+    grp_ws = torch.empty(L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap, T),
+                         dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
 
@@ -488,7 +491,7 @@ def bench_train(args, dev, steps=3, warmup=1):
         ev[1].record()
         ix.select(latq, qpos, sp, idx=idx, cnt=cnt, ws=sel_ws)
         ev[2].record()
-        L.sparse_attn_fwd(q, K, V, idx, cnt, 0, sp, ap, out=out, lse=lse)
+        L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap, out=out, ws=grp_ws, lse=lse)
         ev[3].record()
         L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do, dq=dq, dk=dk, dv=dv,
                           ws=bwd_ws)
@@ -510,11 +513,13 @@ def bench_train(args, dev, steps=3, warmup=1):
            "ms_per_step": total, "tokens_per_s": T / (total * 1e-3),
            "phases_ms": {"index_build": float(ph[0]), "select": float(ph[1]),
                          "forward": float(ph[2]), "backward": float(ph[3])},
-           "forward_algorithmic_gbs": fwd_bytes / (ph[2] * 1e-3) / 1e9,
-           "forward_algorithmic_bytes": fwd_bytes,
+           # per-query accounting (every query's rows counted): the grouped
+           # forward reads less, so this rate can pass the HBM peak
+           "forward_per_query_bytes_gbs": fwd_bytes / (ph[2] * 1e-3) / 1e9,
+           "forward_per_query_bytes": fwd_bytes,
            "selected_keys_per_query": float(cnt_h.mean())}
     log(f"[train] step {total:.1f} ms: build {ph[0]:.2f}, select {ph[1]:.2f}, forward {ph[2]:.2f}, "
-        f"backward {ph[3]:.2f} ms; forward {res['forward_algorithmic_gbs']:.0f} GB/s algorithmic")
+        f"backward {ph[3]:.2f} ms; forward {res['forward_per_query_bytes_gbs']:.0f} GB/s per-query accounting")
     return res
 
 

@@ -71,13 +71,13 @@ EXPORTS = {
                                        c_vp, c_vp]),
     "lsa_sparse_attn_grouped": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                         ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
-                                        c_vp, c_vp, c_sz, c_vp]),
+                                        c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lsa_attn_grouped_prepare": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                          ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                          c_vp, c_sz, c_vp]),
     "lsa_attn_grouped_walk": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                       ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
-                                      c_vp, c_vp, c_sz, c_vp]),
+                                      c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lsa_sparse_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                     ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                     c_vp, c_vp, c_vp]),
@@ -327,10 +327,12 @@ def sparse_attn_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: t
 def sparse_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                         cnt: torch.Tensor, qpos0: int, sp: SelectParams, ap: AttnParams,
                         out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                        stream=None, part: str = "all") -> torch.Tensor:
+                        stream=None, part: str = "all", lse: Optional[torch.Tensor] = None):
     """sparse_attn_window with each group of 16/G queries (ordered by their
     rows' first key) reading the union of its long-range keys once.  part:
-    "all", or "prepare" then "walk" with the same workspace `ws`."""
+    "all", or "prepare" then "walk" with the same workspace `ws`.  With `lse`
+    (float32 [nq][Hq]) the walk also stores the log-sum-exp, as
+    sparse_attn_fwd does."""
     nq = q.shape[0]
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, torch.bfloat16, name)
@@ -346,15 +348,18 @@ def sparse_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: 
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
     common = (_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt), idx.shape[1], nq, qpos0,
               ctypes.byref(sp), ctypes.byref(ap))
+    if lse is not None:
+        _need(lse, torch.float32, "lse", (nq, ap.Hq))
+    lp = _ptr(lse) if lse is not None else None
     if part == "all":
-        _check(lib().lsa_sparse_attn_grouped(*common, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
-               "lsa_sparse_attn_grouped")
+        _check(lib().lsa_sparse_attn_grouped(*common, _ptr(out), lp, _ptr(ws), ws.numel(),
+                                             _stream(stream)), "lsa_sparse_attn_grouped")
     elif part == "prepare":
         _check(lib().lsa_attn_grouped_prepare(*common, _ptr(ws), ws.numel(), _stream(stream)),
                "lsa_attn_grouped_prepare")
     elif part == "walk":
-        _check(lib().lsa_attn_grouped_walk(*common, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
-               "lsa_attn_grouped_walk")
+        _check(lib().lsa_attn_grouped_walk(*common, _ptr(out), lp, _ptr(ws), ws.numel(),
+                                           _stream(stream)), "lsa_attn_grouped_walk")
     else:
         raise ValueError(f"part {part!r}")
     return out

@@ -776,11 +776,15 @@ __global__ void __launch_bounds__(AT, 4) k_attn_grp(AttnArgs a) {
   for (int v = 0; v < 4; ++v) {
     const int col = 4 * grp + v;
     const float lh = __shfl(l_run, col);
+    const float mh = __shfl(m_run, col);
     const int qv = __shfl(qc, col);
     const bool vv = __shfl((int)cval, col) != 0;
     if (!vv) continue;
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     const int64_t ob = ((int64_t)qv * a.Hq + (int64_t)g * G + col % G) * D;
+    // log-sum-exp: m_run and l_run are in the log2 domain of the scaled logits
+    if (a.lse && hl == 0) a.lse[(int64_t)qv * a.Hq + (int64_t)g * G + col % G] =
+        (mh + __log2f(lh)) * 0.6931471805599453f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float val = o[nb][v] * inv;
@@ -1102,7 +1106,7 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                                int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
                                int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
-                               void* ws, int parts, hipStream_t s) {
+                               float* lse, void* ws, int parts, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   if (!grouped_attn_ok(ap, lcap, kv_rows)) return hipErrorInvalidValue;
   const GrpLayout L = grp_layout(nq, ap, lcap);
@@ -1118,6 +1122,7 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
   a.out = out;
   a.qpos0 = qpos0; a.window = window; a.sinks = sinks;
   a.qpw = L.qpw;
+  a.lse = nullptr;                     // the partials carry no log-sum-exp; the walk writes it
   a.part_o = reinterpret_cast<float*>(w + L.part_o);
   a.part_ml = reinterpret_cast<float*>(w + L.part_ml);
   int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
@@ -1174,6 +1179,7 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
     if (e != hipSuccess) return e;
   }
   if (!(parts & kGroupedWalk)) return hipSuccess;
+  a.lse = lse;
 
   // 4. the unions, each column masked to its query's rows, on top of the partials
   if (ap.D == 128) {

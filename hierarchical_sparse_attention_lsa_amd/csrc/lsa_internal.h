@@ -199,7 +199,8 @@ hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16
 // are read once as a union.  Needs D in {64, 128}, G in {4, 8, 16} and
 // grouped_attn_ok(); the workspace holds the sort, the sinks-and-window
 // partials and the unions.  lcap: per-query long-range rows held in a union
-// (a group with a longer row is walked row by row).
+// (a group with a longer row is walked row by row).  lse (nullable): per
+// (query, head) natural log-sum-exp of the scaled logits, as the window path.
 bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows);
 size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap);
 // parts: kGroupedPrepare (sinks-and-window partials, query order, unions into
@@ -209,7 +210,7 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
                                int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                                int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
                                int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
-                               void* ws, int parts, hipStream_t s);
+                               float* lse, void* ws, int parts, hipStream_t s);
 
 // Backward of the sparse attention (dQ, dK, dV) over rows the select wrote
 // for consecutive query positions qpos0.., with the index they came from.

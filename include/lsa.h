@@ -245,19 +245,22 @@ LSA_API int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, con
  * LSA_E_UNSUPPORTED), and a workspace of lsa_workspace_bytes(
  * LSA_OP_ATTN_GROUPED, .., nq) bytes (else LSA_E_CAPACITY).  A group holding
  * a row with more than `budget` long-range entries is walked row by row.
- * (Grouping queries is this library's design; the pages fix only what each
- * query attends to.) */
+ * d_lse (nullable): as in lsa_sparse_attn_fwd, float32 [nq][Hq], for the
+ * training forward.  (Grouping queries is this library's design; the pages
+ * fix only what each query attends to.) */
 LSA_API int lsa_sparse_attn_grouped(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
                                     int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
                                     int32_t max_sel, int32_t nq, int64_t qpos0,
                                     const lsa_select_params* sp, const lsa_attn_params* ap,
-                                    void* d_out, void* d_ws, size_t ws_bytes, void* stream);
+                                    void* d_out, float* d_lse, void* d_ws, size_t ws_bytes,
+                                    void* stream);
 
 /* The two halves of lsa_sparse_attn_grouped, same arguments (prepare takes
- * no output), enqueued one after the other on one stream with the same
+ * no outputs), enqueued one after the other on one stream with the same
  * workspace: prepare attends every query's sinks and window into partial
  * results and builds the query order and the groups' unions in the
- * workspace; walk reads them, attends the unions and writes d_out.  The
+ * workspace; walk reads them, attends the unions and writes d_out (and
+ * d_lse when not NULL).  The
  * split lets a caller time or schedule the long-range walk on its own. */
 LSA_API int lsa_attn_grouped_prepare(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
                                      int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
@@ -268,7 +271,8 @@ LSA_API int lsa_attn_grouped_walk(const uint16_t* d_q, const uint16_t* d_k, cons
                                   int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
                                   int32_t max_sel, int32_t nq, int64_t qpos0,
                                   const lsa_select_params* sp, const lsa_attn_params* ap,
-                                  void* d_out, void* d_ws, size_t ws_bytes, void* stream);
+                                  void* d_out, float* d_lse, void* d_ws, size_t ws_bytes,
+                                  void* stream);
 
 /* Training forward: lsa_sparse_attn_window that also stores, per (query,
  * head), the natural log of the softmax denominator over the query's

@@ -121,6 +121,40 @@ def test_backward_matches_oracle(name, wl, early):
         assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
+GROUPED_CASES = [c for c in CASES if (c[1].Hq // c[1].Hkv) in (4, 8, 16)]
+
+
+@pytest.mark.parametrize("name,wl,early", GROUPED_CASES, ids=[c[0] for c in GROUPED_CASES])
+def test_grouped_forward_for_training(name, wl, early):
+    """The grouped attention as the training forward: its log-sum-exp and
+    output against the oracle's, and the backward taken from them."""
+    dev = _dev()
+    L = _L()
+    r = _setup(wl, dev, early)
+    sels, lse_ref, grads = _oracle(wl, r, early)
+    args = [t.to(dev) for t in (r["q"], r["K"], r["V"])]
+    do = r["do"].to(dev)
+    for out_f32 in (1, 0):
+        ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, out_f32, 0.0)
+        lse = torch.empty((len(r["pos"]), wl.Hq), dtype=torch.float32, device=dev)
+        out = L.sparse_attn_grouped(*args, r["idx"], r["cnt"], 0, r["sp"], ap, lse=lse)
+        out_w, lse_w = L.sparse_attn_fwd(*args, r["idx"], r["cnt"], 0, r["sp"], ap)
+        torch.cuda.synchronize()
+        assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-4
+        if out_f32:
+            assert normwise(out.cpu().numpy().astype(np.float64),
+                            out_w.cpu().numpy().astype(np.float64)) <= TOL
+        dq, dk, dv = L.sparse_attn_bwd(r["ix"], *args, r["idx"], r["cnt"], 0, r["sp"], ap, out, lse,
+                                       do)
+        torch.cuda.synchronize()
+        dQ, dK, dV = grads[out_f32]
+        errs = [normwise(x.cpu().numpy().astype(np.float64), y)
+                for x, y in ((dq, dQ), (dk, dK), (dv, dV))]
+        print(f"{name} grouped forward, out_f32={out_f32}: dQ/dK/dV normwise errors "
+              + " ".join(f"{e:.2e}" for e in errs))
+        assert max(errs) <= TOL
+
+
 def test_backward_of_a_suffix_and_unselected_keys():
     """Queries at positions qpos0.. only (a chunk), so keys after the last
     query get zero gradient and early keys get only the long-range and sink

@@ -448,7 +448,8 @@ def test_train_128k_backward(oracle_pool):
     # the softmax gradients sum to zero over the keys; the value gradients sum
     # to the upstream gradients of each KV head's query heads
     ap32 = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 1, 0.0)
-    out32, lse32 = L.sparse_attn_fwd(q, K, V, idx, cnt, 0, sp, ap32)
+    lse32 = torch.empty((T, wl.Hq), dtype=torch.float32, device=dev)
+    out32 = L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap32, lse=lse32)    # the benchmarked forward
     _, dk32, dv32 = L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap32, out32, lse32, do)
     G = wl.Hq // wl.Hkv
     dks = dk32.double().sum(0)
@@ -456,8 +457,9 @@ def test_train_128k_backward(oracle_pool):
     want = do.double().view(T, wl.Hkv, G, wl.D).sum((0, 2))
     assert float((dv32.double().sum(0) - want).abs().max()) <= 1e-4 * float(want.abs().max())
     del out32, lse32, dk32, dv32
-    # the benchmarked configuration: bf16 forward output
-    out, lse = L.sparse_attn_fwd(q, K, V, idx, cnt, 0, sp, ap)
+    # the benchmarked configuration: grouped forward, bf16 output
+    lse = torch.empty((T, wl.Hq), dtype=torch.float32, device=dev)
+    out = L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap, lse=lse)
     dq, dk, dv = L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do)
     torch.cuda.synchronize()
     # oracle over its own selections
