@@ -1063,8 +1063,10 @@ int grp_table_n(int qpw, int32_t lcap) {    // hash slots: at least twice the en
   while (n < 2 * qpw * lcap) n <<= 1;
   return n;
 }
+// The plan (query order and unions) first, then the sinks-and-window partials:
+// the backward's dQ uses the plan alone.
 struct GrpLayout {
-  size_t keys_a, keys_b, perm, part_o, part_ml, urow, umask, ucnt, total;
+  size_t keys_a, keys_b, perm, urow, umask, ucnt, plan_total, part_o, part_ml, total;
   int n_pad, qpw, ngrp, ucap;
 };
 GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
@@ -1078,13 +1080,61 @@ GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
   L.keys_a = o; o += al256((size_t)L.n_pad * 8);
   L.keys_b = o; o += al256((size_t)L.n_pad * 8);
   L.perm = o; o += al256((size_t)nq * 4);
-  L.part_o = o; o += al256((size_t)nq * ap.Hq * ap.D * 4);
-  L.part_ml = o; o += al256((size_t)nq * ap.Hq * 2 * 4);
   L.urow = o; o += al256((size_t)L.ngrp * L.ucap * 4);
   L.umask = o; o += al256((size_t)L.ngrp * L.ucap);
   L.ucnt = o; o += al256((size_t)L.ngrp * 4);
+  L.plan_total = o;
+  L.part_o = o; o += al256((size_t)nq * ap.Hq * ap.D * 4);
+  L.part_ml = o; o += al256((size_t)nq * ap.Hq * 2 * 4);
   L.total = o;
   return L;
+}
+
+// The query order and the groups' unions (a.idx, a.cnt, a.max_sel, a.nq,
+// a.qpos0, a.window, a.sinks, a.kv_rows and a.qpw set; a.perm, a.urow,
+// a.umask, a.ucnt and a.ucap are set here).
+hipError_t grouped_plan(AttnArgs& a, const GrpLayout& L, char* w, int32_t lcap, hipStream_t s) {
+  int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
+  int32_t* urow = reinterpret_cast<int32_t*>(w + L.urow);
+  uint8_t* umask = reinterpret_cast<uint8_t*>(w + L.umask);
+  int32_t* ucnt = reinterpret_cast<int32_t*>(w + L.ucnt);
+  a.perm = perm;
+  a.urow = urow; a.umask = umask; a.ucnt = ucnt; a.ucap = L.ucap;   // the union kernel's stride
+  const int nq = a.nq;
+  // the order of the queries: sort (first long-range key, MinHash, query)
+  unsigned long long* ka = reinterpret_cast<unsigned long long*>(w + L.keys_a);
+  unsigned long long* kb = reinterpret_cast<unsigned long long*>(w + L.keys_b);
+  const int use_mh = nq < (1 << kGrpMhBits) - 1 ? 1 : 0;
+  hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 3) / 4), dim3(256), 0, s, a, ka, L.n_pad, use_mh);
+  hipLaunchKernelGGL(k_grp_sort_tile, dim3(L.n_pad / GS_TILE), dim3(GS_T), 0, s, ka);
+  for (int wd = GS_TILE; wd < L.n_pad; wd <<= 1) {
+    hipLaunchKernelGGL(k_grp_merge, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, ka, kb, L.n_pad, wd);
+    std::swap(ka, kb);
+  }
+  hipLaunchKernelGGL(k_grp_perm, dim3((nq + 255) / 256), dim3(256), 0, s, ka, perm, nq, use_mh);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the groups' unions of long-range rows
+  const int ts = grp_table_n(L.qpw, lcap);
+#define LSA_UNION(TS_, QP_) \
+  hipLaunchKernelGGL((k_grp_union<TS_, QP_>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt)
+#define LSA_UNION_QP(TS_)                 \
+  switch (L.qpw) {                        \
+    case 4: LSA_UNION(TS_, 4); break;     \
+    case 2: LSA_UNION(TS_, 2); break;     \
+    default: LSA_UNION(TS_, 1); break;    \
+  }
+  switch (ts) {
+    case 2048: LSA_UNION_QP(2048); break;
+    case 4096: LSA_UNION_QP(4096); break;
+    case 8192: LSA_UNION_QP(8192); break;
+    case 16384: LSA_UNION_QP(16384); break;
+    case 32768: LSA_UNION_QP(32768); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef LSA_UNION_QP
+#undef LSA_UNION
+  return hipGetLastError();
 }
 }  // namespace
 
@@ -1100,6 +1150,36 @@ bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows) {
 size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
   if (nq <= 0) return 0;
   return grp_layout(nq, ap, lcap).total;
+}
+
+size_t grouped_plan_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
+  if (nq <= 0) return 0;
+  return grp_layout(nq, ap, lcap).plan_total;
+}
+
+hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t max_sel, int32_t nq,
+                               int64_t qpos0, int32_t window, int32_t sinks, int64_t kv_rows,
+                               int32_t lcap, const lsa_attn_params& ap, void* ws, GroupPlanView* view,
+                               hipStream_t s) {
+  if (nq <= 0) return hipSuccess;
+  if (!grouped_attn_ok(ap, lcap, kv_rows)) return hipErrorInvalidValue;
+  const GrpLayout L = grp_layout(nq, ap, lcap);
+  char* w = static_cast<char*>(ws);
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.kv_rows = kv_rows; a.idx = idx; a.cnt = cnt; a.max_sel = max_sel; a.nq = nq;
+  a.Hq = ap.Hq; a.Hkv = ap.Hkv; a.G = ap.Hq / ap.Hkv;
+  a.qpos0 = qpos0; a.window = window; a.sinks = sinks; a.qpw = L.qpw;
+  hipError_t e = grouped_plan(a, L, w, lcap, s);
+  if (e != hipSuccess) return e;
+  view->perm = reinterpret_cast<const int32_t*>(w + L.perm);
+  view->urow = reinterpret_cast<const int32_t*>(w + L.urow);
+  view->umask = reinterpret_cast<const uint8_t*>(w + L.umask);
+  view->ucnt = reinterpret_cast<const int32_t*>(w + L.ucnt);
+  view->ucap = L.ucap;
+  view->qpw = L.qpw;
+  view->ngrp = L.ngrp;
+  return hipSuccess;
 }
 
 hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -1141,47 +1221,14 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    // 2. the order of the queries: sort (first long-range key, MinHash, query)
-    unsigned long long* ka = reinterpret_cast<unsigned long long*>(w + L.keys_a);
-    unsigned long long* kb = reinterpret_cast<unsigned long long*>(w + L.keys_b);
-    const int use_mh = nq < (1 << kGrpMhBits) - 1 ? 1 : 0;
-    hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 3) / 4), dim3(256), 0, s, a, ka, L.n_pad, use_mh);
-    hipLaunchKernelGGL(k_grp_sort_tile, dim3(L.n_pad / GS_TILE), dim3(GS_T), 0, s, ka);
-    for (int wd = GS_TILE; wd < L.n_pad; wd <<= 1) {
-      hipLaunchKernelGGL(k_grp_merge, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, ka, kb, L.n_pad, wd);
-      std::swap(ka, kb);
-    }
-    hipLaunchKernelGGL(k_grp_perm, dim3((nq + 255) / 256), dim3(256), 0, s, ka, perm, nq, use_mh);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    // 3. the groups' unions of long-range rows
-    const int ts = grp_table_n(L.qpw, lcap);
-#define LSA_UNION(TS_, QP_) \
-    hipLaunchKernelGGL((k_grp_union<TS_, QP_>), dim3(L.ngrp), dim3(GU_T), 0, s, a, lcap, urow, umask, ucnt)
-#define LSA_UNION_QP(TS_)                 \
-    switch (L.qpw) {                      \
-      case 4: LSA_UNION(TS_, 4); break;   \
-      case 2: LSA_UNION(TS_, 2); break;   \
-      default: LSA_UNION(TS_, 1); break;  \
-    }
-    switch (ts) {
-      case 2048: LSA_UNION_QP(2048); break;
-      case 4096: LSA_UNION_QP(4096); break;
-      case 8192: LSA_UNION_QP(8192); break;
-      case 16384: LSA_UNION_QP(16384); break;
-      case 32768: LSA_UNION_QP(32768); break;
-      default: return hipErrorInvalidValue;
-    }
-#undef LSA_UNION_QP
-#undef LSA_UNION
-    e = hipGetLastError();
+    // 2. the query order and the groups' unions
+    e = grouped_plan(a, L, w, lcap, s);
     if (e != hipSuccess) return e;
   }
   if (!(parts & kGroupedWalk)) return hipSuccess;
   a.lse = lse;
 
-  // 4. the unions, each column masked to its query's rows, on top of the partials
+  // 3. the unions, each column masked to its query's rows, on top of the partials
   if (ap.D == 128) {
     if (f32) hipLaunchKernelGGL((k_attn_grp<128, true>), dim3(grid), dim3(AT), 0, s, a);
     else hipLaunchKernelGGL((k_attn_grp<128, false>), dim3(grid), dim3(AT), 0, s, a);

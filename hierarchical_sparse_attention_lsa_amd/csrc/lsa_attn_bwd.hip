@@ -31,6 +31,7 @@
 //   long-range entries in one bucket is one taken bucket, and its last entry
 //   is the largest key taken.  A counting sort over (bucket, query tile)
 //   orders every list by query.
+#include <algorithm>
 #include <climits>
 #include <cstring>
 
@@ -89,6 +90,12 @@ struct BwdArgs {
   int32_t n_tiles;
   float* sink_part;         // [n_sink_chunks][Hkv][KTT][D] dK, then the same for dV
   int32_t n_sink_chunks;
+  // grouped dQ: query order and unions of each group of gqpw slots
+  const int32_t* perm;
+  const int32_t* urow;
+  const uint8_t* umask;
+  const int32_t* ucnt;
+  int32_t ucap, gqpw;
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int nwg) {
@@ -192,7 +199,9 @@ __device__ __forceinline__ void dq_tile(const v8bf (&qb)[D / 32], const v8bf (&d
   wave_sync_lds();
 }
 
-template <int D>
+// MODE 0: a query's long-range rows and the group's sinks and windows; MODE
+// 1: the sinks and windows alone (the grouped pass adds the long range).
+template <int D, int MODE>
 __global__ void __launch_bounds__(BT, 2) k_bwd_dq(BwdArgs a) {
   constexpr int NKK = D / 32;
   constexpr int NB = D / 16;
@@ -251,7 +260,7 @@ __global__ void __launch_bounds__(BT, 2) k_bwd_dq(BwdArgs a) {
   auto nsink_of = [&](int ws) { return max(0, min(a.sinks, ws)); };
 
   // 1. long-range rows of each query (its own columns unmasked)
-  for (int j = 0; j < nqw; ++j) {
+  for (int j = 0; j < (MODE == 0 ? nqw : 0); ++j) {
     const int q = q0 + j;
     const int t = tq0 + j;
     const int ws = wstart_of(t);
@@ -306,6 +315,119 @@ __global__ void __launch_bounds__(BT, 2) k_bwd_dq(BwdArgs a) {
   }
 }
 
+// long-range entries of query qi: the row's entries before its sinks and window
+__device__ __forceinline__ int lr_count(const BwdArgs& a, int qi) {
+  const int t = a.qpos0 + qi;
+  const int ws = max(0, t - a.window + 1);
+  const int nfix = max(0, min(a.sinks, ws)) + (t - ws + 1);
+  return max(0, min(a.cnt[qi], a.max_sel) - nfix);
+}
+
+// Grouped dQ: the long-range part of dQ over the grouped attention's plan.
+// One wave per (group, KV head); the columns are (query slot, head) of the
+// group's queries (perm), the union's rows are walked once, each column
+// masked to its query's rows (a group over the cap walks each query's rows
+// in turn).  dsum comes from the window pass (k_bwd_dq<D, 1>), which also
+// wrote the window part of dQ; this pass adds to it (each (query, head) row
+// of dQ is one wave's in each pass).
+template <int D>
+__global__ void __launch_bounds__(BT, 2) k_bwd_dq_grp(BwdArgs a) {
+  constexpr int NKK = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int KROW = D * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char klds[BW][KT * KROW];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int item = xcd_remap(blockIdx.x, gridDim.x) * BW + wave;
+  const int QPW = a.gqpw;
+  const int ngrp = (a.nq + QPW - 1) / QPW;
+  if (item >= ngrp * a.Hkv) return;
+  const int g = item % a.Hkv;
+  const int gi = item / a.Hkv;
+  const int G = a.G;
+  const int hl = lane & 15, grp = lane >> 4;
+  const int jc = hl / G, hc = hl % G;
+  const int slot = gi * QPW + jc;
+  const bool cval = jc < QPW && slot < a.nq;
+  const int qc = cval ? a.perm[slot] : 0;
+  const int64_t qh = (int64_t)qc * a.Hq + (int64_t)g * G + hc;
+
+  v8bf qb[NKK], db[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int64_t e = qh * D + 32 * kk + 8 * grp;
+    v4i rq = {0, 0, 0, 0}, rd = {0, 0, 0, 0};
+    if (cval) {
+      rq = *reinterpret_cast<const v4i*>(a.q + e);
+      rd = *reinterpret_cast<const v4i*>(a.dout + e);
+    }
+    qb[kk] = __builtin_bit_cast(v8bf, rq);
+    db[kk] = __builtin_bit_cast(v8bf, rd);
+  }
+  const float dsum = cval ? a.dsum[qh] : 0.f;
+  const float lse2 = cval ? a.lse[qh] * kLog2e : 0.f;
+
+  v4f acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  char* kl = klds[wave];
+  const int64_t rowstride = (int64_t)a.Hkv * D;
+  const int64_t rmax = a.kv_rows - 1;
+  const uint16_t* kbase = a.k + (int64_t)g * D;
+  const uint16_t* vbase = a.v + (int64_t)g * D;
+  const int nu = a.ucnt[gi];
+  if (nu >= 0) {
+    const int32_t* ur = a.urow + (int64_t)gi * a.ucap;
+    const uint8_t* um = a.umask + (int64_t)gi * a.ucap;
+    for (int kb = 0; kb < nu; kb += KT) {
+      const int sl = kb + hl;
+      int r = sl < nu ? ur[sl] : 0;
+      r = (int)min((int64_t)max(r, 0), rmax);
+      // masks of union rows kb + 4 grp .. +3 (ucap is a multiple of 4)
+      const int k4 = kb + 4 * grp;
+      const unsigned m4 = k4 < nu ? *reinterpret_cast<const unsigned*>(um + k4) : 0u;
+      unsigned vmask = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bool in = cval && k4 + v < nu && ((m4 >> (8 * v + jc)) & 1u);
+        vmask |= (in ? 1u : 0u) << v;
+      }
+      dq_tile<D>(qb, db, kbase, vbase, rowstride, r, vmask, a.scale_log2, lse2, dsum, kl, acc);
+    }
+  } else {
+    for (int j = 0; j < QPW; ++j) {
+      const int sl = gi * QPW + j;
+      if (sl >= a.nq) break;
+      const int q = a.perm[sl];
+      const int nlr = lr_count(a, q);
+      const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
+      const bool mine = cval && jc == j;
+      for (int kb = 0; kb < nlr; kb += KT) {
+        const int s2 = kb + hl;
+        int r = s2 < nlr ? idxrow[s2] : 0;
+        r = (int)min((int64_t)max(r, 0), rmax);
+        unsigned vmask = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vmask |= (mine && kb + 4 * grp + v < nlr ? 1u : 0u) << v;
+        dq_tile<D>(qb, db, kbase, vbase, rowstride, r, vmask, a.scale_log2, lse2, dsum, kl, acc);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int col = 4 * grp + v;
+    const int qv = __shfl(qc, col);
+    const bool vv = __shfl((int)cval, col) != 0;
+    if (!vv) continue;
+    const int64_t ob = ((int64_t)qv * a.Hq + (int64_t)g * G + col % G) * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) a.dq[ob + 16 * nb + hl] += acc[nb][v] * a.scale;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // (bucket -> queries) lists
 
@@ -322,13 +444,6 @@ __device__ __forceinline__ int bucket_of_key(const BwdArgs& a, int j) {
   return m < a.n_pool ? a.map[m] : -1;
 }
 
-// long-range entries of query qi: the row's entries before its sinks and window
-__device__ __forceinline__ int lr_count(const BwdArgs& a, int qi) {
-  const int t = a.qpos0 + qi;
-  const int ws = max(0, t - a.window + 1);
-  const int nfix = max(0, min(a.sinks, ws)) + (t - ws + 1);
-  return max(0, min(a.cnt[qi], a.max_sel) - nfix);
-}
 
 // MODE 0: count the runs per (bucket, tile); MODE 1: place them.  A run ends
 // at entry e when the next entry lies in another bucket.
@@ -683,8 +798,10 @@ struct BwdLayout {
   int32_t n_tiles, n_sink_chunks;
 };
 
+// plan_bytes: the grouped dQ's plan, which shares the list's bytes (the plan
+// is used up before the lists are written)
 BwdLayout bwd_layout(int32_t nq, int32_t Hq, int32_t Hkv, int32_t D, int64_t max_pool,
-                     int64_t max_bkt, int32_t budget) {
+                     int64_t max_bkt, int32_t budget, int64_t plan_bytes) {
   BwdLayout L;
   L.n_tiles = (nq + QT - 1) / QT;
   L.n_sink_chunks = (nq + SINK_QC - 1) / SINK_QC;
@@ -697,7 +814,7 @@ BwdLayout bwd_layout(int32_t nq, int32_t Hq, int32_t Hkv, int32_t D, int64_t max
   L.ntl = o;    o = align256(o + max_bkt * 4);
   L.bstart = o; o = align256(o + (max_bkt + 1) * 4);
   L.ktile0 = o; o = align256(o + (max_bkt + 1) * 4);
-  L.list = o;   o = align256(o + L.list_cap * 8);
+  L.list = o;   o = align256(o + std::max(L.list_cap * 8, plan_bytes));
   L.sink = o;   o = align256(o + (int64_t)L.n_sink_chunks * Hkv * KTT * D * 2 * 4);
   L.total = o;
   return L;
@@ -705,14 +822,24 @@ BwdLayout bwd_layout(int32_t nq, int32_t Hq, int32_t Hkv, int32_t D, int64_t max
 
 }  // namespace
 
+namespace {
+// bytes of the grouped dQ's plan (0 when the shape takes the ungrouped dQ)
+int64_t bwd_plan_bytes(int32_t nq, const lsa_attn_params& ap, int32_t budget) {
+  return grouped_attn_ok(ap, budget, 1) ? (int64_t)grouped_plan_ws_bytes(nq, ap, budget) : 0;
+}
+}  // namespace
+
 size_t attn_bwd_ws_bytes(int32_t nq, const lsa_attn_params& ap, int64_t max_pool, int64_t max_bkt,
                          int32_t budget) {
-  return (size_t)bwd_layout(nq, ap.Hq, ap.Hkv, ap.D, max_pool, max_bkt, budget).total;
+  return (size_t)bwd_layout(nq, ap.Hq, ap.Hkv, ap.D, max_pool, max_bkt, budget,
+                            bwd_plan_bytes(nq, ap, budget)).total;
 }
 
 hipError_t launch_attn_bwd(const BwdInputs& in, const lsa_attn_params& ap, hipStream_t s) {
   if (in.nq <= 0) return hipSuccess;
-  const BwdLayout L = bwd_layout(in.nq, ap.Hq, ap.Hkv, ap.D, in.max_pool, in.max_bkt, in.budget);
+  const int64_t plan_bytes = bwd_plan_bytes(in.nq, ap, in.budget);
+  const BwdLayout L = bwd_layout(in.nq, ap.Hq, ap.Hkv, ap.D, in.max_pool, in.max_bkt, in.budget,
+                                 plan_bytes);
   char* ws = static_cast<char*>(in.ws);
   BwdArgs a;
   memset(&a, 0, sizeof a);
@@ -740,12 +867,29 @@ hipError_t launch_attn_bwd(const BwdInputs& in, const lsa_attn_params& ap, hipSt
   a.n_sink_chunks = L.n_sink_chunks;
   const bool d128 = ap.D == 128;
 
-  // dQ (and dsum)
+  // dQ (and dsum): grouped (window pass, then the long range over the plan's
+  // unions) when the shape allows, else one pass
   {
     const int64_t items = (int64_t)((in.nq + a.qpw - 1) / a.qpw) * ap.Hkv;
     const unsigned grid = (unsigned)((items + BW - 1) / BW);
-    if (d128) hipLaunchKernelGGL(k_bwd_dq<128>, dim3(grid), dim3(BT), 0, s, a);
-    else hipLaunchKernelGGL(k_bwd_dq<64>, dim3(grid), dim3(BT), 0, s, a);
+    if (plan_bytes > 0 && grouped_attn_ok(ap, in.budget, in.kv_rows)) {
+      GroupPlanView pv;
+      if (hipError_t e = launch_grouped_plan(in.idx, in.cnt, in.max_sel, in.nq, in.qpos0, in.window,
+                                             in.sinks, in.kv_rows, in.budget, ap, ws + L.list, &pv, s))
+        return e;
+      a.perm = pv.perm; a.urow = pv.urow; a.umask = pv.umask; a.ucnt = pv.ucnt;
+      a.ucap = pv.ucap; a.gqpw = pv.qpw;
+      if (d128) hipLaunchKernelGGL((k_bwd_dq<128, 1>), dim3(grid), dim3(BT), 0, s, a);
+      else hipLaunchKernelGGL((k_bwd_dq<64, 1>), dim3(grid), dim3(BT), 0, s, a);
+      if (hipError_t e = hipGetLastError()) return e;
+      const int64_t gitems = (int64_t)pv.ngrp * ap.Hkv;
+      const unsigned ggrid = (unsigned)((gitems + BW - 1) / BW);
+      if (d128) hipLaunchKernelGGL(k_bwd_dq_grp<128>, dim3(ggrid), dim3(BT), 0, s, a);
+      else hipLaunchKernelGGL(k_bwd_dq_grp<64>, dim3(ggrid), dim3(BT), 0, s, a);
+    } else {
+      if (d128) hipLaunchKernelGGL((k_bwd_dq<128, 0>), dim3(grid), dim3(BT), 0, s, a);
+      else hipLaunchKernelGGL((k_bwd_dq<64, 0>), dim3(grid), dim3(BT), 0, s, a);
+    }
     if (hipError_t e = hipGetLastError()) return e;
   }
   // band: stores every key row of dK / dV

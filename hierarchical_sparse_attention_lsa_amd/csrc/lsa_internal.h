@@ -212,6 +212,23 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
                                int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
                                float* lse, void* ws, int parts, hipStream_t s);
 
+// The grouped attention's plan alone: query order (perm: slot -> query) and
+// the unions of each group of qpw consecutive slots (urow / umask, ucap apart;
+// ucnt -1 for a group over the cap), in the workspace's first
+// grouped_plan_ws_bytes bytes.
+struct GroupPlanView {
+  const int32_t* perm;
+  const int32_t* urow;
+  const uint8_t* umask;
+  const int32_t* ucnt;
+  int32_t ucap, qpw, ngrp;
+};
+size_t grouped_plan_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap);
+hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t max_sel, int32_t nq,
+                               int64_t qpos0, int32_t window, int32_t sinks, int64_t kv_rows,
+                               int32_t lcap, const lsa_attn_params& ap, void* ws, GroupPlanView* view,
+                               hipStream_t s);
+
 // Backward of the sparse attention (dQ, dK, dV) over rows the select wrote
 // for consecutive query positions qpos0.., with the index they came from.
 struct BwdInputs {
