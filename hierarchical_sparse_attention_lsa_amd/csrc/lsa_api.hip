@@ -485,7 +485,7 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
       size_t phase = select_fast_ws_bytes((int32_t)n);
       if (aprm) {
         if (int e = check_attn_params(aprm)) return e;
-        if (grouped_attn_ok(*aprm, sprm->budget, 1))
+        if (grouped_attn_ok(*aprm, sprm->budget, 1) && grouped_nq_ok(n))
           phase = std::max(phase, attn_grouped_ws_bytes((int32_t)n, *aprm, sprm->budget));
       }
       *bytes = (size_t)align_up(n * max_sel_of(sprm) * 4) + (size_t)align_up(n * 4) + phase;
@@ -494,7 +494,8 @@ int lsa_workspace_bytes(int op, const lsa_index_params* iprm, const lsa_select_p
     case LSA_OP_ATTN_GROUPED: {
       if (int e = check_select_params(sprm, false)) return e;
       if (int e = check_attn_params(aprm)) return e;
-      if (n > INT32_MAX) return fail(LSA_E_ARG, "n > INT32_MAX");
+      if (!grouped_nq_ok(n)) return fail(LSA_E_UNSUPPORTED, "grouped attention takes at most %lld queries",
+                                         (long long)kGroupedMaxQueries);
       *bytes = attn_grouped_ws_bytes((int32_t)n, *aprm, sprm->budget);
       return LSA_OK;
     }
@@ -609,9 +610,9 @@ static int grouped_parts(const uint16_t* d_q, const uint16_t* d_k, const uint16_
                          const lsa_attn_params* ap, void* d_out, float* d_lse, void* d_ws,
                          size_t ws_bytes, void* stream, int parts) {
   if (int e = check_window_attn(kv_rows, max_sel, nq, qpos0, sp, ap)) return e;
-  if (!grouped_attn_ok(*ap, sp->budget, kv_rows))
+  if (!grouped_attn_ok(*ap, sp->budget, kv_rows) || !grouped_nq_ok(nq))
     return fail(LSA_E_UNSUPPORTED, "grouped attention needs D in {64, 128}, Hq/Hkv in {4, 8, 16}, "
-                "(16 / (Hq/Hkv)) * budget <= 16384 and kv_rows < 2^28");
+                "(16 / (Hq/Hkv)) * budget <= 16384, kv_rows < 2^28 and nq <= 2^26");
   if (nq == 0) return LSA_OK;
   if (!d_q || !d_k || !d_v || !d_idx || !d_cnt || ((parts & kGroupedWalk) && !d_out))
     return fail(LSA_E_ARG, "NULL buffer");
@@ -733,7 +734,7 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
   rc = select_impl(h, d_latq, nullptr, (int32_t)t0, (int32_t)n_chunk, sp, idx, cnt, sel_ws,
                    select_fast_ws_bytes((int32_t)n_chunk), s);
   if (rc != LSA_OK) return rc;
-  if (grouped_attn_ok(*ap, sp->budget, kv_rows) &&
+  if (grouped_attn_ok(*ap, sp->budget, kv_rows) && grouped_nq_ok(n_chunk) &&
       ws_bytes - a_idx >= attn_grouped_ws_bytes((int32_t)n_chunk, *ap, sp->budget)) {
     LSA_HIP(launch_attn_grouped(d_q, d_k, d_v, kv_rows, idx, cnt, max_sel, (int32_t)n_chunk, t0,
                                 sp->window, sp->sinks, sp->budget, *ap, d_out, nullptr, sel_ws,

@@ -1138,6 +1138,8 @@ hipError_t grouped_plan(AttnArgs& a, const GrpLayout& L, char* w, int32_t lcap, 
 }
 }  // namespace
 
+bool grouped_nq_ok(int64_t nq) { return nq >= 0 && nq <= kGroupedMaxQueries; }
+
 bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows) {
   if (ap.D != 64 && ap.D != 128) return false;
   if (ap.Hkv <= 0 || ap.Hq % ap.Hkv != 0) return false;
@@ -1148,12 +1150,12 @@ bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows) {
 }
 
 size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
-  if (nq <= 0) return 0;
+  if (nq <= 0 || !grouped_nq_ok(nq)) return 0;
   return grp_layout(nq, ap, lcap).total;
 }
 
 size_t grouped_plan_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
-  if (nq <= 0) return 0;
+  if (nq <= 0 || !grouped_nq_ok(nq)) return 0;
   return grp_layout(nq, ap, lcap).plan_total;
 }
 
@@ -1162,7 +1164,7 @@ hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t m
                                int32_t lcap, const lsa_attn_params& ap, void* ws, GroupPlanView* view,
                                hipStream_t s) {
   if (nq <= 0) return hipSuccess;
-  if (!grouped_attn_ok(ap, lcap, kv_rows)) return hipErrorInvalidValue;
+  if (!grouped_attn_ok(ap, lcap, kv_rows) || !grouped_nq_ok(nq)) return hipErrorInvalidValue;
   const GrpLayout L = grp_layout(nq, ap, lcap);
   char* w = static_cast<char*>(ws);
   AttnArgs a;
@@ -1188,7 +1190,7 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
                                int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
                                float* lse, void* ws, int parts, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
-  if (!grouped_attn_ok(ap, lcap, kv_rows)) return hipErrorInvalidValue;
+  if (!grouped_attn_ok(ap, lcap, kv_rows) || !grouped_nq_ok(nq)) return hipErrorInvalidValue;
   const GrpLayout L = grp_layout(nq, ap, lcap);
   char* w = static_cast<char*>(ws);
   AttnArgs a;

@@ -825,7 +825,8 @@ BwdLayout bwd_layout(int32_t nq, int32_t Hq, int32_t Hkv, int32_t D, int64_t max
 namespace {
 // bytes of the grouped dQ's plan (0 when the shape takes the ungrouped dQ)
 int64_t bwd_plan_bytes(int32_t nq, const lsa_attn_params& ap, int32_t budget) {
-  return grouped_attn_ok(ap, budget, 1) ? (int64_t)grouped_plan_ws_bytes(nq, ap, budget) : 0;
+  return grouped_attn_ok(ap, budget, 1) && grouped_nq_ok(nq) ? (int64_t)grouped_plan_ws_bytes(nq, ap, budget)
+                                                              : 0;
 }
 }  // namespace
 

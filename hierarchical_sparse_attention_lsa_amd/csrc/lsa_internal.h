@@ -202,6 +202,9 @@ hipError_t launch_attn_window(const uint16_t* q, const uint16_t* k, const uint16
 // (a group with a longer row is walked row by row).  lse (nullable): per
 // (query, head) natural log-sum-exp of the scaled logits, as the window path.
 bool grouped_attn_ok(const lsa_attn_params& ap, int32_t lcap, int64_t kv_rows);
+// queries one grouped call takes (the sort's padded size stays in int32)
+constexpr int64_t kGroupedMaxQueries = (int64_t)1 << 26;
+bool grouped_nq_ok(int64_t nq);
 size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap);
 // parts: kGroupedPrepare (sinks-and-window partials, query order, unions into
 // the workspace) and / or kGroupedWalk (the long-range walk from them).

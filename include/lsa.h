@@ -241,7 +241,7 @@ LSA_API int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, con
  * to its own keys, on top of its sinks and window (attended first, as in
  * lsa_sparse_attn_window).  Same attention over the same key set per query;
  * only the summation order differs, and it is the same on every call.  Needs D in {64, 128}, G = Hq/Hkv in {4,
- * 8, 16}, (16/G) * budget <= 16384 and kv_rows < 2^28 (else
+ * 8, 16}, (16/G) * budget <= 16384, kv_rows < 2^28 and nq <= 2^26 (else
  * LSA_E_UNSUPPORTED), and a workspace of lsa_workspace_bytes(
  * LSA_OP_ATTN_GROUPED, .., nq) bytes (else LSA_E_CAPACITY).  A group holding
  * a row with more than `budget` long-range entries is walked row by row.

@@ -75,6 +75,45 @@ def _fake_index(lib, p):
     return desc
 
 
+def test_grouped_attention_sizes_without_device():
+    """Workspace sizing of the grouped attention: the union arrays hold 16/G x
+    budget rows per group, the prefill workspace grows to hold the grouped
+    attention only when the attention params are given and the shape takes
+    it, and shapes it does not take are refused before anything runs."""
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("library not built")
+    lib = L.lib()
+    sp = L.SelectParams(4096, 512, 4, 0)
+    ap = L.AttnParams(32, 8, 128, 0, 0.0)
+    nq = 32768
+    g = L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap, nq)
+    ngrp = nq // 4
+    # unions (4 B row + 1 B mask per slot) and the sinks-and-window partials
+    assert g >= ngrp * 4 * 4096 * 5 + nq * 32 * (128 + 2) * 4
+    assert g < 2 * (ngrp * 4 * 4096 * 5 + nq * 32 * (128 + 2) * 4)
+    p = L.IndexParams(64, 4, 4096, 256, 4, 0, 0, 0, 10 * 2 ** 20)
+    with_attn = L.workspace_bytes(L.binding.OP_PREFILL, p, sp, ap, nq)
+    without = L.workspace_bytes(L.binding.OP_PREFILL, p, sp, None, nq)
+    assert with_attn >= without and with_attn >= g
+    g1 = L.AttnParams(8, 8, 128, 0, 0.0)              # G = 1: no grouping, no extra space
+    assert L.workspace_bytes(L.binding.OP_PREFILL, p, sp, g1, nq) == without
+    with pytest.raises(L.LsaError):
+        L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap, (1 << 26) + 1)
+    fake = ctypes.c_void_p(16)
+    n = ctypes.c_size_t(0)
+    sp_big = L.SelectParams(8192, 512, 4, 0)          # 4 queries x 8192 rows: over the union cap
+    for a, s_ in ((g1, sp), (L.AttnParams(32, 8, 96, 0, 0.0), sp), (ap, sp_big)):
+        rc = lib.lsa_sparse_attn_grouped(fake, fake, fake, 1 << 20, fake, fake, s_.max_sel, 16, 0,
+                                         ctypes.byref(s_), ctypes.byref(a), fake, None, fake,
+                                         ctypes.c_size_t(1 << 40), None)
+        assert rc == 2, (a.Hq, a.Hkv, a.D, s_.budget)
+    # a workspace below the size is refused, nothing enqueued
+    rc = lib.lsa_sparse_attn_grouped(fake, fake, fake, 1 << 20, fake, fake, sp.max_sel, 16, 0,
+                                     ctypes.byref(sp), ctypes.byref(ap), fake, None, fake,
+                                     ctypes.c_size_t(1024), None)
+    assert rc == 3
+
+
 def test_training_and_tree_argument_validation_without_device():
     if not os.path.exists(L.LIB_PATH):
         pytest.skip("library not built")
