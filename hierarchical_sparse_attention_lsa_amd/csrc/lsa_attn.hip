@@ -667,18 +667,25 @@ __global__ void __launch_bounds__(GU_T) k_grp_union(AttnArgs a, int lcap, int32_
 // One wave per (group, KV head): the group's qpw queries x G heads are the
 // 16 columns; the state starts from the sinks-and-window partial, then the
 // union rows are walked once, each column masked to the rows its query took.
+// GW waves per workgroup (4: a group's KV heads in two workgroups, which
+// measured 1.4% faster than all 8 in one); with kGrpPipe the next tile's
+// loads are in flight during the current tile's MFMAs (168 VGPRs, 3 waves per
+// SIMD: no faster, so off).
+constexpr int GW = 4;
+constexpr bool kGrpPipe = false;
+constexpr int GWAVES = kGrpPipe ? 3 : 4;   // waves per SIMD the registers allow
 template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(AT, 4) k_attn_grp(AttnArgs a) {
+__global__ void __launch_bounds__(GW * 64, GWAVES) k_attn_grp(AttnArgs a) {
   constexpr int NKK = D / 32;
   constexpr int NB = D / 16;
   constexpr int VROW = D * 2 + 16;
-  __shared__ __attribute__((aligned(16))) char vlds[AW][KT * VROW];
-  __shared__ __attribute__((aligned(16))) char qlds[AW][16 * qrow_bytes(D)];
+  __shared__ __attribute__((aligned(16))) char vlds[GW][KT * VROW];
+  __shared__ __attribute__((aligned(16))) char qlds[GW][16 * qrow_bytes(D)];
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int nwg = gridDim.x;
-  const int item = xcd_remap(blockIdx.x, nwg) * AW + wave;
+  const int item = xcd_remap(blockIdx.x, nwg) * GW + wave;
   const int QPW = a.qpw;
   const int ngrp = (a.nq + QPW - 1) / QPW;
   if (item >= ngrp * a.Hkv) return;
@@ -735,10 +742,12 @@ __global__ void __launch_bounds__(AT, 4) k_attn_grp(AttnArgs a) {
   if (nu >= 0) {
     const int32_t* ur = a.urow + (int64_t)gi * a.ucap;
     const uint8_t* um = a.umask + (int64_t)gi * a.ucap;
-    for (int kb = 0; kb < nu; kb += KT) {
-      const int s = kb + hl;
-      int r = s < nu ? ur[s] : 0;
-      r = (int)min((int64_t)max(r, 0), rmax);
+    auto row_of = [&](int kb) -> int {
+      const int sl = kb + hl;
+      const int r = sl < nu ? ur[sl] : 0;
+      return (int)min((int64_t)max(r, 0), rmax);
+    };
+    auto mask_of = [&](int kb) -> unsigned {
       // masks of union rows kb + 4 grp .. +3 (ucap is a multiple of 4)
       const int k4 = kb + 4 * grp;
       const unsigned m4 = k4 < nu ? *reinterpret_cast<const unsigned*>(um + k4) : 0u;
@@ -748,7 +757,23 @@ __global__ void __launch_bounds__(AT, 4) k_attn_grp(AttnArgs a) {
         const bool in = cval && k4 + v < nu && ((m4 >> (8 * v + jc)) & 1u);
         vmask |= (in ? 1u : 0u) << v;
       }
-      attn_tile<D>(qb, kbase, vbase, rowstride, r, vmask, a.scale_log2, vl, o, m_run, l_run);
+      return vmask;
+    };
+    if (kGrpPipe) {
+      TileRegs<D> T0, T1;
+      if (nu > 0) tile_load<D>(T0, kbase, vbase, rowstride, row_of(0));
+      int kb = 0;
+      for (; kb + KT < nu; kb += 2 * KT) {
+        tile_load<D>(T1, kbase, vbase, rowstride, row_of(kb + KT));
+        tile_compute<D>(qb, T0, mask_of(kb), a.scale_log2, vl, o, m_run, l_run);
+        if (kb + 2 * KT < nu) tile_load<D>(T0, kbase, vbase, rowstride, row_of(kb + 2 * KT));
+        tile_compute<D>(qb, T1, mask_of(kb + KT), a.scale_log2, vl, o, m_run, l_run);
+      }
+      if (kb < nu) tile_compute<D>(qb, T0, mask_of(kb), a.scale_log2, vl, o, m_run, l_run);
+    } else {
+      for (int kb = 0; kb < nu; kb += KT)
+        attn_tile<D>(qb, kbase, vbase, rowstride, row_of(kb), mask_of(kb), a.scale_log2, vl, o, m_run,
+                     l_run);
     }
   } else {
     // a row over the union cap: each query's long-range keys in turn
@@ -1231,12 +1256,13 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
   a.lse = lse;
 
   // 3. the unions, each column masked to its query's rows, on top of the partials
+  const unsigned ggrid = (unsigned)(((size_t)L.ngrp * ap.Hkv + GW - 1) / GW);
   if (ap.D == 128) {
-    if (f32) hipLaunchKernelGGL((k_attn_grp<128, true>), dim3(grid), dim3(AT), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_grp<128, false>), dim3(grid), dim3(AT), 0, s, a);
+    if (f32) hipLaunchKernelGGL((k_attn_grp<128, true>), dim3(ggrid), dim3(GW * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_grp<128, false>), dim3(ggrid), dim3(GW * 64), 0, s, a);
   } else {
-    if (f32) hipLaunchKernelGGL((k_attn_grp<64, true>), dim3(grid), dim3(AT), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_grp<64, false>), dim3(grid), dim3(AT), 0, s, a);
+    if (f32) hipLaunchKernelGGL((k_attn_grp<64, true>), dim3(ggrid), dim3(GW * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_grp<64, false>), dim3(ggrid), dim3(GW * 64), 0, s, a);
   }
   return hipGetLastError();
 }
