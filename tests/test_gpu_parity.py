@@ -239,6 +239,40 @@ def test_tiny_prefill_chunk_fused(tiny):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (4, 4), (6, 2)])
+def test_prefill_chunk_grouped_and_window_paths(tiny, Hq, Hkv):
+    """lsa_prefill_chunk takes the grouped attention for G = Hq/Hkv in {4, 8,
+    16} and the window kernel otherwise (G = 1, 3 here); both against the
+    oracle on the same selections."""
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    wl2 = dataclasses.replace(wl, Hq=Hq, Hkv=Hkv)
+    g2 = S.Synth(wl2)
+    t0 = wl.T - wl.chunk
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    ap = L.AttnParams(Hq, Hkv, wl.D, 1, 0.0)
+    K = torch.empty((wl.T, Hkv, wl.D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g2.fill_rows("k", K, 0)
+    g2.fill_rows("v", V, 0)
+    pos = list(range(t0, wl.T))
+    lq = g.latq_rows(torch.tensor(pos))
+    q = g2.q_rows(torch.tensor(pos))
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk[:t0].to(dev))
+    idx = torch.empty((wl.chunk, sp.max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((wl.chunk,), dtype=torch.int32, device=dev)
+    out = ix.prefill_chunk(latk[t0:].to(dev), lq.to(dev), q.to(dev), K.to(dev), V.to(dev), sp, ap,
+                           idx=idx, cnt=cnt)
+    torch.cuda.synchronize()
+    osp = O.SelectParams(wl.budget, wl.window, wl.sinks)
+    sels = [O.select(ref, lq[i].numpy(), t, osp) for i, t in enumerate(pos)]
+    check_selection(idx, cnt, sels, wl.max_sel)
+    err = normwise(out.cpu().numpy().astype(np.float64), oracle_attention(g2, wl2, pos, sels))
+    print(f"prefill chunk G={Hq // Hkv}: normwise error {err:.3e}")
+    assert err <= TOL
+
+
 def test_position_dependent_budget(tiny):
     """Queries before early_until take early_budget long-range keys, later ones
     the full budget; the switch falls inside one launch.  Checked on the
