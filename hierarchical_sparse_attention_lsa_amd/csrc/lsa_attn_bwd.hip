@@ -680,6 +680,11 @@ __global__ void __launch_bounds__(KW * 64, 2) k_bwd_dkv(BwdArgs a) {
     }
   };
 
+  // a wave none of whose key slots holds a key (the tail of a bucket's last
+  // 64-key tile; most tiles of the small buckets queries take) still loads
+  // and stages its share of each group, but computes nothing
+  const bool wave_live = __builtin_amdgcn_ballot_w64(kval) != 0;
+
   // two groups in flight ahead of the one being computed
   Grp ra, rb;
   if (c0 < c1) fetch(ra, c0);
@@ -690,6 +695,7 @@ __global__ void __launch_bounds__(KW * 64, 2) k_bwd_dkv(BwdArgs a) {
     __syncthreads();
     ra = rb;
     if (cg + 2 * QPW < c1) fetch(rb, cg + 2 * QPW);
+    if (!wave_live) continue;        // wave-uniform; the barriers above stay matched
 
     v8bf qa[NKK], da[NKK];
 #pragma unroll
