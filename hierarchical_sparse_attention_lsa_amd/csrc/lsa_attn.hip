@@ -698,7 +698,9 @@ __global__ void __launch_bounds__(GW * 64, GWAVES) k_attn_grp(AttnArgs a) {
   const int jc = hl / G, hc = hl % G;
   const int slot = gi * QPW + jc;
   const bool cval = jc < QPW && slot < a.nq;
-  const int qc = cval ? a.perm[slot] : 0;
+  // the plan comes from the workspace: its order and counts are clamped, so a
+  // walk on a workspace no prepare wrote reads nothing out of bounds
+  const int qc = cval ? min(max(a.perm[slot], 0), a.nq - 1) : 0;
 
   const int64_t rowstride = (int64_t)a.Hkv * D;
   const int64_t rmax = a.kv_rows - 1;
@@ -738,7 +740,7 @@ __global__ void __launch_bounds__(GW * 64, GWAVES) k_attn_grp(AttnArgs a) {
   char* vl = vlds[wave];
   const uint16_t* kbase = a.k + (int64_t)g * D;
   const uint16_t* vbase = a.v + (int64_t)g * D;
-  const int nu = a.ucnt[gi];
+  const int nu = min(a.ucnt[gi], a.ucap);
   if (nu >= 0) {
     const int32_t* ur = a.urow + (int64_t)gi * a.ucap;
     const uint8_t* um = a.umask + (int64_t)gi * a.ucap;
@@ -780,7 +782,7 @@ __global__ void __launch_bounds__(GW * 64, GWAVES) k_attn_grp(AttnArgs a) {
     for (int j = 0; j < QPW; ++j) {
       const int sl = gi * QPW + j;
       if (sl >= a.nq) break;
-      const int q = a.perm[sl];
+      const int q = min(max(a.perm[sl], 0), a.nq - 1);
       const int nlr = long_range_count(a, q);
       const int32_t* idxrow = a.idx + (int64_t)q * a.max_sel;
       const bool mine = cval && jc == j;
