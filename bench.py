@@ -110,21 +110,49 @@ def _grp_mix(x: np.ndarray) -> np.ndarray:
     return x
 
 
-def grouped_unions(wl, t0, idx_h: np.ndarray, cnt_h: np.ndarray):
+def latent_nn_roots(latq_h: np.ndarray) -> np.ndarray:
+    """Host recount of the grouped attention's latent order: each query's
+    nearest other query (the j != i maximising 2 x_i.x_j - |x_j|^2, lowest j
+    of equal scores; float32 holds these integers exactly), then the lower
+    index of the mutual pair each query's chain of neighbours ends in."""
+    x = torch.from_numpy(latq_h.astype(np.float32))
+    n = x.shape[0]
+    nrm = (x * x).sum(1)
+    nn = np.empty(n, dtype=np.int64)
+    for b0 in range(0, n, 2048):
+        s = 2 * x[b0:b0 + 2048] @ x.T - nrm[None, :]
+        r = torch.arange(s.shape[0])
+        s[r, r + b0] = -float("inf")
+        nn[b0:b0 + 2048] = s.argmax(1).numpy() if n > 1 else b0 + r.numpy()
+    p = nn.copy()
+    reach = 1
+    while reach < 2 * n:
+        p = p[p]
+        reach *= 2
+    return np.minimum(p, nn[p])
+
+
+def grouped_unions(wl, t0, idx_h: np.ndarray, cnt_h: np.ndarray, latq_h=None):
     """Host recount of the grouped attention's work: queries ordered by the
     first long-range key of their rows, then by the row's MinHash (the
-    smallest mix of its pooled-group ids, top 16 bits), then by index, taken
-    16/G at a time; each group's union is the set of distinct long-range keys
-    of its rows.  Returns (union rows per group, long-range entries per query)."""
+    smallest mix of its pooled-group ids, top 16 bits), then by index -- or,
+    with the latent queries, by (first long-range key of the query's
+    nearest-neighbour root >> 4, root, index) -- and taken 16/G at a time;
+    each group's union is the set of distinct long-range keys of its rows.
+    Returns (union rows per group, long-range entries per query)."""
     n = idx_h.shape[0]
-    assert n < (1 << 20) - 1, "the MinHash order applies below 2^20 queries"
+    assert n < (1 << 20) - 1, "these orders apply below 2^20 queries"
     t = np.arange(t0, t0 + n)
     wstart = np.maximum(0, t - wl.window + 1)
     lr = cnt_h.astype(np.int64) - (np.maximum(0, np.minimum(wl.sinks, wstart)) + (t - wstart + 1))
     first = np.where(lr > 0, idx_h[:, 0].astype(np.int64), (1 << 28) - 1)
-    mh = np.array([int(_grp_mix(idx_h[q, :lr[q]].astype(np.uint64) >> np.uint64(2)).min()) >> 16
-                   if lr[q] > 0 else 0xFFFF for q in range(n)], dtype=np.int64)
-    order = np.lexsort((np.arange(n), mh, first))
+    if latq_h is not None:
+        root = latent_nn_roots(latq_h)
+        order = np.lexsort((np.arange(n), root, first[root] >> 4))
+    else:
+        mh = np.array([int(_grp_mix(idx_h[q, :lr[q]].astype(np.uint64) >> np.uint64(2)).min()) >> 16
+                       if lr[q] > 0 else 0xFFFF for q in range(n)], dtype=np.int64)
+        order = np.lexsort((np.arange(n), mh, first))
     qpw = 16 // (wl.Hq // wl.Hkv)
     unions = []
     for g0 in range(0, n, qpw):
@@ -199,7 +227,10 @@ def bench_prefill(args, dev):
 
     # one step: append the chunk, select, attend (grouped: prepare, then the
     # long-range walk); every call on torch's current stream, where the events
-    # are recorded
+    # are recorded.  The queries are grouped by their latent neighbours on a
+    # Flat index, by their rows on a Tree index (as lsa_prefill_chunk does).
+    glat = latq if wl.tree_group == 0 else None
+
     def step(evs=None):
         ix.restore(snap)
         if evs: evs[0].record()
@@ -207,7 +238,7 @@ def bench_prefill(args, dev):
         if evs: evs[1].record()
         ix.select(latq, qpos, sp, idx=idx, cnt=cnt, ws=sel_ws)
         if evs: evs[2].record()
-        L.sparse_attn_grouped(q, K, V, idx, cnt, t0, sp, ap, ws=grp_ws, part="prepare")
+        L.sparse_attn_grouped(q, K, V, idx, cnt, t0, sp, ap, ws=grp_ws, part="prepare", latq=glat)
         if evs: evs[3].record()
         L.sparse_attn_grouped(q, K, V, idx, cnt, t0, sp, ap, out=out, ws=grp_ws, part="walk")
         if evs: evs[4].record()
@@ -249,7 +280,8 @@ def bench_prefill(args, dev):
                       torch.equal(out2.view(torch.int16), out.view(torch.int16)))
 
     cnt_h = cnt.cpu().numpy()
-    unions, lr = grouped_unions(wl, t0, idx.cpu().numpy(), cnt_h)
+    unions, lr = grouped_unions(wl, t0, idx.cpu().numpy(), cnt_h,
+                                glat.cpu().numpy() if glat is not None else None)
     walk_bytes, prep_bytes = grouped_attn_bytes(wl, t0, n, unions)
     attn_ms = float(ph4[:, 3].mean())                  # the long-range walk: one launch
     per_query = attn_algorithmic_bytes(wl, t0, n, cnt_h)
@@ -501,7 +533,7 @@ def bench_train(args, dev, steps=3, warmup=1):
         ev[1].record()
         ix.select(latq, qpos, sp, idx=idx, cnt=cnt, ws=sel_ws)
         ev[2].record()
-        L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap, out=out, ws=grp_ws, lse=lse)
+        L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap, out=out, ws=grp_ws, lse=lse, latq=latq)
         ev[3].record()
         L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do, dq=dq, dk=dk, dv=dv,
                           ws=bwd_ws)

@@ -70,11 +70,11 @@ EXPORTS = {
                                        ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                        c_vp, c_vp]),
     "lsa_sparse_attn_grouped": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
-                                        ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
-                                        c_vp, c_vp, c_vp, c_sz, c_vp]),
+                                        c_vp, ctypes.POINTER(SelectParams),
+                                        ctypes.POINTER(AttnParams), c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lsa_attn_grouped_prepare": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
-                                         ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
-                                         c_vp, c_sz, c_vp]),
+                                         c_vp, ctypes.POINTER(SelectParams),
+                                         ctypes.POINTER(AttnParams), c_vp, c_sz, c_vp]),
     "lsa_attn_grouped_walk": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
                                       ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                       c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -327,10 +327,13 @@ def sparse_attn_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: t
 def sparse_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                         cnt: torch.Tensor, qpos0: int, sp: SelectParams, ap: AttnParams,
                         out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                        stream=None, part: str = "all", lse: Optional[torch.Tensor] = None):
-    """sparse_attn_window with each group of 16/G queries (ordered by their
-    rows' first key) reading the union of its long-range keys once.  part:
-    "all", or "prepare" then "walk" with the same workspace `ws`.  With `lse`
+                        stream=None, part: str = "all", lse: Optional[torch.Tensor] = None,
+                        latq: Optional[torch.Tensor] = None):
+    """sparse_attn_window with each group of 16/G queries reading the union of
+    its long-range keys once.  The queries are ordered by their latent
+    nearest-neighbour components when `latq` (int8 [nq][64]) is given, else by
+    their rows' first key and MinHash.  part: "all", or "prepare" then "walk"
+    with the same workspace `ws` (the walk takes no latents).  With `lse`
     (float32 [nq][Hq]) the walk also stores the log-sum-exp, as
     sparse_attn_fwd does."""
     nq = q.shape[0]
@@ -346,19 +349,22 @@ def sparse_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: 
         if part != "all":
             raise LsaError(f"sparse_attn_grouped part {part!r} needs a workspace of {wsb} bytes")
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
-    common = (_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt), idx.shape[1], nq, qpos0,
-              ctypes.byref(sp), ctypes.byref(ap))
+    if latq is not None:
+        _need(latq, torch.int8, "latq", (nq, 64))
+    head = (_ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx), _ptr(cnt), idx.shape[1], nq, qpos0)
+    params = (ctypes.byref(sp), ctypes.byref(ap))
+    lat = (_ptr(latq) if latq is not None else None,)
     if lse is not None:
         _need(lse, torch.float32, "lse", (nq, ap.Hq))
     lp = _ptr(lse) if lse is not None else None
     if part == "all":
-        _check(lib().lsa_sparse_attn_grouped(*common, _ptr(out), lp, _ptr(ws), ws.numel(),
+        _check(lib().lsa_sparse_attn_grouped(*head, *lat, *params, _ptr(out), lp, _ptr(ws), ws.numel(),
                                              _stream(stream)), "lsa_sparse_attn_grouped")
     elif part == "prepare":
-        _check(lib().lsa_attn_grouped_prepare(*common, _ptr(ws), ws.numel(), _stream(stream)),
-               "lsa_attn_grouped_prepare")
+        _check(lib().lsa_attn_grouped_prepare(*head, *lat, *params, _ptr(ws), ws.numel(),
+                                              _stream(stream)), "lsa_attn_grouped_prepare")
     elif part == "walk":
-        _check(lib().lsa_attn_grouped_walk(*common, _ptr(out), lp, _ptr(ws), ws.numel(),
+        _check(lib().lsa_attn_grouped_walk(*head, *params, _ptr(out), lp, _ptr(ws), ws.numel(),
                                            _stream(stream)), "lsa_attn_grouped_walk")
     else:
         raise ValueError(f"part {part!r}")

@@ -606,9 +606,9 @@ int lsa_sparse_attn_window(const uint16_t* d_q, const uint16_t* d_k, const uint1
 
 static int grouped_parts(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
                          int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
-                         int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
-                         const lsa_attn_params* ap, void* d_out, float* d_lse, void* d_ws,
-                         size_t ws_bytes, void* stream, int parts) {
+                         int32_t max_sel, int32_t nq, int64_t qpos0, const int8_t* d_latq,
+                         const lsa_select_params* sp, const lsa_attn_params* ap, void* d_out,
+                         float* d_lse, void* d_ws, size_t ws_bytes, void* stream, int parts) {
   if (int e = check_window_attn(kv_rows, max_sel, nq, qpos0, sp, ap)) return e;
   if (!grouped_attn_ok(*ap, sp->budget, kv_rows) || !grouped_nq_ok(nq))
     return fail(LSA_E_UNSUPPORTED, "grouped attention needs D in {64, 128}, Hq/Hkv in {4, 8, 16}, "
@@ -619,7 +619,7 @@ static int grouped_parts(const uint16_t* d_q, const uint16_t* d_k, const uint16_
   const size_t need = attn_grouped_ws_bytes(nq, *ap, sp->budget);
   if (!d_ws || ws_bytes < need) return fail(LSA_E_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
   LSA_HIP(launch_attn_grouped(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp->window,
-                              sp->sinks, sp->budget, *ap, d_out, d_lse, d_ws, parts,
+                              sp->sinks, sp->budget, *ap, d_latq, d_out, d_lse, d_ws, parts,
                               static_cast<hipStream_t>(stream)),
           "grouped attention");
   return LSA_OK;
@@ -627,19 +627,20 @@ static int grouped_parts(const uint16_t* d_q, const uint16_t* d_k, const uint16_
 
 int lsa_sparse_attn_grouped(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
                             int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
-                            int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
-                            const lsa_attn_params* ap, void* d_out, float* d_lse, void* d_ws,
-                            size_t ws_bytes, void* stream) {
-  return grouped_parts(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp, ap, d_out,
-                       d_lse, d_ws, ws_bytes, stream, kGroupedPrepare | kGroupedWalk);
+                            int32_t max_sel, int32_t nq, int64_t qpos0, const int8_t* d_latq,
+                            const lsa_select_params* sp, const lsa_attn_params* ap, void* d_out,
+                            float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+  return grouped_parts(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, d_latq, sp, ap,
+                       d_out, d_lse, d_ws, ws_bytes, stream, kGroupedPrepare | kGroupedWalk);
 }
 
 int lsa_attn_grouped_prepare(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
                              int64_t kv_rows, const int32_t* d_idx, const int32_t* d_cnt,
-                             int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
-                             const lsa_attn_params* ap, void* d_ws, size_t ws_bytes, void* stream) {
-  return grouped_parts(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp, ap, nullptr,
-                       nullptr, d_ws, ws_bytes, stream, kGroupedPrepare);
+                             int32_t max_sel, int32_t nq, int64_t qpos0, const int8_t* d_latq,
+                             const lsa_select_params* sp, const lsa_attn_params* ap, void* d_ws,
+                             size_t ws_bytes, void* stream) {
+  return grouped_parts(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, d_latq, sp, ap,
+                       nullptr, nullptr, d_ws, ws_bytes, stream, kGroupedPrepare);
 }
 
 int lsa_attn_grouped_walk(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
@@ -647,8 +648,8 @@ int lsa_attn_grouped_walk(const uint16_t* d_q, const uint16_t* d_k, const uint16
                           int32_t max_sel, int32_t nq, int64_t qpos0, const lsa_select_params* sp,
                           const lsa_attn_params* ap, void* d_out, float* d_lse, void* d_ws,
                           size_t ws_bytes, void* stream) {
-  return grouped_parts(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, sp, ap, d_out,
-                       d_lse, d_ws, ws_bytes, stream, kGroupedWalk);
+  return grouped_parts(d_q, d_k, d_v, kv_rows, d_idx, d_cnt, max_sel, nq, qpos0, nullptr, sp, ap,
+                       d_out, d_lse, d_ws, ws_bytes, stream, kGroupedWalk);
 }
 
 int lsa_sparse_attn_fwd(const uint16_t* d_q, const uint16_t* d_k, const uint16_t* d_v,
@@ -736,8 +737,11 @@ int lsa_prefill_chunk(lsa_index* hh, const int8_t* d_latk_chunk, int64_t n_chunk
   if (rc != LSA_OK) return rc;
   if (grouped_attn_ok(*ap, sp->budget, kv_rows) && grouped_nq_ok(n_chunk) &&
       ws_bytes - a_idx >= attn_grouped_ws_bytes((int32_t)n_chunk, *ap, sp->budget)) {
+    // Flat: queries grouped by their latent neighbours; Tree: by their rows
+    // (its neighbours' selections follow the super walk more than the latents)
+    const int8_t* glat = h->prm.tree_group > 0 ? nullptr : d_latq;
     LSA_HIP(launch_attn_grouped(d_q, d_k, d_v, kv_rows, idx, cnt, max_sel, (int32_t)n_chunk, t0,
-                                sp->window, sp->sinks, sp->budget, *ap, d_out, nullptr, sel_ws,
+                                sp->window, sp->sinks, sp->budget, *ap, glat, d_out, nullptr, sel_ws,
                                 kGroupedPrepare | kGroupedWalk, s),
             "grouped attention");
     return LSA_OK;

@@ -563,6 +563,127 @@ __global__ void k_grp_perm(const unsigned long long* keys, int32_t* perm, int nq
   if (i < nq) perm[i] = (int32_t)(keys[i] & qmask);
 }
 
+// ---- grouping by latent neighbours ----
+// Queries whose latent vectors lie close together score the index alike and
+// take much the same buckets.  Given the chunk's query latents (int8 [nq][64]),
+// each query's nearest other query by squared distance is found -- the j != i
+// maximising 2 x_i.x_j - |x_j|^2, exact in int32, ties to the lowest j -- and
+// the components of that nearest-neighbour graph become the sort's classes.
+// Distances are symmetric and ties go to the lowest index, so the graph has no
+// cycle longer than two: each component is a tree hanging off one mutual pair,
+// found by pointer jumping (p <- p[p], ceil(log2 nq) + 1 rounds reach the pair
+// from any depth) and named by the pair's lower index.  The sort key is then
+// (first long-range key of that root >> 4, root, q) in 24 + 20 + 20 bits: a
+// component's queries sit together, components with the same best bucket next
+// to each other.
+
+// |x_i|^2 for i < nq, 0 up to the next multiple of 16
+__global__ void k_grp_nrm(const int8_t* lq, int nq, int n16, int32_t* nrm) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n16) return;
+  int acc = 0;
+  if (i < nq) {
+    const int* r = reinterpret_cast<const int*>(lq + (int64_t)i * 64);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc = __builtin_amdgcn_sdot4(r[d], r[d], acc, false);
+  }
+  nrm[i] = acc;
+}
+
+// One wave per (64 queries, candidate range): int8 MFMAs 16x16x64 with the
+// candidates as A (lane l: candidate l % 16, bytes 16 (l / 16) ..) and 16
+// queries as B, so lane l holds the dot products of candidates 4 (l / 16) + v
+// with query l % 16 of each block; candidates are visited in ascending order,
+// so a strict improvement keeps the lowest j of equal scores.  The best of a
+// range goes to part[range][i], packed so that the larger word is the better
+// (score, then lower j); 0 when the range holds no other query.
+constexpr int NN_QW = 64;
+__global__ void __launch_bounds__(256) k_grp_nn(const int8_t* lq, const int32_t* nrm, int nq, int nrange,
+                                                int csz, unsigned long long* part) {
+  const int lane = lane_id();
+  const int hl = lane & 15, grp = lane >> 4;
+  const int nqb = (nq + NN_QW - 1) / NN_QW;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= nqb * nrange) return;
+  const int qb = item % nqb, rg = item / nqb;     // a workgroup's waves share the range
+  const int i0 = qb * NN_QW;
+  v4i bq[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i = i0 + 16 * b + hl;
+    bq[b] = i < nq ? *reinterpret_cast<const v4i*>(lq + (int64_t)i * 64 + 16 * grp) : v4i{0, 0, 0, 0};
+  }
+  int bs[4], bj[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) { bs[b] = INT_MIN; bj[b] = -1; }
+  const int jb = rg * csz, je = min(nq, jb + csz);
+  for (int j0 = jb; j0 < je; j0 += 16) {
+    const int jr = j0 + hl;
+    const v4i ca = jr < nq ? *reinterpret_cast<const v4i*>(lq + (int64_t)jr * 64 + 16 * grp) : v4i{0, 0, 0, 0};
+    const v4i nv = *reinterpret_cast<const v4i*>(nrm + j0 + 4 * grp);   // nrm holds a multiple of 16
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const v4i c = mfma_i8_16x16x64(ca, bq[b], v4i{0, 0, 0, 0});
+      const int i = i0 + 16 * b + hl;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = j0 + 4 * grp + v;
+        const int sc = 2 * c[v] - nv[v];
+        if (j < je && j != i && sc > bs[b]) { bs[b] = sc; bj[b] = j; }
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      const int os = __shfl_xor(bs[b], o), oj = __shfl_xor(bj[b], o);
+      if (oj >= 0 && (bj[b] < 0 || os > bs[b] || (os == bs[b] && oj < bj[b]))) { bs[b] = os; bj[b] = oj; }
+    }
+    const int i = i0 + 16 * b + hl;
+    if (grp == 0 && i < nq)
+      part[(int64_t)rg * nq + i] =
+          bj[b] < 0 ? 0ull
+                    : ((unsigned long long)((unsigned)bs[b] ^ 0x80000000u) << 32) | (0xffffffffu - (unsigned)bj[b]);
+  }
+}
+
+// nearest neighbour over the ranges (itself when there is no other query),
+// and the first pointer of the jumps
+__global__ void k_grp_nn_fin(const unsigned long long* part, int nq, int nrange, int32_t* nn, int32_t* p) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nq) return;
+  unsigned long long best = 0;
+  for (int r = 0; r < nrange; ++r) best = max(best, part[(int64_t)r * nq + i]);
+  const int j = best ? (int)(0xffffffffu - (unsigned)(best & 0xffffffffull)) : i;
+  nn[i] = j;
+  p[i] = j;
+}
+
+__global__ void k_grp_jump(const int32_t* pin, int32_t* pout, int nq) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nq) return;
+  const int x = min(max(pin[i], 0), nq - 1);
+  pout[i] = pin[x];
+}
+
+// sort key (first long-range key of the root >> 4, root, q); padding last
+__global__ void k_grp_key_nn(AttnArgs a, const int32_t* nn, const int32_t* p, unsigned long long* keys,
+                             int n_pad) {
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_pad) return;
+  unsigned long long k = ~0ull;
+  if (q < a.nq) {
+    const int pq = min(max(p[q], 0), a.nq - 1);
+    const int root = min(pq, min(max(nn[pq], 0), a.nq - 1));
+    const int nlr = long_range_count(a, root);
+    const int kmax = (int)(a.kv_rows - 1);
+    const unsigned first = nlr > 0 ? (unsigned)min(max(a.idx[(int64_t)root * a.max_sel], 0), kmax) : (1u << 28) - 1;
+    k = ((unsigned long long)(first >> 4) << 40) | ((unsigned long long)root << kGrpMhBits) | (unsigned)q;
+  }
+  keys[q] = k;
+}
+
 // Union of a group's long-range rows, one workgroup of GU_T threads per
 // group.  An LDS hash set (linear probing) holds word (key << 4 | mask), one
 // mask bit per query slot of the group.  The group's QP queries are taken
@@ -1093,8 +1214,9 @@ int grp_table_n(int qpw, int32_t lcap) {    // hash slots: at least twice the en
 // The plan (query order and unions) first, then the sinks-and-window partials:
 // the backward's dQ uses the plan alone.
 struct GrpLayout {
-  size_t keys_a, keys_b, perm, urow, umask, ucnt, plan_total, part_o, part_ml, total;
-  int n_pad, qpw, ngrp, ucap;
+  size_t keys_a, keys_b, perm, urow, umask, ucnt, plan_total, part_o, part_ml, nrm, nnpart, nn, pa, pb,
+      total;
+  int n_pad, qpw, ngrp, ucap, nrange, csz;
 };
 GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
   GrpLayout L;
@@ -1113,6 +1235,16 @@ GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
   L.plan_total = o;
   L.part_o = o; o += al256((size_t)nq * ap.Hq * ap.D * 4);
   L.part_ml = o; o += al256((size_t)nq * ap.Hq * 2 * 4);
+  // the latent nearest-neighbour search: enough candidate ranges for about
+  // 2048 waves, each range a multiple of 16 candidates
+  const int nqb = (nq + NN_QW - 1) / NN_QW;
+  L.nrange = std::max(1, std::min(64, (2048 + nqb - 1) / nqb));
+  L.csz = ((nq + L.nrange - 1) / L.nrange + 15) / 16 * 16;
+  L.nrm = o; o += al256((size_t)(nq + 15) / 16 * 16 * 4);
+  L.nnpart = o; o += al256((size_t)L.nrange * nq * 8);
+  L.nn = o; o += al256((size_t)nq * 4);
+  L.pa = o; o += al256((size_t)nq * 4);
+  L.pb = o; o += al256((size_t)nq * 4);
   L.total = o;
   return L;
 }
@@ -1120,7 +1252,8 @@ GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
 // The query order and the groups' unions (a.idx, a.cnt, a.max_sel, a.nq,
 // a.qpos0, a.window, a.sinks, a.kv_rows and a.qpw set; a.perm, a.urow,
 // a.umask, a.ucnt and a.ucap are set here).
-hipError_t grouped_plan(AttnArgs& a, const GrpLayout& L, char* w, int32_t lcap, hipStream_t s) {
+hipError_t grouped_plan(AttnArgs& a, const GrpLayout& L, char* w, int32_t lcap, const int8_t* latq,
+                        hipStream_t s) {
   int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
   int32_t* urow = reinterpret_cast<int32_t*>(w + L.urow);
   uint8_t* umask = reinterpret_cast<uint8_t*>(w + L.umask);
@@ -1132,7 +1265,27 @@ hipError_t grouped_plan(AttnArgs& a, const GrpLayout& L, char* w, int32_t lcap, 
   unsigned long long* ka = reinterpret_cast<unsigned long long*>(w + L.keys_a);
   unsigned long long* kb = reinterpret_cast<unsigned long long*>(w + L.keys_b);
   const int use_mh = nq < (1 << kGrpMhBits) - 1 ? 1 : 0;
-  hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 3) / 4), dim3(256), 0, s, a, ka, L.n_pad, use_mh);
+  if (latq && use_mh) {
+    // components of the latent nearest-neighbour graph
+    const int n16 = (nq + 15) / 16 * 16;
+    int32_t* nrm = reinterpret_cast<int32_t*>(w + L.nrm);
+    unsigned long long* part = reinterpret_cast<unsigned long long*>(w + L.nnpart);
+    int32_t* nn = reinterpret_cast<int32_t*>(w + L.nn);
+    int32_t* pa = reinterpret_cast<int32_t*>(w + L.pa);
+    int32_t* pb = reinterpret_cast<int32_t*>(w + L.pb);
+    hipLaunchKernelGGL(k_grp_nrm, dim3((n16 + 255) / 256), dim3(256), 0, s, latq, nq, n16, nrm);
+    const int nqb = (nq + NN_QW - 1) / NN_QW;
+    hipLaunchKernelGGL(k_grp_nn, dim3((nqb * L.nrange + 3) / 4), dim3(256), 0, s, latq, nrm, nq, L.nrange,
+                       L.csz, part);
+    hipLaunchKernelGGL(k_grp_nn_fin, dim3((nq + 255) / 256), dim3(256), 0, s, part, nq, L.nrange, nn, pa);
+    for (int reach = 1; reach < 2 * nq; reach *= 2) {    // 2^rounds >= 2 nq: on the pair from any depth
+      hipLaunchKernelGGL(k_grp_jump, dim3((nq + 255) / 256), dim3(256), 0, s, pa, pb, nq);
+      std::swap(pa, pb);
+    }
+    hipLaunchKernelGGL(k_grp_key_nn, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, a, nn, pa, ka, L.n_pad);
+  } else {
+    hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 3) / 4), dim3(256), 0, s, a, ka, L.n_pad, use_mh);
+  }
   hipLaunchKernelGGL(k_grp_sort_tile, dim3(L.n_pad / GS_TILE), dim3(GS_T), 0, s, ka);
   for (int wd = GS_TILE; wd < L.n_pad; wd <<= 1) {
     hipLaunchKernelGGL(k_grp_merge, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, ka, kb, L.n_pad, wd);
@@ -1199,7 +1352,7 @@ hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t m
   a.kv_rows = kv_rows; a.idx = idx; a.cnt = cnt; a.max_sel = max_sel; a.nq = nq;
   a.Hq = ap.Hq; a.Hkv = ap.Hkv; a.G = ap.Hq / ap.Hkv;
   a.qpos0 = qpos0; a.window = window; a.sinks = sinks; a.qpw = L.qpw;
-  hipError_t e = grouped_plan(a, L, w, lcap, s);
+  hipError_t e = grouped_plan(a, L, w, lcap, nullptr, s);
   if (e != hipSuccess) return e;
   view->perm = reinterpret_cast<const int32_t*>(w + L.perm);
   view->urow = reinterpret_cast<const int32_t*>(w + L.urow);
@@ -1214,8 +1367,9 @@ hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t m
 hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                                int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
-                               int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
-                               float* lse, void* ws, int parts, hipStream_t s) {
+                               int32_t sinks, int32_t lcap, const lsa_attn_params& ap,
+                               const int8_t* latq, void* out, float* lse, void* ws, int parts,
+                               hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   if (!grouped_attn_ok(ap, lcap, kv_rows) || !grouped_nq_ok(nq)) return hipErrorInvalidValue;
   const GrpLayout L = grp_layout(nq, ap, lcap);
@@ -1251,7 +1405,7 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
     if (e != hipSuccess) return e;
 
     // 2. the query order and the groups' unions
-    e = grouped_plan(a, L, w, lcap, s);
+    e = grouped_plan(a, L, w, lcap, latq, s);
     if (e != hipSuccess) return e;
   }
   if (!(parts & kGroupedWalk)) return hipSuccess;

@@ -208,12 +208,16 @@ bool grouped_nq_ok(int64_t nq);
 size_t attn_grouped_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap);
 // parts: kGroupedPrepare (sinks-and-window partials, query order, unions into
 // the workspace) and / or kGroupedWalk (the long-range walk from them).
+// latq (nullable, int8 [nq][64]): order the queries by the components of
+// their latent nearest-neighbour graph; else by (first long-range key,
+// MinHash of the row).
 constexpr int kGroupedPrepare = 1, kGroupedWalk = 2;
 hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                int64_t kv_rows, const int32_t* idx, const int32_t* cnt,
                                int32_t max_sel, int32_t nq, int64_t qpos0, int32_t window,
-                               int32_t sinks, int32_t lcap, const lsa_attn_params& ap, void* out,
-                               float* lse, void* ws, int parts, hipStream_t s);
+                               int32_t sinks, int32_t lcap, const lsa_attn_params& ap,
+                               const int8_t* latq, void* out, float* lse, void* ws, int parts,
+                               hipStream_t s);
 
 // The grouped attention's plan alone: query order (perm: slot -> query) and
 // the unions of each group of qpw consecutive slots (urow / umask, ucap apart;

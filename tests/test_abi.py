@@ -103,12 +103,12 @@ def test_grouped_attention_sizes_without_device():
     n = ctypes.c_size_t(0)
     sp_big = L.SelectParams(8192, 512, 4, 0)          # 4 queries x 8192 rows: over the union cap
     for a, s_ in ((g1, sp), (L.AttnParams(32, 8, 96, 0, 0.0), sp), (ap, sp_big)):
-        rc = lib.lsa_sparse_attn_grouped(fake, fake, fake, 1 << 20, fake, fake, s_.max_sel, 16, 0,
+        rc = lib.lsa_sparse_attn_grouped(fake, fake, fake, 1 << 20, fake, fake, s_.max_sel, 16, 0, fake,
                                          ctypes.byref(s_), ctypes.byref(a), fake, None, fake,
                                          ctypes.c_size_t(1 << 40), None)
         assert rc == 2, (a.Hq, a.Hkv, a.D, s_.budget)
     # a workspace below the size is refused, nothing enqueued
-    rc = lib.lsa_sparse_attn_grouped(fake, fake, fake, 1 << 20, fake, fake, sp.max_sel, 16, 0,
+    rc = lib.lsa_sparse_attn_grouped(fake, fake, fake, 1 << 20, fake, fake, sp.max_sel, 16, 0, fake,
                                      ctypes.byref(sp), ctypes.byref(ap), fake, None, fake,
                                      ctypes.c_size_t(1024), None)
     assert rc == 3

@@ -457,6 +457,107 @@ def test_grouped_attention_on_select_rows(tiny, Hq, Hkv, D):
         assert e <= TOL
 
 
+def _al256(x):
+    return (x + 255) // 256 * 256
+
+
+def _grouped_plan_from_ws(ws, nq, qpw, budget):
+    """The query order (slot -> query) and the union sizes that
+    lsa_attn_grouped_prepare leaves at the start of its workspace: the two
+    sort-key buffers (8 bytes x the sort's padded size, the next power of two
+    from 2048), the order, the union rows and masks (budget x qpw rounded up
+    to 4 per group), then the union counts."""
+    n_pad = 2048
+    while n_pad < nq:
+        n_pad *= 2
+    ngrp = (nq + qpw - 1) // qpw
+    ucap = (qpw * budget + 3) & ~3
+    o_perm = 2 * _al256(n_pad * 8)
+    o_ucnt = o_perm + _al256(nq * 4) + _al256(ngrp * ucap * 4) + _al256(ngrp * ucap)
+    h = ws.cpu().numpy()
+    perm = h[o_perm:o_perm + nq * 4].view(np.int32)
+    ucnt = h[o_ucnt:o_ucnt + ngrp * 4].view(np.int32)
+    return perm, ucnt
+
+
+def _latent_order(latq, first):
+    """Host statement of the latent order: nearest other query by squared
+    distance (the j != i maximising 2 x_i.x_j - |x_j|^2, lowest j on ties;
+    exact in int64), pointer jumping to the mutual pair each chain ends in,
+    the pair's lower index as root; sorted by (first[root] >> 4, root, q)."""
+    x = latq.astype(np.int64)
+    n = x.shape[0]
+    s = 2 * (x @ x.T) - (x * x).sum(1)[None, :]
+    np.fill_diagonal(s, np.iinfo(np.int64).min)
+    nn = s.argmax(1) if n > 1 else np.zeros(1, dtype=np.int64)
+    p = nn.copy()
+    reach = 1
+    while reach < 2 * n:
+        p = p[p]
+        reach *= 2
+    root = np.minimum(p, nn[p])
+    return np.lexsort((np.arange(n), root, first[root] >> 4))
+
+
+@pytest.mark.parametrize("case", ["select", "equal_latents", "one_query"])
+def test_grouped_attention_latent_order(tiny, case):
+    """lsa_sparse_attn_grouped with the query latents: the order the prepare
+    half leaves in the workspace equals the host statement of the latent
+    nearest-neighbour order (index work, bit-exact), each group's union size
+    equals the distinct long-range keys of its queries' rows, and the output
+    matches the window kernel's (the two halves and the one call alike).
+    Cases: the select's rows for 3000 queries; every query with the same
+    latent (all nearest neighbours tie: the lowest index wins); one query."""
+    wl, g, latk, ref, dev = tiny
+    L = _L()
+    Hq, Hkv, D = 8, 2, 64
+    wl = dataclasses.replace(wl, Hq=Hq, Hkv=Hkv, D=D)
+    g = S.Synth(wl)
+    ix = L.LsaIndex(_iparams(wl), dev)
+    ix.build(latk.to(dev))
+    nq = {"select": 3000, "equal_latents": 700, "one_query": 1}[case]
+    qpos0 = 12000
+    pos = torch.arange(qpos0, qpos0 + nq)
+    lq = g.latq_rows(pos)
+    if case == "equal_latents":
+        lq = lq[:1].repeat(nq, 1).contiguous()
+    sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
+    idx, cnt = ix.select(lq.to(dev), pos.to(torch.int32).to(dev), sp)
+    q = g.q_rows(pos).to(dev)
+    K = torch.empty((wl.T, Hkv, D), dtype=torch.bfloat16)
+    V = torch.empty_like(K)
+    g.fill_rows("k", K, 0)
+    g.fill_rows("v", V, 0)
+    K, V = K.to(dev), V.to(dev)
+    ap32 = L.AttnParams(Hq, Hkv, D, 1, 0.0)
+    lqd = lq.to(dev)
+    ws = torch.zeros(L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap32, nq), dtype=torch.uint8,
+                     device=dev)
+    L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, ap32, ws=ws, part="prepare", latq=lqd)
+    torch.cuda.synchronize()
+    qpw = 16 // (Hq // Hkv)
+    perm, ucnt = _grouped_plan_from_ws(ws, nq, qpw, sp.budget)
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy().astype(np.int64)
+    t = np.arange(qpos0, qpos0 + nq)
+    wstart = np.maximum(0, t - wl.window + 1)
+    lr = cnt_h - (np.maximum(0, np.minimum(wl.sinks, wstart)) + (t - wstart + 1))
+    first = np.where(lr > 0, idx_h[:, 0].astype(np.int64), (1 << 28) - 1)
+    order = _latent_order(lq.numpy(), first)
+    assert np.array_equal(perm, order)
+    sizes = [np.unique(np.concatenate([idx_h[j, :lr[j]] for j in order[g0:g0 + qpw]])).size
+             for g0 in range(0, nq, qpw)]
+    assert np.array_equal(ucnt, np.asarray(sizes, dtype=np.int32))
+    halves = L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, ap32, ws=ws, part="walk")
+    whole = L.sparse_attn_grouped(q, K, V, idx, cnt, qpos0, sp, ap32, latq=lqd)
+    win = L.sparse_attn_window(q, K, V, idx, cnt, qpos0, sp, ap32)
+    torch.cuda.synchronize()
+    assert torch.equal(halves, whole)
+    e = normwise(whole.cpu().numpy().astype(np.float64), win.cpu().numpy().astype(np.float64))
+    print(f"{case}: latent-ordered grouped vs window kernel, {nq} queries: {e:.3e}; "
+          f"unions {sum(sizes) / max(1, lr.sum()):.3f} of the long-range entries")
+    assert e <= TOL
+
+
 def test_grouped_attention_identical_rows():
     """Every query of a group holding the same long-range keys (each union
     row masked for all its queries), rows shorter than a tile, and queries
