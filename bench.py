@@ -752,7 +752,8 @@ N_SIMD = 1024                    # 256 CUs x 4 SIMDs
 # (label, kernel-name substring) of the kernels the prefill summary reports
 PREFILL_KERNELS = [("attention", ATTN_KERNEL),
                    ("attention: sinks and window", "k_attn_win<128, false, 1>"),
-                   ("attention: unions", "k_grp_union<"), ("select: scan", "k_scan<"),
+                   ("attention: unions", "k_grp_union<"),
+                   ("attention: latent neighbours", "k_grp_nn("), ("select: scan", "k_scan<"),
                    ("select: resolve", "k_resolve("), ("index: k-means", "k_kmeans("),
                    ("index: pool", "k_pool("), ("calibration copy", "__amd_rocclr_copyBuffer")]
 

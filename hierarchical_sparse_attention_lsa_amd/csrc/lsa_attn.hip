@@ -577,8 +577,8 @@ __global__ void k_grp_perm(const unsigned long long* keys, int32_t* perm, int nq
 // component's queries sit together, components with the same best bucket next
 // to each other.
 
-// |x_i|^2 for i < nq, 0 up to the next multiple of 16
-__global__ void k_grp_nrm(const int8_t* lq, int nq, int n16, int32_t* nrm) {
+// -|x_i|^2 for i < nq, 0 up to the next multiple of 16
+__global__ void k_grp_nrm(const int8_t* lq, int nq, int n16, int32_t* nnrm) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n16) return;
   int acc = 0;
@@ -587,18 +587,22 @@ __global__ void k_grp_nrm(const int8_t* lq, int nq, int n16, int32_t* nrm) {
 #pragma unroll
     for (int d = 0; d < 16; ++d) acc = __builtin_amdgcn_sdot4(r[d], r[d], acc, false);
   }
-  nrm[i] = acc;
+  nnrm[i] = -acc;
 }
 
-// One wave per (64 queries, candidate range): int8 MFMAs 16x16x64 with the
+// One wave per (64 queries, candidate range): int8 MFMAs 16x16x64 with 16
 // candidates as A (lane l: candidate l % 16, bytes 16 (l / 16) ..) and 16
 // queries as B, so lane l holds the dot products of candidates 4 (l / 16) + v
-// with query l % 16 of each block; candidates are visited in ascending order,
-// so a strict improvement keeps the lowest j of equal scores.  The best of a
-// range goes to part[range][i], packed so that the larger word is the better
-// (score, then lower j); 0 when the range holds no other query.
+// with query l % 16 of each block.  A score s = 2 x_i.x_j - |x_j|^2 lies in
+// (-2^22, 2^20), so (s << 9 | 511 - loc) fits an int32, where loc = 4 tile + v
+// numbers the lane's candidates within a chunk of up to 128 tiles: a plain
+// max then keeps the best score and, of equal ones, the lowest candidate.
+// The next tile's loads are issued before the current tile's MFMAs; the
+// range's best goes to part[range][i], packed so that the larger word is
+// better (score, then lower j); 0 when the range holds no other query.
 constexpr int NN_QW = 64;
-__global__ void __launch_bounds__(256) k_grp_nn(const int8_t* lq, const int32_t* nrm, int nq, int nrange,
+constexpr int NN_CHUNK = 128;
+__global__ void __launch_bounds__(256) k_grp_nn(const int8_t* lq, const int32_t* nnrm, int nq, int nrange,
                                                 int csz, unsigned long long* part) {
   const int lane = lane_id();
   const int hl = lane & 15, grp = lane >> 4;
@@ -613,24 +617,50 @@ __global__ void __launch_bounds__(256) k_grp_nn(const int8_t* lq, const int32_t*
     const int i = i0 + 16 * b + hl;
     bq[b] = i < nq ? *reinterpret_cast<const v4i*>(lq + (int64_t)i * 64 + 16 * grp) : v4i{0, 0, 0, 0};
   }
+  auto load_a = [&](int j0) -> v4i {
+    const int jr = j0 + hl;
+    return jr < nq ? *reinterpret_cast<const v4i*>(lq + (int64_t)jr * 64 + 16 * grp) : v4i{0, 0, 0, 0};
+  };
+  auto load_n = [&](int j0) -> v4i {     // nnrm holds a multiple of 16 entries
+    return *reinterpret_cast<const v4i*>(nnrm + j0 + 4 * grp);
+  };
   int bs[4], bj[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) { bs[b] = INT_MIN; bj[b] = -1; }
   const int jb = rg * csz, je = min(nq, jb + csz);
-  for (int j0 = jb; j0 < je; j0 += 16) {
-    const int jr = j0 + hl;
-    const v4i ca = jr < nq ? *reinterpret_cast<const v4i*>(lq + (int64_t)jr * 64 + 16 * grp) : v4i{0, 0, 0, 0};
-    const v4i nv = *reinterpret_cast<const v4i*>(nrm + j0 + 4 * grp);   // nrm holds a multiple of 16
+  for (int c0 = jb; c0 < je; c0 += 16 * NN_CHUNK) {
+    const int ce = min(je, c0 + 16 * NN_CHUNK);
+    int pk[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+    v4i ca = load_a(c0), nv = load_n(c0);
+    for (int j0 = c0; j0 < ce; j0 += 16) {
+      const int jn = j0 + 16 < ce ? j0 + 16 : j0;
+      const v4i ca_n = load_a(jn), nv_n = load_n(jn);
+      const int low0 = 511 - 4 * ((j0 - c0) >> 4);
+      // the tile crosses the range's end or holds one of the wave's queries
+      const bool edge = j0 + 16 > je || (j0 < i0 + NN_QW && j0 + 16 > i0);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const v4i c = mfma_i8_16x16x64(ca, bq[b], v4i{0, 0, 0, 0});
-      const int i = i0 + 16 * b + hl;
+      for (int b = 0; b < 4; ++b) {
+        const v4i c = mfma_i8_16x16x64(ca, bq[b], v4i{0, 0, 0, 0});
+        const int i = i0 + 16 * b + hl;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = j0 + 4 * grp + v;
-        const int sc = 2 * c[v] - nv[v];
-        if (j < je && j != i && sc > bs[b]) { bs[b] = sc; bj[b] = j; }
+        for (int v = 0; v < 4; ++v) {
+          const int sc = 2 * c[v] + nv[v];
+          int pv = (int)(((unsigned)sc << 9) | (unsigned)(low0 - v));
+          if (edge) {
+            const int j = j0 + 4 * grp + v;
+            pv = j < je && j != i ? pv : INT_MIN;
+          }
+          pk[b] = max(pk[b], pv);
+        }
       }
+      ca = ca_n;
+      nv = nv_n;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {          // chunks ascend: a strictly better score wins
+      if (pk[b] == INT_MIN) continue;
+      const int sc = pk[b] >> 9, loc = 511 - (pk[b] & 511);
+      if (bj[b] < 0 || sc > bs[b]) { bs[b] = sc; bj[b] = c0 + (loc >> 2) * 16 + 4 * grp + (loc & 3); }
     }
   }
 #pragma unroll
@@ -660,11 +690,27 @@ __global__ void k_grp_nn_fin(const unsigned long long* part, int nq, int nrange,
   p[i] = j;
 }
 
+// one round of pointer jumping, pout = pin o pin
 __global__ void k_grp_jump(const int32_t* pin, int32_t* pout, int nq) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nq) return;
   const int x = min(max(pin[i], 0), nq - 1);
   pout[i] = pin[x];
+}
+
+// every round in one workgroup, the pointers in LDS (nq <= kJumpLds): a
+// pointer updated in place only ever moves further along its chain, so each
+// round still at least doubles the reach
+constexpr int kJumpLds = 40960;
+__global__ void __launch_bounds__(1024) k_grp_jump_lds(int32_t* p, int nq) {
+  __shared__ int32_t s[kJumpLds];
+  for (int i = threadIdx.x; i < nq; i += 1024) s[i] = min(max(p[i], 0), nq - 1);
+  __syncthreads();
+  for (int reach = 1; reach < 2 * nq; reach *= 2) {
+    for (int i = threadIdx.x; i < nq; i += 1024) s[i] = s[s[i]];
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < nq; i += 1024) p[i] = s[i];
 }
 
 // sort key (first long-range key of the root >> 4, root, q); padding last
@@ -1236,9 +1282,9 @@ GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
   L.part_o = o; o += al256((size_t)nq * ap.Hq * ap.D * 4);
   L.part_ml = o; o += al256((size_t)nq * ap.Hq * 2 * 4);
   // the latent nearest-neighbour search: enough candidate ranges for about
-  // 2048 waves, each range a multiple of 16 candidates
+  // 8192 waves, each range a multiple of 16 candidates
   const int nqb = (nq + NN_QW - 1) / NN_QW;
-  L.nrange = std::max(1, std::min(64, (2048 + nqb - 1) / nqb));
+  L.nrange = std::max(1, std::min(64, (8192 + nqb - 1) / nqb));
   L.csz = ((nq + L.nrange - 1) / L.nrange + 15) / 16 * 16;
   L.nrm = o; o += al256((size_t)(nq + 15) / 16 * 16 * 4);
   L.nnpart = o; o += al256((size_t)L.nrange * nq * 8);
@@ -1278,9 +1324,13 @@ hipError_t grouped_plan(AttnArgs& a, const GrpLayout& L, char* w, int32_t lcap, 
     hipLaunchKernelGGL(k_grp_nn, dim3((nqb * L.nrange + 3) / 4), dim3(256), 0, s, latq, nrm, nq, L.nrange,
                        L.csz, part);
     hipLaunchKernelGGL(k_grp_nn_fin, dim3((nq + 255) / 256), dim3(256), 0, s, part, nq, L.nrange, nn, pa);
-    for (int reach = 1; reach < 2 * nq; reach *= 2) {    // 2^rounds >= 2 nq: on the pair from any depth
-      hipLaunchKernelGGL(k_grp_jump, dim3((nq + 255) / 256), dim3(256), 0, s, pa, pb, nq);
-      std::swap(pa, pb);
+    if (nq <= kJumpLds) {
+      hipLaunchKernelGGL(k_grp_jump_lds, dim3(1), dim3(1024), 0, s, pa, nq);
+    } else {
+      for (int reach = 1; reach < 2 * nq; reach *= 2) {    // 2^rounds >= 2 nq: on the pair from any depth
+        hipLaunchKernelGGL(k_grp_jump, dim3((nq + 255) / 256), dim3(256), 0, s, pa, pb, nq);
+        std::swap(pa, pb);
+      }
     }
     hipLaunchKernelGGL(k_grp_key_nn, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, a, nn, pa, ka, L.n_pad);
   } else {

@@ -485,11 +485,15 @@ def _latent_order(latq, first):
     distance (the j != i maximising 2 x_i.x_j - |x_j|^2, lowest j on ties;
     exact in int64), pointer jumping to the mutual pair each chain ends in,
     the pair's lower index as root; sorted by (first[root] >> 4, root, q)."""
-    x = latq.astype(np.int64)
+    x = torch.from_numpy(latq.astype(np.float32))     # every partial sum an integer below 2^24: exact
     n = x.shape[0]
-    s = 2 * (x @ x.T) - (x * x).sum(1)[None, :]
-    np.fill_diagonal(s, np.iinfo(np.int64).min)
-    nn = s.argmax(1) if n > 1 else np.zeros(1, dtype=np.int64)
+    nrm = (x * x).sum(1)
+    nn = np.zeros(n, dtype=np.int64)
+    for b0 in range(0, n if n > 1 else 0, 4096):
+        sc = 2 * x[b0:b0 + 4096] @ x.T - nrm[None, :]
+        r = torch.arange(sc.shape[0])
+        sc[r, r + b0] = -float("inf")
+        nn[b0:b0 + 4096] = sc.argmax(1).numpy()        # the first of equal maxima
     p = nn.copy()
     reach = 1
     while reach < 2 * n:
@@ -499,7 +503,7 @@ def _latent_order(latq, first):
     return np.lexsort((np.arange(n), root, first[root] >> 4))
 
 
-@pytest.mark.parametrize("case", ["select", "equal_latents", "one_query"])
+@pytest.mark.parametrize("case", ["select", "equal_latents", "one_query", "many"])
 def test_grouped_attention_latent_order(tiny, case):
     """lsa_sparse_attn_grouped with the query latents: the order the prepare
     half leaves in the workspace equals the host statement of the latent
@@ -507,16 +511,22 @@ def test_grouped_attention_latent_order(tiny, case):
     equals the distinct long-range keys of its queries' rows, and the output
     matches the window kernel's (the two halves and the one call alike).
     Cases: the select's rows for 3000 queries; every query with the same
-    latent (all nearest neighbours tie: the lowest index wins); one query."""
+    latent (all nearest neighbours tie: the lowest index wins); one query;
+    45000 queries on a 64k-key index (more than one workgroup's pointer
+    jumping holds: a launch per round)."""
     wl, g, latk, ref, dev = tiny
     L = _L()
     Hq, Hkv, D = 8, 2, 64
     wl = dataclasses.replace(wl, Hq=Hq, Hkv=Hkv, D=D)
+    if case == "many":
+        wl = dataclasses.replace(wl, T=1 << 16)
     g = S.Synth(wl)
+    if case == "many":
+        latk = g.latk(0, wl.T)
     ix = L.LsaIndex(_iparams(wl), dev)
     ix.build(latk.to(dev))
-    nq = {"select": 3000, "equal_latents": 700, "one_query": 1}[case]
-    qpos0 = 12000
+    nq = {"select": 3000, "equal_latents": 700, "one_query": 1, "many": 45000}[case]
+    qpos0 = 12000 if case != "many" else 20000
     pos = torch.arange(qpos0, qpos0 + nq)
     lq = g.latq_rows(pos)
     if case == "equal_latents":
