@@ -110,23 +110,32 @@ def _grp_mix(x: np.ndarray) -> np.ndarray:
     return x
 
 
+NN_BLOCK = 32768          # queries whose nearest neighbours are searched together
+
+
 def latent_nn_roots(latq_h: np.ndarray) -> np.ndarray:
     """Host recount of the grouped attention's latent order: each query's
-    nearest other query (the j != i maximising 2 x_i.x_j - |x_j|^2, lowest j
-    of equal scores; float32 holds these integers exactly), then the lower
-    index of the mutual pair each query's chain of neighbours ends in."""
+    nearest other query of its block of NN_BLOCK (the j != i maximising
+    2 x_i.x_j - |x_j|^2, lowest j of equal scores; float32 holds these
+    integers exactly), then the lower index of the mutual pair each query's
+    chain of neighbours ends in."""
     x = torch.from_numpy(latq_h.astype(np.float32))
     n = x.shape[0]
     nrm = (x * x).sum(1)
-    nn = np.empty(n, dtype=np.int64)
-    for b0 in range(0, n, 2048):
-        s = 2 * x[b0:b0 + 2048] @ x.T - nrm[None, :]
-        r = torch.arange(s.shape[0])
-        s[r, r + b0] = -float("inf")
-        nn[b0:b0 + 2048] = s.argmax(1).numpy() if n > 1 else b0 + r.numpy()
+    nn = np.arange(n, dtype=np.int64)
+    for base in range(0, n, NN_BLOCK):
+        e = min(n, base + NN_BLOCK)
+        if e - base < 2:
+            continue
+        for b0 in range(base, e, 2048):
+            b1 = min(e, b0 + 2048)
+            s = 2 * x[b0:b1] @ x[base:e].T - nrm[None, base:e]
+            r = torch.arange(b1 - b0)
+            s[r, r + b0 - base] = -float("inf")
+            nn[b0:b1] = base + s.argmax(1).numpy()
     p = nn.copy()
     reach = 1
-    while reach < 2 * n:
+    while reach < 2 * min(n, NN_BLOCK):
         p = p[p]
         reach *= 2
     return np.minimum(p, nn[p])
@@ -536,7 +545,7 @@ def bench_train(args, dev, steps=3, warmup=1):
         L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap, out=out, ws=grp_ws, lse=lse, latq=latq)
         ev[3].record()
         L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do, dq=dq, dk=dk, dv=dv,
-                          ws=bwd_ws)
+                          ws=bwd_ws, latq=latq)
         ev[4].record()
 
     for _ in range(warmup):

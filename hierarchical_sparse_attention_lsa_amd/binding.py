@@ -82,7 +82,7 @@ EXPORTS = {
                                     ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                     c_vp, c_vp, c_vp]),
     "lsa_sparse_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i64,
-                                    ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
+                                    c_vp, ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams),
                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lsa_prefill_chunk": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64,
                                   ctypes.POINTER(SelectParams), ctypes.POINTER(AttnParams), c_vp,
@@ -398,9 +398,11 @@ def sparse_attn_bwd(index: "LsaIndex", q: torch.Tensor, k: torch.Tensor, v: torc
                     ap: AttnParams, out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                     dv: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                    stream=None):
+                    stream=None, latq: Optional[torch.Tensor] = None):
     """Gradients (float32) of the sparse attention for queries at positions
-    qpos0.. over rows that `index` selected with `sp`; returns (dq, dk, dv)."""
+    qpos0.. over rows that `index` selected with `sp`; returns (dq, dk, dv).
+    With `latq` (int8 [nq][64]) dQ's grouped walk orders the queries by their
+    latent neighbours, as sparse_attn_grouped does."""
     nq = q.shape[0]
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, torch.bfloat16, name)
@@ -418,8 +420,11 @@ def sparse_attn_bwd(index: "LsaIndex", q: torch.Tensor, k: torch.Tensor, v: torc
     if ws is None:
         ws = torch.empty(max(workspace_bytes(OP_ATTN_BWD, index.params, sp, ap, nq), 256),
                          dtype=torch.uint8, device=dev)
+    if latq is not None:
+        _need(latq, torch.int8, "latq", (nq, 64))
     _check(lib().lsa_sparse_attn_bwd(index.handle, _ptr(q), _ptr(k), _ptr(v), k.shape[0], _ptr(idx),
-                                     _ptr(cnt), idx.shape[1], nq, qpos0, ctypes.byref(sp),
+                                     _ptr(cnt), idx.shape[1], nq, qpos0,
+                                     _ptr(latq) if latq is not None else None, ctypes.byref(sp),
                                      ctypes.byref(ap), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
                                      _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)),
            "lsa_sparse_attn_bwd")

@@ -668,7 +668,8 @@ int lsa_sparse_attn_fwd(const uint16_t* d_q, const uint16_t* d_k, const uint16_t
 int lsa_sparse_attn_bwd(const lsa_index* hh, const uint16_t* d_q, const uint16_t* d_k,
                         const uint16_t* d_v, int64_t kv_rows, const int32_t* d_idx,
                         const int32_t* d_cnt, int32_t max_sel, int32_t nq, int64_t qpos0,
-                        const lsa_select_params* sp, const lsa_attn_params* ap, const void* d_out,
+                        const int8_t* d_latq, const lsa_select_params* sp,
+                        const lsa_attn_params* ap, const void* d_out,
                         const float* d_lse, const uint16_t* d_dout, float* d_dq, float* d_dk,
                         float* d_dv, void* d_ws, size_t ws_bytes, void* stream) {
   const Index* h = as_index(hh);
@@ -688,7 +689,7 @@ int lsa_sparse_attn_bwd(const lsa_index* hh, const uint16_t* d_q, const uint16_t
   BwdInputs in;
   memset(&in, 0, sizeof in);
   in.q = d_q; in.k = d_k; in.v = d_v; in.o = d_out; in.dout = d_dout; in.lse = d_lse;
-  in.kv_rows = kv_rows; in.idx = d_idx; in.cnt = d_cnt; in.max_sel = max_sel; in.nq = nq;
+  in.kv_rows = kv_rows; in.idx = d_idx; in.cnt = d_cnt; in.latq = d_latq; in.max_sel = max_sel; in.nq = nq;
   in.qpos0 = qpos0; in.window = sp->window; in.sinks = sp->sinks; in.budget = sp->budget;
   in.dq = d_dq; in.dk = d_dk; in.dv = d_dv;
   in.bcnt = v.bcnt; in.boff = v.boff; in.bmem = v.bmem;

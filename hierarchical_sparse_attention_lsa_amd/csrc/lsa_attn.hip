@@ -566,9 +566,10 @@ __global__ void k_grp_perm(const unsigned long long* keys, int32_t* perm, int nq
 // ---- grouping by latent neighbours ----
 // Queries whose latent vectors lie close together score the index alike and
 // take much the same buckets.  Given the chunk's query latents (int8 [nq][64]),
-// each query's nearest other query by squared distance is found -- the j != i
-// maximising 2 x_i.x_j - |x_j|^2, exact in int32, ties to the lowest j -- and
-// the components of that nearest-neighbour graph become the sort's classes.
+// each query's nearest other query by squared distance within its block of
+// kNnBlock consecutive queries is found -- the j != i maximising
+// 2 x_i.x_j - |x_j|^2, exact in int32, ties to the lowest j -- and the
+// components of that nearest-neighbour graph become the sort's classes.
 // Distances are symmetric and ties go to the lowest index, so the graph has no
 // cycle longer than two: each component is a tree hanging off one mutual pair,
 // found by pointer jumping (p <- p[p], ceil(log2 nq) + 1 rounds reach the pair
@@ -602,6 +603,7 @@ __global__ void k_grp_nrm(const int8_t* lq, int nq, int n16, int32_t* nnrm) {
 // better (score, then lower j); 0 when the range holds no other query.
 constexpr int NN_QW = 64;
 constexpr int NN_CHUNK = 128;
+constexpr int kNnBlock = 32768;       // a multiple of NN_QW; its pointers fill 128 KiB of LDS
 __global__ void __launch_bounds__(256) k_grp_nn(const int8_t* lq, const int32_t* nnrm, int nq, int nrange,
                                                 int csz, unsigned long long* part) {
   const int lane = lane_id();
@@ -611,6 +613,7 @@ __global__ void __launch_bounds__(256) k_grp_nn(const int8_t* lq, const int32_t*
   if (item >= nqb * nrange) return;
   const int qb = item % nqb, rg = item / nqb;     // a workgroup's waves share the range
   const int i0 = qb * NN_QW;
+  const int base = i0 / kNnBlock * kNnBlock;      // the wave's queries' block
   v4i bq[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -627,7 +630,7 @@ __global__ void __launch_bounds__(256) k_grp_nn(const int8_t* lq, const int32_t*
   int bs[4], bj[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) { bs[b] = INT_MIN; bj[b] = -1; }
-  const int jb = rg * csz, je = min(nq, jb + csz);
+  const int jb = base + rg * csz, je = min(min(nq, base + kNnBlock), jb + csz);
   for (int c0 = jb; c0 < je; c0 += 16 * NN_CHUNK) {
     const int ce = min(je, c0 + 16 * NN_CHUNK);
     int pk[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
@@ -690,27 +693,21 @@ __global__ void k_grp_nn_fin(const unsigned long long* part, int nq, int nrange,
   p[i] = j;
 }
 
-// one round of pointer jumping, pout = pin o pin
-__global__ void k_grp_jump(const int32_t* pin, int32_t* pout, int nq) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nq) return;
-  const int x = min(max(pin[i], 0), nq - 1);
-  pout[i] = pin[x];
-}
-
-// every round in one workgroup, the pointers in LDS (nq <= kJumpLds): a
-// pointer updated in place only ever moves further along its chain, so each
-// round still at least doubles the reach
-constexpr int kJumpLds = 40960;
-__global__ void __launch_bounds__(1024) k_grp_jump_lds(int32_t* p, int nq) {
-  __shared__ int32_t s[kJumpLds];
-  for (int i = threadIdx.x; i < nq; i += 1024) s[i] = min(max(p[i], 0), nq - 1);
+// pointer jumping, one workgroup per block of kNnBlock queries (the graph's
+// edges stay inside a block), the block's pointers in LDS: a pointer updated
+// in place only ever moves further along its chain, so each round still at
+// least doubles the reach, and 2^rounds >= 2 n reaches the pair from any depth
+__global__ void __launch_bounds__(1024) k_grp_jump(int32_t* p, int nq) {
+  __shared__ int32_t s[kNnBlock];
+  const int base = blockIdx.x * kNnBlock;
+  const int n = min(kNnBlock, nq - base);
+  for (int i = threadIdx.x; i < n; i += 1024) s[i] = min(max(p[base + i] - base, 0), n - 1);
   __syncthreads();
-  for (int reach = 1; reach < 2 * nq; reach *= 2) {
-    for (int i = threadIdx.x; i < nq; i += 1024) s[i] = s[s[i]];
+  for (int reach = 1; reach < 2 * n; reach *= 2) {
+    for (int i = threadIdx.x; i < n; i += 1024) s[i] = s[s[i]];
     __syncthreads();
   }
-  for (int i = threadIdx.x; i < nq; i += 1024) p[i] = s[i];
+  for (int i = threadIdx.x; i < n; i += 1024) p[base + i] = base + s[i];
 }
 
 // sort key (first long-range key of the root >> 4, root, q); padding last
@@ -1260,7 +1257,7 @@ int grp_table_n(int qpw, int32_t lcap) {    // hash slots: at least twice the en
 // The plan (query order and unions) first, then the sinks-and-window partials:
 // the backward's dQ uses the plan alone.
 struct GrpLayout {
-  size_t keys_a, keys_b, perm, urow, umask, ucnt, plan_total, part_o, part_ml, nrm, nnpart, nn, pa, pb,
+  size_t keys_a, keys_b, perm, urow, umask, ucnt, nrm, nnpart, nn, pa, plan_total, part_o, part_ml,
       total;
   int n_pad, qpw, ngrp, ucap, nrange, csz;
 };
@@ -1278,19 +1275,19 @@ GrpLayout grp_layout(int32_t nq, const lsa_attn_params& ap, int32_t lcap) {
   L.urow = o; o += al256((size_t)L.ngrp * L.ucap * 4);
   L.umask = o; o += al256((size_t)L.ngrp * L.ucap);
   L.ucnt = o; o += al256((size_t)L.ngrp * 4);
-  L.plan_total = o;
-  L.part_o = o; o += al256((size_t)nq * ap.Hq * ap.D * 4);
-  L.part_ml = o; o += al256((size_t)nq * ap.Hq * 2 * 4);
-  // the latent nearest-neighbour search: enough candidate ranges for about
-  // 8192 waves, each range a multiple of 16 candidates
+  // the latent nearest-neighbour search: enough candidate ranges per block
+  // for about 8192 waves, each range a multiple of 16 candidates
   const int nqb = (nq + NN_QW - 1) / NN_QW;
   L.nrange = std::max(1, std::min(64, (8192 + nqb - 1) / nqb));
-  L.csz = ((nq + L.nrange - 1) / L.nrange + 15) / 16 * 16;
+  const int nbs = std::min(nq, kNnBlock);
+  L.csz = ((nbs + L.nrange - 1) / L.nrange + 15) / 16 * 16;
   L.nrm = o; o += al256((size_t)(nq + 15) / 16 * 16 * 4);
   L.nnpart = o; o += al256((size_t)L.nrange * nq * 8);
   L.nn = o; o += al256((size_t)nq * 4);
   L.pa = o; o += al256((size_t)nq * 4);
-  L.pb = o; o += al256((size_t)nq * 4);
+  L.plan_total = o;
+  L.part_o = o; o += al256((size_t)nq * ap.Hq * ap.D * 4);
+  L.part_ml = o; o += al256((size_t)nq * ap.Hq * 2 * 4);
   L.total = o;
   return L;
 }
@@ -1318,20 +1315,12 @@ hipError_t grouped_plan(AttnArgs& a, const GrpLayout& L, char* w, int32_t lcap, 
     unsigned long long* part = reinterpret_cast<unsigned long long*>(w + L.nnpart);
     int32_t* nn = reinterpret_cast<int32_t*>(w + L.nn);
     int32_t* pa = reinterpret_cast<int32_t*>(w + L.pa);
-    int32_t* pb = reinterpret_cast<int32_t*>(w + L.pb);
     hipLaunchKernelGGL(k_grp_nrm, dim3((n16 + 255) / 256), dim3(256), 0, s, latq, nq, n16, nrm);
     const int nqb = (nq + NN_QW - 1) / NN_QW;
     hipLaunchKernelGGL(k_grp_nn, dim3((nqb * L.nrange + 3) / 4), dim3(256), 0, s, latq, nrm, nq, L.nrange,
                        L.csz, part);
     hipLaunchKernelGGL(k_grp_nn_fin, dim3((nq + 255) / 256), dim3(256), 0, s, part, nq, L.nrange, nn, pa);
-    if (nq <= kJumpLds) {
-      hipLaunchKernelGGL(k_grp_jump_lds, dim3(1), dim3(1024), 0, s, pa, nq);
-    } else {
-      for (int reach = 1; reach < 2 * nq; reach *= 2) {    // 2^rounds >= 2 nq: on the pair from any depth
-        hipLaunchKernelGGL(k_grp_jump, dim3((nq + 255) / 256), dim3(256), 0, s, pa, pb, nq);
-        std::swap(pa, pb);
-      }
-    }
+    hipLaunchKernelGGL(k_grp_jump, dim3((nq + kNnBlock - 1) / kNnBlock), dim3(1024), 0, s, pa, nq);
     hipLaunchKernelGGL(k_grp_key_nn, dim3((L.n_pad + 255) / 256), dim3(256), 0, s, a, nn, pa, ka, L.n_pad);
   } else {
     hipLaunchKernelGGL(k_grp_key, dim3((L.n_pad + 3) / 4), dim3(256), 0, s, a, ka, L.n_pad, use_mh);
@@ -1391,8 +1380,8 @@ size_t grouped_plan_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap
 
 hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t max_sel, int32_t nq,
                                int64_t qpos0, int32_t window, int32_t sinks, int64_t kv_rows,
-                               int32_t lcap, const lsa_attn_params& ap, void* ws, GroupPlanView* view,
-                               hipStream_t s) {
+                               int32_t lcap, const lsa_attn_params& ap, const int8_t* latq, void* ws,
+                               GroupPlanView* view, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   if (!grouped_attn_ok(ap, lcap, kv_rows) || !grouped_nq_ok(nq)) return hipErrorInvalidValue;
   const GrpLayout L = grp_layout(nq, ap, lcap);
@@ -1402,7 +1391,7 @@ hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t m
   a.kv_rows = kv_rows; a.idx = idx; a.cnt = cnt; a.max_sel = max_sel; a.nq = nq;
   a.Hq = ap.Hq; a.Hkv = ap.Hkv; a.G = ap.Hq / ap.Hkv;
   a.qpos0 = qpos0; a.window = window; a.sinks = sinks; a.qpw = L.qpw;
-  hipError_t e = grouped_plan(a, L, w, lcap, nullptr, s);
+  hipError_t e = grouped_plan(a, L, w, lcap, latq, s);
   if (e != hipSuccess) return e;
   view->perm = reinterpret_cast<const int32_t*>(w + L.perm);
   view->urow = reinterpret_cast<const int32_t*>(w + L.urow);

@@ -882,7 +882,8 @@ hipError_t launch_attn_bwd(const BwdInputs& in, const lsa_attn_params& ap, hipSt
     if (plan_bytes > 0 && grouped_attn_ok(ap, in.budget, in.kv_rows)) {
       GroupPlanView pv;
       if (hipError_t e = launch_grouped_plan(in.idx, in.cnt, in.max_sel, in.nq, in.qpos0, in.window,
-                                             in.sinks, in.kv_rows, in.budget, ap, ws + L.list, &pv, s))
+                                             in.sinks, in.kv_rows, in.budget, ap, in.latq, ws + L.list,
+                                             &pv, s))
         return e;
       a.perm = pv.perm; a.urow = pv.urow; a.umask = pv.umask; a.ucnt = pv.ucnt;
       a.ucap = pv.ucap; a.gqpw = pv.qpw;

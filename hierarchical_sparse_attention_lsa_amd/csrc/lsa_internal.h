@@ -233,8 +233,8 @@ struct GroupPlanView {
 size_t grouped_plan_ws_bytes(int32_t nq, const lsa_attn_params& ap, int32_t lcap);
 hipError_t launch_grouped_plan(const int32_t* idx, const int32_t* cnt, int32_t max_sel, int32_t nq,
                                int64_t qpos0, int32_t window, int32_t sinks, int64_t kv_rows,
-                               int32_t lcap, const lsa_attn_params& ap, void* ws, GroupPlanView* view,
-                               hipStream_t s);
+                               int32_t lcap, const lsa_attn_params& ap, const int8_t* latq, void* ws,
+                               GroupPlanView* view, hipStream_t s);
 
 // Backward of the sparse attention (dQ, dK, dV) over rows the select wrote
 // for consecutive query positions qpos0.., with the index they came from.
@@ -248,6 +248,7 @@ struct BwdInputs {
   int64_t kv_rows;
   const int32_t* idx;
   const int32_t* cnt;
+  const int8_t* latq;       // nullable [nq][64]: the grouped dQ's order by latent neighbours
   int32_t max_sel, nq;
   int64_t qpos0;
   int32_t window, sinks, budget;

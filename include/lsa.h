@@ -307,11 +307,15 @@ LSA_API int lsa_sparse_attn_fwd(const uint16_t* d_q, const uint16_t* d_k, const 
  * 64.  Writes float32 d_dq [nq][Hq][D] and d_dk, d_dv [kv_rows][Hkv][D]
  * (every row; zero for keys no query selected).  Workspace:
  * lsa_workspace_bytes(LSA_OP_ATTN_BWD, .., nq).  Deterministic: every
- * gradient is summed in a fixed order. */
+ * gradient is summed in a fixed order.  d_latq (nullable, int8 [nq][64]):
+ * dQ's long-range part walks groups of queries ordered as
+ * lsa_sparse_attn_grouped orders them with these latents (else by their
+ * rows). */
 LSA_API int lsa_sparse_attn_bwd(const lsa_index* h, const uint16_t* d_q, const uint16_t* d_k,
                                 const uint16_t* d_v, int64_t kv_rows, const int32_t* d_idx,
                                 const int32_t* d_cnt, int32_t max_sel, int32_t nq, int64_t qpos0,
-                                const lsa_select_params* sp, const lsa_attn_params* ap,
+                                const int8_t* d_latq, const lsa_select_params* sp,
+                                const lsa_attn_params* ap,
                                 const void* d_out, const float* d_lse, const uint16_t* d_dout,
                                 float* d_dq, float* d_dk, float* d_dv, void* d_ws,
                                 size_t ws_bytes, void* stream);

@@ -127,7 +127,7 @@ def test_training_and_tree_argument_validation_without_device():
     assert b"tree2_top" in lib.lsa_last_error()
     ap = L.AttnParams(8, 2, 128, 0, 0.0)
     args = lambda spp, nq, qpos0, kv: (desc, fake, fake, fake, kv, fake, fake, spp.max_sel, nq,
-                                       qpos0, ctypes.byref(spp), ctypes.byref(ap), fake, fake,
+                                       qpos0, None, ctypes.byref(spp), ctypes.byref(ap), fake, fake,
                                        fake, fake, fake, fake, fake, 1 << 30, None)
     sp1 = L.SelectParams(100, 32, 65, 0)
     assert lib.lsa_sparse_attn_bwd(*args(sp1, 4, 0, 1000)) == 2          # sinks > 64

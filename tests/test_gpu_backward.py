@@ -106,7 +106,7 @@ def test_backward_matches_oracle(name, wl, early):
         out, lse = L.sparse_attn_fwd(*args, r["idx"], r["cnt"], 0, r["sp"], ap)
         assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-4
         dq, dk, dv = L.sparse_attn_bwd(r["ix"], *args, r["idx"], r["cnt"], 0, r["sp"], ap, out, lse,
-                                       do)
+                                       do, latq=lat)
         torch.cuda.synchronize()
         dQ, dK, dV = grads[out_f32]
         errs = [normwise(x.cpu().numpy().astype(np.float64), y)
@@ -127,7 +127,8 @@ GROUPED_CASES = [c for c in CASES if (c[1].Hq // c[1].Hkv) in (4, 8, 16)]
 @pytest.mark.parametrize("name,wl,early", GROUPED_CASES, ids=[c[0] for c in GROUPED_CASES])
 def test_grouped_forward_for_training(name, wl, early):
     """The grouped attention as the training forward: its log-sum-exp and
-    output against the oracle's, and the backward taken from them."""
+    output against the oracle's, and the backward taken from them.  The bf16
+    pass orders the groups (forward and dQ) by the query latents."""
     dev = _dev()
     L = _L()
     r = _setup(wl, dev, early)
@@ -137,7 +138,8 @@ def test_grouped_forward_for_training(name, wl, early):
     for out_f32 in (1, 0):
         ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, out_f32, 0.0)
         lse = torch.empty((len(r["pos"]), wl.Hq), dtype=torch.float32, device=dev)
-        out = L.sparse_attn_grouped(*args, r["idx"], r["cnt"], 0, r["sp"], ap, lse=lse)
+        lat = r["lq"].to(dev) if not out_f32 else None
+        out = L.sparse_attn_grouped(*args, r["idx"], r["cnt"], 0, r["sp"], ap, lse=lse, latq=lat)
         out_w, lse_w = L.sparse_attn_fwd(*args, r["idx"], r["cnt"], 0, r["sp"], ap)
         torch.cuda.synchronize()
         assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-4

@@ -443,7 +443,8 @@ def test_train_128k_backward(oracle_pool):
     pos = torch.arange(T, device=dev)
     sp = L.SelectParams(wl.budget, wl.window, wl.sinks, 0)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
-    idx, cnt = ix.select(g.latq_rows(pos, device=dev), pos.to(torch.int32), sp)
+    latq = g.latq_rows(pos, device=dev)
+    idx, cnt = ix.select(latq, pos.to(torch.int32), sp)
     # properties over all keys, with a float32 forward output (exact row sums):
     # the softmax gradients sum to zero over the keys; the value gradients sum
     # to the upstream gradients of each KV head's query heads
@@ -457,10 +458,11 @@ def test_train_128k_backward(oracle_pool):
     want = do.double().view(T, wl.Hkv, G, wl.D).sum((0, 2))
     assert float((dv32.double().sum(0) - want).abs().max()) <= 1e-4 * float(want.abs().max())
     del out32, lse32, dk32, dv32
-    # the benchmarked configuration: grouped forward, bf16 output
+    # the benchmarked configuration: grouped forward, bf16 output, groups by
+    # the query latents
     lse = torch.empty((T, wl.Hq), dtype=torch.float32, device=dev)
-    out = L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap, lse=lse)
-    dq, dk, dv = L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do)
+    out = L.sparse_attn_grouped(q, K, V, idx, cnt, 0, sp, ap, lse=lse, latq=latq)
+    dq, dk, dv = L.sparse_attn_bwd(ix, q, K, V, idx, cnt, 0, sp, ap, out, lse, do, latq=latq)
     torch.cuda.synchronize()
     # oracle over its own selections
     cache, latk_h = build_cache_parallel(wl.name, T, oracle_pool)

@@ -480,20 +480,26 @@ def _grouped_plan_from_ws(ws, nq, qpw, budget):
     return perm, ucnt
 
 
-def _latent_order(latq, first):
-    """Host statement of the latent order: nearest other query by squared
-    distance (the j != i maximising 2 x_i.x_j - |x_j|^2, lowest j on ties;
-    exact in int64), pointer jumping to the mutual pair each chain ends in,
+def _latent_order(latq, first, block=32768):
+    """Host statement of the latent order: within each block of `block`
+    consecutive queries, each query's nearest other query by squared distance
+    (the j != i maximising 2 x_i.x_j - |x_j|^2, lowest j on ties; a lone
+    query is its own), pointer jumping to the mutual pair each chain ends in,
     the pair's lower index as root; sorted by (first[root] >> 4, root, q)."""
     x = torch.from_numpy(latq.astype(np.float32))     # every partial sum an integer below 2^24: exact
     n = x.shape[0]
     nrm = (x * x).sum(1)
-    nn = np.zeros(n, dtype=np.int64)
-    for b0 in range(0, n if n > 1 else 0, 4096):
-        sc = 2 * x[b0:b0 + 4096] @ x.T - nrm[None, :]
-        r = torch.arange(sc.shape[0])
-        sc[r, r + b0] = -float("inf")
-        nn[b0:b0 + 4096] = sc.argmax(1).numpy()        # the first of equal maxima
+    nn = np.arange(n, dtype=np.int64)
+    for base in range(0, n, block):
+        e = min(n, base + block)
+        if e - base < 2:
+            continue
+        for b0 in range(base, e, 4096):
+            b1 = min(e, b0 + 4096)
+            sc = 2 * x[b0:b1] @ x[base:e].T - nrm[None, base:e]
+            r = torch.arange(b1 - b0)
+            sc[r, r + b0 - base] = -float("inf")
+            nn[b0:b1] = base + sc.argmax(1).numpy()    # the first of equal maxima
     p = nn.copy()
     reach = 1
     while reach < 2 * n:
@@ -512,8 +518,8 @@ def test_grouped_attention_latent_order(tiny, case):
     matches the window kernel's (the two halves and the one call alike).
     Cases: the select's rows for 3000 queries; every query with the same
     latent (all nearest neighbours tie: the lowest index wins); one query;
-    45000 queries on a 64k-key index (more than one workgroup's pointer
-    jumping holds: a launch per round)."""
+    45000 queries on a 64k-key index (two blocks of the neighbour search:
+    32768 queries, then 12232)."""
     wl, g, latk, ref, dev = tiny
     L = _L()
     Hq, Hkv, D = 8, 2, 64
