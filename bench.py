@@ -931,9 +931,11 @@ def summarize_train(args):
     lines = [f"# rocprofv3 kernel statistics: LSA training step of one layer, T={wl.T}, every "
              f"position a query (Hq={wl.Hq}, Hkv={wl.Hkv}, D={wl.D}, select "
              f"{wl.budget}+{wl.window}+{wl.sinks})", "", f"Command: `{command}`", "",
-             "Each step: index build, select, forward with log-sum-exp (k_attn_win), backward "
-             "(k_bwd_dq, then k_bwd_dkv band / long range / sinks and the list kernels); "
-             "4 steps (1 warmup + 3 timed).", "",
+             "Each step: index build, select, grouped forward with log-sum-exp (sinks and "
+             "window k_attn_win<.., 1>, the plan: latent neighbours k_grp_nn, sort, unions "
+             "k_grp_union; the walk k_attn_grp), backward (the plan again, dQ window pass "
+             "k_bwd_dq<.., 1> and union walk k_bwd_dq_grp, then k_bwd_dkv band / long range / "
+             "sinks and the list kernels); 4 steps (1 warmup + 3 timed).", "",
              "| kernel | calls | average ms | total ms |", "|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         if "lsa" not in r["Name"]:
