@@ -106,7 +106,7 @@ def test_backward_matches_oracle(name, wl, early):
         out, lse = L.sparse_attn_fwd(*args, r["idx"], r["cnt"], 0, r["sp"], ap)
         assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-4
         dq, dk, dv = L.sparse_attn_bwd(r["ix"], *args, r["idx"], r["cnt"], 0, r["sp"], ap, out, lse,
-                                       do, latq=lat)
+                                       do)
         torch.cuda.synchronize()
         dQ, dK, dV = grads[out_f32]
         errs = [normwise(x.cpu().numpy().astype(np.float64), y)
@@ -147,7 +147,7 @@ def test_grouped_forward_for_training(name, wl, early):
             assert normwise(out.cpu().numpy().astype(np.float64),
                             out_w.cpu().numpy().astype(np.float64)) <= TOL
         dq, dk, dv = L.sparse_attn_bwd(r["ix"], *args, r["idx"], r["cnt"], 0, r["sp"], ap, out, lse,
-                                       do)
+                                       do, latq=lat)
         torch.cuda.synchronize()
         dQ, dK, dV = grads[out_f32]
         errs = [normwise(x.cpu().numpy().astype(np.float64), y)
