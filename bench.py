@@ -236,9 +236,9 @@ def bench_prefill(args, dev):
 
     # one step: append the chunk, select, attend (grouped: prepare, then the
     # long-range walk); every call on torch's current stream, where the events
-    # are recorded.  The queries are grouped by their latent neighbours on a
-    # Flat index, by their rows on a Tree index (as lsa_prefill_chunk does).
-    glat = latq if wl.tree_group == 0 else None
+    # are recorded.  The queries are grouped by their latent neighbours, or by
+    # their rows on a three-level Tree index (as lsa_prefill_chunk does).
+    glat = latq if wl.tree2_group == 0 else None
 
     def step(evs=None):
         ix.restore(snap)
@@ -343,6 +343,7 @@ def bench_tree_same_data(res, dev, steps, warmup, name="tree_10m"):
     gws = torch.empty(L.workspace_bytes(L.binding.OP_ATTN_GROUPED, None, sp, ap, n), dtype=torch.uint8,
                       device=dev)
     lk_chunk = res["latk"][t0:]
+    glat = res["latq"] if wl.tree2_group == 0 else None     # as lsa_prefill_chunk orders them
 
     def step(e=None):
         ix.restore(snap)
@@ -351,7 +352,8 @@ def bench_tree_same_data(res, dev, steps, warmup, name="tree_10m"):
         if e: e[1].record()
         ix.select(res["latq"], qpos, sp, idx=idx, cnt=cnt, ws=ws)
         if e: e[2].record()
-        L.sparse_attn_grouped(res["q"], res["K"], res["V"], idx, cnt, t0, sp, ap, out=out, ws=gws)
+        L.sparse_attn_grouped(res["q"], res["K"], res["V"], idx, cnt, t0, sp, ap, out=out, ws=gws,
+                              latq=glat)
         if e: e[3].record()
 
     for _ in range(warmup):
@@ -366,7 +368,8 @@ def bench_tree_same_data(res, dev, steps, warmup, name="tree_10m"):
     ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
                    for e in evs]).mean(0)
     cnt_h = cnt.cpu().numpy()
-    unions, _ = grouped_unions(wl, t0, idx.cpu().numpy(), cnt_h)
+    unions, _ = grouped_unions(wl, t0, idx.cpu().numpy(), cnt_h,
+                               glat.cpu().numpy() if glat is not None else None)
     walk_b, prep_b = grouped_attn_bytes(wl, t0, n, unions)
     del idx, out, ws, gws
     return {"workload": name, "index": f"Flat leaves + Tree G={wl.tree_group} S={wl.tree_super} "

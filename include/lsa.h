@@ -328,7 +328,8 @@ LSA_API int lsa_sparse_attn_bwd(const lsa_index* h, const uint16_t* d_q, const u
  * runs as lsa_sparse_attn_grouped when the shape allows it and the
  * workspace holds lsa_workspace_bytes(LSA_OP_PREFILL, .., ap, n_chunk) (the
  * attention params make that size cover the grouped attention; it passes
- * d_latq on a Flat index and NULL on a Tree index), else as
+ * d_latq on a Flat or two-level Tree index and NULL on a three-level Tree
+ * index, whose queries it then groups by their rows), else as
  * lsa_sparse_attn_window. */
 LSA_API int lsa_prefill_chunk(lsa_index* h, const int8_t* d_latk_chunk, int64_t n_chunk,
                               const int8_t* d_latq, const uint16_t* d_q, const uint16_t* d_k,
