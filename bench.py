@@ -763,7 +763,7 @@ PMC_PASSES = {
 N_SIMD = 1024                    # 256 CUs x 4 SIMDs
 # (label, kernel-name substring) of the kernels the prefill summary reports
 PREFILL_KERNELS = [("attention", ATTN_KERNEL),
-                   ("attention: sinks and window", "k_attn_win<128, false, 1>"),
+                   ("attention: sinks and window", "k_attn_swin<128>"),
                    ("attention: unions", "k_grp_union<"),
                    ("attention: latent neighbours", "k_grp_nn("), ("select: scan", "k_scan<"),
                    ("select: resolve", "k_resolve("), ("index: k-means", "k_kmeans("),
@@ -935,7 +935,7 @@ def summarize_train(args):
              f"position a query (Hq={wl.Hq}, Hkv={wl.Hkv}, D={wl.D}, select "
              f"{wl.budget}+{wl.window}+{wl.sinks})", "", f"Command: `{command}`", "",
              "Each step: index build, select, grouped forward with log-sum-exp (sinks and "
-             "window k_attn_win<.., 1>, the plan: latent neighbours k_grp_nn, sort, unions "
+             "window k_attn_swin, the plan: latent neighbours k_grp_nn, sort, unions "
              "k_grp_union; the walk k_attn_grp), backward (the plan again, dQ window pass "
              "k_bwd_dq<.., 1> and union walk k_bwd_dq_grp, then k_bwd_dkv band / long range / "
              "sinks and the list kernels); 4 steps (1 warmup + 3 timed).", "",

@@ -317,10 +317,7 @@ __global__ void __launch_bounds__(AT) k_attn(AttnArgs a) {
 // group's sinks and windows once, as contiguous K/V rows, each column masked
 // to its own query's sinks and window.  Per query the result is the same
 // attention over the same key set; only the summation order differs.
-// WIN = 1: only the sinks and the window (phase 2), the unnormalised result
-// and (max, sum) per (query, head) to part_o / part_ml for the grouped
-// long-range kernel.
-template <int D, bool OUT_F32, int WIN = 0>
+template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   constexpr int NKK = D / 32;
   constexpr int NB = D / 16;
@@ -381,7 +378,7 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   auto nsink_of = [&](int ws) { return max(0, min(a.sinks, ws)); };
 
   // 1. long-range keys of each query: the row's entries before its sinks and window
-  for (int j = 0; j < (WIN ? 0 : nqw); ++j) {
+  for (int j = 0; j < nqw; ++j) {
     const int q = q0 + j;
     const int t = tq0 + j;
     const int ws = wstart_of(t);
@@ -436,13 +433,6 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
     const float mh = __shfl(m_run, col);
     const int j = col / G, h = col % G;
     if (j >= nqw) continue;
-    if (WIN) {                         // partial result of the sinks and window
-      const int64_t pr = (int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) a.part_o[pr * D + 16 * nb + hl] = o[nb][v];
-      if (hl == 0) { a.part_ml[2 * pr] = mh; a.part_ml[2 * pr + 1] = lh; }
-      continue;
-    }
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     const int64_t ob = ((int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h) * D;
     // log-sum-exp: m_run and l_run are in the log2 domain of the scaled logits
@@ -457,6 +447,199 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
   }
 }
 
+// Sinks-and-window partials for the grouped attention, the K/V tiles shared
+// by a workgroup.  Consecutive queries' windows are nearly the same rows, so
+// a workgroup takes SW * qpw consecutive queries of one KV head: each 16-row
+// tile of the union of their sinks and windows is loaded once into LDS (K and
+// V, double-buffered, one 16-byte load per thread) and each wave multiplies it
+// against its own qpw queries' columns, each column masked to its query's
+// sinks and window (a tile with none of a wave's keys is skipped by that
+// wave).  Per query the key set is the rule's; the unnormalised output and
+// (max, sum) per (query, head) go to part_o / part_ml, where the grouped
+// long-range kernel starts from them.  Each wave reads every tile from LDS instead of from L2, which
+// bounded a per-wave walk of the same windows.
+constexpr int SW = 8;                  // waves (query groups) per workgroup
+
+template <int D>
+__global__ void __launch_bounds__(SW * 64) k_attn_swin(AttnArgs a) {
+  constexpr int NKK = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int VROW = D * 2 + 16;
+  constexpr int VCH = D / 8;           // 16-byte chunks of one head's row
+  constexpr int NCH = KT * VCH;        // chunks of a tile's K (or V) rows: 256 or 128
+  static_assert(NCH <= SW * 32, "K loads by the first half of the threads, V by the second");
+  __shared__ __attribute__((aligned(16))) char klds[2][KT * VROW];
+  __shared__ __attribute__((aligned(16))) char vlds[2][KT * VROW];
+  __shared__ __attribute__((aligned(16))) char qlds[SW][16 * qrow_bytes(D)];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int QPW = a.qpw;
+  const int span = SW * QPW;
+  const int nspan = (a.nq + span - 1) / span;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);     // (query span, KV head)
+  if (item >= nspan * a.Hkv) return;                     // the whole workgroup
+  const int g = item % a.Hkv;
+  const int qs0 = (item / a.Hkv) * span;                 // the workgroup's first query
+  const int nqs = min(span, a.nq - qs0);
+  const int q0 = qs0 + wave * QPW;                       // this wave's first query
+  const int nqw = max(0, min(QPW, a.nq - q0));
+  const int G = a.G;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int jc = hl / G, hc = hl % G;
+  const bool cval = jc < nqw;
+  const int64_t rowstride = (int64_t)a.Hkv * D;
+  const int64_t rmax = a.kv_rows - 1;
+
+  // query operand: column hl = (query q0 + jc, head g*G + hc), in this wave's LDS rows
+  char* ql = qlds[wave];
+  {
+    const int qq = min(q0 + (cval ? jc : 0), a.nq - 1);
+    const uint16_t* qp = a.q + ((int64_t)qq * a.Hq + (int64_t)g * G + hc) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      v4i raw = cval ? *reinterpret_cast<const v4i*>(qp + 32 * kk + 8 * grp) : v4i{0, 0, 0, 0};
+      *reinterpret_cast<v4i*>(ql + hl * qrow_bytes(D) + (32 * kk + 8 * grp) * 2) = raw;
+    }
+  }
+  const QLds<D> qb{ql + hl * qrow_bytes(D) + 16 * grp};
+
+  // the union of the workgroup's sinks and windows: positions [0, nsl), then
+  // [w0, tl] (sink counts grow with the position, so the last query's hold
+  // every query's; w0 >= nsl keeps the two parts apart)
+  auto wstart_of = [&](int t) { return max(0, t - a.window + 1); };
+  auto nsink_of = [&](int ws) { return max(0, min(a.sinks, ws)); };
+  const int tq0 = (int)a.qpos0 + qs0;
+  const int tl = tq0 + nqs - 1;
+  const int nsl = nsink_of(wstart_of(tl));
+  const int w0 = max(wstart_of(tq0), nsl);
+  const int nu = nsl + (tl - w0 + 1);
+  const int shift = w0 - nsl;          // position of union slot u >= nsl is u + shift
+  // this lane's column: its query's sinks [0, cns) and window [cws, ct]
+  const int ct = (int)a.qpos0 + q0 + jc;
+  const int cws = wstart_of(ct);
+  const int cns = nsink_of(cws);
+
+  // tile loads: threads [0, NCH) take K chunks, [SW * 32, SW * 32 + NCH) V chunks
+  const bool ldk = tid < NCH;
+  const bool ldv = tid >= SW * 32 && tid < SW * 32 + NCH;
+  const bool ld = ldk || ldv;
+  const int ci = ldk ? tid : tid - SW * 32;
+  const int ckey = ci / VCH, cch = ci % VCH;
+  const uint16_t* src = (ldk ? a.k : a.v) + (int64_t)g * D + cch * 8;
+  auto gload = [&](int kb) -> v4i {
+    const int u = min(kb + ckey, nu - 1);
+    const int pos = u < nsl ? u : u + shift;
+    return *reinterpret_cast<const v4i*>(src + min((int64_t)pos, rmax) * rowstride);
+  };
+  auto swrite = [&](int buf, v4i x) {
+    *reinterpret_cast<v4i*>((ldk ? klds[buf] : vlds[buf]) + ckey * VROW + cch * 16) = x;
+  };
+
+  v4f o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+
+  // Tile i is computed from LDS buffer i & 1 while tiles i + 1 .. i + NST wait
+  // in registers: st[i % NST] holds tile i + 1 at step i and is refilled with
+  // tile i + 1 + NST once it has gone to LDS.
+  constexpr int NST = 4;
+  const int ntile = (nu + KT - 1) / KT;
+  v4i st[NST];
+  if (ld && ntile > 0) swrite(0, gload(0));
+#pragma unroll
+  for (int k = 0; k < NST; ++k) st[k] = ld && k + 1 < ntile ? gload((k + 1) * KT) : v4i{0, 0, 0, 0};
+  __syncthreads();
+  for (int i0 = 0; i0 < ntile; i0 += NST) {
+#pragma unroll
+  for (int k = 0; k < NST; ++k) {
+    const int i = i0 + k;
+    if (i >= ntile) break;
+    const int buf = i & 1;
+    const int kb = i * KT;
+    unsigned vmask = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int uv = kb + 4 * grp + v;
+      const int pv = uv < nsl ? uv : uv + shift;
+      const bool in = cval && uv < nu && (pv < cns || (pv >= cws && pv <= ct));
+      vmask |= (in ? 1u : 0u) << v;
+    }
+    if (__builtin_amdgcn_ballot_w64(vmask != 0) != 0) {   // wave-uniform
+      // S^T[key][column]: lane l holds K row l % 16, elements 32 kk + 8 (l / 16) ..
+      const char* kr = klds[buf] + hl * VROW + 16 * grp;
+      v4f sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        sc = mfma_bf16_16x16x32(*reinterpret_cast<const v8bf*>(kr + 64 * kk), qb(kk), sc);
+      // online softmax of column hl over keys 4*grp + v, the reference max
+      // moving only past kLazy of headroom (as in tile_compute)
+      float sv[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = (vmask >> v) & 1u ? sc[v] * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, sv[v]);
+      }
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazy) != 0) {
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float av = __shfl(alpha, 4 * grp + v);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[nb][v] *= av;
+        }
+      }
+      v4s phi, plo;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float pr = exp2f(sv[v] - m_run);
+        l_run += pr;
+        const uint32_t hb = f32_to_bf16_bits(pr);
+        phi[v] = (short)hb;
+        plo[v] = (short)f32_to_bf16_bits(pr - bf16_bits_to_f32(hb));
+      }
+      // O += P V, V^T operand read key-major from the shared tile
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const char* vp = vlds[buf] + (4 * grp) * VROW + (16 * nb + hl) * 2;
+        v4s vb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vb[e] = *reinterpret_cast<const short*>(vp + e * VROW);
+        o[nb] = mfma_bf16_16x16x16(phi, vb, o[nb]);
+        o[nb] = mfma_bf16_16x16x16(plo, vb, o[nb]);
+      }
+    }
+    // buffer buf ^ 1 was last read in the previous step, before its barrier
+    if (ld && i + 1 < ntile) swrite(buf ^ 1, st[k]);
+    if (ld && i + 1 + NST < ntile) st[k] = gload((i + 1 + NST) * KT);
+    __syncthreads();
+  }
+  }
+
+  l_run = finish_l(l_run);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int col = 4 * grp + v;
+    const float lh = __shfl(l_run, col);
+    const float mh = __shfl(m_run, col);
+    const int j = col / G, h = col % G;
+    if (j >= nqw) continue;
+    const int64_t pr = (int64_t)(q0 + j) * a.Hq + (int64_t)g * G + h;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) a.part_o[pr * D + 16 * nb + hl] = o[nb][v];
+    if (hl == 0) { a.part_ml[2 * pr] = mh; a.part_ml[2 * pr + 1] = lh; }
+  }
+}
+
 // ---- grouped long-range attention ----
 // Queries with similar selections share most of their long-range keys (the
 // select writes a row's best bucket first, so equal first keys mean the same
@@ -464,7 +647,7 @@ __global__ void __launch_bounds__(AT, 4) k_attn_win(AttnArgs a) {
 // the row, index) and taken qpw at a time; each group's long-range rows are merged into one list
 // with a mask of the queries that selected each row, so a shared K/V row is
 // read once per group instead of once per query.  The sinks and window are
-// attended separately, in position order (k_attn_win<.., 1>), and the grouped
+// attended separately, in position order (k_attn_swin), and the grouped
 // kernel starts each query's softmax state from that partial result.
 
 // Long-range entries of a row: the select's rows end with the sinks and window.
@@ -1438,8 +1621,10 @@ hipError_t launch_attn_grouped(const uint16_t* q, const uint16_t* k, const uint1
   hipError_t e = hipSuccess;
   if (parts & kGroupedPrepare) {
     // 1. sinks and window of every query, in position order, as partials
-    if (ap.D == 128) hipLaunchKernelGGL((k_attn_win<128, false, 1>), dim3(grid), dim3(AT), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_win<64, false, 1>), dim3(grid), dim3(AT), 0, s, a);
+    const size_t span = (size_t)SW * L.qpw;
+    const unsigned sgrid = (unsigned)((nq + span - 1) / span * ap.Hkv);
+    if (ap.D == 128) hipLaunchKernelGGL((k_attn_swin<128>), dim3(sgrid), dim3(SW * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_swin<64>), dim3(sgrid), dim3(SW * 64), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
