@@ -382,6 +382,38 @@ def bench_tree_same_data(res, dev, steps, warmup, name="tree_10m"):
             "union_fraction": float(unions.sum()) / float(res["grouped"]["long_range_entries"])}
 
 
+def bench_other_config(name, args, dev):
+    """The same prefill step (prebuilt index, append, select, grouped
+    attention) on another Flat workload, with its roofline fractions: the
+    walk against the HBM peak (per-query and union bytes), the step against
+    its layer roof, and the index build against its roof."""
+    a = argparse.Namespace(**vars(args))
+    a.config = name
+    r = bench_prefill(a, dev)
+    wl = r["wl"]
+    ms = r["ms_per_step"]
+    roof = layer_roof_ms(wl, r, r["attn_phase_bytes_per_query"])
+    out = {"workload": name, "context_tokens": wl.T, "chunk_queries": r["n"],
+           "attention": f"GQA {wl.Hq}/{wl.Hkv} D={wl.D} bf16",
+           "select": f"{wl.budget}+{wl.window}+{wl.sinks}",
+           "ms_per_step": ms, "queries_per_s": r["n"] / (ms * 1e-3),
+           "phases_ms": {"append": r["phase_ms"][0], "select": r["phase_ms"][1],
+                         "attention": r["phase_ms"][2]},
+           "selected_keys_per_query": r["cnt_mean"],
+           "union_fraction": r["grouped"]["union_fraction"],
+           "walk_ms": r["attn_ms"],
+           "walk_frac_per_query_bytes": r["achieved_gbs"] / HBM_PEAK_GBS,
+           "walk_frac_union_bytes": r["union_gbs"] / HBM_PEAK_GBS,
+           "layer": {"roof_ms": roof, "frac": roof / ms},
+           "index_build": {"keys": wl.T, "ms": r["build_ms"],
+                           "keys_per_s": wl.T / (r["build_ms"] * 1e-3),
+                           "roof_ms": build_roof_ms(wl), "frac": build_roof_ms(wl) / r["build_ms"]},
+           "fused_entry_point_identical": r["fused_same"]}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_copy_gbs(dev, nbytes=2 << 30):
     """Read + write bandwidth of a plain device copy (torch), for context."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -962,6 +994,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-tree", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 1M and tiny Flat prefill steps of the default line")
     ap.add_argument("--profile", action="store_true",
                     help="one prefill step plus a 2 GiB calibration copy (for rocprofv3 runs)")
     ap.add_argument("--full-prefill", action="store_true",
@@ -1069,6 +1103,14 @@ def main():
         log(f"[bench] tree_10m step {tree['ms_per_step']:.2f} ms, selected keys per query "
             f"{tree['selected_keys_per_query']}")
 
+    others = None
+    if not args.no_configs and wl.name == "flat_10m":
+        others = {}
+        for name in ("flat_1m", "tiny_flat"):
+            others[name] = bench_other_config(name, args, dev)
+            log(f"[bench] {name} step {others[name]['ms_per_step']:.3f} ms "
+                f"({others[name]['queries_per_s']:.0f} queries/s)")
+
     # counters of the attention kernel (profiles/attn_traffic.json), valid
     # while the kernel's source is unchanged
     traffic = dram = prof_ms = None
@@ -1166,6 +1208,7 @@ def main():
         "index_build": {"keys": wl.T, "ms": res["build_ms"], "roof_ms": build_roof_ms(wl),
                         "frac": build_roof_ms(wl) / res["build_ms"]},
         "tree_10m": tree,
+        "other_configs": others,
         "decode": decode,
         "dense_scan": dense,
         "train_step_128k": train,
