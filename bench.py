@@ -497,16 +497,18 @@ def bench_dense(res, dev):
                     "selection rule (p=1 singleton buckets)"}
 
 
-def bench_full_prefill(args, dev):
+def bench_full_prefill(args, dev, data=None):
     """Every chunk of the context through lsa_prefill_chunk, the index grown
     chunk by chunk from empty: the whole prefill of one layer (a per-layer
     time-to-first-token analogue).  Only the fused calls are timed; the next
-    chunk's Q and latent queries are generated outside the timed regions."""
+    chunk's Q and latent queries are generated outside the timed regions.
+    `data`: the workload's (generator, latents, K, V) when already on the
+    device."""
     wl = S.WORKLOADS[args.config]
     n = wl.chunk
     nchunks = wl.T // n
     log(f"[full] {wl.name}: {nchunks} chunks of {n} queries")
-    g, latk, K, V = gen_inputs(wl, dev)
+    g, latk, K, V = data if data is not None else gen_inputs(wl, dev)
     sp = L.SelectParams(wl.budget, wl.window, wl.sinks, wl.tree_top)
     ap = L.AttnParams(wl.Hq, wl.Hkv, wl.D, 0, 0.0)
     ix = L.LsaIndex(iparams(wl, wl.T), dev)
@@ -994,6 +996,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-tree", action="store_true")
+    ap.add_argument("--no-full", action="store_true",
+                    help="skip the whole 10M prefill (320 chunks) of the default line")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the 1M and tiny Flat prefill steps of the default line")
     ap.add_argument("--profile", action="store_true",
@@ -1111,6 +1115,11 @@ def main():
             log(f"[bench] {name} step {others[name]['ms_per_step']:.3f} ms "
                 f"({others[name]['queries_per_s']:.0f} queries/s)")
 
+    full = None
+    if not args.no_full and wl.name == "flat_10m":
+        full = bench_full_prefill(args, dev, data=(res["g"], res["latk"], res["K"], res["V"]))
+        torch.cuda.empty_cache()
+
     # counters of the attention kernel (profiles/attn_traffic.json), valid
     # while the kernel's source is unchanged
     traffic = dram = prof_ms = None
@@ -1209,6 +1218,7 @@ def main():
                         "frac": build_roof_ms(wl) / res["build_ms"]},
         "tree_10m": tree,
         "other_configs": others,
+        "full_prefill_10m": full,
         "decode": decode,
         "dense_scan": dense,
         "train_step_128k": train,
